@@ -1,0 +1,102 @@
+"""Oracle: tree-masked grouped-query attention, dense softmax in float64.
+
+Test infrastructure only (see oracle/__init__.py).
+
+What is computed ([HB] tree_spec.py forward_with_mask and the correctness check;
+[E2] section 4 tree_decoding; [TRT] packed ancestor mask): for request b, query head
+h and tree node i < T_b the visible keys are every committed prefix row
+0..P_b-1 of kv head g = h // (Hq/Hkv) (the KV heads are repeated across the
+query-head group) plus the tree rows P_b + j for which node j is node i itself
+or one of its ancestors (bit j of the packed mask row i).  The output is
+softmax(q . k * scale) . v over those keys, scale = 1/sqrt(d) by default (the
+scaled-dot-product default).  Q and K are taken after any rotary embedding.
+
+Inputs are fed exactly as the library receives them: bf16 bit patterns (uint16)
+or float32.  bf16 -> float64 is exact; all arithmetic is float64; a matmul from
+numpy is the only library primitive.  Rows i >= T_b of the output are left as
+given; a request with non-zero status is the root-only tree (T_b = 1).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+def to_f64(x: np.ndarray) -> np.ndarray:
+    """Decode the stored element type exactly: uint16 arrays are bfloat16 bit patterns
+    (the upper 16 bits of a float32), anything else is cast."""
+    if x.dtype == np.uint16:
+        return (x.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    return x.astype(np.float64)
+
+
+def visible_tree_nodes(mask_row: np.ndarray, T: int):
+    """Node ids j < T whose bit is set in a packed mask row (bit j&31 of word j>>5)."""
+    return [j for j in range(T) if (int(mask_row[j >> 5]) >> (j & 31)) & 1]
+
+
+def full_mask(tree_mask_b: np.ndarray, T: int, P: int) -> np.ndarray:
+    """[T][P+T] boolean visibility for one request, built as [HB] forward_with_mask
+    builds it: every node sees all P prefix columns, followed by the T x T tree mask
+    (unpacked from the packed rows)."""
+    m = np.zeros((T, P + T), dtype=bool)
+    m[:, :P] = True
+    for i in range(T):
+        for j in visible_tree_nodes(tree_mask_b[i], T):
+            m[i, P + j] = True
+    return m
+
+
+def tree_attention(Q, Kc, Vc, prefix_len, tree_size, tree_mask, status=None, scale=None, out=None,
+                   requests=None):
+    """Returns float64 O shaped like Q.  ``requests`` limits the work to a subset of
+    request ids (the others are left as in ``out``, default zero).
+
+    Per request and kv head the scores of all T*rep query rows against all P+T keys
+    are one float64 matmul; masked entries get -inf; each row is soft-maxed
+    (max-subtracted) and multiplied by V -- the dense masked attention of the
+    definition."""
+    B, T_max, Hq, d = Q.shape
+    Hkv = Kc.shape[1]
+    rep = Hq // Hkv
+    if scale is None or scale <= 0:
+        scale = 1.0 / math.sqrt(d)
+    O = np.zeros(Q.shape, np.float64) if out is None else np.array(out, dtype=np.float64, copy=True)
+    for b in (range(B) if requests is None else requests):
+        T = int(tree_size[b])
+        if status is not None and int(status[b]) != 0:
+            T = 1
+        P = int(prefix_len[b])
+        vis = full_mask(tree_mask[b], T, P)                            # [T][P+T]
+        for g in range(Hkv):
+            keys = to_f64(Kc[b, g, :P + T])                            # [P+T][d]
+            vals = to_f64(Vc[b, g, :P + T])
+            q = to_f64(Q[b, :T, g * rep:(g + 1) * rep])                # [T][rep][d]
+            s = (q.reshape(T * rep, d) @ keys.T).reshape(T, rep, P + T) * scale   # [T][rep][P+T]
+            s = np.where(vis[:, None, :], s, -np.inf)
+            p = np.exp(s - s.max(axis=2, keepdims=True))
+            O[b, :T, g * rep:(g + 1) * rep] = (p @ vals) / p.sum(axis=2, keepdims=True)
+    return O
+
+
+def attention_rows(Q, Kc, Vc, prefix_len, tree_size, tree_mask, samples, scale=None, status=None):
+    """Oracle output for a list of sampled (b, i, h) rows only (for full-size checks)."""
+    B, T_max, Hq, d = Q.shape
+    rep = Hq // Kc.shape[1]
+    if scale is None or scale <= 0:
+        scale = 1.0 / math.sqrt(d)
+    res = []
+    for b, i, h in samples:
+        T = int(tree_size[b])
+        if status is not None and int(status[b]) != 0:
+            T = 1
+        P = int(prefix_len[b])
+        g = h // rep
+        vis = list(range(P)) + [P + j for j in visible_tree_nodes(tree_mask[b, i], T)]
+        k_i = to_f64(Kc[b, g][vis])
+        v_i = to_f64(Vc[b, g][vis])
+        s = (k_i @ to_f64(Q[b, i, h])) * scale
+        p = np.exp(s - s.max())
+        res.append((p @ v_i) / p.sum())
+    return np.array(res)
