@@ -1,0 +1,250 @@
+"""Benchmark of one full tree-verification step on one MI355X.
+
+A step = tree_build -> tree_mask_positions -> tree_attention -> tree_accept ->
+kv_compact over one batch of synthetic inputs, all through the C ABI on one HIP
+stream.  The default workload is the EAGLE-2 dynamic tree at batch 1 (top_k 10,
+depth 6, 60 draft nodes + root, prefix 2048, Llama-3-8B attention heads 32/8/128,
+bf16); --config 1..5 selects another of the five measured workloads.
+
+Inputs are resident in HBM before the timed region.  Input copies are rotated
+(>= --rotate-mb of them) so that repeated steps stream from HBM instead of the
+256 MB last-level cache.  Prints ONE JSON line on stdout; diagnostics go to stderr.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
+FP32_PEAK_TFLOPS = 157.3     # MI355X fp32 vector, published
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def attention_work(w, tree_size, depth, status):
+    """Algorithmic bytes and flops of one tree_attention call: each visible K/V row is
+    read once per kv head, Q read and O written once, the packed mask read once;
+    flops count QK^T and PV over the visible keys only (prefix + ancestors + self)."""
+    eb = 2 if w.dtype == "bf16" else 4
+    W = (w.T_max + 31) // 32
+    nbytes = 0
+    flops = 0
+    for b in range(w.B):
+        T = 1 if status[b] != 0 else int(tree_size[b])
+        P = int(w.prefix_len[b])
+        nbytes += (P + T) * w.Hkv * w.d * eb * 2 + 2 * T * w.Hq * w.d * eb + T * W * 4
+        flops += sum(w.Hq * 4 * w.d * (P + int(depth[b, i]) + 1) for i in range(T))
+    return nbytes, flops
+
+
+def source_hash():
+    path = os.path.join(ROOT, "tree_attention_verification_amd", "csrc", "tree_attention.hip")
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload_name):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken
+    on the current attention source (else None)."""
+    path = os.path.join(ROOT, "profiles", "attention_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    ent = rec.get("workloads", {}).get(workload_name)
+    if not ent or ent.get("source_sha") != source_hash():
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, seconds: float):
+    """The oracle, as it stands, on a bounded sample of the same workload."""
+    from oracle import attention as oa
+    from oracle import kv as okv
+    from oracle import tree as ot
+    from workloads import gen
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+
+    def one_step(ws):
+        t = ot.tree_build(ws)
+        m = ot.tree_mask_positions(t["parents"], t["tree_size"], ws.prefix_len, ws.T_max, ws.dcap,
+                                   t["status"] if ws.mode != "given" else None)
+        oa.tree_attention(ws.Q, ws.Kc, ws.Vc, ws.prefix_len, t["tree_size"], m["tree_mask"], status=m["status"])
+        tp = gen.synthetic_target_predict(ws, t["draft_tokens"], t["parents"], t["tree_size"])
+        a = ot.tree_accept(t["draft_tokens"], t["parents"], t["tree_size"], tp, m["status"], ws.dcap)
+        okv.kv_compact(ws.Kc, ws.Vc, ws.prefix_len, a["accept_path"], a["accept_len"])
+        return int(np.where(m["status"] != 0, 1, t["tree_size"]).sum())
+
+    # sample: the first requests of the batch, as many as fit the time budget
+    import copy
+    nb = w.B
+    sample = w
+    t0 = time.perf_counter()
+    nodes = one_step(sample)
+    dt = time.perf_counter() - t0
+    while dt > seconds and nb > 1:
+        nb = max(1, nb // 2)
+        sample = copy.copy(w)
+        for k in ("logprobs", "root_token", "given_parents", "given_tokens", "given_size", "prefix_len", "Q", "Kc",
+                  "Vc", "tgt_u", "tgt_choice", "tgt_rand"):
+            v = getattr(w, k)
+            if v is not None:
+                setattr(sample, k, v[:nb])
+        sample.B = nb
+        t0 = time.perf_counter()
+        nodes = one_step(sample)
+        dt = time.perf_counter() - t0
+    reps, total_nodes, total_t = 1, nodes, dt
+    while total_t < seconds:
+        t0 = time.perf_counter()
+        total_nodes += one_step(sample)
+        total_t += time.perf_counter() - t0
+        reps += 1
+    return {"value": total_nodes / total_t, "unit": "tree-nodes/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{reps} full step(s) of the first {nb} of {w.B} request(s) ({total_t:.1f} s; tree ops "
+                      f"single-threaded, float64 attention on {threads} BLAS thread(s))"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--rotate-mb", type=float, default=512.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (requests or kv heads would be "
+              "sharded across GPUs with no exchange; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from tree_attention_verification_amd import _lib
+    from tree_attention_verification_amd.step import TreeVerifyStep
+    from workloads import gen
+
+    _lib.lib()
+    torch.cuda.set_device(0)
+    w = gen.make_workload(args.config)
+    per_copy = w.Q.nbytes + w.Kc.nbytes + w.Vc.nbytes + (w.logprobs.nbytes if w.logprobs is not None else 0)
+    n_copies = max(1, min(64, math.ceil(args.rotate_mb * 2 ** 20 / per_copy)))
+    log(f"workload {w.name}: {per_copy / 2**20:.1f} MiB of inputs per copy, {n_copies} copies rotated")
+    step = TreeVerifyStep(w, n_copies=n_copies)
+    stream = torch.cuda.current_stream()
+
+    # the synthetic target's argmax needs the tree: build once and read it back (untimed)
+    step.build()
+    step.meta()
+    torch.cuda.synchronize()
+    th = step.tree_host()
+    mh = step.meta_host()
+    step.set_target_predict(gen.synthetic_target_predict(w, th["draft_tokens"], th["parents"], th["tree_size"]))
+    torch.cuda.synchronize()
+    status = mh["status"]
+    nodes = int(np.where(status != 0, 1, th["tree_size"]).sum())
+
+    def one(k, ev=None):
+        step.copy = k % n_copies
+        step.build()
+        step.meta()
+        if ev is not None:
+            ev[0].record(stream)
+        step.attention()
+        if ev is not None:
+            ev[1].record(stream)
+        step.accept()
+        step.compact()
+
+    for k in range(args.warmup):
+        one(k)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        one(args.warmup + k, evs[k])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    ms_per_step = elapsed * 1e3 / args.steps
+
+    # stage breakdown (untimed extra pass, events between every call)
+    names = ["tree_build", "tree_mask_positions", "tree_attention", "tree_accept", "kv_compact"]
+    reps = min(50, args.steps)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(reps)]
+    for r in range(reps):
+        step.copy = r % n_copies
+        ev[r][0].record(stream)
+        step.build(); ev[r][1].record(stream)
+        step.meta(); ev[r][2].record(stream)
+        step.attention(); ev[r][3].record(stream)
+        step.accept(); ev[r][4].record(stream)
+        step.compact(); ev[r][5].record(stream)
+    torch.cuda.synchronize()
+    stages = {n: round(float(np.mean([ev[r][i].elapsed_time(ev[r][i + 1]) for r in range(reps)])) * 1e3, 2)
+              for i, n in enumerate(names)}
+
+    nbytes, flops = attention_work(w, th["tree_size"], mh["tree_position_ids"], status)
+    t_attn = attn_ms * 1e-3
+    mfma_peak = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
+    if nbytes / (HBM_PEAK_GBS * 1e9) >= flops / (mfma_peak * 1e12):
+        roof = {"bound": "hbm", "achieved": round(nbytes / t_attn / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma" if w.dtype == "bf16" else "alu", "achieved": round(flops / t_attn / 1e12, 2),
+                "peak": mfma_peak, "unit": "TFLOP/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = measured_traffic(w.name)
+    roof["kernel"] = "tree_attention call (k_attn_bf16 + k_attn_combine when the keys are split)"
+    roof["algorithmic_bytes"] = int(nbytes)
+    roof["algorithmic_flops"] = int(flops)
+    roof["avg_us"] = round(attn_ms * 1e3, 3)
+
+    out = {
+        "metric": "tree-verify nodes/sec (batch x tree) + % of HBM/MFMA roofline, 1 MI355X",
+        "value": round(nodes / (ms_per_step * 1e-3), 1),
+        "unit": "tree-nodes/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded draft log-probs, Q/K/V and target argmax; no weights)",
+        "config": {"workload": w.name, "batch": w.B, "prefix_len": [int(x) for x in w.prefix_len[:4]] +
+                   (["..."] if w.B > 4 else []), "tree_nodes_per_step": nodes, "top_k": w.K, "depth": w.D,
+                   "total_tokens": w.total_tokens, "Hq": w.Hq, "Hkv": w.Hkv, "head_dim": w.d, "vocab": w.V,
+                   "input_copies_rotated": n_copies},
+        "stages_us": stages,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle ...")
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,215 @@
+/*
+ * treeverify.h -- C ABI of libtreeverify.so, the tree-verification step of
+ * EAGLE-2/3 dynamic-tree speculative decoding on AMD Instinct MI355X (gfx950).
+ *
+ * One verification step is five calls, in this order:
+ *   tree_build          draft log-probs  -> draft_tokens, parents, tree_size
+ *   tree_mask_positions parents          -> packed ancestor mask, positions,
+ *                                           retrieve_indices, child/sibling lists
+ *   tree_attention      Q, K/V cache, mask -> O (every node over prefix + ancestors)
+ *   tree_accept         target argmax per node -> accepted path, bonus token
+ *   kv_compact          accepted path    -> K/V rows moved to contiguous slots
+ *
+ * Sources for what each call computes (cited by page title and section):
+ *   [E2]  EAGLE v2 dynamic-tree decoding walkthrough -- section 2 initialize_tree
+ *         (outputs draft_tokens, retrieve_indices, tree_mask, tree_position_ids),
+ *         section 3 topK_generate, section 4 tree_decoding, section 5
+ *         evaluate_posterior.
+ *   [HB]  AI-infra handbook, "Advanced speculative decoding: tree drafts and
+ *         EAGLE" -- tree_spec.py (forward_with_mask, tree_mask, depths,
+ *         build_draft_tree, tree_speculative_generate) and the KV note after it.
+ *   [TRT] "TensorRT-LLM source dissection (22): EAGLE-3 one-model drafter" --
+ *         section "dynamic draft tree": the three ledgers (parent buffer, packed
+ *         mask [bs, N, ceil(N/32)], position offsets), the tree-build kernel,
+ *         greedy verification on the child/sibling lists, KV relocation.
+ *
+ * Conventions (all calls):
+ *   - Every pointer is a DEVICE pointer unless marked "host".  The caller owns
+ *     and allocates every buffer; the library keeps no state and allocates no
+ *     memory.  Scratch memory comes from the caller as a workspace sized by the
+ *     matching *_workspace_bytes() query.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue
+ *     work on that stream and never synchronize.
+ *   - Return value: TV_OK, or a negative TV_E* code.  Arguments are validated on
+ *     the host before anything is enqueued; nothing is clamped or truncated
+ *     silently.  Out-of-range data that only the device can see (tree sizes,
+ *     parents, prefix lengths) is reported per request in `status[b]`.
+ *   - Per-request status (int32, in/out along the pipeline): TV_ST_OK or a
+ *     TV_ST_* code.  A request with non-zero status degrades to the root-only
+ *     tree (mask = bit 0, position = prefix_len, accept_len = 0, bonus =
+ *     target_predict[0], compaction a no-op), mirroring the default linear
+ *     chain / tree_valid fallback of [TRT] ("per-request trees stored by slot").
+ *   - Tree layout: node 0 is the root; tree_size counts the root; parents[0] =
+ *     -1 and 0 <= parents[i] < i.  T_max is the padded node dimension of every
+ *     per-node array (this version supports T_max <= 64).  Padding entries are
+ *     -1 for tokens / parents / node ids, 0 for masks and positions, -inf for
+ *     scores.  dcap is the deepest node depth the caller provisions for
+ *     (retrieve rows and accepted paths have dcap + 1 columns).
+ */
+#ifndef TREEVERIFY_H
+#define TREEVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* return codes */
+#define TV_OK 0
+#define TV_EINVAL (-1)       /* null pointer, bad dimension or inconsistent sizes */
+#define TV_EUNSUPPORTED (-2) /* a size this build does not implement (d, T_max, dtype, K) */
+#define TV_EWORKSPACE (-3)   /* workspace missing or smaller than the query says */
+#define TV_ELAUNCH (-4)      /* the HIP runtime rejected a kernel launch */
+
+/* per-request status codes */
+#define TV_ST_OK 0
+#define TV_ST_PARENTS 1   /* parents[0] != -1, or parents[i] outside [0, i) */
+#define TV_ST_DEPTH 2     /* a node deeper than dcap */
+#define TV_ST_SIZE 3      /* tree_size outside [1, T_max] */
+#define TV_ST_LOGPROB 4   /* NaN / positive log-prob read, or a kept node whose parent was dropped */
+
+#define TV_MODE_DYNAMIC 0
+#define TV_MODE_STATIC 1
+#define TV_DTYPE_BF16 0
+#define TV_DTYPE_FP32 1
+
+/* ------------------------------------------------------------------------- *
+ * tree_build -- [E2] section 3 (topK_generate), [TRT] _select_topk_draft_tokens,
+ * [HB] build_draft_tree.
+ *
+ * mode TV_MODE_DYNAMIC (EAGLE-2): logprobs is float32 [B][rows_per_req][V] with
+ *   rows_per_req = 1 + D*K.  Row 0 is the draft distribution after the root; row
+ *   1 + (l-1)*K + j is the distribution after frontier slot j of expansion round
+ *   l (l = 1..D).  Base layer: the K best tokens of row 0 (log-prob descending,
+ *   token ascending) are candidates 0..K-1 with score = log-prob.  Round l: every
+ *   frontier slot j expands into the K best tokens r of its row, candidate id
+ *   K + (l-1)K^2 + jK + r, score = float32(log-prob + score of slot j); the K best
+ *   of those K^2 (score descending, jK+r ascending) are the next frontier.  Final:
+ *   the total_tokens best of all C = K + D*K^2 candidates (score descending, id
+ *   ascending) become nodes 1..total_tokens in ascending id; node 0 is the root
+ *   (draft_tokens[0] = root_token[b], score 0).  tree_size = total_tokens + 1.
+ *   Requires 1 <= K <= 16, 0 <= D <= 64, 0 <= total_tokens <= C, C <= 3072,
+ *   total_tokens + 1 <= T_max, K <= V.  `branching` is ignored.
+ * mode TV_MODE_STATIC ([HB] build_draft_tree): branching (host, n_levels
+ *   entries, each 1..16) gives the width of each level; every node of the
+ *   current frontier, in order, appends the top-branching[l] tokens of its own
+ *   row as children.  Row n of logprobs is the distribution after node n;
+ *   rows_per_req must equal the number of expanded (non-last-level) nodes.
+ *   Node score = float32(log-prob + parent score).  K, D, total_tokens ignored.
+ * Outputs (each [B][T_max], padded): draft_tokens int32, parents int32,
+ *   node_score float32 (nullable), tree_size int32 [B], status int32 [B]
+ *   (TV_ST_OK or TV_ST_LOGPROB: any NaN or positive value in a row that is read
+ *   gives the root-only tree).
+ * Workspace: tree_build_workspace_bytes(mode, B, V, K, rows_per_req).
+ * ------------------------------------------------------------------------- */
+size_t tree_build_workspace_bytes(int mode, int B, int V, int K, int rows_per_req);
+int tree_build(int mode, int B, int V, int K, int D, int total_tokens,
+               const int* branching /* host */, int n_levels,
+               const float* logprobs, int rows_per_req, const int* root_token,
+               int T_max, int* draft_tokens, int* parents, int* tree_size,
+               float* node_score /* nullable */, int* status,
+               void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------- *
+ * tree_mask_positions -- [TRT] tree-build kernel (parents -> packed ancestor
+ * mask, position offsets, retrieve lists; outputs fully rewritten each step),
+ * [HB] tree_mask / depths, [E2] section 3 third step (tree_mask,
+ * retrieve_indices, tree_position_ids).
+ *
+ * In:  parents [B][T_max], tree_size [B], prefix_len [B], status_in [B]
+ *      (nullable = all TV_ST_OK; a non-zero entry is kept and gives the
+ *      root-only tree; may alias status_out).
+ * Out: tree_mask uint32 [B][T_max][W], W = ceil(T_max/32): row i has bit j&31 of
+ *        word j>>5 set iff node j is node i or one of its ancestors;
+ *      tree_position_ids [B][T_max] = node depth (root 0);
+ *      positions [B][T_max] = prefix_len[b] + depth (siblings share a position);
+ *      retrieve_indices [B][T_max][dcap+1]: one row per leaf (a node without
+ *        children), leaves in ascending id, column k = the node at depth k on
+ *        the root-to-leaf path, -1 padded; rows >= leaf_count all -1;
+ *      leaf_count [B];
+ *      first_child / next_sibling [B][T_max] (nullable): children in ascending
+ *        id, -1 where none;
+ *      status_out [B]: status_in if non-zero, else TV_ST_SIZE, TV_ST_PARENTS,
+ *        TV_ST_DEPTH (checked in that order) or TV_ST_OK.
+ * Requires 1 <= T_max <= 64, 0 <= dcap < T_max.
+ * ------------------------------------------------------------------------- */
+int tree_mask_positions(int B, int T_max, int dcap, const int* parents,
+                        const int* tree_size, const int* prefix_len,
+                        uint32_t* tree_mask, int* tree_position_ids, int* positions,
+                        int* retrieve_indices, int* leaf_count,
+                        int* first_child /* nullable */, int* next_sibling /* nullable */,
+                        const int* status_in /* nullable */, int* status_out, void* stream);
+
+/* ------------------------------------------------------------------------- *
+ * tree_attention -- [HB] forward_with_mask (full mask = all-visible prefix
+ * columns followed by the tree mask; grouped KV heads repeated over the query
+ * heads; default softmax scale), [E2] section 4 tree_decoding.
+ *
+ * For request b, query head h and node i < T_b (T_b = tree_size[b], or 1 when
+ * status[b] != 0): keys = cache rows 0..P_b-1 (P_b = prefix_len[b]) and rows
+ * P_b + j for every node j whose bit is set in tree_mask row i, of kv head
+ * g = h / (Hq/Hkv).  O[b][i][h] = softmax(scale * q . k) . v.
+ * Layouts (elements of dtype: bf16 or float32, row-major):
+ *   Q, O  [B][T_max][Hq][d];  Kc, Vc  [B][Hkv][S_cap][d], tree node j's K/V at
+ *   row P_b + j (already written by the caller's projection of the tree).
+ * scale <= 0 selects 1/sqrt(d).  bf16 inputs accumulate in float32; the softmax
+ * is computed online in float32.  Rows i >= T_b of O are not written.  A request
+ * whose prefix does not fit the cache (prefix_len < 0 or prefix_len + T_b >
+ * S_cap) reads no K/V and gets O rows 0..T_b-1 set to zero (status is read,
+ * never written, by this call).
+ * Requires d in {64, 128}, Hq % Hkv == 0, Hq/Hkv <= 16, T_max <= 64.
+ * Workspace: tree_attention_workspace_bytes(...) with the same shape arguments.
+ * ------------------------------------------------------------------------- */
+size_t tree_attention_workspace_bytes(int dtype, int B, int T_max, int Hq, int Hkv, int d,
+                                      long long S_cap);
+int tree_attention(int dtype, int B, int T_max, int Hq, int Hkv, int d,
+                   const void* Q, const void* Kc, const void* Vc, long long S_cap,
+                   const int* prefix_len, const int* tree_size, const uint32_t* tree_mask,
+                   const int* status, float scale, void* O,
+                   void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------- *
+ * tree_accept -- [TRT] greedy verification (walk from the root: accept the child
+ * whose token equals the target's argmax, else stop; path <= depth + 1), [HB]
+ * tree_speculative_generate (first matching child by index; next root = target
+ * argmax at the path end), [E2] section 5 (same result as the longest
+ * cumprod-accepted retrieve row when sibling tokens are distinct).
+ *
+ * In:  draft_tokens, parents, target_predict [B][T_max] (the target's argmax at
+ *      every node), tree_size [B], status [B].
+ * Out: accept_len [B] = accepted draft nodes (0..dcap), accept_path
+ *      [B][dcap+1] = node ids root first, -1 padded, bonus_token [B] =
+ *      target_predict at the last node of the path.
+ * ------------------------------------------------------------------------- */
+int tree_accept(int B, int T_max, int dcap, const int* draft_tokens, const int* parents,
+                const int* tree_size, const int* target_predict, const int* status,
+                int* accept_len, int* accept_path, int* bonus_token, void* stream);
+
+/* ------------------------------------------------------------------------- *
+ * kv_compact -- [TRT] "after acceptance: KV from tree layout back to linear",
+ * [HB] note after tree_spec.py (accepted KV is reused, not recomputed; it is
+ * compacted into the sequence's positions, rejected slots are dropped).
+ *
+ * Kc, Vc: n_layers blocks of [B][Hkv][S_cap][d] elements of elem_bytes (2 or
+ * 4), block l at element offset l * layer_stride_elems.  For every layer, kv
+ * head and k = 1..L (L = accept_len[b]) row P_b + k receives the old row
+ * P_b + accept_path[b][k]; all sources of a (request, head, layer) are read
+ * before any destination is written, so overlapping paths are safe.  Other rows
+ * are untouched.  new_prefix_len[b] = P_b + L + 1 (nullable).  Requires
+ * d*elem_bytes to be a multiple of 16 and <= 1024, dcap < 64.
+ * ------------------------------------------------------------------------- */
+int kv_compact(int B, int n_layers, int Hkv, int d, int elem_bytes, void* Kc, void* Vc,
+               long long S_cap, long long layer_stride_elems, const int* prefix_len,
+               const int* accept_path, const int* accept_len, int dcap,
+               int* new_prefix_len /* nullable */, void* stream);
+
+/* human-readable names for return codes and status codes */
+const char* tv_error_string(int code);
+const char* tv_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TREEVERIFY_H */

@@ -1,0 +1,172 @@
+"""GPU parity: the HIP library (through the C ABI) against the CPU oracle.
+
+Every test runs the five calls on the GPU and compares each stage with the oracle
+on the same seeded inputs (tests/parity_util.py states the bars).  Sizes: the five
+configurations at sizes the oracle finishes in seconds (spanning several key
+tiles and a ragged tail), the long-context and large-batch configurations at full
+size in the launch configuration the benchmark times (attention checked on
+sampled rows), plus fuzzed shapes and the degenerate cases of the method.
+"""
+import numpy as np
+import pytest
+
+from tests.conftest import gpu_available
+from workloads import gen
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not gpu_available():
+        pytest.skip("no GPU")
+    from tree_attention_verification_amd import _lib
+    _lib.lib()   # raises if the library is missing: no fallback
+
+
+def run(w, **kw):
+    from tests.parity_util import run_pipeline_and_compare
+    return run_pipeline_and_compare(w, **kw)
+
+
+# ----------------------------------------------------------------------------- configurations
+def test_cfg1_tiny_static_fp32():
+    r = run(gen.make_workload(1))
+    assert list(r["tree_size"]) == [11]
+
+
+def test_cfg2_eagle2_dynamic_full():
+    r = run(gen.make_workload(2))
+    assert list(r["tree_size"]) == [61]
+
+
+def test_cfg3_ragged_batch16_full():
+    r = run(gen.make_workload(3))
+    assert (r["tree_size"] == 49).all()
+
+
+def test_cfg4_long_context_reduced_prefix():
+    run(gen.make_workload(4, batch=2, prefix=3000))
+
+
+def test_cfg5_random_trees_reduced():
+    run(gen.make_workload(5, batch=12, prefix=777))
+
+
+def test_cfg4_full_size_sampled():
+    run(gen.make_workload(4), attention="sampled", samples=96)
+
+
+def test_cfg5_full_size_sampled():
+    run(gen.make_workload(5), attention="sampled", samples=96)
+
+
+def test_cfg3_full_size_sampled_more_rows():
+    run(gen.make_workload(3), attention="sampled", samples=256, seed=3)
+
+
+# ----------------------------------------------------------------------------- tree shapes
+def test_peaked_drafts_give_deep_dynamic_trees():
+    w = gen.make_workload(2, peaked=True, prefix=300)
+    r = run(w)
+    assert r["tree_size"][0] == 61
+
+
+@pytest.mark.parametrize("K,D,TT", [(1, 6, 6), (3, 0, 2), (2, 2, 10), (16, 2, 63), (4, 3, 52), (5, 1, 30)])
+def test_dynamic_build_shapes(K, D, TT):
+    w = gen.make_custom(cfg_id=500 + K * 10 + D, mode="dynamic", K=K, D=D, total_tokens=TT, V=777, P=70,
+                        Hq=4, Hkv=2, d=64, dtype="bf16")
+    run(w)
+
+
+@pytest.mark.parametrize("br", [[2, 2, 1, 1], [3, 3, 2], [1] * 20, [7], [4, 1, 4]])
+def test_static_build_shapes(br):
+    w = gen.make_custom(cfg_id=600 + len(br), mode="static", branching=br, V=1003, P=65, Hq=8, Hkv=4, d=128,
+                        dtype="bf16", dcap=20)
+    run(w)
+
+
+def test_dynamic_total_tokens_equal_to_all_candidates():
+    w = gen.make_custom(cfg_id=650, mode="dynamic", K=3, D=2, total_tokens=3 + 2 * 9, V=64, P=10, T_max=32,
+                        dcap=3, Hq=2, Hkv=1, d=64)
+    run(w)
+
+
+# ----------------------------------------------------------------------------- fuzzed given trees
+@pytest.mark.parametrize("seed", range(12))
+def test_fuzz_given_trees(seed):
+    rng = np.random.default_rng(seed)
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    rep = int(rng.choice([1, 2, 4, 8]))
+    d = int(rng.choice([64, 128]))
+    dtype = "bf16" if seed % 4 else "fp32"
+    B = int(rng.integers(1, 6))
+    P = [int(x) for x in rng.integers(0, 700, size=B)]
+    T_max = int(rng.choice([32, 64]))
+    sizes = [int(x) for x in rng.integers(1, T_max + 1, size=B)]
+    w = gen.make_custom(cfg_id=700 + seed, B=B, P=P, mode="given", given_sizes=sizes, given_depth=int(rng.integers(1, 9)),
+                        T_max=T_max, dcap=8, Hq=Hkv * rep, Hkv=Hkv, d=d, dtype=dtype, V=50)
+    run(w)
+
+
+def test_edge_prefix_zero_and_single_node():
+    w = gen.make_custom(cfg_id=800, B=4, P=[0, 1, 63, 64], mode="given", given_sizes=[1, 64, 1, 33],
+                        Hq=8, Hkv=2, d=128, dtype="bf16", V=40)
+    run(w)
+
+
+def test_edge_chain_of_64_with_full_depth_cap():
+    w = gen.make_custom(cfg_id=801, B=2, P=[100, 5], mode="given", given_sizes=[64, 64], given_depth=63, T_max=64,
+                        dcap=63, Hq=4, Hkv=4, d=64, dtype="bf16", V=100)
+    run(w)
+
+
+def test_edge_long_prefix_many_splits_bf16_d64():
+    w = gen.make_custom(cfg_id=802, B=2, P=[9000, 4321], mode="given", given_sizes=[40, 17], Hq=16, Hkv=2, d=64,
+                        dtype="bf16", V=100)
+    run(w)
+
+
+# ----------------------------------------------------------------------------- failure handling
+def test_status_codes_and_root_only_fallback():
+    """Malformed parents, depth above the cap and out-of-range sizes give the status
+    codes the oracle gives, and the root-only tree everywhere downstream."""
+    w = gen.make_custom(cfg_id=900, B=6, P=[50, 60, 70, 80, 90, 100], mode="given",
+                        given_sizes=[10, 10, 10, 10, 10, 10], given_depth=9, dcap=3, Hq=4, Hkv=2, d=64, V=30)
+    w.given_parents[0, 0] = 0            # root with a parent
+    w.given_parents[1, 5] = 7            # parent after child
+    w.given_parents[2, 3] = 3            # self loop
+    w.given_size[3] = 0                  # empty tree
+    w.given_size[4] = 65                 # larger than T_max
+    w.given_parents[5, 1:10] = np.arange(0, 9)   # a chain deeper than dcap = 3
+    w.given_tokens[5, 1:10] = np.arange(1, 10)
+    run(w)
+
+
+def test_bad_logprobs_status():
+    w = gen.make_custom(cfg_id=901, B=3, mode="dynamic", K=4, D=2, total_tokens=12, V=257, P=33, d=64)
+    w.logprobs[1, 3, 100] = 0.25         # a positive log-prob
+    w.logprobs[2, 0, 5] = np.nan
+    w.logprobs[0, 2, 7] = -np.inf        # zero probability is fine
+    run(w)
+
+
+def test_prefix_that_does_not_fit_gives_zero_rows():
+    import torch
+    from tree_attention_verification_amd.step import TreeVerifyStep
+    w = gen.make_custom(cfg_id=902, B=2, P=[10, 40], mode="given", given_sizes=[5, 30], Hq=4, Hkv=2, d=64,
+                        S_cap=64, V=40)
+    st = TreeVerifyStep(w)
+    st.O.fill_(1.0)
+    st.meta()
+    st.attention()
+    torch.cuda.synchronize()
+    o = st.O.float().cpu().numpy()
+    assert (o[1, :30] == 0).all()                    # 40 + 30 > 64: zeros
+    assert (o[1, 30:] == 1).all()                    # rows past the tree untouched
+    assert np.isfinite(o[0, :5]).all() and (o[0, 5:] == 1).all()
+
+
+def test_vocab_not_multiple_of_four_and_misaligned_rows():
+    w = gen.make_custom(cfg_id=903, B=2, mode="dynamic", K=5, D=2, total_tokens=20, V=1001, P=20, d=64)
+    run(w)

@@ -1,0 +1,75 @@
+"""The C-ABI library without a GPU: it loads, exports every function the header
+declares, and rejects invalid arguments on the host before touching the device."""
+import ctypes
+
+import pytest
+
+from tree_attention_verification_amd import _lib as tv
+
+
+def test_library_exports_every_declared_symbol():
+    L = tv.lib()
+    names = tv.declared_functions()
+    assert {"tree_build", "tree_mask_positions", "tree_attention", "tree_accept", "kv_compact"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_error_and_status_strings():
+    assert tv.error_string(tv.TV_EINVAL) == "invalid argument"
+    assert tv.error_string(tv.TV_EWORKSPACE).startswith("workspace")
+    assert tv.status_string(tv.TV_ST_DEPTH).startswith("tree deeper")
+
+
+X = ctypes.c_void_p(0x1000)   # a non-null dummy; never dereferenced on the error paths below
+
+
+def test_tree_build_host_validation():
+    L = tv.lib()
+    br = (ctypes.c_int * 3)(2, 2, 1)
+    # B = 0
+    assert L.tree_build(0, 0, 100, 4, 2, 5, None, 0, X, 9, X, 64, X, X, X, None, X, X, 1 << 20, None) == tv.TV_EINVAL
+    # total_tokens larger than K + D*K^2
+    assert L.tree_build(0, 1, 100, 2, 1, 7, None, 0, X, 3, X, 64, X, X, X, None, X, X, 1 << 20, None) == tv.TV_EINVAL
+    # rows_per_req != 1 + D*K
+    assert L.tree_build(0, 1, 100, 2, 1, 5, None, 0, X, 4, X, 64, X, X, X, None, X, X, 1 << 20, None) == tv.TV_EINVAL
+    # K above the supported maximum
+    assert L.tree_build(0, 1, 100, 17, 1, 5, None, 0, X, 18, X, 64, X, X, X, None, X, X, 1 << 20,
+                        None) == tv.TV_EUNSUPPORTED
+    # tree does not fit T_max
+    assert L.tree_build(0, 1, 100, 4, 2, 40, None, 0, X, 9, X, 32, X, X, X, None, X, X, 1 << 20, None) == tv.TV_EINVAL
+    # workspace too small
+    assert L.tree_build(0, 1, 100, 4, 2, 10, None, 0, X, 9, X, 64, X, X, X, None, X, X, 8, None) == tv.TV_EWORKSPACE
+    # static: rows_per_req must be the number of expanded nodes (7 for [2,2,1])
+    assert L.tree_build(1, 1, 100, 0, 0, 0, br, 3, X, 6, X, 64, X, X, X, None, X, X, 1 << 20, None) == tv.TV_EINVAL
+    # null output
+    assert L.tree_build(1, 1, 100, 0, 0, 0, br, 3, X, 7, X, 64, None, X, X, None, X, X, 1 << 20, None) == tv.TV_EINVAL
+
+
+def test_other_calls_host_validation():
+    L = tv.lib()
+    # tree_mask_positions: dcap must be < T_max, T_max <= 64
+    assert L.tree_mask_positions(1, 64, 64, X, X, X, X, X, X, X, X, None, None, None, X, None) == tv.TV_EINVAL
+    assert L.tree_mask_positions(1, 65, 7, X, X, X, X, X, X, X, X, None, None, None, X, None) == tv.TV_EUNSUPPORTED
+    # tree_attention: Hq % Hkv, head dim, dtype, misaligned pointers, workspace
+    args = dict(Q=X, K=X, V=X)
+    assert L.tree_attention(0, 1, 64, 6, 4, 128, X, X, X, 4096, X, X, X, X, 0.0, X, None, 0, None) == tv.TV_EINVAL
+    assert L.tree_attention(0, 1, 64, 8, 4, 96, X, X, X, 4096, X, X, X, X, 0.0, X, None, 0, None) == tv.TV_EUNSUPPORTED
+    assert L.tree_attention(7, 1, 64, 8, 4, 128, X, X, X, 4096, X, X, X, X, 0.0, X, None, 0, None) == tv.TV_EUNSUPPORTED
+    odd = ctypes.c_void_p(0x1002)
+    assert L.tree_attention(0, 1, 64, 8, 4, 128, odd, X, X, 4096, X, X, X, X, 0.0, X, None, 0, None) == tv.TV_EINVAL
+    need = tv.tree_attention_workspace_bytes(0, 1, 64, 32, 8, 128, 65536)
+    assert need > 0
+    assert L.tree_attention(0, 1, 64, 32, 8, 128, X, X, X, 65536, X, X, X, X, 0.0, X, X, need - 1,
+                            None) == tv.TV_EWORKSPACE
+    # tree_accept: dcap >= T_max
+    assert L.tree_accept(1, 16, 16, X, X, X, X, X, X, X, X, None) == tv.TV_EINVAL
+    # kv_compact: row bytes must be a multiple of 16
+    assert L.kv_compact(1, 1, 8, 100, 2, X, X, 4096, 0, X, X, X, 7, None, None) == tv.TV_EUNSUPPORTED
+    assert L.kv_compact(1, 1, 8, 128, 3, X, X, 4096, 0, X, X, X, 7, None, None) == tv.TV_EINVAL
+
+
+def test_python_binding_refuses_host_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        tv.tree_accept(1, 8, 3, torch.zeros(1, 8, dtype=torch.int32), None, None, None, None, None, None, None)

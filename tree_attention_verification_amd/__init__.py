@@ -1,0 +1,12 @@
+"""MI355X-native tree-verification step for EAGLE-2/3 dynamic-tree speculative decoding.
+
+The work is done by libtreeverify.so (hand-written HIP for gfx950, C ABI in
+include/treeverify.h); `_lib` is the ctypes binding with the same call names and
+`step.TreeVerifyStep` holds one batch's device buffers and runs the five calls.
+"""
+from . import _lib
+from ._lib import (tree_build, tree_build_workspace_bytes, tree_mask_positions, tree_attention,
+                   tree_attention_workspace_bytes, tree_accept, kv_compact, TVError)
+
+__all__ = ["tree_build", "tree_build_workspace_bytes", "tree_mask_positions", "tree_attention",
+           "tree_attention_workspace_bytes", "tree_accept", "kv_compact", "TVError"]

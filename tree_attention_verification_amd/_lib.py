@@ -1,0 +1,175 @@
+"""ctypes binding to libtreeverify.so -- argument marshalling only.
+
+Every function has the name and argument order of the C call it wraps
+(include/treeverify.h).  Device buffers are passed as torch tensors on the GPU
+(their data_ptr() is handed to the library), sizes as Python ints, and the
+stream is torch's current HIP stream unless one is given.  No computation of
+the step happens here: every step runs in the library's HIP kernels.  There is
+no fallback -- if the library is missing or a tensor is not on the GPU the call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtreeverify.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "treeverify.h")
+
+TV_OK, TV_EINVAL, TV_EUNSUPPORTED, TV_EWORKSPACE, TV_ELAUNCH = 0, -1, -2, -3, -4
+TV_ST_OK, TV_ST_PARENTS, TV_ST_DEPTH, TV_ST_SIZE, TV_ST_LOGPROB = 0, 1, 2, 3, 4
+MODE_DYNAMIC, MODE_STATIC = 0, 1
+DTYPE_BF16, DTYPE_FP32 = 0, 1
+
+
+class TVError(RuntimeError):
+    def __init__(self, call: str, code: int):
+        super().__init__(f"{call} failed: {error_string(code)} ({code})")
+        self.code = code
+
+
+_lib = None
+
+P = ctypes.c_void_p
+I = ctypes.c_int
+LL = ctypes.c_longlong
+SZ = ctypes.c_size_t
+F = ctypes.c_float
+
+_SIGS = {
+    "tree_build_workspace_bytes": (SZ, [I, I, I, I, I]),
+    "tree_build": (I, [I, I, I, I, I, I, P, I, P, I, P, I, P, P, P, P, P, P, SZ, P]),
+    "tree_mask_positions": (I, [I, I, I, P, P, P, P, P, P, P, P, P, P, P, P, P]),
+    "tree_attention_workspace_bytes": (SZ, [I, I, I, I, I, I, LL]),
+    "tree_attention": (I, [I, I, I, I, I, I, P, P, P, LL, P, P, P, P, F, P, P, SZ, P]),
+    "tree_accept": (I, [I, I, I, P, P, P, P, P, P, P, P, P]),
+    "kv_compact": (I, [I, I, I, I, I, P, P, LL, LL, P, P, P, I, P, P]),
+    "tv_error_string": (ctypes.c_char_p, [I]),
+    "tv_status_string": (ctypes.c_char_p, [I]),
+}
+
+
+def lib():
+    """Load the in-tree library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m tree_attention_verification_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def declared_functions():
+    """Names of the functions include/treeverify.h declares."""
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def error_string(code: int) -> str:
+    return lib().tv_error_string(int(code)).decode()
+
+
+def status_string(st: int) -> str:
+    return lib().tv_status_string(int(st)).decode()
+
+
+def _dev(t, name):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: tensor must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: tensor must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ws(ws):
+    if ws is None:
+        return None, 0
+    return _dev(ws, "workspace"), ws.numel() * ws.element_size()
+
+
+def _check(name, rc):
+    if rc != TV_OK:
+        raise TVError(name, rc)
+
+
+def tree_build_workspace_bytes(mode, B, V, K, rows_per_req) -> int:
+    return int(lib().tree_build_workspace_bytes(mode, B, V, K, rows_per_req))
+
+
+def tree_build(mode, B, V, K, D, total_tokens, branching, logprobs, rows_per_req, root_token, T_max,
+               draft_tokens, parents, tree_size, node_score, status, workspace, stream=None):
+    br = None
+    n_levels = 0
+    if branching:
+        n_levels = len(branching)
+        br = (ctypes.c_int * n_levels)(*[int(x) for x in branching])
+    wp, wn = _ws(workspace)
+    rc = lib().tree_build(mode, B, V, K, D, total_tokens, br, n_levels, _dev(logprobs, "logprobs"), rows_per_req,
+                          _dev(root_token, "root_token"), T_max, _dev(draft_tokens, "draft_tokens"),
+                          _dev(parents, "parents"), _dev(tree_size, "tree_size"), _dev(node_score, "node_score"),
+                          _dev(status, "status"), wp, wn, _stream(stream))
+    _check("tree_build", rc)
+
+
+def tree_mask_positions(B, T_max, dcap, parents, tree_size, prefix_len, tree_mask, tree_position_ids, positions,
+                        retrieve_indices, leaf_count, first_child, next_sibling, status_in, status_out, stream=None):
+    rc = lib().tree_mask_positions(B, T_max, dcap, _dev(parents, "parents"), _dev(tree_size, "tree_size"),
+                                   _dev(prefix_len, "prefix_len"), _dev(tree_mask, "tree_mask"),
+                                   _dev(tree_position_ids, "tree_position_ids"), _dev(positions, "positions"),
+                                   _dev(retrieve_indices, "retrieve_indices"), _dev(leaf_count, "leaf_count"),
+                                   _dev(first_child, "first_child"), _dev(next_sibling, "next_sibling"),
+                                   _dev(status_in, "status_in"), _dev(status_out, "status_out"), _stream(stream))
+    _check("tree_mask_positions", rc)
+
+
+def tree_attention_workspace_bytes(dtype, B, T_max, Hq, Hkv, d, S_cap) -> int:
+    return int(lib().tree_attention_workspace_bytes(dtype, B, T_max, Hq, Hkv, d, S_cap))
+
+
+def tree_attention(dtype, B, T_max, Hq, Hkv, d, Q, Kc, Vc, S_cap, prefix_len, tree_size, tree_mask, status, scale,
+                   O, workspace, stream=None):
+    wp, wn = _ws(workspace)
+    rc = lib().tree_attention(dtype, B, T_max, Hq, Hkv, d, _dev(Q, "Q"), _dev(Kc, "Kc"), _dev(Vc, "Vc"), S_cap,
+                              _dev(prefix_len, "prefix_len"), _dev(tree_size, "tree_size"),
+                              _dev(tree_mask, "tree_mask"), _dev(status, "status"), float(scale), _dev(O, "O"),
+                              wp, wn, _stream(stream))
+    _check("tree_attention", rc)
+
+
+def tree_accept(B, T_max, dcap, draft_tokens, parents, tree_size, target_predict, status, accept_len, accept_path,
+                bonus_token, stream=None):
+    rc = lib().tree_accept(B, T_max, dcap, _dev(draft_tokens, "draft_tokens"), _dev(parents, "parents"),
+                           _dev(tree_size, "tree_size"), _dev(target_predict, "target_predict"),
+                           _dev(status, "status"), _dev(accept_len, "accept_len"), _dev(accept_path, "accept_path"),
+                           _dev(bonus_token, "bonus_token"), _stream(stream))
+    _check("tree_accept", rc)
+
+
+def kv_compact(B, n_layers, Hkv, d, elem_bytes, Kc, Vc, S_cap, layer_stride_elems, prefix_len, accept_path,
+               accept_len, dcap, new_prefix_len, stream=None):
+    rc = lib().kv_compact(B, n_layers, Hkv, d, elem_bytes, _dev(Kc, "Kc"), _dev(Vc, "Vc"), S_cap, layer_stride_elems,
+                          _dev(prefix_len, "prefix_len"), _dev(accept_path, "accept_path"),
+                          _dev(accept_len, "accept_len"), dcap, _dev(new_prefix_len, "new_prefix_len"),
+                          _stream(stream))
+    _check("kv_compact", rc)

@@ -1,0 +1,164 @@
+// tree_accept: greedy acceptance walk; kv_compact: accepted K/V rows to
+// contiguous slots.
+//
+// tree_accept follows the greedy verification of the TensorRT-LLM EAGLE-3
+// dissection (walk from the root; at each node accept the child whose draft
+// token equals the target's argmax there, else stop; the path is at most
+// depth + 1 long) and the handbook's tree_speculative_generate (the matching
+// child is the first by index; the next root is the target's argmax at the end
+// of the path).  One wavefront per request, lane c = node c: each step is one
+// ballot over "parent == current node and token == prediction" and the lowest
+// set lane is the child, so a step costs O(1) instead of a scan of the tree.
+//
+// kv_compact follows the KV note after the handbook's tree_spec.py and the
+// dissection's "after acceptance: KV from tree layout back to linear": the
+// accepted nodes' K/V are moved (not recomputed) to rows P+1..P+L.  One
+// workgroup per (request, kv head, layer) reads every source row into
+// registers, synchronises, then writes, so a source that is also an earlier
+// destination is read before it is overwritten.
+#include "tv_common.h"
+
+namespace tv {
+namespace {
+
+__global__ __launch_bounds__(64) void k_tree_accept(int T_max, int dcap, const int* __restrict__ draft_tokens,
+                                                    const int* __restrict__ parents,
+                                                    const int* __restrict__ tree_size,
+                                                    const int* __restrict__ target_predict,
+                                                    const int* __restrict__ status, int* __restrict__ accept_len,
+                                                    int* __restrict__ accept_path, int* __restrict__ bonus_token) {
+  const int b = blockIdx.x, c = threadIdx.x;
+  const long long ob = (long long)b * T_max;
+  int T = tree_size[b];
+  if (status[b] != TV_ST_OK || T < 1 || T > T_max) T = 1;
+  const int tok = c < T ? draft_tokens[ob + c] : -1;
+  const int par = (c > 0 && c < T) ? parents[ob + c] : -2;
+  int node = 0, len = 0, mine = c == 0 ? 0 : -1;
+  for (int step = 0; step < dcap; ++step) {
+    const int pred = target_predict[ob + node];
+    const unsigned long long hit = __ballot(par == node && tok == pred);
+    if (!hit) break;
+    node = __ffsll((long long)hit) - 1;  // lowest-index matching child
+    ++len;
+    if (c == len) mine = node;
+  }
+  if (c <= dcap) accept_path[(long long)b * (dcap + 1) + c] = mine;
+  if (c == 0) {
+    accept_len[b] = len;
+    bonus_token[b] = target_predict[ob + node];
+  }
+}
+
+constexpr int kCompactThreads = 256;
+constexpr int kCompactPerThread = 16;  // 63 rows x 64 16-byte chunks / 256 threads
+
+__global__ __launch_bounds__(kCompactThreads) void k_kv_compact(int B, int Hkv, int chunks16, uint4* __restrict__ Kc,
+                                                                uint4* __restrict__ Vc, long long S_cap,
+                                                                long long layer_stride16,
+                                                                const int* __restrict__ prefix_len,
+                                                                const int* __restrict__ accept_path,
+                                                                const int* __restrict__ accept_len, int dcap,
+                                                                int* __restrict__ new_prefix_len) {
+  const int g = blockIdx.x % Hkv;
+  const int b = blockIdx.x / Hkv;
+  const int layer = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int P = prefix_len[b];
+  int L = accept_len[b];
+  const int* path = accept_path + (long long)b * (dcap + 1);
+  bool ok = L >= 1 && L <= dcap && P >= 0;
+  // every source and destination row must lie inside the cache
+  if (ok) {
+    for (int k = 1; k <= L; ++k) {
+      const int n = path[k];
+      if (n < k || (long long)P + n >= S_cap) ok = false;
+    }
+  }
+  // a request whose path does not fit is left untouched (its prefix grows by the root only)
+  if (g == 0 && layer == 0 && tid == 0 && new_prefix_len) new_prefix_len[b] = P + (ok ? L : 0) + 1;
+  if (!ok) return;
+  const long long head = ((long long)layer * layer_stride16) + ((long long)b * Hkv + g) * S_cap * chunks16;
+  const int items = L * chunks16;
+  for (int t = 0; t < 2; ++t) {
+    uint4* base = (t == 0 ? Kc : Vc) + head;
+    uint4 v[kCompactPerThread];
+#pragma unroll
+    for (int u = 0; u < kCompactPerThread; ++u) {
+      const int q = tid + u * kCompactThreads;
+      if (q < items) {
+        const int k = 1 + q / chunks16, c = q % chunks16;
+        v[u] = base[((long long)P + path[k]) * chunks16 + c];
+      }
+    }
+    __syncthreads();  // every source read before any destination write
+#pragma unroll
+    for (int u = 0; u < kCompactPerThread; ++u) {
+      const int q = tid + u * kCompactThreads;
+      if (q < items) {
+        const int k = 1 + q / chunks16, c = q % chunks16;
+        base[((long long)P + k) * chunks16 + c] = v[u];
+      }
+    }
+  }
+}
+
+}  // namespace
+}  // namespace tv
+
+extern "C" int tree_accept(int B, int T_max, int dcap, const int* draft_tokens, const int* parents,
+                           const int* tree_size, const int* target_predict, const int* status, int* accept_len,
+                           int* accept_path, int* bonus_token, void* stream) {
+  if (B <= 0 || T_max <= 0 || dcap < 0 || dcap >= T_max) return TV_EINVAL;
+  if (T_max > tv::kTMaxLimit) return TV_EUNSUPPORTED;
+  if (!draft_tokens || !parents || !tree_size || !target_predict || !status || !accept_len || !accept_path ||
+      !bonus_token)
+    return TV_EINVAL;
+  hipLaunchKernelGGL(tv::k_tree_accept, dim3(B), dim3(64), 0, reinterpret_cast<hipStream_t>(stream), T_max, dcap,
+                     draft_tokens, parents, tree_size, target_predict, status, accept_len, accept_path, bonus_token);
+  TV_CHECK_LAUNCH();
+  return TV_OK;
+}
+
+extern "C" int kv_compact(int B, int n_layers, int Hkv, int d, int elem_bytes, void* Kc, void* Vc, long long S_cap,
+                          long long layer_stride_elems, const int* prefix_len, const int* accept_path,
+                          const int* accept_len, int dcap, int* new_prefix_len, void* stream) {
+  if (B <= 0 || n_layers <= 0 || Hkv <= 0 || d <= 0 || S_cap <= 0 || dcap < 0 || dcap >= 64) return TV_EINVAL;
+  if (elem_bytes != 2 && elem_bytes != 4) return TV_EINVAL;
+  if (!Kc || !Vc || !prefix_len || !accept_path || !accept_len) return TV_EINVAL;
+  const long long row_bytes = (long long)d * elem_bytes;
+  if (row_bytes % 16 != 0 || row_bytes > 1024) return TV_EUNSUPPORTED;
+  const long long per_layer = (long long)B * Hkv * S_cap * d;
+  if (n_layers > 1 && layer_stride_elems < per_layer) return TV_EINVAL;
+  if ((layer_stride_elems * elem_bytes) % 16 != 0) return TV_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(Kc) & 15) || (reinterpret_cast<uintptr_t>(Vc) & 15)) return TV_EINVAL;
+  if ((long long)B * Hkv > 2147483647LL || n_layers > 65535) return TV_EINVAL;
+  const int chunks16 = (int)(row_bytes / 16);
+  hipLaunchKernelGGL(tv::k_kv_compact, dim3(B * Hkv, n_layers), dim3(tv::kCompactThreads), 0,
+                     reinterpret_cast<hipStream_t>(stream), B, Hkv, chunks16, reinterpret_cast<uint4*>(Kc),
+                     reinterpret_cast<uint4*>(Vc), S_cap, layer_stride_elems * elem_bytes / 16, prefix_len,
+                     accept_path, accept_len, dcap, new_prefix_len);
+  TV_CHECK_LAUNCH();
+  return TV_OK;
+}
+
+extern "C" const char* tv_error_string(int code) {
+  switch (code) {
+    case TV_OK: return "ok";
+    case TV_EINVAL: return "invalid argument";
+    case TV_EUNSUPPORTED: return "unsupported size or type";
+    case TV_EWORKSPACE: return "workspace missing or too small";
+    case TV_ELAUNCH: return "kernel launch failed";
+    default: return "unknown error";
+  }
+}
+
+extern "C" const char* tv_status_string(int st) {
+  switch (st) {
+    case TV_ST_OK: return "ok";
+    case TV_ST_PARENTS: return "malformed parents";
+    case TV_ST_DEPTH: return "tree deeper than dcap";
+    case TV_ST_SIZE: return "tree size out of range";
+    case TV_ST_LOGPROB: return "invalid log-prob or unclosed tree";
+    default: return "unknown status";
+  }
+}

@@ -1,0 +1,176 @@
+"""Device buffers for one batch of the verification step, and the five calls in order.
+
+Marshalling only: inputs are copied to the GPU once, outputs and workspaces are
+allocated once, and `run()` enqueues tree_build -> tree_mask_positions ->
+tree_attention -> tree_accept -> kv_compact on one stream through the C ABI.
+
+The batch description is any object with these attributes (numpy arrays):
+  mode ('dynamic' | 'static' | 'given'), B, V, K, D, total_tokens, branching,
+  T_max, dcap, logprobs [B][R][V] float32 (None for 'given'), root_token [B],
+  given_parents / given_tokens [B][T_max], given_size [B] ('given' only),
+  prefix_len [B], Hq, Hkv, d, dtype ('bf16' | 'fp32'), S_cap,
+  Q [B][T_max][Hq][d], Kc / Vc [B][Hkv][S_cap][d] (uint16 bf16 bits or float32).
+In 'given' mode the drafter's tree is an input and the build call is skipped.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import _lib as tv
+
+_MODES = {"dynamic": tv.MODE_DYNAMIC, "static": tv.MODE_STATIC}
+
+
+def _t(a, device, dtype=None):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:          # bf16 bit patterns travel as int16 storage
+        t = torch.from_numpy(a.view(np.int16)).to(device)
+        return t.view(torch.bfloat16)
+    t = torch.from_numpy(a).to(device)
+    return t if dtype is None else t.to(dtype)
+
+
+def _copies(t, n):
+    return [t] + [t.clone() for _ in range(n - 1)]
+
+
+class TreeVerifyStep:
+    def __init__(self, w, device: str = "cuda", n_copies: int = 1):
+        self.w = w
+        self.device = device
+        B, T_max, dcap = w.B, w.T_max, w.dcap
+        self.B, self.T_max, self.dcap = B, T_max, dcap
+        W = (T_max + 31) // 32
+        i32 = dict(dtype=torch.int32, device=device)
+        # inputs
+        self.prefix_len = _t(w.prefix_len.astype(np.int32), device)
+        self.root_token = _t(w.root_token.astype(np.int32), device)
+        self.mode = w.mode
+        if w.mode == "given":
+            self.logprobs_copies = [None]
+            self.draft_tokens = _t(w.given_tokens.astype(np.int32), device)
+            self.parents = _t(w.given_parents.astype(np.int32), device)
+            self.tree_size = _t(w.given_size.astype(np.int32), device)
+        else:
+            self.logprobs_copies = _copies(_t(w.logprobs.astype(np.float32), device), n_copies)
+            self.draft_tokens = torch.full((B, T_max), -7, **i32)
+            self.parents = torch.full((B, T_max), -7, **i32)
+            self.tree_size = torch.zeros(B, **i32)
+        self.node_score = torch.zeros((B, T_max), dtype=torch.float32, device=device)
+        self.status = torch.full((B,), 99, **i32)
+        # input copies (more than one lets a benchmark rotate its inputs through HBM
+        # so that repeated steps do not run out of the last-level cache)
+        self.Q_copies = _copies(_t(w.Q, device), n_copies)
+        self.Kc = _copies(_t(w.Kc, device), n_copies)
+        self.Vc = _copies(_t(w.Vc, device), n_copies)
+        # outputs
+        self.tree_mask = torch.full((B, T_max, W), 0x5A5A5A5A, dtype=torch.int32, device=device)
+        self.tree_position_ids = torch.full((B, T_max), -7, **i32)
+        self.positions = torch.full((B, T_max), -7, **i32)
+        self.retrieve_indices = torch.full((B, T_max, dcap + 1), -7, **i32)
+        self.leaf_count = torch.full((B,), -7, **i32)
+        self.first_child = torch.full((B, T_max), -7, **i32)
+        self.next_sibling = torch.full((B, T_max), -7, **i32)
+        self.O = torch.zeros_like(self.Q_copies[0])
+        self.target_predict = torch.full((B, T_max), -1, **i32)
+        self.accept_len = torch.full((B,), -7, **i32)
+        self.accept_path = torch.full((B, dcap + 1), -7, **i32)
+        self.bonus_token = torch.full((B,), -7, **i32)
+        self.new_prefix_len = torch.full((B,), -7, **i32)
+        # workspaces
+        self.dtype_code = tv.DTYPE_BF16 if w.dtype == "bf16" else tv.DTYPE_FP32
+        self.elem_bytes = 2 if w.dtype == "bf16" else 4
+        if w.mode != "given":
+            R = w.logprobs.shape[1]
+            K = w.K if w.mode == "dynamic" else max(w.branching)
+            nb = tv.tree_build_workspace_bytes(_MODES[w.mode], B, w.V, K, R)
+            self.ws_build = torch.zeros(max(nb, 1), dtype=torch.uint8, device=device)
+        else:
+            self.ws_build = None
+        na = tv.tree_attention_workspace_bytes(self.dtype_code, B, T_max, w.Hq, w.Hkv, w.d, w.S_cap)
+        self.ws_attn = torch.zeros(na, dtype=torch.uint8, device=device) if na else None
+        self.copy = 0
+
+    @property
+    def logprobs(self):
+        return self.logprobs_copies[self.copy % len(self.logprobs_copies)]
+
+    @property
+    def Q(self):
+        return self.Q_copies[self.copy]
+
+    # ---- the five calls -------------------------------------------------------
+    def build(self, stream=None):
+        w = self.w
+        if w.mode == "given":
+            return
+        R = w.logprobs.shape[1]
+        tv.tree_build(_MODES[w.mode], self.B, w.V, w.K, w.D, w.total_tokens,
+                      w.branching if w.mode == "static" else None, self.logprobs, R, self.root_token,
+                      self.T_max, self.draft_tokens, self.parents, self.tree_size, self.node_score, self.status,
+                      self.ws_build, stream)
+
+    def meta(self, stream=None):
+        status_in = None if self.w.mode == "given" else self.status
+        tv.tree_mask_positions(self.B, self.T_max, self.dcap, self.parents, self.tree_size, self.prefix_len,
+                               self.tree_mask, self.tree_position_ids, self.positions, self.retrieve_indices,
+                               self.leaf_count, self.first_child, self.next_sibling, status_in, self.status, stream)
+
+    def attention(self, stream=None, copy=None):
+        w = self.w
+        c = self.copy if copy is None else copy
+        tv.tree_attention(self.dtype_code, self.B, self.T_max, w.Hq, w.Hkv, w.d, self.Q_copies[c], self.Kc[c],
+                          self.Vc[c],
+                          w.S_cap, self.prefix_len, self.tree_size, self.tree_mask, self.status, 0.0, self.O,
+                          self.ws_attn, stream)
+
+    def accept(self, stream=None):
+        tv.tree_accept(self.B, self.T_max, self.dcap, self.draft_tokens, self.parents, self.tree_size,
+                       self.target_predict, self.status, self.accept_len, self.accept_path, self.bonus_token, stream)
+
+    def compact(self, stream=None, copy=None):
+        w = self.w
+        c = self.copy if copy is None else copy
+        tv.kv_compact(self.B, 1, w.Hkv, w.d, self.elem_bytes, self.Kc[c], self.Vc[c], w.S_cap, 0, self.prefix_len,
+                      self.accept_path, self.accept_len, self.dcap, self.new_prefix_len, stream)
+
+    def run(self, stream=None):
+        """One full pass of the step (target_predict must already be set)."""
+        self.build(stream)
+        self.meta(stream)
+        self.attention(stream)
+        self.accept(stream)
+        self.compact(stream)
+
+    def set_target_predict(self, tp: np.ndarray):
+        self.target_predict.copy_(torch.from_numpy(np.ascontiguousarray(tp.astype(np.int32))))
+
+    # ---- host copies ----------------------------------------------------------
+    def tree_host(self):
+        return dict(draft_tokens=self.draft_tokens.cpu().numpy(), parents=self.parents.cpu().numpy(),
+                    tree_size=self.tree_size.cpu().numpy(), node_score=self.node_score.cpu().numpy(),
+                    status=self.status.cpu().numpy())
+
+    def meta_host(self):
+        return dict(tree_mask=self.tree_mask.cpu().numpy().view(np.uint32),
+                    tree_position_ids=self.tree_position_ids.cpu().numpy(), positions=self.positions.cpu().numpy(),
+                    retrieve_indices=self.retrieve_indices.cpu().numpy(), leaf_count=self.leaf_count.cpu().numpy(),
+                    first_child=self.first_child.cpu().numpy(), next_sibling=self.next_sibling.cpu().numpy(),
+                    status=self.status.cpu().numpy())
+
+    def out_host(self):
+        o = self.O.cpu()
+        if o.dtype == torch.bfloat16:
+            return o.view(torch.int16).numpy().view(np.uint16)
+        return o.numpy()
+
+    def kv_host(self, copy=0):
+        def h(t):
+            t = t.cpu()
+            return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+        return h(self.Kc[copy]), h(self.Vc[copy])
+
+    def accept_host(self):
+        return dict(accept_len=self.accept_len.cpu().numpy(), accept_path=self.accept_path.cpu().numpy(),
+                    bonus_token=self.bonus_token.cpu().numpy(), new_prefix_len=self.new_prefix_len.cpu().numpy())

@@ -299,6 +299,8 @@ def synthetic_target_predict(w: Workload, draft_tokens: np.ndarray, parents: np.
     out = np.full((B, T_max), -1, dtype=np.int32)
     for b in range(B):
         T = int(tree_size[b])
+        if T < 1 or T > T_max:          # a malformed tree is verified as its root alone
+            T = 1
         for i in range(T):
             kids = [c for c in range(1, T) if parents[b, c] == i]
             if kids and w.tgt_u[b, i] < w.accept_prob:
