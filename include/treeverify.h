@@ -102,7 +102,8 @@ extern "C" {
  *   node_score float32 (nullable), tree_size int32 [B], status int32 [B]
  *   (TV_ST_OK or TV_ST_LOGPROB: any NaN or positive value in a row that is read
  *   gives the root-only tree).
- * Workspace: tree_build_workspace_bytes(mode, B, V, K, rows_per_req).
+ * Workspace: tree_build_workspace_bytes(mode, B, V, K, rows_per_req) bytes (any
+ *   contents); calls that share a workspace must not overlap in time.
  * ------------------------------------------------------------------------- */
 size_t tree_build_workspace_bytes(int mode, int B, int V, int K, int rows_per_req);
 int tree_build(int mode, int B, int V, int K, int D, int total_tokens,

@@ -29,23 +29,30 @@ __global__ __launch_bounds__(64) void k_tree_accept(int T_max, int dcap, const i
                                                     int* __restrict__ accept_path, int* __restrict__ bonus_token) {
   const int b = blockIdx.x, c = threadIdx.x;
   const long long ob = (long long)b * T_max;
+  // every per-node value is fetched at once (lane c holds node c); the walk itself
+  // then only moves data between lanes
   int T = tree_size[b];
-  if (status[b] != TV_ST_OK || T < 1 || T > T_max) T = 1;
-  const int tok = c < T ? draft_tokens[ob + c] : -1;
-  const int par = (c > 0 && c < T) ? parents[ob + c] : -2;
+  const int st = status[b];
+  const int tok_l = c < T_max ? draft_tokens[ob + c] : -1;
+  const int par_l = c < T_max ? parents[ob + c] : -2;
+  const int pred_l = c < T_max ? target_predict[ob + c] : -1;
+  if (st != TV_ST_OK || T < 1 || T > T_max) T = 1;
+  const int tok = c < T ? tok_l : -1;
+  const int par = (c > 0 && c < T) ? par_l : -2;
   int node = 0, len = 0, mine = c == 0 ? 0 : -1;
   for (int step = 0; step < dcap; ++step) {
-    const int pred = target_predict[ob + node];
+    const int pred = __shfl(pred_l, node, 64);
     const unsigned long long hit = __ballot(par == node && tok == pred);
     if (!hit) break;
     node = __ffsll((long long)hit) - 1;  // lowest-index matching child
     ++len;
     if (c == len) mine = node;
   }
+  const int bonus = __shfl(pred_l, node, 64);
   if (c <= dcap) accept_path[(long long)b * (dcap + 1) + c] = mine;
   if (c == 0) {
     accept_len[b] = len;
-    bonus_token[b] = target_predict[ob + node];
+    bonus_token[b] = bonus;
   }
 }
 

@@ -14,17 +14,18 @@
 // MFMA with fp32 accumulation.
 //   * A workgroup is 4 or 8 wavefronts; each wavefront owns one block of 32 query
 //     rows and keeps its Q fragments in registers for the whole kernel.
-//   * Keys are streamed in tiles of 64 through double-buffered LDS: K rows are
-//     copied with coalesced 16-byte loads into an XOR-swizzled layout; V rows are
-//     transposed in registers (v_perm) on the way in, so the PV operand is one
-//     16-byte LDS read.  The next tile's global loads are in flight while the
-//     current tile is computed.
+//   * Keys are streamed in tiles of 64 through double-buffered LDS: K and V rows
+//     are copied with coalesced 16-byte loads into row-major, XOR-swizzled tiles;
+//     the PV operand is read with the gfx950 transpose read (ds_read_b64_tr_b16),
+//     so V is never transposed in registers.  Two register sets keep the loads of
+//     two tiles in flight while a third is computed.
 //   * S^T = K Q^T is formed so that each lane holds 16 keys of one query row:
 //     the row max needs one cross-half exchange, and the accumulator becomes the
 //     PV B-operand directly (keys are permuted consistently in the V^T tile).
 //   * Softmax is online in fp32 in the exp2 domain (scale*log2(e) folded into one
 //     FMA); the running max is only raised when a tile exceeds it by more than
-//     8 (log2 units), so rescaling the accumulators is rare.
+//     8 (log2 units), so rescaling the accumulators is rare; row sums add the
+//     bf16-rounded P that the PV product uses, two at a time with v_dot2.
 //   * The tree mask is read once per row (one 64-bit word) and only the tile(s)
 //     reaching past the prefix apply it; no T x T boolean is formed.
 //   * Long key ranges are split across workgroups (split-KV); each split writes
@@ -86,7 +87,21 @@ Plan make_plan(int B, int T_max, int Hq, int Hkv, long long S_cap) {
   return p;
 }
 
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2, v); }
+#define kOnes2 (bf16x2{(__bf16)1.0f, (__bf16)1.0f})
+
+__device__ __forceinline__ bf16x4 ds_read_tr16(const uint16_t* lds_ptr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(const __attribute__((address_space(3))) uint16_t*)lds_ptr);
+}
+
+// s_waitcnt immediate that waits for lgkmcnt == 0 only (gfx9 encoding: vmcnt bits
+// 3:0 and 15:14 at their maximum, expcnt 6:4 at its maximum, lgkmcnt 11:8 = 0)
+constexpr int kLgkmOnlyZero = 15 | (3 << 14) | (7 << 4);
 
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -101,16 +116,20 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_attn_bf16(
     const uint32_t* __restrict__ tree_mask, const int* __restrict__ status, int T_max, int Hq, int Hkv, int W,
     float sl2, uint16_t* __restrict__ O, float* __restrict__ ws_o, float* __restrict__ ws_ml, int n_split,
     int chunk_keys, int n_rowblk, int n_units, long long m_pad) {
-  constexpr int RB = 1;           // 32-row blocks per wavefront
   constexpr int NT = NW * 64;
-  constexpr int KSTEPS = D / 16;  // 16-wide k-steps of QK^T (8 per half of d)
-  constexpr int DB = D / 32;      // 32-wide d blocks of the output
-  constexpr int CH = D / 8;       // 16-byte chunks per K/V row
-  constexpr int VTS = KT + 8;     // padded V^T row (elements): 144 B for KT = 64
-  constexpr int KLD = KT * CH / NT;
-  constexpr int VITEMS = (KT / 4) * CH;  // (run of 4 keys, chunk) pairs per tile (<= NT)
+  constexpr int KSTEPS = D / 16;     // 16-wide k-steps of QK^T (KSTEPS/2 per half of d)
+  constexpr int DB = D / 32;         // 32-wide d blocks of the output
+  constexpr int CH = D / 8;          // 16-byte chunks per K/V row
+  constexpr int KLD = KT * CH / NT;  // 16-byte chunks per thread per tile and tensor
+  // K and V tiles are row-major (key rows of D elements) in LDS with their 16-byte
+  // chunks XOR-swizzled per row: chunk c of K row r sits at c ^ kswz(r), so the 16
+  // consecutive rows that one 16-byte read serves land on distinct banks; chunk c
+  // of V row r sits at c ^ vswz(r), which spreads the 4-row x 32-byte footprint of
+  // a transpose read over the banks.
+  auto kswz = [](int r) { return CH == 16 ? (r & 15) : ((r >> 1) & 7); };
+  auto vswz = [](int r) { return CH == 16 ? 4 * (r & 3) : 2 * (r & 3); };
   __shared__ __attribute__((aligned(16))) uint16_t s_k[2][KT * D];
-  __shared__ __attribute__((aligned(16))) uint16_t s_vt[2][D * VTS];
+  __shared__ __attribute__((aligned(16))) uint16_t s_v[2][KT * D];
 
   // ---- which (request, kv head, split, row block) this workgroup owns
   const int wg = blockIdx.x;
@@ -129,12 +148,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_attn_bf16(
   const int P = prefix_len[b];
   if (status[b] != TV_ST_OK || T < 1 || T > T_max) T = 1;
   const int M = rep * T;
-  const int row0 = rbk * NW * 32 * RB;
+  const int row0 = rbk * NW * 32;
   if (row0 >= M) return;
   if (P < 0 || (long long)P + T > S_cap) {
     // the prefix does not fit the cache: zero this block's output rows once
     if (split == 0) {
-      for (int q = tid; q < NW * 32 * RB * CH; q += NT) {
+      for (int q = tid; q < NW * 32 * CH; q += NT) {
         const int r = row0 + q / CH;
         if (r < M) {
           const int i = r / rep, head = g * rep + r % rep;
@@ -153,219 +172,215 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_attn_bf16(
   const uint16_t* Kb = Kc + ((long long)b * Hkv + g) * S_cap * D;
   const uint16_t* Vb = Vc + ((long long)b * Hkv + g) * S_cap * D;
 
-  // ---- Q fragments and mask rows of this wavefront's query rows
-  bf16x8 qf[RB][KSTEPS];
-  unsigned long long mrow[RB];
+  // ---- Q fragments and the packed mask row of this lane's query row
+  const int r = row0 + wave * 32 + l32;
+  bf16x8 qf[KSTEPS];
+  unsigned long long mrow = 0ull;
+  if (r < M) {
+    const int i = r / rep, head = g * rep + r % rep;
+    const u32x4* qp = reinterpret_cast<const u32x4*>(Q + (((long long)b * T_max + i) * Hq + head) * D + h * (D / 2));
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int r = row0 + (wave * RB + rb) * 32 + l32;
-    if (r < M) {
-      const int i = r / rep, head = g * rep + r % rep;
-      const u32x4* qp = reinterpret_cast<const u32x4*>(Q + (((long long)b * T_max + i) * Hq + head) * D + h * (D / 2));
+    for (int kk = 0; kk < KSTEPS; ++kk) qf[kk] = as_bf16x8(qp[kk]);
+    const uint32_t* mp = tree_mask + ((long long)b * T_max + i) * W;
+    mrow = (unsigned long long)mp[0] | (W > 1 ? ((unsigned long long)mp[1] << 32) : 0ull);
+  } else {
 #pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) qf[rb][kk] = as_bf16x8(qp[kk]);
-      const uint32_t* mp = tree_mask + ((long long)b * T_max + i) * W;
-      mrow[rb] = (unsigned long long)mp[0] | (W > 1 ? ((unsigned long long)mp[1] << 32) : 0ull);
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) qf[rb][kk] = as_bf16x8(u32x4{0, 0, 0, 0});
-      mrow[rb] = 0ull;
-    }
+    for (int kk = 0; kk < KSTEPS; ++kk) qf[kk] = as_bf16x8(u32x4{0, 0, 0, 0});
   }
 
-  f32x16 acc[RB][DB];
-  float m_run[RB], l_part[RB];
+  f32x16 acc[DB];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    m_run[rb] = -INFINITY;
-    l_part[rb] = 0.0f;
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[rb][db][v] = 0.0f;
-  }
+    for (int v = 0; v < 16; ++v) acc[db][v] = 0.0f;
+  float m_run = -INFINITY, l_part = 0.0f;
 
-  // ---- tile staging: global -> registers -> LDS
-  u32x4 kreg[KLD];
-  u32x4 vreg[4];
-  const int v_run = tid / CH, v_c = tid % CH;  // V item of this thread (if tid < VITEMS)
-  auto load_tile = [&](int kt0) {
+  // ---- tile staging: coalesced 16-byte global loads into one of two register
+  // sets, then swizzled 16-byte LDS stores into one of two LDS buffers.  Tile t+2
+  // is loaded while tile t is computed and tile t+1 is stored, so two tiles of
+  // loads are in flight.  The loop is unrolled by two so each register set is a
+  // fixed set of registers.  Loads are issued unconditionally (keys are clamped to
+  // the last row, so a load past the last tile re-reads valid memory): with the
+  // same number of loads on every path the compiler waits exactly for the older
+  // set.  The barrier between tiles waits for LDS traffic only.
+  u32x4 rk0[KLD], rv0[KLD], rk1[KLD], rv1[KLD];
+  auto load_regs = [&](int kt0, u32x4 (&rk)[KLD], u32x4 (&rv)[KLD]) {
 #pragma unroll
     for (int j = 0; j < KLD; ++j) {
       const int q = tid + j * NT;
       const int row = q / CH, c = q % CH;
-      const int key = min(kt0 + row, nkeys - 1);
-      kreg[j] = reinterpret_cast<const u32x4*>(Kb + (long long)key * D)[c];
-    }
-    if (tid < VITEMS) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int key = min(kt0 + 4 * v_run + e, nkeys - 1);
-        vreg[e] = reinterpret_cast<const u32x4*>(Vb + (long long)key * D)[v_c];
-      }
+      const long long key = min(kt0 + row, nkeys - 1);
+      rk[j] = reinterpret_cast<const u32x4*>(Kb + key * D)[c];
+      rv[j] = reinterpret_cast<const u32x4*>(Vb + key * D)[c];
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_regs = [&](int b, const u32x4 (&rk)[KLD], const u32x4 (&rv)[KLD]) {
 #pragma unroll
     for (int j = 0; j < KLD; ++j) {
       const int q = tid + j * NT;
       const int row = q / CH, c = q % CH;
-      *reinterpret_cast<u32x4*>(&s_k[buf][row * D + ((c ^ (row & 7)) * 8)]) = kreg[j];
-    }
-    if (tid < VITEMS) {
-      // keys 4*v_run .. +3 sit at permuted positions p..p+3 of their 16-key group:
-      // key k of a group goes to 8*((k/4)%2) + 4*(k/8) + k%4 (bits 2 and 3 swapped)
-      const int s4 = v_run & 3;
-      const int pos = 16 * (v_run >> 2) + 8 * (s4 & 1) + 4 * (s4 >> 1);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        const uint32_t lo = __builtin_amdgcn_perm(vreg[1][e >> 1], vreg[0][e >> 1], sel);
-        const uint32_t hi = __builtin_amdgcn_perm(vreg[3][e >> 1], vreg[2][e >> 1], sel);
-        *reinterpret_cast<u32x2*>(&s_vt[buf][(8 * v_c + e) * VTS + pos]) = u32x2{lo, hi};
-      }
+      *reinterpret_cast<u32x4*>(&s_k[b][row * D + ((c ^ kswz(row)) * 8)]) = rk[j];
+      *reinterpret_cast<u32x4*>(&s_v[b][row * D + ((c ^ vswz(row)) * 8)]) = rv[j];
     }
   };
+  auto lds_barrier = []() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(kLgkmOnlyZero);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
 
-  load_tile(k_begin);
-  store_tile(0);
-  __syncthreads();
-  int buf = 0;
-  for (int t = 0; t < n_tiles; ++t) {
-    const int kt0 = k_begin + t * KT;
-    const bool more = t + 1 < n_tiles;
-    if (more) load_tile(kt0 + KT);
+  // a wavefront whose rows are all padding only helps stage the tiles
+  const bool active = row0 + wave * 32 < M;
+  const int tg = lane >> 4, tj = lane & 15;
 
-    const uint16_t* sk = s_k[buf];
-    const uint16_t* svt = s_vt[buf];
+  auto compute_tile = [&](int kt0, const uint16_t* sk, const uint16_t* sv) {
     // S^T = K Q^T for two 32-key blocks
-    f32x16 s[RB][2];
+    f32x16 s[2];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) s[rb][kb][v] = 0.0f;
+      for (int v = 0; v < 16; ++v) s[kb][v] = 0.0f;
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const int krow = 32 * kb + l32;
         const int c = h * KSTEPS + kk;
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sk[krow * D + ((c ^ (krow & 7)) * 8)]);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-          s[rb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[rb][kk], s[rb][kb], 0, 0, 0);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sk[krow * D + ((c ^ kswz(krow)) * 8)]);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[kb], 0, 0, 0);
       }
     }
-
-    // tree mask (only tiles that reach past the prefix) and online softmax
-    const bool tail = kt0 + KT > P;
-    bf16x8 pt[RB][4];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      if (tail) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int key = kt0 + 32 * kb + 8 * (v >> 2) + 4 * h + (v & 3);
-            const bool vis = key < P || (key < nkeys && ((mrow[rb] >> (key - P)) & 1ull));
-            if (!vis) s[rb][kb][v] = -INFINITY;
-          }
-      }
-      float mx = s[rb][0][0];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[rb][kb][v]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float tmax = mx * sl2;
-      const bool need = tmax > m_run[rb] + kSlack;
-      if (__ballot(need)) {
-        const float alpha = need ? __builtin_amdgcn_exp2f(m_run[rb] - tmax) : 1.0f;
-        if (need) m_run[rb] = tmax;
-        l_part[rb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) acc[rb][db][v] *= alpha;
-      }
-      const float mb = m_run[rb] == -INFINITY ? 0.0f : m_run[rb];
-      float lsum = 0.0f;
+    // tree mask (only tiles that reach past the prefix), branch-free: the lane's
+    // mask row is shifted once so that bit e stands for key kt0 + e
+    if (kt0 + KT > P) {
+      const int sh = kt0 - P;  // key kt0+e is tree node sh+e
+      const unsigned long long mt =
+          sh >= 64 ? 0ull : (sh >= 0 ? (mrow >> sh) : (sh <= -64 ? ~0ull : ((mrow << -sh) | ((1ull << -sh) - 1ull))));
+      const int lim = nkeys - kt0;  // keys of this tile that exist (1..64)
+      const unsigned long long mv = lim >= 64 ? mt : (mt & ((1ull << lim) - 1ull));
+      const unsigned long long mh = mv >> (4 * h);
+      const uint32_t lo = (uint32_t)mh, hi = (uint32_t)(mh >> 32);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[rb][kb][v], sl2, -mb));
-          s[rb][kb][v] = p;
-          lsum += p;
+          const int e = 32 * kb + 8 * (v >> 2) + (v & 3);  // key offset minus 4h
+          const uint32_t word = e < 32 ? lo : hi;
+          s[kb][v] = ((word >> (e & 31)) & 1u) ? s[kb][v] : -INFINITY;
         }
-      l_part[rb] += lsum;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int kb = ks >> 1, o = 8 * (ks & 1);
-        u32x4 w4;
-        w4[0] = pack_bf16(s[rb][kb][o + 0], s[rb][kb][o + 1]);
-        w4[1] = pack_bf16(s[rb][kb][o + 2], s[rb][kb][o + 3]);
-        w4[2] = pack_bf16(s[rb][kb][o + 4], s[rb][kb][o + 5]);
-        w4[3] = pack_bf16(s[rb][kb][o + 6], s[rb][kb][o + 7]);
-        pt[rb][ks] = as_bf16x8(w4);
-      }
     }
-
-    // O^T += V^T P^T
+    float mx = s[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float tmax = mx * sl2;
+    const bool need = tmax > m_run + kSlack;
+    if (__ballot(need)) {
+      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - tmax) : 1.0f;
+      if (need) m_run = tmax;
+      l_part *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[db][v] *= alpha;
+    }
+    const float mb = m_run == -INFINITY ? 0.0f : m_run;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s[kb][v] = __builtin_amdgcn_exp2f(fmaf(s[kb][v], sl2, -mb));
+    // P is rounded to bf16 for the PV product; the row sum adds exactly those
+    // rounded values, two per v_dot2 (bf16 pair . (1, 1) + acc in fp32)
+    bf16x8 pt[4];
+    float lsum = l_part;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int kb = ks >> 1, o = 8 * (ks & 1);
+      u32x4 w4;
+      w4[0] = pack_bf16(s[kb][o + 0], s[kb][o + 1]);
+      w4[1] = pack_bf16(s[kb][o + 2], s[kb][o + 3]);
+      w4[2] = pack_bf16(s[kb][o + 4], s[kb][o + 5]);
+      w4[3] = pack_bf16(s[kb][o + 6], s[kb][o + 7]);
+      pt[ks] = as_bf16x8(w4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) lsum = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w4[e]), kOnes2, lsum, false);
+    }
+    l_part = lsum;
+    // O^T += V^T P^T.  The A operand (32 d x 16 keys) comes from the row-major V
+    // tile through two transpose reads: in each 16-lane group, lane i receives
+    // element i%4 of the 8-byte pieces addressed by lanes i/4, i/4+4, i/4+8,
+    // i/4+12, so lane j of the group addresses key row base+j/4, columns
+    // 4*(j%4)..+3 of its 16-column slice and gets 4 consecutive keys of one d
+    // column.  Keys 16ks+8hr+4h+0..3 (hr = 0, 1) are exactly the runs the S^T
+    // accumulator holds for this lane, so P^T needs no shuffling.
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&svt[(32 * db + l32) * VTS + 16 * ks + 8 * h]);
+        bf16x4 half[2];
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-          acc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pt[rb][ks], acc[rb][db], 0, 0, 0);
+        for (int hr = 0; hr < 2; ++hr) {
+          const int row = 16 * ks + 8 * hr + 4 * (tg >> 1) + (tj >> 2);
+          const int col = 32 * db + 16 * (tg & 1) + 4 * (tj & 3);
+          half[hr] = ds_read_tr16(&sv[row * D + (((col >> 3) ^ vswz(row)) * 8) + (col & 7)]);
+        }
+        const bf16x8 a = __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7);
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pt[ks], acc[db], 0, 0, 0);
       }
     }
+  };
 
-    if (more) store_tile(buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
+  load_regs(k_begin, rk0, rv0);
+  load_regs(k_begin + KT, rk1, rv1);
+  store_regs(0, rk0, rv0);
+  lds_barrier();
+  auto tile_step = [&](int t, int buf, u32x4 (&rk_this)[KLD], u32x4 (&rv_this)[KLD],
+                       const u32x4 (&rk_next)[KLD], const u32x4 (&rv_next)[KLD]) {
+    const int kt0 = k_begin + t * KT;
+    load_regs(kt0 + 2 * KT, rk_this, rv_this);
+    if (active) compute_tile(kt0, s_k[buf], s_v[buf]);
+    if (t + 1 < n_tiles) store_regs(buf ^ 1, rk_next, rv_next);
+    lds_barrier();
+  };
+  for (int t = 0; t < n_tiles; t += 2) {
+    tile_step(t, 0, rk0, rv0, rk1, rv1);
+    if (t + 1 < n_tiles) tile_step(t + 1, 1, rk1, rv1, rk0, rv0);
   }
 
   // ---- epilogue
+  const float l_tot = l_part + __shfl_xor(l_part, 32, 64);
+  if (r >= M) return;
+  if (n_split == 1) {
+    const int i = r / rep, head = g * rep + r % rep;
+    uint16_t* op = O + (((long long)b * T_max + i) * Hq + head) * D;
+    const float inv = 1.0f / l_tot;
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const float l_tot = l_part[rb] + __shfl_xor(l_part[rb], 32, 64);
-    const int r = row0 + (wave * RB + rb) * 32 + l32;
-    if (r >= M) continue;
-    if (n_split == 1) {
-      const int i = r / rep, head = g * rep + r % rep;
-      uint16_t* op = O + (((long long)b * T_max + i) * Hq + head) * D;
-      const float inv = 1.0f / l_tot;
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int v4 = 0; v4 < 4; ++v4) {
-          const int d0 = 32 * db + 8 * v4 + 4 * h;
-          u32x2 w2;
-          w2[0] = pack_bf16(acc[rb][db][4 * v4 + 0] * inv, acc[rb][db][4 * v4 + 1] * inv);
-          w2[1] = pack_bf16(acc[rb][db][4 * v4 + 2] * inv, acc[rb][db][4 * v4 + 3] * inv);
-          *reinterpret_cast<u32x2*>(op + d0) = w2;
-        }
-    } else {
-      const long long prow = ((long long)bg * n_split + split) * m_pad + r;
-      float* wp = ws_o + prow * D;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int v4 = 0; v4 < 4; ++v4) {
-          const int d0 = 32 * db + 8 * v4 + 4 * h;
-          *reinterpret_cast<f32x4*>(wp + d0) =
-              f32x4{acc[rb][db][4 * v4 + 0], acc[rb][db][4 * v4 + 1], acc[rb][db][4 * v4 + 2], acc[rb][db][4 * v4 + 3]};
-        }
-      if (h == 0) {
-        ws_ml[2 * prow] = m_run[rb];
-        ws_ml[2 * prow + 1] = l_tot;
+      for (int v4 = 0; v4 < 4; ++v4) {
+        const int d0 = 32 * db + 8 * v4 + 4 * h;
+        u32x2 w2;
+        w2[0] = pack_bf16(acc[db][4 * v4 + 0] * inv, acc[db][4 * v4 + 1] * inv);
+        w2[1] = pack_bf16(acc[db][4 * v4 + 2] * inv, acc[db][4 * v4 + 3] * inv);
+        *reinterpret_cast<u32x2*>(op + d0) = w2;
       }
+  } else {
+    const long long prow = ((long long)bg * n_split + split) * m_pad + r;
+    float* wp = ws_o + prow * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4) {
+        const int d0 = 32 * db + 8 * v4 + 4 * h;
+        *reinterpret_cast<f32x4*>(wp + d0) =
+            f32x4{acc[db][4 * v4 + 0], acc[db][4 * v4 + 1], acc[db][4 * v4 + 2], acc[db][4 * v4 + 3]};
+      }
+    if (h == 0) {
+      ws_ml[2 * prow] = m_run;
+      ws_ml[2 * prow + 1] = l_tot;
     }
   }
 }

@@ -33,8 +33,68 @@ struct Branching {
   int w[kMaxLevels];
 };
 
+// Workspace layout (rows = B * rows_per_req): each (row, chunk) workgroup of K1
+// writes its sorted top-K rank keys and a bad-value flag; K2 merges the chunks.
+struct BuildWs {
+  unsigned long long* chunk_keys;  // [rows][n_chunks][K]
+  int* chunk_bad;                  // [rows][n_chunks]
+  int n_chunks;
+};
+
+__host__ __device__ inline size_t build_ws_bytes(long long rows, int K) {
+  return (size_t)rows * ((size_t)kMaxChunks * K * 8 + kMaxChunks * 4) + 256;
+}
+
+__host__ __device__ inline BuildWs build_ws(void* base, long long rows, int K, int n_chunks) {
+  BuildWs w;
+  unsigned char* p = reinterpret_cast<unsigned char*>(base);
+  w.chunk_keys = reinterpret_cast<unsigned long long*>(p);
+  p += (size_t)rows * n_chunks * K * 8;
+  w.chunk_bad = reinterpret_cast<int*>(p);
+  w.n_chunks = n_chunks;
+  return w;
+}
+
+// Merge the n_chunks sorted chunk lists of every row of request b into the row's
+// top-K rank keys, written to s_key[row*K + r] (r = rank in the row).  A group of
+// n_chunks lanes (power of two <= 8) handles a row: each lane holds one chunk's
+// list in registers and K rounds of a group argmax pop the winners.
+__device__ void merge_rows(const BuildWs& ws, long long row_base, int R, int K, unsigned long long* s_key,
+                           int* s_bad) {
+  const int tid = threadIdx.x;
+  const int G = ws.n_chunks;
+  const int rows_per_pass = kSelectThreads / G;
+  for (int row0 = 0; row0 < R; row0 += rows_per_pass) {
+    const int row = row0 + tid / G;
+    const int c = tid % G;
+    unsigned long long l[kKMax];
+#pragma unroll
+    for (int i = 0; i < kKMax; ++i) l[i] = 0ull;
+    if (row < R) {
+      const unsigned long long* src = ws.chunk_keys + ((row_base + row) * G + c) * K;
+#pragma unroll
+      for (int i = 0; i < kKMax; ++i)
+        if (i < K) l[i] = src[i];
+      if (ws.chunk_bad[(row_base + row) * G + c]) *s_bad = 1;
+    }
+    for (int k = 0; k < K; ++k) {
+      unsigned long long best = l[0];
+      for (int m = 1; m < G; m <<= 1) {
+        const unsigned long long o = shfl_xor_u64(best, m);
+        best = o > best ? o : best;
+      }
+      if (row < R && c == 0) s_key[row * K + k] = best;
+      if (l[0] == best) {
+#pragma unroll
+        for (int i = 0; i < kKMax - 1; ++i) l[i] = l[i + 1];
+        l[kKMax - 1] = 0ull;
+      }
+    }
+  }
+}
+
 // --------------------------------------------------------------------------
-// K1: per-(row, chunk) top-K.
+// K1: per-(row, chunk) top-K, then the row's top-K by the last chunk to finish.
 // --------------------------------------------------------------------------
 template <int K>
 __device__ __forceinline__ void list_insert(uint32_t (&lv)[K], uint32_t (&li)[K], uint32_t key, uint32_t idx) {
@@ -53,16 +113,31 @@ __device__ __forceinline__ void list_insert(uint32_t (&lv)[K], uint32_t (&li)[K]
   }
 }
 
+// Rank-count selection inside one wavefront: n (<= 128) unique non-zero keys in
+// LDS (zeros pad), the K largest are written in order to out[0..K).
+__device__ __forceinline__ void wave_select_sorted(const unsigned long long* keys, int n, int K,
+                                                   unsigned long long* out, int lane) {
+  for (int e = lane; e < K; e += 64) out[e] = 0ull;
+  __builtin_amdgcn_wave_barrier();
+  for (int e = lane; e < n; e += 64) {
+    const unsigned long long my = keys[e];
+    if (my == 0ull) continue;
+    int rank = 0;
+    for (int o = 0; o < n; ++o) rank += keys[o] > my;
+    if (rank < K) out[rank] = my;
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
 template <int K>
 __global__ __launch_bounds__(kTopkThreads) void k_row_topk(const float* __restrict__ lp, int V, int chunk_len,
-                                                           unsigned long long* __restrict__ out_keys,
-                                                           int* __restrict__ out_bad, int vec4) {
+                                                           int vec4, BuildWs ws) {
   const int chunk = blockIdx.x, n_chunks = gridDim.x;
   const long long row = blockIdx.y;
   const float* r = lp + row * (long long)V;
   const int begin = chunk * chunk_len;
   const int end = min(V, begin + chunk_len);
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
   uint32_t lv[K], li[K];
 #pragma unroll
@@ -76,7 +151,6 @@ __global__ __launch_bounds__(kTopkThreads) void k_row_topk(const float* __restri
     const uint32_t key = order_key(v);
     if (key > lv[K - 1]) list_insert<K>(lv, li, key, (uint32_t)idx);
   };
-
   if (vec4) {
     // 16-byte loads (V % 4 == 0 and a 16-byte aligned base; chunk_len is a
     // multiple of 4, so every float4 is aligned).
@@ -93,24 +167,13 @@ __global__ __launch_bounds__(kTopkThreads) void k_row_topk(const float* __restri
     for (int e = begin + tid; e < end; e += kTopkThreads) consider(r[e], e);
   }
 
-  // Merge the per-thread lists: K rounds of a workgroup argmax over list heads.
-  __shared__ unsigned long long s_best[kTopkThreads / 64];
-  __shared__ int s_bad;
-  if (tid == 0) s_bad = 0;
-  __syncthreads();
-  if (bad) s_bad = 1;
-  const int lane = tid & 63, wave = tid >> 6;
-  unsigned long long* dst = out_keys + (row * n_chunks + chunk) * K;
+  // wavefront merge without barriers: K rounds of a wave argmax over list heads,
+  // the round-k winner is kept by lane k
+  unsigned long long mine = 0ull;
   for (int k = 0; k < K; ++k) {
     const unsigned long long head = lv[0] ? (((unsigned long long)lv[0] << 32) | (0xFFFFFFFFu - li[0])) : 0ull;
-    unsigned long long m = wave_max_u64(head);
-    if (lane == 0) s_best[wave] = m;
-    __syncthreads();
-    unsigned long long best = s_best[0];
-#pragma unroll
-    for (int w = 1; w < kTopkThreads / 64; ++w) best = s_best[w] > best ? s_best[w] : best;
+    const unsigned long long best = wave_max_u64(head);
     if (head == best && head != 0ull) {
-      // pop the head of the winning list
 #pragma unroll
       for (int i = 0; i < K - 1; ++i) {
         lv[i] = lv[i + 1];
@@ -119,56 +182,25 @@ __global__ __launch_bounds__(kTopkThreads) void k_row_topk(const float* __restri
       lv[K - 1] = 0u;
       li[K - 1] = 0xFFFFFFFFu;
     }
-    if (tid == 0) dst[k] = best;
-    __syncthreads();
+    if (lane == k) mine = best;
   }
-  if (tid == 0) out_bad[row * n_chunks + chunk] = s_bad;
+  __shared__ unsigned long long s_w[4 * kKMax];
+  __shared__ unsigned long long s_out[kKMax];
+  __shared__ int s_bad;
+  if (tid == 0) s_bad = 0;
+  __syncthreads();
+  if (lane < K) s_w[wave * K + lane] = mine;
+  if (__ballot(bad) && lane == 0) atomicOr(&s_bad, 1);
+  __syncthreads();
+  if (wave == 0) wave_select_sorted(s_w, 4 * K, K, s_out, lane);
+  __syncthreads();
+  if (tid < K) ws.chunk_keys[(row * n_chunks + chunk) * K + tid] = s_out[tid];
+  if (tid == 0) ws.chunk_bad[row * n_chunks + chunk] = s_bad;
 }
 
 // --------------------------------------------------------------------------
 // K2 helpers
 // --------------------------------------------------------------------------
-// Merge the n_chunks sorted chunk lists of every row into the row's top-K
-// (token, log-prob), written to s_tok / s_val at [row*K + r].
-__device__ void merge_rows(const unsigned long long* __restrict__ keys, const int* __restrict__ badf, int R,
-                           int K, int n_chunks, int* s_tok, float* s_val, int* s_bad) {
-  const int tid = threadIdx.x;
-  const int G = n_chunks;                 // lanes per row (power of two <= 8)
-  const int rows_per_pass = kSelectThreads / G;
-  for (int row0 = 0; row0 < R; row0 += rows_per_pass) {
-    const int row = row0 + tid / G;
-    const int c = tid % G;
-    unsigned long long l[kKMax];
-#pragma unroll
-    for (int i = 0; i < kKMax; ++i) l[i] = 0ull;
-    if (row < R) {
-      const unsigned long long* src = keys + ((long long)row * n_chunks + c) * K;
-#pragma unroll
-      for (int i = 0; i < kKMax; ++i)
-        if (i < K) l[i] = src[i];
-      if (badf[row * n_chunks + c]) *s_bad = 1;
-    }
-    for (int k = 0; k < K; ++k) {
-      unsigned long long best = l[0];
-      for (int m = 1; m < G; m <<= 1) {
-        unsigned long long o = shfl_xor_u64(best, m);
-        best = o > best ? o : best;
-      }
-      if (row < R) {
-        if (c == 0) {
-          s_tok[row * K + k] = (int)key_index(best);
-          s_val[row * K + k] = key_value(best);
-        }
-        if (l[0] == best) {
-#pragma unroll
-          for (int i = 0; i < kKMax - 1; ++i) l[i] = l[i + 1];
-          l[kKMax - 1] = 0ull;
-        }
-      }
-    }
-  }
-}
-
 // Block-wide exclusive scan of one int per thread; returns the exclusive prefix
 // and writes the total to *total.
 __device__ int block_excl_scan(int v, int* s_tmp, int* total) {
@@ -191,15 +223,44 @@ __device__ int block_excl_scan(int v, int* s_tmp, int* total) {
   return base + x - v;
 }
 
-// Radix select: threshold tau such that exactly n of the C unique keys are >= tau.
+__device__ unsigned long long block_reduce_u64(unsigned long long v, bool take_max, unsigned long long* s_tmp) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const unsigned long long o = shfl_xor_u64(v, m);
+    v = take_max ? (o > v ? o : v) : (o < v ? o : v);
+  }
+  if (lane == 0) s_tmp[wave] = v;
+  __syncthreads();
+  v = s_tmp[0];
+  for (int w = 1; w < kSelectThreads / 64; ++w) v = take_max ? (s_tmp[w] > v ? s_tmp[w] : v) : (s_tmp[w] < v ? s_tmp[w] : v);
+  __syncthreads();
+  return v;
+}
+
+// Radix select: threshold tau such that exactly n of the C unique keys
+// rank_key(s_sc[id], id) are >= tau.  Digits of 8 bits, starting at the first
+// byte where the largest and smallest key differ.
 __device__ unsigned long long radix_select_threshold(const int C, const int n, const float* s_sc, int* s_hist,
-                                                     unsigned long long* s_bcast) {
+                                                     unsigned long long* s_bcast, unsigned long long* s_tmp) {
   const int tid = threadIdx.x;
-  if (n <= 0) return ~0ull;  // nothing: no key is >= all-ones (keys never reach it)
+  if (n <= 0) return ~0ull;  // nothing: no key reaches all-ones
   if (n >= C) return 0ull;
-  unsigned long long prefix = 0ull, mask = 0ull;
+  unsigned long long kmax = 0ull, kmin = ~0ull;
+  for (int id = tid; id < C; id += kSelectThreads) {
+    const unsigned long long k = rank_key(s_sc[id], (uint32_t)id);
+    kmax = k > kmax ? k : kmax;
+    kmin = k < kmin ? k : kmin;
+  }
+  kmax = block_reduce_u64(kmax, true, s_tmp);
+  kmin = block_reduce_u64(kmin, false, s_tmp);
+  int shift = 56;
+  while (shift > 0 && ((kmax ^ kmin) >> shift) == 0ull) shift -= 8;
+  // bytes above `shift` are common to every key: they form the starting prefix
+  unsigned long long mask = shift == 56 ? 0ull : ~((1ull << (shift + 8)) - 1ull);
+  unsigned long long prefix = kmax & mask;
   int need = n;
-  for (int shift = 56; shift >= 0; shift -= 8) {
+  for (; shift >= 0; shift -= 8) {
     for (int i = tid; i < 256; i += kSelectThreads) s_hist[i] = 0;
     __syncthreads();
     for (int id = tid; id < C; id += kSelectThreads) {
@@ -244,20 +305,20 @@ __device__ unsigned long long radix_select_threshold(const int C, const int n, c
 }
 
 __global__ __launch_bounds__(kSelectThreads) void k_tree_select_dynamic(
-    const unsigned long long* __restrict__ keys, const int* __restrict__ badf, int R, int K, int D,
-    int total_tokens, int n_chunks, const int* __restrict__ root_token, int T_max, int* __restrict__ draft_tokens,
-    int* __restrict__ parents, int* __restrict__ tree_size, float* __restrict__ node_score,
-    int* __restrict__ status) {
+    BuildWs ws, int R, int K, int D, int total_tokens, const int* __restrict__ root_token, int T_max,
+    int* __restrict__ draft_tokens, int* __restrict__ parents, int* __restrict__ tree_size,
+    float* __restrict__ node_score, int* __restrict__ status) {
   extern __shared__ unsigned char smem[];
   const int C = R * K;  // = K + D*K*K: candidate id == row*K + rank
-  int* s_tok = reinterpret_cast<int*>(smem);
-  float* s_sc = reinterpret_cast<float*>(s_tok + C);
-  int* s_par = reinterpret_cast<int*>(s_sc + C);
-  int* s_node = s_par + C;
+  unsigned long long* s_key = reinterpret_cast<unsigned long long*>(smem);
+  float* s_sc = reinterpret_cast<float*>(s_key + C);
+  short* s_par = reinterpret_cast<short*>(s_sc + C);
+  short* s_node = s_par + C;
   __shared__ int s_hist[256];
-  __shared__ unsigned long long s_bcast[4];
+  __shared__ unsigned long long s_bcast[4], s_tmp64[kSelectThreads / 64];
   __shared__ int s_front[2][kKMax];
   __shared__ float s_fsc[2][kKMax];
+  __shared__ unsigned long long s_lkey[256];
   __shared__ int s_rank[256];
   __shared__ int s_tmp[kSelectThreads / 64];
   __shared__ int s_bad;
@@ -265,51 +326,64 @@ __global__ __launch_bounds__(kSelectThreads) void k_tree_select_dynamic(
   const int b = blockIdx.x, tid = threadIdx.x;
   if (tid == 0) s_bad = 0;
   __syncthreads();
-  merge_rows(keys + (long long)b * R * n_chunks * K, badf + (long long)b * R * n_chunks, R, K, n_chunks, s_tok,
-             s_sc, &s_bad);
-  for (int id = tid; id < C; id += kSelectThreads) s_par[id] = -1;
-  if (tid < K) {
-    s_front[0][tid] = tid;
-    s_fsc[0][tid] = 0.0f;
+  merge_rows(ws, (long long)b * R, R, K, s_key, &s_bad);
+  __syncthreads();
+  for (int id = tid; id < C; id += kSelectThreads) {
+    s_sc[id] = key_value(s_key[id]);
+    s_par[id] = -1;
   }
   __syncthreads();
-  if (tid < K) s_fsc[0][tid] = s_sc[tid];
+  if (tid < K) {
+    s_front[0][tid] = tid;
+    s_fsc[0][tid] = s_sc[tid];
+  }
   __syncthreads();
 
-  // D dependent rounds of K*K cumulative scores and a frontier top-K.
+  // D dependent rounds of K*K cumulative scores and a frontier top-K
   const int KK = K * K;
+  const int split = KK <= 64 ? 4 : (KK <= 128 ? 2 : 1);
   for (int l = 1; l <= D; ++l) {
     const int cur = (l - 1) & 1, nxt = l & 1;
     const int base = K + (l - 1) * KK;
     for (int q = tid; q < KK; q += kSelectThreads) {
       const int j = q / K;
-      s_sc[base + q] = __fadd_rn(s_sc[base + q], s_fsc[cur][j]);
-      s_par[base + q] = s_front[cur][j];
+      const float sc = __fadd_rn(s_sc[base + q], s_fsc[cur][j]);
+      s_sc[base + q] = sc;
+      s_par[base + q] = (short)s_front[cur][j];
+      s_lkey[q] = rank_key(sc, (uint32_t)q);
       s_rank[q] = 0;
     }
     __syncthreads();
-    // rank by counting (two threads per candidate when K*K <= 128)
-    const int split = KK <= kSelectThreads / 2 ? 2 : 1;
     for (int t = tid; t < KK * split; t += kSelectThreads) {
       const int q = t % KK, part = t / KK;
-      const unsigned long long mine = rank_key(s_sc[base + q], (uint32_t)q);
+      const unsigned long long mine = s_lkey[q];
+      const int o0 = part * (KK / split), o1 = part == split - 1 ? KK : o0 + KK / split;
       int cnt = 0;
-      for (int o = part; o < KK; o += split) cnt += rank_key(s_sc[base + o], (uint32_t)o) > mine;
-      atomicAdd(&s_rank[q], cnt);
+      int o = o0;
+      for (; o + 8 <= o1; o += 8) {  // eight LDS reads in flight
+        unsigned long long x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = s_lkey[o + u];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) cnt += x[u] > mine;
+      }
+      for (; o < o1; ++o) cnt += s_lkey[o] > mine;
+      if (split == 1) s_rank[q] = cnt;
+      else atomicAdd(&s_rank[q], cnt);
     }
     __syncthreads();
     for (int q = tid; q < KK; q += kSelectThreads) {
-      const int rk = s_rank[q];
-      if (rk < K) {
-        s_front[nxt][rk] = base + q;
-        s_fsc[nxt][rk] = s_sc[base + q];
+      const int rk2 = s_rank[q];
+      if (rk2 < K) {
+        s_front[nxt][rk2] = base + q;
+        s_fsc[nxt][rk2] = s_sc[base + q];
       }
     }
     __syncthreads();
   }
 
-  // Final: keep the total_tokens best candidates, number them by ascending id.
-  const unsigned long long tau = radix_select_threshold(C, total_tokens, s_sc, s_hist, s_bcast);
+  // final: keep the total_tokens best candidates, number them by ascending id
+  const unsigned long long tau = radix_select_threshold(C, total_tokens, s_sc, s_hist, s_bcast, s_tmp64);
   const int per = (C + kSelectThreads - 1) / kSelectThreads;
   const int lo = min(C, tid * per), hi = min(C, lo + per);
   int cnt = 0;
@@ -318,7 +392,7 @@ __global__ __launch_bounds__(kSelectThreads) void k_tree_select_dynamic(
   int node = 1 + block_excl_scan(cnt, s_tmp, &total);
   for (int id = lo; id < hi; ++id) {
     const bool keep = rank_key(s_sc[id], (uint32_t)id) >= tau;
-    s_node[id] = keep ? node++ : -1;
+    s_node[id] = keep ? (short)node++ : (short)-1;
   }
   __syncthreads();
   // closure check: a kept node's parent must be kept
@@ -329,17 +403,18 @@ __global__ __launch_bounds__(kSelectThreads) void k_tree_select_dynamic(
   const long long ob = (long long)b * T_max;
   const bool ok = s_bad == 0;
   const int T = ok ? total + 1 : 1;
-  for (int i = tid; i < T_max; i += kSelectThreads) {
-    draft_tokens[ob + i] = i == 0 ? root_token[b] : -1;
-    parents[ob + i] = -1;
-    if (node_score) node_score[ob + i] = i == 0 ? 0.0f : -INFINITY;
-  }
-  __syncthreads();
+  // the root and the padding; kept nodes 1..T-1 are written from their candidates
+  for (int i = tid; i < T_max; i += kSelectThreads)
+    if (i == 0 || i >= T) {
+      draft_tokens[ob + i] = i == 0 ? root_token[b] : -1;
+      parents[ob + i] = -1;
+      if (node_score) node_score[ob + i] = i == 0 ? 0.0f : -INFINITY;
+    }
   if (ok) {
     for (int id = tid; id < C; id += kSelectThreads) {
       const int n = s_node[id];
       if (n > 0) {
-        draft_tokens[ob + n] = s_tok[id];
+        draft_tokens[ob + n] = (int)key_index(s_key[id]);
         parents[ob + n] = s_par[id] < 0 ? 0 : s_node[s_par[id]];
         if (node_score) node_score[ob + n] = s_sc[id];
       }
@@ -352,23 +427,18 @@ __global__ __launch_bounds__(kSelectThreads) void k_tree_select_dynamic(
 }
 
 __global__ __launch_bounds__(kSelectThreads) void k_tree_select_static(
-    const unsigned long long* __restrict__ keys, const int* __restrict__ badf, int R, int K, int n_chunks,
-    Branching br, const int* __restrict__ root_token, int T_max, int* __restrict__ draft_tokens,
-    int* __restrict__ parents, int* __restrict__ tree_size, float* __restrict__ node_score,
-    int* __restrict__ status) {
+    BuildWs ws, int R, int K, Branching br, const int* __restrict__ root_token, int T_max,
+    int* __restrict__ draft_tokens, int* __restrict__ parents, int* __restrict__ tree_size,
+    float* __restrict__ node_score, int* __restrict__ status) {
   extern __shared__ unsigned char smem[];
-  const int C = R * K;
-  int* s_tok = reinterpret_cast<int*>(smem);
-  float* s_val = reinterpret_cast<float*>(s_tok + C);
-  __shared__ int s_bad;
+  unsigned long long* rk = reinterpret_cast<unsigned long long*>(smem);
   __shared__ int t_tok[kTMaxLimit], t_par[kTMaxLimit];
   __shared__ float t_sc[kTMaxLimit];
-  __shared__ int s_T;
+  __shared__ int s_T, s_bad;
   const int b = blockIdx.x, tid = threadIdx.x;
   if (tid == 0) s_bad = 0;
   __syncthreads();
-  merge_rows(keys + (long long)b * R * n_chunks * K, badf + (long long)b * R * n_chunks, R, K, n_chunks, s_tok,
-             s_val, &s_bad);
+  merge_rows(ws, (long long)b * R, R, K, rk, &s_bad);
   __syncthreads();
   if (tid == 0) {
     // level by level: every frontier node, in order, appends its row's top-w
@@ -381,9 +451,10 @@ __global__ __launch_bounds__(kSelectThreads) void k_tree_select_static(
       const int w = br.w[l];
       for (int nd = fs; nd < fe; ++nd)
         for (int r = 0; r < w; ++r) {
-          t_tok[T] = s_tok[nd * K + r];
+          const unsigned long long k = rk[nd * K + r];
+          t_tok[T] = (int)key_index(k);
           t_par[T] = nd;
-          t_sc[T] = __fadd_rn(s_val[nd * K + r], t_sc[nd]);
+          t_sc[T] = __fadd_rn(key_value(k), t_sc[nd]);
           ++T;
         }
       fs = fe;
@@ -414,17 +485,16 @@ int pick_chunks(long long rows_total, int V, int K) {
 }
 
 template <int K>
-void launch_topk(dim3 grid, const float* lp, int V, int chunk_len, unsigned long long* keys, int* bad, int vec4,
-                 hipStream_t s) {
-  hipLaunchKernelGGL(k_row_topk<K>, grid, dim3(kTopkThreads), 0, s, lp, V, chunk_len, keys, bad, vec4);
+void launch_topk(dim3 grid, const float* lp, int V, int chunk_len, int vec4, BuildWs ws, hipStream_t s) {
+  hipLaunchKernelGGL(k_row_topk<K>, grid, dim3(kTopkThreads), 0, s, lp, V, chunk_len, vec4, ws);
 }
 
-void launch_topk_any(int K, dim3 grid, const float* lp, int V, int chunk_len, unsigned long long* keys, int* bad,
-                     int vec4, hipStream_t s) {
+void launch_topk_any(int K, dim3 grid, const float* lp, int V, int chunk_len, int vec4, BuildWs ws,
+                     hipStream_t s) {
   switch (K) {
 #define TV_TOPK_CASE(k) \
   case k:               \
-    launch_topk<k>(grid, lp, V, chunk_len, keys, bad, vec4, s); break;
+    launch_topk<k>(grid, lp, V, chunk_len, vec4, ws, s); break;
     TV_TOPK_CASE(1) TV_TOPK_CASE(2) TV_TOPK_CASE(3) TV_TOPK_CASE(4) TV_TOPK_CASE(5) TV_TOPK_CASE(6)
     TV_TOPK_CASE(7) TV_TOPK_CASE(8) TV_TOPK_CASE(9) TV_TOPK_CASE(10) TV_TOPK_CASE(11) TV_TOPK_CASE(12)
     TV_TOPK_CASE(13) TV_TOPK_CASE(14) TV_TOPK_CASE(15) TV_TOPK_CASE(16)
@@ -440,9 +510,7 @@ extern "C" size_t tree_build_workspace_bytes(int mode, int B, int V, int K, int 
   (void)mode;
   (void)V;
   if (B <= 0 || K <= 0 || rows_per_req <= 0) return 0;
-  const long long rows = (long long)B * rows_per_req;
-  const long long per_row = tv::kMaxChunks * ((long long)K * 8 + 4);
-  return (size_t)(rows * per_row + 256);
+  return tv::build_ws_bytes((long long)B * rows_per_req, K);
 }
 
 extern "C" int tree_build(int mode, int B, int V, int K, int D, int total_tokens, const int* branching,
@@ -491,26 +559,23 @@ extern "C" int tree_build(int mode, int B, int V, int K, int D, int total_tokens
   const int n_chunks = pick_chunks(rows_total, V, K);
   int chunk_len = (V + n_chunks - 1) / n_chunks;
   chunk_len = (chunk_len + 3) & ~3;
-  unsigned long long* keys = reinterpret_cast<unsigned long long*>(workspace);
-  int* bad = reinterpret_cast<int*>(keys + rows_total * n_chunks * K);
+  const BuildWs ws = build_ws(workspace, rows_total, K, n_chunks);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
   dim3 grid(n_chunks, (unsigned)rows_total);
   const int vec4 = (V % 4 == 0) && ((reinterpret_cast<uintptr_t>(logprobs) & 15) == 0);
-  launch_topk_any(K, grid, logprobs, V, chunk_len, keys, bad, vec4, s);
+  launch_topk_any(K, grid, logprobs, V, chunk_len, vec4, ws, s);
   TV_CHECK_LAUNCH();
 
   if (mode == TV_MODE_DYNAMIC) {
     const int C = rows_per_req * K;
     const size_t smem = (size_t)C * 16;
-    hipLaunchKernelGGL(k_tree_select_dynamic, dim3(B), dim3(kSelectThreads), smem, s, keys, bad, rows_per_req, K,
-                       D, total_tokens, n_chunks, root_token, T_max, draft_tokens, parents, tree_size, node_score,
-                       status);
+    hipLaunchKernelGGL(k_tree_select_dynamic, dim3(B), dim3(kSelectThreads), smem, s, ws, rows_per_req, K, D,
+                       total_tokens, root_token, T_max, draft_tokens, parents, tree_size, node_score, status);
   } else {
-    const int C = rows_per_req * K;
-    const size_t smem = (size_t)C * 8;
-    hipLaunchKernelGGL(k_tree_select_static, dim3(B), dim3(kSelectThreads), smem, s, keys, bad, rows_per_req, K,
-                       n_chunks, br, root_token, T_max, draft_tokens, parents, tree_size, node_score, status);
+    const size_t smem = (size_t)rows_per_req * K * 8;
+    hipLaunchKernelGGL(k_tree_select_static, dim3(B), dim3(kSelectThreads), smem, s, ws, rows_per_req, K, br,
+                       root_token, T_max, draft_tokens, parents, tree_size, node_score, status);
   }
   TV_CHECK_LAUNCH();
   return TV_OK;

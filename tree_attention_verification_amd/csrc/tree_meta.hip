@@ -59,13 +59,15 @@ __global__ __launch_bounds__(64) void k_tree_mask_positions(int T_max, int dcap,
                                                             const int* status_in, int* status_out) {
   const int b = blockIdx.x, i = threadIdx.x;
   const long long ob = (long long)b * T_max;
+  // all loads issued together (one memory round trip)
   int st = status_in ? status_in[b] : TV_ST_OK;
   int T = tree_size[b];
   const int P = prefix_len[b];
+  const int p_l = i < T_max ? parents[ob + i] : -1;
   if (st == TV_ST_OK && (T < 1 || T > T_max)) st = TV_ST_SIZE;
   int p = -1;
   if (st == TV_ST_OK) {
-    p = i < T ? parents[ob + i] : -1;
+    p = i < T ? p_l : -1;
     const bool bad = (i == 0) ? (p != -1) : (i < T && !(p >= 0 && p < i));
     if (__ballot(bad)) st = TV_ST_PARENTS;
   }
