@@ -78,11 +78,9 @@ __device__ void merge_rows(const BuildWs& ws, long long row_base, int R, int K, 
       if (ws.chunk_bad[(row_base + row) * G + c]) *s_bad = 1;
     }
     for (int k = 0; k < K; ++k) {
-      unsigned long long best = l[0];
-      for (int m = 1; m < G; m <<= 1) {
-        const unsigned long long o = shfl_xor_u64(best, m);
-        best = o > best ? o : best;
-      }
+      const unsigned long long best = G == 8 ? group_max_u64<8>(l[0])
+                                      : G == 4 ? group_max_u64<4>(l[0])
+                                      : G == 2 ? group_max_u64<2>(l[0]) : l[0];
       if (row < R && c == 0) s_key[row * K + k] = best;
       if (l[0] == best) {
 #pragma unroll
@@ -113,19 +111,17 @@ __device__ __forceinline__ void list_insert(uint32_t (&lv)[K], uint32_t (&li)[K]
   }
 }
 
-// Rank-count selection inside one wavefront: n (<= 128) unique non-zero keys in
-// LDS (zeros pad), the K largest are written in order to out[0..K).
+// Rank-count selection inside one wavefront: n (<= 64) unique non-zero keys in
+// LDS (zeros pad), the K largest are written in order to out[0..K).  Each lane
+// holds one key; the others are broadcast through scalar registers.
 __device__ __forceinline__ void wave_select_sorted(const unsigned long long* keys, int n, int K,
                                                    unsigned long long* out, int lane) {
-  for (int e = lane; e < K; e += 64) out[e] = 0ull;
+  const unsigned long long my = lane < n ? keys[lane] : 0ull;
+  int rank = 0;
+  for (int o = 0; o < n; ++o) rank += readlane_u64(my, o) > my;
+  if (lane < K) out[lane] = 0ull;
   __builtin_amdgcn_wave_barrier();
-  for (int e = lane; e < n; e += 64) {
-    const unsigned long long my = keys[e];
-    if (my == 0ull) continue;
-    int rank = 0;
-    for (int o = 0; o < n; ++o) rank += keys[o] > my;
-    if (rank < K) out[rank] = my;
-  }
+  if (lane < n && my != 0ull && rank < K) out[rank] = my;
   __builtin_amdgcn_wave_barrier();
 }
 
@@ -360,12 +356,12 @@ __global__ __launch_bounds__(kSelectThreads) void k_tree_select_dynamic(
       const int o0 = part * (KK / split), o1 = part == split - 1 ? KK : o0 + KK / split;
       int cnt = 0;
       int o = o0;
-      for (; o + 8 <= o1; o += 8) {  // eight LDS reads in flight
-        unsigned long long x[8];
+      for (; o + 16 <= o1; o += 16) {  // sixteen keys per batch of LDS reads
+        unsigned long long x[16];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) x[u] = s_lkey[o + u];
+        for (int u = 0; u < 16; ++u) x[u] = s_lkey[o + u];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) cnt += x[u] > mine;
+        for (int u = 0; u < 16; ++u) cnt += x[u] > mine;
       }
       for (; o < o1; ++o) cnt += s_lkey[o] > mine;
       if (split == 1) s_rank[q] = cnt;

@@ -46,13 +46,40 @@ __device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v,
   return ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
 }
 
-__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    unsigned long long o = shfl_xor_u64(v, m);
-    v = o > v ? o : v;
-  }
+// DPP lane moves (VALU-rate, no LDS round trip).  Control codes: quad_perm
+// [1,0,3,2] = 0xB1 (lane ^ 1), quad_perm [2,3,0,1] = 0x4E (lane ^ 2),
+// row_half_mirror = 0x141 (lane i <-> 7 - i within 8), row_mirror = 0x140
+// (lane i <-> 15 - i within 16).
+template <int CTRL>
+__device__ __forceinline__ unsigned long long dpp_u64(unsigned long long v) {
+  const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+  return ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+__device__ __forceinline__ unsigned long long umax64(unsigned long long a, unsigned long long b) { return a > b ? a : b; }
+
+// max over aligned groups of G lanes (G = 1, 2, 4, 8, 16); every lane gets its group's max
+template <int G>
+__device__ __forceinline__ unsigned long long group_max_u64(unsigned long long v) {
+  if (G >= 2) v = umax64(v, dpp_u64<0xB1>(v));
+  if (G >= 4) v = umax64(v, dpp_u64<0x4E>(v));
+  if (G >= 8) v = umax64(v, dpp_u64<0x141>(v));
+  if (G >= 16) v = umax64(v, dpp_u64<0x140>(v));
   return v;
+}
+
+__device__ __forceinline__ unsigned long long readlane_u64(unsigned long long v, int lane) {
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, lane);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+// max over the whole wavefront: 16-lane groups by DPP, then the four group maxima
+// combined through scalar registers
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
+  v = group_max_u64<16>(v);
+  return umax64(umax64(readlane_u64(v, 0), readlane_u64(v, 16)), umax64(readlane_u64(v, 32), readlane_u64(v, 48)));
 }
 
 }  // namespace tv
