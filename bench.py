@@ -8,7 +8,12 @@ bf16); --config 1..5 selects another of the five measured workloads.
 
 Inputs are resident in HBM before the timed region.  Input copies are rotated
 (>= --rotate-mb of them) so that repeated steps stream from HBM instead of the
-256 MB last-level cache.  Prints ONE JSON line on stdout; diagnostics go to stderr.
+256 MB last-level cache.  The steps are timed twice: launched eagerly call by call
+(HIP events around every attention call give the kernel's roofline figures), and
+replayed from HIP graphs captured once per input copy (the headline rate; the
+same kernels and arguments, without per-call host launch overhead; --no-graph
+reports the eager rate instead).  Prints ONE JSON line on stdout; diagnostics go
+to stderr.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
 """
@@ -133,6 +138,7 @@ def main():
     ap.add_argument("--rotate-mb", type=float, default=512.0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches only")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (requests or kv heads would be "
@@ -176,6 +182,7 @@ def main():
         step.accept()
         step.compact()
 
+    # eager launches, with HIP events around the attention call of every step
     for k in range(args.warmup):
         one(k)
     torch.cuda.synchronize()
@@ -185,9 +192,39 @@ def main():
     for k in range(args.steps):
         one(args.warmup + k, evs[k])
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    eager_elapsed = time.perf_counter() - t0
     attn_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
-    ms_per_step = elapsed * 1e3 / args.steps
+    ms_per_step_eager = eager_elapsed * 1e3 / args.steps
+
+    # the same steps replayed from captured HIP graphs (one per input copy), the way
+    # a serving loop launches a fixed-shape verification step
+    ms_per_step = ms_per_step_eager
+    launch = "eager"
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for k in range(3):
+                one(k)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graphs = []
+        for c in range(n_copies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                one(c)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for k in range(args.warmup):
+            graphs[k % n_copies].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(args.steps):
+            graphs[(args.warmup + k) % n_copies].replay()
+        torch.cuda.synchronize()
+        ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+        launch = "hip_graph"
+        stream = torch.cuda.current_stream()
 
     # stage breakdown (untimed extra pass, events between every call)
     names = ["tree_build", "tree_mask_positions", "tree_attention", "tree_accept", "kv_compact"]
@@ -228,6 +265,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step_eager": round(ms_per_step_eager, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -236,7 +274,7 @@ def main():
         "config": {"workload": w.name, "batch": w.B, "prefix_len": [int(x) for x in w.prefix_len[:4]] +
                    (["..."] if w.B > 4 else []), "tree_nodes_per_step": nodes, "top_k": w.K, "depth": w.D,
                    "total_tokens": w.total_tokens, "Hq": w.Hq, "Hkv": w.Hkv, "head_dim": w.d, "vocab": w.V,
-                   "input_copies_rotated": n_copies},
+                   "input_copies_rotated": n_copies, "launch": launch},
         "stages_us": stages,
         "roofline": roof,
     }

@@ -170,3 +170,34 @@ def test_prefix_that_does_not_fit_gives_zero_rows():
 def test_vocab_not_multiple_of_four_and_misaligned_rows():
     w = gen.make_custom(cfg_id=903, B=2, mode="dynamic", K=5, D=2, total_tokens=20, V=1001, P=20, d=64)
     run(w)
+
+
+def test_heavy_ties_constant_rows_and_two_vocab_tiles():
+    # row block 0: every entry of every row tied (the row top-K falls back to its
+    # exact bisection); block 1: the 24 best entries of every row are 0.0, so every
+    # candidate of the tree ties and the final selection goes by candidate id;
+    # block 2: the best entries of half the rows lie past the first 32768 entries
+    w = gen.make_custom(cfg_id=904, B=3, mode="dynamic", K=8, D=5, total_tokens=60, V=40000, P=40, d=64)
+    w.logprobs[0, :, :] = np.float32(-np.log(40000.0))
+    w.logprobs[1, :, :24] = 0.0
+    w.logprobs[2, ::2, 33000:33010] = -0.5
+    run(w)
+
+
+def test_large_vocabulary_four_tiles():
+    w = gen.make_custom(cfg_id=905, B=2, mode="dynamic", K=10, D=3, total_tokens=40, V=128256, P=50, d=64)
+    run(w)
+
+
+def test_nan_in_unused_cache_rows_and_query_slots():
+    # rows past each request's keys and query slots past its tree hold NaN: they
+    # may be read (the first key tiles of a split are loaded before the request's
+    # sizes are known) but must never reach the output
+    w = gen.make_custom(cfg_id=906, B=2, P=[2000, 300], mode="given", given_sizes=[40, 5], Hq=8, Hkv=2, d=128)
+    nan_bf16 = np.uint16(0x7FC0)
+    for b in range(w.B):
+        n = int(w.prefix_len[b]) + int(w.given_size[b])
+        w.Kc[b, :, n:, :] = nan_bf16
+        w.Vc[b, :, n:, :] = nan_bf16
+        w.Q[b, int(w.given_size[b]):] = nan_bf16
+    run(w)

@@ -29,8 +29,13 @@
 //   * The tree mask is read once per row (one 64-bit word) and only the tile(s)
 //     reaching past the prefix apply it; no T x T boolean is formed.
 //   * Long key ranges are split across workgroups (split-KV); each split writes
-//     (max, sum, unnormalised output) partials and k_attn_combine merges them
-//     with a log-sum-exp weighting.  Workgroups that share a (request, head,
+//     its running max and row sum (fp32) and its normalised output (fp16, half
+//     the bytes of fp32; the values are bounded by max |v|), and k_attn_combine
+//     merges them with a log-sum-exp weighting.
+//   * The first two K/V tiles, the Q fragments and the mask row are loaded before
+//     the request's tree size and prefix length arrive (keys clamped to the cache
+//     slab, nodes to T_max - 1), so the kernel waits for one memory round trip
+//     instead of two before its first tile; rows past the request are zeroed.  Workgroups that share a (request, head,
 //     split) but hold different row blocks are placed on the same XCD (the
 //     dispatcher assigns workgroups round-robin to the 8 XCDs), so their K/V
 //     tiles are fetched from HBM once and hit the shared L2 afterwards.
@@ -62,16 +67,16 @@ struct Plan {
   int grid;
 };
 
-Plan make_plan(int B, int T_max, int Hq, int Hkv, long long S_cap) {
+Plan plan_with(int B, int T_max, int Hq, int Hkv, long long S_cap, int nw, long long min_keys) {
   Plan p{};
   const int rep = Hq / Hkv;
   const long long m_max = (long long)rep * T_max;
-  p.nw = m_max <= 128 ? 4 : 8;
+  p.nw = nw;
   p.rows_wg = 32 * p.nw;
   p.n_rowblk = (int)((m_max + p.rows_wg - 1) / p.rows_wg);
   const long long base = (long long)B * Hkv * p.n_rowblk;
   const long long target = 512;  // two workgroups per CU
-  long long max_split = (S_cap + 4 * KT - 1) / (4 * KT);  // >= 256 keys per split
+  long long max_split = (S_cap + min_keys - 1) / min_keys;
   if (max_split < 1) max_split = 1;
   long long ns = (target + base - 1) / base;
   if (ns > max_split) ns = max_split;
@@ -84,6 +89,20 @@ Plan make_plan(int B, int T_max, int Hq, int Hkv, long long S_cap) {
   p.m_pad = (long long)p.n_rowblk * p.rows_wg;
   p.n_units = (int)((long long)B * Hkv * ns);
   p.grid = 8 * p.n_rowblk * ((p.n_units + 7) / 8);
+  return p;
+}
+
+// Launch shape: 8-wavefront workgroups (two per SIMD, so one wavefront's softmax
+// overlaps the other's MFMAs) with splits of >= 256 keys, aiming at 512
+// workgroups.  When that leaves most of the chip idle (a single request: 8 kv
+// heads x ~9 splits = 72 workgroups), 4-wavefront workgroups with >= 192-key
+// splits spread the same work over more than twice as many CUs (measured on
+// MI355X: 17.9 vs 21.7 us for 61 nodes x 32 heads over a 2048-token prefix).
+Plan make_plan(int B, int T_max, int Hq, int Hkv, long long S_cap) {
+  const long long m_max = (long long)(Hq / Hkv) * T_max;
+  if (m_max <= 128) return plan_with(B, T_max, Hq, Hkv, S_cap, 4, 4 * KT);
+  const Plan p = plan_with(B, T_max, Hq, Hkv, S_cap, 8, 4 * KT);
+  if (p.grid < 128) return plan_with(B, T_max, Hq, Hkv, S_cap, 4, 3 * KT);
   return p;
 }
 
@@ -114,7 +133,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_attn_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Kc, const uint16_t* __restrict__ Vc,
     long long S_cap, const int* __restrict__ prefix_len, const int* __restrict__ tree_size,
     const uint32_t* __restrict__ tree_mask, const int* __restrict__ status, int T_max, int Hq, int Hkv, int W,
-    float sl2, uint16_t* __restrict__ O, float* __restrict__ ws_o, float* __restrict__ ws_ml, int n_split,
+    float sl2, uint16_t* __restrict__ O, _Float16* __restrict__ ws_o, float* __restrict__ ws_ml, int n_split,
     int chunk_keys, int n_rowblk, int n_units, long long m_pad) {
   constexpr int NT = NW * 64;
   constexpr int KSTEPS = D / 16;     // 16-wide k-steps of QK^T (KSTEPS/2 per half of d)
@@ -143,20 +162,55 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_attn_bf16(
   const int rep = Hq / Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
+  const int row0 = rbk * NW * 32;
+  const int k_begin = split * chunk_keys;
+
+  const uint16_t* Kb = Kc + ((long long)b * Hkv + g) * S_cap * D;
+  const uint16_t* Vb = Vc + ((long long)b * Hkv + g) * S_cap * D;
+
+  // ---- first loads, issued before the request's tree size and prefix length are
+  // known (they only decide what is kept): the first two K/V tiles with keys
+  // clamped to the cache slab, this lane's Q row and packed mask row with the node
+  // clamped to T_max - 1.  Rows past the request's keys or nodes are neutralised
+  // below, once those are known.
+  u32x4 rk0[KLD], rv0[KLD], rk1[KLD], rv1[KLD];
+  auto load_regs = [&](int kt0, int last_key, u32x4 (&rk)[KLD], u32x4 (&rv)[KLD]) {
+#pragma unroll
+    for (int j = 0; j < KLD; ++j) {
+      const int q = tid + j * NT;
+      const int row = q / CH, c = q % CH;
+      const long long key = min(kt0 + row, last_key);
+      rk[j] = reinterpret_cast<const u32x4*>(Kb + key * D)[c];
+      rv[j] = reinterpret_cast<const u32x4*>(Vb + key * D)[c];
+    }
+  };
+  load_regs(k_begin, (int)S_cap - 1, rk0, rv0);
+  load_regs(k_begin + KT, (int)S_cap - 1, rk1, rv1);
+  const int r = row0 + wave * 32 + l32;
+  const int i_row = min(r / rep, T_max - 1);
+  bf16x8 qf[KSTEPS];
+  {
+    const int head = g * rep + r % rep;
+    const u32x4* qp =
+        reinterpret_cast<const u32x4*>(Q + (((long long)b * T_max + i_row) * Hq + head) * D + h * (D / 2));
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) qf[kk] = as_bf16x8(qp[kk]);
+  }
+  const uint32_t* mp = tree_mask + ((long long)b * T_max + i_row) * W;
+  unsigned long long mrow = (unsigned long long)mp[0] | (W > 1 ? ((unsigned long long)mp[1] << 32) : 0ull);
 
   int T = tree_size[b];
   const int P = prefix_len[b];
   if (status[b] != TV_ST_OK || T < 1 || T > T_max) T = 1;
   const int M = rep * T;
-  const int row0 = rbk * NW * 32;
   if (row0 >= M) return;
   if (P < 0 || (long long)P + T > S_cap) {
     // the prefix does not fit the cache: zero this block's output rows once
     if (split == 0) {
       for (int q = tid; q < NW * 32 * CH; q += NT) {
-        const int r = row0 + q / CH;
-        if (r < M) {
-          const int i = r / rep, head = g * rep + r % rep;
+        const int rr = row0 + q / CH;
+        if (rr < M) {
+          const int i = rr / rep, head = g * rep + rr % rep;
           reinterpret_cast<u32x4*>(O + (((long long)b * T_max + i) * Hq + head) * D)[q % CH] = u32x4{0, 0, 0, 0};
         }
       }
@@ -164,28 +218,22 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_attn_bf16(
     return;
   }
   const int nkeys = P + T;
-  const int k_begin = split * chunk_keys;
   if (k_begin >= nkeys) return;
   const int k_end = min(nkeys, k_begin + chunk_keys);
   const int n_tiles = (k_end - k_begin + KT - 1) / KT;
-
-  const uint16_t* Kb = Kc + ((long long)b * Hkv + g) * S_cap * D;
-  const uint16_t* Vb = Vc + ((long long)b * Hkv + g) * S_cap * D;
-
-  // ---- Q fragments and the packed mask row of this lane's query row
-  const int r = row0 + wave * 32 + l32;
-  bf16x8 qf[KSTEPS];
-  unsigned long long mrow = 0ull;
-  if (r < M) {
-    const int i = r / rep, head = g * rep + r % rep;
-    const u32x4* qp = reinterpret_cast<const u32x4*>(Q + (((long long)b * T_max + i) * Hq + head) * D + h * (D / 2));
+  // V rows past the last key are zeroed (their scores are masked to -inf, and a
+  // zero row keeps 0 * garbage out of the PV product); padding query rows get a
+  // zero Q and no mask
 #pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) qf[kk] = as_bf16x8(qp[kk]);
-    const uint32_t* mp = tree_mask + ((long long)b * T_max + i) * W;
-    mrow = (unsigned long long)mp[0] | (W > 1 ? ((unsigned long long)mp[1] << 32) : 0ull);
-  } else {
+  for (int j = 0; j < KLD; ++j) {
+    const int row = (tid + j * NT) / CH;
+    if (k_begin + row >= nkeys) rv0[j] = u32x4{0, 0, 0, 0};
+    if (k_begin + KT + row >= nkeys) rv1[j] = u32x4{0, 0, 0, 0};
+  }
+  if (r >= M) {
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) qf[kk] = as_bf16x8(u32x4{0, 0, 0, 0});
+    mrow = 0ull;
   }
 
   f32x16 acc[DB];
@@ -203,17 +251,6 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_attn_bf16(
   // the last row, so a load past the last tile re-reads valid memory): with the
   // same number of loads on every path the compiler waits exactly for the older
   // set.  The barrier between tiles waits for LDS traffic only.
-  u32x4 rk0[KLD], rv0[KLD], rk1[KLD], rv1[KLD];
-  auto load_regs = [&](int kt0, u32x4 (&rk)[KLD], u32x4 (&rv)[KLD]) {
-#pragma unroll
-    for (int j = 0; j < KLD; ++j) {
-      const int q = tid + j * NT;
-      const int row = q / CH, c = q % CH;
-      const long long key = min(kt0 + row, nkeys - 1);
-      rk[j] = reinterpret_cast<const u32x4*>(Kb + key * D)[c];
-      rv[j] = reinterpret_cast<const u32x4*>(Vb + key * D)[c];
-    }
-  };
   auto store_regs = [&](int b, const u32x4 (&rk)[KLD], const u32x4 (&rv)[KLD]) {
 #pragma unroll
     for (int j = 0; j < KLD; ++j) {
@@ -333,14 +370,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_attn_bf16(
     }
   };
 
-  load_regs(k_begin, rk0, rv0);
-  load_regs(k_begin + KT, rk1, rv1);
   store_regs(0, rk0, rv0);
   lds_barrier();
   auto tile_step = [&](int t, int buf, u32x4 (&rk_this)[KLD], u32x4 (&rv_this)[KLD],
                        const u32x4 (&rk_next)[KLD], const u32x4 (&rv_next)[KLD]) {
     const int kt0 = k_begin + t * KT;
-    load_regs(kt0 + 2 * KT, rk_this, rv_this);
+    load_regs(kt0 + 2 * KT, nkeys - 1, rk_this, rv_this);
     if (active) compute_tile(kt0, s_k[buf], s_v[buf]);
     if (t + 1 < n_tiles) store_regs(buf ^ 1, rk_next, rv_next);
     lds_barrier();
@@ -369,14 +404,18 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_attn_bf16(
       }
   } else {
     const long long prow = ((long long)bg * n_split + split) * m_pad + r;
-    float* wp = ws_o + prow * D;
+    _Float16* wp = ws_o + prow * D;
+    // a split can see no key of a row (tree keys only, none an ancestor): l = 0
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int v4 = 0; v4 < 4; ++v4) {
         const int d0 = 32 * db + 8 * v4 + 4 * h;
-        *reinterpret_cast<f32x4*>(wp + d0) =
-            f32x4{acc[db][4 * v4 + 0], acc[db][4 * v4 + 1], acc[db][4 * v4 + 2], acc[db][4 * v4 + 3]};
+        typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+        *reinterpret_cast<h4*>(wp + d0) =
+            h4{(_Float16)(acc[db][4 * v4 + 0] * inv), (_Float16)(acc[db][4 * v4 + 1] * inv),
+               (_Float16)(acc[db][4 * v4 + 2] * inv), (_Float16)(acc[db][4 * v4 + 3] * inv)};
       }
     if (h == 0) {
       ws_ml[2 * prow] = m_run;
@@ -385,16 +424,22 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_attn_bf16(
   }
 }
 
-// Merge split partials: weights exp2(m_s - max m), output sum(w o_s) / sum(w l_s).
+// Merge split partials.  Split s left its normalised output o_s (fp16), its
+// running max m_s (log2 domain) and its row sum l_s; the result is
+// sum_s w_s o_s / sum_s w_s with w_s = exp2(m_s - max m) l_s.  Splits are read
+// eight at a time (all loads in flight together) and merged online.
 template <int D>
-__global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ ws_o, const float* __restrict__ ws_ml,
+__global__ __launch_bounds__(256) void k_attn_combine(const _Float16* __restrict__ ws_o,
+                                                      const float* __restrict__ ws_ml,
                                                       const int* __restrict__ prefix_len,
                                                       const int* __restrict__ tree_size,
                                                       const int* __restrict__ status, long long S_cap, int T_max,
                                                       int Hq, int Hkv, int n_split, int chunk_keys, long long m_pad,
                                                       uint16_t* __restrict__ O) {
-  constexpr int TPR = D / 4;          // threads per row, 4 outputs each
+  typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+  constexpr int TPR = D / 8;          // threads per row, 8 outputs each
   constexpr int RPB = 256 / TPR;      // rows per block
+  constexpr int BATCH = 8;
   const int bg = blockIdx.x;
   const int b = bg / Hkv, g = bg % Hkv;
   const int rep = Hq / Hkv;
@@ -405,26 +450,44 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ 
   const int M = rep * T;
   const int r = blockIdx.y * RPB + threadIdx.x / TPR;
   if (r >= M) return;
-  const int d0 = 4 * (threadIdx.x % TPR);
+  const int d0 = 8 * (threadIdx.x % TPR);
   const int nkeys = P + T;
   const int n_act = (nkeys + chunk_keys - 1) / chunk_keys;
   const long long base = (long long)bg * n_split * m_pad + r;
-  float mx = -INFINITY;
-  for (int s = 0; s < n_act; ++s) mx = fmaxf(mx, ws_ml[2 * (base + s * m_pad)]);
-  f32x4 o = {0.f, 0.f, 0.f, 0.f};
-  float l = 0.0f;
-  for (int s = 0; s < n_act; ++s) {
-    const long long pr = base + s * m_pad;
-    const float ms = ws_ml[2 * pr];
-    const float w = ms == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ms - mx);
-    l += w * ws_ml[2 * pr + 1];
-    const f32x4 x = *reinterpret_cast<const f32x4*>(ws_o + pr * D + d0);
-    o += w * x;
+  float mx = -INFINITY, l = 0.0f;
+  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < n_act; s0 += BATCH) {
+    float ms[BATCH], ls[BATCH];
+    h8 x[BATCH];
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) {
+      const long long pr = base + (long long)min(s0 + j, n_act - 1) * m_pad;
+      ms[j] = ws_ml[2 * pr];
+      ls[j] = ws_ml[2 * pr + 1];
+      x[j] = *reinterpret_cast<const h8*>(ws_o + pr * D + d0);
+    }
+    float bm = mx;
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j)
+      if (s0 + j < n_act) bm = fmaxf(bm, ms[j]);
+    const float a = mx == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mx - bm);
+    l *= a;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] *= a;
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) {
+      const float w = (s0 + j < n_act && ms[j] != -INFINITY) ? __builtin_amdgcn_exp2f(ms[j] - bm) * ls[j] : 0.0f;
+      l += w;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = fmaf(w, (float)x[j][e], o[e]);
+    }
+    mx = bm;
   }
   const float inv = 1.0f / l;
   const int i = r / rep, head = g * rep + r % rep;
   uint16_t* op = O + (((long long)b * T_max + i) * Hq + head) * D + d0;
-  *reinterpret_cast<u32x2*>(op) = u32x2{pack_bf16(o[0] * inv, o[1] * inv), pack_bf16(o[2] * inv, o[3] * inv)};
+  *reinterpret_cast<u32x4*>(op) = u32x4{pack_bf16(o[0] * inv, o[1] * inv), pack_bf16(o[2] * inv, o[3] * inv),
+                                        pack_bf16(o[4] * inv, o[5] * inv), pack_bf16(o[6] * inv, o[7] * inv)};
 }
 
 // fp32 path: one wavefront per (node, query head, request).
@@ -498,7 +561,7 @@ __global__ __launch_bounds__(64) void k_attn_fp32(const float* __restrict__ Q, c
 template <int D, int NW>
 void launch_bf16(const Plan& p, hipStream_t s, const void* Q, const void* Kc, const void* Vc, long long S_cap,
                  const int* prefix_len, const int* tree_size, const uint32_t* tree_mask, const int* status,
-                 int T_max, int Hq, int Hkv, int W, float sl2, void* O, float* ws_o, float* ws_ml) {
+                 int T_max, int Hq, int Hkv, int W, float sl2, void* O, _Float16* ws_o, float* ws_ml) {
   hipLaunchKernelGGL((k_attn_bf16<D, NW>), dim3(p.grid), dim3(NW * 64), 0, s, (const uint16_t*)Q, (const uint16_t*)Kc,
                      (const uint16_t*)Vc, S_cap, prefix_len, tree_size, tree_mask, status, T_max, Hq, Hkv, W, sl2,
                      (uint16_t*)O, ws_o, ws_ml, p.n_split, p.chunk_keys, p.n_rowblk, p.n_units, p.m_pad);
@@ -506,7 +569,7 @@ void launch_bf16(const Plan& p, hipStream_t s, const void* Q, const void* Kc, co
 
 size_t ws_bytes_for(const Plan& p, int B, int Hkv, int d) {
   if (p.n_split <= 1) return 0;
-  return (size_t)B * Hkv * p.n_split * p.m_pad * (size_t)(d + 2) * sizeof(float) + 256;
+  return (size_t)B * Hkv * p.n_split * p.m_pad * ((size_t)d * sizeof(_Float16) + 2 * sizeof(float)) + 256;
 }
 
 }  // namespace
@@ -526,6 +589,7 @@ extern "C" int tree_attention(int dtype, int B, int T_max, int Hq, int Hkv, int 
   using namespace tv;
   if (B <= 0 || T_max <= 0 || Hq <= 0 || Hkv <= 0 || S_cap <= 0) return TV_EINVAL;
   if (Hq % Hkv != 0) return TV_EINVAL;
+  if (S_cap > (1LL << 30)) return TV_EUNSUPPORTED;
   if (!Q || !Kc || !Vc || !prefix_len || !tree_size || !tree_mask || !status || !O) return TV_EINVAL;
   if (dtype != TV_DTYPE_BF16 && dtype != TV_DTYPE_FP32) return TV_EUNSUPPORTED;
   if (d != 64 && d != 128) return TV_EUNSUPPORTED;
@@ -553,8 +617,8 @@ extern "C" int tree_attention(int dtype, int B, int T_max, int Hq, int Hkv, int 
   const Plan p = make_plan(B, T_max, Hq, Hkv, S_cap);
   const size_t need = ws_bytes_for(p, B, Hkv, d);
   if (need && (!workspace || ws_bytes < need)) return TV_EWORKSPACE;
-  float* ws_o = reinterpret_cast<float*>(workspace);
-  float* ws_ml = need ? ws_o + (size_t)B * Hkv * p.n_split * p.m_pad * d : nullptr;
+  _Float16* ws_o = reinterpret_cast<_Float16*>(workspace);
+  float* ws_ml = need ? reinterpret_cast<float*>(ws_o + (size_t)B * Hkv * p.n_split * p.m_pad * d) : nullptr;
   const float sl2 = scale * kLog2e;
   if (d == 128) {
     if (p.nw == 4)
@@ -573,7 +637,7 @@ extern "C" int tree_attention(int dtype, int B, int T_max, int Hq, int Hkv, int 
   }
   TV_CHECK_LAUNCH();
   if (p.n_split > 1) {
-    const int rpb = 256 / (d / 4);
+    const int rpb = 256 / (d / 8);
     dim3 grid(B * Hkv, (unsigned)((p.m_pad + rpb - 1) / rpb));
     if (d == 128)
       hipLaunchKernelGGL(k_attn_combine<128>, grid, dim3(256), 0, s, ws_o, ws_ml, prefix_len, tree_size, status, S_cap,

@@ -8,23 +8,26 @@
 // (value descending, index ascending) everywhere.
 //
 // Kernels
-//   k_row_topk    one workgroup per (draft row, vocabulary chunk): streams the
-//                 row once with 16-byte loads (HBM-bound scan), keeps a per-thread
-//                 sorted top-K in registers, merges the 256 lists with K rounds
-//                 of a workgroup argmax, writes the chunk's sorted top-K keys.
-//   k_tree_select one workgroup per request: merges the chunk lists of every row
-//                 (lane groups, one lane per chunk), then runs the D dependent
-//                 K*K rounds and the final top-total_tokens selection (radix
-//                 select on unique 64-bit rank keys) entirely in LDS, and writes
-//                 the numbered tree.  Static mode builds level by level instead.
+//   k_row_topk    one workgroup per draft row: streams the row once with 16-byte
+//                 loads (HBM-bound scan), bounds the row's K-th best entry by the
+//                 K-th largest sixteen-lane group maximum, ranks the few entries
+//                 that reach the bound and writes the row's sorted top-K keys.
+//   k_tree_select one workgroup per request: runs the D dependent K*K rounds and
+//                 the final top-total_tokens selection (one bucket histogram of
+//                 the score range, then an exact rank inside the boundary
+//                 bucket) entirely in LDS, and writes the numbered tree.  Static
+//                 mode builds level by level instead.
 #include "tv_common.h"
 
 namespace tv {
 namespace {
 
-constexpr int kTopkThreads = 256;
+constexpr int kTopkThreads = 1024;                      // one workgroup per draft row
+constexpr int kTopkVec = 8;                              // 16-byte loads per thread per tile
+constexpr int kTopkTile = kTopkThreads * kTopkVec * 4;   // 32768 vocabulary entries
+constexpr int kTopkGroups = kTopkThreads / 16;           // sixteen-lane groups per workgroup
+constexpr int kCandCap = 2048;                           // LDS candidate buffer (8 B each)
 constexpr int kSelectThreads = 256;
-constexpr int kMaxChunks = 8;
 constexpr int kMaxCand = 3072;   // LDS: 16 B per candidate
 constexpr int kMaxLevels = 64;
 
@@ -33,165 +36,202 @@ struct Branching {
   int w[kMaxLevels];
 };
 
-// Workspace layout (rows = B * rows_per_req): each (row, chunk) workgroup of K1
-// writes its sorted top-K rank keys and a bad-value flag; K2 merges the chunks.
+// Workspace layout (rows = B * rows_per_req): K1 writes every row's sorted
+// top-K rank keys and a bad-value flag, K2 reads them.
 struct BuildWs {
-  unsigned long long* chunk_keys;  // [rows][n_chunks][K]
-  int* chunk_bad;                  // [rows][n_chunks]
-  int n_chunks;
+  unsigned long long* row_keys;  // [rows][K]
+  int* row_bad;                  // [rows]
 };
 
-__host__ __device__ inline size_t build_ws_bytes(long long rows, int K) {
-  return (size_t)rows * ((size_t)kMaxChunks * K * 8 + kMaxChunks * 4) + 256;
-}
+inline size_t build_ws_bytes(long long rows, int K) { return (size_t)rows * ((size_t)K * 8 + 4) + 256; }
 
-__host__ __device__ inline BuildWs build_ws(void* base, long long rows, int K, int n_chunks) {
+inline BuildWs build_ws(void* base, long long rows, int K) {
   BuildWs w;
   unsigned char* p = reinterpret_cast<unsigned char*>(base);
-  w.chunk_keys = reinterpret_cast<unsigned long long*>(p);
-  p += (size_t)rows * n_chunks * K * 8;
-  w.chunk_bad = reinterpret_cast<int*>(p);
-  w.n_chunks = n_chunks;
+  w.row_keys = reinterpret_cast<unsigned long long*>(p);
+  w.row_bad = reinterpret_cast<int*>(p + (size_t)rows * K * 8);
   return w;
 }
 
-// Merge the n_chunks sorted chunk lists of every row of request b into the row's
-// top-K rank keys, written to s_key[row*K + r] (r = rank in the row).  A group of
-// n_chunks lanes (power of two <= 8) handles a row: each lane holds one chunk's
-// list in registers and K rounds of a group argmax pop the winners.
-__device__ void merge_rows(const BuildWs& ws, long long row_base, int R, int K, unsigned long long* s_key,
-                           int* s_bad) {
-  const int tid = threadIdx.x;
-  const int G = ws.n_chunks;
-  const int rows_per_pass = kSelectThreads / G;
-  for (int row0 = 0; row0 < R; row0 += rows_per_pass) {
-    const int row = row0 + tid / G;
-    const int c = tid % G;
-    unsigned long long l[kKMax];
-#pragma unroll
-    for (int i = 0; i < kKMax; ++i) l[i] = 0ull;
-    if (row < R) {
-      const unsigned long long* src = ws.chunk_keys + ((row_base + row) * G + c) * K;
-#pragma unroll
-      for (int i = 0; i < kKMax; ++i)
-        if (i < K) l[i] = src[i];
-      if (ws.chunk_bad[(row_base + row) * G + c]) *s_bad = 1;
-    }
-    for (int k = 0; k < K; ++k) {
-      const unsigned long long best = G == 8 ? group_max_u64<8>(l[0])
-                                      : G == 4 ? group_max_u64<4>(l[0])
-                                      : G == 2 ? group_max_u64<2>(l[0]) : l[0];
-      if (row < R && c == 0) s_key[row * K + k] = best;
-      if (l[0] == best) {
-#pragma unroll
-        for (int i = 0; i < kKMax - 1; ++i) l[i] = l[i + 1];
-        l[kKMax - 1] = 0ull;
-      }
-    }
-  }
+// Copy the K sorted row keys of every row of one request into LDS
+// (s_key[row*K + r], r = rank in the row) and OR the rows' bad-value flags.
+__device__ void load_row_keys(const BuildWs& ws, long long row_base, int R, int K, unsigned long long* s_key,
+                              int* s_bad) {
+  for (int i = threadIdx.x; i < R * K; i += blockDim.x) s_key[i] = ws.row_keys[row_base * K + i];
+  for (int i = threadIdx.x; i < R; i += blockDim.x)
+    if (ws.row_bad[row_base + i]) *s_bad = 1;
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
+
+// max / sum over aligned groups of 16 lanes (every lane gets the result)
+__device__ __forceinline__ uint32_t group16_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<0xB1>(v));
+  v = max(v, dpp_u32<0x4E>(v));
+  v = max(v, dpp_u32<0x141>(v));
+  return max(v, dpp_u32<0x140>(v));
+}
+
+__device__ __forceinline__ uint32_t group16_sum_u32(uint32_t v) {
+  v += dpp_u32<0xB1>(v);
+  v += dpp_u32<0x4E>(v);
+  v += dpp_u32<0x141>(v);
+  return v + dpp_u32<0x140>(v);
+}
+
+// Unique 64-bit rank key of vocabulary entry idx whose order key is k32.
+__device__ __forceinline__ unsigned long long make_key64(uint32_t k32, uint32_t idx) {
+  return ((unsigned long long)k32 << 32) | (unsigned long long)(0xFFFFFFFFu - idx);
 }
 
 // --------------------------------------------------------------------------
-// K1: per-(row, chunk) top-K, then the row's top-K by the last chunk to finish.
+// K1: the K best entries of one draft row, by (log-prob desc, token asc).
+//
+// The row is read in tiles of 32768 entries held in registers (eight 16-byte
+// loads per thread, all in flight together).  Per tile:
+//   1. every sixteen-lane group takes the maximum of its 16 x 32 entries;
+//   2. tau = the largest group maximum that at least K group maxima reach:
+//      K distinct entries are >= tau, so no entry below tau is in the top-K;
+//   3. entries >= tau that beat the K-th best of the earlier tiles are
+//      appended to an LDS buffer next to those K (typically a dozen);
+//   4. an exact rank count among the buffer gives the new sorted top-K.
+// A buffer overflow (heavy ties, e.g. a constant row) switches that tile to a
+// bisection on the unique 64-bit keys, which is exact for any input.
 // --------------------------------------------------------------------------
-template <int K>
-__device__ __forceinline__ void list_insert(uint32_t (&lv)[K], uint32_t (&li)[K], uint32_t key, uint32_t idx) {
-  // lv is sorted descending; the caller guarantees key > lv[K-1].  An equal key
-  // never displaces an earlier (lower-index) entry because indices increase.
-#pragma unroll
-  for (int i = K - 1; i >= 1; --i) {
-    const bool shift = key > lv[i - 1];
-    const bool here = !shift && key > lv[i];
-    lv[i] = shift ? lv[i - 1] : (here ? key : lv[i]);
-    li[i] = shift ? li[i - 1] : (here ? idx : li[i]);
-  }
-  if (key > lv[0]) {
-    lv[0] = key;
-    li[0] = idx;
-  }
-}
-
-// Rank-count selection inside one wavefront: n (<= 64) unique non-zero keys in
-// LDS (zeros pad), the K largest are written in order to out[0..K).  Each lane
-// holds one key; the others are broadcast through scalar registers.
-__device__ __forceinline__ void wave_select_sorted(const unsigned long long* keys, int n, int K,
-                                                   unsigned long long* out, int lane) {
-  const unsigned long long my = lane < n ? keys[lane] : 0ull;
-  int rank = 0;
-  for (int o = 0; o < n; ++o) rank += readlane_u64(my, o) > my;
-  if (lane < K) out[lane] = 0ull;
-  __builtin_amdgcn_wave_barrier();
-  if (lane < n && my != 0ull && rank < K) out[rank] = my;
-  __builtin_amdgcn_wave_barrier();
-}
-
-template <int K>
-__global__ __launch_bounds__(kTopkThreads) void k_row_topk(const float* __restrict__ lp, int V, int chunk_len,
-                                                           int vec4, BuildWs ws) {
-  const int chunk = blockIdx.x, n_chunks = gridDim.x;
-  const long long row = blockIdx.y;
+__global__ __launch_bounds__(kTopkThreads) void k_row_topk(const float* __restrict__ lp, int V, int K, int vec4,
+                                                           BuildWs ws) {
+  const long long row = blockIdx.x;
   const float* r = lp + row * (long long)V;
-  const int begin = chunk * chunk_len;
-  const int end = min(V, begin + chunk_len);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  __shared__ unsigned long long s_cand[kCandCap];
+  __shared__ unsigned long long s_best[kKMax];
+  __shared__ uint32_t s_gmax[kTopkGroups];
+  __shared__ int s_n, s_bad, s_cnt[3];
 
-  uint32_t lv[K], li[K];
-#pragma unroll
-  for (int i = 0; i < K; ++i) {
-    lv[i] = 0u;  // below every real key (order_key(-inf) = 0x007FFFFF)
-    li[i] = 0xFFFFFFFFu;
-  }
-  bool bad = false;
-  auto consider = [&](float v, int idx) {
-    bad |= !(v <= 0.0f);  // NaN or positive
-    const uint32_t key = order_key(v);
-    if (key > lv[K - 1]) list_insert<K>(lv, li, key, (uint32_t)idx);
-  };
-  if (vec4) {
-    // 16-byte loads (V % 4 == 0 and a 16-byte aligned base; chunk_len is a
-    // multiple of 4, so every float4 is aligned).
-    typedef float f4 __attribute__((ext_vector_type(4)));
-    const f4* r4 = reinterpret_cast<const f4*>(r);
-    for (int e = begin + 4 * tid; e < end; e += 4 * kTopkThreads) {
-      const f4 x = __builtin_nontemporal_load(r4 + (e >> 2));
-      consider(x[0], e);
-      consider(x[1], e + 1);
-      consider(x[2], e + 2);
-      consider(x[3], e + 3);
-    }
-  } else {
-    for (int e = begin + tid; e < end; e += kTopkThreads) consider(r[e], e);
-  }
-
-  // wavefront merge without barriers: K rounds of a wave argmax over list heads,
-  // the round-k winner is kept by lane k
-  unsigned long long mine = 0ull;
-  for (int k = 0; k < K; ++k) {
-    const unsigned long long head = lv[0] ? (((unsigned long long)lv[0] << 32) | (0xFFFFFFFFu - li[0])) : 0ull;
-    const unsigned long long best = wave_max_u64(head);
-    if (head == best && head != 0ull) {
-#pragma unroll
-      for (int i = 0; i < K - 1; ++i) {
-        lv[i] = lv[i + 1];
-        li[i] = li[i + 1];
-      }
-      lv[K - 1] = 0u;
-      li[K - 1] = 0xFFFFFFFFu;
-    }
-    if (lane == k) mine = best;
-  }
-  __shared__ unsigned long long s_w[4 * kKMax];
-  __shared__ unsigned long long s_out[kKMax];
-  __shared__ int s_bad;
   if (tid == 0) s_bad = 0;
+  bool bad = false;
+  int have = 0;                       // entries in s_best: 0 before the first tile, then K
+  unsigned long long tau_run = 0ull;  // K-th best key of the earlier tiles (0: none)
+
+  for (int t0 = 0; t0 < V; t0 += kTopkTile) {
+    // entry j (0..31) of this thread: vocabulary index idx_of(j)
+    auto idx_of = [&](int j) -> int {
+      return vec4 ? t0 + 4 * ((j >> 2) * kTopkThreads + tid) + (j & 3) : t0 + j * kTopkThreads + tid;
+    };
+    uint32_t k[kTopkVec * 4];
+    if (vec4) {
+      typedef float f4 __attribute__((ext_vector_type(4)));
+      const f4* r4 = reinterpret_cast<const f4*>(r);
+      const int last4 = V / 4 - 1;
+      f4 x[kTopkVec];
+#pragma unroll
+      for (int i = 0; i < kTopkVec; ++i)  // clamped addresses: every load is in bounds and issued at once
+        x[i] = __builtin_nontemporal_load(r4 + min(t0 / 4 + i * kTopkThreads + tid, last4));
+#pragma unroll
+      for (int j = 0; j < kTopkVec * 4; ++j) {
+        const bool in = idx_of(j) < V;
+        const float v = x[j >> 2][j & 3];
+        bad |= in && !(v <= 0.0f);  // NaN or positive
+        k[j] = in ? order_key(v) : 0u;
+      }
+    } else {
+      float x[kTopkVec * 4];
+#pragma unroll
+      for (int j = 0; j < kTopkVec * 4; ++j) x[j] = r[min(idx_of(j), V - 1)];
+#pragma unroll
+      for (int j = 0; j < kTopkVec * 4; ++j) {
+        const bool in = idx_of(j) < V;
+        bad |= in && !(x[j] <= 0.0f);
+        k[j] = in ? order_key(x[j]) : 0u;
+      }
+    }
+    uint32_t tmax = 0u;
+#pragma unroll
+    for (int j = 0; j < kTopkVec * 4; ++j) tmax = max(tmax, k[j]);
+    tmax = group16_max_u32(tmax);
+    if ((lane & 15) == 0) s_gmax[tid >> 4] = tmax;
+    if (tid < have) s_cand[tid] = s_best[tid];
+    if (tid == 0) s_n = have;
+    __syncthreads();
+
+    // tau (every wave computes it): lane l holds group maximum g_l and counts
+    // the group maxima >= g_l; tau = max { g_l : count >= K }
+    uint32_t tau;
+    {
+      const uint32_t g = s_gmax[lane];
+      int c = 0;
+      const uint4* g4 = reinterpret_cast<const uint4*>(s_gmax);
+#pragma unroll
+      for (int i = 0; i < kTopkGroups / 4; ++i) {
+        const uint4 q = g4[i];
+        c += (q.x >= g) + (q.y >= g) + (q.z >= g) + (q.w >= g);
+      }
+      const uint32_t t = group16_max_u32(c >= K ? g : 0u);
+      tau = max(max((uint32_t)__builtin_amdgcn_readlane((int)t, 0), (uint32_t)__builtin_amdgcn_readlane((int)t, 16)),
+                max((uint32_t)__builtin_amdgcn_readlane((int)t, 32), (uint32_t)__builtin_amdgcn_readlane((int)t, 48)));
+    }
+#pragma unroll
+    for (int j = 0; j < kTopkVec * 4; ++j) {
+      if (k[j] != 0u && k[j] >= tau) {
+        const unsigned long long kk = make_key64(k[j], (uint32_t)idx_of(j));
+        if (kk > tau_run) {
+          const int slot = atomicAdd(&s_n, 1);
+          if (slot < kCandCap) s_cand[slot] = kk;
+        }
+      }
+    }
+    __syncthreads();
+    int n = s_n;
+
+    if (n > kCandCap) {
+      // exact fallback: the K-th largest unique key x of (earlier best, this
+      // tile) by bisection on count(key >= x) >= K, then exactly K candidates
+      if (tid < 3) s_cnt[tid] = 0;
+      __syncthreads();
+      unsigned long long lo = 1ull, hi = ~0ull;  // count(lo) >= K always holds
+      for (int it = 0; lo < hi; ++it) {
+        const unsigned long long mid = lo + (hi - lo) / 2 + 1;
+        int c = (tid < have && s_best[tid] >= mid) ? 1 : 0;
+#pragma unroll
+        for (int j = 0; j < kTopkVec * 4; ++j) c += k[j] != 0u && make_key64(k[j], (uint32_t)idx_of(j)) >= mid;
+        if (c) atomicAdd(&s_cnt[it % 3], c);
+        __syncthreads();
+        const int tot = s_cnt[it % 3];
+        if (tid == 0) s_cnt[(it + 2) % 3] = 0;
+        if (tot >= K) lo = mid;
+        else hi = mid - 1;
+      }
+      __syncthreads();
+      if (tid == 0) s_n = 0;
+      __syncthreads();
+      if (tid < have && s_best[tid] >= lo) s_cand[atomicAdd(&s_n, 1)] = s_best[tid];
+#pragma unroll
+      for (int j = 0; j < kTopkVec * 4; ++j) {
+        const unsigned long long kk = make_key64(k[j], (uint32_t)idx_of(j));
+        if (k[j] != 0u && kk >= lo) s_cand[atomicAdd(&s_n, 1)] = kk;
+      }
+      __syncthreads();
+      n = s_n;  // == K
+    }
+
+    // exact rank among the n unique candidates; the K best, in order, to s_best
+    for (int t = tid; t < n; t += kTopkThreads) {
+      const unsigned long long my = s_cand[t];
+      int rk = 0;
+      for (int o = 0; o < n; ++o) rk += s_cand[o] > my;
+      if (rk < K) s_best[rk] = my;
+    }
+    __syncthreads();
+    have = K;
+    tau_run = s_best[K - 1];
+  }
+  if (bad) s_bad = 1;
   __syncthreads();
-  if (lane < K) s_w[wave * K + lane] = mine;
-  if (__ballot(bad) && lane == 0) atomicOr(&s_bad, 1);
-  __syncthreads();
-  if (wave == 0) wave_select_sorted(s_w, 4 * K, K, s_out, lane);
-  __syncthreads();
-  if (tid < K) ws.chunk_keys[(row * n_chunks + chunk) * K + tid] = s_out[tid];
-  if (tid == 0) ws.chunk_bad[row * n_chunks + chunk] = s_bad;
+  if (tid < K) ws.row_keys[row * K + tid] = s_best[tid];
+  if (tid == 0) ws.row_bad[row] = s_bad;
 }
 
 // --------------------------------------------------------------------------
@@ -300,8 +340,96 @@ __device__ unsigned long long radix_select_threshold(const int C, const int n, c
   return prefix;
 }
 
+// Threshold of the n best of the C candidates under (score desc, id asc):
+// returns tau such that exactly n of the unique keys rank_key(s_sc[id], id) are
+// >= tau.  One histogram of the 32-bit score keys over at most kBuckets
+// equal-width buckets of their range finds the bucket that holds the boundary;
+// its members are ranked exactly by their 64-bit keys.  A boundary bucket with
+// more than kBucketRankMax members (heavy ties) falls back to the radix select.
+constexpr int kBucketBits = 10;
+constexpr int kBuckets = 1 << kBucketBits;
+static_assert(kBuckets == 4 * kSelectThreads, "four buckets per thread in the boundary scan");
+constexpr int kBucketRankMax = 256;
+
+__device__ unsigned long long bucket_select_threshold(const int C, const int n, const float* s_sc, int* s_hist,
+                                                      short* s_mem, int* s_misc, uint32_t* s_red, int* s_tmp,
+                                                      unsigned long long* s_bcast, unsigned long long* s_tmp64) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int kWaves = kSelectThreads / 64;
+  if (n <= 0) return ~0ull;  // nothing: no key reaches all-ones
+  if (n >= C) return 0ull;
+  uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
+  for (int id = tid; id < C; id += kSelectThreads) {
+    const uint32_t k = order_key(s_sc[id]);
+    kmax = max(kmax, k);
+    kmin = min(kmin, k);
+  }
+  for (int i = tid; i < kBuckets; i += kSelectThreads) s_hist[i] = 0;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, m, 64));
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, m, 64));
+  }
+  if (lane == 0) {
+    s_red[2 * wave] = kmax;
+    s_red[2 * wave + 1] = kmin;
+  }
+  if (tid == 0) s_misc[1] = 0;
+  __syncthreads();
+  kmax = s_red[0];
+  kmin = s_red[1];
+  for (int w = 1; w < kWaves; ++w) {
+    kmax = max(kmax, s_red[2 * w]);
+    kmin = min(kmin, s_red[2 * w + 1]);
+  }
+  const uint32_t range = kmax - kmin;
+  // buckets used: (range >> shift) + 1 <= kBuckets
+  const int shift = range < (uint32_t)kBuckets ? 0 : 32 - __clz(range) - kBucketBits;
+  for (int id = tid; id < C; id += kSelectThreads) atomicAdd(&s_hist[(order_key(s_sc[id]) - kmin) >> shift], 1);
+  __syncthreads();
+  // thread t owns buckets b0..b0+3, thread 0 the top four; count from the top
+  const int b0 = kBuckets - 4 - 4 * tid;
+  const int h3 = s_hist[b0 + 3], h2 = s_hist[b0 + 2], h1 = s_hist[b0 + 1], h0 = s_hist[b0];
+  const int mine = h0 + h1 + h2 + h3;
+  int total = 0;
+  const int above = block_excl_scan(mine, s_tmp, &total);
+  if (above < n && n <= above + mine) {
+    int a = above, bk;
+    if (n <= a + h3) bk = b0 + 3;
+    else if (n <= a + h3 + h2) { a += h3; bk = b0 + 2; }
+    else if (n <= a + h3 + h2 + h1) { a += h3 + h2; bk = b0 + 1; }
+    else { a += h3 + h2 + h1; bk = b0; }
+    s_misc[0] = bk;
+    s_misc[2] = n - a;  // still needed inside the bucket
+  }
+  __syncthreads();
+  const uint32_t bstar = (uint32_t)s_misc[0];
+  const int need = s_misc[2];
+  for (int id = tid; id < C; id += kSelectThreads)
+    if (((order_key(s_sc[id]) - kmin) >> shift) == bstar) {
+      const int slot = atomicAdd(&s_misc[1], 1);
+      if (slot < kBucketRankMax) s_mem[slot] = (short)id;
+    }
+  __syncthreads();
+  const int m = s_misc[1];
+  if (m > kBucketRankMax) return radix_select_threshold(C, n, s_sc, s_hist, s_bcast, s_tmp64);
+  for (int t = tid; t < m; t += kSelectThreads) {
+    const int id = s_mem[t];
+    const unsigned long long my = rank_key(s_sc[id], (uint32_t)id);
+    int rk = 0;
+    for (int o = 0; o < m; ++o) {
+      const int io = s_mem[o];
+      rk += rank_key(s_sc[io], (uint32_t)io) > my;
+    }
+    if (rk == need - 1) s_bcast[3] = my;
+  }
+  __syncthreads();
+  return s_bcast[3];
+}
+
+template <int K>
 __global__ __launch_bounds__(kSelectThreads) void k_tree_select_dynamic(
-    BuildWs ws, int R, int K, int D, int total_tokens, const int* __restrict__ root_token, int T_max,
+    BuildWs ws, int R, int D, int total_tokens, const int* __restrict__ root_token, int T_max,
     int* __restrict__ draft_tokens, int* __restrict__ parents, int* __restrict__ tree_size,
     float* __restrict__ node_score, int* __restrict__ status) {
   extern __shared__ unsigned char smem[];
@@ -310,76 +438,78 @@ __global__ __launch_bounds__(kSelectThreads) void k_tree_select_dynamic(
   float* s_sc = reinterpret_cast<float*>(s_key + C);
   short* s_par = reinterpret_cast<short*>(s_sc + C);
   short* s_node = s_par + C;
-  __shared__ int s_hist[256];
+  __shared__ int s_hist[kBuckets];
+  __shared__ short s_mem[kBucketRankMax];
+  __shared__ int s_misc[4];
+  __shared__ uint32_t s_red[2 * (kSelectThreads / 64)];
   __shared__ unsigned long long s_bcast[4], s_tmp64[kSelectThreads / 64];
   __shared__ int s_front[2][kKMax];
   __shared__ float s_fsc[2][kKMax];
-  __shared__ unsigned long long s_lkey[256];
-  __shared__ int s_rank[256];
   __shared__ int s_tmp[kSelectThreads / 64];
   __shared__ int s_bad;
 
   const int b = blockIdx.x, tid = threadIdx.x;
   if (tid == 0) s_bad = 0;
   __syncthreads();
-  merge_rows(ws, (long long)b * R, R, K, s_key, &s_bad);
+  load_row_keys(ws, (long long)b * R, R, K, s_key, &s_bad);
   __syncthreads();
   for (int id = tid; id < C; id += kSelectThreads) {
     s_sc[id] = key_value(s_key[id]);
     s_par[id] = -1;
   }
-  __syncthreads();
   if (tid < K) {
     s_front[0][tid] = tid;
-    s_fsc[0][tid] = s_sc[tid];
+    s_fsc[0][tid] = key_value(s_key[tid]);
   }
   __syncthreads();
 
-  // D dependent rounds of K*K cumulative scores and a frontier top-K
-  const int KK = K * K;
-  const int split = KK <= 64 ? 4 : (KK <= 128 ? 2 : 1);
+  // D dependent rounds: the K*K cumulative scores of a layer, then its K best
+  // (score desc, index asc) become the next frontier.  One phase and one
+  // barrier per layer: a group of 16 lanes ranks one candidate q, each lane
+  // computing and comparing the scores of every 16th candidate of the layer
+  // (o = part, part + 16, ...) in registers; the group sums the counts.  Raw
+  // row log-probs are read from s_key, cumulative scores written to s_sc.
+  constexpr int KK = K * K;
+  constexpr int kGroups = kSelectThreads / 16;
+  constexpr int kPer = (KK + 15) / 16;  // candidates per lane
+  const int grp = tid >> 4, part = tid & 15;
   for (int l = 1; l <= D; ++l) {
     const int cur = (l - 1) & 1, nxt = l & 1;
     const int base = K + (l - 1) * KK;
-    for (int q = tid; q < KK; q += kSelectThreads) {
-      const int j = q / K;
-      const float sc = __fadd_rn(s_sc[base + q], s_fsc[cur][j]);
-      s_sc[base + q] = sc;
-      s_par[base + q] = (short)s_front[cur][j];
-      s_lkey[q] = rank_key(sc, (uint32_t)q);
-      s_rank[q] = 0;
+    unsigned long long ok[kPer];  // rank keys of candidates part + 16 i
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int o = part + 16 * i;
+      ok[i] = 0ull;
+      if (o < KK) ok[i] = rank_key(__fadd_rn(key_value(s_key[base + o]), s_fsc[cur][o / K]), (uint32_t)o);
     }
-    __syncthreads();
-    for (int t = tid; t < KK * split; t += kSelectThreads) {
-      const int q = t % KK, part = t / KK;
-      const unsigned long long mine = s_lkey[q];
-      const int o0 = part * (KK / split), o1 = part == split - 1 ? KK : o0 + KK / split;
-      int cnt = 0;
-      int o = o0;
-      for (; o + 16 <= o1; o += 16) {  // sixteen keys per batch of LDS reads
-        unsigned long long x[16];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) x[u] = s_lkey[o + u];
+    for (int q0 = 0; q0 < KK; q0 += kGroups) {
+      const int q = q0 + grp;
+      uint32_t cnt = 0;
+      float sc = 0.0f;
+      if (q < KK) {
+        sc = __fadd_rn(key_value(s_key[base + q]), s_fsc[cur][q / K]);
+        const unsigned long long mine = rank_key(sc, (uint32_t)q);
 #pragma unroll
-        for (int u = 0; u < 16; ++u) cnt += x[u] > mine;
+        for (int i = 0; i < kPer; ++i) cnt += ok[i] > mine;
       }
-      for (; o < o1; ++o) cnt += s_lkey[o] > mine;
-      if (split == 1) s_rank[q] = cnt;
-      else atomicAdd(&s_rank[q], cnt);
-    }
-    __syncthreads();
-    for (int q = tid; q < KK; q += kSelectThreads) {
-      const int rk2 = s_rank[q];
-      if (rk2 < K) {
-        s_front[nxt][rk2] = base + q;
-        s_fsc[nxt][rk2] = s_sc[base + q];
+      cnt = group16_sum_u32(cnt);
+      if (q < KK && part == 0) {
+        s_sc[base + q] = sc;
+        s_par[base + q] = (short)s_front[cur][q / K];
+        if (cnt < (uint32_t)K) {
+          s_front[nxt][cnt] = base + q;
+          s_fsc[nxt][cnt] = sc;
+        }
       }
     }
     __syncthreads();
   }
 
   // final: keep the total_tokens best candidates, number them by ascending id
-  const unsigned long long tau = radix_select_threshold(C, total_tokens, s_sc, s_hist, s_bcast, s_tmp64);
+  const unsigned long long tau = bucket_select_threshold(C, total_tokens, s_sc, s_hist, s_mem, s_misc, s_red, s_tmp,
+                                                        s_bcast, s_tmp64);
   const int per = (C + kSelectThreads - 1) / kSelectThreads;
   const int lo = min(C, tid * per), hi = min(C, lo + per);
   int cnt = 0;
@@ -434,7 +564,7 @@ __global__ __launch_bounds__(kSelectThreads) void k_tree_select_static(
   const int b = blockIdx.x, tid = threadIdx.x;
   if (tid == 0) s_bad = 0;
   __syncthreads();
-  merge_rows(ws, (long long)b * R, R, K, rk, &s_bad);
+  load_row_keys(ws, (long long)b * R, R, K, rk, &s_bad);
   __syncthreads();
   if (tid == 0) {
     // level by level: every frontier node, in order, appends its row's top-w
@@ -471,31 +601,6 @@ __global__ __launch_bounds__(kSelectThreads) void k_tree_select_static(
   if (tid == 0) {
     tree_size[b] = T;
     status[b] = ok ? TV_ST_OK : TV_ST_LOGPROB;
-  }
-}
-
-int pick_chunks(long long rows_total, int V, int K) {
-  int n = 1;
-  while (n < kMaxChunks && rows_total * n < 256 && (V / (n * 2)) >= 4 * kTopkThreads && V / (n * 2) >= K) n *= 2;
-  return n;
-}
-
-template <int K>
-void launch_topk(dim3 grid, const float* lp, int V, int chunk_len, int vec4, BuildWs ws, hipStream_t s) {
-  hipLaunchKernelGGL(k_row_topk<K>, grid, dim3(kTopkThreads), 0, s, lp, V, chunk_len, vec4, ws);
-}
-
-void launch_topk_any(int K, dim3 grid, const float* lp, int V, int chunk_len, int vec4, BuildWs ws,
-                     hipStream_t s) {
-  switch (K) {
-#define TV_TOPK_CASE(k) \
-  case k:               \
-    launch_topk<k>(grid, lp, V, chunk_len, vec4, ws, s); break;
-    TV_TOPK_CASE(1) TV_TOPK_CASE(2) TV_TOPK_CASE(3) TV_TOPK_CASE(4) TV_TOPK_CASE(5) TV_TOPK_CASE(6)
-    TV_TOPK_CASE(7) TV_TOPK_CASE(8) TV_TOPK_CASE(9) TV_TOPK_CASE(10) TV_TOPK_CASE(11) TV_TOPK_CASE(12)
-    TV_TOPK_CASE(13) TV_TOPK_CASE(14) TV_TOPK_CASE(15) TV_TOPK_CASE(16)
-#undef TV_TOPK_CASE
-    default: break;
   }
 }
 
@@ -551,23 +656,29 @@ extern "C" int tree_build(int mode, int B, int V, int K, int D, int total_tokens
   if (!workspace || ws_bytes < need) return TV_EWORKSPACE;
 
   const long long rows_total = (long long)B * rows_per_req;
-  if (rows_total > 65535) return TV_EUNSUPPORTED;
-  const int n_chunks = pick_chunks(rows_total, V, K);
-  int chunk_len = (V + n_chunks - 1) / n_chunks;
-  chunk_len = (chunk_len + 3) & ~3;
-  const BuildWs ws = build_ws(workspace, rows_total, K, n_chunks);
+  if (rows_total > 0x7FFFFFFFll) return TV_EUNSUPPORTED;
+  const BuildWs ws = build_ws(workspace, rows_total, K);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
-  dim3 grid(n_chunks, (unsigned)rows_total);
   const int vec4 = (V % 4 == 0) && ((reinterpret_cast<uintptr_t>(logprobs) & 15) == 0);
-  launch_topk_any(K, grid, logprobs, V, chunk_len, vec4, ws, s);
+  hipLaunchKernelGGL(k_row_topk, dim3((unsigned)rows_total), dim3(kTopkThreads), 0, s, logprobs, V, K, vec4, ws);
   TV_CHECK_LAUNCH();
 
   if (mode == TV_MODE_DYNAMIC) {
     const int C = rows_per_req * K;
     const size_t smem = (size_t)C * 16;
-    hipLaunchKernelGGL(k_tree_select_dynamic, dim3(B), dim3(kSelectThreads), smem, s, ws, rows_per_req, K, D,
-                       total_tokens, root_token, T_max, draft_tokens, parents, tree_size, node_score, status);
+    switch (K) {
+#define TV_SELECT_CASE(k)                                                                                          \
+  case k:                                                                                                          \
+    hipLaunchKernelGGL(k_tree_select_dynamic<k>, dim3(B), dim3(kSelectThreads), smem, s, ws, rows_per_req, D,     \
+                       total_tokens, root_token, T_max, draft_tokens, parents, tree_size, node_score, status);     \
+    break;
+      TV_SELECT_CASE(1) TV_SELECT_CASE(2) TV_SELECT_CASE(3) TV_SELECT_CASE(4) TV_SELECT_CASE(5) TV_SELECT_CASE(6)
+      TV_SELECT_CASE(7) TV_SELECT_CASE(8) TV_SELECT_CASE(9) TV_SELECT_CASE(10) TV_SELECT_CASE(11)
+      TV_SELECT_CASE(12) TV_SELECT_CASE(13) TV_SELECT_CASE(14) TV_SELECT_CASE(15) TV_SELECT_CASE(16)
+#undef TV_SELECT_CASE
+      default: return TV_EUNSUPPORTED;
+    }
   } else {
     const size_t smem = (size_t)rows_per_req * K * 8;
     hipLaunchKernelGGL(k_tree_select_static, dim3(B), dim3(kSelectThreads), smem, s, ws, rows_per_req, K, br,
