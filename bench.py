@@ -139,6 +139,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches only")
+    ap.add_argument("--copy-mb", type=float, default=0.0,
+                    help="before warmup, one device-to-device copy of this many MiB (a plain copy kernel of known "
+                         "size that calibrates the HBM byte counters of a profiler run)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (requests or kv heads would be "
@@ -158,6 +161,16 @@ def main():
     log(f"workload {w.name}: {per_copy / 2**20:.1f} MiB of inputs per copy, {n_copies} copies rotated")
     step = TreeVerifyStep(w, n_copies=n_copies)
     stream = torch.cuda.current_stream()
+
+    if args.copy_mb > 0:
+        n = int(args.copy_mb * 2 ** 20)
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {n} bytes read, {n} bytes written")
+        del src, dst
 
     # the synthetic target's argmax needs the tree: build once and read it back (untimed)
     step.build()

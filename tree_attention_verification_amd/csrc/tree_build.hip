@@ -62,6 +62,8 @@ __device__ void load_row_keys(const BuildWs& ws, long long row_base, int R, int 
     if (ws.row_bad[row_base + i]) *s_bad = 1;
 }
 
+typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
+
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
@@ -445,6 +447,7 @@ __global__ __launch_bounds__(kSelectThreads) void k_tree_select_dynamic(
   __shared__ unsigned long long s_bcast[4], s_tmp64[kSelectThreads / 64];
   __shared__ int s_front[2][kKMax];
   __shared__ float s_fsc[2][kKMax];
+  __shared__ __attribute__((aligned(16))) unsigned long long s_cand[kKMax * kKMax + 16];
   __shared__ int s_tmp[kSelectThreads / 64];
   __shared__ int s_bad;
 
@@ -464,48 +467,72 @@ __global__ __launch_bounds__(kSelectThreads) void k_tree_select_dynamic(
   __syncthreads();
 
   // D dependent rounds: the K*K cumulative scores of a layer, then its K best
-  // (score desc, index asc) become the next frontier.  One phase and one
-  // barrier per layer: a group of 16 lanes ranks one candidate q, each lane
-  // computing and comparing the scores of every 16th candidate of the layer
-  // (o = part, part + 16, ...) in registers; the group sums the counts.  Raw
-  // row log-probs are read from s_key, cumulative scores written to s_sc.
+  // (score desc, index asc) become the next frontier.  Wavefront 0 runs them
+  // alone, so no workgroup barrier is needed inside a round:
+  //   1. each lane forms the scores of candidates lane + 64 i in registers
+  //      (and records score and parent slot in LDS for the final selection);
+  //   2. tau = the worst of the K list heads (candidate j*K is the best child of
+  //      frontier slot j): K distinct candidates reach tau, so nothing below it
+  //      can be in the frontier;
+  //   3. the candidates >= tau are compacted into LDS (ballot + mbcnt);
+  //   4. an exact rank count among them places the K best.
   constexpr int KK = K * K;
-  constexpr int kGroups = kSelectThreads / 16;
-  constexpr int kPer = (KK + 15) / 16;  // candidates per lane
-  const int grp = tid >> 4, part = tid & 15;
-  for (int l = 1; l <= D; ++l) {
-    const int cur = (l - 1) & 1, nxt = l & 1;
-    const int base = K + (l - 1) * KK;
-    unsigned long long ok[kPer];  // rank keys of candidates part + 16 i
+  constexpr int kPerLane = (KK + 63) / 64;
+  if (tid < 64) {
+    for (int l = 1; l <= D; ++l) {
+      const int cur = (l - 1) & 1, nxt = l & 1;
+      const int base = K + (l - 1) * KK;
+      unsigned long long key[kPerLane];
+      unsigned long long heads = ~0ull;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int o = part + 16 * i;
-      ok[i] = 0ull;
-      if (o < KK) ok[i] = rank_key(__fadd_rn(key_value(s_key[base + o]), s_fsc[cur][o / K]), (uint32_t)o);
-    }
-#pragma unroll
-    for (int q0 = 0; q0 < KK; q0 += kGroups) {
-      const int q = q0 + grp;
-      uint32_t cnt = 0;
-      float sc = 0.0f;
-      if (q < KK) {
-        sc = __fadd_rn(key_value(s_key[base + q]), s_fsc[cur][q / K]);
-        const unsigned long long mine = rank_key(sc, (uint32_t)q);
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) cnt += ok[i] > mine;
-      }
-      cnt = group16_sum_u32(cnt);
-      if (q < KK && part == 0) {
-        s_sc[base + q] = sc;
-        s_par[base + q] = (short)s_front[cur][q / K];
-        if (cnt < (uint32_t)K) {
-          s_front[nxt][cnt] = base + q;
-          s_fsc[nxt][cnt] = sc;
+      for (int i = 0; i < kPerLane; ++i) {
+        const int o = tid + 64 * i;
+        key[i] = 0ull;
+        if (o < KK) {
+          const int j = o / K;
+          const float sc = __fadd_rn(key_value(s_key[base + o]), s_fsc[cur][j]);
+          s_sc[base + o] = sc;
+          s_par[base + o] = (short)s_front[cur][j];
+          key[i] = rank_key(sc, (uint32_t)o);
+          if (o == j * K) heads = key[i] < heads ? key[i] : heads;
         }
       }
+      const unsigned long long tau = ~wave_max_u64(~heads);
+      int n = 0;
+#pragma unroll
+      for (int i = 0; i < kPerLane; ++i) {
+        const bool keep = key[i] != 0ull && key[i] >= tau;
+        const unsigned long long m = __ballot(keep);
+        const int pos = n + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        if (keep) s_cand[pos] = key[i];
+        n += __popcll(m);
+      }
+      if (tid < 16) s_cand[n + tid] = 0ull;  // zero keys pad the last batch
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      for (int t = tid; t < n; t += 64) {
+        const unsigned long long my = s_cand[t];
+        int rk = 0;
+        for (int o0 = 0; o0 < n; o0 += 16) {  // 16 keys per batch, all reads in flight
+          u64x2 x[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) x[u] = reinterpret_cast<const u64x2*>(s_cand + o0)[u];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) rk += (x[u][0] > my) + (x[u][1] > my);
+        }
+        if (rk < K) {
+          const int q = (int)key_index(my);
+          s_front[nxt][rk] = base + q;
+          s_fsc[nxt][rk] = s_sc[base + q];
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
-    __syncthreads();
   }
+  __syncthreads();
 
   // final: keep the total_tokens best candidates, number them by ascending id
   const unsigned long long tau = bucket_select_threshold(C, total_tokens, s_sc, s_hist, s_mem, s_misc, s_red, s_tmp,
