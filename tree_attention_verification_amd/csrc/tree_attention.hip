@@ -128,8 +128,30 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// One 16-byte global -> LDS copy per lane (global_load_lds_dwordx4): lane l's
+// 16 bytes land at LDS byte address m0 + 16 l; each lane supplies its own global
+// address.  Written as inline assembly so that the compiler does not track it:
+// its own wait placement cannot tell the stage buffers apart and would wait for
+// every copy in flight before each tile.  The kernel waits explicitly instead
+// (vm_wait_imm), counting these copies; the compiler's waits for its own loads
+// can only be stricter than needed, since it does not see the younger copies.
+__device__ __forceinline__ void dma16(const uint16_t* g, uint32_t lds_byte_addr) {
+  // (one wait state between the m0 write and the LDS-DMA instruction that reads it)
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_byte_addr)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)p;
+}
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of this
+// wavefront are outstanding (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt
+// and lgkmcnt left at their maximum)
+constexpr int vm_wait_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
 template <int D, int NW>
-__global__ __launch_bounds__(NW * 64, 8 / NW) void k_attn_bf16(
+__global__ __launch_bounds__(NW * 64, 1) void k_attn_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Kc, const uint16_t* __restrict__ Vc,
     long long S_cap, const int* __restrict__ prefix_len, const int* __restrict__ tree_size,
     const uint32_t* __restrict__ tree_mask, const int* __restrict__ status, int T_max, int Hq, int Hkv, int W,
@@ -139,7 +161,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_attn_bf16(
   constexpr int KSTEPS = D / 16;     // 16-wide k-steps of QK^T (KSTEPS/2 per half of d)
   constexpr int DB = D / 32;         // 32-wide d blocks of the output
   constexpr int CH = D / 8;          // 16-byte chunks per K/V row
-  constexpr int KLD = KT * CH / NT;  // 16-byte chunks per thread per tile and tensor
+  constexpr int NSTAGE = 4;          // LDS tile buffers: three tiles in flight while one is computed
+  constexpr int INSTR = KT * CH / 64;  // 64-lane DMA instructions per tensor per tile
+  static_assert(INSTR % NW == 0, "DMA instructions split evenly over the wavefronts");
+  constexpr int DMA_WAVE = 2 * INSTR / NW;  // DMA instructions per wavefront per tile (K and V)
   // K and V tiles are row-major (key rows of D elements) in LDS with their 16-byte
   // chunks XOR-swizzled per row: chunk c of K row r sits at c ^ kswz(r), so the 16
   // consecutive rows that one 16-byte read serves land on distinct banks; chunk c
@@ -147,8 +172,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_attn_bf16(
   // a transpose read over the banks.
   auto kswz = [](int r) { return CH == 16 ? (r & 15) : ((r >> 1) & 7); };
   auto vswz = [](int r) { return CH == 16 ? 4 * (r & 3) : 2 * (r & 3); };
-  __shared__ __attribute__((aligned(16))) uint16_t s_k[2][KT * D];
-  __shared__ __attribute__((aligned(16))) uint16_t s_v[2][KT * D];
+  // one array per stage (not one indexed array): the compiler then knows which
+  // buffer each LDS read touches and does not wait for DMA into the others
+  __shared__ __attribute__((aligned(16))) uint16_t s_k0[KT * D], s_k1[KT * D], s_k2[KT * D], s_k3[KT * D];
+  __shared__ __attribute__((aligned(16))) uint16_t s_v0[KT * D], s_v1[KT * D], s_v2[KT * D], s_v3[KT * D];
 
   // ---- which (request, kv head, split, row block) this workgroup owns
   const int wg = blockIdx.x;
@@ -168,24 +195,30 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_attn_bf16(
   const uint16_t* Kb = Kc + ((long long)b * Hkv + g) * S_cap * D;
   const uint16_t* Vb = Vc + ((long long)b * Hkv + g) * S_cap * D;
 
-  // ---- first loads, issued before the request's tree size and prefix length are
-  // known (they only decide what is kept): the first two K/V tiles with keys
-  // clamped to the cache slab, this lane's Q row and packed mask row with the node
-  // clamped to T_max - 1.  Rows past the request's keys or nodes are neutralised
-  // below, once those are known.
-  u32x4 rk0[KLD], rv0[KLD], rk1[KLD], rv1[KLD];
-  auto load_regs = [&](int kt0, int last_key, u32x4 (&rk)[KLD], u32x4 (&rv)[KLD]) {
+  // ---- tile staging: K/V tiles go straight from global memory into LDS (no
+  // registers) through four stage buffers; tile t+3 is requested while tile t is
+  // computed, so three tiles (96 KB at d = 128) are in flight per workgroup.  The
+  // 64 lanes of one DMA instruction fill 1 KB of LDS in order, so the XOR swizzle
+  // is applied on the global side: LDS slot (row, c) receives chunk c ^ swz(row).
+  // Requests are issued unconditionally (keys clamped to a valid row) so that
+  // every wavefront has the same count in flight and one vmcnt bound is exact.
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform (LDS base goes to m0)
+  auto dma_tile = [&](int kt0, int last_key, uint16_t* sk, uint16_t* sv) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < KLD; ++j) {
-      const int q = tid + j * NT;
-      const int row = q / CH, c = q % CH;
+    for (int ii = 0; ii < INSTR / NW; ++ii) {
+      const int i = wave_u + ii * NW;
+      const int idx = 64 * i + lane;
+      const int row = idx / CH, cs = idx % CH;
       const long long key = min(kt0 + row, last_key);
-      rk[j] = reinterpret_cast<const u32x4*>(Kb + key * D)[c];
-      rv[j] = reinterpret_cast<const u32x4*>(Vb + key * D)[c];
+      dma16(Kb + key * D + 8 * (cs ^ kswz(row)), lds_addr(sk) + 1024u * i);
+      dma16(Vb + key * D + 8 * (cs ^ vswz(row)), lds_addr(sv) + 1024u * i);
     }
   };
-  load_regs(k_begin, (int)S_cap - 1, rk0, rv0);
-  load_regs(k_begin + KT, (int)S_cap - 1, rk1, rv1);
+
+  // ---- first loads, issued before the request's tree size and prefix length are
+  // known (they only decide what is kept): this lane's Q row and packed mask row
+  // with the node clamped to T_max - 1, then the first three K/V tiles with keys
+  // clamped to the cache slab.  What lies past the request is neutralised below.
   const int r = row0 + wave * 32 + l32;
   const int i_row = min(r / rep, T_max - 1);
   bf16x8 qf[KSTEPS];
@@ -198,13 +231,20 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_attn_bf16(
   }
   const uint32_t* mp = tree_mask + ((long long)b * T_max + i_row) * W;
   unsigned long long mrow = (unsigned long long)mp[0] | (W > 1 ? ((unsigned long long)mp[1] << 32) : 0ull);
+  dma_tile(k_begin, (int)S_cap - 1, s_k0, s_v0);
+  dma_tile(k_begin + KT, (int)S_cap - 1, s_k1, s_v1);
+  dma_tile(k_begin + 2 * KT, (int)S_cap - 1, s_k2, s_v2);
 
   int T = tree_size[b];
   const int P = prefix_len[b];
   if (status[b] != TV_ST_OK || T < 1 || T > T_max) T = 1;
   const int M = rep * T;
-  if (row0 >= M) return;
+  if (row0 >= M) {
+    __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));  // no LDS DMA may outlive the workgroup
+    return;
+  }
   if (P < 0 || (long long)P + T > S_cap) {
+    __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
     // the prefix does not fit the cache: zero this block's output rows once
     if (split == 0) {
       for (int q = tid; q < NW * 32 * CH; q += NT) {
@@ -218,18 +258,26 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_attn_bf16(
     return;
   }
   const int nkeys = P + T;
-  if (k_begin >= nkeys) return;
+  if (k_begin >= nkeys) {
+    __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+    return;
+  }
   const int k_end = min(nkeys, k_begin + chunk_keys);
   const int n_tiles = (k_end - k_begin + KT - 1) / KT;
-  // V rows past the last key are zeroed (their scores are masked to -inf, and a
-  // zero row keeps 0 * garbage out of the PV product); padding query rows get a
-  // zero Q and no mask
-#pragma unroll
-  for (int j = 0; j < KLD; ++j) {
-    const int row = (tid + j * NT) / CH;
-    if (k_begin + row >= nkeys) rv0[j] = u32x4{0, 0, 0, 0};
-    if (k_begin + KT + row >= nkeys) rv1[j] = u32x4{0, 0, 0, 0};
+  // A first tile that reaches past the last key was fetched with keys clamped to
+  // the slab, so its rows past the request hold whatever the cache holds there:
+  // fetch it again with keys clamped to the last key (its scores there are masked
+  // to -inf, and finite V rows keep 0 * garbage out of the PV product).  The
+  // re-fetch lands after the first one (returns are in order); the one-off full
+  // wait below covers it.
+  bool refetched = false;
+  if (k_begin + 3 * KT > nkeys) {
+    if (k_begin + KT > nkeys) dma_tile(k_begin, nkeys - 1, s_k0, s_v0);
+    else if (k_begin + 2 * KT > nkeys) dma_tile(k_begin + KT, nkeys - 1, s_k1, s_v1);
+    else dma_tile(k_begin + 2 * KT, nkeys - 1, s_k2, s_v2);
+    refetched = true;
   }
+  // padding query rows get a zero Q and no mask
   if (r >= M) {
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) qf[kk] = as_bf16x8(u32x4{0, 0, 0, 0});
@@ -243,23 +291,6 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_attn_bf16(
     for (int v = 0; v < 16; ++v) acc[db][v] = 0.0f;
   float m_run = -INFINITY, l_part = 0.0f;
 
-  // ---- tile staging: coalesced 16-byte global loads into one of two register
-  // sets, then swizzled 16-byte LDS stores into one of two LDS buffers.  Tile t+2
-  // is loaded while tile t is computed and tile t+1 is stored, so two tiles of
-  // loads are in flight.  The loop is unrolled by two so each register set is a
-  // fixed set of registers.  Loads are issued unconditionally (keys are clamped to
-  // the last row, so a load past the last tile re-reads valid memory): with the
-  // same number of loads on every path the compiler waits exactly for the older
-  // set.  The barrier between tiles waits for LDS traffic only.
-  auto store_regs = [&](int b, const u32x4 (&rk)[KLD], const u32x4 (&rv)[KLD]) {
-#pragma unroll
-    for (int j = 0; j < KLD; ++j) {
-      const int q = tid + j * NT;
-      const int row = q / CH, c = q % CH;
-      *reinterpret_cast<u32x4*>(&s_k[b][row * D + ((c ^ kswz(row)) * 8)]) = rk[j];
-      *reinterpret_cast<u32x4*>(&s_v[b][row * D + ((c ^ vswz(row)) * 8)]) = rv[j];
-    }
-  };
   auto lds_barrier = []() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(kLgkmOnlyZero);
@@ -271,7 +302,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_attn_bf16(
   const bool active = row0 + wave * 32 < M;
   const int tg = lane >> 4, tj = lane & 15;
 
-  auto compute_tile = [&](int kt0, const uint16_t* sk, const uint16_t* sv) {
+  auto compute_tile = [&](int kt0, const uint16_t* sk, const uint16_t* sv) __attribute__((always_inline)) {
     // S^T = K Q^T for two 32-key blocks
     f32x16 s[2];
 #pragma unroll
@@ -370,20 +401,24 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_attn_bf16(
     }
   };
 
-  store_regs(0, rk0, rv0);
-  lds_barrier();
-  auto tile_step = [&](int t, int buf, u32x4 (&rk_this)[KLD], u32x4 (&rv_this)[KLD],
-                       const u32x4 (&rk_next)[KLD], const u32x4 (&rv_next)[KLD]) {
+  if (refetched) __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+  // step t: wait for this wavefront's part of tile t (tiles t+1, t+2 may still be
+  // in flight), barrier (every part landed, and every wavefront is done with tile
+  // t-1), request tile t+3 into tile t-1's buffer, compute tile t.
+  auto tile_step = [&](int t, const uint16_t* sk, const uint16_t* sv, uint16_t* nk, uint16_t* nv) __attribute__((always_inline)) {
     const int kt0 = k_begin + t * KT;
-    load_regs(kt0 + 2 * KT, nkeys - 1, rk_this, rv_this);
-    if (active) compute_tile(kt0, s_k[buf], s_v[buf]);
-    if (t + 1 < n_tiles) store_regs(buf ^ 1, rk_next, rv_next);
+    __builtin_amdgcn_s_waitcnt(vm_wait_imm(2 * DMA_WAVE));
     lds_barrier();
+    dma_tile(kt0 + 3 * KT, nkeys - 1, nk, nv);
+    if (active) compute_tile(kt0, sk, sv);
   };
-  for (int t = 0; t < n_tiles; t += 2) {
-    tile_step(t, 0, rk0, rv0, rk1, rv1);
-    if (t + 1 < n_tiles) tile_step(t + 1, 1, rk1, rv1, rk0, rv0);
+  for (int t = 0; t < n_tiles; t += NSTAGE) {
+    tile_step(t, s_k0, s_v0, s_k3, s_v3);
+    if (t + 1 < n_tiles) tile_step(t + 1, s_k1, s_v1, s_k0, s_v0);
+    if (t + 2 < n_tiles) tile_step(t + 2, s_k2, s_v2, s_k1, s_v1);
+    if (t + 3 < n_tiles) tile_step(t + 3, s_k3, s_v3, s_k2, s_v2);
   }
+  __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));  // the requests past the last tile
 
   // ---- epilogue
   const float l_tot = l_part + __shfl_xor(l_part, 32, 64);
