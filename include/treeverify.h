@@ -202,7 +202,9 @@ int tree_accept(int B, int T_max, int dcap, const int* draft_tokens, const int* 
  * P_b + accept_path[b][k]; all sources of a (request, head, layer) are read
  * before any destination is written, so overlapping paths are safe.  Other rows
  * are untouched.  new_prefix_len[b] = P_b + L + 1 (nullable).  Requires
- * d*elem_bytes to be a multiple of 16 and <= 1024, dcap < 64.
+ * d*elem_bytes to be a multiple of 16 and <= 1024, dcap < 64, and
+ * 2 * dcap * d * elem_bytes <= 65536 (the K and V rows of one path are staged
+ * in on-chip memory; TV_EUNSUPPORTED otherwise).
  * ------------------------------------------------------------------------- */
 int kv_compact(int B, int n_layers, int Hkv, int d, int elem_bytes, void* Kc, void* Vc,
                long long S_cap, long long layer_stride_elems, const int* prefix_len,

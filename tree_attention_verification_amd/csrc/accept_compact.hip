@@ -13,8 +13,8 @@
 // kv_compact follows the KV note after the handbook's tree_spec.py and the
 // dissection's "after acceptance: KV from tree layout back to linear": the
 // accepted nodes' K/V are moved (not recomputed) to rows P+1..P+L.  One
-// workgroup per (request, kv head, layer) reads every source row into
-// registers, synchronises, then writes, so a source that is also an earlier
+// workgroup per (request, kv head, layer) stages every source row of K and V in
+// LDS, synchronises, then writes, so a source that is also an earlier
 // destination is read before it is overwritten.
 #include "tv_common.h"
 
@@ -40,15 +40,16 @@ __global__ __launch_bounds__(64) void k_tree_accept(int T_max, int dcap, const i
   const int tok = c < T ? tok_l : -1;
   const int par = (c > 0 && c < T) ? par_l : -2;
   int node = 0, len = 0, mine = c == 0 ? 0 : -1;
+  // node is wave-uniform, so the prediction at it is read with readlane
   for (int step = 0; step < dcap; ++step) {
-    const int pred = __shfl(pred_l, node, 64);
+    const int pred = __builtin_amdgcn_readlane(pred_l, node);
     const unsigned long long hit = __ballot(par == node && tok == pred);
     if (!hit) break;
     node = __ffsll((long long)hit) - 1;  // lowest-index matching child
     ++len;
     if (c == len) mine = node;
   }
-  const int bonus = __shfl(pred_l, node, 64);
+  const int bonus = __builtin_amdgcn_readlane(pred_l, node);
   if (c <= dcap) accept_path[(long long)b * (dcap + 1) + c] = mine;
   if (c == 0) {
     accept_len[b] = len;
@@ -57,7 +58,6 @@ __global__ __launch_bounds__(64) void k_tree_accept(int T_max, int dcap, const i
 }
 
 constexpr int kCompactThreads = 256;
-constexpr int kCompactPerThread = 16;  // 63 rows x 64 16-byte chunks / 256 threads
 
 __global__ __launch_bounds__(kCompactThreads) void k_kv_compact(int B, int Hkv, int chunks16, uint4* __restrict__ Kc,
                                                                 uint4* __restrict__ Vc, long long S_cap,
@@ -70,42 +70,44 @@ __global__ __launch_bounds__(kCompactThreads) void k_kv_compact(int B, int Hkv, 
   const int b = blockIdx.x / Hkv;
   const int layer = blockIdx.y;
   const int tid = threadIdx.x;
+  // the request's prefix, length and path, read once (path entries by the first
+  // dcap + 1 threads, into LDS)
+  __shared__ int s_path[64];
+  __shared__ int s_bad;
   const int P = prefix_len[b];
-  int L = accept_len[b];
-  const int* path = accept_path + (long long)b * (dcap + 1);
-  bool ok = L >= 1 && L <= dcap && P >= 0;
+  const int L = accept_len[b];
+  if (tid == 0) s_bad = 0;
+  if (tid <= dcap) s_path[tid] = accept_path[(long long)b * (dcap + 1) + tid];
+  __syncthreads();
   // every source and destination row must lie inside the cache
-  if (ok) {
-    for (int k = 1; k <= L; ++k) {
-      const int n = path[k];
-      if (n < k || (long long)P + n >= S_cap) ok = false;
-    }
+  if (tid >= 1 && tid <= L && tid <= dcap) {
+    const int n = s_path[tid];
+    if (n < tid || (long long)P + n >= S_cap) s_bad = 1;
   }
+  __syncthreads();
+  const bool ok = L >= 1 && L <= dcap && P >= 0 && s_bad == 0;
   // a request whose path does not fit is left untouched (its prefix grows by the root only)
   if (g == 0 && layer == 0 && tid == 0 && new_prefix_len) new_prefix_len[b] = P + (ok ? L : 0) + 1;
   if (!ok) return;
   const long long head = ((long long)layer * layer_stride16) + ((long long)b * Hkv + g) * S_cap * chunks16;
+  uint4* kb = Kc + head;
+  uint4* vb = Vc + head;
+  // every K and V source row is read into LDS before any destination is written
+  // (a source may be an earlier destination); stage = [K rows | V rows]
+  extern __shared__ uint4 s_stage[];
   const int items = L * chunks16;
-  for (int t = 0; t < 2; ++t) {
-    uint4* base = (t == 0 ? Kc : Vc) + head;
-    uint4 v[kCompactPerThread];
-#pragma unroll
-    for (int u = 0; u < kCompactPerThread; ++u) {
-      const int q = tid + u * kCompactThreads;
-      if (q < items) {
-        const int k = 1 + q / chunks16, c = q % chunks16;
-        v[u] = base[((long long)P + path[k]) * chunks16 + c];
-      }
-    }
-    __syncthreads();  // every source read before any destination write
-#pragma unroll
-    for (int u = 0; u < kCompactPerThread; ++u) {
-      const int q = tid + u * kCompactThreads;
-      if (q < items) {
-        const int k = 1 + q / chunks16, c = q % chunks16;
-        base[((long long)P + k) * chunks16 + c] = v[u];
-      }
-    }
+#pragma unroll 4
+  for (int q = tid; q < 2 * items; q += kCompactThreads) {
+    const int t = q >= items, r = q - t * items;
+    const int k = 1 + r / chunks16, c = r % chunks16;
+    s_stage[q] = (t ? vb : kb)[((long long)P + s_path[k]) * chunks16 + c];
+  }
+  __syncthreads();
+#pragma unroll 4
+  for (int q = tid; q < 2 * items; q += kCompactThreads) {
+    const int t = q >= items, r = q - t * items;
+    const int k = 1 + r / chunks16, c = r % chunks16;
+    (t ? vb : kb)[((long long)P + k) * chunks16 + c] = s_stage[q];
   }
 }
 
@@ -140,7 +142,9 @@ extern "C" int kv_compact(int B, int n_layers, int Hkv, int d, int elem_bytes, v
   if ((reinterpret_cast<uintptr_t>(Kc) & 15) || (reinterpret_cast<uintptr_t>(Vc) & 15)) return TV_EINVAL;
   if ((long long)B * Hkv > 2147483647LL || n_layers > 65535) return TV_EINVAL;
   const int chunks16 = (int)(row_bytes / 16);
-  hipLaunchKernelGGL(tv::k_kv_compact, dim3(B * Hkv, n_layers), dim3(tv::kCompactThreads), 0,
+  const size_t stage = 2 * (size_t)dcap * (size_t)(row_bytes / 16) * 16;  // K and V rows of one path
+  if (stage > 65536) return TV_EUNSUPPORTED;
+  hipLaunchKernelGGL(tv::k_kv_compact, dim3(B * Hkv, n_layers), dim3(tv::kCompactThreads), stage,
                      reinterpret_cast<hipStream_t>(stream), B, Hkv, chunks16, reinterpret_cast<uint4*>(Kc),
                      reinterpret_cast<uint4*>(Vc), S_cap, layer_stride_elems * elem_bytes / 16, prefix_len,
                      accept_path, accept_len, dcap, new_prefix_len);

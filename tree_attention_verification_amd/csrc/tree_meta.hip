@@ -91,12 +91,20 @@ __global__ __launch_bounds__(64) void k_tree_mask_positions(int T_max, int dcap,
     positions[ob + i] = in ? P + an.depth : 0;
   }
 
-  // children in ascending id: first child of i, next sibling of i
-  int fc = -1, ns = -1;
-  for (int j = T - 1; j >= 1; --j) {
-    const int pj = __shfl(p, j, 64);
-    if (pj == i) fc = j;
-    if (j > i && in && i > 0 && pj == p) ns = j;
+  // children in ascending id: every node sets its bit in its parent's child mask
+  // (one LDS atomic per node); the first child of i is the lowest bit of i's mask,
+  // the next sibling of i the lowest bit of its parent's mask above i
+  __shared__ unsigned long long s_cm[64];
+  s_cm[i] = 0ull;
+  __syncthreads();
+  if (in && i > 0) atomicOr(&s_cm[p], 1ull << i);
+  __syncthreads();
+  const unsigned long long cm = in ? s_cm[i] : 0ull;
+  const int fc = cm ? __ffsll((long long)cm) - 1 : -1;
+  int ns = -1;
+  if (in && i > 0) {
+    const unsigned long long later = s_cm[p] & ~((2ull << i) - 1ull);  // i = 63: 2 << 63 wraps to 0, no bits
+    ns = later ? __ffsll((long long)later) - 1 : -1;
   }
   if (i < T_max) {
     if (first_child) first_child[ob + i] = fc;
