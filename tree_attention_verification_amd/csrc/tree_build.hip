@@ -8,10 +8,11 @@
 // (value descending, index ascending) everywhere.
 //
 // Kernels
-//   k_row_topk    one workgroup per draft row: streams the row once with 16-byte
-//                 loads (HBM-bound scan), bounds the row's K-th best entry by the
-//                 K-th largest sixteen-lane group maximum, ranks the few entries
-//                 that reach the bound and writes the row's sorted top-K keys.
+//   k_row_topk    one workgroup per (draft row, vocabulary chunk): streams its
+//                 chunk once with 16-byte loads (HBM-bound scan), bounds the
+//                 chunk's K-th best entry by the K-th largest sixteen-lane group
+//                 maximum, ranks the few entries that reach the bound and writes
+//                 the chunk's sorted top-K keys (the select kernel merges chunks).
 //   k_tree_select one workgroup per request: runs the D dependent K*K rounds and
 //                 the final top-total_tokens selection (one bucket histogram of
 //                 the score range, then an exact rank inside the boundary
@@ -22,10 +23,13 @@
 namespace tv {
 namespace {
 
-constexpr int kTopkThreads = 1024;                      // one workgroup per draft row
+constexpr int kTopkThreads = 256;                       // one workgroup per (draft row, vocabulary chunk)
 constexpr int kTopkVec = 8;                              // 16-byte loads per thread per tile
-constexpr int kTopkTile = kTopkThreads * kTopkVec * 4;   // 32768 vocabulary entries
-constexpr int kTopkGroups = kTopkThreads / 16;           // sixteen-lane groups per workgroup
+constexpr int kTopkTile = kTopkThreads * kTopkVec * 4;   // 8192 vocabulary entries
+constexpr int kTopkGroups = kTopkThreads / 16;           // sixteen-lane groups per workgroup (>= K)
+constexpr int kMaxSplit = 8;                             // vocabulary chunks per row
+constexpr int kStageKeys = 6144;                         // chunk lists staged in the select kernel (48 KB)
+static_assert(kTopkGroups >= kKMax, "the group-maximum bound needs at least K groups");
 constexpr int kCandCap = 2048;                           // LDS candidate buffer (8 B each)
 constexpr int kSelectThreads = 256;
 constexpr int kMaxCand = 3072;   // LDS: 16 B per candidate
@@ -36,30 +40,97 @@ struct Branching {
   int w[kMaxLevels];
 };
 
-// Workspace layout (rows = B * rows_per_req): K1 writes every row's sorted
-// top-K rank keys and a bad-value flag, K2 reads them.
+// A draft row is split into S vocabulary chunks, each ranked by its own
+// workgroup, so that a small batch still spreads its rows over the CUs: one
+// chunk per 8192 entries, at most kMaxSplit, and no more than the select
+// kernel can stage next to its 16 B per candidate within 48 KB of dynamic LDS
+// (R*K*16 + R*S*K*8 <= 8 * kStageKeys).
+inline int pick_split(int V, int K, int R) {
+  int S = (V + kTopkTile - 1) / kTopkTile;
+  if (S > kMaxSplit) S = kMaxSplit;
+  const long long rk = (long long)R * K;
+  const long long cap = (kStageKeys - 2 * rk) / rk;
+  if (S > cap) S = (int)cap;
+  return S < 1 ? 1 : S;
+}
+
+// Workspace layout (rows = B * rows_per_req): K1 writes the sorted top-K rank
+// keys and a bad-value flag of every (row, chunk); K2 merges a row's chunks.
 struct BuildWs {
-  unsigned long long* row_keys;  // [rows][K]
-  int* row_bad;                  // [rows]
+  unsigned long long* row_keys;  // [rows][S][K]
+  int* row_bad;                  // [rows][S]
+  int S;
 };
 
-inline size_t build_ws_bytes(long long rows, int K) { return (size_t)rows * ((size_t)K * 8 + 4) + 256; }
+inline size_t build_ws_bytes(long long rows, int K, int S) {
+  return (size_t)rows * S * ((size_t)K * 8 + 4) + 256;
+}
 
-inline BuildWs build_ws(void* base, long long rows, int K) {
+inline BuildWs build_ws(void* base, long long rows, int K, int S) {
   BuildWs w;
   unsigned char* p = reinterpret_cast<unsigned char*>(base);
   w.row_keys = reinterpret_cast<unsigned long long*>(p);
-  w.row_bad = reinterpret_cast<int*>(p + (size_t)rows * K * 8);
+  w.row_bad = reinterpret_cast<int*>(p + (size_t)rows * S * K * 8);
+  w.S = S;
   return w;
 }
 
-// Copy the K sorted row keys of every row of one request into LDS
-// (s_key[row*K + r], r = rank in the row) and OR the rows' bad-value flags.
+// The sorted top-K rank keys of every row of one request into LDS (s_key[row*K
+// + r], r = rank in the row), and the OR of the rows' bad-value flags.  With S
+// chunks per row, the chunk lists are staged in s_stage and merged by groups of
+// G lanes (G = S rounded up to a power of two, one lane per chunk list): K
+// rounds of a DPP group maximum over the list heads; the winning lane moves to
+// its next key (already in a register) and prefetches the one after.
+template <int G>
+__device__ void merge_chunk_lists(const unsigned long long* s_stage, int R, int K, int S,
+                                  unsigned long long* s_key) {
+  const int tid = threadIdx.x, c = tid % G;
+  for (int row0 = 0; row0 < R; row0 += kSelectThreads / G) {
+    const int row = row0 + tid / G;
+    const bool live = row < R && c < S;
+    const unsigned long long* lst = s_stage + ((long long)row * S + c) * K;
+    unsigned long long head = live ? lst[0] : 0ull;
+    unsigned long long next = live && K > 1 ? lst[1] : 0ull;
+    int ptr = 1;  // index of `next`
+    for (int k = 0; k < K; ++k) {
+      const unsigned long long best = group_max_u64<G>(head);
+      if (row < R && c == 0) s_key[row * K + k] = best;
+      if (head == best && head != 0ull) {  // keys are unique: exactly one lane wins
+        head = next;
+        ++ptr;
+        next = live && ptr < K ? lst[ptr] : 0ull;
+      }
+    }
+  }
+}
+
 __device__ void load_row_keys(const BuildWs& ws, long long row_base, int R, int K, unsigned long long* s_key,
-                              int* s_bad) {
-  for (int i = threadIdx.x; i < R * K; i += blockDim.x) s_key[i] = ws.row_keys[row_base * K + i];
-  for (int i = threadIdx.x; i < R; i += blockDim.x)
-    if (ws.row_bad[row_base + i]) *s_bad = 1;
+                              unsigned long long* s_stage, int* s_bad) {
+  const int S = ws.S;
+  const long long base = row_base * S * K;
+  // global -> LDS in batches of eight loads per thread, all in flight together
+  unsigned long long* dst = S == 1 ? s_key : s_stage;
+  const int n = R * S * K;
+  for (int i0 = 0; i0 < n; i0 += 8 * kSelectThreads) {
+    unsigned long long v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * kSelectThreads + threadIdx.x;
+      v[u] = i < n ? ws.row_keys[base + i] : 0ull;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * kSelectThreads + threadIdx.x;
+      if (i < n) dst[i] = v[u];
+    }
+  }
+  for (int i = threadIdx.x; i < R * S; i += blockDim.x)
+    if (ws.row_bad[row_base * S + i]) *s_bad = 1;
+  if (S == 1) return;
+  __syncthreads();
+  if (S <= 2) merge_chunk_lists<2>(s_stage, R, K, S, s_key);
+  else if (S <= 4) merge_chunk_lists<4>(s_stage, R, K, S, s_key);
+  else merge_chunk_lists<8>(s_stage, R, K, S, s_key);
 }
 
 typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
@@ -105,12 +176,17 @@ __device__ __forceinline__ unsigned long long make_key64(uint32_t k32, uint32_t 
 // --------------------------------------------------------------------------
 __global__ __launch_bounds__(kTopkThreads) void k_row_topk(const float* __restrict__ lp, int V, int K, int vec4,
                                                            BuildWs ws) {
-  const long long row = blockIdx.x;
+  const int S = ws.S;
+  const long long row = blockIdx.x / S;
+  const int chunk = blockIdx.x % S;
   const float* r = lp + row * (long long)V;
+  // this workgroup's vocabulary range (a multiple of 4 long, so 16-byte loads stay aligned)
+  const int span = ((V + S - 1) / S + 3) & ~3;
+  const int begin = chunk * span, end = min(V, begin + span);
   const int tid = threadIdx.x, lane = tid & 63;
   __shared__ unsigned long long s_cand[kCandCap];
   __shared__ unsigned long long s_best[kKMax];
-  __shared__ uint32_t s_gmax[kTopkGroups];
+  __shared__ __attribute__((aligned(16))) uint32_t s_gmax[kTopkGroups];
   __shared__ int s_n, s_bad, s_cnt[3];
 
   if (tid == 0) s_bad = 0;
@@ -118,7 +194,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_row_topk(const float* __restri
   int have = 0;                       // entries in s_best: 0 before the first tile, then K
   unsigned long long tau_run = 0ull;  // K-th best key of the earlier tiles (0: none)
 
-  for (int t0 = 0; t0 < V; t0 += kTopkTile) {
+  for (int t0 = begin; t0 < end; t0 += kTopkTile) {
     // entry j (0..31) of this thread: vocabulary index idx_of(j)
     auto idx_of = [&](int j) -> int {
       return vec4 ? t0 + 4 * ((j >> 2) * kTopkThreads + tid) + (j & 3) : t0 + j * kTopkThreads + tid;
@@ -127,14 +203,14 @@ __global__ __launch_bounds__(kTopkThreads) void k_row_topk(const float* __restri
     if (vec4) {
       typedef float f4 __attribute__((ext_vector_type(4)));
       const f4* r4 = reinterpret_cast<const f4*>(r);
-      const int last4 = V / 4 - 1;
+      const int last4 = end / 4 - 1;
       f4 x[kTopkVec];
 #pragma unroll
       for (int i = 0; i < kTopkVec; ++i)  // clamped addresses: every load is in bounds and issued at once
         x[i] = __builtin_nontemporal_load(r4 + min(t0 / 4 + i * kTopkThreads + tid, last4));
 #pragma unroll
       for (int j = 0; j < kTopkVec * 4; ++j) {
-        const bool in = idx_of(j) < V;
+        const bool in = idx_of(j) < end;
         const float v = x[j >> 2][j & 3];
         bad |= in && !(v <= 0.0f);  // NaN or positive
         k[j] = in ? order_key(v) : 0u;
@@ -142,10 +218,10 @@ __global__ __launch_bounds__(kTopkThreads) void k_row_topk(const float* __restri
     } else {
       float x[kTopkVec * 4];
 #pragma unroll
-      for (int j = 0; j < kTopkVec * 4; ++j) x[j] = r[min(idx_of(j), V - 1)];
+      for (int j = 0; j < kTopkVec * 4; ++j) x[j] = r[min(idx_of(j), end - 1)];
 #pragma unroll
       for (int j = 0; j < kTopkVec * 4; ++j) {
-        const bool in = idx_of(j) < V;
+        const bool in = idx_of(j) < end;
         bad |= in && !(x[j] <= 0.0f);
         k[j] = in ? order_key(x[j]) : 0u;
       }
@@ -163,7 +239,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_row_topk(const float* __restri
     // the group maxima >= g_l; tau = max { g_l : count >= K }
     uint32_t tau;
     {
-      const uint32_t g = s_gmax[lane];
+      const uint32_t g = lane < kTopkGroups ? s_gmax[lane] : 0u;  // lanes past the groups hold nothing
       int c = 0;
       const uint4* g4 = reinterpret_cast<const uint4*>(s_gmax);
 #pragma unroll
@@ -232,23 +308,33 @@ __global__ __launch_bounds__(kTopkThreads) void k_row_topk(const float* __restri
   }
   if (bad) s_bad = 1;
   __syncthreads();
-  if (tid < K) ws.row_keys[row * K + tid] = s_best[tid];
-  if (tid == 0) ws.row_bad[row] = s_bad;
+  if (tid < K) ws.row_keys[(row * S + chunk) * K + tid] = s_best[tid];
+  if (tid == 0) ws.row_bad[row * S + chunk] = s_bad;
 }
 
 // --------------------------------------------------------------------------
 // K2 helpers
 // --------------------------------------------------------------------------
+// Inclusive prefix sum over the 64 lanes of a wavefront with DPP (no LDS round
+// trip): shifts by 1, 2, 4, 8 inside each 16-lane row (lanes shifted in from
+// outside the row read 0), then row 0's total is broadcast into row 1 and row
+// 2's into row 3 (row_bcast:15), and rows 0-1's total into rows 2 and 3
+// (row_bcast:31).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);
+  return v;
+}
+
 // Block-wide exclusive scan of one int per thread; returns the exclusive prefix
 // and writes the total to *total.
 __device__ int block_excl_scan(int v, int* s_tmp, int* total) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
+  const int x = wave_incl_scan(v);
   if (lane == 63) s_tmp[wave] = x;
   __syncthreads();
   int base = 0, tot = 0;
@@ -311,12 +397,7 @@ __device__ unsigned long long radix_select_threshold(const int C, const int n, c
       const int b0 = 4 * (63 - tid);
       const int h3 = s_hist[b0 + 3], h2 = s_hist[b0 + 2], h1 = s_hist[b0 + 1], h0 = s_hist[b0];
       const int mine = h0 + h1 + h2 + h3;
-      int incl = mine;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        int y = __shfl_up(incl, o, 64);
-        if (tid >= o) incl += y;
-      }
+      const int incl = wave_incl_scan(mine);
       const int above = incl - mine;  // keys in strictly higher bins
       if (above < need && need <= incl) {
         int a = above, digit, cnt;
@@ -367,10 +448,12 @@ __device__ unsigned long long bucket_select_threshold(const int C, const int n, 
     kmin = min(kmin, k);
   }
   for (int i = tid; i < kBuckets; i += kSelectThreads) s_hist[i] = 0;
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, m, 64));
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, m, 64));
+  {
+    const uint32_t a = group16_max_u32(kmax), n = group16_max_u32(~kmin);  // min = ~max(~x)
+    kmax = max(max((uint32_t)__builtin_amdgcn_readlane((int)a, 0), (uint32_t)__builtin_amdgcn_readlane((int)a, 16)),
+               max((uint32_t)__builtin_amdgcn_readlane((int)a, 32), (uint32_t)__builtin_amdgcn_readlane((int)a, 48)));
+    kmin = ~max(max((uint32_t)__builtin_amdgcn_readlane((int)n, 0), (uint32_t)__builtin_amdgcn_readlane((int)n, 16)),
+                max((uint32_t)__builtin_amdgcn_readlane((int)n, 32), (uint32_t)__builtin_amdgcn_readlane((int)n, 48)));
   }
   if (lane == 0) {
     s_red[2 * wave] = kmax;
@@ -454,7 +537,7 @@ __global__ __launch_bounds__(kSelectThreads) void k_tree_select_dynamic(
   const int b = blockIdx.x, tid = threadIdx.x;
   if (tid == 0) s_bad = 0;
   __syncthreads();
-  load_row_keys(ws, (long long)b * R, R, K, s_key, &s_bad);
+  load_row_keys(ws, (long long)b * R, R, K, s_key, reinterpret_cast<unsigned long long*>(s_node + C), &s_bad);
   __syncthreads();
   for (int id = tid; id < C; id += kSelectThreads) {
     s_sc[id] = key_value(s_key[id]);
@@ -591,7 +674,7 @@ __global__ __launch_bounds__(kSelectThreads) void k_tree_select_static(
   const int b = blockIdx.x, tid = threadIdx.x;
   if (tid == 0) s_bad = 0;
   __syncthreads();
-  load_row_keys(ws, (long long)b * R, R, K, rk, &s_bad);
+  load_row_keys(ws, (long long)b * R, R, K, rk, rk + R * K, &s_bad);
   __syncthreads();
   if (tid == 0) {
     // level by level: every frontier node, in order, appends its row's top-w
@@ -638,7 +721,7 @@ extern "C" size_t tree_build_workspace_bytes(int mode, int B, int V, int K, int 
   (void)mode;
   (void)V;
   if (B <= 0 || K <= 0 || rows_per_req <= 0) return 0;
-  return tv::build_ws_bytes((long long)B * rows_per_req, K);
+  return tv::build_ws_bytes((long long)B * rows_per_req, K, tv::pick_split(V, K, rows_per_req));
 }
 
 extern "C" int tree_build(int mode, int B, int V, int K, int D, int total_tokens, const int* branching,
@@ -684,16 +767,20 @@ extern "C" int tree_build(int mode, int B, int V, int K, int D, int total_tokens
 
   const long long rows_total = (long long)B * rows_per_req;
   if (rows_total > 0x7FFFFFFFll) return TV_EUNSUPPORTED;
-  const BuildWs ws = build_ws(workspace, rows_total, K);
+  const int S = pick_split(V, K, rows_per_req);
+  if (rows_total * S > 0x7FFFFFFFll) return TV_EUNSUPPORTED;
+  const BuildWs ws = build_ws(workspace, rows_total, K, S);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const size_t stage = S > 1 ? (size_t)rows_per_req * S * K * 8 : 0;  // chunk lists merged in the select kernel
 
   const int vec4 = (V % 4 == 0) && ((reinterpret_cast<uintptr_t>(logprobs) & 15) == 0);
-  hipLaunchKernelGGL(k_row_topk, dim3((unsigned)rows_total), dim3(kTopkThreads), 0, s, logprobs, V, K, vec4, ws);
+  hipLaunchKernelGGL(k_row_topk, dim3((unsigned)(rows_total * S)), dim3(kTopkThreads), 0, s, logprobs, V, K, vec4,
+                     ws);
   TV_CHECK_LAUNCH();
 
   if (mode == TV_MODE_DYNAMIC) {
     const int C = rows_per_req * K;
-    const size_t smem = (size_t)C * 16;
+    const size_t smem = (size_t)C * 16 + stage;
     switch (K) {
 #define TV_SELECT_CASE(k)                                                                                          \
   case k:                                                                                                          \
@@ -707,7 +794,7 @@ extern "C" int tree_build(int mode, int B, int V, int K, int D, int total_tokens
       default: return TV_EUNSUPPORTED;
     }
   } else {
-    const size_t smem = (size_t)rows_per_req * K * 8;
+    const size_t smem = (size_t)rows_per_req * K * 8 + stage;
     hipLaunchKernelGGL(k_tree_select_static, dim3(B), dim3(kSelectThreads), smem, s, ws, rows_per_req, K, br,
                        root_token, T_max, draft_tokens, parents, tree_size, node_score, status);
   }
