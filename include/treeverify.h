@@ -160,7 +160,7 @@ int tree_mask_positions(int B, int T_max, int dcap, const int* parents,
  * whose prefix does not fit the cache (prefix_len < 0 or prefix_len + T_b >
  * S_cap) reads no K/V and gets O rows 0..T_b-1 set to zero (status is read,
  * never written, by this call).
- * Requires d in {64, 128}, Hq % Hkv == 0, Hq/Hkv <= 16, T_max <= 64,
+ * Requires d in {64, 128}, Hq % Hkv == 0 (any group size), T_max <= 64,
  * S_cap <= 2^30.  Every buffer must be allocated to its full layout size: rows
  * past a request's keys or nodes may be read, but their contents (any bits,
  * NaN included) never reach the output.

@@ -201,3 +201,12 @@ def test_nan_in_unused_cache_rows_and_query_slots():
         w.Vc[b, :, n:, :] = nan_bf16
         w.Q[b, int(w.given_size[b]):] = nan_bf16
     run(w)
+
+
+@pytest.mark.parametrize("Hq,Hkv,d", [(8, 8, 128), (32, 2, 128), (64, 2, 64), (16, 1, 64)])
+def test_gqa_group_sizes(Hq, Hkv, d):
+    # plain multi-head (1 query head per kv head) up to 32 and 16 query heads per
+    # kv head: the (node, head-in-group) rows of one kv head span 1 to 32 row blocks
+    w = gen.make_custom(cfg_id=910 + Hq // Hkv + d, B=3, P=[700, 1500, 64], mode="given", given_sizes=[64, 23, 41],
+                        Hq=Hq, Hkv=Hkv, d=d, given_depth=7)
+    run(w)
