@@ -210,3 +210,44 @@ def test_gqa_group_sizes(Hq, Hkv, d):
     w = gen.make_custom(cfg_id=910 + Hq // Hkv + d, B=3, P=[700, 1500, 64], mode="given", given_sizes=[64, 23, 41],
                         Hq=Hq, Hkv=Hkv, d=d, given_depth=7)
     run(w)
+
+
+def test_kv_compact_several_layers_with_padded_layer_stride():
+    # three layers whose slabs are 64 elements apart beyond their own size; paths
+    # with an aliasing source (row P+2 is read for k=1 and written for k=2), an
+    # empty acceptance and a longer path.  Every byte of the buffers (padding
+    # included) must match the definition applied layer by layer.
+    import torch
+    from oracle import kv as okv
+    from tree_attention_verification_amd import _lib
+    n_layers, B, Hkv, S_cap, d, dcap = 3, 3, 2, 100, 64, 7
+    per_layer = B * Hkv * S_cap * d
+    stride = per_layer + 64
+    rng = np.random.default_rng(1234)
+    K0 = rng.integers(0, 2 ** 16, size=n_layers * stride, dtype=np.uint16)
+    V0 = rng.integers(0, 2 ** 16, size=n_layers * stride, dtype=np.uint16)
+    prefix = np.array([10, 20, 40], np.int32)
+    paths = np.full((B, dcap + 1), -1, np.int32)
+    paths[0, :3] = [0, 2, 3]
+    paths[1, :1] = [0]
+    paths[2, :4] = [0, 1, 4, 9]
+    lens = np.array([2, 0, 3], np.int32)
+    dev = "cuda"
+    Kt = torch.from_numpy(K0.view(np.int16).copy()).to(dev)
+    Vt = torch.from_numpy(V0.view(np.int16).copy()).to(dev)
+    newlen = torch.full((B,), -7, dtype=torch.int32, device=dev)
+    _lib.kv_compact(B, n_layers, Hkv, d, 2, Kt, Vt, S_cap, stride, torch.from_numpy(prefix).to(dev),
+                    torch.from_numpy(paths).to(dev), torch.from_numpy(lens).to(dev), dcap, newlen)
+    torch.cuda.synchronize()
+    Kg = Kt.cpu().numpy().view(np.uint16)
+    Vg = Vt.cpu().numpy().view(np.uint16)
+
+    def layered(x):
+        return np.stack([x[l * stride:l * stride + per_layer].reshape(B, Hkv, S_cap, d) for l in range(n_layers)])
+    Kr, Vr, nl = okv.kv_compact(layered(K0), layered(V0), prefix, paths, lens)
+    np.testing.assert_array_equal(layered(Kg), Kr)
+    np.testing.assert_array_equal(layered(Vg), Vr)
+    for l in range(n_layers):   # the padding between layers is untouched
+        np.testing.assert_array_equal(Kg[l * stride + per_layer:(l + 1) * stride], K0[l * stride + per_layer:(l + 1) * stride])
+        np.testing.assert_array_equal(Vg[l * stride + per_layer:(l + 1) * stride], V0[l * stride + per_layer:(l + 1) * stride])
+    np.testing.assert_array_equal(newlen.cpu().numpy(), nl)

@@ -462,7 +462,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_attn_bf16(
 // Merge split partials.  Split s left its normalised output o_s (fp16), its
 // running max m_s (log2 domain) and its row sum l_s; the result is
 // sum_s w_s o_s / sum_s w_s with w_s = exp2(m_s - max m) l_s.  Splits are read
-// eight at a time (all loads in flight together) and merged online.
+// sixteen at a time (all loads in flight together) and merged online.
 template <int D>
 __global__ __launch_bounds__(256) void k_attn_combine(const _Float16* __restrict__ ws_o,
                                                       const float* __restrict__ ws_ml,
@@ -474,7 +474,7 @@ __global__ __launch_bounds__(256) void k_attn_combine(const _Float16* __restrict
   typedef _Float16 h8 __attribute__((ext_vector_type(8)));
   constexpr int TPR = D / 8;          // threads per row, 8 outputs each
   constexpr int RPB = 256 / TPR;      // rows per block
-  constexpr int BATCH = 8;
+  constexpr int BATCH = 16;
   const int bg = blockIdx.x;
   const int b = bg / Hkv, g = bg % Hkv;
   const int rep = Hq / Hkv;
