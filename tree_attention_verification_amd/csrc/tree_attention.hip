@@ -200,8 +200,8 @@ __global__ __launch_bounds__(NW * 64, 1) void k_attn_bf16(
   // computed, so three tiles (96 KB at d = 128) are in flight per workgroup.  The
   // 64 lanes of one DMA instruction fill 1 KB of LDS in order, so the XOR swizzle
   // is applied on the global side: LDS slot (row, c) receives chunk c ^ swz(row).
-  // Requests are issued unconditionally (keys clamped to a valid row) so that
-  // every wavefront has the same count in flight and one vmcnt bound is exact.
+  // Only tiles inside the split are requested; the wait before tile t allows
+  // exactly the younger tiles that were requested (up to two) to stay in flight.
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform (LDS base goes to m0)
   auto dma_tile = [&](int kt0, int last_key, uint16_t* sk, uint16_t* sv) __attribute__((always_inline)) {
 #pragma unroll
@@ -231,9 +231,11 @@ __global__ __launch_bounds__(NW * 64, 1) void k_attn_bf16(
   }
   const uint32_t* mp = tree_mask + ((long long)b * T_max + i_row) * W;
   unsigned long long mrow = (unsigned long long)mp[0] | (W > 1 ? ((unsigned long long)mp[1] << 32) : 0ull);
+  // tiles of this split (known before the request's sizes: the split's chunk)
+  const int split_tiles = chunk_keys / KT;
   dma_tile(k_begin, (int)S_cap - 1, s_k0, s_v0);
-  dma_tile(k_begin + KT, (int)S_cap - 1, s_k1, s_v1);
-  dma_tile(k_begin + 2 * KT, (int)S_cap - 1, s_k2, s_v2);
+  if (split_tiles > 1) dma_tile(k_begin + KT, (int)S_cap - 1, s_k1, s_v1);
+  if (split_tiles > 2) dma_tile(k_begin + 2 * KT, (int)S_cap - 1, s_k2, s_v2);
 
   int T = tree_size[b];
   const int P = prefix_len[b];
@@ -271,10 +273,14 @@ __global__ __launch_bounds__(NW * 64, 1) void k_attn_bf16(
   // re-fetch lands after the first one (returns are in order); the one-off full
   // wait below covers it.
   bool refetched = false;
-  if (k_begin + 3 * KT > nkeys) {
-    if (k_begin + KT > nkeys) dma_tile(k_begin, nkeys - 1, s_k0, s_v0);
-    else if (k_begin + 2 * KT > nkeys) dma_tile(k_begin + KT, nkeys - 1, s_k1, s_v1);
-    else dma_tile(k_begin + 2 * KT, nkeys - 1, s_k2, s_v2);
+  if (k_begin + KT > nkeys) {
+    dma_tile(k_begin, nkeys - 1, s_k0, s_v0);
+    refetched = true;
+  } else if (n_tiles > 1 && k_begin + 2 * KT > nkeys) {
+    dma_tile(k_begin + KT, nkeys - 1, s_k1, s_v1);
+    refetched = true;
+  } else if (n_tiles > 2 && k_begin + 3 * KT > nkeys) {
+    dma_tile(k_begin + 2 * KT, nkeys - 1, s_k2, s_v2);
     refetched = true;
   }
   // padding query rows get a zero Q and no mask
@@ -403,13 +409,20 @@ __global__ __launch_bounds__(NW * 64, 1) void k_attn_bf16(
 
   if (refetched) __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
   // step t: wait for this wavefront's part of tile t (tiles t+1, t+2 may still be
-  // in flight), barrier (every part landed, and every wavefront is done with tile
-  // t-1), request tile t+3 into tile t-1's buffer, compute tile t.
+  // in flight, when they exist), barrier (every part landed, and every wavefront
+  // is done with tile t-1), request tile t+3 (when it exists) into tile t-1's
+  // buffer, compute tile t.  Tiles past the split's last tile are never
+  // requested, so nothing is left in flight at the end.  (Tiles requested in the
+  // prologue for a split that turned out shorter are older than tile t and are
+  // covered by the same bound.)
   auto tile_step = [&](int t, const uint16_t* sk, const uint16_t* sv, uint16_t* nk, uint16_t* nv) __attribute__((always_inline)) {
     const int kt0 = k_begin + t * KT;
-    __builtin_amdgcn_s_waitcnt(vm_wait_imm(2 * DMA_WAVE));
+    const int younger = min(n_tiles - 1 - t, 2);
+    if (younger >= 2) __builtin_amdgcn_s_waitcnt(vm_wait_imm(2 * DMA_WAVE));
+    else if (younger == 1) __builtin_amdgcn_s_waitcnt(vm_wait_imm(DMA_WAVE));
+    else __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
     lds_barrier();
-    dma_tile(kt0 + 3 * KT, nkeys - 1, nk, nv);
+    if (t + 3 < n_tiles) dma_tile(kt0 + 3 * KT, nkeys - 1, nk, nv);
     if (active) compute_tile(kt0, sk, sv);
   };
   for (int t = 0; t < n_tiles; t += NSTAGE) {
@@ -418,7 +431,6 @@ __global__ __launch_bounds__(NW * 64, 1) void k_attn_bf16(
     if (t + 2 < n_tiles) tile_step(t + 2, s_k2, s_v2, s_k1, s_v1);
     if (t + 3 < n_tiles) tile_step(t + 3, s_k3, s_v3, s_k2, s_v2);
   }
-  __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));  // the requests past the last tile
 
   // ---- epilogue
   const float l_tot = l_part + __shfl_xor(l_part, 32, 64);
