@@ -80,7 +80,7 @@ inline BuildWs build_ws(void* base, long long rows, int K, int S) {
 // chunks per row, the chunk lists are staged in s_stage and merged by groups of
 // G lanes (G = S rounded up to a power of two, one lane per chunk list): K
 // rounds of a DPP group maximum over the list heads; the winning lane moves to
-// its next key (already in a register) and prefetches the one after.
+// its next key (already in a register) and prefetches two ahead.
 template <int G>
 __device__ void merge_chunk_lists(const unsigned long long* s_stage, int R, int K, int S,
                                   unsigned long long* s_key) {
@@ -89,16 +89,20 @@ __device__ void merge_chunk_lists(const unsigned long long* s_stage, int R, int 
     const int row = row0 + tid / G;
     const bool live = row < R && c < S;
     const unsigned long long* lst = s_stage + ((long long)row * S + c) * K;
+    // the head and the next two keys of this lane's list are in registers, so
+    // the LDS read a win triggers is not needed before the round after next
     unsigned long long head = live ? lst[0] : 0ull;
-    unsigned long long next = live && K > 1 ? lst[1] : 0ull;
-    int ptr = 1;  // index of `next`
+    unsigned long long n1 = live && K > 1 ? lst[1] : 0ull;
+    unsigned long long n2 = live && K > 2 ? lst[2] : 0ull;
+    int ptr = 2;  // index of n2
     for (int k = 0; k < K; ++k) {
       const unsigned long long best = group_max_u64<G>(head);
       if (row < R && c == 0) s_key[row * K + k] = best;
       if (head == best && head != 0ull) {  // keys are unique: exactly one lane wins
-        head = next;
+        head = n1;
+        n1 = n2;
         ++ptr;
-        next = live && ptr < K ? lst[ptr] : 0ull;
+        n2 = live && ptr < K ? lst[ptr] : 0ull;
       }
     }
   }
