@@ -144,19 +144,12 @@ __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
 }
 
-// max / sum over aligned groups of 16 lanes (every lane gets the result)
+// max over aligned groups of 16 lanes (every lane gets the result)
 __device__ __forceinline__ uint32_t group16_max_u32(uint32_t v) {
   v = max(v, dpp_u32<0xB1>(v));
   v = max(v, dpp_u32<0x4E>(v));
   v = max(v, dpp_u32<0x141>(v));
   return max(v, dpp_u32<0x140>(v));
-}
-
-__device__ __forceinline__ uint32_t group16_sum_u32(uint32_t v) {
-  v += dpp_u32<0xB1>(v);
-  v += dpp_u32<0x4E>(v);
-  v += dpp_u32<0x141>(v);
-  return v + dpp_u32<0x140>(v);
 }
 
 // Unique 64-bit rank key of vocabulary entry idx whose order key is k32.
