@@ -113,8 +113,11 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 __device__ __forceinline__ bf16x2 as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2, v); }
 #define kOnes2 (bf16x2{(__bf16)1.0f, (__bf16)1.0f})
 
-__device__ __forceinline__ bf16x4 ds_read_tr16(const uint16_t* lds_ptr) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(const __attribute__((address_space(3))) uint16_t*)lds_ptr);
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+
+__device__ __forceinline__ bf16x4 ds_read_tr16(const lds_char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
 }
 
 // s_waitcnt immediate that waits for lgkmcnt == 0 only (gfx9 encoding: vmcnt bits
@@ -161,6 +164,8 @@ __global__ __launch_bounds__(NW * 64, 1) void k_attn_bf16(
   constexpr int DB = D / 32;         // 32-wide d blocks of the output
   constexpr int CH = D / 8;          // 16-byte chunks per K/V row
   constexpr int NSTAGE = 4;          // LDS tile buffers: three tiles in flight while one is computed
+  constexpr bool kPair = false;
+  constexpr int kAhead = 5;
   constexpr int INSTR = KT * CH / 64;  // 64-lane DMA instructions per tensor per tile
   static_assert(INSTR % NW == 0, "DMA instructions split evenly over the wavefronts");
   constexpr int DMA_WAVE = 2 * INSTR / NW;  // DMA instructions per wavefront per tile (K and V)
@@ -171,10 +176,12 @@ __global__ __launch_bounds__(NW * 64, 1) void k_attn_bf16(
   // a transpose read over the banks.
   auto kswz = [](int r) { return CH == 16 ? (r & 15) : ((r >> 1) & 7); };
   auto vswz = [](int r) { return CH == 16 ? 4 * (r & 3) : 2 * (r & 3); };
-  // one array per stage (not one indexed array): the compiler then knows which
-  // buffer each LDS read touches and does not wait for DMA into the others
-  __shared__ __attribute__((aligned(16))) uint16_t s_k0[KT * D], s_k1[KT * D], s_k2[KT * D], s_k3[KT * D];
-  __shared__ __attribute__((aligned(16))) uint16_t s_v0[KT * D], s_v1[KT * D], s_v2[KT * D], s_v3[KT * D];
+  // NSTAGE K tile buffers followed by NSTAGE V tile buffers (TB bytes each)
+  constexpr int ROWB = 2 * D;        // bytes per K/V row
+  constexpr int TB = KT * ROWB;      // bytes per tile buffer
+  __shared__ __attribute__((aligned(1024))) uint16_t s_kv[2 * NSTAGE * KT * D];
+  lds_char* const kv_lds = (lds_char*)(__attribute__((address_space(3))) uint16_t*)s_kv;
+  const uint32_t kv_base = lds_addr(s_kv);
 
   // ---- which (request, kv head, split, row block) this workgroup owns
   const int wg = blockIdx.x;
@@ -202,24 +209,25 @@ __global__ __launch_bounds__(NW * 64, 1) void k_attn_bf16(
   // Only tiles inside the split are requested; the wait before tile t allows
   // exactly the younger tiles that were requested (up to two) to stay in flight.
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform (LDS base goes to m0)
-  auto dma_tile = [&](int kt0, int last_key, uint16_t* sk, uint16_t* sv) __attribute__((always_inline)) {
+  auto dma_tile = [&](int kt0, int last_key, int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int ii = 0; ii < INSTR / NW; ++ii) {
       const int i = wave_u + ii * NW;
       const int idx = 64 * i + lane;
       const int row = idx / CH, cs = idx % CH;
       const long long key = min(kt0 + row, last_key);
-      dma16(Kb + key * D + 8 * (cs ^ kswz(row)), lds_addr(sk) + 1024u * i);
-      dma16(Vb + key * D + 8 * (cs ^ vswz(row)), lds_addr(sv) + 1024u * i);
+      dma16(Kb + key * D + 8 * (cs ^ kswz(row)), kv_base + buf * TB + 1024u * i);
+      dma16(Vb + key * D + 8 * (cs ^ vswz(row)), kv_base + (NSTAGE + buf) * TB + 1024u * i);
     }
   };
 
   // ---- first loads, issued before the request's tree size and prefix length are
-  // known (they only decide what is kept): this lane's Q row and packed mask row
-  // with the node clamped to T_max - 1, then the first three K/V tiles with keys
-  // clamped to the cache slab.  What lies past the request is neutralised below.
+  // known (they only decide what is kept): K/V tile 0 with keys clamped to the
+  // cache slab, then this lane's Q row and packed mask row with the node clamped
+  // to T_max - 1.  What lies past the request is neutralised below.
   const int r = row0 + wave * 32 + l32;
   const int i_row = min(r / rep, T_max - 1);
+  dma_tile(k_begin, (int)S_cap - 1, 0);
   bf16x8 qf[KSTEPS];
   {
     const int head = g * rep + r % rep;
@@ -230,11 +238,6 @@ __global__ __launch_bounds__(NW * 64, 1) void k_attn_bf16(
   }
   const uint32_t* mp = tree_mask + ((long long)b * T_max + i_row) * W;
   unsigned long long mrow = (unsigned long long)mp[0] | (W > 1 ? ((unsigned long long)mp[1] << 32) : 0ull);
-  // tiles of this split (known before the request's sizes: the split's chunk)
-  const int split_tiles = chunk_keys / KT;
-  dma_tile(k_begin, (int)S_cap - 1, s_k0, s_v0);
-  if (split_tiles > 1) dma_tile(k_begin + KT, (int)S_cap - 1, s_k1, s_v1);
-  if (split_tiles > 2) dma_tile(k_begin + 2 * KT, (int)S_cap - 1, s_k2, s_v2);
 
   int T = tree_size[b];
   const int P = prefix_len[b];
@@ -265,29 +268,28 @@ __global__ __launch_bounds__(NW * 64, 1) void k_attn_bf16(
   }
   const int k_end = min(nkeys, k_begin + chunk_keys);
   const int n_tiles = (k_end - k_begin + KT - 1) / KT;
-  // A first tile that reaches past the last key was fetched with keys clamped to
-  // the slab, so its rows past the request hold whatever the cache holds there:
-  // fetch it again with keys clamped to the last key (its scores there are masked
-  // to -inf, and finite V rows keep 0 * garbage out of the PV product).  The
-  // re-fetch lands after the first one (returns are in order); the one-off full
-  // wait below covers it.
-  bool refetched = false;
-  if (k_begin + KT > nkeys) {
-    dma_tile(k_begin, nkeys - 1, s_k0, s_v0);
-    refetched = true;
-  } else if (n_tiles > 1 && k_begin + 2 * KT > nkeys) {
-    dma_tile(k_begin + KT, nkeys - 1, s_k1, s_v1);
-    refetched = true;
-  } else if (n_tiles > 2 && k_begin + 3 * KT > nkeys) {
-    dma_tile(k_begin + 2 * KT, nkeys - 1, s_k2, s_v2);
-    refetched = true;
-  }
+  // A tile 0 that reaches past the last key was fetched with keys clamped to the
+  // slab, so its rows past the request hold whatever the cache holds there: fetch
+  // it again with keys clamped to the last key (its scores there are masked to
+  // -inf, and finite V rows keep 0 * garbage out of the PV product).  The re-fetch
+  // lands after the first one (returns are in order).
+  if (k_begin + KT > nkeys) dma_tile(k_begin, nkeys - 1, 0);
   // padding query rows get a zero Q and no mask
   if (r >= M) {
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) qf[kk] = as_bf16x8(u32x4{0, 0, 0, 0});
     mrow = 0ull;
   }
+  // Q and the mask row are needed now (the empty statement below reads them), so
+  // the compiler waits for its loads here; that wait counts every older vector
+  // memory operation, tile 0 included, and nothing younger is in flight yet.
+  // Tiles 1 and 2 follow, with the request's sizes known (keys clamped to the
+  // last key, only tiles of this split), so they need no re-fetch, and stay in
+  // flight while tile 0 is computed.
+  __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+  asm volatile("" ::"v"(qf[0]), "v"(qf[KSTEPS / 2]), "v"(qf[KSTEPS - 1]), "v"(mrow));
+  if (n_tiles > 1) dma_tile(k_begin + KT, nkeys - 1, 1);
+  if (n_tiles > 2) dma_tile(k_begin + 2 * KT, nkeys - 1, 2);
 
   f32x16 acc[DB];
 #pragma unroll
@@ -307,9 +309,21 @@ __global__ __launch_bounds__(NW * 64, 1) void k_attn_bf16(
   const bool active = row0 + wave * 32 < M;
   const int tg = lane >> 4, tj = lane & 15;
 
-  auto compute_tile = [&](int kt0, const uint16_t* sk, const uint16_t* sv) __attribute__((always_inline)) {
-    // S^T = K Q^T for two 32-key blocks
-    f32x16 s[2];
+  // LDS byte offsets of this lane's fragments, written so that everything except
+  // one XOR with a constant is an instruction immediate.  K: key row 32 kb + l32,
+  // chunk (h KSTEPS + kk) ^ kswz(l32) = u ^ kk with u = h KSTEPS ^ kswz(l32), so
+  // the offset is 32 kb ROWB + (ka ^ 16 kk).  V (transpose reads): key row
+  // 16 ks + 8 hr + r0, column 32 db + c0, chunk 4 db ^ (c0 / 8) ^ vswz(r0), so the
+  // offset is (16 ks + 8 hr) ROWB + (va ^ 64 db).
+  const uint32_t ka = l32 * ROWB + 16 * ((h * KSTEPS) ^ kswz(l32));
+  uint32_t va;
+  {
+    const int r0 = 4 * (tg >> 1) + (tj >> 2), c0 = 16 * (tg & 1) + 4 * (tj & 3);
+    va = r0 * ROWB + 16 * ((c0 >> 3) ^ vswz(r0)) + 2 * (c0 & 7);
+  }
+
+  // S^T = K Q^T for two 32-key blocks
+  auto qk = [&](int buf, f32x16 (&s)[2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -318,14 +332,24 @@ __global__ __launch_bounds__(NW * 64, 1) void k_attn_bf16(
     for (int kk = 0; kk < KSTEPS; ++kk) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const int krow = 32 * kb + l32;
-        const int c = h * KSTEPS + kk;
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sk[krow * D + ((c ^ kswz(krow)) * 8)]);
+        const bf16x8 a =
+            *reinterpret_cast<const lds_bf16x8*>(kv_lds + buf * TB + 32 * kb * ROWB + (ka ^ (16u * kk)));
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[kb], 0, 0, 0);
       }
     }
-    // tree mask (only tiles that reach past the prefix), branch-free: the lane's
-    // mask row is shifted once so that bit e stands for key kt0 + e
+    if constexpr (kAhead > 0) {
+      __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * KSTEPS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i + kAhead < 2 * KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    }
+  };
+  // tree mask of the tile starting at key kt0 (only tiles that reach past the
+  // prefix), branch-free: the lane's mask row is shifted once so that bit e
+  // stands for key kt0 + e
+  auto mask = [&](int kt0, f32x16 (&s)[2]) __attribute__((always_inline)) {
     if (kt0 + KT > P) {
       const int sh = kt0 - P;  // key kt0+e is tree node sh+e
       const unsigned long long mt =
@@ -343,32 +367,31 @@ __global__ __launch_bounds__(NW * 64, 1) void k_attn_bf16(
           s[kb][v] = ((word >> (e & 31)) & 1u) ? s[kb][v] : -INFINITY;
         }
     }
+  };
+  // Online softmax without branches: tile max, running max raised only past the
+  // slack, exp2, P^T rounded to bf16 and its row sum (which adds exactly the
+  // rounded values, two per v_dot2).  Returns the factor the earlier
+  // accumulation must be scaled by (1 while the running max stays).
+  auto smax = [&](f32x16 (&s)[2], bf16x8 (&pt)[4]) __attribute__((always_inline)) -> float {
     float mx = s[0][0];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    {  // the other half of the row sits in lane l ^ 32 (a VALU lane swap, no LDS)
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
     const float tmax = mx * sl2;
     const bool need = tmax > m_run + kSlack;
-    if (__ballot(need)) {
-      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - tmax) : 1.0f;
-      if (need) m_run = tmax;
-      l_part *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[db][v] *= alpha;
-    }
+    const float alpha = need ? __builtin_amdgcn_exp2f(m_run - tmax) : 1.0f;
+    m_run = need ? tmax : m_run;
     const float mb = m_run == -INFINITY ? 0.0f : m_run;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) s[kb][v] = __builtin_amdgcn_exp2f(fmaf(s[kb][v], sl2, -mb));
-    // P is rounded to bf16 for the PV product; the row sum adds exactly those
-    // rounded values, two per v_dot2 (bf16 pair . (1, 1) + acc in fp32)
-    bf16x8 pt[4];
-    float lsum = l_part;
+    float lsum = l_part * alpha;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int kb = ks >> 1, o = 8 * (ks & 1);
@@ -382,13 +405,16 @@ __global__ __launch_bounds__(NW * 64, 1) void k_attn_bf16(
       for (int e = 0; e < 4; ++e) lsum = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w4[e]), kOnes2, lsum, false);
     }
     l_part = lsum;
-    // O^T += V^T P^T.  The A operand (32 d x 16 keys) comes from the row-major V
-    // tile through two transpose reads: in each 16-lane group, lane i receives
-    // element i%4 of the 8-byte pieces addressed by lanes i/4, i/4+4, i/4+8,
-    // i/4+12, so lane j of the group addresses key row base+j/4, columns
-    // 4*(j%4)..+3 of its 16-column slice and gets 4 consecutive keys of one d
-    // column.  Keys 16ks+8hr+4h+0..3 (hr = 0, 1) are exactly the runs the S^T
-    // accumulator holds for this lane, so P^T needs no shuffling.
+    return alpha;
+  };
+  // O^T += V^T P^T.  The A operand (32 d x 16 keys) comes from the row-major V
+  // tile through two transpose reads: in each 16-lane group, lane i receives
+  // element i%4 of the 8-byte pieces addressed by lanes i/4, i/4+4, i/4+8,
+  // i/4+12, so lane j of the group addresses key row base+j/4, columns
+  // 4*(j%4)..+3 of its 16-column slice and gets 4 consecutive keys of one d
+  // column.  Keys 16ks+8hr+4h+0..3 (hr = 0, 1) are exactly the runs the S^T
+  // accumulator holds for this lane, so P^T needs no shuffling.
+  auto pv = [&](int buf, const bf16x8 (&pt)[4]) __attribute__((always_inline)) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -396,17 +422,37 @@ __global__ __launch_bounds__(NW * 64, 1) void k_attn_bf16(
         bf16x4 half[2];
 #pragma unroll
         for (int hr = 0; hr < 2; ++hr) {
-          const int row = 16 * ks + 8 * hr + 4 * (tg >> 1) + (tj >> 2);
-          const int col = 32 * db + 16 * (tg & 1) + 4 * (tj & 3);
-          half[hr] = ds_read_tr16(&sv[row * D + (((col >> 3) ^ vswz(row)) * 8) + (col & 7)]);
+          half[hr] = ds_read_tr16(kv_lds + (NSTAGE + buf) * TB + (16 * ks + 8 * hr) * ROWB + (va ^ (64u * db)));
         }
         const bf16x8 a = __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7);
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pt[ks], acc[db], 0, 0, 0);
       }
     }
+    if constexpr (kAhead > 0) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 0);
+#pragma unroll
+      for (int i = 0; i < 4 * DB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i + kAhead < 4 * DB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+    }
   };
 
-  if (refetched) __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+  auto compute = [&](int t, int buf) __attribute__((always_inline)) {
+    f32x16 s[2];
+    bf16x8 pt[4];
+    qk(buf, s);
+    mask(k_begin + t * KT, s);
+    const float alpha = smax(s, pt);
+    if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[db][v] *= alpha;
+    }
+    pv(buf, pt);
+  };
+  if constexpr (!kPair) {
   // step t: wait for this wavefront's part of tile t (tiles t+1, t+2 may still be
   // in flight, when they exist), barrier (every part landed, and every wavefront
   // is done with tile t-1), request tile t+3 (when it exists) into tile t-1's
@@ -414,21 +460,41 @@ __global__ __launch_bounds__(NW * 64, 1) void k_attn_bf16(
   // requested, so nothing is left in flight at the end.  (Tiles requested in the
   // prologue for a split that turned out shorter are older than tile t and are
   // covered by the same bound.)
-  auto tile_step = [&](int t, const uint16_t* sk, const uint16_t* sv, uint16_t* nk, uint16_t* nv) __attribute__((always_inline)) {
-    const int kt0 = k_begin + t * KT;
+  auto step = [&](int t, int buf) __attribute__((always_inline)) {
     const int younger = min(n_tiles - 1 - t, 2);
     if (younger >= 2) __builtin_amdgcn_s_waitcnt(vm_wait_imm(2 * DMA_WAVE));
     else if (younger == 1) __builtin_amdgcn_s_waitcnt(vm_wait_imm(DMA_WAVE));
     else __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
     lds_barrier();
-    if (t + 3 < n_tiles) dma_tile(kt0 + 3 * KT, nkeys - 1, nk, nv);
-    if (active) compute_tile(kt0, sk, sv);
+    if (t + 3 < n_tiles) dma_tile(k_begin + (t + 3) * KT, nkeys - 1, (buf + 3) % NSTAGE);
+    if (active) compute(t, buf);
   };
   for (int t = 0; t < n_tiles; t += NSTAGE) {
-    tile_step(t, s_k0, s_v0, s_k3, s_v3);
-    if (t + 1 < n_tiles) tile_step(t + 1, s_k1, s_v1, s_k0, s_v0);
-    if (t + 2 < n_tiles) tile_step(t + 2, s_k2, s_v2, s_k1, s_v1);
-    if (t + 3 < n_tiles) tile_step(t + 3, s_k3, s_v3, s_k2, s_v2);
+    step(t, 0);
+    if (t + 1 < n_tiles) step(t + 1, 1);
+    if (t + 2 < n_tiles) step(t + 2, 2);
+    if (t + 3 < n_tiles) step(t + 3, 3);
+  }
+  } else {
+  // one barrier per pair of tiles t, t+1 (t even): wait for this wavefront's
+  // parts of both (only the prologue's tile 2 may stay in flight), barrier, then
+  // request tiles t+2 and t+3 into the buffers of tiles t-2 and t-1 (tile 2 came
+  // with the prologue) and compute the pair.
+  auto step2 = [&](int t, int buf) __attribute__((always_inline)) {
+    if (t == 0 && n_tiles > 2) __builtin_amdgcn_s_waitcnt(vm_wait_imm(DMA_WAVE));
+    else __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+    lds_barrier();
+    if (t > 0 && t + 2 < n_tiles) dma_tile(k_begin + (t + 2) * KT, nkeys - 1, (buf + 2) % NSTAGE);
+    if (t + 3 < n_tiles) dma_tile(k_begin + (t + 3) * KT, nkeys - 1, (buf + 3) % NSTAGE);
+    if (active) {
+      compute(t, buf);
+      if (t + 1 < n_tiles) compute(t + 1, buf + 1);
+    }
+  };
+  for (int t = 0; t < n_tiles; t += NSTAGE) {
+    step2(t, 0);
+    if (t + 2 < n_tiles) step2(t + 2, 2);
+  }
   }
 
   // ---- epilogue
