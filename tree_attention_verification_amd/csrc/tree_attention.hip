@@ -164,8 +164,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_attn_bf16(
   constexpr int DB = D / 32;         // 32-wide d blocks of the output
   constexpr int CH = D / 8;          // 16-byte chunks per K/V row
   constexpr int NSTAGE = 4;          // LDS tile buffers: three tiles in flight while one is computed
-  constexpr bool kPair = false;
-  constexpr int kAhead = 5;
+  constexpr int kAhead = 5;         // LDS fragment reads issued ahead of the MFMAs that use them
   constexpr int INSTR = KT * CH / 64;  // 64-lane DMA instructions per tensor per tile
   static_assert(INSTR % NW == 0, "DMA instructions split evenly over the wavefronts");
   constexpr int DMA_WAVE = 2 * INSTR / NW;  // DMA instructions per wavefront per tile (K and V)
@@ -337,6 +336,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_attn_bf16(
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[kb], 0, 0, 0);
       }
     }
+    // schedule: kAhead K fragment reads first, then one MFMA and one read at a time
     if constexpr (kAhead > 0) {
       __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
 #pragma unroll
@@ -428,6 +428,8 @@ __global__ __launch_bounds__(NW * 64, 1) void k_attn_bf16(
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pt[ks], acc[db], 0, 0, 0);
       }
     }
+    // schedule: the two transpose reads of kAhead MFMAs first, then one MFMA and
+    // its two reads at a time
     if constexpr (kAhead > 0) {
       __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 0);
 #pragma unroll
@@ -452,14 +454,11 @@ __global__ __launch_bounds__(NW * 64, 1) void k_attn_bf16(
     }
     pv(buf, pt);
   };
-  if constexpr (!kPair) {
   // step t: wait for this wavefront's part of tile t (tiles t+1, t+2 may still be
   // in flight, when they exist), barrier (every part landed, and every wavefront
   // is done with tile t-1), request tile t+3 (when it exists) into tile t-1's
-  // buffer, compute tile t.  Tiles past the split's last tile are never
-  // requested, so nothing is left in flight at the end.  (Tiles requested in the
-  // prologue for a split that turned out shorter are older than tile t and are
-  // covered by the same bound.)
+  // buffer, compute tile t.  Tiles past the request's last tile in this split
+  // are never requested, so nothing is left in flight at the end.
   auto step = [&](int t, int buf) __attribute__((always_inline)) {
     const int younger = min(n_tiles - 1 - t, 2);
     if (younger >= 2) __builtin_amdgcn_s_waitcnt(vm_wait_imm(2 * DMA_WAVE));
@@ -474,27 +473,6 @@ __global__ __launch_bounds__(NW * 64, 1) void k_attn_bf16(
     if (t + 1 < n_tiles) step(t + 1, 1);
     if (t + 2 < n_tiles) step(t + 2, 2);
     if (t + 3 < n_tiles) step(t + 3, 3);
-  }
-  } else {
-  // one barrier per pair of tiles t, t+1 (t even): wait for this wavefront's
-  // parts of both (only the prologue's tile 2 may stay in flight), barrier, then
-  // request tiles t+2 and t+3 into the buffers of tiles t-2 and t-1 (tile 2 came
-  // with the prologue) and compute the pair.
-  auto step2 = [&](int t, int buf) __attribute__((always_inline)) {
-    if (t == 0 && n_tiles > 2) __builtin_amdgcn_s_waitcnt(vm_wait_imm(DMA_WAVE));
-    else __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
-    lds_barrier();
-    if (t > 0 && t + 2 < n_tiles) dma_tile(k_begin + (t + 2) * KT, nkeys - 1, (buf + 2) % NSTAGE);
-    if (t + 3 < n_tiles) dma_tile(k_begin + (t + 3) * KT, nkeys - 1, (buf + 3) % NSTAGE);
-    if (active) {
-      compute(t, buf);
-      if (t + 1 < n_tiles) compute(t + 1, buf + 1);
-    }
-  };
-  for (int t = 0; t < n_tiles; t += NSTAGE) {
-    step2(t, 0);
-    if (t + 2 < n_tiles) step2(t + 2, 2);
-  }
   }
 
   // ---- epilogue
