@@ -139,6 +139,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches only")
+    ap.add_argument("--unfused", action="store_true",
+                    help="run the step as the five separate calls (default: tree_build_meta, tree_attention, "
+                         "tree_accept_compact -- the same five stages in two kernel launches fewer)")
     ap.add_argument("--copy-mb", type=float, default=0.0,
                     help="before warmup, one device-to-device copy of this many MiB (a plain copy kernel of known "
                          "size that calibrates the HBM byte counters of a profiler run)")
@@ -185,15 +188,21 @@ def main():
 
     def one(k, ev=None):
         step.copy = k % n_copies
-        step.build()
-        step.meta()
+        if args.unfused:
+            step.build()
+            step.meta()
+        else:
+            step.build_meta()
         if ev is not None:
             ev[0].record(stream)
         step.attention()
         if ev is not None:
             ev[1].record(stream)
-        step.accept()
-        step.compact()
+        if args.unfused:
+            step.accept()
+            step.compact()
+        else:
+            step.accept_compact()
 
     # eager launches, with HIP events around the attention call of every step
     for k in range(args.warmup):
@@ -287,7 +296,9 @@ def main():
         "config": {"workload": w.name, "batch": w.B, "prefix_len": [int(x) for x in w.prefix_len[:4]] +
                    (["..."] if w.B > 4 else []), "tree_nodes_per_step": nodes, "top_k": w.K, "depth": w.D,
                    "total_tokens": w.total_tokens, "Hq": w.Hq, "Hkv": w.Hkv, "head_dim": w.d, "vocab": w.V,
-                   "input_copies_rotated": n_copies, "launch": launch},
+                   "input_copies_rotated": n_copies, "launch": launch,
+                   "calls": ("tree_build, tree_mask_positions, tree_attention, tree_accept, kv_compact"
+                             if args.unfused else "tree_build_meta, tree_attention, tree_accept_compact")},
         "stages_us": stages,
         "roofline": roof,
     }

@@ -4,11 +4,13 @@
  *
  * One verification step is five calls, in this order:
  *   tree_build          draft log-probs  -> draft_tokens, parents, tree_size
+ *   (tree_build_meta    tree_build and tree_mask_positions in tree_build's launches)
  *   tree_mask_positions parents          -> packed ancestor mask, positions,
  *                                           retrieve_indices, child/sibling lists
  *   tree_attention      Q, K/V cache, mask -> O (every node over prefix + ancestors)
  *   tree_accept         target argmax per node -> accepted path, bonus token
  *   kv_compact          accepted path    -> K/V rows moved to contiguous slots
+ *   tree_accept_compact the last two in one launch
  *
  * Sources for what each call computes (cited by page title and section):
  *   [E2]  EAGLE v2 dynamic-tree decoding walkthrough -- section 2 initialize_tree
@@ -144,6 +146,27 @@ int tree_mask_positions(int B, int T_max, int dcap, const int* parents,
                         const int* status_in /* nullable */, int* status_out, void* stream);
 
 /* ------------------------------------------------------------------------- *
+ * tree_build_meta -- tree_build followed by tree_mask_positions on its output,
+ * in the launches of tree_build alone.  Arguments: those of tree_build, then
+ * dcap, prefix_len and the outputs of tree_mask_positions (status is both the
+ * build's status and the metadata's status_out).  Results equal tree_build then
+ * tree_mask_positions(status_in = status_out = status) on the same inputs, and
+ * the checks of both calls apply.  For a step that runs both calls back to
+ * back: the build's last kernel, which holds the new tree on chip, writes the
+ * metadata too, which saves one kernel boundary.
+ * ------------------------------------------------------------------------- */
+int tree_build_meta(int mode, int B, int V, int K, int D, int total_tokens,
+                    const int* branching /* host */, int n_levels,
+                    const float* logprobs, int rows_per_req, const int* root_token,
+                    int T_max, int* draft_tokens, int* parents, int* tree_size,
+                    float* node_score /* nullable */, int* status,
+                    void* workspace, size_t ws_bytes, int dcap, const int* prefix_len,
+                    uint32_t* tree_mask, int* tree_position_ids, int* positions,
+                    int* retrieve_indices, int* leaf_count,
+                    int* first_child /* nullable */, int* next_sibling /* nullable */,
+                    void* stream);
+
+/* ------------------------------------------------------------------------- *
  * tree_attention -- [HB] forward_with_mask (full mask = all-visible prefix
  * columns followed by the tree mask; grouped KV heads repeated over the query
  * heads; default softmax scale), [E2] section 4 tree_decoding.
@@ -210,6 +233,22 @@ int kv_compact(int B, int n_layers, int Hkv, int d, int elem_bytes, void* Kc, vo
                long long S_cap, long long layer_stride_elems, const int* prefix_len,
                const int* accept_path, const int* accept_len, int dcap,
                int* new_prefix_len /* nullable */, void* stream);
+
+/* ------------------------------------------------------------------------- *
+ * tree_accept_compact -- tree_accept followed by kv_compact, in one launch.
+ * Same arguments, outputs and checks as the two calls (tree_accept's first,
+ * then kv_compact's; accept_path and accept_len are outputs here, and the walk
+ * is taken from draft_tokens/parents/target_predict directly).  Results equal
+ * tree_accept then kv_compact on the same inputs.  For a step that runs both
+ * calls back to back: each (request, kv head, layer) workgroup repeats the
+ * request's walk, which saves one kernel boundary.
+ * ------------------------------------------------------------------------- */
+int tree_accept_compact(int B, int T_max, int dcap, const int* draft_tokens, const int* parents,
+                        const int* tree_size, const int* target_predict, const int* status,
+                        int* accept_len, int* accept_path, int* bonus_token, int n_layers, int Hkv,
+                        int d, int elem_bytes, void* Kc, void* Vc, long long S_cap,
+                        long long layer_stride_elems, const int* prefix_len,
+                        int* new_prefix_len /* nullable */, void* stream);
 
 /* human-readable names for return codes and status codes */
 const char* tv_error_string(int code);

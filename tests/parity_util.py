@@ -27,9 +27,9 @@ def oracle_tree(w):
     return ot.tree_build(w)
 
 
-def check_tree(gpu, ref, w):
-    B = w.B
-    np.testing.assert_array_equal(gpu["status"], ref["status"])
+def check_tree(gpu, ref, w, with_status=True):
+    if with_status:
+        np.testing.assert_array_equal(gpu["status"], ref["status"])
     np.testing.assert_array_equal(gpu["tree_size"], ref["tree_size"])
     np.testing.assert_array_equal(gpu["draft_tokens"], ref["draft_tokens"])
     np.testing.assert_array_equal(gpu["parents"], ref["parents"])
@@ -65,24 +65,31 @@ def check_attention(o_gpu, o_ref, w, tree_size, status, label=""):
     return float(err), 0.0
 
 
-def run_pipeline_and_compare(w, *, attention="full", samples=64, seed=0):
+def run_pipeline_and_compare(w, *, attention="full", samples=64, seed=0, fused=False):
     """Full pass on the GPU, each stage checked against the oracle.
 
     attention: 'full' compares every written row with the dense oracle; 'sampled'
-    compares `samples` random rows (b, i, h) computed one by one by the oracle."""
+    compares `samples` random rows (b, i, h) computed one by one by the oracle.
+    fused: run the step as tree_build_meta, tree_attention, tree_accept_compact
+    (the same stages, checked against the same oracle results)."""
     import torch
     from tree_attention_verification_amd.step import TreeVerifyStep
 
     step = TreeVerifyStep(w)
-    # 1. tree build
-    step.build()
+    # 1. tree build (with the metadata when fused)
+    if fused:
+        step.build_meta()
+    else:
+        step.build()
     torch.cuda.synchronize()
     ref_tree = oracle_tree(w)
     if w.mode != "given":
-        check_tree(step.tree_host(), ref_tree, w)
+        # fused, the status array already holds the metadata's status (checked below)
+        check_tree(step.tree_host(), ref_tree, w, with_status=not fused)
     # 2. mask / positions
-    step.meta()
-    torch.cuda.synchronize()
+    if not fused:
+        step.meta()
+        torch.cuda.synchronize()
     ref_meta = ot.tree_mask_positions(ref_tree["parents"], ref_tree["tree_size"], w.prefix_len, w.T_max, w.dcap,
                                       ref_tree["status"] if w.mode != "given" else None)
     check_meta(step.meta_host(), ref_meta)
@@ -120,15 +127,19 @@ def run_pipeline_and_compare(w, *, attention="full", samples=64, seed=0):
     # 4. acceptance, with the synthetic target read off the oracle's tree
     tp = gen.synthetic_target_predict(w, ref_tree["draft_tokens"], ref_tree["parents"], ref_tree["tree_size"])
     step.set_target_predict(tp)
-    step.accept()
+    if fused:
+        step.accept_compact()
+    else:
+        step.accept()
     torch.cuda.synchronize()
     ref_acc = ot.tree_accept(ref_tree["draft_tokens"], ref_tree["parents"], ref_tree["tree_size"], tp, status, w.dcap)
     got = step.accept_host()
     for k in ("accept_len", "accept_path", "bonus_token"):
         np.testing.assert_array_equal(got[k], ref_acc[k], err_msg=k)
-    # 5. compaction of the whole K/V buffer
-    step.compact()
-    torch.cuda.synchronize()
+    # 5. compaction of the whole K/V buffer (done above when fused)
+    if not fused:
+        step.compact()
+        torch.cuda.synchronize()
     K2, V2, newlen = okv.kv_compact(w.Kc, w.Vc, w.prefix_len, ref_acc["accept_path"], ref_acc["accept_len"])
     kg, vg = step.kv_host()
     np.testing.assert_array_equal(step.accept_host()["new_prefix_len"], newlen)

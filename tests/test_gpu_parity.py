@@ -251,3 +251,37 @@ def test_kv_compact_several_layers_with_padded_layer_stride():
         np.testing.assert_array_equal(Kg[l * stride + per_layer:(l + 1) * stride], K0[l * stride + per_layer:(l + 1) * stride])
         np.testing.assert_array_equal(Vg[l * stride + per_layer:(l + 1) * stride], V0[l * stride + per_layer:(l + 1) * stride])
     np.testing.assert_array_equal(newlen.cpu().numpy(), nl)
+
+
+# ----------------------------------------------------------------------------- fused entry points
+def _fused_cases():
+    return {
+        "cfg1-static-fp32": lambda: gen.make_workload(1),
+        "cfg2": lambda: gen.make_workload(2),
+        "cfg3-ragged": lambda: gen.make_workload(3),
+        "cfg5-reduced": lambda: gen.make_workload(5, batch=12, prefix=777),
+        "dynamic-K16": lambda: gen.make_custom(cfg_id=516, mode="dynamic", K=16, D=2, total_tokens=63, V=777,
+                                               P=70, Hq=4, Hkv=2, d=64, dtype="bf16"),
+        "dynamic-deeper-than-dcap": lambda: gen.make_custom(cfg_id=517, mode="dynamic", K=1, D=6, total_tokens=6,
+                                                            V=300, P=40, dcap=3, Hq=4, Hkv=2, d=64),
+        "static-chain-20": lambda: gen.make_custom(cfg_id=620, mode="static", branching=[1] * 20, V=1003, P=65,
+                                                   Hq=8, Hkv=4, d=128, dtype="bf16", dcap=20),
+        "static-deeper-than-dcap": lambda: gen.make_custom(cfg_id=621, mode="static", branching=[2, 2, 2], V=500,
+                                                           P=12, Hq=4, Hkv=2, d=64, dcap=2),
+        "given-trees": lambda: gen.make_custom(cfg_id=790, B=3, P=[5, 300, 64], mode="given",
+                                               given_sizes=[64, 17, 1], given_depth=7, T_max=64, dcap=8, Hq=8,
+                                               Hkv=2, d=128, dtype="bf16", V=50),
+    }
+
+
+@pytest.mark.parametrize("case", list(_fused_cases()))
+def test_fused_calls(case):
+    """tree_build_meta and tree_accept_compact give the oracle's results."""
+    run(_fused_cases()[case](), fused=True)
+
+
+def test_fused_bad_logprobs_status():
+    w = gen.make_custom(cfg_id=901, B=3, mode="dynamic", K=4, D=2, total_tokens=12, V=257, P=33, d=64)
+    w.logprobs[1, 3, 100] = 0.25
+    w.logprobs[2, 0, 5] = np.nan
+    run(w, fused=True)

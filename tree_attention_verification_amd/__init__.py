@@ -5,8 +5,8 @@ include/treeverify.h); `_lib` is the ctypes binding with the same call names and
 `step.TreeVerifyStep` holds one batch's device buffers and runs the five calls.
 """
 from . import _lib
-from ._lib import (tree_build, tree_build_workspace_bytes, tree_mask_positions, tree_attention,
-                   tree_attention_workspace_bytes, tree_accept, kv_compact, TVError)
+from ._lib import (tree_build, tree_build_workspace_bytes, tree_build_meta, tree_mask_positions, tree_attention,
+                   tree_attention_workspace_bytes, tree_accept, kv_compact, tree_accept_compact, TVError)
 
-__all__ = ["tree_build", "tree_build_workspace_bytes", "tree_mask_positions", "tree_attention",
-           "tree_attention_workspace_bytes", "tree_accept", "kv_compact", "TVError"]
+__all__ = ["tree_build", "tree_build_workspace_bytes", "tree_build_meta", "tree_mask_positions", "tree_attention",
+           "tree_attention_workspace_bytes", "tree_accept", "kv_compact", "tree_accept_compact", "TVError"]

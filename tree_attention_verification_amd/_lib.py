@@ -44,10 +44,12 @@ _SIGS = {
     "tree_build_workspace_bytes": (SZ, [I, I, I, I, I]),
     "tree_build": (I, [I, I, I, I, I, I, P, I, P, I, P, I, P, P, P, P, P, P, SZ, P]),
     "tree_mask_positions": (I, [I, I, I, P, P, P, P, P, P, P, P, P, P, P, P, P]),
+    "tree_build_meta": (I, [I, I, I, I, I, I, P, I, P, I, P, I, P, P, P, P, P, P, SZ, I, P, P, P, P, P, P, P, P, P]),
     "tree_attention_workspace_bytes": (SZ, [I, I, I, I, I, I, LL]),
     "tree_attention": (I, [I, I, I, I, I, I, P, P, P, LL, P, P, P, P, F, P, P, SZ, P]),
     "tree_accept": (I, [I, I, I, P, P, P, P, P, P, P, P, P]),
     "kv_compact": (I, [I, I, I, I, I, P, P, LL, LL, P, P, P, I, P, P]),
+    "tree_accept_compact": (I, [I, I, I, P, P, P, P, P, P, P, P, I, I, I, I, P, P, LL, LL, P, P, P]),
     "tv_error_string": (ctypes.c_char_p, [I]),
     "tv_status_string": (ctypes.c_char_p, [I]),
 }
@@ -132,6 +134,28 @@ def tree_build(mode, B, V, K, D, total_tokens, branching, logprobs, rows_per_req
     _check("tree_build", rc)
 
 
+def tree_build_meta(mode, B, V, K, D, total_tokens, branching, logprobs, rows_per_req, root_token, T_max,
+                    draft_tokens, parents, tree_size, node_score, status, workspace, dcap, prefix_len, tree_mask,
+                    tree_position_ids, positions, retrieve_indices, leaf_count, first_child, next_sibling,
+                    stream=None):
+    br = None
+    n_levels = 0
+    if branching:
+        n_levels = len(branching)
+        br = (ctypes.c_int * n_levels)(*[int(x) for x in branching])
+    wp, wn = _ws(workspace)
+    rc = lib().tree_build_meta(mode, B, V, K, D, total_tokens, br, n_levels, _dev(logprobs, "logprobs"),
+                               rows_per_req, _dev(root_token, "root_token"), T_max,
+                               _dev(draft_tokens, "draft_tokens"), _dev(parents, "parents"),
+                               _dev(tree_size, "tree_size"), _dev(node_score, "node_score"), _dev(status, "status"),
+                               wp, wn, dcap, _dev(prefix_len, "prefix_len"), _dev(tree_mask, "tree_mask"),
+                               _dev(tree_position_ids, "tree_position_ids"), _dev(positions, "positions"),
+                               _dev(retrieve_indices, "retrieve_indices"), _dev(leaf_count, "leaf_count"),
+                               _dev(first_child, "first_child"), _dev(next_sibling, "next_sibling"),
+                               _stream(stream))
+    _check("tree_build_meta", rc)
+
+
 def tree_mask_positions(B, T_max, dcap, parents, tree_size, prefix_len, tree_mask, tree_position_ids, positions,
                         retrieve_indices, leaf_count, first_child, next_sibling, status_in, status_out, stream=None):
     rc = lib().tree_mask_positions(B, T_max, dcap, _dev(parents, "parents"), _dev(tree_size, "tree_size"),
@@ -173,3 +197,16 @@ def kv_compact(B, n_layers, Hkv, d, elem_bytes, Kc, Vc, S_cap, layer_stride_elem
                           _dev(accept_len, "accept_len"), dcap, _dev(new_prefix_len, "new_prefix_len"),
                           _stream(stream))
     _check("kv_compact", rc)
+
+
+def tree_accept_compact(B, T_max, dcap, draft_tokens, parents, tree_size, target_predict, status, accept_len,
+                        accept_path, bonus_token, n_layers, Hkv, d, elem_bytes, Kc, Vc, S_cap, layer_stride_elems,
+                        prefix_len, new_prefix_len, stream=None):
+    rc = lib().tree_accept_compact(B, T_max, dcap, _dev(draft_tokens, "draft_tokens"), _dev(parents, "parents"),
+                                   _dev(tree_size, "tree_size"), _dev(target_predict, "target_predict"),
+                                   _dev(status, "status"), _dev(accept_len, "accept_len"),
+                                   _dev(accept_path, "accept_path"), _dev(bonus_token, "bonus_token"), n_layers, Hkv,
+                                   d, elem_bytes, _dev(Kc, "Kc"), _dev(Vc, "Vc"), S_cap, layer_stride_elems,
+                                   _dev(prefix_len, "prefix_len"), _dev(new_prefix_len, "new_prefix_len"),
+                                   _stream(stream))
+    _check("tree_accept_compact", rc)

@@ -21,13 +21,16 @@
 namespace tv {
 namespace {
 
-__global__ __launch_bounds__(64) void k_tree_accept(int T_max, int dcap, const int* __restrict__ draft_tokens,
-                                                    const int* __restrict__ parents,
-                                                    const int* __restrict__ tree_size,
-                                                    const int* __restrict__ target_predict,
-                                                    const int* __restrict__ status, int* __restrict__ accept_len,
-                                                    int* __restrict__ accept_path, int* __restrict__ bonus_token) {
-  const int b = blockIdx.x, c = threadIdx.x;
+struct Walk {
+  int len;    // accepted draft nodes past the root
+  int mine;   // path entry c for lane c <= len (entry 0 is the root), else -1
+  int bonus;  // the target's prediction at the last accepted node
+};
+
+// The walk of request b on one wavefront (lane c = node c, T_max <= 64).
+__device__ __forceinline__ Walk accept_walk(int b, int c, int T_max, int dcap, const int* __restrict__ draft_tokens,
+                                            const int* __restrict__ parents, const int* __restrict__ tree_size,
+                                            const int* __restrict__ target_predict, const int* __restrict__ status) {
   const long long ob = (long long)b * T_max;
   // every per-node value is fetched at once (lane c holds node c); the walk itself
   // then only moves data between lanes
@@ -49,35 +52,36 @@ __global__ __launch_bounds__(64) void k_tree_accept(int T_max, int dcap, const i
     ++len;
     if (c == len) mine = node;
   }
-  const int bonus = __builtin_amdgcn_readlane(pred_l, node);
-  if (c <= dcap) accept_path[(long long)b * (dcap + 1) + c] = mine;
+  return {len, mine, __builtin_amdgcn_readlane(pred_l, node)};
+}
+
+__global__ __launch_bounds__(64) void k_tree_accept(int T_max, int dcap, const int* __restrict__ draft_tokens,
+                                                    const int* __restrict__ parents,
+                                                    const int* __restrict__ tree_size,
+                                                    const int* __restrict__ target_predict,
+                                                    const int* __restrict__ status, int* __restrict__ accept_len,
+                                                    int* __restrict__ accept_path, int* __restrict__ bonus_token) {
+  const int b = blockIdx.x, c = threadIdx.x;
+  const Walk w = accept_walk(b, c, T_max, dcap, draft_tokens, parents, tree_size, target_predict, status);
+  if (c <= dcap) accept_path[(long long)b * (dcap + 1) + c] = w.mine;
   if (c == 0) {
-    accept_len[b] = len;
-    bonus_token[b] = bonus;
+    accept_len[b] = w.len;
+    bonus_token[b] = w.bonus;
   }
 }
 
 constexpr int kCompactThreads = 256;
 
-__global__ __launch_bounds__(kCompactThreads) void k_kv_compact(int B, int Hkv, int chunks16, uint4* __restrict__ Kc,
-                                                                uint4* __restrict__ Vc, long long S_cap,
-                                                                long long layer_stride16,
-                                                                const int* __restrict__ prefix_len,
-                                                                const int* __restrict__ accept_path,
-                                                                const int* __restrict__ accept_len, int dcap,
-                                                                int* __restrict__ new_prefix_len) {
-  const int g = blockIdx.x % Hkv;
-  const int b = blockIdx.x / Hkv;
-  const int layer = blockIdx.y;
+// Moves request b's accepted rows of one (kv head, layer).  The caller has
+// written s_path[0..dcap] (the first barrier here publishes it) and passes the
+// length L.
+__device__ __forceinline__ void compact_rows(int b, int g, int layer, int Hkv, int chunks16, uint4* __restrict__ Kc,
+                                             uint4* __restrict__ Vc, long long S_cap, long long layer_stride16,
+                                             int P, int L, const int* s_path, int dcap,
+                                             int* __restrict__ new_prefix_len) {
   const int tid = threadIdx.x;
-  // the request's prefix, length and path, read once (path entries by the first
-  // dcap + 1 threads, into LDS)
-  __shared__ int s_path[64];
   __shared__ int s_bad;
-  const int P = prefix_len[b];
-  const int L = accept_len[b];
   if (tid == 0) s_bad = 0;
-  if (tid <= dcap) s_path[tid] = accept_path[(long long)b * (dcap + 1) + tid];
   __syncthreads();
   // every source and destination row must lie inside the cache
   if (tid >= 1 && tid <= L && tid <= dcap) {
@@ -109,6 +113,58 @@ __global__ __launch_bounds__(kCompactThreads) void k_kv_compact(int B, int Hkv, 
     const int k = 1 + r / chunks16, c = r % chunks16;
     (t ? vb : kb)[((long long)P + k) * chunks16 + c] = s_stage[q];
   }
+}
+
+__global__ __launch_bounds__(kCompactThreads) void k_kv_compact(int Hkv, int chunks16, uint4* __restrict__ Kc,
+                                                                uint4* __restrict__ Vc, long long S_cap,
+                                                                long long layer_stride16,
+                                                                const int* __restrict__ prefix_len,
+                                                                const int* __restrict__ accept_path,
+                                                                const int* __restrict__ accept_len, int dcap,
+                                                                int* __restrict__ new_prefix_len) {
+  const int g = blockIdx.x % Hkv;
+  const int b = blockIdx.x / Hkv;
+  const int tid = threadIdx.x;
+  // the request's prefix, length and path, read once (path entries by the first
+  // dcap + 1 threads, into LDS)
+  __shared__ int s_path[64];
+  const int P = prefix_len[b];
+  const int L = accept_len[b];
+  if (tid <= dcap) s_path[tid] = accept_path[(long long)b * (dcap + 1) + tid];
+  compact_rows(b, g, blockIdx.y, Hkv, chunks16, Kc, Vc, S_cap, layer_stride16, P, L, s_path, dcap, new_prefix_len);
+}
+
+// tree_accept and kv_compact in one launch: every (request, kv head, layer)
+// workgroup runs the request's walk on its first wavefront (the walk reads a few
+// hundred bytes and is the same in every workgroup), the (request, 0, 0)
+// workgroup also writes the acceptance outputs, then the rows are moved.
+__global__ __launch_bounds__(kCompactThreads) void k_accept_compact(
+    int T_max, int dcap, const int* __restrict__ draft_tokens, const int* __restrict__ parents,
+    const int* __restrict__ tree_size, const int* __restrict__ target_predict, const int* __restrict__ status,
+    int* __restrict__ accept_len, int* __restrict__ accept_path, int* __restrict__ bonus_token, int Hkv,
+    int chunks16, uint4* __restrict__ Kc, uint4* __restrict__ Vc, long long S_cap, long long layer_stride16,
+    const int* __restrict__ prefix_len, int* __restrict__ new_prefix_len) {
+  const int g = blockIdx.x % Hkv;
+  const int b = blockIdx.x / Hkv;
+  const int tid = threadIdx.x;
+  __shared__ int s_path[64];
+  __shared__ int s_len;
+  const int P = prefix_len[b];
+  if (tid < 64) {
+    const Walk w = accept_walk(b, tid, T_max, dcap, draft_tokens, parents, tree_size, target_predict, status);
+    if (tid <= dcap) s_path[tid] = w.mine;
+    if (tid == 0) s_len = w.len;
+    if (g == 0 && blockIdx.y == 0) {
+      if (tid <= dcap) accept_path[(long long)b * (dcap + 1) + tid] = w.mine;
+      if (tid == 0) {
+        accept_len[b] = w.len;
+        bonus_token[b] = w.bonus;
+      }
+    }
+  }
+  __syncthreads();
+  compact_rows(b, g, blockIdx.y, Hkv, chunks16, Kc, Vc, S_cap, layer_stride16, P, s_len, s_path, dcap,
+               new_prefix_len);
 }
 
 }  // namespace
@@ -145,9 +201,42 @@ extern "C" int kv_compact(int B, int n_layers, int Hkv, int d, int elem_bytes, v
   const size_t stage = 2 * (size_t)dcap * (size_t)(row_bytes / 16) * 16;  // K and V rows of one path
   if (stage > 65536) return TV_EUNSUPPORTED;
   hipLaunchKernelGGL(tv::k_kv_compact, dim3(B * Hkv, n_layers), dim3(tv::kCompactThreads), stage,
-                     reinterpret_cast<hipStream_t>(stream), B, Hkv, chunks16, reinterpret_cast<uint4*>(Kc),
+                     reinterpret_cast<hipStream_t>(stream), Hkv, chunks16, reinterpret_cast<uint4*>(Kc),
                      reinterpret_cast<uint4*>(Vc), S_cap, layer_stride_elems * elem_bytes / 16, prefix_len,
                      accept_path, accept_len, dcap, new_prefix_len);
+  TV_CHECK_LAUNCH();
+  return TV_OK;
+}
+
+extern "C" int tree_accept_compact(int B, int T_max, int dcap, const int* draft_tokens, const int* parents,
+                                   const int* tree_size, const int* target_predict, const int* status,
+                                   int* accept_len, int* accept_path, int* bonus_token, int n_layers, int Hkv, int d,
+                                   int elem_bytes, void* Kc, void* Vc, long long S_cap, long long layer_stride_elems,
+                                   const int* prefix_len, int* new_prefix_len, void* stream) {
+  // the checks of tree_accept, then those of kv_compact
+  if (B <= 0 || T_max <= 0 || dcap < 0 || dcap >= T_max) return TV_EINVAL;
+  if (T_max > tv::kTMaxLimit) return TV_EUNSUPPORTED;
+  if (!draft_tokens || !parents || !tree_size || !target_predict || !status || !accept_len || !accept_path ||
+      !bonus_token)
+    return TV_EINVAL;
+  if (n_layers <= 0 || Hkv <= 0 || d <= 0 || S_cap <= 0) return TV_EINVAL;
+  if (elem_bytes != 2 && elem_bytes != 4) return TV_EINVAL;
+  if (!Kc || !Vc || !prefix_len) return TV_EINVAL;
+  const long long row_bytes = (long long)d * elem_bytes;
+  if (row_bytes % 16 != 0 || row_bytes > 1024) return TV_EUNSUPPORTED;
+  const long long per_layer = (long long)B * Hkv * S_cap * d;
+  if (n_layers > 1 && layer_stride_elems < per_layer) return TV_EINVAL;
+  if ((layer_stride_elems * elem_bytes) % 16 != 0) return TV_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(Kc) & 15) || (reinterpret_cast<uintptr_t>(Vc) & 15)) return TV_EINVAL;
+  if ((long long)B * Hkv > 2147483647LL || n_layers > 65535) return TV_EINVAL;
+  const int chunks16 = (int)(row_bytes / 16);
+  const size_t stage = 2 * (size_t)dcap * (size_t)(row_bytes / 16) * 16;
+  if (stage > 65536) return TV_EUNSUPPORTED;
+  hipLaunchKernelGGL(tv::k_accept_compact, dim3(B * Hkv, n_layers), dim3(tv::kCompactThreads), stage,
+                     reinterpret_cast<hipStream_t>(stream), T_max, dcap, draft_tokens, parents, tree_size,
+                     target_predict, status, accept_len, accept_path, bonus_token, Hkv, chunks16,
+                     reinterpret_cast<uint4*>(Kc), reinterpret_cast<uint4*>(Vc), S_cap,
+                     layer_stride_elems * elem_bytes / 16, prefix_len, new_prefix_len);
   TV_CHECK_LAUNCH();
   return TV_OK;
 }

@@ -18,7 +18,7 @@
 //                 the score range, then an exact rank inside the boundary
 //                 bucket) entirely in LDS, and writes the numbered tree.  Static
 //                 mode builds level by level instead.
-#include "tv_common.h"
+#include "tree_meta_body.h"
 
 namespace tv {
 namespace {
@@ -509,11 +509,13 @@ __device__ unsigned long long bucket_select_threshold(const int C, const int n, 
   return s_bcast[3];
 }
 
-template <int K>
+// With META, the first wavefront then also runs tree_mask_positions on the tree
+// just built (its parents taken from LDS), so the step saves a launch.
+template <int K, bool META>
 __global__ __launch_bounds__(kSelectThreads) void k_tree_select_dynamic(
     BuildWs ws, int R, int D, int total_tokens, const int* __restrict__ root_token, int T_max,
     int* __restrict__ draft_tokens, int* __restrict__ parents, int* __restrict__ tree_size,
-    float* __restrict__ node_score, int* __restrict__ status) {
+    float* __restrict__ node_score, int* __restrict__ status, MetaOut mo) {
   extern __shared__ unsigned char smem[];
   const int C = R * K;  // = K + D*K*K: candidate id == row*K + rank
   unsigned long long* s_key = reinterpret_cast<unsigned long long*>(smem);
@@ -530,6 +532,7 @@ __global__ __launch_bounds__(kSelectThreads) void k_tree_select_dynamic(
   __shared__ __attribute__((aligned(16))) unsigned long long s_cand[kKMax * kKMax + 16];
   __shared__ int s_tmp[kSelectThreads / 64];
   __shared__ int s_bad;
+  __shared__ int s_pn[META ? kTMaxLimit : 1];  // parent of each node (META)
 
   const int b = blockIdx.x, tid = threadIdx.x;
   if (tid == 0) s_bad = 0;
@@ -647,22 +650,34 @@ __global__ __launch_bounds__(kSelectThreads) void k_tree_select_dynamic(
     for (int id = tid; id < C; id += kSelectThreads) {
       const int n = s_node[id];
       if (n > 0) {
+        const int pn = s_par[id] < 0 ? 0 : s_node[s_par[id]];
         draft_tokens[ob + n] = (int)key_index(s_key[id]);
-        parents[ob + n] = s_par[id] < 0 ? 0 : s_node[s_par[id]];
+        parents[ob + n] = pn;
         if (node_score) node_score[ob + n] = s_sc[id];
+        if constexpr (META) s_pn[n] = pn;
       }
     }
   }
-  if (tid == 0) {
-    tree_size[b] = T;
-    status[b] = ok ? TV_ST_OK : TV_ST_LOGPROB;
+  if (tid == 0) tree_size[b] = T;
+  if constexpr (!META) {
+    if (tid == 0) status[b] = ok ? TV_ST_OK : TV_ST_LOGPROB;
+  } else {
+    __syncthreads();
+    if (tid < 64) {
+      int st = ok ? TV_ST_OK : TV_ST_LOGPROB, Tm = T;
+      const int P = mo.prefix_len[b];
+      const int p = check_tree(tid, T_max, st, Tm, (tid > 0 && tid < T) ? s_pn[tid] : -1);
+      meta_body(b, tid, T_max, mo.dcap, mo.W, Tm, st, p, P, mo.tree_mask, mo.tree_position_ids, mo.positions,
+                mo.retrieve_indices, mo.leaf_count, mo.first_child, mo.next_sibling, status);
+    }
   }
 }
 
+template <bool META>
 __global__ __launch_bounds__(kSelectThreads) void k_tree_select_static(
     BuildWs ws, int R, int K, Branching br, const int* __restrict__ root_token, int T_max,
     int* __restrict__ draft_tokens, int* __restrict__ parents, int* __restrict__ tree_size,
-    float* __restrict__ node_score, int* __restrict__ status) {
+    float* __restrict__ node_score, int* __restrict__ status, MetaOut mo) {
   extern __shared__ unsigned char smem[];
   unsigned long long* rk = reinterpret_cast<unsigned long long*>(smem);
   __shared__ int t_tok[kTMaxLimit], t_par[kTMaxLimit];
@@ -705,9 +720,17 @@ __global__ __launch_bounds__(kSelectThreads) void k_tree_select_static(
     parents[ob + i] = in ? t_par[i] : -1;
     if (node_score) node_score[ob + i] = i == 0 ? 0.0f : (in ? t_sc[i] : -INFINITY);
   }
-  if (tid == 0) {
-    tree_size[b] = T;
-    status[b] = ok ? TV_ST_OK : TV_ST_LOGPROB;
+  if (tid == 0) tree_size[b] = T;
+  if constexpr (!META) {
+    if (tid == 0) status[b] = ok ? TV_ST_OK : TV_ST_LOGPROB;
+  } else {
+    if (tid < 64) {  // t_par was published by the barrier after the levels
+      int st = ok ? TV_ST_OK : TV_ST_LOGPROB, Tm = T;
+      const int P = mo.prefix_len[b];
+      const int p = check_tree(tid, T_max, st, Tm, (tid > 0 && tid < T) ? t_par[tid] : -1);
+      meta_body(b, tid, T_max, mo.dcap, mo.W, Tm, st, p, P, mo.tree_mask, mo.tree_position_ids, mo.positions,
+                mo.retrieve_indices, mo.leaf_count, mo.first_child, mo.next_sibling, status);
+    }
   }
 }
 
@@ -721,10 +744,11 @@ extern "C" size_t tree_build_workspace_bytes(int mode, int B, int V, int K, int 
   return tv::build_ws_bytes((long long)B * rows_per_req, K, tv::pick_split(V, K, rows_per_req));
 }
 
-extern "C" int tree_build(int mode, int B, int V, int K, int D, int total_tokens, const int* branching,
-                          int n_levels, const float* logprobs, int rows_per_req, const int* root_token, int T_max,
-                          int* draft_tokens, int* parents, int* tree_size, float* node_score, int* status,
-                          void* workspace, size_t ws_bytes, void* stream) {
+namespace {
+int build_impl(int mode, int B, int V, int K, int D, int total_tokens, const int* branching, int n_levels,
+               const float* logprobs, int rows_per_req, const int* root_token, int T_max, int* draft_tokens,
+               int* parents, int* tree_size, float* node_score, int* status, void* workspace, size_t ws_bytes,
+               const tv::MetaOut* meta, void* stream) {
   using namespace tv;
   if (B <= 0 || V <= 0 || T_max <= 0 || rows_per_req <= 0) return TV_EINVAL;
   if (!logprobs || !root_token || !draft_tokens || !parents || !tree_size || !status) return TV_EINVAL;
@@ -781,8 +805,14 @@ extern "C" int tree_build(int mode, int B, int V, int K, int D, int total_tokens
     switch (K) {
 #define TV_SELECT_CASE(k)                                                                                          \
   case k:                                                                                                          \
-    hipLaunchKernelGGL(k_tree_select_dynamic<k>, dim3(B), dim3(kSelectThreads), smem, s, ws, rows_per_req, D,     \
-                       total_tokens, root_token, T_max, draft_tokens, parents, tree_size, node_score, status);     \
+    if (meta)                                                                                                      \
+      hipLaunchKernelGGL((k_tree_select_dynamic<k, true>), dim3(B), dim3(kSelectThreads), smem, s, ws,           \
+                         rows_per_req, D, total_tokens, root_token, T_max, draft_tokens, parents, tree_size,      \
+                         node_score, status, *meta);                                                               \
+    else                                                                                                           \
+      hipLaunchKernelGGL((k_tree_select_dynamic<k, false>), dim3(B), dim3(kSelectThreads), smem, s, ws,          \
+                         rows_per_req, D, total_tokens, root_token, T_max, draft_tokens, parents, tree_size,      \
+                         node_score, status, MetaOut{});                                                           \
     break;
       TV_SELECT_CASE(1) TV_SELECT_CASE(2) TV_SELECT_CASE(3) TV_SELECT_CASE(4) TV_SELECT_CASE(5) TV_SELECT_CASE(6)
       TV_SELECT_CASE(7) TV_SELECT_CASE(8) TV_SELECT_CASE(9) TV_SELECT_CASE(10) TV_SELECT_CASE(11)
@@ -792,9 +822,40 @@ extern "C" int tree_build(int mode, int B, int V, int K, int D, int total_tokens
     }
   } else {
     const size_t smem = (size_t)rows_per_req * K * 8 + stage;
-    hipLaunchKernelGGL(k_tree_select_static, dim3(B), dim3(kSelectThreads), smem, s, ws, rows_per_req, K, br,
-                       root_token, T_max, draft_tokens, parents, tree_size, node_score, status);
+    if (meta)
+      hipLaunchKernelGGL(k_tree_select_static<true>, dim3(B), dim3(kSelectThreads), smem, s, ws, rows_per_req, K,
+                         br, root_token, T_max, draft_tokens, parents, tree_size, node_score, status, *meta);
+    else
+      hipLaunchKernelGGL(k_tree_select_static<false>, dim3(B), dim3(kSelectThreads), smem, s, ws, rows_per_req, K,
+                         br, root_token, T_max, draft_tokens, parents, tree_size, node_score, status, MetaOut{});
   }
   TV_CHECK_LAUNCH();
   return TV_OK;
+}
+}  // namespace
+
+extern "C" int tree_build(int mode, int B, int V, int K, int D, int total_tokens, const int* branching,
+                          int n_levels, const float* logprobs, int rows_per_req, const int* root_token, int T_max,
+                          int* draft_tokens, int* parents, int* tree_size, float* node_score, int* status,
+                          void* workspace, size_t ws_bytes, void* stream) {
+  return build_impl(mode, B, V, K, D, total_tokens, branching, n_levels, logprobs, rows_per_req, root_token, T_max,
+                    draft_tokens, parents, tree_size, node_score, status, workspace, ws_bytes, nullptr, stream);
+}
+
+extern "C" int tree_build_meta(int mode, int B, int V, int K, int D, int total_tokens, const int* branching,
+                               int n_levels, const float* logprobs, int rows_per_req, const int* root_token,
+                               int T_max, int* draft_tokens, int* parents, int* tree_size, float* node_score,
+                               int* status, void* workspace, size_t ws_bytes, int dcap, const int* prefix_len,
+                               uint32_t* tree_mask, int* tree_position_ids, int* positions, int* retrieve_indices,
+                               int* leaf_count, int* first_child, int* next_sibling, void* stream) {
+  // the checks of tree_mask_positions (those of tree_build follow)
+  if (B <= 0 || T_max <= 0 || dcap < 0 || dcap >= T_max) return TV_EINVAL;
+  if (T_max > tv::kTMaxLimit) return TV_EUNSUPPORTED;
+  if (!prefix_len || !tree_mask || !tree_position_ids || !positions || !retrieve_indices || !leaf_count)
+    return TV_EINVAL;
+  if (B > 2147483647 / 64) return TV_EINVAL;
+  const tv::MetaOut mo{dcap, (T_max + 31) / 32, prefix_len, tree_mask, tree_position_ids, positions,
+                       retrieve_indices, leaf_count, first_child, next_sibling};
+  return build_impl(mode, B, V, K, D, total_tokens, branching, n_levels, logprobs, rows_per_req, root_token, T_max,
+                    draft_tokens, parents, tree_size, node_score, status, workspace, ws_bytes, &mo, stream);
 }

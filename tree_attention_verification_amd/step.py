@@ -135,8 +135,37 @@ class TreeVerifyStep:
         tv.kv_compact(self.B, 1, w.Hkv, w.d, self.elem_bytes, self.Kc[c], self.Vc[c], w.S_cap, 0, self.prefix_len,
                       self.accept_path, self.accept_len, self.dcap, self.new_prefix_len, stream)
 
-    def run(self, stream=None):
-        """One full pass of the step (target_predict must already be set)."""
+    def build_meta(self, stream=None):
+        """tree_build and tree_mask_positions in tree_build's launches."""
+        w = self.w
+        if w.mode == "given":
+            return self.meta(stream)
+        R = w.logprobs.shape[1]
+        tv.tree_build_meta(_MODES[w.mode], self.B, w.V, w.K, w.D, w.total_tokens,
+                           w.branching if w.mode == "static" else None, self.logprobs, R, self.root_token,
+                           self.T_max, self.draft_tokens, self.parents, self.tree_size, self.node_score, self.status,
+                           self.ws_build, self.dcap, self.prefix_len, self.tree_mask, self.tree_position_ids,
+                           self.positions, self.retrieve_indices, self.leaf_count, self.first_child,
+                           self.next_sibling, stream)
+
+    def accept_compact(self, stream=None, copy=None):
+        """tree_accept and kv_compact in one launch."""
+        w = self.w
+        c = self.copy if copy is None else copy
+        tv.tree_accept_compact(self.B, self.T_max, self.dcap, self.draft_tokens, self.parents, self.tree_size,
+                               self.target_predict, self.status, self.accept_len, self.accept_path,
+                               self.bonus_token, 1, w.Hkv, w.d, self.elem_bytes, self.Kc[c], self.Vc[c], w.S_cap, 0,
+                               self.prefix_len, self.new_prefix_len, stream)
+
+    def run(self, stream=None, fused=False):
+        """One full pass of the step (target_predict must already be set).  With
+        fused, the five calls run as tree_build_meta, tree_attention and
+        tree_accept_compact (same results, two kernel launches fewer)."""
+        if fused:
+            self.build_meta(stream)
+            self.attention(stream)
+            self.accept_compact(stream)
+            return
         self.build(stream)
         self.meta(stream)
         self.attention(stream)
