@@ -32,6 +32,9 @@ constexpr int kStageKeys = 6144;                         // chunk lists staged i
 static_assert(kTopkGroups >= kKMax, "the group-maximum bound needs at least K groups");
 constexpr int kCandCap = 2048;                           // LDS candidate buffer (8 B each)
 constexpr int kSelectThreads = 256;
+// row keys staged per thread by the select kernels' single load batch
+constexpr int kLoadBatch = 24;
+static_assert(kLoadBatch * kSelectThreads >= kStageKeys, "one batch stages every chunk list");
 constexpr int kMaxCand = 3072;   // LDS: 16 B per candidate
 constexpr int kMaxLevels = 64;
 
@@ -112,18 +115,18 @@ __device__ void load_row_keys(const BuildWs& ws, long long row_base, int R, int 
                               unsigned long long* s_stage, int* s_bad) {
   const int S = ws.S;
   const long long base = row_base * S * K;
-  // global -> LDS in batches of eight loads per thread, all in flight together
+  // global -> LDS, every load of the block in flight together (n <= 24 per thread)
   unsigned long long* dst = S == 1 ? s_key : s_stage;
   const int n = R * S * K;
-  for (int i0 = 0; i0 < n; i0 += 8 * kSelectThreads) {
-    unsigned long long v[8];
+  for (int i0 = 0; i0 < n; i0 += kLoadBatch * kSelectThreads) {
+    unsigned long long v[kLoadBatch];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < kLoadBatch; ++u) {
       const int i = i0 + u * kSelectThreads + threadIdx.x;
       v[u] = i < n ? ws.row_keys[base + i] : 0ull;
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < kLoadBatch; ++u) {
       const int i = i0 + u * kSelectThreads + threadIdx.x;
       if (i < n) dst[i] = v[u];
     }
@@ -150,6 +153,12 @@ __device__ __forceinline__ uint32_t group16_max_u32(uint32_t v) {
   v = max(v, dpp_u32<0x4E>(v));
   v = max(v, dpp_u32<0x141>(v));
   return max(v, dpp_u32<0x140>(v));
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = group16_max_u32(v);
+  return max(max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16)),
+             max((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
 }
 
 // Unique 64-bit rank key of vocabulary entry idx whose order key is k32.
@@ -423,7 +432,8 @@ __device__ unsigned long long radix_select_threshold(const int C, const int n, c
 // Threshold of the n best of the C candidates under (score desc, id asc):
 // returns tau such that exactly n of the unique keys rank_key(s_sc[id], id) are
 // >= tau.  One histogram of the 32-bit score keys over at most kBuckets
-// equal-width buckets of their range finds the bucket that holds the boundary;
+// equal-width buckets of their range [kmin, kmax] finds the bucket that holds
+// the boundary;
 // its members are ranked exactly by their 64-bit keys.  A boundary bucket with
 // more than kBucketRankMax members (heavy ties) falls back to the radix select.
 constexpr int kBucketBits = 10;
@@ -431,39 +441,16 @@ constexpr int kBuckets = 1 << kBucketBits;
 static_assert(kBuckets == 4 * kSelectThreads, "four buckets per thread in the boundary scan");
 constexpr int kBucketRankMax = 256;
 
-__device__ unsigned long long bucket_select_threshold(const int C, const int n, const float* s_sc, int* s_hist,
-                                                      short* s_mem, int* s_misc, uint32_t* s_red, int* s_tmp,
-                                                      unsigned long long* s_bcast, unsigned long long* s_tmp64) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  constexpr int kWaves = kSelectThreads / 64;
+__device__ unsigned long long bucket_select_threshold(const int C, const int n, const float* s_sc, uint32_t kmin,
+                                                      uint32_t kmax, int* s_hist, short* s_mem, int* s_misc,
+                                                      int* s_tmp, unsigned long long* s_bcast,
+                                                      unsigned long long* s_tmp64) {
+  const int tid = threadIdx.x;
   if (n <= 0) return ~0ull;  // nothing: no key reaches all-ones
   if (n >= C) return 0ull;
-  uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
-  for (int id = tid; id < C; id += kSelectThreads) {
-    const uint32_t k = order_key(s_sc[id]);
-    kmax = max(kmax, k);
-    kmin = min(kmin, k);
-  }
   for (int i = tid; i < kBuckets; i += kSelectThreads) s_hist[i] = 0;
-  {
-    const uint32_t a = group16_max_u32(kmax), n = group16_max_u32(~kmin);  // min = ~max(~x)
-    kmax = max(max((uint32_t)__builtin_amdgcn_readlane((int)a, 0), (uint32_t)__builtin_amdgcn_readlane((int)a, 16)),
-               max((uint32_t)__builtin_amdgcn_readlane((int)a, 32), (uint32_t)__builtin_amdgcn_readlane((int)a, 48)));
-    kmin = ~max(max((uint32_t)__builtin_amdgcn_readlane((int)n, 0), (uint32_t)__builtin_amdgcn_readlane((int)n, 16)),
-                max((uint32_t)__builtin_amdgcn_readlane((int)n, 32), (uint32_t)__builtin_amdgcn_readlane((int)n, 48)));
-  }
-  if (lane == 0) {
-    s_red[2 * wave] = kmax;
-    s_red[2 * wave + 1] = kmin;
-  }
   if (tid == 0) s_misc[1] = 0;
   __syncthreads();
-  kmax = s_red[0];
-  kmin = s_red[1];
-  for (int w = 1; w < kWaves; ++w) {
-    kmax = max(kmax, s_red[2 * w]);
-    kmin = min(kmin, s_red[2 * w + 1]);
-  }
   const uint32_t range = kmax - kmin;
   // buckets used: (range >> shift) + 1 <= kBuckets
   const int shift = range < (uint32_t)kBuckets ? 0 : 32 - __clz(range) - kBucketBits;
@@ -525,11 +512,12 @@ __global__ __launch_bounds__(kSelectThreads) void k_tree_select_dynamic(
   __shared__ int s_hist[kBuckets];
   __shared__ short s_mem[kBucketRankMax];
   __shared__ int s_misc[4];
-  __shared__ uint32_t s_red[2 * (kSelectThreads / 64)];
   __shared__ unsigned long long s_bcast[4], s_tmp64[kSelectThreads / 64];
   __shared__ int s_front[2][kKMax];
   __shared__ float s_fsc[2][kKMax];
-  __shared__ __attribute__((aligned(16))) unsigned long long s_cand[kKMax * kKMax + 16];
+  __shared__ __attribute__((aligned(16))) unsigned long long s_cand[kKMax * kKMax + 32];
+  __shared__ float s_cand_sc[kKMax * kKMax];
+  __shared__ uint32_t s_krange[2];
   __shared__ int s_tmp[kSelectThreads / 64];
   __shared__ int s_bad;
   __shared__ int s_pn[META ? kTMaxLimit : 1];  // parent of each node (META)
@@ -561,65 +549,79 @@ __global__ __launch_bounds__(kSelectThreads) void k_tree_select_dynamic(
   //   4. an exact rank count among them places the K best.
   constexpr int KK = K * K;
   constexpr int kPerLane = (KK + 63) / 64;
+  // order-key range of every candidate score (wavefront 0), for the final selection
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
   if (tid < 64) {
+    if (tid < K) kmin = kmax = order_key(key_value(s_key[tid]));
     for (int l = 1; l <= D; ++l) {
       const int cur = (l - 1) & 1, nxt = l & 1;
       const int base = K + (l - 1) * KK;
       unsigned long long key[kPerLane];
-      unsigned long long heads = ~0ull;
+      float sc[kPerLane];
 #pragma unroll
       for (int i = 0; i < kPerLane; ++i) {
         const int o = tid + 64 * i;
         key[i] = 0ull;
+        sc[i] = 0.0f;
         if (o < KK) {
           const int j = o / K;
-          const float sc = __fadd_rn(key_value(s_key[base + o]), s_fsc[cur][j]);
-          s_sc[base + o] = sc;
+          sc[i] = __fadd_rn(key_value(s_key[base + o]), s_fsc[cur][j]);
+          s_sc[base + o] = sc[i];
           s_par[base + o] = (short)s_front[cur][j];
-          key[i] = rank_key(sc, (uint32_t)o);
-          if (o == j * K) heads = key[i] < heads ? key[i] : heads;
+          key[i] = rank_key(sc[i], (uint32_t)o);
+          const uint32_t k32 = (uint32_t)(key[i] >> 32);
+          kmin = min(kmin, k32);
+          kmax = max(kmax, k32);
         }
       }
-      const unsigned long long tau = ~wave_max_u64(~heads);
+      // the list heads (candidate j*K, the best child of slot j) in lanes 0..K-1
+      unsigned long long head = ~0ull;
+      if (tid < K) head = rank_key(__fadd_rn(key_value(s_key[base + tid * K]), s_fsc[cur][tid]), (uint32_t)(tid * K));
+      const unsigned long long tau = readlane_u64(~group_max_u64<16>(~head), 0);
       int n = 0;
 #pragma unroll
       for (int i = 0; i < kPerLane; ++i) {
         const bool keep = key[i] != 0ull && key[i] >= tau;
         const unsigned long long m = __ballot(keep);
         const int pos = n + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-        if (keep) s_cand[pos] = key[i];
+        if (keep) {
+          s_cand[pos] = key[i];
+          s_cand_sc[pos] = sc[i];
+        }
         n += __popcll(m);
       }
-      if (tid < 16) s_cand[n + tid] = 0ull;  // zero keys pad the last batch
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      if (tid < 32) s_cand[n + tid] = 0ull;  // zero keys pad the last batch
+      wave_sync();
       for (int t = tid; t < n; t += 64) {
         const unsigned long long my = s_cand[t];
+        const float my_sc = s_cand_sc[t];
         int rk = 0;
-        for (int o0 = 0; o0 < n; o0 += 16) {  // 16 keys per batch, all reads in flight
-          u64x2 x[8];
+        for (int o0 = 0; o0 < n; o0 += 32) {  // 32 keys per batch, all reads in flight
+          u64x2 x[16];
 #pragma unroll
-          for (int u = 0; u < 8; ++u) x[u] = reinterpret_cast<const u64x2*>(s_cand + o0)[u];
+          for (int u = 0; u < 16; ++u) x[u] = reinterpret_cast<const u64x2*>(s_cand + o0)[u];
 #pragma unroll
-          for (int u = 0; u < 8; ++u) rk += (x[u][0] > my) + (x[u][1] > my);
+          for (int u = 0; u < 16; ++u) rk += (x[u][0] > my) + (x[u][1] > my);
         }
         if (rk < K) {
-          const int q = (int)key_index(my);
-          s_front[nxt][rk] = base + q;
-          s_fsc[nxt][rk] = s_sc[base + q];
+          s_front[nxt][rk] = base + (int)key_index(my);
+          s_fsc[nxt][rk] = my_sc;
         }
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      wave_sync();
+    }
+    kmin = ~wave_max_u32(~kmin);
+    kmax = wave_max_u32(kmax);
+    if (tid == 0) {
+      s_krange[0] = kmin;
+      s_krange[1] = kmax;
     }
   }
   __syncthreads();
 
   // final: keep the total_tokens best candidates, number them by ascending id
-  const unsigned long long tau = bucket_select_threshold(C, total_tokens, s_sc, s_hist, s_mem, s_misc, s_red, s_tmp,
-                                                        s_bcast, s_tmp64);
+  const unsigned long long tau = bucket_select_threshold(C, total_tokens, s_sc, s_krange[0], s_krange[1], s_hist,
+                                                        s_mem, s_misc, s_tmp, s_bcast, s_tmp64);
   const int per = (C + kSelectThreads - 1) / kSelectThreads;
   const int lo = min(C, tid * per), hi = min(C, lo + per);
   int cnt = 0;

@@ -29,8 +29,8 @@ struct Anc {
 __device__ __forceinline__ Anc ancestors(int i, int T, int p) {
   unsigned long long m = i < T ? (1ull << i) : 0ull;
   int a = (i < T && i > 0) ? p : -1;
-#pragma unroll
   for (int r = 0; r < 6; ++r) {
+    if (!__ballot(a >= 0)) break;  // every lane reached the root (depth < 2^r)
     const unsigned long long ma = shfl_u64(m, a < 0 ? i : a);
     const int aa = __shfl(a, a < 0 ? i : a, 64);
     if (a >= 0) {
