@@ -285,3 +285,21 @@ def test_fused_bad_logprobs_status():
     w.logprobs[1, 3, 100] = 0.25
     w.logprobs[2, 0, 5] = np.nan
     run(w, fused=True)
+
+
+def test_many_requests_beyond_the_reordered_batch():
+    """More than 64 requests: the splits follow the cache capacity (no reordering)."""
+    rng = np.random.default_rng(77)
+    B = 70
+    P = [int(x) for x in rng.integers(0, 400, size=B)]
+    sizes = [int(x) for x in rng.integers(1, 33, size=B)]
+    w = gen.make_custom(cfg_id=910, B=B, P=P, mode="given", given_sizes=sizes, given_depth=5, T_max=32, dcap=6,
+                        Hq=8, Hkv=2, d=128, dtype="bf16", V=50)
+    run(w)
+
+
+def test_ragged_batch_with_short_and_empty_splits():
+    """Requests much shorter than the longest: some of their key splits are empty."""
+    w = gen.make_custom(cfg_id=911, B=5, P=[3000, 10, 0, 700, 64], mode="given", given_sizes=[40, 3, 1, 64, 17],
+                        given_depth=6, T_max=64, dcap=8, Hq=16, Hkv=4, d=128, dtype="bf16", V=50)
+    run(w)

@@ -64,6 +64,7 @@ struct Plan {
   long long m_pad; // padded rows per (request, kv head) in the workspace
   int n_units;     // B * Hkv * n_split
   int grid;
+  int rel;         // splits relative to each request's own length, longest request first
 };
 
 Plan plan_with(int B, int T_max, int Hq, int Hkv, long long S_cap, int nw, long long min_keys) {
@@ -88,6 +89,7 @@ Plan plan_with(int B, int T_max, int Hq, int Hkv, long long S_cap, int nw, long 
   p.m_pad = (long long)p.n_rowblk * p.rows_wg;
   p.n_units = (int)((long long)B * Hkv * ns);
   p.grid = 8 * p.n_rowblk * ((p.n_units + 7) / 8);
+  p.rel = B > 1 && B <= 64;
   return p;
 }
 
@@ -158,7 +160,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_attn_bf16(
     long long S_cap, const int* __restrict__ prefix_len, const int* __restrict__ tree_size,
     const uint32_t* __restrict__ tree_mask, const int* __restrict__ status, int T_max, int Hq, int Hkv, int W,
     float sl2, uint16_t* __restrict__ O, _Float16* __restrict__ ws_o, float* __restrict__ ws_ml, int n_split,
-    int chunk_keys, int n_rowblk, int n_units, long long m_pad) {
+    int chunk_keys, int n_rowblk, int n_units, long long m_pad, int B, int rel) {
   constexpr int NT = NW * 64;
   constexpr int KSTEPS = D / 16;     // 16-wide k-steps of QK^T (KSTEPS/2 per half of d)
   constexpr int DB = D / 32;         // 32-wide d blocks of the output
@@ -189,13 +191,39 @@ __global__ __launch_bounds__(NW * 64, 1) void k_attn_bf16(
   const int u = (slot / n_rowblk) * 8 + (wg & 7);
   if (u >= n_units) return;
   const int split = u % n_split;
-  const int bg = u / n_split;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int bg = u / n_split;
+  // Several requests (rel): their sizes are read first, one lane per request, and
+  // the requests are taken in descending order of key count (ties: lower index
+  // first), so the longest ones start first; each request's keys are then split
+  // into n_split nearly equal parts (below).
+  int rel_T = 0, rel_P = 0, rel_st = 0;
+  if (rel) {
+    int nk = -1, Tl = 0, Pl = 0, sl = 0;
+    if (lane < B) {
+      Tl = tree_size[lane];
+      Pl = prefix_len[lane];
+      sl = status[lane];
+      const int Te = (sl != TV_ST_OK || Tl < 1 || Tl > T_max) ? 1 : Tl;
+      nk = (Pl < 0 || (long long)Pl + Te > S_cap) ? 0 : Pl + Te;
+    }
+    int rank = 0;
+    for (int o = 0; o < B; ++o) {
+      const int x = __builtin_amdgcn_readlane(nk, o);
+      rank += (x > nk) || (x == nk && o < lane);
+    }
+    const unsigned long long m = __ballot(lane < B && rank == bg / Hkv);
+    const int bsel = __ffsll((long long)m) - 1;
+    bg = bsel * Hkv + bg % Hkv;
+    rel_T = __builtin_amdgcn_readlane(Tl, bsel);
+    rel_P = __builtin_amdgcn_readlane(Pl, bsel);
+    rel_st = __builtin_amdgcn_readlane(sl, bsel);
+  }
   const int g = bg % Hkv, b = bg / Hkv;
   const int rep = Hq / Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
   const int row0 = rbk * NW * 32;
-  const int k_begin = split * chunk_keys;
+  int k_begin = split * chunk_keys;  // (rel: set once the request's size is known)
 
   const uint16_t* Kb = Kc + ((long long)b * Hkv + g) * S_cap * D;
   const uint16_t* Vb = Vc + ((long long)b * Hkv + g) * S_cap * D;
@@ -226,7 +254,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_attn_bf16(
   // to T_max - 1.  What lies past the request is neutralised below.
   const int r = row0 + wave * 32 + l32;
   const int i_row = min(r / rep, T_max - 1);
-  dma_tile(k_begin, (int)S_cap - 1, 0);
+  if (!rel) dma_tile(k_begin, (int)S_cap - 1, 0);
   bf16x8 qf[KSTEPS];
   {
     const int head = g * rep + r % rep;
@@ -238,9 +266,9 @@ __global__ __launch_bounds__(NW * 64, 1) void k_attn_bf16(
   const uint32_t* mp = tree_mask + ((long long)b * T_max + i_row) * W;
   unsigned long long mrow = (unsigned long long)mp[0] | (W > 1 ? ((unsigned long long)mp[1] << 32) : 0ull);
 
-  int T = tree_size[b];
-  const int P = prefix_len[b];
-  if (status[b] != TV_ST_OK || T < 1 || T > T_max) T = 1;
+  int T = rel ? rel_T : tree_size[b];
+  const int P = rel ? rel_P : prefix_len[b];
+  if ((rel ? rel_st : status[b]) != TV_ST_OK || T < 1 || T > T_max) T = 1;
   const int M = rep * T;
   if (row0 >= M) {
     __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));  // no LDS DMA may outlive the workgroup
@@ -261,18 +289,32 @@ __global__ __launch_bounds__(NW * 64, 1) void k_attn_bf16(
     return;
   }
   const int nkeys = P + T;
-  if (k_begin >= nkeys) {
-    __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
-    return;
+  int k_end, n_tiles;
+  if (rel) {
+    // split `split` of min(n_split, tiles) nearly equal parts of the request's
+    // tiles; the later splits of a short request are empty
+    const int tiles = (nkeys + KT - 1) / KT;
+    const int n_eff = min(n_split, tiles);
+    if (split >= n_eff) return;  // nothing requested yet
+    const int t0 = (int)((long long)split * tiles / n_eff), t1 = (int)((long long)(split + 1) * tiles / n_eff);
+    k_begin = t0 * KT;
+    k_end = min(nkeys, t1 * KT);
+    n_tiles = t1 - t0;
+    dma_tile(k_begin, nkeys - 1, 0);
+  } else {
+    if (k_begin >= nkeys) {
+      __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+      return;
+    }
+    k_end = min(nkeys, k_begin + chunk_keys);
+    n_tiles = (k_end - k_begin + KT - 1) / KT;
+    // A tile 0 that reaches past the last key was fetched with keys clamped to
+    // the slab, so its rows past the request hold whatever the cache holds there:
+    // fetch it again with keys clamped to the last key (its scores there are
+    // masked to -inf, and finite V rows keep 0 * garbage out of the PV product).
+    // The re-fetch lands after the first one (returns are in order).
+    if (k_begin + KT > nkeys) dma_tile(k_begin, nkeys - 1, 0);
   }
-  const int k_end = min(nkeys, k_begin + chunk_keys);
-  const int n_tiles = (k_end - k_begin + KT - 1) / KT;
-  // A tile 0 that reaches past the last key was fetched with keys clamped to the
-  // slab, so its rows past the request hold whatever the cache holds there: fetch
-  // it again with keys clamped to the last key (its scores there are masked to
-  // -inf, and finite V rows keep 0 * garbage out of the PV product).  The re-fetch
-  // lands after the first one (returns are in order).
-  if (k_begin + KT > nkeys) dma_tile(k_begin, nkeys - 1, 0);
   // padding query rows get a zero Q and no mask
   if (r >= M) {
 #pragma unroll
@@ -525,7 +567,7 @@ __global__ __launch_bounds__(256) void k_attn_combine(const _Float16* __restrict
                                                       const int* __restrict__ tree_size,
                                                       const int* __restrict__ status, long long S_cap, int T_max,
                                                       int Hq, int Hkv, int n_split, int chunk_keys, long long m_pad,
-                                                      uint16_t* __restrict__ O) {
+                                                      int rel, uint16_t* __restrict__ O) {
   typedef _Float16 h8 __attribute__((ext_vector_type(8)));
   constexpr int TPR = D / 8;          // threads per row, 8 outputs each
   constexpr int RPB = 256 / TPR;      // rows per block
@@ -542,7 +584,8 @@ __global__ __launch_bounds__(256) void k_attn_combine(const _Float16* __restrict
   if (r >= M) return;
   const int d0 = 8 * (threadIdx.x % TPR);
   const int nkeys = P + T;
-  const int n_act = (nkeys + chunk_keys - 1) / chunk_keys;
+  // splits that saw keys (a prefix): the same partition as the attention kernel's
+  const int n_act = rel ? min(n_split, (nkeys + KT - 1) / KT) : (nkeys + chunk_keys - 1) / chunk_keys;
   const long long base = (long long)bg * n_split * m_pad + r;
   float mx = -INFINITY, l = 0.0f;
   float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -649,12 +692,12 @@ __global__ __launch_bounds__(64) void k_attn_fp32(const float* __restrict__ Q, c
 }
 
 template <int D, int NW>
-void launch_bf16(const Plan& p, hipStream_t s, const void* Q, const void* Kc, const void* Vc, long long S_cap,
+void launch_bf16(const Plan& p, int B, hipStream_t s, const void* Q, const void* Kc, const void* Vc, long long S_cap,
                  const int* prefix_len, const int* tree_size, const uint32_t* tree_mask, const int* status,
                  int T_max, int Hq, int Hkv, int W, float sl2, void* O, _Float16* ws_o, float* ws_ml) {
   hipLaunchKernelGGL((k_attn_bf16<D, NW>), dim3(p.grid), dim3(NW * 64), 0, s, (const uint16_t*)Q, (const uint16_t*)Kc,
                      (const uint16_t*)Vc, S_cap, prefix_len, tree_size, tree_mask, status, T_max, Hq, Hkv, W, sl2,
-                     (uint16_t*)O, ws_o, ws_ml, p.n_split, p.chunk_keys, p.n_rowblk, p.n_units, p.m_pad);
+                     (uint16_t*)O, ws_o, ws_ml, p.n_split, p.chunk_keys, p.n_rowblk, p.n_units, p.m_pad, B, p.rel);
 }
 
 size_t ws_bytes_for(const Plan& p, int B, int Hkv, int d) {
@@ -712,17 +755,17 @@ extern "C" int tree_attention(int dtype, int B, int T_max, int Hq, int Hkv, int 
   const float sl2 = scale * kLog2e;
   if (d == 128) {
     if (p.nw == 4)
-      launch_bf16<128, 4>(p, s, Q, Kc, Vc, S_cap, prefix_len, tree_size, tree_mask, status, T_max, Hq, Hkv, W, sl2,
+      launch_bf16<128, 4>(p, B, s, Q, Kc, Vc, S_cap, prefix_len, tree_size, tree_mask, status, T_max, Hq, Hkv, W, sl2,
                           O, ws_o, ws_ml);
     else
-      launch_bf16<128, 8>(p, s, Q, Kc, Vc, S_cap, prefix_len, tree_size, tree_mask, status, T_max, Hq, Hkv, W, sl2,
+      launch_bf16<128, 8>(p, B, s, Q, Kc, Vc, S_cap, prefix_len, tree_size, tree_mask, status, T_max, Hq, Hkv, W, sl2,
                           O, ws_o, ws_ml);
   } else {
     if (p.nw == 4)
-      launch_bf16<64, 4>(p, s, Q, Kc, Vc, S_cap, prefix_len, tree_size, tree_mask, status, T_max, Hq, Hkv, W, sl2,
+      launch_bf16<64, 4>(p, B, s, Q, Kc, Vc, S_cap, prefix_len, tree_size, tree_mask, status, T_max, Hq, Hkv, W, sl2,
                          O, ws_o, ws_ml);
     else
-      launch_bf16<64, 8>(p, s, Q, Kc, Vc, S_cap, prefix_len, tree_size, tree_mask, status, T_max, Hq, Hkv, W, sl2,
+      launch_bf16<64, 8>(p, B, s, Q, Kc, Vc, S_cap, prefix_len, tree_size, tree_mask, status, T_max, Hq, Hkv, W, sl2,
                          O, ws_o, ws_ml);
   }
   TV_CHECK_LAUNCH();
@@ -731,10 +774,10 @@ extern "C" int tree_attention(int dtype, int B, int T_max, int Hq, int Hkv, int 
     dim3 grid(B * Hkv, (unsigned)((p.m_pad + rpb - 1) / rpb));
     if (d == 128)
       hipLaunchKernelGGL(k_attn_combine<128>, grid, dim3(256), 0, s, ws_o, ws_ml, prefix_len, tree_size, status, S_cap,
-                         T_max, Hq, Hkv, p.n_split, p.chunk_keys, p.m_pad, (uint16_t*)O);
+                         T_max, Hq, Hkv, p.n_split, p.chunk_keys, p.m_pad, p.rel, (uint16_t*)O);
     else
       hipLaunchKernelGGL(k_attn_combine<64>, grid, dim3(256), 0, s, ws_o, ws_ml, prefix_len, tree_size, status, S_cap,
-                         T_max, Hq, Hkv, p.n_split, p.chunk_keys, p.m_pad, (uint16_t*)O);
+                         T_max, Hq, Hkv, p.n_split, p.chunk_keys, p.m_pad, p.rel, (uint16_t*)O);
     TV_CHECK_LAUNCH();
   }
   return TV_OK;
