@@ -190,7 +190,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_row_topk(const float* __restri
   const int span = ((V + S - 1) / S + 3) & ~3;
   const int begin = chunk * span, end = min(V, begin + span);
   const int tid = threadIdx.x, lane = tid & 63;
-  __shared__ unsigned long long s_cand[kCandCap];
+  __shared__ __attribute__((aligned(16))) unsigned long long s_cand[kCandCap + 16];  // + one batch of slack
   __shared__ unsigned long long s_best[kKMax];
   __shared__ __attribute__((aligned(16))) uint32_t s_gmax[kTopkGroups];
   __shared__ int s_n, s_bad, s_cnt[3];
@@ -302,10 +302,17 @@ __global__ __launch_bounds__(kTopkThreads) void k_row_topk(const float* __restri
     }
 
     // exact rank among the n unique candidates; the K best, in order, to s_best
+    // (16 keys per batch, all reads in flight; entries past n are not counted)
     for (int t = tid; t < n; t += kTopkThreads) {
       const unsigned long long my = s_cand[t];
       int rk = 0;
-      for (int o = 0; o < n; ++o) rk += s_cand[o] > my;
+      for (int o0 = 0; o0 < n; o0 += 16) {
+        u64x2 x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = reinterpret_cast<const u64x2*>(s_cand + o0)[u];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) rk += (o0 + 2 * u < n && x[u][0] > my) + (o0 + 2 * u + 1 < n && x[u][1] > my);
+      }
       if (rk < K) s_best[rk] = my;
     }
     __syncthreads();
