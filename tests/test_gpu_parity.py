@@ -303,3 +303,11 @@ def test_ragged_batch_with_short_and_empty_splits():
     w = gen.make_custom(cfg_id=911, B=5, P=[3000, 10, 0, 700, 64], mode="given", given_sizes=[40, 3, 1, 64, 17],
                         given_depth=6, T_max=64, dcap=8, Hq=16, Hkv=4, d=128, dtype="bf16", V=50)
     run(w)
+
+
+def test_single_request_two_stage_plan_d64():
+    """One request whose 8-wavefront plan leaves the chip idle: 4-wavefront workgroups with two stage
+    buffers, at d = 64 (the benchmark's request covers d = 128)."""
+    w = gen.make_custom(cfg_id=912, B=1, P=[1500], mode="given", given_sizes=[50], given_depth=6, T_max=64,
+                        dcap=8, Hq=16, Hkv=2, d=64, dtype="bf16", V=50)
+    run(w)

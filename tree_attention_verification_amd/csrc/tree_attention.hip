@@ -65,6 +65,7 @@ struct Plan {
   int n_units;     // B * Hkv * n_split
   int grid;
   int rel;         // splits relative to each request's own length, longest request first
+  int nstage;      // LDS stage buffers (4: one workgroup per CU, 2: two)
 };
 
 Plan plan_with(int B, int T_max, int Hq, int Hkv, long long S_cap, int nw, long long min_keys) {
@@ -90,6 +91,7 @@ Plan plan_with(int B, int T_max, int Hq, int Hkv, long long S_cap, int nw, long 
   p.n_units = (int)((long long)B * Hkv * ns);
   p.grid = 8 * p.n_rowblk * ((p.n_units + 7) / 8);
   p.rel = B > 1 && B <= 64;
+  p.nstage = 4;
   return p;
 }
 
@@ -98,12 +100,17 @@ Plan plan_with(int B, int T_max, int Hq, int Hkv, long long S_cap, int nw, long 
 // workgroups.  When that leaves most of the chip idle (a single request: 8 kv
 // heads x ~9 splits = 72 workgroups), 4-wavefront workgroups with >= 192-key
 // splits spread the same work over more than twice as many CUs (measured on
-// MI355X: 17.9 vs 21.7 us for 61 nodes x 32 heads over a 2048-token prefix).
+// MI355X: 17.9 vs 21.7 us for 61 nodes x 32 heads over a 2048-token prefix),
+// with two stage buffers (3-tile splits need no deeper prefetch; 16.4 vs 18.3 us).
 Plan make_plan(int B, int T_max, int Hq, int Hkv, long long S_cap) {
   const long long m_max = (long long)(Hq / Hkv) * T_max;
   if (m_max <= 128) return plan_with(B, T_max, Hq, Hkv, S_cap, 4, 4 * KT);
   const Plan p = plan_with(B, T_max, Hq, Hkv, S_cap, 8, 4 * KT);
-  if (p.grid < 128) return plan_with(B, T_max, Hq, Hkv, S_cap, 4, 3 * KT);
+  if (p.grid < 128) {
+    Plan q = plan_with(B, T_max, Hq, Hkv, S_cap, 4, 3 * KT);
+    q.nstage = 2;
+    return q;
+  }
   return p;
 }
 
@@ -154,8 +161,8 @@ __device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
 // and lgkmcnt left at their maximum)
 constexpr int vm_wait_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64, 1) void k_attn_bf16(
+template <int D, int NW, int NSTAGE>
+__global__ __launch_bounds__(NW * 64, NSTAGE == 2 ? 2 : 1) void k_attn_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Kc, const uint16_t* __restrict__ Vc,
     long long S_cap, const int* __restrict__ prefix_len, const int* __restrict__ tree_size,
     const uint32_t* __restrict__ tree_mask, const int* __restrict__ status, int T_max, int Hq, int Hkv, int W,
@@ -165,7 +172,10 @@ __global__ __launch_bounds__(NW * 64, 1) void k_attn_bf16(
   constexpr int KSTEPS = D / 16;     // 16-wide k-steps of QK^T (KSTEPS/2 per half of d)
   constexpr int DB = D / 32;         // 32-wide d blocks of the output
   constexpr int CH = D / 8;          // 16-byte chunks per K/V row
-  constexpr int NSTAGE = 4;          // LDS tile buffers: three tiles in flight while one is computed
+  // NSTAGE LDS tile buffers: NSTAGE - 1 tiles in flight while one is computed
+  // (4: one workgroup per CU; 2: two workgroups per CU, whose barriers are
+  // independent, so their wavefronts drift out of phase on each SIMD)
+  static_assert(NSTAGE == 2 || NSTAGE == 4, "two or four stage buffers");
   constexpr int kAhead = 5;         // LDS fragment reads issued ahead of the MFMAs that use them
   constexpr int INSTR = KT * CH / 64;  // 64-lane DMA instructions per tensor per tile
   static_assert(INSTR % NW == 0, "DMA instructions split evenly over the wavefronts");
@@ -329,8 +339,9 @@ __global__ __launch_bounds__(NW * 64, 1) void k_attn_bf16(
   // flight while tile 0 is computed.
   __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
   asm volatile("" ::"v"(qf[0]), "v"(qf[KSTEPS / 2]), "v"(qf[KSTEPS - 1]), "v"(mrow));
-  if (n_tiles > 1) dma_tile(k_begin + KT, nkeys - 1, 1);
-  if (n_tiles > 2) dma_tile(k_begin + 2 * KT, nkeys - 1, 2);
+#pragma unroll
+  for (int j = 1; j < NSTAGE - 1; ++j)
+    if (n_tiles > j) dma_tile(k_begin + j * KT, nkeys - 1, j);
 
   f32x16 acc[DB];
 #pragma unroll
@@ -496,25 +507,26 @@ __global__ __launch_bounds__(NW * 64, 1) void k_attn_bf16(
     }
     pv(buf, pt);
   };
-  // step t: wait for this wavefront's part of tile t (tiles t+1, t+2 may still be
-  // in flight, when they exist), barrier (every part landed, and every wavefront
-  // is done with tile t-1), request tile t+3 (when it exists) into tile t-1's
-  // buffer, compute tile t.  Tiles past the request's last tile in this split
-  // are never requested, so nothing is left in flight at the end.
+  // step t: wait for this wavefront's part of tile t (the up to NSTAGE - 2 younger
+  // tiles may still be in flight, when they exist), barrier (every part landed,
+  // and every wavefront is done with tile t-1), request tile t + NSTAGE - 1 (when
+  // it exists) into tile t-1's buffer, compute tile t.  Tiles past the request's
+  // last tile in this split are never requested, so nothing is left in flight at
+  // the end.
   auto step = [&](int t, int buf) __attribute__((always_inline)) {
-    const int younger = min(n_tiles - 1 - t, 2);
-    if (younger >= 2) __builtin_amdgcn_s_waitcnt(vm_wait_imm(2 * DMA_WAVE));
-    else if (younger == 1) __builtin_amdgcn_s_waitcnt(vm_wait_imm(DMA_WAVE));
+    const int younger = min(n_tiles - 1 - t, NSTAGE - 2);
+    if (NSTAGE == 4 && younger >= 2) __builtin_amdgcn_s_waitcnt(vm_wait_imm(2 * DMA_WAVE));
+    else if (NSTAGE == 4 && younger == 1) __builtin_amdgcn_s_waitcnt(vm_wait_imm(DMA_WAVE));
     else __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
     lds_barrier();
-    if (t + 3 < n_tiles) dma_tile(k_begin + (t + 3) * KT, nkeys - 1, (buf + 3) % NSTAGE);
+    if (t + NSTAGE - 1 < n_tiles)
+      dma_tile(k_begin + (t + NSTAGE - 1) * KT, nkeys - 1, (buf + NSTAGE - 1) % NSTAGE);
     if (active) compute(t, buf);
   };
   for (int t = 0; t < n_tiles; t += NSTAGE) {
-    step(t, 0);
-    if (t + 1 < n_tiles) step(t + 1, 1);
-    if (t + 2 < n_tiles) step(t + 2, 2);
-    if (t + 3 < n_tiles) step(t + 3, 3);
+#pragma unroll
+    for (int j = 0; j < NSTAGE; ++j)
+      if (t + j < n_tiles) step(t + j, j);
   }
 
   // ---- epilogue
@@ -691,11 +703,11 @@ __global__ __launch_bounds__(64) void k_attn_fp32(const float* __restrict__ Q, c
   }
 }
 
-template <int D, int NW>
+template <int D, int NW, int NS>
 void launch_bf16(const Plan& p, int B, hipStream_t s, const void* Q, const void* Kc, const void* Vc, long long S_cap,
                  const int* prefix_len, const int* tree_size, const uint32_t* tree_mask, const int* status,
                  int T_max, int Hq, int Hkv, int W, float sl2, void* O, _Float16* ws_o, float* ws_ml) {
-  hipLaunchKernelGGL((k_attn_bf16<D, NW>), dim3(p.grid), dim3(NW * 64), 0, s, (const uint16_t*)Q, (const uint16_t*)Kc,
+  hipLaunchKernelGGL((k_attn_bf16<D, NW, NS>), dim3(p.grid), dim3(NW * 64), 0, s, (const uint16_t*)Q, (const uint16_t*)Kc,
                      (const uint16_t*)Vc, S_cap, prefix_len, tree_size, tree_mask, status, T_max, Hq, Hkv, W, sl2,
                      (uint16_t*)O, ws_o, ws_ml, p.n_split, p.chunk_keys, p.n_rowblk, p.n_units, p.m_pad, B, p.rel);
 }
@@ -753,21 +765,19 @@ extern "C" int tree_attention(int dtype, int B, int T_max, int Hq, int Hkv, int 
   _Float16* ws_o = reinterpret_cast<_Float16*>(workspace);
   float* ws_ml = need ? reinterpret_cast<float*>(ws_o + (size_t)B * Hkv * p.n_split * p.m_pad * d) : nullptr;
   const float sl2 = scale * kLog2e;
+#define TV_ATTN_LAUNCH(DD, NWW, NSS)                                                                             \
+  launch_bf16<DD, NWW, NSS>(p, B, s, Q, Kc, Vc, S_cap, prefix_len, tree_size, tree_mask, status, T_max, Hq, Hkv, W, \
+                            sl2, O, ws_o, ws_ml)
   if (d == 128) {
-    if (p.nw == 4)
-      launch_bf16<128, 4>(p, B, s, Q, Kc, Vc, S_cap, prefix_len, tree_size, tree_mask, status, T_max, Hq, Hkv, W, sl2,
-                          O, ws_o, ws_ml);
-    else
-      launch_bf16<128, 8>(p, B, s, Q, Kc, Vc, S_cap, prefix_len, tree_size, tree_mask, status, T_max, Hq, Hkv, W, sl2,
-                          O, ws_o, ws_ml);
+    if (p.nw == 4 && p.nstage == 2) TV_ATTN_LAUNCH(128, 4, 2);
+    else if (p.nw == 4) TV_ATTN_LAUNCH(128, 4, 4);
+    else TV_ATTN_LAUNCH(128, 8, 4);
   } else {
-    if (p.nw == 4)
-      launch_bf16<64, 4>(p, B, s, Q, Kc, Vc, S_cap, prefix_len, tree_size, tree_mask, status, T_max, Hq, Hkv, W, sl2,
-                         O, ws_o, ws_ml);
-    else
-      launch_bf16<64, 8>(p, B, s, Q, Kc, Vc, S_cap, prefix_len, tree_size, tree_mask, status, T_max, Hq, Hkv, W, sl2,
-                         O, ws_o, ws_ml);
+    if (p.nw == 4 && p.nstage == 2) TV_ATTN_LAUNCH(64, 4, 2);
+    else if (p.nw == 4) TV_ATTN_LAUNCH(64, 4, 4);
+    else TV_ATTN_LAUNCH(64, 8, 4);
   }
+#undef TV_ATTN_LAUNCH
   TV_CHECK_LAUNCH();
   if (p.n_split > 1) {
     const int rpb = 256 / (d / 8);
