@@ -65,7 +65,6 @@ struct Plan {
   int n_units;     // B * Hkv * n_split
   int grid;
   int rel;         // splits relative to each request's own length, longest request first
-  int nstage;      // LDS stage buffers (4: one workgroup per CU, 2: two)
 };
 
 Plan plan_with(int B, int T_max, int Hq, int Hkv, long long S_cap, int nw, long long min_keys) {
@@ -91,7 +90,6 @@ Plan plan_with(int B, int T_max, int Hq, int Hkv, long long S_cap, int nw, long 
   p.n_units = (int)((long long)B * Hkv * ns);
   p.grid = 8 * p.n_rowblk * ((p.n_units + 7) / 8);
   p.rel = B > 1 && B <= 64;
-  p.nstage = 4;
   return p;
 }
 
@@ -100,17 +98,12 @@ Plan plan_with(int B, int T_max, int Hq, int Hkv, long long S_cap, int nw, long 
 // workgroups.  When that leaves most of the chip idle (a single request: 8 kv
 // heads x ~9 splits = 72 workgroups), 4-wavefront workgroups with >= 192-key
 // splits spread the same work over more than twice as many CUs (measured on
-// MI355X: 17.9 vs 21.7 us for 61 nodes x 32 heads over a 2048-token prefix),
-// with two stage buffers (3-tile splits need no deeper prefetch; 16.4 vs 18.3 us).
+// MI355X: 17.9 vs 21.7 us for 61 nodes x 32 heads over a 2048-token prefix).
 Plan make_plan(int B, int T_max, int Hq, int Hkv, long long S_cap) {
   const long long m_max = (long long)(Hq / Hkv) * T_max;
   if (m_max <= 128) return plan_with(B, T_max, Hq, Hkv, S_cap, 4, 4 * KT);
   const Plan p = plan_with(B, T_max, Hq, Hkv, S_cap, 8, 4 * KT);
-  if (p.grid < 128) {
-    Plan q = plan_with(B, T_max, Hq, Hkv, S_cap, 4, 3 * KT);
-    q.nstage = 2;
-    return q;
-  }
+  if (p.grid < 128) return plan_with(B, T_max, Hq, Hkv, S_cap, 4, 3 * KT);
   return p;
 }
 
@@ -162,7 +155,7 @@ __device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
 constexpr int vm_wait_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 template <int D, int NW, int NSTAGE>
-__global__ __launch_bounds__(NW * 64, NSTAGE == 2 ? 2 : 1) void k_attn_bf16(
+__global__ __launch_bounds__(NW * 64, (NSTAGE == 2 && NW == 4) ? 2 : 1) void k_attn_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Kc, const uint16_t* __restrict__ Vc,
     long long S_cap, const int* __restrict__ prefix_len, const int* __restrict__ tree_size,
     const uint32_t* __restrict__ tree_mask, const int* __restrict__ status, int T_max, int Hq, int Hkv, int W,
@@ -172,9 +165,10 @@ __global__ __launch_bounds__(NW * 64, NSTAGE == 2 ? 2 : 1) void k_attn_bf16(
   constexpr int KSTEPS = D / 16;     // 16-wide k-steps of QK^T (KSTEPS/2 per half of d)
   constexpr int DB = D / 32;         // 32-wide d blocks of the output
   constexpr int CH = D / 8;          // 16-byte chunks per K/V row
-  // NSTAGE LDS tile buffers: NSTAGE - 1 tiles in flight while one is computed
-  // (4: one workgroup per CU; 2: two workgroups per CU, whose barriers are
-  // independent, so their wavefronts drift out of phase on each SIMD)
+  // NSTAGE LDS tile buffers: NSTAGE - 1 tiles in flight while one is computed.
+  // Two are used (64 KB at d = 128; with 4-wavefront workgroups two fit on a CU):
+  // measured on MI355X, one tile in flight beat three at every configuration
+  // (cfg2 18.3 -> 16.4 us, cfg3 93.6 -> 89.6, cfg4 284 -> 279, cfg5 264 -> 256).
   static_assert(NSTAGE == 2 || NSTAGE == 4, "two or four stage buffers");
   constexpr int kAhead = 5;         // LDS fragment reads issued ahead of the MFMAs that use them
   constexpr int INSTR = KT * CH / 64;  // 64-lane DMA instructions per tensor per tile
@@ -239,12 +233,12 @@ __global__ __launch_bounds__(NW * 64, NSTAGE == 2 ? 2 : 1) void k_attn_bf16(
   const uint16_t* Vb = Vc + ((long long)b * Hkv + g) * S_cap * D;
 
   // ---- tile staging: K/V tiles go straight from global memory into LDS (no
-  // registers) through four stage buffers; tile t+3 is requested while tile t is
-  // computed, so three tiles (96 KB at d = 128) are in flight per workgroup.  The
-  // 64 lanes of one DMA instruction fill 1 KB of LDS in order, so the XOR swizzle
-  // is applied on the global side: LDS slot (row, c) receives chunk c ^ swz(row).
-  // Only tiles inside the split are requested; the wait before tile t allows
-  // exactly the younger tiles that were requested (up to two) to stay in flight.
+  // registers) through NSTAGE stage buffers; tile t + NSTAGE - 1 is requested
+  // while tile t is computed.  The 64 lanes of one DMA instruction fill 1 KB of LDS
+  // in order, so the XOR swizzle is applied on the global side: LDS slot (row, c)
+  // receives chunk c ^ swz(row).  Only tiles inside the split are requested; the
+  // wait before tile t allows exactly the younger tiles that were requested (up to
+  // NSTAGE - 2) to stay in flight.
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform (LDS base goes to m0)
   auto dma_tile = [&](int kt0, int last_key, int buf) __attribute__((always_inline)) {
 #pragma unroll
@@ -769,13 +763,11 @@ extern "C" int tree_attention(int dtype, int B, int T_max, int Hq, int Hkv, int 
   launch_bf16<DD, NWW, NSS>(p, B, s, Q, Kc, Vc, S_cap, prefix_len, tree_size, tree_mask, status, T_max, Hq, Hkv, W, \
                             sl2, O, ws_o, ws_ml)
   if (d == 128) {
-    if (p.nw == 4 && p.nstage == 2) TV_ATTN_LAUNCH(128, 4, 2);
-    else if (p.nw == 4) TV_ATTN_LAUNCH(128, 4, 4);
-    else TV_ATTN_LAUNCH(128, 8, 4);
+    if (p.nw == 4) TV_ATTN_LAUNCH(128, 4, 2);
+    else TV_ATTN_LAUNCH(128, 8, 2);
   } else {
-    if (p.nw == 4 && p.nstage == 2) TV_ATTN_LAUNCH(64, 4, 2);
-    else if (p.nw == 4) TV_ATTN_LAUNCH(64, 4, 4);
-    else TV_ATTN_LAUNCH(64, 8, 4);
+    if (p.nw == 4) TV_ATTN_LAUNCH(64, 4, 2);
+    else TV_ATTN_LAUNCH(64, 8, 2);
   }
 #undef TV_ATTN_LAUNCH
   TV_CHECK_LAUNCH();
