@@ -2,7 +2,8 @@
 
 A step = tree_build -> tree_mask_positions -> tree_attention -> tree_accept ->
 kv_compact over one batch of synthetic inputs, all through the C ABI on one HIP
-stream.  The default workload is the EAGLE-2 dynamic tree at batch 1 (top_k 10,
+stream (by default through tree_build_meta, tree_attention, tree_accept_compact:
+the same five stages in two kernel launches fewer; --unfused runs five calls).  The default workload is the EAGLE-2 dynamic tree at batch 1 (top_k 10,
 depth 6, 60 draft nodes + root, prefix 2048, Llama-3-8B attention heads 32/8/128,
 bf16); --config 1..5 selects another of the five measured workloads.
 
@@ -61,6 +62,41 @@ def source_hash():
     path = os.path.join(ROOT, "tree_attention_verification_amd", "csrc", "tree_attention.hip")
     with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def machine_peaks(torch):
+    """What this GPU sustains right now on plain library work, to put the roofline
+    fractions next to: a 1 GiB device copy (torch) and an 8192^3 bf16 GEMM
+    (torch.matmul, hipBLASLt).  Measured under the same power and clock limits as
+    the step, so they sit below the published peaks."""
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(5):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * n * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, b
+    m = 8192
+    x = torch.randn(m, m, device="cuda", dtype=torch.bfloat16)
+    y = torch.randn(m, m, device="cuda", dtype=torch.bfloat16)
+    torch.matmul(x, y)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(5):
+        torch.matmul(x, y)
+    e1.record()
+    torch.cuda.synchronize()
+    gemm_tf = 2 * m ** 3 * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del x, y
+    torch.cuda.empty_cache()
+    return {"hbm_copy_GBps": round(copy_gbs, 1), "bf16_gemm_TFLOPs": round(gemm_tf, 1),
+            "what": "1 GiB device copy (read + write bytes) and 8192^3 bf16 torch.matmul on this GPU in this run"}
 
 
 def measured_traffic(workload_name):
@@ -139,6 +175,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches only")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the copy / GEMM measurement of what this GPU sustains (reported beside the roofline)")
     ap.add_argument("--unfused", action="store_true",
                     help="run the step as the five separate calls (default: tree_build_meta, tree_attention, "
                          "tree_accept_compact -- the same five stages in two kernel launches fewer)")
@@ -264,6 +302,7 @@ def main():
     stages = {n: round(float(np.mean([ev[r][i].elapsed_time(ev[r][i + 1]) for r in range(reps)])) * 1e3, 2)
               for i, n in enumerate(names)}
 
+    peaks = None if args.no_peaks else machine_peaks(torch)
     nbytes, flops = attention_work(w, th["tree_size"], mh["tree_position_ids"], status)
     t_attn = attn_ms * 1e-3
     mfma_peak = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
@@ -273,6 +312,10 @@ def main():
         roof = {"bound": "mfma" if w.dtype == "bf16" else "alu", "achieved": round(flops / t_attn / 1e12, 2),
                 "peak": mfma_peak, "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    if peaks:
+        ref = peaks["hbm_copy_GBps"] if roof["unit"] == "GB/s" else peaks["bf16_gemm_TFLOPs"]
+        if roof["bound"] in ("hbm", "mfma"):
+            roof["frac_of_measured"] = round(roof["achieved"] / ref, 4)
     roof["traffic"] = measured_traffic(w.name)
     roof["kernel"] = "tree_attention call (k_attn_bf16 + k_attn_combine when the keys are split)"
     roof["algorithmic_bytes"] = int(nbytes)
@@ -302,6 +345,8 @@ def main():
         "stages_us": stages,
         "roofline": roof,
     }
+    if peaks:
+        out["measured_peaks"] = peaks
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
