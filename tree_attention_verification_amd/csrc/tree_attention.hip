@@ -581,30 +581,37 @@ __global__ __launch_bounds__(256) void k_attn_combine(const _Float16* __restrict
   const int bg = blockIdx.x;
   const int b = bg / Hkv, g = bg % Hkv;
   const int rep = Hq / Hkv;
+  const int r = blockIdx.y * RPB + threadIdx.x / TPR;  // < m_pad (a multiple of RPB)
+  const int d0 = 8 * (threadIdx.x % TPR);
+  const long long base = (long long)bg * n_split * m_pad + r;
+  // the first batch of partials is requested together with the request's sizes
+  // (one memory round trip): splits past the ones that saw keys are read (they
+  // lie inside the workspace) but never used
+  float ms[BATCH], ls[BATCH];
+  h8 x[BATCH];
+  auto load_batch = [&](int s0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) {
+      const long long pr = base + (long long)min(s0 + j, n_split - 1) * m_pad;
+      ms[j] = ws_ml[2 * pr];
+      ls[j] = ws_ml[2 * pr + 1];
+      x[j] = *reinterpret_cast<const h8*>(ws_o + pr * D + d0);
+    }
+  };
+  load_batch(0);
   int T = tree_size[b];
   const int P = prefix_len[b];
   if (status[b] != TV_ST_OK || T < 1 || T > T_max) T = 1;
   if (P < 0 || (long long)P + T > S_cap) return;
   const int M = rep * T;
-  const int r = blockIdx.y * RPB + threadIdx.x / TPR;
   if (r >= M) return;
-  const int d0 = 8 * (threadIdx.x % TPR);
   const int nkeys = P + T;
   // splits that saw keys (a prefix): the same partition as the attention kernel's
   const int n_act = rel ? min(n_split, (nkeys + KT - 1) / KT) : (nkeys + chunk_keys - 1) / chunk_keys;
-  const long long base = (long long)bg * n_split * m_pad + r;
   float mx = -INFINITY, l = 0.0f;
   float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < n_act; s0 += BATCH) {
-    float ms[BATCH], ls[BATCH];
-    h8 x[BATCH];
-#pragma unroll
-    for (int j = 0; j < BATCH; ++j) {
-      const long long pr = base + (long long)min(s0 + j, n_act - 1) * m_pad;
-      ms[j] = ws_ml[2 * pr];
-      ls[j] = ws_ml[2 * pr + 1];
-      x[j] = *reinterpret_cast<const h8*>(ws_o + pr * D + d0);
-    }
+    if (s0 > 0) load_batch(s0);
     float bm = mx;
 #pragma unroll
     for (int j = 0; j < BATCH; ++j)
@@ -615,10 +622,12 @@ __global__ __launch_bounds__(256) void k_attn_combine(const _Float16* __restrict
     for (int e = 0; e < 8; ++e) o[e] *= a;
 #pragma unroll
     for (int j = 0; j < BATCH; ++j) {
-      const float w = (s0 + j < n_act && ms[j] != -INFINITY) ? __builtin_amdgcn_exp2f(ms[j] - bm) * ls[j] : 0.0f;
-      l += w;
+      if (s0 + j < n_act && ms[j] != -INFINITY) {
+        const float w = __builtin_amdgcn_exp2f(ms[j] - bm) * ls[j];
+        l += w;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = fmaf(w, (float)x[j][e], o[e]);
+        for (int e = 0; e < 8; ++e) o[e] = fmaf(w, (float)x[j][e], o[e]);
+      }
     }
     mx = bm;
   }
