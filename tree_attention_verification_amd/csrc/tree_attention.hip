@@ -14,11 +14,11 @@
 // MFMA with fp32 accumulation.
 //   * A workgroup is 4 or 8 wavefronts; each wavefront owns one block of 32 query
 //     rows and keeps its Q fragments in registers for the whole kernel.
-//   * Keys are streamed in tiles of 64 through double-buffered LDS: K and V rows
-//     are copied with coalesced 16-byte loads into row-major, XOR-swizzled tiles;
-//     the PV operand is read with the gfx950 transpose read (ds_read_b64_tr_b16),
-//     so V is never transposed in registers.  Two register sets keep the loads of
-//     two tiles in flight while a third is computed.
+//   * Keys are streamed in tiles of 64 straight from HBM into LDS with gfx950's
+//     global_load_lds_dwordx4 (no registers), into row-major, XOR-swizzled tile
+//     buffers; one tile is in flight while the previous one is computed.  The PV
+//     operand is read with the gfx950 transpose read (ds_read_b64_tr_b16), so V
+//     is never transposed in registers.
 //   * S^T = K Q^T is formed so that each lane holds 16 keys of one query row:
 //     the row max needs one cross-half exchange, and the accumulator becomes the
 //     PV B-operand directly (keys are permuted consistently in the V^T tile).
@@ -31,14 +31,15 @@
 //   * Long key ranges are split across workgroups (split-KV); each split writes
 //     its running max and row sum (fp32) and its normalised output (fp16, half
 //     the bytes of fp32; the values are bounded by max |v|), and k_attn_combine
-//     merges them with a log-sum-exp weighting.
-//   * The first two K/V tiles, the Q fragments and the mask row are loaded before
-//     the request's tree size and prefix length arrive (keys clamped to the cache
+//     merges them with a log-sum-exp weighting.  With several requests the splits
+//     follow each request's own length and the longest requests start first.
+//   * K/V tile 0, the Q fragments and the mask row are requested before the
+//     request's tree size and prefix length arrive (keys clamped to the cache
 //     slab, nodes to T_max - 1), so the kernel waits for one memory round trip
-//     instead of two before its first tile; rows past the request are zeroed.  Workgroups that share a (request, head,
-//     split) but hold different row blocks are placed on the same XCD (the
-//     dispatcher assigns workgroups round-robin to the 8 XCDs), so their K/V
-//     tiles are fetched from HBM once and hit the shared L2 afterwards.
+//     instead of two before its first tile.  Workgroups that share a (request,
+//     head, split) but hold different row blocks are placed on the same XCD (the
+//     dispatcher assigns workgroups round-robin to the 8 XCDs), so their K/V tiles
+//     are fetched from HBM once and hit the shared L2 afterwards.
 // fp32 path (k_attn_fp32): one wavefront per (request, head, node), keys spread
 // over lanes with a per-lane online softmax, merged through LDS.
 #include "tv_common.h"
@@ -75,7 +76,10 @@ Plan plan_with(int B, int T_max, int Hq, int Hkv, long long S_cap, int nw, long 
   p.rows_wg = 32 * p.nw;
   p.n_rowblk = (int)((m_max + p.rows_wg - 1) / p.rows_wg);
   const long long base = (long long)B * Hkv * p.n_rowblk;
-  const long long target = 512;  // two workgroups per CU
+  // 512 workgroups: two per CU over the run (256 CUs), which leaves room to
+  // balance unequal splits (measured: 256 was 2% faster for equal-length
+  // requests, 30% slower for the ragged batch of 16)
+  const long long target = 512;
   long long max_split = (S_cap + min_keys - 1) / min_keys;
   if (max_split < 1) max_split = 1;
   long long ns = (target + base - 1) / base;
