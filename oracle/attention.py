@@ -100,3 +100,39 @@ def attention_rows(Q, Kc, Vc, prefix_len, tree_size, tree_mask, samples, scale=N
         p = np.exp(s - s.max())
         res.append((p @ v_i) / p.sum())
     return np.array(res)
+
+
+def paged_to_linear(pool, block_table, tokens_per_block, n_rows):
+    """The linear cache [B][Hkv][n_rows][d] a paged pool describes ([TRT] "after
+    acceptance: KV from tree layout back to linear": a token's physical slot is its
+    request's block-table entry plus the offset inside the block).  Row s of request b
+    is pool[block_table[b][s // tokens_per_block], :, s % tokens_per_block]; pool is
+    [n_blocks][Hkv][tokens_per_block][d]."""
+    table = np.asarray(block_table)
+    s = np.arange(n_rows)
+    blk = table[:, s // tokens_per_block]                      # [B][n_rows]
+    off = np.broadcast_to(s % tokens_per_block, blk.shape)     # [B][n_rows]
+    rows = pool[blk, :, off]                                   # [B][n_rows][Hkv][d]
+    return np.ascontiguousarray(rows.transpose(0, 2, 1, 3))
+
+
+def tree_attention_paged(Q, K_pool, V_pool, block_table, tokens_per_block, prefix_len, tree_size, tree_mask,
+                         status=None, scale=None, requests=None):
+    """tree_attention over a paged cache: the rows each request reads (P_b + T_b of them)
+    are gathered through its block table, then the dense definition above applies."""
+    n = max(int(prefix_len[b]) + max(int(tree_size[b]), 1) for b in range(Q.shape[0]))
+    n = min(n, np.asarray(block_table).shape[1] * tokens_per_block)
+    Kc = paged_to_linear(K_pool, block_table, tokens_per_block, n)
+    Vc = paged_to_linear(V_pool, block_table, tokens_per_block, n)
+    return tree_attention(Q, Kc, Vc, prefix_len, tree_size, tree_mask, status=status, scale=scale,
+                          requests=requests)
+
+
+def attention_rows_paged(Q, K_pool, V_pool, block_table, tokens_per_block, prefix_len, tree_size, tree_mask,
+                         samples, scale=None, status=None):
+    """attention_rows over a paged cache (rows gathered through the block table)."""
+    B, T_max = Q.shape[:2]
+    n = min(int(np.max(np.asarray(prefix_len))) + T_max, np.asarray(block_table).shape[1] * tokens_per_block)
+    Kc = paged_to_linear(K_pool, block_table, tokens_per_block, n)
+    Vc = paged_to_linear(V_pool, block_table, tokens_per_block, n)
+    return attention_rows(Q, Kc, Vc, prefix_len, tree_size, tree_mask, samples, scale=scale, status=status)

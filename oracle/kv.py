@@ -38,3 +38,34 @@ def kv_compact(Kc: np.ndarray, Vc: np.ndarray, prefix_len, accept_path, accept_l
     if squeeze:
         K2, V2 = K2[0], V2[0]
     return K2, V2, new_len
+
+
+def kv_compact_paged(K_pool, V_pool, block_table, tokens_per_block, prefix_len, accept_path, accept_len):
+    """The same compaction on a paged cache ([TRT]: the relocation walks the block
+    table and copies inside blocks): logical row s of request b is
+    pool[block_table[b][s // tokens_per_block], :, s % tokens_per_block].
+    K_pool, V_pool: [n_layers][n_blocks][Hkv][bs][d] (or without the layer axis);
+    returns new copies and new_prefix_len."""
+    K2, V2 = np.array(K_pool, copy=True), np.array(V_pool, copy=True)
+    squeeze = K2.ndim == 4
+    if squeeze:
+        K2, V2 = K2[None], V2[None]
+    bs = int(tokens_per_block)
+    B = len(prefix_len)
+    new_len = np.zeros(B, np.int32)
+
+    def slot(b, s):
+        return int(block_table[b][s // bs]), s % bs
+
+    for b in range(B):
+        P, L = int(prefix_len[b]), int(accept_len[b])
+        src = [slot(b, P + int(accept_path[b][k])) for k in range(1, L + 1)]
+        dst = [slot(b, P + k) for k in range(1, L + 1)]
+        for T in (K2, V2):
+            snapshot = [T[:, blk, :, off].copy() for blk, off in src]     # read every source first
+            for (blk, off), rows in zip(dst, snapshot):
+                T[:, blk, :, off] = rows
+        new_len[b] = P + L + 1
+    if squeeze:
+        K2, V2 = K2[0], V2[0]
+    return K2, V2, new_len

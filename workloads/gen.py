@@ -7,7 +7,7 @@ HIP path and the CPU oracle are fed the *same bytes* from here.
 
 Every stream is a PCG64 generator seeded with ``[cfg_id, stream, b]``:
   0 draft logits, 1 Q, 2 K, 3 V, 4 target draws, 5 shapes/topology, 6 root
-  tokens.
+  tokens, 7 paged-cache block placement.
 
 Workload shapes follow the five configurations the tree-verification step is
 measured on (tree sizes as in the EAGLE-2 walkthrough's ``topK_generate``
@@ -23,7 +23,7 @@ from typing import List, Optional
 
 import numpy as np
 
-STREAM_LOGITS, STREAM_Q, STREAM_K, STREAM_V, STREAM_TARGET, STREAM_SHAPE, STREAM_ROOT = range(7)
+STREAM_LOGITS, STREAM_Q, STREAM_K, STREAM_V, STREAM_TARGET, STREAM_SHAPE, STREAM_ROOT, STREAM_PAGES = range(8)
 
 T_MAX_DEFAULT = 64
 DCAP_DEFAULT = 7
@@ -309,3 +309,51 @@ def synthetic_target_predict(w: Workload, draft_tokens: np.ndarray, parents: np.
                 out[b, i] = w.tgt_rand[b, i]
     return out
 
+
+
+@dataclasses.dataclass
+class PagedCache:
+    """A paged copy of a workload's K/V cache (pure data placement, nothing computed).
+
+    K_pool, V_pool [n_blocks][Hkv][tokens_per_block][d]: block_table[b][j] is the
+    physical block that holds logical rows j*tokens_per_block .. (j+1)*tokens_per_block-1
+    of request b (all kv heads).  Blocks no request owns, and rows of a request's last
+    block past the linear cache's S_cap, hold NaN bit patterns."""
+    tokens_per_block: int
+    max_blocks: int
+    n_blocks: int
+    block_table: np.ndarray   # int32 [B][max_blocks]
+    K_pool: np.ndarray
+    V_pool: np.ndarray
+
+    @property
+    def capacity(self) -> int:
+        return self.max_blocks * self.tokens_per_block
+
+
+def nan_bits(dtype) -> object:
+    """A quiet-NaN fill value of the stored element type (uint16 = bfloat16 bits)."""
+    return np.uint16(0x7FC0) if np.dtype(dtype) == np.uint16 else np.float32(np.nan)
+
+
+def paged_layout(w: Workload, tokens_per_block: int, spare_blocks: Optional[int] = None) -> PagedCache:
+    """Place w.Kc / w.Vc block by block at seeded random physical blocks of a pool with
+    ``spare_blocks`` extra blocks (default B*max_blocks/8, at least 1) that no request owns."""
+    B, Hkv, S_cap, d = w.Kc.shape
+    bs = int(tokens_per_block)
+    max_blocks = -(-S_cap // bs)
+    n_used = B * max_blocks
+    spare = max(1, n_used // 8) if spare_blocks is None else int(spare_blocks)
+    n_blocks = n_used + spare
+    perm = rng(w.cfg_id, STREAM_PAGES, 0).permutation(n_blocks)[:n_used].astype(np.int32)
+    table = perm.reshape(B, max_blocks)
+    pools = []
+    for lin in (w.Kc, w.Vc):
+        pool = np.full((n_blocks, Hkv, bs, d), nan_bits(lin.dtype), dtype=lin.dtype)
+        padded = np.full((B, Hkv, max_blocks * bs, d), nan_bits(lin.dtype), dtype=lin.dtype)
+        padded[:, :, :S_cap] = lin
+        # [B][Hkv][max_blocks][bs][d] -> [B][max_blocks][Hkv][bs][d], one physical block each
+        blocks = padded.reshape(B, Hkv, max_blocks, bs, d).transpose(0, 2, 1, 3, 4)
+        pool[table.reshape(-1)] = blocks.reshape(n_used, Hkv, bs, d)
+        pools.append(pool)
+    return PagedCache(bs, max_blocks, n_blocks, table, pools[0], pools[1])
