@@ -5,7 +5,10 @@ kv_compact over one batch of synthetic inputs, all through the C ABI on one HIP
 stream (by default through tree_build_meta, tree_attention, tree_accept_compact:
 the same five stages in two kernel launches fewer; --unfused runs five calls).  The default workload is the EAGLE-2 dynamic tree at batch 1 (top_k 10,
 depth 6, 60 draft nodes + root, prefix 2048, Llama-3-8B attention heads 32/8/128,
-bf16); --config 1..5 selects another of the five measured workloads.
+bf16); --config 1..5 selects another of the five measured workloads, and
+--paged N keeps the K/V cache in a paged pool of N-token blocks placed at seeded
+random physical blocks (tree_attention_paged, tree_accept_compact_paged /
+kv_compact_paged through the block table).
 
 Inputs are resident in HBM before the timed region.  Input copies are rotated
 (>= --rotate-mb of them) so that repeated steps stream from HBM instead of the
@@ -121,8 +124,9 @@ def measured_traffic(workload_name):
     return ent.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, seconds: float):
-    """The oracle, as it stands, on a bounded sample of the same workload."""
+def cpu_baseline(w, seconds: float, paged=None):
+    """The oracle, as it stands, on a bounded sample of the same workload (with a paged
+    cache: the oracle's paged attention and compaction through the block table)."""
     from oracle import attention as oa
     from oracle import kv as okv
     from oracle import tree as ot
@@ -137,10 +141,17 @@ def cpu_baseline(w, seconds: float):
         t = ot.tree_build(ws)
         m = ot.tree_mask_positions(t["parents"], t["tree_size"], ws.prefix_len, ws.T_max, ws.dcap,
                                    t["status"] if ws.mode != "given" else None)
-        oa.tree_attention(ws.Q, ws.Kc, ws.Vc, ws.prefix_len, t["tree_size"], m["tree_mask"], status=m["status"])
         tp = gen.synthetic_target_predict(ws, t["draft_tokens"], t["parents"], t["tree_size"])
         a = ot.tree_accept(t["draft_tokens"], t["parents"], t["tree_size"], tp, m["status"], ws.dcap)
-        okv.kv_compact(ws.Kc, ws.Vc, ws.prefix_len, a["accept_path"], a["accept_len"])
+        if paged is None:
+            oa.tree_attention(ws.Q, ws.Kc, ws.Vc, ws.prefix_len, t["tree_size"], m["tree_mask"], status=m["status"])
+            okv.kv_compact(ws.Kc, ws.Vc, ws.prefix_len, a["accept_path"], a["accept_len"])
+        else:
+            table = paged.block_table[:ws.B]
+            oa.tree_attention_paged(ws.Q, paged.K_pool, paged.V_pool, table, paged.tokens_per_block, ws.prefix_len,
+                                    t["tree_size"], m["tree_mask"], status=m["status"])
+            okv.kv_compact_paged(paged.K_pool, paged.V_pool, table, paged.tokens_per_block, ws.prefix_len,
+                                 a["accept_path"], a["accept_len"])
         return int(np.where(m["status"] != 0, 1, t["tree_size"]).sum())
 
     # sample: the first requests of the batch, as many as fit the time budget
@@ -188,6 +199,8 @@ def main():
     ap.add_argument("--unfused", action="store_true",
                     help="run the step as the five separate calls (default: tree_build_meta, tree_attention, "
                          "tree_accept_compact -- the same five stages in two kernel launches fewer)")
+    ap.add_argument("--paged", type=int, default=0, metavar="N",
+                    help="keep the K/V cache in a paged pool of N-token blocks (a power of two, 1..1024)")
     ap.add_argument("--copy-mb", type=float, default=0.0,
                     help="before warmup, one device-to-device copy of this many MiB (a plain copy kernel of known "
                          "size that calibrates the HBM byte counters of a profiler run)")
@@ -205,10 +218,13 @@ def main():
     _lib.lib()
     torch.cuda.set_device(0)
     w = gen.make_workload(args.config)
-    per_copy = w.Q.nbytes + w.Kc.nbytes + w.Vc.nbytes + (w.logprobs.nbytes if w.logprobs is not None else 0)
+    paged = gen.paged_layout(w, args.paged) if args.paged else None
+    kv_bytes = (w.Kc.nbytes + w.Vc.nbytes) if paged is None else (paged.K_pool.nbytes + paged.V_pool.nbytes)
+    per_copy = w.Q.nbytes + kv_bytes + (w.logprobs.nbytes if w.logprobs is not None else 0)
     n_copies = max(1, min(64, math.ceil(args.rotate_mb * 2 ** 20 / per_copy)))
-    log(f"workload {w.name}: {per_copy / 2**20:.1f} MiB of inputs per copy, {n_copies} copies rotated")
-    step = TreeVerifyStep(w, n_copies=n_copies)
+    workload = w.name if paged is None else f"{w.name}+paged{args.paged}"
+    log(f"workload {workload}: {per_copy / 2**20:.1f} MiB of inputs per copy, {n_copies} copies rotated")
+    step = TreeVerifyStep(w, n_copies=n_copies, paged=paged)
     stream = torch.cuda.current_stream()
 
     if args.copy_mb > 0:
@@ -324,8 +340,9 @@ def main():
         ref = peaks["hbm_copy_GBps"] if roof["unit"] == "GB/s" else peaks["bf16_gemm_TFLOPs"]
         if roof["bound"] in ("hbm", "mfma"):
             roof["frac_of_measured"] = round(roof["achieved"] / ref, 4)
-    roof["traffic"] = measured_traffic(w.name)
-    roof["kernel"] = "tree_attention call (k_attn_bf16 + k_attn_combine when the keys are split)"
+    roof["traffic"] = measured_traffic(workload)
+    roof["kernel"] = (("tree_attention" if paged is None else "tree_attention_paged") +
+                      " call (k_attn_bf16 + k_attn_combine when the keys are split)")
     roof["algorithmic_bytes"] = int(nbytes)
     roof["algorithmic_flops"] = int(flops)
     roof["avg_us"] = round(attn_ms * 1e3, 3)
@@ -344,10 +361,12 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic (seeded draft log-probs, Q/K/V and target argmax; no weights)",
-        "config": {"workload": w.name, "batch": w.B, "prefix_len": [int(x) for x in w.prefix_len[:4]] +
+        "config": {"workload": workload, "batch": w.B, "prefix_len": [int(x) for x in w.prefix_len[:4]] +
                    (["..."] if w.B > 4 else []), "tree_nodes_per_step": nodes, "top_k": w.K, "depth": w.D,
                    "total_tokens": w.total_tokens, "Hq": w.Hq, "Hkv": w.Hkv, "head_dim": w.d, "vocab": w.V,
                    "input_copies_rotated": n_copies, "launch": launch,
+                   "kv_cache": "linear" if paged is None else
+                   f"paged, {args.paged} tokens per block, {paged.n_blocks} blocks in random order",
                    "calls": ("tree_build, tree_mask_positions, tree_attention, tree_accept, kv_compact"
                              if args.unfused else "tree_build_meta, tree_attention, tree_accept_compact")},
         "stages_us": stages,
@@ -357,7 +376,7 @@ def main():
         out["measured_peaks"] = peaks
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, paged)
     print(json.dumps(out), flush=True)
 
 

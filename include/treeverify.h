@@ -11,6 +11,8 @@
  *   tree_accept         target argmax per node -> accepted path, bonus token
  *   kv_compact          accepted path    -> K/V rows moved to contiguous slots
  *   tree_accept_compact the last two in one launch
+ * and the same attention and compaction over a paged K/V cache (a block table
+ * per request): tree_attention_paged, kv_compact_paged, tree_accept_compact_paged.
  *
  * Sources for what each call computes (cited by page title and section):
  *   [E2]  EAGLE v2 dynamic-tree decoding walkthrough -- section 2 initialize_tree
@@ -249,6 +251,54 @@ int tree_accept_compact(int B, int T_max, int dcap, const int* draft_tokens, con
                         int d, int elem_bytes, void* Kc, void* Vc, long long S_cap,
                         long long layer_stride_elems, const int* prefix_len,
                         int* new_prefix_len /* nullable */, void* stream);
+
+/* ------------------------------------------------------------------------- *
+ * Paged K/V cache -- [TRT] "after acceptance: KV from tree layout back to
+ * linear" (the cache is paged: a token's physical slot is given by its request's
+ * block table and its offset inside the block; the relocation kernel walks the
+ * block table and copies inside blocks), [HB] "implementing it in an engine"
+ * (compact the accepted slots, or only update the block table).
+ *
+ * K_pool, V_pool: [num_blocks][Hkv][tokens_per_block][d] elements (kv head g's
+ *   rows of one block are contiguous); for the compaction calls, n_layers such
+ *   pools at element offsets l * layer_stride_elems.
+ * block_table: int32 [B][max_blocks_per_seq]; logical row s of request b (the
+ *   row the linear calls call s) lives in block block_table[b][s /
+ *   tokens_per_block] at offset s % tokens_per_block.  tokens_per_block is a
+ *   power of two in [1, 1024].  A request holds at most S_cap = max_blocks_per_seq
+ *   * tokens_per_block rows, which takes the place of the linear calls' S_cap
+ *   everywhere (workspace size included).
+ * Table entries must lie in [0, num_blocks) for every logical row a call reads
+ *   or writes (rows below prefix_len + tree_size, resp. the accepted path's
+ *   rows).  Entries past those rows are never read.  An entry outside the pool
+ *   is never dereferenced: tree_attention_paged clamps it into the pool (that
+ *   request's output is then unspecified, other requests are unaffected) and
+ *   the compaction calls leave that request untouched (new_prefix_len = P_b + 1,
+ *   as for a path that does not fit).
+ * Everything else -- arguments, results, checks, workspace -- is that of
+ * tree_attention, kv_compact and tree_accept_compact; results equal those calls
+ * on the linear cache the table describes.
+ * ------------------------------------------------------------------------- */
+int tree_attention_paged(int dtype, int B, int T_max, int Hq, int Hkv, int d,
+                         const void* Q, const void* K_pool, const void* V_pool,
+                         long long num_blocks, int tokens_per_block,
+                         const int* block_table, int max_blocks_per_seq,
+                         const int* prefix_len, const int* tree_size, const uint32_t* tree_mask,
+                         const int* status, float scale, void* O,
+                         void* workspace, size_t ws_bytes, void* stream);
+int kv_compact_paged(int B, int n_layers, int Hkv, int d, int elem_bytes,
+                     void* K_pool, void* V_pool, long long num_blocks, int tokens_per_block,
+                     const int* block_table, int max_blocks_per_seq, long long layer_stride_elems,
+                     const int* prefix_len, const int* accept_path, const int* accept_len, int dcap,
+                     int* new_prefix_len /* nullable */, void* stream);
+int tree_accept_compact_paged(int B, int T_max, int dcap, const int* draft_tokens, const int* parents,
+                              const int* tree_size, const int* target_predict, const int* status,
+                              int* accept_len, int* accept_path, int* bonus_token, int n_layers,
+                              int Hkv, int d, int elem_bytes, void* K_pool, void* V_pool,
+                              long long num_blocks, int tokens_per_block, const int* block_table,
+                              int max_blocks_per_seq, long long layer_stride_elems,
+                              const int* prefix_len, int* new_prefix_len /* nullable */,
+                              void* stream);
 
 /* human-readable names for return codes and status codes */
 const char* tv_error_string(int code);

@@ -65,17 +65,19 @@ def check_attention(o_gpu, o_ref, w, tree_size, status, label=""):
     return float(err), 0.0
 
 
-def run_pipeline_and_compare(w, *, attention="full", samples=64, seed=0, fused=False):
+def run_pipeline_and_compare(w, *, attention="full", samples=64, seed=0, fused=False, paged=None):
     """Full pass on the GPU, each stage checked against the oracle.
 
     attention: 'full' compares every written row with the dense oracle; 'sampled'
     compares `samples` random rows (b, i, h) computed one by one by the oracle.
     fused: run the step as tree_build_meta, tree_attention, tree_accept_compact
-    (the same stages, checked against the same oracle results)."""
+    (the same stages, checked against the same oracle results).
+    paged: a workloads.gen.PagedCache of w's cache; attention and compaction then run
+    on that pool and are checked against the oracle's paged functions."""
     import torch
     from tree_attention_verification_amd.step import TreeVerifyStep
 
-    step = TreeVerifyStep(w)
+    step = TreeVerifyStep(w, paged=paged)
     # 1. tree build (with the metadata when fused)
     if fused:
         step.build_meta()
@@ -99,8 +101,13 @@ def run_pipeline_and_compare(w, *, attention="full", samples=64, seed=0, fused=F
     o_gpu = step.out_host()
     status = ref_meta["status"]
     if attention == "full":
-        o_ref = oa.tree_attention(w.Q, w.Kc, w.Vc, w.prefix_len, ref_tree["tree_size"], ref_meta["tree_mask"],
-                                  status=status)
+        if paged is None:
+            o_ref = oa.tree_attention(w.Q, w.Kc, w.Vc, w.prefix_len, ref_tree["tree_size"], ref_meta["tree_mask"],
+                                      status=status)
+        else:
+            o_ref = oa.tree_attention_paged(w.Q, paged.K_pool, paged.V_pool, paged.block_table,
+                                            paged.tokens_per_block, w.prefix_len, ref_tree["tree_size"],
+                                            ref_meta["tree_mask"], status=status)
         errs = check_attention(o_gpu, o_ref, w, ref_tree["tree_size"], status, w.name)
     else:
         rng = np.random.default_rng(seed)
@@ -109,8 +116,13 @@ def run_pipeline_and_compare(w, *, attention="full", samples=64, seed=0, fused=F
         for _ in range(samples):
             b = int(rng.integers(0, w.B))
             picks.append((b, int(rng.integers(0, T_eff[b])), int(rng.integers(0, w.Hq))))
-        ref_rows = oa.attention_rows(w.Q, w.Kc, w.Vc, w.prefix_len, ref_tree["tree_size"], ref_meta["tree_mask"],
-                                     picks, status=status)
+        if paged is None:
+            ref_rows = oa.attention_rows(w.Q, w.Kc, w.Vc, w.prefix_len, ref_tree["tree_size"],
+                                         ref_meta["tree_mask"], picks, status=status)
+        else:
+            ref_rows = oa.attention_rows_paged(w.Q, paged.K_pool, paged.V_pool, paged.block_table,
+                                               paged.tokens_per_block, w.prefix_len, ref_tree["tree_size"],
+                                               ref_meta["tree_mask"], picks, status=status)
         g = np.stack([oa.to_f64(o_gpu[b, i, h]) for b, i, h in picks])
         err = np.abs(g - ref_rows)
         assert np.isfinite(g).all()
@@ -140,7 +152,11 @@ def run_pipeline_and_compare(w, *, attention="full", samples=64, seed=0, fused=F
     if not fused:
         step.compact()
         torch.cuda.synchronize()
-    K2, V2, newlen = okv.kv_compact(w.Kc, w.Vc, w.prefix_len, ref_acc["accept_path"], ref_acc["accept_len"])
+    if paged is None:
+        K2, V2, newlen = okv.kv_compact(w.Kc, w.Vc, w.prefix_len, ref_acc["accept_path"], ref_acc["accept_len"])
+    else:
+        K2, V2, newlen = okv.kv_compact_paged(paged.K_pool, paged.V_pool, paged.block_table, paged.tokens_per_block,
+                                              w.prefix_len, ref_acc["accept_path"], ref_acc["accept_len"])
     kg, vg = step.kv_host()
     np.testing.assert_array_equal(step.accept_host()["new_prefix_len"], newlen)
     assert np.array_equal(kg.view(np.uint8), K2.view(np.uint8)), "compacted K differs"

@@ -73,3 +73,36 @@ def test_python_binding_refuses_host_tensors():
     import torch
     with pytest.raises(ValueError):
         tv.tree_accept(1, 8, 3, torch.zeros(1, 8, dtype=torch.int32), None, None, None, None, None, None, None)
+
+
+def test_paged_calls_host_validation():
+    L = tv.lib()
+    # tree_attention_paged(dtype, B, T_max, Hq, Hkv, d, Q, Kp, Vp, num_blocks, tokens_per_block, table,
+    #                      max_blocks, prefix, size, mask, status, scale, O, ws, ws_bytes, stream)
+    ok_args = (0, 1, 64, 8, 4, 128, X, X, X, 1000, 16, X, 64, X, X, X, X, 0.0, X, None, 0, None)
+    bad_bs = list(ok_args); bad_bs[10] = 24          # not a power of two
+    assert L.tree_attention_paged(*bad_bs) == tv.TV_EINVAL
+    big_bs = list(ok_args); big_bs[10] = 2048        # above 1024 tokens per block
+    assert L.tree_attention_paged(*big_bs) == tv.TV_EINVAL
+    no_table = list(ok_args); no_table[11] = None
+    assert L.tree_attention_paged(*no_table) == tv.TV_EINVAL
+    no_blocks = list(ok_args); no_blocks[9] = 0
+    assert L.tree_attention_paged(*no_blocks) == tv.TV_EINVAL
+    bad_d = list(ok_args); bad_d[5] = 96
+    assert L.tree_attention_paged(*bad_d) == tv.TV_EUNSUPPORTED
+    # the capacity max_blocks * tokens_per_block sizes the workspace like S_cap
+    need = tv.tree_attention_workspace_bytes(0, 1, 64, 32, 8, 128, 4096 * 16)
+    assert need > 0
+    small_ws = (0, 1, 64, 32, 8, 128, X, X, X, 100000, 16, X, 4096, X, X, X, X, 0.0, X, X, need - 1, None)
+    assert L.tree_attention_paged(*small_ws) == tv.TV_EWORKSPACE
+    # kv_compact_paged(B, n_layers, Hkv, d, elem, Kp, Vp, num_blocks, bs, table, max_blocks, stride, prefix,
+    #                  path, len, dcap, newlen, stream)
+    assert L.kv_compact_paged(1, 1, 8, 128, 2, X, X, 100, 3, X, 10, 0, X, X, X, 7, None, None) == tv.TV_EINVAL
+    assert L.kv_compact_paged(1, 1, 8, 128, 2, X, X, 100, 16, None, 10, 0, X, X, X, 7, None, None) == tv.TV_EINVAL
+    assert L.kv_compact_paged(1, 1, 8, 100, 2, X, X, 100, 16, X, 10, 0, X, X, X, 7, None, None) == tv.TV_EUNSUPPORTED
+    # several layers need a layer stride of at least one pool
+    assert L.kv_compact_paged(1, 2, 8, 128, 2, X, X, 100, 16, X, 10, 100 * 8 * 16 * 128 - 8, X, X, X, 7, None,
+                              None) == tv.TV_EINVAL
+    # tree_accept_compact_paged: tree_accept's checks first (dcap >= T_max)
+    assert L.tree_accept_compact_paged(1, 16, 16, X, X, X, X, X, X, X, X, 1, 8, 128, 2, X, X, 100, 16, X, 10, 0,
+                                       X, None, None) == tv.TV_EINVAL

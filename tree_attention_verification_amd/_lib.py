@@ -50,6 +50,9 @@ _SIGS = {
     "tree_accept": (I, [I, I, I, P, P, P, P, P, P, P, P, P]),
     "kv_compact": (I, [I, I, I, I, I, P, P, LL, LL, P, P, P, I, P, P]),
     "tree_accept_compact": (I, [I, I, I, P, P, P, P, P, P, P, P, I, I, I, I, P, P, LL, LL, P, P, P]),
+    "tree_attention_paged": (I, [I, I, I, I, I, I, P, P, P, LL, I, P, I, P, P, P, P, F, P, P, SZ, P]),
+    "kv_compact_paged": (I, [I, I, I, I, I, P, P, LL, I, P, I, LL, P, P, P, I, P, P]),
+    "tree_accept_compact_paged": (I, [I, I, I, P, P, P, P, P, P, P, P, I, I, I, I, P, P, LL, I, P, I, LL, P, P, P]),
     "tv_error_string": (ctypes.c_char_p, [I]),
     "tv_status_string": (ctypes.c_char_p, [I]),
 }
@@ -210,3 +213,43 @@ def tree_accept_compact(B, T_max, dcap, draft_tokens, parents, tree_size, target
                                    _dev(prefix_len, "prefix_len"), _dev(new_prefix_len, "new_prefix_len"),
                                    _stream(stream))
     _check("tree_accept_compact", rc)
+
+
+def tree_attention_paged(dtype, B, T_max, Hq, Hkv, d, Q, K_pool, V_pool, num_blocks, tokens_per_block, block_table,
+                         max_blocks_per_seq, prefix_len, tree_size, tree_mask, status, scale, O, workspace,
+                         stream=None):
+    wp, wn = _ws(workspace)
+    rc = lib().tree_attention_paged(dtype, B, T_max, Hq, Hkv, d, _dev(Q, "Q"), _dev(K_pool, "K_pool"),
+                                    _dev(V_pool, "V_pool"), num_blocks, tokens_per_block,
+                                    _dev(block_table, "block_table"), max_blocks_per_seq,
+                                    _dev(prefix_len, "prefix_len"), _dev(tree_size, "tree_size"),
+                                    _dev(tree_mask, "tree_mask"), _dev(status, "status"), float(scale), _dev(O, "O"),
+                                    wp, wn, _stream(stream))
+    _check("tree_attention_paged", rc)
+
+
+def kv_compact_paged(B, n_layers, Hkv, d, elem_bytes, K_pool, V_pool, num_blocks, tokens_per_block, block_table,
+                     max_blocks_per_seq, layer_stride_elems, prefix_len, accept_path, accept_len, dcap,
+                     new_prefix_len, stream=None):
+    rc = lib().kv_compact_paged(B, n_layers, Hkv, d, elem_bytes, _dev(K_pool, "K_pool"), _dev(V_pool, "V_pool"),
+                                num_blocks, tokens_per_block, _dev(block_table, "block_table"), max_blocks_per_seq,
+                                layer_stride_elems, _dev(prefix_len, "prefix_len"), _dev(accept_path, "accept_path"),
+                                _dev(accept_len, "accept_len"), dcap, _dev(new_prefix_len, "new_prefix_len"),
+                                _stream(stream))
+    _check("kv_compact_paged", rc)
+
+
+def tree_accept_compact_paged(B, T_max, dcap, draft_tokens, parents, tree_size, target_predict, status, accept_len,
+                              accept_path, bonus_token, n_layers, Hkv, d, elem_bytes, K_pool, V_pool, num_blocks,
+                              tokens_per_block, block_table, max_blocks_per_seq, layer_stride_elems, prefix_len,
+                              new_prefix_len, stream=None):
+    rc = lib().tree_accept_compact_paged(B, T_max, dcap, _dev(draft_tokens, "draft_tokens"),
+                                         _dev(parents, "parents"), _dev(tree_size, "tree_size"),
+                                         _dev(target_predict, "target_predict"), _dev(status, "status"),
+                                         _dev(accept_len, "accept_len"), _dev(accept_path, "accept_path"),
+                                         _dev(bonus_token, "bonus_token"), n_layers, Hkv, d, elem_bytes,
+                                         _dev(K_pool, "K_pool"), _dev(V_pool, "V_pool"), num_blocks,
+                                         tokens_per_block, _dev(block_table, "block_table"), max_blocks_per_seq,
+                                         layer_stride_elems, _dev(prefix_len, "prefix_len"),
+                                         _dev(new_prefix_len, "new_prefix_len"), _stream(stream))
+    _check("tree_accept_compact_paged", rc)

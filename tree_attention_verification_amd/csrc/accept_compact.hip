@@ -74,28 +74,48 @@ constexpr int kCompactThreads = 256;
 
 // Moves request b's accepted rows of one (kv head, layer).  The caller has
 // written s_path[0..dcap] (the first barrier here publishes it) and passes the
-// length L.
+// length L.  S_cap is the rows a request can hold (the linear slab, or the
+// block-table capacity); with a paged cache every source and destination row is
+// looked up in the request's block table once, and an entry outside the pool
+// leaves the request untouched like a path that does not fit.
 __device__ __forceinline__ void compact_rows(int b, int g, int layer, int Hkv, int chunks16, uint4* __restrict__ Kc,
                                              uint4* __restrict__ Vc, long long S_cap, long long layer_stride16,
                                              int P, int L, const int* s_path, int dcap,
-                                             int* __restrict__ new_prefix_len) {
+                                             int* __restrict__ new_prefix_len, const Paging& pg) {
   const int tid = threadIdx.x;
   __shared__ int s_bad;
+  __shared__ long long s_src[64], s_dst[64];  // 16-byte chunk offsets of rows P + path[k] and P + k
   if (tid == 0) s_bad = 0;
   __syncthreads();
+  // offset of logical row s (0 <= s < S_cap) of (b, g) in this layer; false for a
+  // block-table entry outside the pool
+  auto row16 = [&](long long s, long long& off) -> bool {
+    long long r;
+    if (pg.table) {
+      const long long blk = pg.table[(long long)b * pg.max_blocks + (s >> pg.lbs)];
+      if (blk < 0 || blk >= pg.n_blocks) return false;
+      r = ((blk * Hkv + g) << pg.lbs) + (s & ((1 << pg.lbs) - 1));
+    } else {
+      r = ((long long)b * Hkv + g) * S_cap + s;
+    }
+    off = layer * layer_stride16 + r * chunks16;
+    return true;
+  };
   // every source and destination row must lie inside the cache
   if (tid >= 1 && tid <= L && tid <= dcap) {
     const int n = s_path[tid];
-    if (n < tid || (long long)P + n >= S_cap) s_bad = 1;
+    long long so = 0, dof = 0;
+    const bool bad = P < 0 || n < tid || (long long)P + n >= S_cap || !row16((long long)P + n, so) ||
+                     !row16((long long)P + tid, dof);
+    if (bad) s_bad = 1;
+    s_src[tid] = so;
+    s_dst[tid] = dof;
   }
   __syncthreads();
   const bool ok = L >= 1 && L <= dcap && P >= 0 && s_bad == 0;
   // a request whose path does not fit is left untouched (its prefix grows by the root only)
   if (g == 0 && layer == 0 && tid == 0 && new_prefix_len) new_prefix_len[b] = P + (ok ? L : 0) + 1;
   if (!ok) return;
-  const long long head = ((long long)layer * layer_stride16) + ((long long)b * Hkv + g) * S_cap * chunks16;
-  uint4* kb = Kc + head;
-  uint4* vb = Vc + head;
   // every K and V source row is read into LDS before any destination is written
   // (a source may be an earlier destination); stage = [K rows | V rows]
   extern __shared__ uint4 s_stage[];
@@ -104,14 +124,14 @@ __device__ __forceinline__ void compact_rows(int b, int g, int layer, int Hkv, i
   for (int q = tid; q < 2 * items; q += kCompactThreads) {
     const int t = q >= items, r = q - t * items;
     const int k = 1 + r / chunks16, c = r % chunks16;
-    s_stage[q] = (t ? vb : kb)[((long long)P + s_path[k]) * chunks16 + c];
+    s_stage[q] = (t ? Vc : Kc)[s_src[k] + c];
   }
   __syncthreads();
 #pragma unroll 4
   for (int q = tid; q < 2 * items; q += kCompactThreads) {
     const int t = q >= items, r = q - t * items;
     const int k = 1 + r / chunks16, c = r % chunks16;
-    (t ? vb : kb)[((long long)P + k) * chunks16 + c] = s_stage[q];
+    (t ? Vc : Kc)[s_dst[k] + c] = s_stage[q];
   }
 }
 
@@ -121,7 +141,7 @@ __global__ __launch_bounds__(kCompactThreads) void k_kv_compact(int Hkv, int chu
                                                                 const int* __restrict__ prefix_len,
                                                                 const int* __restrict__ accept_path,
                                                                 const int* __restrict__ accept_len, int dcap,
-                                                                int* __restrict__ new_prefix_len) {
+                                                                int* __restrict__ new_prefix_len, Paging pg) {
   const int g = blockIdx.x % Hkv;
   const int b = blockIdx.x / Hkv;
   const int tid = threadIdx.x;
@@ -131,7 +151,8 @@ __global__ __launch_bounds__(kCompactThreads) void k_kv_compact(int Hkv, int chu
   const int P = prefix_len[b];
   const int L = accept_len[b];
   if (tid <= dcap) s_path[tid] = accept_path[(long long)b * (dcap + 1) + tid];
-  compact_rows(b, g, blockIdx.y, Hkv, chunks16, Kc, Vc, S_cap, layer_stride16, P, L, s_path, dcap, new_prefix_len);
+  compact_rows(b, g, blockIdx.y, Hkv, chunks16, Kc, Vc, S_cap, layer_stride16, P, L, s_path, dcap, new_prefix_len,
+               pg);
 }
 
 // tree_accept and kv_compact in one launch: every (request, kv head, layer)
@@ -143,7 +164,7 @@ __global__ __launch_bounds__(kCompactThreads) void k_accept_compact(
     const int* __restrict__ tree_size, const int* __restrict__ target_predict, const int* __restrict__ status,
     int* __restrict__ accept_len, int* __restrict__ accept_path, int* __restrict__ bonus_token, int Hkv,
     int chunks16, uint4* __restrict__ Kc, uint4* __restrict__ Vc, long long S_cap, long long layer_stride16,
-    const int* __restrict__ prefix_len, int* __restrict__ new_prefix_len) {
+    const int* __restrict__ prefix_len, int* __restrict__ new_prefix_len, Paging pg) {
   const int g = blockIdx.x % Hkv;
   const int b = blockIdx.x / Hkv;
   const int tid = threadIdx.x;
@@ -164,7 +185,7 @@ __global__ __launch_bounds__(kCompactThreads) void k_accept_compact(
   }
   __syncthreads();
   compact_rows(b, g, blockIdx.y, Hkv, chunks16, Kc, Vc, S_cap, layer_stride16, P, s_len, s_path, dcap,
-               new_prefix_len);
+               new_prefix_len, pg);
 }
 
 }  // namespace
@@ -184,28 +205,109 @@ extern "C" int tree_accept(int B, int T_max, int dcap, const int* draft_tokens, 
   return TV_OK;
 }
 
-extern "C" int kv_compact(int B, int n_layers, int Hkv, int d, int elem_bytes, void* Kc, void* Vc, long long S_cap,
-                          long long layer_stride_elems, const int* prefix_len, const int* accept_path,
-                          const int* accept_len, int dcap, int* new_prefix_len, void* stream) {
+namespace tv {
+namespace {
+
+// checks shared by the compaction entry points; returns TV_OK and the 16-byte
+// chunks per row, or an error code.  S_cap: rows a request can hold; per_layer:
+// elements of one layer's cache (pool) per tensor.
+int compact_checks(int B, int n_layers, int Hkv, int d, int elem_bytes, const void* Kc, const void* Vc,
+                   long long S_cap, long long per_layer, long long layer_stride_elems, int dcap, int* chunks16,
+                   size_t* stage) {
   if (B <= 0 || n_layers <= 0 || Hkv <= 0 || d <= 0 || S_cap <= 0 || dcap < 0 || dcap >= 64) return TV_EINVAL;
   if (elem_bytes != 2 && elem_bytes != 4) return TV_EINVAL;
-  if (!Kc || !Vc || !prefix_len || !accept_path || !accept_len) return TV_EINVAL;
+  if (!Kc || !Vc) return TV_EINVAL;
   const long long row_bytes = (long long)d * elem_bytes;
   if (row_bytes % 16 != 0 || row_bytes > 1024) return TV_EUNSUPPORTED;
-  const long long per_layer = (long long)B * Hkv * S_cap * d;
   if (n_layers > 1 && layer_stride_elems < per_layer) return TV_EINVAL;
   if ((layer_stride_elems * elem_bytes) % 16 != 0) return TV_EINVAL;
   if ((reinterpret_cast<uintptr_t>(Kc) & 15) || (reinterpret_cast<uintptr_t>(Vc) & 15)) return TV_EINVAL;
   if ((long long)B * Hkv > 2147483647LL || n_layers > 65535) return TV_EINVAL;
-  const int chunks16 = (int)(row_bytes / 16);
-  const size_t stage = 2 * (size_t)dcap * (size_t)(row_bytes / 16) * 16;  // K and V rows of one path
-  if (stage > 65536) return TV_EUNSUPPORTED;
-  hipLaunchKernelGGL(tv::k_kv_compact, dim3(B * Hkv, n_layers), dim3(tv::kCompactThreads), stage,
+  *chunks16 = (int)(row_bytes / 16);
+  *stage = 2 * (size_t)dcap * (size_t)(row_bytes / 16) * 16;  // K and V rows of one path
+  if (*stage > 65536) return TV_EUNSUPPORTED;
+  return TV_OK;
+}
+
+// the paged-cache arguments: Paging and the capacity per request, or an error
+int paged_args(int B, int Hkv, int d, long long num_blocks, int tokens_per_block, const int* block_table,
+               int max_blocks_per_seq, Paging* pg, long long* cap, long long* per_layer) {
+  const int lbs = log2_block(tokens_per_block);
+  if (lbs < 0 || !block_table || max_blocks_per_seq <= 0 || num_blocks <= 0 || Hkv <= 0 || d <= 0) return TV_EINVAL;
+  if ((long long)B * max_blocks_per_seq > (1LL << 31)) return TV_EINVAL;
+  if (num_blocks > (1LL << 40) / ((long long)Hkv * tokens_per_block)) return TV_EINVAL;
+  *pg = Paging{block_table, max_blocks_per_seq, lbs, num_blocks};
+  *cap = (long long)max_blocks_per_seq << lbs;
+  *per_layer = num_blocks * Hkv * tokens_per_block * d;
+  return TV_OK;
+}
+
+int kv_compact_impl(int B, int n_layers, int Hkv, int d, int elem_bytes, void* Kc, void* Vc, long long S_cap,
+                    long long per_layer, long long layer_stride_elems, const int* prefix_len, const int* accept_path,
+                    const int* accept_len, int dcap, int* new_prefix_len, void* stream, const Paging& pg) {
+  int chunks16 = 0;
+  size_t stage = 0;
+  const int rc = compact_checks(B, n_layers, Hkv, d, elem_bytes, Kc, Vc, S_cap, per_layer, layer_stride_elems, dcap,
+                                &chunks16, &stage);
+  if (rc != TV_OK) return rc;
+  if (!prefix_len || !accept_path || !accept_len) return TV_EINVAL;
+  hipLaunchKernelGGL(k_kv_compact, dim3(B * Hkv, n_layers), dim3(kCompactThreads), stage,
                      reinterpret_cast<hipStream_t>(stream), Hkv, chunks16, reinterpret_cast<uint4*>(Kc),
                      reinterpret_cast<uint4*>(Vc), S_cap, layer_stride_elems * elem_bytes / 16, prefix_len,
-                     accept_path, accept_len, dcap, new_prefix_len);
+                     accept_path, accept_len, dcap, new_prefix_len, pg);
   TV_CHECK_LAUNCH();
   return TV_OK;
+}
+
+int accept_compact_impl(int B, int T_max, int dcap, const int* draft_tokens, const int* parents,
+                        const int* tree_size, const int* target_predict, const int* status, int* accept_len,
+                        int* accept_path, int* bonus_token, int n_layers, int Hkv, int d, int elem_bytes, void* Kc,
+                        void* Vc, long long S_cap, long long per_layer, long long layer_stride_elems,
+                        const int* prefix_len, int* new_prefix_len, void* stream, const Paging& pg) {
+  // the checks of tree_accept, then those of kv_compact
+  if (B <= 0 || T_max <= 0 || dcap < 0 || dcap >= T_max) return TV_EINVAL;
+  if (T_max > kTMaxLimit) return TV_EUNSUPPORTED;
+  if (!draft_tokens || !parents || !tree_size || !target_predict || !status || !accept_len || !accept_path ||
+      !bonus_token)
+    return TV_EINVAL;
+  int chunks16 = 0;
+  size_t stage = 0;
+  const int rc = compact_checks(B, n_layers, Hkv, d, elem_bytes, Kc, Vc, S_cap, per_layer, layer_stride_elems, dcap,
+                                &chunks16, &stage);
+  if (rc != TV_OK) return rc;
+  if (!prefix_len) return TV_EINVAL;
+  hipLaunchKernelGGL(k_accept_compact, dim3(B * Hkv, n_layers), dim3(kCompactThreads), stage,
+                     reinterpret_cast<hipStream_t>(stream), T_max, dcap, draft_tokens, parents, tree_size,
+                     target_predict, status, accept_len, accept_path, bonus_token, Hkv, chunks16,
+                     reinterpret_cast<uint4*>(Kc), reinterpret_cast<uint4*>(Vc), S_cap,
+                     layer_stride_elems * elem_bytes / 16, prefix_len, new_prefix_len, pg);
+  TV_CHECK_LAUNCH();
+  return TV_OK;
+}
+
+}  // namespace
+}  // namespace tv
+
+extern "C" int kv_compact(int B, int n_layers, int Hkv, int d, int elem_bytes, void* Kc, void* Vc, long long S_cap,
+                          long long layer_stride_elems, const int* prefix_len, const int* accept_path,
+                          const int* accept_len, int dcap, int* new_prefix_len, void* stream) {
+  return tv::kv_compact_impl(B, n_layers, Hkv, d, elem_bytes, Kc, Vc, S_cap, (long long)B * Hkv * S_cap * d,
+                             layer_stride_elems, prefix_len, accept_path, accept_len, dcap, new_prefix_len, stream,
+                             tv::Paging{});
+}
+
+extern "C" int kv_compact_paged(int B, int n_layers, int Hkv, int d, int elem_bytes, void* K_pool, void* V_pool,
+                                long long num_blocks, int tokens_per_block, const int* block_table,
+                                int max_blocks_per_seq, long long layer_stride_elems, const int* prefix_len,
+                                const int* accept_path, const int* accept_len, int dcap, int* new_prefix_len,
+                                void* stream) {
+  tv::Paging pg{};
+  long long cap = 0, per_layer = 0;
+  const int rc = tv::paged_args(B, Hkv, d, num_blocks, tokens_per_block, block_table, max_blocks_per_seq, &pg, &cap,
+                                &per_layer);
+  if (rc != TV_OK) return rc;
+  return tv::kv_compact_impl(B, n_layers, Hkv, d, elem_bytes, K_pool, V_pool, cap, per_layer, layer_stride_elems,
+                             prefix_len, accept_path, accept_len, dcap, new_prefix_len, stream, pg);
 }
 
 extern "C" int tree_accept_compact(int B, int T_max, int dcap, const int* draft_tokens, const int* parents,
@@ -213,32 +315,27 @@ extern "C" int tree_accept_compact(int B, int T_max, int dcap, const int* draft_
                                    int* accept_len, int* accept_path, int* bonus_token, int n_layers, int Hkv, int d,
                                    int elem_bytes, void* Kc, void* Vc, long long S_cap, long long layer_stride_elems,
                                    const int* prefix_len, int* new_prefix_len, void* stream) {
-  // the checks of tree_accept, then those of kv_compact
-  if (B <= 0 || T_max <= 0 || dcap < 0 || dcap >= T_max) return TV_EINVAL;
-  if (T_max > tv::kTMaxLimit) return TV_EUNSUPPORTED;
-  if (!draft_tokens || !parents || !tree_size || !target_predict || !status || !accept_len || !accept_path ||
-      !bonus_token)
-    return TV_EINVAL;
-  if (n_layers <= 0 || Hkv <= 0 || d <= 0 || S_cap <= 0) return TV_EINVAL;
-  if (elem_bytes != 2 && elem_bytes != 4) return TV_EINVAL;
-  if (!Kc || !Vc || !prefix_len) return TV_EINVAL;
-  const long long row_bytes = (long long)d * elem_bytes;
-  if (row_bytes % 16 != 0 || row_bytes > 1024) return TV_EUNSUPPORTED;
-  const long long per_layer = (long long)B * Hkv * S_cap * d;
-  if (n_layers > 1 && layer_stride_elems < per_layer) return TV_EINVAL;
-  if ((layer_stride_elems * elem_bytes) % 16 != 0) return TV_EINVAL;
-  if ((reinterpret_cast<uintptr_t>(Kc) & 15) || (reinterpret_cast<uintptr_t>(Vc) & 15)) return TV_EINVAL;
-  if ((long long)B * Hkv > 2147483647LL || n_layers > 65535) return TV_EINVAL;
-  const int chunks16 = (int)(row_bytes / 16);
-  const size_t stage = 2 * (size_t)dcap * (size_t)(row_bytes / 16) * 16;
-  if (stage > 65536) return TV_EUNSUPPORTED;
-  hipLaunchKernelGGL(tv::k_accept_compact, dim3(B * Hkv, n_layers), dim3(tv::kCompactThreads), stage,
-                     reinterpret_cast<hipStream_t>(stream), T_max, dcap, draft_tokens, parents, tree_size,
-                     target_predict, status, accept_len, accept_path, bonus_token, Hkv, chunks16,
-                     reinterpret_cast<uint4*>(Kc), reinterpret_cast<uint4*>(Vc), S_cap,
-                     layer_stride_elems * elem_bytes / 16, prefix_len, new_prefix_len);
-  TV_CHECK_LAUNCH();
-  return TV_OK;
+  return tv::accept_compact_impl(B, T_max, dcap, draft_tokens, parents, tree_size, target_predict, status, accept_len,
+                                 accept_path, bonus_token, n_layers, Hkv, d, elem_bytes, Kc, Vc, S_cap,
+                                 (long long)B * Hkv * S_cap * d, layer_stride_elems, prefix_len, new_prefix_len,
+                                 stream, tv::Paging{});
+}
+
+extern "C" int tree_accept_compact_paged(int B, int T_max, int dcap, const int* draft_tokens, const int* parents,
+                                         const int* tree_size, const int* target_predict, const int* status,
+                                         int* accept_len, int* accept_path, int* bonus_token, int n_layers, int Hkv,
+                                         int d, int elem_bytes, void* K_pool, void* V_pool, long long num_blocks,
+                                         int tokens_per_block, const int* block_table, int max_blocks_per_seq,
+                                         long long layer_stride_elems, const int* prefix_len, int* new_prefix_len,
+                                         void* stream) {
+  tv::Paging pg{};
+  long long cap = 0, per_layer = 0;
+  const int rc = tv::paged_args(B, Hkv, d, num_blocks, tokens_per_block, block_table, max_blocks_per_seq, &pg, &cap,
+                                &per_layer);
+  if (rc != TV_OK) return rc;
+  return tv::accept_compact_impl(B, T_max, dcap, draft_tokens, parents, tree_size, target_predict, status, accept_len,
+                                 accept_path, bonus_token, n_layers, Hkv, d, elem_bytes, K_pool, V_pool, cap,
+                                 per_layer, layer_stride_elems, prefix_len, new_prefix_len, stream, pg);
 }
 
 extern "C" const char* tv_error_string(int code) {

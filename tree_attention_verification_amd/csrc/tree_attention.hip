@@ -158,13 +158,13 @@ __device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
 // and lgkmcnt left at their maximum)
 constexpr int vm_wait_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-template <int D, int NW, int NSTAGE>
+template <int D, int NW, int NSTAGE, bool PAGED>
 __global__ __launch_bounds__(NW * 64, (NSTAGE == 2 && NW == 4) ? 2 : 1) void k_attn_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Kc, const uint16_t* __restrict__ Vc,
     long long S_cap, const int* __restrict__ prefix_len, const int* __restrict__ tree_size,
     const uint32_t* __restrict__ tree_mask, const int* __restrict__ status, int T_max, int Hq, int Hkv, int W,
     float sl2, uint16_t* __restrict__ O, _Float16* __restrict__ ws_o, float* __restrict__ ws_ml, int n_split,
-    int chunk_keys, int n_rowblk, int n_units, long long m_pad, int B, int rel) {
+    int chunk_keys, int n_rowblk, int n_units, long long m_pad, int B, int rel, Paging pg) {
   constexpr int NT = NW * 64;
   constexpr int KSTEPS = D / 16;     // 16-wide k-steps of QK^T (KSTEPS/2 per half of d)
   constexpr int DB = D / 32;         // 32-wide d blocks of the output
@@ -174,6 +174,7 @@ __global__ __launch_bounds__(NW * 64, (NSTAGE == 2 && NW == 4) ? 2 : 1) void k_a
   // measured on MI355X, one tile in flight beat three at every configuration
   // (cfg2 18.3 -> 16.4 us, cfg3 93.6 -> 89.6, cfg4 284 -> 279, cfg5 264 -> 256).
   static_assert(NSTAGE == 2 || NSTAGE == 4, "two or four stage buffers");
+  static_assert(!PAGED || NSTAGE == 2, "the paged cache's block numbers are fetched one tile ahead");
   constexpr int kAhead = 5;         // LDS fragment reads issued ahead of the MFMAs that use them
   constexpr int INSTR = KT * CH / 64;  // 64-lane DMA instructions per tensor per tile
   static_assert(INSTR % NW == 0, "DMA instructions split evenly over the wavefronts");
@@ -233,8 +234,12 @@ __global__ __launch_bounds__(NW * 64, (NSTAGE == 2 && NW == 4) ? 2 : 1) void k_a
   const int row0 = rbk * NW * 32;
   int k_begin = split * chunk_keys;  // (rel: set once the request's size is known)
 
-  const uint16_t* Kb = Kc + ((long long)b * Hkv + g) * S_cap * D;
-  const uint16_t* Vb = Vc + ((long long)b * Hkv + g) * S_cap * D;
+  // linear cache: row `key` of (b, g) is Kb + key D.  Paged cache: it is row
+  // ((blk Hkv + g) << lbs) + key % tokens_per_block of the pool, blk the request's
+  // block-table entry for key >> lbs, so Kb holds the g << lbs part.
+  const uint16_t* Kb = Kc + (PAGED ? ((long long)g << pg.lbs) : ((long long)b * Hkv + g) * S_cap) * D;
+  const uint16_t* Vb = Vc + (PAGED ? ((long long)g << pg.lbs) : ((long long)b * Hkv + g) * S_cap) * D;
+  const int* const bt = PAGED ? pg.table + (long long)b * pg.max_blocks : nullptr;
 
   // ---- tile staging: K/V tiles go straight from global memory into LDS (no
   // registers) through NSTAGE stage buffers; tile t + NSTAGE - 1 is requested
@@ -244,15 +249,35 @@ __global__ __launch_bounds__(NW * 64, (NSTAGE == 2 && NW == 4) ? 2 : 1) void k_a
   // wait before tile t allows exactly the younger tiles that were requested (up to
   // NSTAGE - 2) to stay in flight.
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform (LDS base goes to m0)
+  // paged cache: the block numbers of this lane's rows of the next tile to be
+  // requested, loaded one tile ahead.  They are kept as loaded and only clamped
+  // into the pool (so a bad table cannot make the kernel read outside it) where
+  // the copy uses them: arithmetic on them here would make the wavefront wait
+  // for the load, and with it for the tile copy issued just before.
+  int pblk[PAGED ? INSTR / NW : 1];
+  auto load_tbl = [&](int kt0, int last_key) __attribute__((always_inline)) {
+    if constexpr (PAGED) {
+#pragma unroll
+      for (int ii = 0; ii < INSTR / NW; ++ii) {
+        const int row = (64 * (wave_u + ii * NW) + lane) / CH;
+        pblk[ii] = bt[min(kt0 + row, last_key) >> pg.lbs];
+      }
+    }
+  };
   auto dma_tile = [&](int kt0, int last_key, int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int ii = 0; ii < INSTR / NW; ++ii) {
       const int i = wave_u + ii * NW;
       const int idx = 64 * i + lane;
       const int row = idx / CH, cs = idx % CH;
-      const long long key = min(kt0 + row, last_key);
-      dma16(Kb + key * D + 8 * (cs ^ kswz(row)), kv_base + buf * TB + 1024u * i);
-      dma16(Vb + key * D + 8 * (cs ^ vswz(row)), kv_base + (NSTAGE + buf) * TB + 1024u * i);
+      const int key = min(kt0 + row, last_key);
+      long long roff = key;
+      if constexpr (PAGED) {
+        const long long blk = min(max((long long)pblk[ii], 0ll), pg.n_blocks - 1);
+        roff = ((blk * Hkv) << pg.lbs) + (key & ((1 << pg.lbs) - 1));
+      }
+      dma16(Kb + roff * D + 8 * (cs ^ kswz(row)), kv_base + buf * TB + 1024u * i);
+      dma16(Vb + roff * D + 8 * (cs ^ vswz(row)), kv_base + (NSTAGE + buf) * TB + 1024u * i);
     }
   };
 
@@ -262,7 +287,8 @@ __global__ __launch_bounds__(NW * 64, (NSTAGE == 2 && NW == 4) ? 2 : 1) void k_a
   // to T_max - 1.  What lies past the request is neutralised below.
   const int r = row0 + wave * 32 + l32;
   const int i_row = min(r / rep, T_max - 1);
-  if (!rel) dma_tile(k_begin, (int)S_cap - 1, 0);
+  // (paged: the first tile's block numbers wait for the request's sizes)
+  if (!PAGED && !rel) dma_tile(k_begin, (int)S_cap - 1, 0);
   bf16x8 qf[KSTEPS];
   {
     const int head = g * rep + r % rep;
@@ -308,6 +334,7 @@ __global__ __launch_bounds__(NW * 64, (NSTAGE == 2 && NW == 4) ? 2 : 1) void k_a
     k_begin = t0 * KT;
     k_end = min(nkeys, t1 * KT);
     n_tiles = t1 - t0;
+    load_tbl(k_begin, nkeys - 1);
     dma_tile(k_begin, nkeys - 1, 0);
   } else {
     if (k_begin >= nkeys) {
@@ -321,8 +348,15 @@ __global__ __launch_bounds__(NW * 64, (NSTAGE == 2 && NW == 4) ? 2 : 1) void k_a
     // fetch it again with keys clamped to the last key (its scores there are
     // masked to -inf, and finite V rows keep 0 * garbage out of the PV product).
     // The re-fetch lands after the first one (returns are in order).
-    if (k_begin + KT > nkeys) dma_tile(k_begin, nkeys - 1, 0);
+    if (PAGED) {
+      load_tbl(k_begin, nkeys - 1);
+      dma_tile(k_begin, nkeys - 1, 0);
+    } else if (k_begin + KT > nkeys) {
+      dma_tile(k_begin, nkeys - 1, 0);
+    }
   }
+  // paged: the block numbers of tile 1 travel with tile 0
+  if (n_tiles > 1) load_tbl(k_begin + KT, nkeys - 1);
   // padding query rows get a zero Q and no mask
   if (r >= M) {
 #pragma unroll
@@ -517,8 +551,12 @@ __global__ __launch_bounds__(NW * 64, (NSTAGE == 2 && NW == 4) ? 2 : 1) void k_a
     else if (NSTAGE == 4 && younger == 1) __builtin_amdgcn_s_waitcnt(vm_wait_imm(DMA_WAVE));
     else __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
     lds_barrier();
-    if (t + NSTAGE - 1 < n_tiles)
+    if (t + NSTAGE - 1 < n_tiles) {
       dma_tile(k_begin + (t + NSTAGE - 1) * KT, nkeys - 1, (buf + NSTAGE - 1) % NSTAGE);
+      // paged: the block numbers of the tile after it (the wait at the next step
+      // covers them, so the compiler's own wait before their use costs nothing)
+      if (t + NSTAGE < n_tiles) load_tbl(k_begin + (t + NSTAGE) * KT, nkeys - 1);
+    }
     if (active) compute(t, buf);
   };
   for (int t = 0; t < n_tiles; t += NSTAGE) {
@@ -643,14 +681,14 @@ __global__ __launch_bounds__(256) void k_attn_combine(const _Float16* __restrict
 }
 
 // fp32 path: one wavefront per (node, query head, request).
-template <int D>
+template <int D, bool PAGED>
 __global__ __launch_bounds__(64) void k_attn_fp32(const float* __restrict__ Q, const float* __restrict__ Kc,
                                                   const float* __restrict__ Vc, long long S_cap,
                                                   const int* __restrict__ prefix_len,
                                                   const int* __restrict__ tree_size,
                                                   const uint32_t* __restrict__ tree_mask,
                                                   const int* __restrict__ status, int T_max, int Hq, int Hkv, int W,
-                                                  float scale, float* __restrict__ O) {
+                                                  float scale, float* __restrict__ O, Paging pg) {
   const int i = blockIdx.x, hq = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
   int T = tree_size[b];
   const int P = prefix_len[b];
@@ -664,8 +702,16 @@ __global__ __launch_bounds__(64) void k_attn_fp32(const float* __restrict__ Q, c
   const int g = hq / (Hq / Hkv);
   const int nkeys = P + T;
   const float* qp = Q + (((long long)b * T_max + i) * Hq + hq) * D;
-  const float* Kb = Kc + ((long long)b * Hkv + g) * S_cap * D;
-  const float* Vb = Vc + ((long long)b * Hkv + g) * S_cap * D;
+  // row offset of key `key` (linear, or through the block table as in k_attn_bf16)
+  auto row = [&](int key) -> long long {
+    if constexpr (PAGED) {
+      const long long e = pg.table[(long long)b * pg.max_blocks + (key >> pg.lbs)];
+      const long long blk = min(max(e, 0ll), pg.n_blocks - 1);
+      return (((blk * Hkv + g) << pg.lbs) + (key & ((1 << pg.lbs) - 1))) * D;
+    } else {
+      return (((long long)b * Hkv + g) * S_cap + key) * D;
+    }
+  };
   const uint32_t* mp = tree_mask + ((long long)b * T_max + i) * W;
   const unsigned long long mrow = (unsigned long long)mp[0] | (W > 1 ? ((unsigned long long)mp[1] << 32) : 0ull);
   __shared__ float s_q[D];
@@ -676,7 +722,8 @@ __global__ __launch_bounds__(64) void k_attn_fp32(const float* __restrict__ Q, c
   for (int d = 0; d < D; ++d) acc[d] = 0.0f;
   for (int key = lane; key < nkeys; key += 64) {
     if (!(key < P || ((mrow >> (key - P)) & 1ull))) continue;
-    const float* kr = Kb + (long long)key * D;
+    const long long ro = row(key);
+    const float* kr = Kc + ro;
     float sc = 0.0f;
 #pragma unroll
     for (int d = 0; d < D; ++d) sc = fmaf(s_q[d], kr[d], sc);
@@ -684,7 +731,7 @@ __global__ __launch_bounds__(64) void k_attn_fp32(const float* __restrict__ Q, c
     const float mn = fmaxf(m, sc);
     const float a = expf(m - mn);  // m = -inf -> 0
     const float p = expf(sc - mn);
-    const float* vr = Vb + (long long)key * D;
+    const float* vr = Vc + ro;
     l = l * a + p;
 #pragma unroll
     for (int d = 0; d < D; ++d) acc[d] = fmaf(p, vr[d], acc[d] * a);
@@ -710,18 +757,95 @@ __global__ __launch_bounds__(64) void k_attn_fp32(const float* __restrict__ Q, c
   }
 }
 
-template <int D, int NW, int NS>
+template <int D, int NW, int NS, bool PAGED>
 void launch_bf16(const Plan& p, int B, hipStream_t s, const void* Q, const void* Kc, const void* Vc, long long S_cap,
                  const int* prefix_len, const int* tree_size, const uint32_t* tree_mask, const int* status,
-                 int T_max, int Hq, int Hkv, int W, float sl2, void* O, _Float16* ws_o, float* ws_ml) {
-  hipLaunchKernelGGL((k_attn_bf16<D, NW, NS>), dim3(p.grid), dim3(NW * 64), 0, s, (const uint16_t*)Q, (const uint16_t*)Kc,
-                     (const uint16_t*)Vc, S_cap, prefix_len, tree_size, tree_mask, status, T_max, Hq, Hkv, W, sl2,
-                     (uint16_t*)O, ws_o, ws_ml, p.n_split, p.chunk_keys, p.n_rowblk, p.n_units, p.m_pad, B, p.rel);
+                 int T_max, int Hq, int Hkv, int W, float sl2, void* O, _Float16* ws_o, float* ws_ml,
+                 const Paging& pg) {
+  hipLaunchKernelGGL((k_attn_bf16<D, NW, NS, PAGED>), dim3(p.grid), dim3(NW * 64), 0, s, (const uint16_t*)Q,
+                     (const uint16_t*)Kc, (const uint16_t*)Vc, S_cap, prefix_len, tree_size, tree_mask, status, T_max,
+                     Hq, Hkv, W, sl2, (uint16_t*)O, ws_o, ws_ml, p.n_split, p.chunk_keys, p.n_rowblk, p.n_units,
+                     p.m_pad, B, p.rel, pg);
 }
 
 size_t ws_bytes_for(const Plan& p, int B, int Hkv, int d) {
   if (p.n_split <= 1) return 0;
   return (size_t)B * Hkv * p.n_split * p.m_pad * ((size_t)d * sizeof(_Float16) + 2 * sizeof(float)) + 256;
+}
+
+// Both entry points: S_cap is the rows each request can hold (the linear slab, or
+// max_blocks << lbs with a block table).
+int attention_impl(int dtype, int B, int T_max, int Hq, int Hkv, int d, const void* Q, const void* Kc,
+                   const void* Vc, long long S_cap, const int* prefix_len, const int* tree_size,
+                   const uint32_t* tree_mask, const int* status, float scale, void* O, void* workspace,
+                   size_t ws_bytes, void* stream, const Paging& pg) {
+  if (B <= 0 || T_max <= 0 || Hq <= 0 || Hkv <= 0 || S_cap <= 0) return TV_EINVAL;
+  if (Hq % Hkv != 0) return TV_EINVAL;
+  if (S_cap > (1LL << 30)) return TV_EUNSUPPORTED;
+  if (!Q || !Kc || !Vc || !prefix_len || !tree_size || !tree_mask || !status || !O) return TV_EINVAL;
+  if (dtype != TV_DTYPE_BF16 && dtype != TV_DTYPE_FP32) return TV_EUNSUPPORTED;
+  if (d != 64 && d != 128) return TV_EUNSUPPORTED;
+  if (T_max > kTMaxLimit) return TV_EUNSUPPORTED;
+  if ((long long)B * T_max * Hq > (1LL << 31) || (long long)B * Hkv > (1LL << 24)) return TV_EINVAL;
+  const uintptr_t mis = reinterpret_cast<uintptr_t>(Q) | reinterpret_cast<uintptr_t>(Kc) |
+                        reinterpret_cast<uintptr_t>(Vc) | reinterpret_cast<uintptr_t>(O);
+  if (mis & 15) return TV_EINVAL;
+  if (!(scale > 0.0f)) scale = 1.0f / sqrtf((float)d);
+  const int W = (T_max + 31) / 32;
+  const bool paged = pg.table != nullptr;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (dtype == TV_DTYPE_FP32) {
+    dim3 grid(T_max, Hq, B);
+    if (B > 65535 || Hq > 65535) return TV_EUNSUPPORTED;
+#define TV_FP32_LAUNCH(DD, PG)                                                                                     \
+  hipLaunchKernelGGL((k_attn_fp32<DD, PG>), grid, dim3(64), 0, s, (const float*)Q, (const float*)Kc,                \
+                     (const float*)Vc, S_cap, prefix_len, tree_size, tree_mask, status, T_max, Hq, Hkv, W, scale,    \
+                     (float*)O, pg)
+    if (d == 64) {
+      if (paged) TV_FP32_LAUNCH(64, true);
+      else TV_FP32_LAUNCH(64, false);
+    } else {
+      if (paged) TV_FP32_LAUNCH(128, true);
+      else TV_FP32_LAUNCH(128, false);
+    }
+#undef TV_FP32_LAUNCH
+    TV_CHECK_LAUNCH();
+    return TV_OK;
+  }
+  const Plan p = make_plan(B, T_max, Hq, Hkv, S_cap);
+  const size_t need = ws_bytes_for(p, B, Hkv, d);
+  if (need && (!workspace || ws_bytes < need)) return TV_EWORKSPACE;
+  _Float16* ws_o = reinterpret_cast<_Float16*>(workspace);
+  float* ws_ml = need ? reinterpret_cast<float*>(ws_o + (size_t)B * Hkv * p.n_split * p.m_pad * d) : nullptr;
+  const float sl2 = scale * kLog2e;
+#define TV_ATTN_LAUNCH(DD, NWW, NSS, PG)                                                                         \
+  launch_bf16<DD, NWW, NSS, PG>(p, B, s, Q, Kc, Vc, S_cap, prefix_len, tree_size, tree_mask, status, T_max, Hq,  \
+                                Hkv, W, sl2, O, ws_o, ws_ml, pg)
+#define TV_ATTN_NW(DD, PG)           \
+  if (p.nw == 4) TV_ATTN_LAUNCH(DD, 4, 2, PG); \
+  else TV_ATTN_LAUNCH(DD, 8, 2, PG)
+  if (d == 128) {
+    if (paged) TV_ATTN_NW(128, true);
+    else TV_ATTN_NW(128, false);
+  } else {
+    if (paged) TV_ATTN_NW(64, true);
+    else TV_ATTN_NW(64, false);
+  }
+#undef TV_ATTN_NW
+#undef TV_ATTN_LAUNCH
+  TV_CHECK_LAUNCH();
+  if (p.n_split > 1) {
+    const int rpb = 256 / (d / 8);
+    dim3 grid(B * Hkv, (unsigned)((p.m_pad + rpb - 1) / rpb));
+    if (d == 128)
+      hipLaunchKernelGGL(k_attn_combine<128>, grid, dim3(256), 0, s, ws_o, ws_ml, prefix_len, tree_size, status, S_cap,
+                         T_max, Hq, Hkv, p.n_split, p.chunk_keys, p.m_pad, p.rel, (uint16_t*)O);
+    else
+      hipLaunchKernelGGL(k_attn_combine<64>, grid, dim3(256), 0, s, ws_o, ws_ml, prefix_len, tree_size, status, S_cap,
+                         T_max, Hq, Hkv, p.n_split, p.chunk_keys, p.m_pad, p.rel, (uint16_t*)O);
+    TV_CHECK_LAUNCH();
+  }
+  return TV_OK;
 }
 
 }  // namespace
@@ -738,62 +862,23 @@ extern "C" int tree_attention(int dtype, int B, int T_max, int Hq, int Hkv, int 
                               const void* Vc, long long S_cap, const int* prefix_len, const int* tree_size,
                               const uint32_t* tree_mask, const int* status, float scale, void* O, void* workspace,
                               size_t ws_bytes, void* stream) {
-  using namespace tv;
-  if (B <= 0 || T_max <= 0 || Hq <= 0 || Hkv <= 0 || S_cap <= 0) return TV_EINVAL;
-  if (Hq % Hkv != 0) return TV_EINVAL;
-  if (S_cap > (1LL << 30)) return TV_EUNSUPPORTED;
-  if (!Q || !Kc || !Vc || !prefix_len || !tree_size || !tree_mask || !status || !O) return TV_EINVAL;
-  if (dtype != TV_DTYPE_BF16 && dtype != TV_DTYPE_FP32) return TV_EUNSUPPORTED;
-  if (d != 64 && d != 128) return TV_EUNSUPPORTED;
-  if (T_max > kTMaxLimit) return TV_EUNSUPPORTED;
-  if ((long long)B * T_max * Hq > (1LL << 31) || (long long)B * Hkv > (1LL << 24)) return TV_EINVAL;
-  const uintptr_t mis = reinterpret_cast<uintptr_t>(Q) | reinterpret_cast<uintptr_t>(Kc) |
-                        reinterpret_cast<uintptr_t>(Vc) | reinterpret_cast<uintptr_t>(O);
-  if (mis & 15) return TV_EINVAL;
-  if (!(scale > 0.0f)) scale = 1.0f / sqrtf((float)d);
-  const int W = (T_max + 31) / 32;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (dtype == TV_DTYPE_FP32) {
-    dim3 grid(T_max, Hq, B);
-    if (B > 65535 || Hq > 65535) return TV_EUNSUPPORTED;
-    if (d == 64)
-      hipLaunchKernelGGL(k_attn_fp32<64>, grid, dim3(64), 0, s, (const float*)Q, (const float*)Kc, (const float*)Vc,
-                         S_cap, prefix_len, tree_size, tree_mask, status, T_max, Hq, Hkv, W, scale, (float*)O);
-    else
-      hipLaunchKernelGGL(k_attn_fp32<128>, grid, dim3(64), 0, s, (const float*)Q, (const float*)Kc,
-                         (const float*)Vc, S_cap, prefix_len, tree_size, tree_mask, status, T_max, Hq, Hkv, W, scale,
-                         (float*)O);
-    TV_CHECK_LAUNCH();
-    return TV_OK;
-  }
-  const Plan p = make_plan(B, T_max, Hq, Hkv, S_cap);
-  const size_t need = ws_bytes_for(p, B, Hkv, d);
-  if (need && (!workspace || ws_bytes < need)) return TV_EWORKSPACE;
-  _Float16* ws_o = reinterpret_cast<_Float16*>(workspace);
-  float* ws_ml = need ? reinterpret_cast<float*>(ws_o + (size_t)B * Hkv * p.n_split * p.m_pad * d) : nullptr;
-  const float sl2 = scale * kLog2e;
-#define TV_ATTN_LAUNCH(DD, NWW, NSS)                                                                             \
-  launch_bf16<DD, NWW, NSS>(p, B, s, Q, Kc, Vc, S_cap, prefix_len, tree_size, tree_mask, status, T_max, Hq, Hkv, W, \
-                            sl2, O, ws_o, ws_ml)
-  if (d == 128) {
-    if (p.nw == 4) TV_ATTN_LAUNCH(128, 4, 2);
-    else TV_ATTN_LAUNCH(128, 8, 2);
-  } else {
-    if (p.nw == 4) TV_ATTN_LAUNCH(64, 4, 2);
-    else TV_ATTN_LAUNCH(64, 8, 2);
-  }
-#undef TV_ATTN_LAUNCH
-  TV_CHECK_LAUNCH();
-  if (p.n_split > 1) {
-    const int rpb = 256 / (d / 8);
-    dim3 grid(B * Hkv, (unsigned)((p.m_pad + rpb - 1) / rpb));
-    if (d == 128)
-      hipLaunchKernelGGL(k_attn_combine<128>, grid, dim3(256), 0, s, ws_o, ws_ml, prefix_len, tree_size, status, S_cap,
-                         T_max, Hq, Hkv, p.n_split, p.chunk_keys, p.m_pad, p.rel, (uint16_t*)O);
-    else
-      hipLaunchKernelGGL(k_attn_combine<64>, grid, dim3(256), 0, s, ws_o, ws_ml, prefix_len, tree_size, status, S_cap,
-                         T_max, Hq, Hkv, p.n_split, p.chunk_keys, p.m_pad, p.rel, (uint16_t*)O);
-    TV_CHECK_LAUNCH();
-  }
-  return TV_OK;
+  return tv::attention_impl(dtype, B, T_max, Hq, Hkv, d, Q, Kc, Vc, S_cap, prefix_len, tree_size, tree_mask, status,
+                            scale, O, workspace, ws_bytes, stream, tv::Paging{});
+}
+
+extern "C" int tree_attention_paged(int dtype, int B, int T_max, int Hq, int Hkv, int d, const void* Q,
+                                    const void* K_pool, const void* V_pool, long long num_blocks,
+                                    int tokens_per_block, const int* block_table, int max_blocks_per_seq,
+                                    const int* prefix_len, const int* tree_size, const uint32_t* tree_mask,
+                                    const int* status, float scale, void* O, void* workspace, size_t ws_bytes,
+                                    void* stream) {
+  const int lbs = tv::log2_block(tokens_per_block);
+  if (lbs < 0 || !block_table || max_blocks_per_seq <= 0 || num_blocks <= 0 || Hkv <= 0) return TV_EINVAL;
+  if ((long long)B * max_blocks_per_seq > (1LL << 31)) return TV_EINVAL;
+  // pool rows (num_blocks * Hkv * tokens_per_block) are addressed with 64-bit offsets
+  if (num_blocks > (1LL << 40) / ((long long)Hkv * tokens_per_block)) return TV_EINVAL;
+  const long long cap = (long long)max_blocks_per_seq << lbs;
+  return tv::attention_impl(dtype, B, T_max, Hq, Hkv, d, Q, K_pool, V_pool, cap, prefix_len, tree_size, tree_mask,
+                            status, scale, O, workspace, ws_bytes, stream,
+                            tv::Paging{block_table, max_blocks_per_seq, lbs, num_blocks});
 }

@@ -12,6 +12,27 @@
 
 namespace tv {
 
+// Paged K/V cache (the TensorRT-LLM EAGLE-3 dissection, "after acceptance: KV
+// from tree layout back to linear": a token's physical slot is its request's
+// block-table entry plus the offset inside the block).  Pools are
+// [n_blocks][Hkv][1 << lbs][d]; logical row s of request b is row
+// s & ((1 << lbs) - 1) of block table[b * max_blocks + (s >> lbs)] (kv head g's
+// rows of a block are contiguous).  A null table means the linear cache
+// [B][Hkv][S_cap][d].
+struct Paging {
+  const int* table;
+  int max_blocks;      // table row stride (blocks per request)
+  int lbs;             // log2 of tokens per block
+  long long n_blocks;  // blocks in each pool
+};
+
+// log2 of a power of two in [1, 1024], else -1 (host)
+inline int log2_block(int tokens_per_block) {
+  for (int l = 0; l <= 10; ++l)
+    if (tokens_per_block == (1 << l)) return l;
+  return -1;
+}
+
 // Largest supported padded node count (one wavefront lane per node).
 constexpr int kTMaxLimit = 64;
 // Largest supported top_k (per-thread register lists).

@@ -11,6 +11,11 @@ The batch description is any object with these attributes (numpy arrays):
   prefix_len [B], Hq, Hkv, d, dtype ('bf16' | 'fp32'), S_cap,
   Q [B][T_max][Hq][d], Kc / Vc [B][Hkv][S_cap][d] (uint16 bf16 bits or float32).
 In 'given' mode the drafter's tree is an input and the build call is skipped.
+
+With ``paged`` (any object with tokens_per_block, max_blocks, n_blocks,
+block_table [B][max_blocks] int32 and K_pool / V_pool [n_blocks][Hkv][tokens_per_block][d])
+the cache is that paged pool, and attention and compaction go through
+tree_attention_paged, kv_compact_paged and tree_accept_compact_paged.
 """
 from __future__ import annotations
 
@@ -36,8 +41,9 @@ def _copies(t, n):
 
 
 class TreeVerifyStep:
-    def __init__(self, w, device: str = "cuda", n_copies: int = 1):
+    def __init__(self, w, device: str = "cuda", n_copies: int = 1, paged=None):
         self.w = w
+        self.paged = paged
         self.device = device
         B, T_max, dcap = w.B, w.T_max, w.dcap
         self.B, self.T_max, self.dcap = B, T_max, dcap
@@ -62,8 +68,15 @@ class TreeVerifyStep:
         # input copies (more than one lets a benchmark rotate its inputs through HBM
         # so that repeated steps do not run out of the last-level cache)
         self.Q_copies = _copies(_t(w.Q, device), n_copies)
-        self.Kc = _copies(_t(w.Kc, device), n_copies)
-        self.Vc = _copies(_t(w.Vc, device), n_copies)
+        if paged is None:
+            self.Kc = _copies(_t(w.Kc, device), n_copies)
+            self.Vc = _copies(_t(w.Vc, device), n_copies)
+            self.S_cap = w.S_cap
+        else:   # the pools take the linear cache's place
+            self.Kc = _copies(_t(paged.K_pool, device), n_copies)
+            self.Vc = _copies(_t(paged.V_pool, device), n_copies)
+            self.block_table = _t(np.asarray(paged.block_table, np.int32), device)
+            self.S_cap = paged.max_blocks * paged.tokens_per_block
         # outputs
         self.tree_mask = torch.full((B, T_max, W), 0x5A5A5A5A, dtype=torch.int32, device=device)
         self.tree_position_ids = torch.full((B, T_max), -7, **i32)
@@ -88,7 +101,7 @@ class TreeVerifyStep:
             self.ws_build = torch.zeros(max(nb, 1), dtype=torch.uint8, device=device)
         else:
             self.ws_build = None
-        na = tv.tree_attention_workspace_bytes(self.dtype_code, B, T_max, w.Hq, w.Hkv, w.d, w.S_cap)
+        na = tv.tree_attention_workspace_bytes(self.dtype_code, B, T_max, w.Hq, w.Hkv, w.d, self.S_cap)
         self.ws_attn = torch.zeros(na, dtype=torch.uint8, device=device) if na else None
         self.copy = 0
 
@@ -120,6 +133,13 @@ class TreeVerifyStep:
     def attention(self, stream=None, copy=None):
         w = self.w
         c = self.copy if copy is None else copy
+        if self.paged is not None:
+            pg = self.paged
+            tv.tree_attention_paged(self.dtype_code, self.B, self.T_max, w.Hq, w.Hkv, w.d, self.Q_copies[c],
+                                    self.Kc[c], self.Vc[c], pg.n_blocks, pg.tokens_per_block, self.block_table,
+                                    pg.max_blocks, self.prefix_len, self.tree_size, self.tree_mask, self.status, 0.0,
+                                    self.O, self.ws_attn, stream)
+            return
         tv.tree_attention(self.dtype_code, self.B, self.T_max, w.Hq, w.Hkv, w.d, self.Q_copies[c], self.Kc[c],
                           self.Vc[c],
                           w.S_cap, self.prefix_len, self.tree_size, self.tree_mask, self.status, 0.0, self.O,
@@ -132,6 +152,12 @@ class TreeVerifyStep:
     def compact(self, stream=None, copy=None):
         w = self.w
         c = self.copy if copy is None else copy
+        if self.paged is not None:
+            pg = self.paged
+            tv.kv_compact_paged(self.B, 1, w.Hkv, w.d, self.elem_bytes, self.Kc[c], self.Vc[c], pg.n_blocks,
+                                pg.tokens_per_block, self.block_table, pg.max_blocks, 0, self.prefix_len,
+                                self.accept_path, self.accept_len, self.dcap, self.new_prefix_len, stream)
+            return
         tv.kv_compact(self.B, 1, w.Hkv, w.d, self.elem_bytes, self.Kc[c], self.Vc[c], w.S_cap, 0, self.prefix_len,
                       self.accept_path, self.accept_len, self.dcap, self.new_prefix_len, stream)
 
@@ -152,6 +178,14 @@ class TreeVerifyStep:
         """tree_accept and kv_compact in one launch."""
         w = self.w
         c = self.copy if copy is None else copy
+        if self.paged is not None:
+            pg = self.paged
+            tv.tree_accept_compact_paged(self.B, self.T_max, self.dcap, self.draft_tokens, self.parents,
+                                         self.tree_size, self.target_predict, self.status, self.accept_len,
+                                         self.accept_path, self.bonus_token, 1, w.Hkv, w.d, self.elem_bytes,
+                                         self.Kc[c], self.Vc[c], pg.n_blocks, pg.tokens_per_block, self.block_table,
+                                         pg.max_blocks, 0, self.prefix_len, self.new_prefix_len, stream)
+            return
         tv.tree_accept_compact(self.B, self.T_max, self.dcap, self.draft_tokens, self.parents, self.tree_size,
                                self.target_predict, self.status, self.accept_len, self.accept_path,
                                self.bonus_token, 1, w.Hkv, w.d, self.elem_bytes, self.Kc[c], self.Vc[c], w.S_cap, 0,
