@@ -105,6 +105,13 @@ def build_dynamic(logprobs: np.ndarray, root_token: int, K: int, D: int, total_t
         order = sorted(range(K * K), key=lambda q: (-layer_scores[q], q))
         frontier = [base + q for q in order[:K]]
         fscore = [layer_scores[q] for q in order[:K]]
+    return _select_and_number(cand_score, cand_token, cand_parent, root_token, total_tokens, T_max)
+
+
+def _select_and_number(cand_score, cand_token, cand_parent, root_token, total_tokens, T_max):
+    """The final step of [E2] section 3: keep the total_tokens best candidates (score
+    descending, id ascending), number them 1..T-1 in ascending id, node 0 = root,
+    rewrite parents as node indices (a kept node whose parent was dropped -> status 4)."""
     C = len(cand_score)
     order = sorted(range(C), key=lambda c: (-cand_score[c], c))
     chosen = sorted(order[:total_tokens])
@@ -118,6 +125,79 @@ def build_dynamic(logprobs: np.ndarray, root_token: int, K: int, D: int, total_t
         parents[n] = 0 if p == -1 else node_of[p]
         scores[n] = cand_score[c]
     return tokens, parents, scores, 1 + len(chosen), ST_OK
+
+
+# ---------------------------------------------------------------------------
+# layer-by-layer dynamic build ([E2] section 3: the draft model runs on the
+# current frontier between rounds, so a round's rows exist only once the round
+# before it has chosen its frontier)
+# ---------------------------------------------------------------------------
+def log_softmax_row(z: np.ndarray) -> np.ndarray:
+    """fp32 logits -> fp32 log-probs: fp32(z - lse), lse = m + log(sum(exp(z - m))) in
+    float64 with m = max(z) (the draft head's log-softmax, [E2] section 3)."""
+    z64 = np.asarray(z, dtype=np.float32).astype(np.float64)
+    m = z64.max()
+    with np.errstate(invalid="ignore", over="ignore"):   # non-finite rows are rejected by the caller
+        lse = m + np.log(np.exp(z64 - m).sum())
+        return (z64 - lse).astype(np.float32)
+
+
+def logits_row_topk(z: np.ndarray, k: int):
+    """The k best tokens of a row of fp32 logits by (logit descending, token ascending),
+    which is the order of the row's log-softmax before its values are rounded, and
+    their log-probs (log_softmax_row)."""
+    toks, _ = row_topk(z, k)
+    lp = log_softmax_row(z)
+    return toks, [np.float32(lp[t]) for t in toks]
+
+
+def logits_row_is_valid(z: np.ndarray) -> bool:
+    return bool(np.isfinite(np.asarray(z, dtype=np.float32)).all())
+
+
+def build_dynamic_layers(layers, root_token: int, K: int, D: int, total_tokens: int, T_max: int,
+                         logits: bool = False):
+    """build_dynamic taking its rows one layer at a time, as a draft loop produces them.
+
+    layers[0] is the root's row ([V] or [1][V]); layers[l] (l = 1..D) is [K][V], row j
+    the draft distribution after frontier slot j of layer l.  With logits=True the rows
+    are raw logits: each row is ranked by logit and scored by its log-softmax
+    (logits_row_topk).  Same rounds and final selection as build_dynamic.
+    Returns tokens, parents, scores, tree_size, status, and frontiers: frontiers[l] =
+    (tokens [K], parent slots [K]) of the frontier chosen at layer l, the parent slot
+    being the slot of layer l-1's frontier it extends (-1 at layer 0)."""
+    topk = logits_row_topk if logits else row_topk
+    valid = logits_row_is_valid if logits else row_is_valid
+    rows0 = np.asarray(layers[0]).reshape(-1, np.asarray(layers[0]).shape[-1])
+    all_rows = [rows0[0]] + [np.asarray(layers[l])[j] for l in range(1, D + 1) for j in range(K)]
+    ok = all(valid(r) for r in all_rows)
+    cand_score, cand_token, cand_parent = [], [], []
+    toks, vals = topk(rows0[0], K)
+    for r in range(K):
+        cand_score.append(vals[r])
+        cand_token.append(toks[r])
+        cand_parent.append(-1)
+    frontier, fscore = list(range(K)), list(vals)
+    frontiers = [(list(toks), [-1] * K)]
+    for l in range(1, D + 1):
+        base = len(cand_score)
+        layer_scores, layer_tokens = [], []
+        for j in range(K):
+            toks, vals = topk(np.asarray(layers[l])[j], K)
+            for r in range(K):
+                s = np.float32(vals[r] + fscore[j])
+                cand_score.append(s)
+                cand_token.append(toks[r])
+                cand_parent.append(frontier[j])
+                layer_scores.append(s)
+                layer_tokens.append(toks[r])
+        order = sorted(range(K * K), key=lambda q: (-layer_scores[q], q))[:K]
+        frontier = [base + q for q in order]
+        fscore = [layer_scores[q] for q in order]
+        frontiers.append(([layer_tokens[q] for q in order], [q // K for q in order]))
+    if not ok:
+        return (*_root_only(root_token, T_max), ST_LOGPROB, frontiers)
+    return (*_select_and_number(cand_score, cand_token, cand_parent, root_token, total_tokens, T_max), frontiers)
 
 
 # ---------------------------------------------------------------------------
