@@ -201,6 +201,9 @@ def main():
                          "tree_accept_compact -- the same five stages in two kernel launches fewer)")
     ap.add_argument("--paged", type=int, default=0, metavar="N",
                     help="keep the K/V cache in a paged pool of N-token blocks (a power of two, 1..1024)")
+    ap.add_argument("--layerwise", choices=["logprobs", "logits"], default=None,
+                    help="build the dynamic tree one draft layer at a time (tree_build_layer x (D+1), then "
+                         "tree_build_finish with the metadata), from log-prob rows or raw logits")
     ap.add_argument("--copy-mb", type=float, default=0.0,
                     help="before warmup, one device-to-device copy of this many MiB (a plain copy kernel of known "
                          "size that calibrates the HBM byte counters of a profiler run)")
@@ -225,6 +228,12 @@ def main():
     workload = w.name if paged is None else f"{w.name}+paged{args.paged}"
     log(f"workload {workload}: {per_copy / 2**20:.1f} MiB of inputs per copy, {n_copies} copies rotated")
     step = TreeVerifyStep(w, n_copies=n_copies, paged=paged)
+    if args.layerwise:
+        if w.mode != "dynamic":
+            print("--layerwise needs a dynamic-tree workload (--config 2, 3 or 4)", file=sys.stderr)
+            sys.exit(2)
+        rows = gen.draft_logits(w.cfg_id, w.B, w.rows_per_req, w.V) if args.layerwise == "logits" else None
+        step.prepare_layers(rows=rows, logits=args.layerwise == "logits", n_copies=n_copies)
     stream = torch.cuda.current_stream()
 
     if args.copy_mb > 0:
@@ -250,7 +259,9 @@ def main():
 
     def one(k, ev=None):
         step.copy = k % n_copies
-        if args.unfused:
+        if args.layerwise:
+            step.build_layers(meta=True)
+        elif args.unfused:
             step.build()
             step.meta()
         else:
@@ -367,8 +378,12 @@ def main():
                    "input_copies_rotated": n_copies, "launch": launch,
                    "kv_cache": "linear" if paged is None else
                    f"paged, {args.paged} tokens per block, {paged.n_blocks} blocks in random order",
-                   "calls": ("tree_build, tree_mask_positions, tree_attention, tree_accept, kv_compact"
-                             if args.unfused else "tree_build_meta, tree_attention, tree_accept_compact")},
+                   "calls": ", ".join([
+                       f"tree_build_layer x {w.D + 1} ({args.layerwise} rows), tree_build_finish" if args.layerwise
+                       else ("tree_build, tree_mask_positions" if args.unfused else "tree_build_meta"),
+                       "tree_attention" + ("_paged" if paged is not None else ""),
+                       ("tree_accept, kv_compact" if args.unfused else "tree_accept_compact") +
+                       ("_paged" if paged is not None else "")])},
         "stages_us": stages,
         "roofline": roof,
     }

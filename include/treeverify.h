@@ -12,7 +12,10 @@
  *   kv_compact          accepted path    -> K/V rows moved to contiguous slots
  *   tree_accept_compact the last two in one launch
  * and the same attention and compaction over a paged K/V cache (a block table
- * per request): tree_attention_paged, kv_compact_paged, tree_accept_compact_paged.
+ * per request): tree_attention_paged, kv_compact_paged, tree_accept_compact_paged;
+ * and the dynamic build one draft layer at a time, for a draft loop that runs
+ * the draft model on each layer's frontier: tree_build_layer (D + 1 times),
+ * then tree_build_finish.
  *
  * Sources for what each call computes (cited by page title and section):
  *   [E2]  EAGLE v2 dynamic-tree decoding walkthrough -- section 2 initialize_tree
@@ -116,6 +119,45 @@ int tree_build(int mode, int B, int V, int K, int D, int total_tokens,
                int T_max, int* draft_tokens, int* parents, int* tree_size,
                float* node_score /* nullable */, int* status,
                void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------- *
+ * tree_build_layer / tree_build_finish -- the dynamic build of tree_build, one
+ * draft layer at a time ([E2] section 3, topK_generate: the draft model runs on
+ * the frontier each round chooses, so a round's rows exist only after it).
+ *
+ * Call tree_build_layer for layer = 0, 1, ..., D in order on one state, then
+ * tree_build_finish.  Layer 0 takes rows [B][1][V], the draft distribution
+ * after the root; layer l >= 1 takes rows [B][K][V], row j the distribution
+ * after frontier slot j of layer l - 1 (what the draft model gives for the
+ * token frontier_tokens[b][j] returned by the previous call).  Each call writes
+ * the new frontier: frontier_tokens [B][K] in rank order, and (nullable)
+ * frontier_parents [B][K], the slot of the previous frontier each extends (-1
+ * at layer 0).  tree_build_finish then writes what tree_build writes (and, when
+ * prefix_len is not NULL, what tree_mask_positions writes, as tree_build_meta
+ * does; with prefix_len NULL the metadata pointers are ignored).
+ * Results equal tree_build on the same rows stacked as [B][1 + D K][V].
+ * rows_are_logits = 1: the rows are raw draft logits instead of log-probs.  A
+ *   row's K best tokens are then taken by logit (token ascending on ties), the
+ *   order of the row's log-softmax before rounding, and scored by its log-prob
+ *   float32(x - lse), lse = m + log(sum exp(x - m)) computed in float64; NaN or
+ *   +-inf in a row is a bad value (TV_ST_LOGPROB at finish).
+ * The frontier outputs of a layer with a bad value are unspecified.
+ * state: tree_build_layer_workspace_bytes(B, V, K, D) bytes (any contents
+ *   before layer 0); it carries the build from call to call, so the calls of one
+ *   build must not overlap another build on the same state.
+ * Requires the dynamic-mode conditions of tree_build; total_tokens and T_max
+ *   are checked by tree_build_finish.
+ * ------------------------------------------------------------------------- */
+size_t tree_build_layer_workspace_bytes(int B, int V, int K, int D);
+int tree_build_layer(int layer, int B, int V, int K, int D, const float* rows, int rows_are_logits,
+                     void* state, size_t state_bytes, int* frontier_tokens,
+                     int* frontier_parents /* nullable */, void* stream);
+int tree_build_finish(int B, int V, int K, int D, int total_tokens, const int* root_token, int T_max,
+                      const void* state, size_t state_bytes, int* draft_tokens, int* parents,
+                      int* tree_size, float* node_score /* nullable */, int* status, int dcap,
+                      const int* prefix_len /* nullable: no metadata */, uint32_t* tree_mask,
+                      int* tree_position_ids, int* positions, int* retrieve_indices, int* leaf_count,
+                      int* first_child /* nullable */, int* next_sibling /* nullable */, void* stream);
 
 /* ------------------------------------------------------------------------- *
  * tree_mask_positions -- [TRT] tree-build kernel (parents -> packed ancestor

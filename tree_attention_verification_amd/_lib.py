@@ -53,6 +53,9 @@ _SIGS = {
     "tree_attention_paged": (I, [I, I, I, I, I, I, P, P, P, LL, I, P, I, P, P, P, P, F, P, P, SZ, P]),
     "kv_compact_paged": (I, [I, I, I, I, I, P, P, LL, I, P, I, LL, P, P, P, I, P, P]),
     "tree_accept_compact_paged": (I, [I, I, I, P, P, P, P, P, P, P, P, I, I, I, I, P, P, LL, I, P, I, LL, P, P, P]),
+    "tree_build_layer_workspace_bytes": (SZ, [I, I, I, I]),
+    "tree_build_layer": (I, [I, I, I, I, I, P, I, P, SZ, P, P, P]),
+    "tree_build_finish": (I, [I, I, I, I, I, P, I, P, SZ, P, P, P, P, P, I, P, P, P, P, P, P, P, P, P]),
     "tv_error_string": (ctypes.c_char_p, [I]),
     "tv_status_string": (ctypes.c_char_p, [I]),
 }
@@ -253,3 +256,32 @@ def tree_accept_compact_paged(B, T_max, dcap, draft_tokens, parents, tree_size, 
                                          layer_stride_elems, _dev(prefix_len, "prefix_len"),
                                          _dev(new_prefix_len, "new_prefix_len"), _stream(stream))
     _check("tree_accept_compact_paged", rc)
+
+
+def tree_build_layer_workspace_bytes(B, V, K, D) -> int:
+    return int(lib().tree_build_layer_workspace_bytes(B, V, K, D))
+
+
+def tree_build_layer(layer, B, V, K, D, rows, rows_are_logits, state, frontier_tokens, frontier_parents=None,
+                     stream=None):
+    sp, sn = _ws(state)
+    rc = lib().tree_build_layer(layer, B, V, K, D, _dev(rows, "rows"), int(bool(rows_are_logits)), sp, sn,
+                                _dev(frontier_tokens, "frontier_tokens"), _dev(frontier_parents, "frontier_parents"),
+                                _stream(stream))
+    _check("tree_build_layer", rc)
+
+
+def tree_build_finish(B, V, K, D, total_tokens, root_token, T_max, state, draft_tokens, parents, tree_size,
+                      node_score, status, dcap=0, prefix_len=None, tree_mask=None, tree_position_ids=None,
+                      positions=None, retrieve_indices=None, leaf_count=None, first_child=None, next_sibling=None,
+                      stream=None):
+    sp, sn = _ws(state)
+    rc = lib().tree_build_finish(B, V, K, D, total_tokens, _dev(root_token, "root_token"), T_max, sp, sn,
+                                 _dev(draft_tokens, "draft_tokens"), _dev(parents, "parents"),
+                                 _dev(tree_size, "tree_size"), _dev(node_score, "node_score"), _dev(status, "status"),
+                                 dcap, _dev(prefix_len, "prefix_len"), _dev(tree_mask, "tree_mask"),
+                                 _dev(tree_position_ids, "tree_position_ids"), _dev(positions, "positions"),
+                                 _dev(retrieve_indices, "retrieve_indices"), _dev(leaf_count, "leaf_count"),
+                                 _dev(first_child, "first_child"), _dev(next_sibling, "next_sibling"),
+                                 _stream(stream))
+    _check("tree_build_finish", rc)

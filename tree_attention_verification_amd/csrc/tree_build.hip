@@ -63,6 +63,9 @@ struct BuildWs {
   unsigned long long* row_keys;  // [rows][S][K]
   int* row_bad;                  // [rows][S]
   int S;
+  // raw-logit rows only: every (row, chunk)'s maximum and sum of exp(x - max)
+  float* row_max;                // [rows][S]
+  double* row_sum;               // [rows][S]
 };
 
 inline size_t build_ws_bytes(long long rows, int K, int S) {
@@ -75,6 +78,8 @@ inline BuildWs build_ws(void* base, long long rows, int K, int S) {
   w.row_keys = reinterpret_cast<unsigned long long*>(p);
   w.row_bad = reinterpret_cast<int*>(p + (size_t)rows * S * K * 8);
   w.S = S;
+  w.row_max = nullptr;
+  w.row_sum = nullptr;
   return w;
 }
 
@@ -137,7 +142,8 @@ __device__ void load_row_keys(const BuildWs& ws, long long row_base, int R, int 
   __syncthreads();
   if (S <= 2) merge_chunk_lists<2>(s_stage, R, K, S, s_key);
   else if (S <= 4) merge_chunk_lists<4>(s_stage, R, K, S, s_key);
-  else merge_chunk_lists<8>(s_stage, R, K, S, s_key);
+  else if (S <= 8) merge_chunk_lists<8>(s_stage, R, K, S, s_key);
+  else merge_chunk_lists<16>(s_stage, R, K, S, s_key);
 }
 
 typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
@@ -179,7 +185,13 @@ __device__ __forceinline__ unsigned long long make_key64(uint32_t k32, uint32_t 
 //   4. an exact rank count among the buffer gives the new sorted top-K.
 // A buffer overflow (heavy ties, e.g. a constant row) switches that tile to a
 // bisection on the unique 64-bit keys, which is exact for any input.
+// LOGITS: the row holds raw logits (any finite value; NaN and +-inf are bad
+// values), ranked by logit, and the pass also leaves the chunk's maximum m and
+// sum of exp(x - m) in float64 (each thread keeps its own running pair, rescaled
+// when its maximum rises; the workgroup merges them), from which the layer
+// kernel forms the row's log-sum-exp.
 // --------------------------------------------------------------------------
+template <bool LOGITS>
 __global__ __launch_bounds__(kTopkThreads) void k_row_topk(const float* __restrict__ lp, int V, int K, int vec4,
                                                            BuildWs ws) {
   const int S = ws.S;
@@ -199,6 +211,22 @@ __global__ __launch_bounds__(kTopkThreads) void k_row_topk(const float* __restri
   bool bad = false;
   int have = 0;                       // entries in s_best: 0 before the first tile, then K
   unsigned long long tau_run = 0ull;  // K-th best key of the earlier tiles (0: none)
+  float lse_m = -INFINITY;            // LOGITS: this thread's running maximum and sum of exp(x - max)
+  double lse_s = 0.0;
+  // LOGITS: fold this thread's finite entries of a tile into (lse_m, lse_s)
+  auto lse_add = [&](const float* xs, auto in_of) __attribute__((always_inline)) {
+    float tm = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kTopkVec * 4; ++j)
+      if (in_of(j) && isfinite(xs[j])) tm = fmaxf(tm, xs[j]);
+    if (tm > lse_m) {
+      lse_s = lse_m == -INFINITY ? 0.0 : lse_s * exp((double)lse_m - (double)tm);
+      lse_m = tm;
+    }
+#pragma unroll
+    for (int j = 0; j < kTopkVec * 4; ++j)
+      if (in_of(j) && isfinite(xs[j])) lse_s += exp((double)xs[j] - (double)lse_m);
+  };
 
   for (int t0 = begin; t0 < end; t0 += kTopkTile) {
     // entry j (0..31) of this thread: vocabulary index idx_of(j)
@@ -218,8 +246,14 @@ __global__ __launch_bounds__(kTopkThreads) void k_row_topk(const float* __restri
       for (int j = 0; j < kTopkVec * 4; ++j) {
         const bool in = idx_of(j) < end;
         const float v = x[j >> 2][j & 3];
-        bad |= in && !(v <= 0.0f);  // NaN or positive
+        bad |= in && (LOGITS ? !isfinite(v) : !(v <= 0.0f));  // log-probs: NaN or positive
         k[j] = in ? order_key(v) : 0u;
+      }
+      if constexpr (LOGITS) {
+        float xs[kTopkVec * 4];
+#pragma unroll
+        for (int j = 0; j < kTopkVec * 4; ++j) xs[j] = x[j >> 2][j & 3];
+        lse_add(xs, [&](int j) { return idx_of(j) < end; });
       }
     } else {
       float x[kTopkVec * 4];
@@ -228,9 +262,10 @@ __global__ __launch_bounds__(kTopkThreads) void k_row_topk(const float* __restri
 #pragma unroll
       for (int j = 0; j < kTopkVec * 4; ++j) {
         const bool in = idx_of(j) < end;
-        bad |= in && !(x[j] <= 0.0f);
+        bad |= in && (LOGITS ? !isfinite(x[j]) : !(x[j] <= 0.0f));
         k[j] = in ? order_key(x[j]) : 0u;
       }
+      if constexpr (LOGITS) lse_add(x, [&](int j) { return idx_of(j) < end; });
     }
     uint32_t tmax = 0u;
 #pragma unroll
@@ -320,6 +355,30 @@ __global__ __launch_bounds__(kTopkThreads) void k_row_topk(const float* __restri
     tau_run = s_best[K - 1];
   }
   if (bad) s_bad = 1;
+  if constexpr (LOGITS) {
+    // merge the threads' (max, sum) pairs: the chunk's maximum first (shuffles,
+    // then the wavefronts' maxima through LDS), then each thread rescales its own
+    // sum to it (one exponential each, all in parallel) and the sums are added
+    __shared__ float s_lm[kTopkThreads / 64];
+    __shared__ double s_ls[kTopkThreads / 64];
+    float M = lse_m;
+    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+    if (lane == 0) s_lm[tid >> 6] = M;
+    __syncthreads();
+    M = s_lm[0];
+#pragma unroll
+    for (int w = 1; w < kTopkThreads / 64; ++w) M = fmaxf(M, s_lm[w]);
+    double part = lse_m == -INFINITY ? 0.0 : lse_s * exp((double)lse_m - (double)M);
+    for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
+    if (lane == 0) s_ls[tid >> 6] = part;
+    __syncthreads();
+    if (tid == 0) {
+      double sum = 0.0;
+      for (int w = 0; w < kTopkThreads / 64; ++w) sum += s_ls[w];
+      ws.row_max[row * S + chunk] = M;
+      ws.row_sum[row * S + chunk] = sum;
+    }
+  }
   __syncthreads();
   if (tid < K) ws.row_keys[(row * S + chunk) * K + tid] = s_best[tid];
   if (tid == 0) ws.row_bad[row * S + chunk] = s_bad;
@@ -743,6 +802,167 @@ __global__ __launch_bounds__(kSelectThreads) void k_tree_select_static(
   }
 }
 
+// --------------------------------------------------------------------------
+// Layer-by-layer build ([E2] section 3: the draft model runs on each round's
+// frontier, so a round's rows exist only after the round before it).  The state
+// keeps every layer's merged row lists in the layout the select kernel reads
+// (one chunk per row), so tree_build_finish is k_tree_select_dynamic on it: it
+// replays the rounds (the same float32 adds and ranking, hence the same
+// frontiers) and makes the final selection.
+// --------------------------------------------------------------------------
+struct LayerState {
+  unsigned long long* keys;  // [B][R][K] sorted rank keys of every row (R = 1 + D K)
+  int* bad;                  // [B][R]
+  float* fsc;                // [B][K] scores of the current frontier
+};
+
+// Merge one layer's rows (1 at layer 0, else K: row j = frontier slot j) into
+// the state, and choose the next frontier: at layer 0 the root row's K best, at
+// layer l the K best of the K*K cumulative scores fl32(log-prob + score of slot
+// j), ranked (score desc, jK + r asc) -- the rounds of k_tree_select_dynamic.
+template <int K, bool LOGITS>
+__global__ __launch_bounds__(kSelectThreads) void k_build_layer(BuildWs rws, int layer, int R, LayerState st,
+                                                                int* __restrict__ frontier_tokens,
+                                                                int* __restrict__ frontier_parents) {
+  extern __shared__ unsigned char smem[];  // chunk lists of this layer's rows (when a row has several)
+  constexpr int KK = K * K;
+  __shared__ unsigned long long s_key[KK];
+  __shared__ __attribute__((aligned(16))) unsigned long long s_ck[KK + 2];
+  __shared__ float s_fsc[K];
+  __shared__ double s_lse[K];
+  __shared__ int s_bad;
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int Rl = layer == 0 ? 1 : K;
+  if (tid == 0) s_bad = 0;
+  if (layer > 0 && tid < K) s_fsc[tid] = st.fsc[(long long)b * K + tid];
+  __syncthreads();
+  load_row_keys(rws, (long long)b * Rl, Rl, K, s_key, reinterpret_cast<unsigned long long*>(smem), &s_bad);
+  __syncthreads();
+  if constexpr (LOGITS) {
+    // log-sum-exp of each row from its chunks' (max, sum), then every kept logit
+    // becomes its log-prob fl32(x - lse); the order inside a row is the logits'
+    // one thread per (row, chunk): the row's maximum from all its chunks, this
+    // chunk's sum rescaled to it (the exponentials in parallel), then per row the
+    // sum of its chunks' terms and the logarithm
+    __shared__ double s_part[kKMax * 16];
+    const int S = rws.S;
+    if (tid < Rl * S) {
+      const int rw = tid / S, c = tid % S;
+      const long long rb = ((long long)b * Rl + rw) * S;
+      float M = -INFINITY;
+      for (int q = 0; q < S; ++q) M = fmaxf(M, rws.row_max[rb + q]);
+      const float m = rws.row_max[rb + c];
+      s_part[tid] = m == -INFINITY ? 0.0 : rws.row_sum[rb + c] * exp((double)m - (double)M);
+      if (c == 0) s_lse[rw] = (double)M;
+    }
+    __syncthreads();
+    if (tid < Rl) {
+      double sum = 0.0;
+      for (int q = 0; q < S; ++q) sum += s_part[tid * S + q];
+      s_lse[tid] += log(sum);
+    }
+    __syncthreads();
+    for (int i = tid; i < Rl * K; i += kSelectThreads) {
+      const unsigned long long k0 = s_key[i];
+      const float lpv = (float)((double)key_value(k0) - s_lse[i / K]);
+      s_key[i] = rank_key(lpv, key_index(k0));
+    }
+    __syncthreads();
+  }
+  // the rows into the state (row 0 at layer 0, rows 1 + (layer-1) K + j after)
+  const long long rrow = (long long)b * R + (layer == 0 ? 0 : 1 + (long long)(layer - 1) * K);
+  for (int i = tid; i < Rl * K; i += kSelectThreads) st.keys[rrow * K + i] = s_key[i];
+  if (tid < Rl) st.bad[rrow + tid] = s_bad;
+  if (tid >= 64) return;
+  // the next frontier, on the first wavefront
+  const long long fo = (long long)b * K;
+  if (layer == 0) {
+    if (tid < K) {
+      st.fsc[fo + tid] = key_value(s_key[tid]);
+      frontier_tokens[fo + tid] = (int)key_index(s_key[tid]);
+      if (frontier_parents) frontier_parents[fo + tid] = -1;
+    }
+    return;
+  }
+  constexpr int kPerLane = (KK + 63) / 64;
+  unsigned long long key[kPerLane];
+  float sc[kPerLane];
+#pragma unroll
+  for (int i = 0; i < kPerLane; ++i) {
+    const int o = tid + 64 * i;
+    key[i] = 0ull;
+    sc[i] = 0.0f;
+    if (o < KK) {
+      sc[i] = __fadd_rn(key_value(s_key[o]), s_fsc[o / K]);
+      key[i] = rank_key(sc[i], (uint32_t)o);
+      s_ck[o] = key[i];
+    }
+  }
+  if (tid < 2) s_ck[KK + tid] = 0ull;  // pads the last pair read
+  wave_sync();
+#pragma unroll
+  for (int i = 0; i < kPerLane; ++i) {
+    const int o = tid + 64 * i;
+    if (o < KK) {
+      int rk = 0;
+      for (int q = 0; q < KK; q += 2) {
+        const u64x2 x = *reinterpret_cast<const u64x2*>(s_ck + q);
+        rk += (x[0] > key[i]) + (x[1] > key[i]);
+      }
+      if (rk < K) {
+        st.fsc[fo + rk] = sc[i];
+        frontier_tokens[fo + rk] = (int)key_index(s_key[o]);
+        if (frontier_parents) frontier_parents[fo + rk] = o / K;
+      }
+    }
+  }
+}
+
+// Vocabulary chunks per row in a layer call: one layer has at most K rows per
+// request, so rows are cut finer than in the batch build (chunks of ~4096
+// entries, up to 16) to put more workgroups on the chip; with raw logits each
+// chunk also evaluates its float64 exponentials, ~16 per thread at 4096.
+inline int pick_split_layer(int V, int K) {
+  int S = (V + 4095) / 4096;
+  if (S > 16) S = 16;
+  const long long rk = (long long)K * K;
+  const long long cap = (kStageKeys - 2 * rk) / rk;
+  if (S > cap) S = (int)cap;
+  return S < 1 ? 1 : S;
+}
+
+size_t layer_state_bytes(int B, int V, int K, int D, int* S_out) {
+  const long long R = 1 + (long long)D * K;
+  const int S = pick_split_layer(V, K);
+  if (S_out) *S_out = S;
+  const long long rows = (long long)B * K;  // row-top-K scratch: one layer's rows
+  size_t n = (size_t)B * R * K * 8 + (size_t)B * R * 4 + (size_t)B * K * 4;
+  n = (n + 255) & ~(size_t)255;
+  n += build_ws_bytes(rows, K, S);
+  n = (n + 255) & ~(size_t)255;
+  n += (size_t)rows * S * (4 + 8) + 256;
+  return n;
+}
+
+// carve the state: [keys | bad | fsc] then the row-top-K scratch and its log-sum-exp parts
+void layer_state(void* base, int B, int V, int K, int D, LayerState* st, BuildWs* rws) {
+  const long long R = 1 + (long long)D * K;
+  int S = 1;
+  layer_state_bytes(B, V, K, D, &S);
+  unsigned char* p = reinterpret_cast<unsigned char*>(base);
+  st->keys = reinterpret_cast<unsigned long long*>(p);
+  st->bad = reinterpret_cast<int*>(p + (size_t)B * R * K * 8);
+  st->fsc = reinterpret_cast<float*>(p + (size_t)B * R * K * 8 + (size_t)B * R * 4);
+  size_t off = (size_t)B * R * K * 8 + (size_t)B * R * 4 + (size_t)B * K * 4;
+  off = (off + 255) & ~(size_t)255;
+  const long long rows = (long long)B * K;
+  *rws = build_ws(p + off, rows, K, S);
+  off += build_ws_bytes(rows, K, S);
+  off = (off + 255) & ~(size_t)255;
+  rws->row_sum = reinterpret_cast<double*>(p + off);
+  rws->row_max = reinterpret_cast<float*>(p + off + (size_t)rows * S * 8);
+}
+
 }  // namespace
 }  // namespace tv
 
@@ -804,8 +1024,8 @@ int build_impl(int mode, int B, int V, int K, int D, int total_tokens, const int
   const size_t stage = S > 1 ? (size_t)rows_per_req * S * K * 8 : 0;  // chunk lists merged in the select kernel
 
   const int vec4 = (V % 4 == 0) && ((reinterpret_cast<uintptr_t>(logprobs) & 15) == 0);
-  hipLaunchKernelGGL(k_row_topk, dim3((unsigned)(rows_total * S)), dim3(kTopkThreads), 0, s, logprobs, V, K, vec4,
-                     ws);
+  hipLaunchKernelGGL(k_row_topk<false>, dim3((unsigned)(rows_total * S)), dim3(kTopkThreads), 0, s, logprobs, V, K,
+                     vec4, ws);
   TV_CHECK_LAUNCH();
 
   if (mode == TV_MODE_DYNAMIC) {
@@ -867,4 +1087,121 @@ extern "C" int tree_build_meta(int mode, int B, int V, int K, int D, int total_t
                        retrieve_indices, leaf_count, first_child, next_sibling};
   return build_impl(mode, B, V, K, D, total_tokens, branching, n_levels, logprobs, rows_per_req, root_token, T_max,
                     draft_tokens, parents, tree_size, node_score, status, workspace, ws_bytes, &mo, stream);
+}
+
+extern "C" size_t tree_build_layer_workspace_bytes(int B, int V, int K, int D) {
+  if (B <= 0 || V <= 0 || K <= 0 || K > tv::kKMax || D < 0 || D > 64) return 0;
+  return tv::layer_state_bytes(B, V, K, D, nullptr);
+}
+
+namespace {
+// the dynamic-mode checks shared by the layer calls
+int layer_checks(int B, int V, int K, int D) {
+  using namespace tv;
+  if (B <= 0 || V <= 0 || K < 1 || D < 0 || D > 64) return TV_EINVAL;
+  if (K > kKMax) return TV_EUNSUPPORTED;
+  if (K > V) return TV_EINVAL;
+  const long long C = (long long)K + (long long)D * K * K;
+  if (C > kMaxCand) return TV_EUNSUPPORTED;
+  if ((long long)B * K * tv::pick_split_layer(V, K) > 0x7FFFFFFFll) return TV_EUNSUPPORTED;
+  return TV_OK;
+}
+}  // namespace
+
+extern "C" int tree_build_layer(int layer, int B, int V, int K, int D, const float* rows, int rows_are_logits,
+                                void* state, size_t state_bytes, int* frontier_tokens, int* frontier_parents,
+                                void* stream) {
+  using namespace tv;
+  const int rc = layer_checks(B, V, K, D);
+  if (rc != TV_OK) return rc;
+  if (layer < 0 || layer > D) return TV_EINVAL;
+  if (!rows || !state || !frontier_tokens) return TV_EINVAL;
+  if (state_bytes < layer_state_bytes(B, V, K, D, nullptr)) return TV_EWORKSPACE;
+  LayerState st{};
+  BuildWs rws{};
+  layer_state(state, B, V, K, D, &st, &rws);
+  const int Rl = layer == 0 ? 1 : K;
+  const long long rows_total = (long long)B * Rl;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int vec4 = (V % 4 == 0) && ((reinterpret_cast<uintptr_t>(rows) & 15) == 0);
+  if (rows_are_logits)
+    hipLaunchKernelGGL(k_row_topk<true>, dim3((unsigned)(rows_total * rws.S)), dim3(kTopkThreads), 0, s, rows, V, K,
+                       vec4, rws);
+  else
+    hipLaunchKernelGGL(k_row_topk<false>, dim3((unsigned)(rows_total * rws.S)), dim3(kTopkThreads), 0, s, rows, V,
+                       K, vec4, rws);
+  TV_CHECK_LAUNCH();
+  const size_t stage = rws.S > 1 ? (size_t)Rl * rws.S * K * 8 : 0;
+  const int R = 1 + D * K;
+  switch (K) {
+#define TV_LAYER_CASE(k)                                                                                         \
+  case k:                                                                                                        \
+    if (rows_are_logits)                                                                                         \
+      hipLaunchKernelGGL((k_build_layer<k, true>), dim3(B), dim3(kSelectThreads), stage, s, rws, layer, R, st,   \
+                         frontier_tokens, frontier_parents);                                                     \
+    else                                                                                                         \
+      hipLaunchKernelGGL((k_build_layer<k, false>), dim3(B), dim3(kSelectThreads), stage, s, rws, layer, R, st,  \
+                         frontier_tokens, frontier_parents);                                                     \
+    break;
+    TV_LAYER_CASE(1) TV_LAYER_CASE(2) TV_LAYER_CASE(3) TV_LAYER_CASE(4) TV_LAYER_CASE(5) TV_LAYER_CASE(6)
+    TV_LAYER_CASE(7) TV_LAYER_CASE(8) TV_LAYER_CASE(9) TV_LAYER_CASE(10) TV_LAYER_CASE(11) TV_LAYER_CASE(12)
+    TV_LAYER_CASE(13) TV_LAYER_CASE(14) TV_LAYER_CASE(15) TV_LAYER_CASE(16)
+#undef TV_LAYER_CASE
+    default: return TV_EUNSUPPORTED;
+  }
+  TV_CHECK_LAUNCH();
+  return TV_OK;
+}
+
+extern "C" int tree_build_finish(int B, int V, int K, int D, int total_tokens, const int* root_token, int T_max,
+                                 const void* state, size_t state_bytes, int* draft_tokens, int* parents,
+                                 int* tree_size, float* node_score, int* status, int dcap, const int* prefix_len,
+                                 uint32_t* tree_mask, int* tree_position_ids, int* positions, int* retrieve_indices,
+                                 int* leaf_count, int* first_child, int* next_sibling, void* stream) {
+  using namespace tv;
+  const int rc = layer_checks(B, V, K, D);
+  if (rc != TV_OK) return rc;
+  if (T_max <= 0) return TV_EINVAL;
+  if (T_max > kTMaxLimit) return TV_EUNSUPPORTED;
+  const long long C = (long long)K + (long long)D * K * K;
+  if (total_tokens < 0 || total_tokens > C || total_tokens + 1 > T_max) return TV_EINVAL;
+  if (!root_token || !state || !draft_tokens || !parents || !tree_size || !status) return TV_EINVAL;
+  if (state_bytes < layer_state_bytes(B, V, K, D, nullptr)) return TV_EWORKSPACE;
+  MetaOut mo{};
+  const bool meta = prefix_len != nullptr;
+  if (meta) {  // the checks of tree_mask_positions
+    if (dcap < 0 || dcap >= T_max) return TV_EINVAL;
+    if (!tree_mask || !tree_position_ids || !positions || !retrieve_indices || !leaf_count) return TV_EINVAL;
+    if (B > 2147483647 / 64) return TV_EINVAL;
+    mo = MetaOut{dcap, (T_max + 31) / 32, prefix_len, tree_mask, tree_position_ids, positions, retrieve_indices,
+                 leaf_count, first_child, next_sibling};
+  }
+  LayerState st{};
+  BuildWs rws{};
+  layer_state(const_cast<void*>(state), B, V, K, D, &st, &rws);
+  BuildWs ws{};
+  ws.row_keys = st.keys;
+  ws.row_bad = st.bad;
+  ws.S = 1;
+  const int R = 1 + D * K;
+  const size_t smem = (size_t)R * K * 16;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  switch (K) {
+#define TV_FINISH_CASE(k)                                                                                         \
+  case k:                                                                                                         \
+    if (meta)                                                                                                     \
+      hipLaunchKernelGGL((k_tree_select_dynamic<k, true>), dim3(B), dim3(kSelectThreads), smem, s, ws, R, D,      \
+                         total_tokens, root_token, T_max, draft_tokens, parents, tree_size, node_score, status, mo); \
+    else                                                                                                          \
+      hipLaunchKernelGGL((k_tree_select_dynamic<k, false>), dim3(B), dim3(kSelectThreads), smem, s, ws, R, D,     \
+                         total_tokens, root_token, T_max, draft_tokens, parents, tree_size, node_score, status, mo); \
+    break;
+    TV_FINISH_CASE(1) TV_FINISH_CASE(2) TV_FINISH_CASE(3) TV_FINISH_CASE(4) TV_FINISH_CASE(5) TV_FINISH_CASE(6)
+    TV_FINISH_CASE(7) TV_FINISH_CASE(8) TV_FINISH_CASE(9) TV_FINISH_CASE(10) TV_FINISH_CASE(11) TV_FINISH_CASE(12)
+    TV_FINISH_CASE(13) TV_FINISH_CASE(14) TV_FINISH_CASE(15) TV_FINISH_CASE(16)
+#undef TV_FINISH_CASE
+    default: return TV_EUNSUPPORTED;
+  }
+  TV_CHECK_LAUNCH();
+  return TV_OK;
 }

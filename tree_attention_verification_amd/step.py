@@ -67,8 +67,12 @@ class TreeVerifyStep:
         self.status = torch.full((B,), 99, **i32)
         # input copies (more than one lets a benchmark rotate its inputs through HBM
         # so that repeated steps do not run out of the last-level cache)
-        self.Q_copies = _copies(_t(w.Q, device), n_copies)
-        if paged is None:
+        has_attn = w.Q is not None   # a tree-only batch has no attention tensors
+        self.Q_copies = _copies(_t(w.Q, device), n_copies) if has_attn else [None]
+        if not has_attn:
+            self.Kc = self.Vc = [None]
+            self.S_cap = w.S_cap
+        elif paged is None:
             self.Kc = _copies(_t(w.Kc, device), n_copies)
             self.Vc = _copies(_t(w.Vc, device), n_copies)
             self.S_cap = w.S_cap
@@ -85,7 +89,7 @@ class TreeVerifyStep:
         self.leaf_count = torch.full((B,), -7, **i32)
         self.first_child = torch.full((B, T_max), -7, **i32)
         self.next_sibling = torch.full((B, T_max), -7, **i32)
-        self.O = torch.zeros_like(self.Q_copies[0])
+        self.O = torch.zeros_like(self.Q_copies[0]) if has_attn else None
         self.target_predict = torch.full((B, T_max), -1, **i32)
         self.accept_len = torch.full((B,), -7, **i32)
         self.accept_path = torch.full((B, dcap + 1), -7, **i32)
@@ -101,7 +105,8 @@ class TreeVerifyStep:
             self.ws_build = torch.zeros(max(nb, 1), dtype=torch.uint8, device=device)
         else:
             self.ws_build = None
-        na = tv.tree_attention_workspace_bytes(self.dtype_code, B, T_max, w.Hq, w.Hkv, w.d, self.S_cap)
+        na = tv.tree_attention_workspace_bytes(self.dtype_code, B, T_max, w.Hq, w.Hkv, w.d, self.S_cap) \
+            if has_attn else 0
         self.ws_attn = torch.zeros(na, dtype=torch.uint8, device=device) if na else None
         self.copy = 0
 
@@ -173,6 +178,52 @@ class TreeVerifyStep:
                            self.ws_build, self.dcap, self.prefix_len, self.tree_mask, self.tree_position_ids,
                            self.positions, self.retrieve_indices, self.leaf_count, self.first_child,
                            self.next_sibling, stream)
+
+    # ---- the dynamic build one draft layer at a time --------------------------
+    def prepare_layers(self, rows=None, logits: bool = False, n_copies: int = 1):
+        """Stage one device buffer per draft layer (layer 0: [B][1][V], layer l: [B][K][V])
+        from rows [B][1 + D K][V] (default: the batch's log-probs; logits=True: raw
+        logits), plus the build state and the per-layer frontier outputs.  n_copies
+        copies of the rows are kept (build_layers uses copy `self.copy`)."""
+        w = self.w
+        assert w.mode == "dynamic"
+        src = w.logprobs if rows is None else rows
+        B, K, D = self.B, w.K, w.D
+        self.layers_logits = bool(logits)
+        rows0 = [_t(np.ascontiguousarray(src[:, :1]).astype(np.float32), self.device)]
+        for l in range(1, D + 1):
+            blk = np.ascontiguousarray(src[:, 1 + (l - 1) * K:1 + l * K]).astype(np.float32)
+            rows0.append(_t(blk, self.device))
+        self.layer_rows_copies = [rows0] + [[t.clone() for t in rows0] for _ in range(n_copies - 1)]
+        n = tv.tree_build_layer_workspace_bytes(B, w.V, K, D)
+        if getattr(self, "layer_state", None) is None or self.layer_state.numel() < n:
+            self.layer_state = torch.zeros(n, dtype=torch.uint8, device=self.device)
+        i32 = dict(dtype=torch.int32, device=self.device)
+        self.frontier_tokens = torch.full((D + 1, B, K), -7, **i32)
+        self.frontier_parents = torch.full((D + 1, B, K), -7, **i32)
+
+    def build_layers(self, meta: bool = True, stream=None):
+        """tree_build_layer for layers 0..D, then tree_build_finish (with the tree
+        metadata when meta, as tree_build_meta)."""
+        w = self.w
+        B, K, D = self.B, w.K, w.D
+        rows = self.layer_rows_copies[self.copy % len(self.layer_rows_copies)]
+        for l in range(D + 1):
+            tv.tree_build_layer(l, B, w.V, K, D, rows[l], self.layers_logits, self.layer_state,
+                                self.frontier_tokens[l], self.frontier_parents[l], stream)
+        if meta:
+            tv.tree_build_finish(B, w.V, K, D, w.total_tokens, self.root_token, self.T_max, self.layer_state,
+                                 self.draft_tokens, self.parents, self.tree_size, self.node_score, self.status,
+                                 self.dcap, self.prefix_len, self.tree_mask, self.tree_position_ids, self.positions,
+                                 self.retrieve_indices, self.leaf_count, self.first_child, self.next_sibling,
+                                 stream=stream)
+        else:
+            tv.tree_build_finish(B, w.V, K, D, w.total_tokens, self.root_token, self.T_max, self.layer_state,
+                                 self.draft_tokens, self.parents, self.tree_size, self.node_score, self.status,
+                                 stream=stream)
+
+    def frontiers_host(self):
+        return self.frontier_tokens.cpu().numpy(), self.frontier_parents.cpu().numpy()
 
     def accept_compact(self, stream=None, copy=None):
         """tree_accept and kv_compact in one launch."""

@@ -103,6 +103,20 @@ def _draft_logprobs(cfg_id: int, B: int, R: int, V: int, std: float, peaked: boo
     return out
 
 
+def draft_logits(cfg_id: int, B: int, R: int, V: int, std: float = 2.0, peaked: bool = False) -> np.ndarray:
+    """The raw draft logits behind _draft_logprobs (same draws), rounded to float32:
+    the input of the layer-by-layer build's fused log-softmax."""
+    out = np.empty((B, R, V), dtype=np.float32)
+    for b in range(B):
+        g = rng(cfg_id, STREAM_LOGITS, b)
+        z = g.standard_normal((R, V)) * std
+        if peaked:
+            hot = g.integers(0, V, size=R)
+            z[np.arange(R), hot] += 12.0
+        out[b] = z.astype(np.float32)
+    return out
+
+
 def _attn_tensors(cfg_id: int, B: int, T_max: int, Hq: int, Hkv: int, d: int, S_cap: int,
                   scale: float, dtype: str):
     Q = np.empty((B, T_max, Hq, d), dtype=np.uint16 if dtype == "bf16" else np.float32)
