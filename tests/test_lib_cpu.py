@@ -106,3 +106,28 @@ def test_paged_calls_host_validation():
     # tree_accept_compact_paged: tree_accept's checks first (dcap >= T_max)
     assert L.tree_accept_compact_paged(1, 16, 16, X, X, X, X, X, X, X, X, 1, 8, 128, 2, X, X, 100, 16, X, 10, 0,
                                        X, None, None) == tv.TV_EINVAL
+
+
+def test_layer_calls_host_validation():
+    L = tv.lib()
+    need = tv.tree_build_layer_workspace_bytes(2, 32000, 10, 6)
+    assert need > 0 and tv.tree_build_layer_workspace_bytes(2, 32000, 17, 6) == 0
+    # tree_build_layer(layer, B, V, K, D, rows, logits, state, state_bytes, ftok, fpar, stream)
+    assert L.tree_build_layer(7, 2, 32000, 10, 6, X, 0, X, need, X, None, None) == tv.TV_EINVAL      # layer > D
+    assert L.tree_build_layer(-1, 2, 32000, 10, 6, X, 0, X, need, X, None, None) == tv.TV_EINVAL
+    assert L.tree_build_layer(0, 2, 32000, 17, 6, X, 0, X, need, X, None, None) == tv.TV_EUNSUPPORTED
+    assert L.tree_build_layer(0, 2, 8, 10, 6, X, 0, X, need, X, None, None) == tv.TV_EINVAL          # K > V
+    assert L.tree_build_layer(0, 2, 32000, 10, 6, None, 0, X, need, X, None, None) == tv.TV_EINVAL
+    assert L.tree_build_layer(0, 2, 32000, 10, 6, X, 1, X, need - 1, X, None, None) == tv.TV_EWORKSPACE
+    # tree_build_finish(B, V, K, D, total, root, T_max, state, bytes, tok, par, size, score, status, dcap, prefix, ...)
+    tail = (X, X, X, X, X, X, X, X, None)
+    assert L.tree_build_finish(2, 32000, 10, 6, 611, X, 64, X, need, X, X, X, None, X, 7, None,
+                               *tail) == tv.TV_EINVAL   # total_tokens > C
+    assert L.tree_build_finish(2, 32000, 10, 6, 64, X, 64, X, need, X, X, X, None, X, 7, None,
+                               *tail) == tv.TV_EINVAL   # total_tokens + 1 > T_max
+    assert L.tree_build_finish(2, 32000, 10, 6, 60, X, 65, X, need, X, X, X, None, X, 7, None,
+                               *tail) == tv.TV_EUNSUPPORTED
+    assert L.tree_build_finish(2, 32000, 10, 6, 60, X, 64, X, need, X, X, X, None, X, 64, X,
+                               *tail) == tv.TV_EINVAL   # dcap >= T_max with metadata
+    assert L.tree_build_finish(2, 32000, 10, 6, 60, X, 64, X, need - 1, X, X, X, None, X, 7, None,
+                               *tail) == tv.TV_EWORKSPACE
