@@ -350,6 +350,72 @@ def accept_walk(draft_tokens, parents, tree_size: int, target_predict, status: i
     return len(path) - 1, padded, int(target_predict[path[-1]])
 
 
+def _residual_sample(row, removed, u):
+    """A token from norm(row with the `removed` tokens' mass taken out): the smallest v
+    whose cumulative residual mass exceeds u times the residual total (float64, in
+    token order); if rounding leaves no such v, the last token with residual mass, and
+    with no residual mass at all the row's best token (probability desc, token asc)."""
+    r = np.asarray(row, dtype=np.float64).copy()
+    if removed:
+        r[sorted(removed)] = 0.0
+    total = r.sum()
+    if not total > 0.0:
+        return int(np.argsort(-np.asarray(row, np.float32), kind="stable")[0])
+    cum = np.cumsum(r)
+    hit = np.nonzero(cum > u * total)[0]
+    if len(hit):
+        return int(hit[0])
+    return int(np.nonzero(r > 0.0)[0][-1])
+
+
+def accept_sample(draft_tokens, parents, tree_size: int, target_probs, uniforms, status: int, dcap: int):
+    """Tree rejection sampling with the target distribution only ([TRT] "non-greedy:
+    rejection sampling from the target distribution alone"; [HB] exercise "trees
+    when sampling": at a node, consider its children in order, accept each with
+    min(1, p(x)/q(x)); on rejection continue with norm(max(0, p - q)); if every child
+    is rejected, sample the correction token from the final residual).
+
+    The tree's candidates are the drafter's deterministic top-K picks, so q for a
+    candidate is the point mass on its token: the acceptance test is p(x) against
+    the remaining mass, and the residual is p with the rejected tokens' mass removed.
+    target_probs[i] is the target's (already filtered) distribution at node i;
+    uniforms[c] (c >= 1) is the draw for child c's test, uniforms[0] the draw for the
+    correction token.  At node n with row p, Z = sum(p) and R = the mass of the tokens
+    rejected so far at n (float64): child c (ascending id) with token x is accepted iff
+    uniforms[c] * (Z - R) < p(x) (p(x) = 0 for an already-rejected token).  The walk
+    stops at depth dcap (the correction is then sampled from the full row there).
+    Returns accept_len, the padded path (root first) and the correction (bonus) token."""
+    path = [0]
+    node = 0
+    removed = set()
+    if status == ST_OK:
+        T = int(tree_size)
+        while True:
+            removed = set()
+            if len(path) > dcap:
+                break
+            row = np.asarray(target_probs[node], dtype=np.float64)
+            Z = row.sum()
+            R = 0.0
+            nxt = None
+            for c in (c for c in range(1, T) if parents[c] == node):
+                x = int(draft_tokens[c])
+                px = 0.0 if x in removed else float(row[x])
+                if float(uniforms[c]) * (Z - R) < px:
+                    nxt = c
+                    break
+                if x not in removed:
+                    R += px
+                    removed.add(x)
+            if nxt is None:
+                break
+            path.append(nxt)
+            node = nxt
+    bonus = _residual_sample(target_probs[node], removed, float(uniforms[0]))
+    padded = path + [-1] * (dcap + 1 - len(path))
+    return len(path) - 1, padded, bonus
+
+
 def accept_posterior(draft_tokens, retrieve_rows, leaf_count: int, target_predict):
     """[E2] section 5: for every retrieve row (a root-to-leaf path) mark position k >= 1
     accepted when the draft token there equals the target's argmax at position k-1;
@@ -403,6 +469,18 @@ def tree_mask_positions(parents, tree_size, prefix_len, T_max: int, dcap: int, s
         for k, v in r.items():
             out[k][b] = v
     return out
+
+
+def tree_accept_sample(draft_tokens, parents, tree_size, target_probs, uniforms, status, dcap: int):
+    B = draft_tokens.shape[0]
+    alen = np.zeros(B, np.int32)
+    apath = np.full((B, dcap + 1), -1, np.int32)
+    bonus = np.zeros(B, np.int32)
+    for b in range(B):
+        a, p, bt = accept_sample(list(draft_tokens[b]), list(parents[b]), int(tree_size[b]), target_probs[b],
+                                 uniforms[b], int(status[b]), dcap)
+        alen[b], apath[b], bonus[b] = a, p, bt
+    return dict(accept_len=alen, accept_path=apath, bonus_token=bonus)
 
 
 def tree_accept(draft_tokens, parents, tree_size, target_predict, status, dcap: int):
