@@ -204,6 +204,9 @@ def main():
     ap.add_argument("--layerwise", choices=["logprobs", "logits"], default=None,
                     help="build the dynamic tree one draft layer at a time (tree_build_layer x (D+1), then "
                          "tree_build_finish with the metadata), from log-prob rows or raw logits")
+    ap.add_argument("--sampling", action="store_true",
+                    help="accept by target-only tree rejection sampling (tree_accept_sample, then the compaction) "
+                         "from synthetic target distributions instead of the greedy walk")
     ap.add_argument("--copy-mb", type=float, default=0.0,
                     help="before warmup, one device-to-device copy of this many MiB (a plain copy kernel of known "
                          "size that calibrates the HBM byte counters of a profiler run)")
@@ -253,6 +256,10 @@ def main():
     th = step.tree_host()
     mh = step.meta_host()
     step.set_target_predict(gen.synthetic_target_predict(w, th["draft_tokens"], th["parents"], th["tree_size"]))
+    if args.sampling:
+        probs, uni = gen.synthetic_target_probs(w, th["draft_tokens"], th["parents"], th["tree_size"])
+        step.set_target_probs(probs, uni)
+        del probs
     torch.cuda.synchronize()
     status = mh["status"]
     nodes = int(np.where(status != 0, 1, th["tree_size"]).sum())
@@ -271,7 +278,10 @@ def main():
         step.attention()
         if ev is not None:
             ev[1].record(stream)
-        if args.unfused:
+        if args.sampling:
+            step.accept_sample()
+            step.compact()
+        elif args.unfused:
             step.accept()
             step.compact()
         else:
@@ -382,7 +392,8 @@ def main():
                        f"tree_build_layer x {w.D + 1} ({args.layerwise} rows), tree_build_finish" if args.layerwise
                        else ("tree_build, tree_mask_positions" if args.unfused else "tree_build_meta"),
                        "tree_attention" + ("_paged" if paged is not None else ""),
-                       ("tree_accept, kv_compact" if args.unfused else "tree_accept_compact") +
+                       ("tree_accept_sample, kv_compact" if args.sampling else
+                        "tree_accept, kv_compact" if args.unfused else "tree_accept_compact") +
                        ("_paged" if paged is not None else "")])},
         "stages_us": stages,
         "roofline": roof,

@@ -9,6 +9,7 @@
  *                                           retrieve_indices, child/sibling lists
  *   tree_attention      Q, K/V cache, mask -> O (every node over prefix + ancestors)
  *   tree_accept         target argmax per node -> accepted path, bonus token
+ *   (tree_accept_sample the same from target distributions, by rejection sampling)
  *   kv_compact          accepted path    -> K/V rows moved to contiguous slots
  *   tree_accept_compact the last two in one launch
  * and the same attention and compaction over a paged K/V cache (a block table
@@ -257,6 +258,40 @@ int tree_attention(int dtype, int B, int T_max, int Hq, int Hkv, int d,
 int tree_accept(int B, int T_max, int dcap, const int* draft_tokens, const int* parents,
                 const int* tree_size, const int* target_predict, const int* status,
                 int* accept_len, int* accept_path, int* bonus_token, void* stream);
+
+/* ------------------------------------------------------------------------- *
+ * tree_accept_sample -- non-greedy acceptance: [TRT] target-only rejection
+ * sampling (one probability test per node instead of an argmax comparison, and
+ * a correction token sampled from the target distribution at the point of
+ * rejection), [HB] exercise "trees when sampling" (children in order, accept
+ * with min(1, p/q), continue with norm(max(0, p - q)), sample the correction
+ * from the last residual when every child is rejected).
+ *
+ * The tree's candidates are the drafter's deterministic top-K picks, so a
+ * candidate's draft distribution q is the point mass on its token.  From the
+ * root: at node n with target row p = target_probs[b][n] (Z = sum of the row,
+ * float64), try the children in ascending id; child c with token x is accepted
+ * iff uniforms[b][c] * (Z - R) < p(x), R being the mass of the tokens already
+ * rejected at n (a token already rejected, or outside [0, V), has p(x) = 0);
+ * on acceptance move to c.  The walk stops when every child is rejected, at
+ * depth dcap, or at once when status != 0.  bonus_token = the correction at the
+ * last node: with r = p minus the rejected tokens' mass, the smallest v whose
+ * cumulative sum of r (float64, token order) exceeds uniforms[b][0] * sum(r);
+ * if rounding leaves none, the last v with r(v) > 0; if sum(r) = 0, the row's
+ * best token (probability desc, token asc).
+ * In:  draft_tokens, parents [B][T_max], tree_size [B], status [B];
+ *      target_probs float32 [B][T_max][V] (the target's distribution at every
+ *      node after the caller's temperature / top-k / top-p filtering; rows of
+ *      nodes the walk does not reach are not read); uniforms float32 [B][T_max]
+ *      in [0, 1): entry c >= 1 is the draw for child c's test, entry 0 the draw
+ *      for the correction token.
+ * Out: accept_len, accept_path, bonus_token as tree_accept.
+ * Requires 1 <= T_max <= 64, 0 <= dcap < T_max, V >= 1.
+ * ------------------------------------------------------------------------- */
+int tree_accept_sample(int B, int T_max, int dcap, int V, const int* draft_tokens, const int* parents,
+                       const int* tree_size, const float* target_probs, const float* uniforms,
+                       const int* status, int* accept_len, int* accept_path, int* bonus_token,
+                       void* stream);
 
 /* ------------------------------------------------------------------------- *
  * kv_compact -- [TRT] "after acceptance: KV from tree layout back to linear",

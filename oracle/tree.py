@@ -400,11 +400,12 @@ def accept_sample(draft_tokens, parents, tree_size: int, target_probs, uniforms,
             nxt = None
             for c in (c for c in range(1, T) if parents[c] == node):
                 x = int(draft_tokens[c])
-                px = 0.0 if x in removed else float(row[x])
+                inside = 0 <= x < len(row)                  # a token outside the vocabulary has no mass
+                px = 0.0 if (x in removed or not inside) else float(row[x])
                 if float(uniforms[c]) * (Z - R) < px:
                     nxt = c
                     break
-                if x not in removed:
+                if inside and x not in removed:
                     R += px
                     removed.add(x)
             if nxt is None:

@@ -131,3 +131,13 @@ def test_layer_calls_host_validation():
                                *tail) == tv.TV_EINVAL   # dcap >= T_max with metadata
     assert L.tree_build_finish(2, 32000, 10, 6, 60, X, 64, X, need - 1, X, X, X, None, X, 7, None,
                                *tail) == tv.TV_EWORKSPACE
+
+
+def test_accept_sample_host_validation():
+    L = tv.lib()
+    # tree_accept_sample(B, T_max, dcap, V, tokens, parents, size, probs, uniforms, status, len, path, bonus, stream)
+    assert L.tree_accept_sample(1, 16, 16, 100, X, X, X, X, X, X, X, X, X, None) == tv.TV_EINVAL   # dcap >= T_max
+    assert L.tree_accept_sample(1, 65, 7, 100, X, X, X, X, X, X, X, X, X, None) == tv.TV_EUNSUPPORTED
+    assert L.tree_accept_sample(1, 16, 7, 0, X, X, X, X, X, X, X, X, X, None) == tv.TV_EINVAL      # V = 0
+    assert L.tree_accept_sample(1, 16, 7, 100, X, X, X, None, X, X, X, X, X, None) == tv.TV_EINVAL
+    assert L.tree_accept_sample(0, 16, 7, 100, X, X, X, X, X, X, X, X, X, None) == tv.TV_EINVAL

@@ -56,6 +56,7 @@ _SIGS = {
     "tree_build_layer_workspace_bytes": (SZ, [I, I, I, I]),
     "tree_build_layer": (I, [I, I, I, I, I, P, I, P, SZ, P, P, P]),
     "tree_build_finish": (I, [I, I, I, I, I, P, I, P, SZ, P, P, P, P, P, I, P, P, P, P, P, P, P, P, P]),
+    "tree_accept_sample": (I, [I, I, I, I, P, P, P, P, P, P, P, P, P, P]),
     "tv_error_string": (ctypes.c_char_p, [I]),
     "tv_status_string": (ctypes.c_char_p, [I]),
 }
@@ -285,3 +286,13 @@ def tree_build_finish(B, V, K, D, total_tokens, root_token, T_max, state, draft_
                                  _dev(first_child, "first_child"), _dev(next_sibling, "next_sibling"),
                                  _stream(stream))
     _check("tree_build_finish", rc)
+
+
+def tree_accept_sample(B, T_max, dcap, V, draft_tokens, parents, tree_size, target_probs, uniforms, status,
+                       accept_len, accept_path, bonus_token, stream=None):
+    rc = lib().tree_accept_sample(B, T_max, dcap, V, _dev(draft_tokens, "draft_tokens"), _dev(parents, "parents"),
+                                  _dev(tree_size, "tree_size"), _dev(target_probs, "target_probs"),
+                                  _dev(uniforms, "uniforms"), _dev(status, "status"), _dev(accept_len, "accept_len"),
+                                  _dev(accept_path, "accept_path"), _dev(bonus_token, "bonus_token"),
+                                  _stream(stream))
+    _check("tree_accept_sample", rc)

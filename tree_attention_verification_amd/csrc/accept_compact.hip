@@ -70,6 +70,187 @@ __global__ __launch_bounds__(64) void k_tree_accept(int T_max, int dcap, const i
   }
 }
 
+// --------------------------------------------------------------------------
+// Tree rejection sampling with the target distribution only (the TensorRT-LLM
+// dissection's target-only rejection sampling; the handbook's exercise on trees
+// when sampling).  The tree's candidates are the drafter's deterministic top-K
+// picks, so a candidate's draft distribution is the point mass on its token: at
+// node n with target row p (mass Z), children are tried in ascending id and
+// child c with token x is accepted iff u_c (Z - R) < p(x), R the mass of the
+// tokens already rejected at n; if none is accepted (or the depth cap is
+// reached) the correction token is drawn from p with the rejected tokens'
+// mass removed: the smallest v whose cumulative residual mass exceeds u_0 times
+// the residual total.  Sums are float64.
+//
+// One 256-thread workgroup per request.  Per visited node one pass over the row
+// gives Z while the first wavefront fetches p(x) of every child at once (lane c
+// = node c), so the sequential decisions only move data between lanes.  The
+// correction makes one more pass: each thread sums its contiguous slice of the
+// residual, a block scan of the slice sums finds the slice holding the target,
+// and that thread walks its slice.
+// --------------------------------------------------------------------------
+constexpr int kSampleThreads = 256;
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__global__ __launch_bounds__(kSampleThreads) void k_tree_accept_sample(
+    int T_max, int dcap, int V, const int* __restrict__ draft_tokens, const int* __restrict__ parents,
+    const int* __restrict__ tree_size, const float* __restrict__ target_probs, const float* __restrict__ uniforms,
+    const int* __restrict__ status, int* __restrict__ accept_len, int* __restrict__ accept_path,
+    int* __restrict__ bonus_token) {
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int NWV = kSampleThreads / 64;
+  __shared__ double s_red[NWV];
+  __shared__ int s_rem[64];  // tokens rejected at the current node
+  __shared__ int s_path[64];
+  __shared__ int s_next, s_nrem, s_pick;
+  const long long ob = (long long)b * T_max;
+  int T = tree_size[b];
+  const bool ok = status[b] == TV_ST_OK && T >= 1 && T <= T_max;
+  if (!ok) T = 1;
+  // per-node data in the first wavefront's lanes (lane c = node c)
+  const int tok_l = lane < T ? draft_tokens[ob + lane] : -1;
+  const int par_l = (lane > 0 && lane < T) ? parents[ob + lane] : -2;
+  const float u_l = lane < T_max ? uniforms[ob + lane] : 0.0f;
+  // block sum of one double per thread
+  auto block_sum = [&](double v) -> double {
+    v = wave_sum_f64(v);
+    if (lane == 0) s_red[wave] = v;
+    __syncthreads();
+    double t = 0.0;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) t += s_red[w];
+    __syncthreads();
+    return t;
+  };
+  const int span = (V + kSampleThreads - 1) / kSampleThreads;  // this thread's slice of a row
+  const int v0 = min(V, tid * span), v1 = min(V, v0 + span);
+
+  int node = 0, len = 0, nrem = 0;
+  if (tid == 0) s_path[0] = 0;
+  while (ok && len < dcap) {
+    const float* row = target_probs + (ob + node) * (long long)V;
+    // p(x) of every child of this node, fetched together (first wavefront)
+    float pc = 0.0f;
+    const bool kid = par_l == node;
+    if (wave == 0 && kid && tok_l >= 0 && tok_l < V) pc = row[tok_l];  // a token outside the vocabulary has no mass
+    double part = 0.0;
+    for (int v = v0; v < v1; ++v) part += (double)row[v];
+    const double Z = block_sum(part);
+    if (wave == 0) {
+      // children in ascending id (the current node and every decision are
+      // wave-uniform); lane q keeps the q-th token rejected here
+      unsigned long long kids = __ballot(kid);
+      double R = 0.0;
+      int next = -1, nr = 0, rem_l = -1;
+      while (kids) {
+        const int c = __ffsll((long long)kids) - 1;
+        kids &= kids - 1;
+        const int x = __builtin_amdgcn_readlane(tok_l, c);
+        const bool seen = __ballot(rem_l == x) != 0ull;
+        const double px = seen ? 0.0 : (double)__int_as_float(__builtin_amdgcn_readlane(__float_as_int(pc), c));
+        const double uc = (double)__int_as_float(__builtin_amdgcn_readlane(__float_as_int(u_l), c));
+        if (uc * (Z - R) < px) {
+          next = c;
+          break;
+        }
+        if (!seen) {
+          R += px;
+          if (lane == nr) rem_l = x;
+          ++nr;
+        }
+      }
+      if (lane < nr) s_rem[lane] = rem_l;
+      if (lane == 0) {
+        s_next = next;
+        s_nrem = nr;
+      }
+    }
+    __syncthreads();
+    const int next = s_next;
+    nrem = s_nrem;
+    if (next < 0) break;
+    ++len;
+    node = next;
+    nrem = 0;
+    if (tid == 0) s_path[len] = node;
+  }
+  __syncthreads();
+
+  // the correction token at `node`, from the row with the nrem rejected tokens removed
+  const float* row = target_probs + (ob + node) * (long long)V;
+  auto removed = [&](int v) {
+    for (int q = 0; q < nrem; ++q)
+      if (s_rem[q] == v) return true;
+    return false;
+  };
+  double slice = 0.0;
+  for (int v = v0; v < v1; ++v)
+    if (!removed(v)) slice += (double)row[v];
+  // inclusive scan of the slice sums over the workgroup
+  double incl = slice;
+  for (int o = 1; o < 64; o <<= 1) {
+    const double y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) s_red[wave] = incl;
+  __syncthreads();
+  double before = 0.0, total = 0.0;
+#pragma unroll
+  for (int w = 0; w < NWV; ++w) {
+    if (w < wave) before += s_red[w];
+    total += s_red[w];
+  }
+  const double excl = before + incl - slice;
+  if (tid == 0) s_pick = -1;
+  __syncthreads();
+  const double target = (double)__int_as_float(__builtin_amdgcn_readlane(__float_as_int(u_l), 0)) * total;
+  if (total > 0.0) {
+    // the slice where the cumulative mass first exceeds the target
+    if (excl <= target && excl + slice > target) {
+      double cum = excl;
+      for (int v = v0; v < v1; ++v) {
+        if (removed(v)) continue;
+        cum += (double)row[v];
+        if (cum > target) {
+          s_pick = v;
+          break;
+        }
+      }
+    }
+    __syncthreads();
+    if (s_pick < 0) {  // rounding left the target past the total: the last token with residual mass
+      int last = -1;
+      for (int v = v0; v < v1; ++v)
+        if (!removed(v) && row[v] > 0.0f) last = v;
+      if (last >= 0) atomicMax(&s_pick, last);
+      __syncthreads();
+    }
+  } else {
+    // no residual mass: the row's best token (probability desc, token asc)
+    unsigned long long best = 0ull;
+    for (int v = v0; v < v1; ++v) best = umax64(best, rank_key(row[v], (uint32_t)v));
+    best = wave_max_u64(best);
+    __shared__ unsigned long long s_best[NWV];
+    if (lane == 0) s_best[wave] = best;
+    __syncthreads();
+    if (tid == 0) {
+      unsigned long long m = 0ull;
+      for (int w = 0; w < NWV; ++w) m = umax64(m, s_best[w]);
+      s_pick = (int)key_index(m);
+    }
+    __syncthreads();
+  }
+  if (tid <= dcap) accept_path[(long long)b * (dcap + 1) + tid] = tid <= len ? s_path[tid] : -1;
+  if (tid == 0) {
+    accept_len[b] = len;
+    bonus_token[b] = s_pick;
+  }
+}
+
 constexpr int kCompactThreads = 256;
 
 // Moves request b's accepted rows of one (kv head, layer).  The caller has
@@ -287,6 +468,22 @@ int accept_compact_impl(int B, int T_max, int dcap, const int* draft_tokens, con
 
 }  // namespace
 }  // namespace tv
+
+extern "C" int tree_accept_sample(int B, int T_max, int dcap, int V, const int* draft_tokens, const int* parents,
+                                  const int* tree_size, const float* target_probs, const float* uniforms,
+                                  const int* status, int* accept_len, int* accept_path, int* bonus_token,
+                                  void* stream) {
+  if (B <= 0 || T_max <= 0 || dcap < 0 || dcap >= T_max || V <= 0) return TV_EINVAL;
+  if (T_max > tv::kTMaxLimit) return TV_EUNSUPPORTED;
+  if (!draft_tokens || !parents || !tree_size || !target_probs || !uniforms || !status || !accept_len ||
+      !accept_path || !bonus_token)
+    return TV_EINVAL;
+  hipLaunchKernelGGL(tv::k_tree_accept_sample, dim3(B), dim3(tv::kSampleThreads), 0,
+                     reinterpret_cast<hipStream_t>(stream), T_max, dcap, V, draft_tokens, parents, tree_size,
+                     target_probs, uniforms, status, accept_len, accept_path, bonus_token);
+  TV_CHECK_LAUNCH();
+  return TV_OK;
+}
 
 extern "C" int kv_compact(int B, int n_layers, int Hkv, int d, int elem_bytes, void* Kc, void* Vc, long long S_cap,
                           long long layer_stride_elems, const int* prefix_len, const int* accept_path,

@@ -257,6 +257,18 @@ class TreeVerifyStep:
         self.accept(stream)
         self.compact(stream)
 
+    # ---- non-greedy acceptance ------------------------------------------------
+    def set_target_probs(self, probs: np.ndarray, uniforms: np.ndarray):
+        """The target's distribution at every node [B][T_max][V] and the draws [B][T_max]."""
+        self.target_probs = _t(np.ascontiguousarray(probs, dtype=np.float32), self.device)
+        self.uniforms = _t(np.ascontiguousarray(uniforms, dtype=np.float32), self.device)
+
+    def accept_sample(self, stream=None):
+        """tree_accept_sample: target-only tree rejection sampling."""
+        tv.tree_accept_sample(self.B, self.T_max, self.dcap, self.target_probs.shape[-1], self.draft_tokens,
+                              self.parents, self.tree_size, self.target_probs, self.uniforms, self.status,
+                              self.accept_len, self.accept_path, self.bonus_token, stream)
+
     def set_target_predict(self, tp: np.ndarray):
         self.target_predict.copy_(torch.from_numpy(np.ascontiguousarray(tp.astype(np.int32))))
 

@@ -7,7 +7,7 @@ HIP path and the CPU oracle are fed the *same bytes* from here.
 
 Every stream is a PCG64 generator seeded with ``[cfg_id, stream, b]``:
   0 draft logits, 1 Q, 2 K, 3 V, 4 target draws, 5 shapes/topology, 6 root
-  tokens, 7 paged-cache block placement.
+  tokens, 7 paged-cache block placement, 8 target distributions for sampling.
 
 Workload shapes follow the five configurations the tree-verification step is
 measured on (tree sizes as in the EAGLE-2 walkthrough's ``topK_generate``
@@ -23,7 +23,7 @@ from typing import List, Optional
 
 import numpy as np
 
-STREAM_LOGITS, STREAM_Q, STREAM_K, STREAM_V, STREAM_TARGET, STREAM_SHAPE, STREAM_ROOT, STREAM_PAGES = range(8)
+STREAM_LOGITS, STREAM_Q, STREAM_K, STREAM_V, STREAM_TARGET, STREAM_SHAPE, STREAM_ROOT, STREAM_PAGES, STREAM_PROBS = range(9)
 
 T_MAX_DEFAULT = 64
 DCAP_DEFAULT = 7
@@ -371,3 +371,34 @@ def paged_layout(w: Workload, tokens_per_block: int, spare_blocks: Optional[int]
         pool[table.reshape(-1)] = blocks.reshape(n_used, Hkv, bs, d)
         pools.append(pool)
     return PagedCache(bs, max_blocks, n_blocks, table, pools[0], pools[1])
+
+
+def synthetic_target_probs(w: Workload, draft_tokens: np.ndarray, parents: np.ndarray, tree_size: np.ndarray,
+                           concentration: float = 0.3):
+    """Stand-in for the target model's (filtered) next-token distribution at every node,
+    and the uniform draws of rejection sampling.  Row i of a tree node is Gamma(
+    concentration) noise normalised to sum 1 - m plus mass m ~ U[0.5, 0.95] on the
+    token of one of node i's children (chosen uniformly) with probability
+    accept_prob; rows of padding nodes are zero.  Returns float32 probs
+    [B][T_max][V] and float32 uniforms [B][T_max] in [0, 1)."""
+    B, T_max = draft_tokens.shape
+    V = w.V
+    probs = np.zeros((B, T_max, V), np.float32)
+    uni = np.zeros((B, T_max), np.float32)
+    for b in range(B):
+        g = rng(w.cfg_id, STREAM_PROBS, b)
+        T = int(tree_size[b])
+        T = 1 if T < 1 or T > T_max else T
+        for i in range(T):
+            noise = g.gamma(concentration, size=V)
+            kids = [c for c in range(1, T) if parents[b, c] == i]
+            row = noise / noise.sum()
+            if kids and g.random() < w.accept_prob:
+                m = g.uniform(0.5, 0.95)
+                x = int(draft_tokens[b, kids[int(g.integers(0, len(kids)))]])
+                if 0 <= x < V:
+                    row = row * (1.0 - m)
+                    row[x] += m
+            probs[b, i] = row.astype(np.float32)
+        uni[b] = g.random(T_max).astype(np.float32)
+    return probs, uni
