@@ -82,22 +82,35 @@ __global__ __launch_bounds__(64) void k_tree_accept(int T_max, int dcap, const i
 // mass removed: the smallest v whose cumulative residual mass exceeds u_0 times
 // the residual total.  Sums are float64.
 //
-// One 256-thread workgroup per request.  Per visited node one pass over the row
-// gives Z while the first wavefront fetches p(x) of every child at once (lane c
-// = node c), so the sequential decisions only move data between lanes.  The
-// correction makes one more pass: each thread sums its contiguous slice of the
-// residual, a block scan of the slice sums finds the slice holding the target,
-// and that thread walks its slice.
+// One 1024-thread workgroup per request (a row is 128 KB at V = 32000: eight
+// 16-byte loads in flight per thread cover it in one round trip).  Per visited
+// node one coalesced pass over the row gives Z while the
+// first wavefront fetches p(x) of every child at once (lane c = node c), so the
+// sequential decisions only move data between lanes.  The correction cuts the
+// row into 1024 contiguous chunks: each wavefront sums its chunks with coalesced
+// loads, a block scan of the chunk sums finds the chunk holding the target, and
+// the first wavefront scans that chunk.
 // --------------------------------------------------------------------------
-constexpr int kSampleThreads = 256;
+constexpr int kSampleThreads = 1024;
+constexpr int kPiece = 8 * kSampleThreads;  // row entries read per pass step (8 per thread)
+constexpr int kMaxPieces = 32;              // V <= 262144
 
 __device__ __forceinline__ double wave_sum_f64(double v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
 }
 
+// inclusive prefix sum over the wavefront
+__device__ __forceinline__ double wave_incl_f64(double v, int lane) {
+  for (int o = 1; o < 64; o <<= 1) {
+    const double y = __shfl_up(v, o, 64);
+    if (lane >= o) v += y;
+  }
+  return v;
+}
+
 __global__ __launch_bounds__(kSampleThreads) void k_tree_accept_sample(
-    int T_max, int dcap, int V, const int* __restrict__ draft_tokens, const int* __restrict__ parents,
+    int T_max, int dcap, int V, int vec4, const int* __restrict__ draft_tokens, const int* __restrict__ parents,
     const int* __restrict__ tree_size, const float* __restrict__ target_probs, const float* __restrict__ uniforms,
     const int* __restrict__ status, int* __restrict__ accept_len, int* __restrict__ accept_path,
     int* __restrict__ bonus_token) {
@@ -115,7 +128,6 @@ __global__ __launch_bounds__(kSampleThreads) void k_tree_accept_sample(
   const int tok_l = lane < T ? draft_tokens[ob + lane] : -1;
   const int par_l = (lane > 0 && lane < T) ? parents[ob + lane] : -2;
   const float u_l = lane < T_max ? uniforms[ob + lane] : 0.0f;
-  // block sum of one double per thread
   auto block_sum = [&](double v) -> double {
     v = wave_sum_f64(v);
     if (lane == 0) s_red[wave] = v;
@@ -126,20 +138,48 @@ __global__ __launch_bounds__(kSampleThreads) void k_tree_accept_sample(
     __syncthreads();
     return t;
   };
-  const int span = (V + kSampleThreads - 1) / kSampleThreads;  // this thread's slice of a row
-  const int v0 = min(V, tid * span), v1 = min(V, v0 + span);
+  // A row is read in pieces of kPiece entries; in piece k thread t owns the 8
+  // contiguous entries [k kPiece + 8 t, + 8) (a wavefront reads 2 KB contiguous).
+  const int n_pieces = (V + kPiece - 1) / kPiece;
+  auto load8 = [&](const float* row, int k, float (&x)[8]) __attribute__((always_inline)) {
+    const int v0 = k * kPiece + 8 * tid;
+    if (vec4 && v0 + 8 <= V) {
+      typedef float f4 __attribute__((ext_vector_type(4)));
+      const f4 a = *reinterpret_cast<const f4*>(row + v0), c = *reinterpret_cast<const f4*>(row + v0 + 4);
+      x[0] = a[0]; x[1] = a[1]; x[2] = a[2]; x[3] = a[3];
+      x[4] = c[0]; x[5] = c[1]; x[6] = c[2]; x[7] = c[3];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = v0 + e < V ? row[v0 + e] : 0.0f;
+    }
+  };
+  // float64 sum of a whole row (four pieces' loads in flight at a time)
+  auto row_sum = [&](const float* row) -> double {
+    double acc = 0.0;
+    for (int k0 = 0; k0 < n_pieces; k0 += 4) {
+      float x[4][8];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (k0 + u < n_pieces) load8(row, k0 + u, x[u]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (k0 + u < n_pieces)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc += (double)x[u][e];
+    }
+    return block_sum(acc);
+  };
 
   int node = 0, len = 0, nrem = 0;
   if (tid == 0) s_path[0] = 0;
   while (ok && len < dcap) {
     const float* row = target_probs + (ob + node) * (long long)V;
-    // p(x) of every child of this node, fetched together (first wavefront)
+    // p(x) of every child of this node, fetched together (first wavefront); a
+    // token outside the vocabulary has no mass
     float pc = 0.0f;
     const bool kid = par_l == node;
-    if (wave == 0 && kid && tok_l >= 0 && tok_l < V) pc = row[tok_l];  // a token outside the vocabulary has no mass
-    double part = 0.0;
-    for (int v = v0; v < v1; ++v) part += (double)row[v];
-    const double Z = block_sum(part);
+    if (wave == 0 && kid && tok_l >= 0 && tok_l < V) pc = row[tok_l];
+    const double Z = row_sum(row);
     if (wave == 0) {
       // children in ascending id (the current node and every decision are
       // wave-uniform); lane q keeps the q-th token rejected here
@@ -180,59 +220,89 @@ __global__ __launch_bounds__(kSampleThreads) void k_tree_accept_sample(
   }
   __syncthreads();
 
-  // the correction token at `node`, from the row with the nrem rejected tokens removed
+  // ---- the correction token at `node`, from the row with the nrem rejected tokens removed
   const float* row = target_probs + (ob + node) * (long long)V;
   auto removed = [&](int v) {
-    for (int q = 0; q < nrem; ++q)
-      if (s_rem[q] == v) return true;
-    return false;
+    bool r = false;
+    for (int q = 0; q < nrem; ++q) r |= s_rem[q] == v;
+    return r;
   };
-  double slice = 0.0;
-  for (int v = v0; v < v1; ++v)
-    if (!removed(v)) slice += (double)row[v];
-  // inclusive scan of the slice sums over the workgroup
-  double incl = slice;
-  for (int o = 1; o < 64; o <<= 1) {
-    const double y = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += y;
-  }
-  if (lane == 63) s_red[wave] = incl;
-  __syncthreads();
-  double before = 0.0, total = 0.0;
+  // residual mass of this thread's run of a piece
+  auto run_mass = [&](int k, float (&x)[8]) -> double {
+    const int v0 = k * kPiece + 8 * tid;
+    double run = 0.0;
 #pragma unroll
-  for (int w = 0; w < NWV; ++w) {
-    if (w < wave) before += s_red[w];
-    total += s_red[w];
+    for (int e = 0; e < 8; ++e)
+      if (v0 + e < V && !removed(v0 + e)) run += (double)x[e];
+    return run;
+  };
+  // pass 1: the residual total, hence the target
+  double acc = 0.0;
+  for (int k0 = 0; k0 < n_pieces; k0 += 4) {
+    float x[4][8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (k0 + u < n_pieces) load8(row, k0 + u, x[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (k0 + u < n_pieces) acc += run_mass(k0 + u, x[u]);
   }
-  const double excl = before + incl - slice;
+  const double total = block_sum(acc);
   if (tid == 0) s_pick = -1;
   __syncthreads();
   const double target = (double)__int_as_float(__builtin_amdgcn_readlane(__float_as_int(u_l), 0)) * total;
+  __shared__ double s_last[NWV];
+  __shared__ double s_carry;
   if (total > 0.0) {
-    // the slice where the cumulative mass first exceeds the target
-    if (excl <= target && excl + slice > target) {
-      double cum = excl;
-      for (int v = v0; v < v1; ++v) {
-        if (removed(v)) continue;
-        cum += (double)row[v];
-        if (cum > target) {
-          s_pick = v;
-          break;
+    // pass 2, piece by piece: a block inclusive scan of the runs' masses; run
+    // (k, t) spans [I(k, t-1), I(k, t)) of the cumulative mass, each boundary one
+    // stored number shared by both neighbours, so at most one run holds the target
+    double carry = 0.0;
+    for (int k = 0; k < n_pieces; ++k) {
+      float x[8];
+      load8(row, k, x);
+      const double incl = wave_incl_f64(run_mass(k, x), lane);
+      if (lane == 63) s_last[wave] = incl;
+      __syncthreads();
+      double off = carry;
+      for (int w = 0; w < wave; ++w) off += s_last[w];
+      const double hi = off + incl;
+      const double up = __shfl_up(hi, 1, 64);
+      const double lo = lane > 0 ? up : off;
+      if (lo <= target && target < hi) {
+        // this run holds the target: walk it; if rounding keeps the sum below the
+        // target, its last entry with mass
+        const int v0 = k * kPiece + 8 * tid;
+        double cum = lo;
+        int pick = -1, last = -1;
+        for (int e = 0; e < 8 && v0 + e < V; ++e) {
+          if (removed(v0 + e)) continue;
+          if (x[e] > 0.0f) last = v0 + e;
+          cum += (double)x[e];
+          if (cum > target) {
+            pick = v0 + e;
+            break;
+          }
         }
+        s_pick = pick >= 0 ? pick : last;
       }
+      if (tid == kSampleThreads - 1) s_carry = hi;
+      __syncthreads();
+      carry = s_carry;
+      __syncthreads();
     }
     __syncthreads();
     if (s_pick < 0) {  // rounding left the target past the total: the last token with residual mass
       int last = -1;
-      for (int v = v0; v < v1; ++v)
-        if (!removed(v) && row[v] > 0.0f) last = v;
+      for (int v = tid; v < V; v += kSampleThreads)
+        if (row[v] > 0.0f && !removed(v)) last = v;
       if (last >= 0) atomicMax(&s_pick, last);
       __syncthreads();
     }
   } else {
     // no residual mass: the row's best token (probability desc, token asc)
     unsigned long long best = 0ull;
-    for (int v = v0; v < v1; ++v) best = umax64(best, rank_key(row[v], (uint32_t)v));
+    for (int v = tid; v < V; v += kSampleThreads) best = umax64(best, rank_key(row[v], (uint32_t)v));
     best = wave_max_u64(best);
     __shared__ unsigned long long s_best[NWV];
     if (lane == 0) s_best[wave] = best;
@@ -474,12 +544,13 @@ extern "C" int tree_accept_sample(int B, int T_max, int dcap, int V, const int* 
                                   const int* status, int* accept_len, int* accept_path, int* bonus_token,
                                   void* stream) {
   if (B <= 0 || T_max <= 0 || dcap < 0 || dcap >= T_max || V <= 0) return TV_EINVAL;
-  if (T_max > tv::kTMaxLimit) return TV_EUNSUPPORTED;
+  if (T_max > tv::kTMaxLimit || V > tv::kMaxPieces * tv::kPiece) return TV_EUNSUPPORTED;
   if (!draft_tokens || !parents || !tree_size || !target_probs || !uniforms || !status || !accept_len ||
       !accept_path || !bonus_token)
     return TV_EINVAL;
+  const int vec4 = (V % 4 == 0) && ((reinterpret_cast<uintptr_t>(target_probs) & 15) == 0);
   hipLaunchKernelGGL(tv::k_tree_accept_sample, dim3(B), dim3(tv::kSampleThreads), 0,
-                     reinterpret_cast<hipStream_t>(stream), T_max, dcap, V, draft_tokens, parents, tree_size,
+                     reinterpret_cast<hipStream_t>(stream), T_max, dcap, V, vec4, draft_tokens, parents, tree_size,
                      target_probs, uniforms, status, accept_len, accept_path, bonus_token);
   TV_CHECK_LAUNCH();
   return TV_OK;
