@@ -136,3 +136,29 @@ def attention_rows_paged(Q, K_pool, V_pool, block_table, tokens_per_block, prefi
     Kc = paged_to_linear(K_pool, block_table, tokens_per_block, n)
     Vc = paged_to_linear(V_pool, block_table, tokens_per_block, n)
     return attention_rows(Q, Kc, Vc, prefix_len, tree_size, tree_mask, samples, scale=scale, status=status)
+
+
+def rope_rotate(x, positions, theta):
+    """Rotary position embedding of the last axis of x at the given positions ([HB]
+    forward_with_mask applies it to the tree's queries and keys at position
+    prefix + depth).  Pairs (i, i + d/2) rotate by angle pos * theta**(-2i/d) (the
+    rotate-half layout): out_i = x_i cos - x_(i+d/2) sin, out_(i+d/2) = x_(i+d/2) cos
+    + x_i sin.  x: [..., d] (float64 after to_f64), positions broadcast against x's
+    leading axes.  All in float64."""
+    x = to_f64(x) if np.asarray(x).dtype == np.uint16 else np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    half = d // 2
+    inv = theta ** (-2.0 * np.arange(half, dtype=np.float64) / d)
+    ang = np.asarray(positions, dtype=np.float64)[..., None] * inv
+    c, s = np.cos(ang), np.sin(ang)
+    a, b = x[..., :half], x[..., half:]
+    return np.concatenate([a * c - b * s, b * c + a * s], axis=-1)
+
+
+def tree_attention_rope(Q, Kc, Vc, prefix_len, tree_size, tree_mask, positions, theta, status=None, scale=None):
+    """tree_attention with the queries given before their rotary embedding: each node's
+    query heads are rotated at its position (positions [B][T_max] = prefix + depth, as
+    tree_mask_positions writes them), then the dense definition applies.  The cache
+    holds keys after their rotary embedding."""
+    Qr = rope_rotate(Q, np.asarray(positions)[:, :, None], theta)    # [B][T_max][Hq][d]
+    return tree_attention(Qr, Kc, Vc, prefix_len, tree_size, tree_mask, status=status, scale=scale)
