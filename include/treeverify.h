@@ -8,6 +8,7 @@
  *   tree_mask_positions parents          -> packed ancestor mask, positions,
  *                                           retrieve_indices, child/sibling lists
  *   tree_attention      Q, K/V cache, mask -> O (every node over prefix + ancestors)
+ *   (tree_attention_rope the same with the queries' rotary embedding fused in)
  *   tree_accept         target argmax per node -> accepted path, bonus token
  *   (tree_accept_sample the same from target distributions, by rejection sampling)
  *   kv_compact          accepted path    -> K/V rows moved to contiguous slots
@@ -241,6 +242,28 @@ int tree_attention(int dtype, int B, int T_max, int Hq, int Hkv, int d,
                    const int* prefix_len, const int* tree_size, const uint32_t* tree_mask,
                    const int* status, float scale, void* O,
                    void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------- *
+ * tree_attention_rope -- tree_attention with the rotary position embedding of
+ * the queries fused in ([HB] forward_with_mask rotates the tree's queries and
+ * keys at position prefix + depth, siblings sharing a position).
+ *
+ * Q holds the queries BEFORE their rotary embedding; the kernel rotates query
+ * row (node i, head h) at position P_b + depth_i (depth_i = the number of node
+ * i's ancestors in its tree_mask row, i.e. tree_position_ids), in the
+ * rotate-half layout: pair (j, j + d/2) turns by the angle
+ * pos * rope_theta^(-2j/d) (out_j = q_j cos - q_(j+d/2) sin, out_(j+d/2) =
+ * q_(j+d/2) cos + q_j sin), in float32 with the angle reduced to revolutions
+ * with ~1e-7 accuracy, then rounds to bf16 for the products.  The cache holds
+ * keys after their rotary embedding (prefix rows and tree rows alike).
+ * Everything else is tree_attention's.  Requires rope_theta > 1 and
+ * S_cap <= 2^24 (positions exact in float32).
+ * ------------------------------------------------------------------------- */
+int tree_attention_rope(int dtype, int B, int T_max, int Hq, int Hkv, int d,
+                        const void* Q, const void* Kc, const void* Vc, long long S_cap,
+                        const int* prefix_len, const int* tree_size, const uint32_t* tree_mask,
+                        const int* status, float rope_theta, float scale, void* O,
+                        void* workspace, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------- *
  * tree_accept -- [TRT] greedy verification (walk from the root: accept the child

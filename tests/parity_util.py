@@ -65,7 +65,7 @@ def check_attention(o_gpu, o_ref, w, tree_size, status, label=""):
     return float(err), 0.0
 
 
-def run_pipeline_and_compare(w, *, attention="full", samples=64, seed=0, fused=False, paged=None):
+def run_pipeline_and_compare(w, *, attention="full", samples=64, seed=0, fused=False, paged=None, rope_theta=None):
     """Full pass on the GPU, each stage checked against the oracle.
 
     attention: 'full' compares every written row with the dense oracle; 'sampled'
@@ -73,11 +73,13 @@ def run_pipeline_and_compare(w, *, attention="full", samples=64, seed=0, fused=F
     fused: run the step as tree_build_meta, tree_attention, tree_accept_compact
     (the same stages, checked against the same oracle results).
     paged: a workloads.gen.PagedCache of w's cache; attention and compaction then run
-    on that pool and are checked against the oracle's paged functions."""
+    on that pool and are checked against the oracle's paged functions.
+    rope_theta: w.Q holds pre-rotary queries; attention runs as tree_attention_rope and
+    is checked against the oracle's attention of the queries rotated at their positions."""
     import torch
     from tree_attention_verification_amd.step import TreeVerifyStep
 
-    step = TreeVerifyStep(w, paged=paged)
+    step = TreeVerifyStep(w, paged=paged, rope_theta=rope_theta)
     # 1. tree build (with the metadata when fused)
     if fused:
         step.build_meta()
@@ -100,9 +102,10 @@ def run_pipeline_and_compare(w, *, attention="full", samples=64, seed=0, fused=F
     torch.cuda.synchronize()
     o_gpu = step.out_host()
     status = ref_meta["status"]
+    Q_ref = w.Q if rope_theta is None else oa.rope_rotate(w.Q, ref_meta["positions"][:, :, None], rope_theta)
     if attention == "full":
         if paged is None:
-            o_ref = oa.tree_attention(w.Q, w.Kc, w.Vc, w.prefix_len, ref_tree["tree_size"], ref_meta["tree_mask"],
+            o_ref = oa.tree_attention(Q_ref, w.Kc, w.Vc, w.prefix_len, ref_tree["tree_size"], ref_meta["tree_mask"],
                                       status=status)
         else:
             o_ref = oa.tree_attention_paged(w.Q, paged.K_pool, paged.V_pool, paged.block_table,
@@ -117,7 +120,7 @@ def run_pipeline_and_compare(w, *, attention="full", samples=64, seed=0, fused=F
             b = int(rng.integers(0, w.B))
             picks.append((b, int(rng.integers(0, T_eff[b])), int(rng.integers(0, w.Hq))))
         if paged is None:
-            ref_rows = oa.attention_rows(w.Q, w.Kc, w.Vc, w.prefix_len, ref_tree["tree_size"],
+            ref_rows = oa.attention_rows(Q_ref, w.Kc, w.Vc, w.prefix_len, ref_tree["tree_size"],
                                          ref_meta["tree_mask"], picks, status=status)
         else:
             ref_rows = oa.attention_rows_paged(w.Q, paged.K_pool, paged.V_pool, paged.block_table,

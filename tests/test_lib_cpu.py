@@ -141,3 +141,15 @@ def test_accept_sample_host_validation():
     assert L.tree_accept_sample(1, 16, 7, 0, X, X, X, X, X, X, X, X, X, None) == tv.TV_EINVAL      # V = 0
     assert L.tree_accept_sample(1, 16, 7, 100, X, X, X, None, X, X, X, X, X, None) == tv.TV_EINVAL
     assert L.tree_accept_sample(0, 16, 7, 100, X, X, X, X, X, X, X, X, X, None) == tv.TV_EINVAL
+
+
+def test_rope_call_host_validation():
+    L = tv.lib()
+    # tree_attention_rope(dtype, B, T_max, Hq, Hkv, d, Q, K, V, S_cap, prefix, size, mask, status, theta, scale, O,
+    #                     ws, ws_bytes, stream)
+    assert L.tree_attention_rope(0, 1, 64, 8, 4, 128, X, X, X, 4096, X, X, X, X, 0.5, 0.0, X, None, 0,
+                                 None) == tv.TV_EINVAL          # theta <= 1
+    assert L.tree_attention_rope(0, 1, 64, 8, 4, 128, X, X, X, (1 << 24) + 1, X, X, X, X, 1e4, 0.0, X, None, 0,
+                                 None) == tv.TV_EUNSUPPORTED    # positions past 2^24
+    assert L.tree_attention_rope(0, 1, 64, 8, 4, 96, X, X, X, 4096, X, X, X, X, 1e4, 0.0, X, None, 0,
+                                 None) == tv.TV_EUNSUPPORTED

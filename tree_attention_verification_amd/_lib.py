@@ -57,6 +57,7 @@ _SIGS = {
     "tree_build_layer": (I, [I, I, I, I, I, P, I, P, SZ, P, P, P]),
     "tree_build_finish": (I, [I, I, I, I, I, P, I, P, SZ, P, P, P, P, P, I, P, P, P, P, P, P, P, P, P]),
     "tree_accept_sample": (I, [I, I, I, I, P, P, P, P, P, P, P, P, P, P]),
+    "tree_attention_rope": (I, [I, I, I, I, I, I, P, P, P, LL, P, P, P, P, F, F, P, P, SZ, P]),
     "tv_error_string": (ctypes.c_char_p, [I]),
     "tv_status_string": (ctypes.c_char_p, [I]),
 }
@@ -296,3 +297,13 @@ def tree_accept_sample(B, T_max, dcap, V, draft_tokens, parents, tree_size, targ
                                   _dev(accept_path, "accept_path"), _dev(bonus_token, "bonus_token"),
                                   _stream(stream))
     _check("tree_accept_sample", rc)
+
+
+def tree_attention_rope(dtype, B, T_max, Hq, Hkv, d, Q, Kc, Vc, S_cap, prefix_len, tree_size, tree_mask, status,
+                        rope_theta, scale, O, workspace, stream=None):
+    wp, wn = _ws(workspace)
+    rc = lib().tree_attention_rope(dtype, B, T_max, Hq, Hkv, d, _dev(Q, "Q"), _dev(Kc, "Kc"), _dev(Vc, "Vc"), S_cap,
+                                   _dev(prefix_len, "prefix_len"), _dev(tree_size, "tree_size"),
+                                   _dev(tree_mask, "tree_mask"), _dev(status, "status"), float(rope_theta),
+                                   float(scale), _dev(O, "O"), wp, wn, _stream(stream))
+    _check("tree_attention_rope", rc)

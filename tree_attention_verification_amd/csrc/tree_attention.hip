@@ -68,6 +68,16 @@ struct Plan {
   int rel;         // splits relative to each request's own length, longest request first
 };
 
+// Rotary embedding of the queries inside the attention kernel ([HB]
+// forward_with_mask rotates the tree's queries at position prefix + depth):
+// pair (i, i + d/2) turns by pos * f_i revolutions, f_i = theta^(-2i/d) / 2 pi,
+// given as a float pair (f_hi + f_lo) so that pos * f_i keeps ~1e-7 revolutions
+// of accuracy at any position below 2^24.
+struct Rope {
+  float f_hi[64];
+  float f_lo[64];
+};
+
 Plan plan_with(int B, int T_max, int Hq, int Hkv, long long S_cap, int nw, long long min_keys) {
   Plan p{};
   const int rep = Hq / Hkv;
@@ -158,13 +168,13 @@ __device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
 // and lgkmcnt left at their maximum)
 constexpr int vm_wait_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-template <int D, int NW, int NSTAGE, bool PAGED>
+template <int D, int NW, int NSTAGE, bool PAGED, bool ROPE>
 __global__ __launch_bounds__(NW * 64, (NSTAGE == 2 && NW == 4) ? 2 : 1) void k_attn_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Kc, const uint16_t* __restrict__ Vc,
     long long S_cap, const int* __restrict__ prefix_len, const int* __restrict__ tree_size,
     const uint32_t* __restrict__ tree_mask, const int* __restrict__ status, int T_max, int Hq, int Hkv, int W,
     float sl2, uint16_t* __restrict__ O, _Float16* __restrict__ ws_o, float* __restrict__ ws_ml, int n_split,
-    int chunk_keys, int n_rowblk, int n_units, long long m_pad, int B, int rel, Paging pg) {
+    int chunk_keys, int n_rowblk, int n_units, long long m_pad, int B, int rel, Paging pg, Rope rope) {
   constexpr int NT = NW * 64;
   constexpr int KSTEPS = D / 16;     // 16-wide k-steps of QK^T (KSTEPS/2 per half of d)
   constexpr int DB = D / 32;         // 32-wide d blocks of the output
@@ -371,6 +381,33 @@ __global__ __launch_bounds__(NW * 64, (NSTAGE == 2 && NW == 4) ? 2 : 1) void k_a
   // flight while tile 0 is computed.
   __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
   asm volatile("" ::"v"(qf[0]), "v"(qf[KSTEPS / 2]), "v"(qf[KSTEPS - 1]), "v"(mrow));
+  if constexpr (ROPE) {
+    // the queries arrive before their rotary embedding: rotate this lane's half
+    // of its row at the node's position P + depth (depth = ancestors in the mask
+    // row); the other half of the row is in lane ^ 32
+    const float posf = (float)(P + __popcll(mrow) - 1);
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      const u32x4 mine = __builtin_bit_cast(u32x4, qf[kk]);
+      u32x4 other;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) other[c] = (uint32_t)__shfl_xor((int)mine[c], 32, 64);
+      const bf16x8 qo = __builtin_bit_cast(bf16x8, other);
+      bf16x8 out;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int i = 8 * kk + e;  // pair index (the same for both halves)
+        const float fh = rope.f_hi[i], fl = rope.f_lo[i];
+        const float p = posf * fh;
+        const float err = fmaf(posf, fh, -p) + posf * fl;
+        const float rev = (p - rintf(p)) + err;  // the angle in revolutions, |rev| <~ 0.5
+        const float sn = __builtin_amdgcn_sinf(rev), cs = __builtin_amdgcn_cosf(rev);
+        const float a = (float)qf[kk][e], o = (float)qo[e];
+        out[e] = (__bf16)(h == 0 ? fmaf(a, cs, -o * sn) : fmaf(a, cs, o * sn));
+      }
+      qf[kk] = out;
+    }
+  }
 #pragma unroll
   for (int j = 1; j < NSTAGE - 1; ++j)
     if (n_tiles > j) dma_tile(k_begin + j * KT, nkeys - 1, j);
@@ -681,14 +718,14 @@ __global__ __launch_bounds__(256) void k_attn_combine(const _Float16* __restrict
 }
 
 // fp32 path: one wavefront per (node, query head, request).
-template <int D, bool PAGED>
+template <int D, bool PAGED, bool ROPE>
 __global__ __launch_bounds__(64) void k_attn_fp32(const float* __restrict__ Q, const float* __restrict__ Kc,
                                                   const float* __restrict__ Vc, long long S_cap,
                                                   const int* __restrict__ prefix_len,
                                                   const int* __restrict__ tree_size,
                                                   const uint32_t* __restrict__ tree_mask,
                                                   const int* __restrict__ status, int T_max, int Hq, int Hkv, int W,
-                                                  float scale, float* __restrict__ O, Paging pg) {
+                                                  float scale, float* __restrict__ O, Paging pg, Rope rope) {
   const int i = blockIdx.x, hq = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
   int T = tree_size[b];
   const int P = prefix_len[b];
@@ -715,7 +752,20 @@ __global__ __launch_bounds__(64) void k_attn_fp32(const float* __restrict__ Q, c
   const uint32_t* mp = tree_mask + ((long long)b * T_max + i) * W;
   const unsigned long long mrow = (unsigned long long)mp[0] | (W > 1 ? ((unsigned long long)mp[1] << 32) : 0ull);
   __shared__ float s_q[D];
-  for (int d = lane; d < D; d += 64) s_q[d] = qp[d];
+  if constexpr (ROPE) {
+    // the query before its rotary embedding: pair (j, j + D/2) turns at P + depth
+    const float posf = (float)(P + __popcll(mrow) - 1);
+    for (int j = lane; j < D / 2; j += 64) {
+      const float p = posf * rope.f_hi[j];
+      const float rev = (p - rintf(p)) + (fmaf(posf, rope.f_hi[j], -p) + posf * rope.f_lo[j]);
+      const float sn = __builtin_amdgcn_sinf(rev), cs = __builtin_amdgcn_cosf(rev);
+      const float a = qp[j], o = qp[j + D / 2];
+      s_q[j] = fmaf(a, cs, -o * sn);
+      s_q[j + D / 2] = fmaf(o, cs, a * sn);
+    }
+  } else {
+    for (int d = lane; d < D; d += 64) s_q[d] = qp[d];
+  }
   __syncthreads();
   float m = -INFINITY, l = 0.0f, acc[D];
 #pragma unroll
@@ -757,15 +807,15 @@ __global__ __launch_bounds__(64) void k_attn_fp32(const float* __restrict__ Q, c
   }
 }
 
-template <int D, int NW, int NS, bool PAGED>
+template <int D, int NW, int NS, bool PAGED, bool ROPE>
 void launch_bf16(const Plan& p, int B, hipStream_t s, const void* Q, const void* Kc, const void* Vc, long long S_cap,
                  const int* prefix_len, const int* tree_size, const uint32_t* tree_mask, const int* status,
                  int T_max, int Hq, int Hkv, int W, float sl2, void* O, _Float16* ws_o, float* ws_ml,
-                 const Paging& pg) {
-  hipLaunchKernelGGL((k_attn_bf16<D, NW, NS, PAGED>), dim3(p.grid), dim3(NW * 64), 0, s, (const uint16_t*)Q,
+                 const Paging& pg, const Rope& rope) {
+  hipLaunchKernelGGL((k_attn_bf16<D, NW, NS, PAGED, ROPE>), dim3(p.grid), dim3(NW * 64), 0, s, (const uint16_t*)Q,
                      (const uint16_t*)Kc, (const uint16_t*)Vc, S_cap, prefix_len, tree_size, tree_mask, status, T_max,
                      Hq, Hkv, W, sl2, (uint16_t*)O, ws_o, ws_ml, p.n_split, p.chunk_keys, p.n_rowblk, p.n_units,
-                     p.m_pad, B, p.rel, pg);
+                     p.m_pad, B, p.rel, pg, rope);
 }
 
 size_t ws_bytes_for(const Plan& p, int B, int Hkv, int d) {
@@ -778,7 +828,7 @@ size_t ws_bytes_for(const Plan& p, int B, int Hkv, int d) {
 int attention_impl(int dtype, int B, int T_max, int Hq, int Hkv, int d, const void* Q, const void* Kc,
                    const void* Vc, long long S_cap, const int* prefix_len, const int* tree_size,
                    const uint32_t* tree_mask, const int* status, float scale, void* O, void* workspace,
-                   size_t ws_bytes, void* stream, const Paging& pg) {
+                   size_t ws_bytes, void* stream, const Paging& pg, const Rope* rope = nullptr) {
   if (B <= 0 || T_max <= 0 || Hq <= 0 || Hkv <= 0 || S_cap <= 0) return TV_EINVAL;
   if (Hq % Hkv != 0) return TV_EINVAL;
   if (S_cap > (1LL << 30)) return TV_EUNSUPPORTED;
@@ -793,20 +843,23 @@ int attention_impl(int dtype, int B, int T_max, int Hq, int Hkv, int d, const vo
   if (!(scale > 0.0f)) scale = 1.0f / sqrtf((float)d);
   const int W = (T_max + 31) / 32;
   const bool paged = pg.table != nullptr;
+  const Rope rp = rope ? *rope : Rope{};
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (dtype == TV_DTYPE_FP32) {
     dim3 grid(T_max, Hq, B);
     if (B > 65535 || Hq > 65535) return TV_EUNSUPPORTED;
-#define TV_FP32_LAUNCH(DD, PG)                                                                                     \
-  hipLaunchKernelGGL((k_attn_fp32<DD, PG>), grid, dim3(64), 0, s, (const float*)Q, (const float*)Kc,                \
+#define TV_FP32_LAUNCH(DD, PG, RP)                                                                                 \
+  hipLaunchKernelGGL((k_attn_fp32<DD, PG, RP>), grid, dim3(64), 0, s, (const float*)Q, (const float*)Kc,            \
                      (const float*)Vc, S_cap, prefix_len, tree_size, tree_mask, status, T_max, Hq, Hkv, W, scale,    \
-                     (float*)O, pg)
+                     (float*)O, pg, rp)
     if (d == 64) {
-      if (paged) TV_FP32_LAUNCH(64, true);
-      else TV_FP32_LAUNCH(64, false);
+      if (paged) TV_FP32_LAUNCH(64, true, false);
+      else if (rope) TV_FP32_LAUNCH(64, false, true);
+      else TV_FP32_LAUNCH(64, false, false);
     } else {
-      if (paged) TV_FP32_LAUNCH(128, true);
-      else TV_FP32_LAUNCH(128, false);
+      if (paged) TV_FP32_LAUNCH(128, true, false);
+      else if (rope) TV_FP32_LAUNCH(128, false, true);
+      else TV_FP32_LAUNCH(128, false, false);
     }
 #undef TV_FP32_LAUNCH
     TV_CHECK_LAUNCH();
@@ -818,18 +871,20 @@ int attention_impl(int dtype, int B, int T_max, int Hq, int Hkv, int d, const vo
   _Float16* ws_o = reinterpret_cast<_Float16*>(workspace);
   float* ws_ml = need ? reinterpret_cast<float*>(ws_o + (size_t)B * Hkv * p.n_split * p.m_pad * d) : nullptr;
   const float sl2 = scale * kLog2e;
-#define TV_ATTN_LAUNCH(DD, NWW, NSS, PG)                                                                         \
-  launch_bf16<DD, NWW, NSS, PG>(p, B, s, Q, Kc, Vc, S_cap, prefix_len, tree_size, tree_mask, status, T_max, Hq,  \
-                                Hkv, W, sl2, O, ws_o, ws_ml, pg)
-#define TV_ATTN_NW(DD, PG)           \
-  if (p.nw == 4) TV_ATTN_LAUNCH(DD, 4, 2, PG); \
-  else TV_ATTN_LAUNCH(DD, 8, 2, PG)
+#define TV_ATTN_LAUNCH(DD, NWW, NSS, PG, RP)                                                                     \
+  launch_bf16<DD, NWW, NSS, PG, RP>(p, B, s, Q, Kc, Vc, S_cap, prefix_len, tree_size, tree_mask, status, T_max, Hq, \
+                                    Hkv, W, sl2, O, ws_o, ws_ml, pg, rp)
+#define TV_ATTN_NW(DD, PG, RP)           \
+  if (p.nw == 4) TV_ATTN_LAUNCH(DD, 4, 2, PG, RP); \
+  else TV_ATTN_LAUNCH(DD, 8, 2, PG, RP)
   if (d == 128) {
-    if (paged) TV_ATTN_NW(128, true);
-    else TV_ATTN_NW(128, false);
+    if (paged) TV_ATTN_NW(128, true, false);
+    else if (rope) TV_ATTN_NW(128, false, true);
+    else TV_ATTN_NW(128, false, false);
   } else {
-    if (paged) TV_ATTN_NW(64, true);
-    else TV_ATTN_NW(64, false);
+    if (paged) TV_ATTN_NW(64, true, false);
+    else if (rope) TV_ATTN_NW(64, false, true);
+    else TV_ATTN_NW(64, false, false);
   }
 #undef TV_ATTN_NW
 #undef TV_ATTN_LAUNCH
@@ -864,6 +919,25 @@ extern "C" int tree_attention(int dtype, int B, int T_max, int Hq, int Hkv, int 
                               size_t ws_bytes, void* stream) {
   return tv::attention_impl(dtype, B, T_max, Hq, Hkv, d, Q, Kc, Vc, S_cap, prefix_len, tree_size, tree_mask, status,
                             scale, O, workspace, ws_bytes, stream, tv::Paging{});
+}
+
+extern "C" int tree_attention_rope(int dtype, int B, int T_max, int Hq, int Hkv, int d, const void* Q,
+                                   const void* Kc, const void* Vc, long long S_cap, const int* prefix_len,
+                                   const int* tree_size, const uint32_t* tree_mask, const int* status,
+                                   float rope_theta, float scale, void* O, void* workspace, size_t ws_bytes,
+                                   void* stream) {
+  if (!(rope_theta > 1.0f) || !(rope_theta < 3.0e38f)) return TV_EINVAL;
+  if (S_cap > (1LL << 24)) return TV_EUNSUPPORTED;  // positions stay exact in float32
+  if (d != 64 && d != 128) return TV_EUNSUPPORTED;
+  tv::Rope rope{};
+  const double two_pi = 6.283185307179586476925286766559;
+  for (int i = 0; i < d / 2; ++i) {
+    const double f = pow((double)rope_theta, -2.0 * i / d) / two_pi;
+    rope.f_hi[i] = (float)f;
+    rope.f_lo[i] = (float)(f - (double)rope.f_hi[i]);
+  }
+  return tv::attention_impl(dtype, B, T_max, Hq, Hkv, d, Q, Kc, Vc, S_cap, prefix_len, tree_size, tree_mask, status,
+                            scale, O, workspace, ws_bytes, stream, tv::Paging{}, &rope);
 }
 
 extern "C" int tree_attention_paged(int dtype, int B, int T_max, int Hq, int Hkv, int d, const void* Q,

@@ -41,9 +41,10 @@ def _copies(t, n):
 
 
 class TreeVerifyStep:
-    def __init__(self, w, device: str = "cuda", n_copies: int = 1, paged=None):
+    def __init__(self, w, device: str = "cuda", n_copies: int = 1, paged=None, rope_theta=None):
         self.w = w
         self.paged = paged
+        self.rope_theta = rope_theta   # set: Q holds pre-rotary queries (tree_attention_rope)
         self.device = device
         B, T_max, dcap = w.B, w.T_max, w.dcap
         self.B, self.T_max, self.dcap = B, T_max, dcap
@@ -144,6 +145,11 @@ class TreeVerifyStep:
                                     self.Kc[c], self.Vc[c], pg.n_blocks, pg.tokens_per_block, self.block_table,
                                     pg.max_blocks, self.prefix_len, self.tree_size, self.tree_mask, self.status, 0.0,
                                     self.O, self.ws_attn, stream)
+            return
+        if self.rope_theta is not None:
+            tv.tree_attention_rope(self.dtype_code, self.B, self.T_max, w.Hq, w.Hkv, w.d, self.Q_copies[c],
+                                   self.Kc[c], self.Vc[c], w.S_cap, self.prefix_len, self.tree_size, self.tree_mask,
+                                   self.status, self.rope_theta, 0.0, self.O, self.ws_attn, stream)
             return
         tv.tree_attention(self.dtype_code, self.B, self.T_max, w.Hq, w.Hkv, w.d, self.Q_copies[c], self.Kc[c],
                           self.Vc[c],
