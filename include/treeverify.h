@@ -50,7 +50,8 @@
  *     chain / tree_valid fallback of [TRT] ("per-request trees stored by slot").
  *   - Tree layout: node 0 is the root; tree_size counts the root; parents[0] =
  *     -1 and 0 <= parents[i] < i.  T_max is the padded node dimension of every
- *     per-node array (this version supports T_max <= 64).  Padding entries are
+ *     per-node array (T_max <= 256; trees of up to 64 nodes take one wavefront per
+ *     request, larger ones a 256-thread workgroup).  Padding entries are
  *     -1 for tokens / parents / node ids, 0 for masks and positions, -inf for
  *     scores.  dcap is the deepest node depth the caller provisions for
  *     (retrieve rows and accepted paths have dcap + 1 columns).
@@ -182,7 +183,7 @@ int tree_build_finish(int B, int V, int K, int D, int total_tokens, const int* r
  *        id, -1 where none;
  *      status_out [B]: status_in if non-zero, else TV_ST_SIZE, TV_ST_PARENTS,
  *        TV_ST_DEPTH (checked in that order) or TV_ST_OK.
- * Requires 1 <= T_max <= 64, 0 <= dcap < T_max.
+ * Requires 1 <= T_max <= 256, 0 <= dcap < T_max.
  * ------------------------------------------------------------------------- */
 int tree_mask_positions(int B, int T_max, int dcap, const int* parents,
                         const int* tree_size, const int* prefix_len,
@@ -229,7 +230,7 @@ int tree_build_meta(int mode, int B, int V, int K, int D, int total_tokens,
  * whose prefix does not fit the cache (prefix_len < 0 or prefix_len + T_b >
  * S_cap) reads no K/V and gets O rows 0..T_b-1 set to zero (status is read,
  * never written, by this call).
- * Requires d in {64, 128}, Hq % Hkv == 0 (any group size), T_max <= 64,
+ * Requires d in {64, 128}, Hq % Hkv == 0 (any group size), T_max <= 256,
  * S_cap <= 2^30.  Every buffer must be allocated to its full layout size: rows
  * past a request's keys or nodes may be read, but their contents (any bits,
  * NaN included) never reach the output.
@@ -309,7 +310,7 @@ int tree_accept(int B, int T_max, int dcap, const int* draft_tokens, const int* 
  *      in [0, 1): entry c >= 1 is the draw for child c's test, entry 0 the draw
  *      for the correction token.
  * Out: accept_len, accept_path, bonus_token as tree_accept.
- * Requires 1 <= T_max <= 64, 0 <= dcap < T_max, V >= 1.
+ * Requires 1 <= T_max <= 256, 0 <= dcap < T_max, 1 <= V <= 262144.
  * ------------------------------------------------------------------------- */
 int tree_accept_sample(int B, int T_max, int dcap, int V, const int* draft_tokens, const int* parents,
                        const int* tree_size, const float* target_probs, const float* uniforms,

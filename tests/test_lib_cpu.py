@@ -50,7 +50,7 @@ def test_other_calls_host_validation():
     L = tv.lib()
     # tree_mask_positions: dcap must be < T_max, T_max <= 64
     assert L.tree_mask_positions(1, 64, 64, X, X, X, X, X, X, X, X, None, None, None, X, None) == tv.TV_EINVAL
-    assert L.tree_mask_positions(1, 65, 7, X, X, X, X, X, X, X, X, None, None, None, X, None) == tv.TV_EUNSUPPORTED
+    assert L.tree_mask_positions(1, 257, 7, X, X, X, X, X, X, X, X, None, None, None, X, None) == tv.TV_EUNSUPPORTED
     # tree_attention: Hq % Hkv, head dim, dtype, misaligned pointers, workspace
     args = dict(Q=X, K=X, V=X)
     assert L.tree_attention(0, 1, 64, 6, 4, 128, X, X, X, 4096, X, X, X, X, 0.0, X, None, 0, None) == tv.TV_EINVAL
@@ -125,7 +125,7 @@ def test_layer_calls_host_validation():
                                *tail) == tv.TV_EINVAL   # total_tokens > C
     assert L.tree_build_finish(2, 32000, 10, 6, 64, X, 64, X, need, X, X, X, None, X, 7, None,
                                *tail) == tv.TV_EINVAL   # total_tokens + 1 > T_max
-    assert L.tree_build_finish(2, 32000, 10, 6, 60, X, 65, X, need, X, X, X, None, X, 7, None,
+    assert L.tree_build_finish(2, 32000, 10, 6, 60, X, 257, X, need, X, X, X, None, X, 7, None,
                                *tail) == tv.TV_EUNSUPPORTED
     assert L.tree_build_finish(2, 32000, 10, 6, 60, X, 64, X, need, X, X, X, None, X, 64, X,
                                *tail) == tv.TV_EINVAL   # dcap >= T_max with metadata
@@ -137,7 +137,7 @@ def test_accept_sample_host_validation():
     L = tv.lib()
     # tree_accept_sample(B, T_max, dcap, V, tokens, parents, size, probs, uniforms, status, len, path, bonus, stream)
     assert L.tree_accept_sample(1, 16, 16, 100, X, X, X, X, X, X, X, X, X, None) == tv.TV_EINVAL   # dcap >= T_max
-    assert L.tree_accept_sample(1, 65, 7, 100, X, X, X, X, X, X, X, X, X, None) == tv.TV_EUNSUPPORTED
+    assert L.tree_accept_sample(1, 257, 7, 100, X, X, X, X, X, X, X, X, X, None) == tv.TV_EUNSUPPORTED
     assert L.tree_accept_sample(1, 16, 7, 0, X, X, X, X, X, X, X, X, X, None) == tv.TV_EINVAL      # V = 0
     assert L.tree_accept_sample(1, 16, 7, 100, X, X, X, None, X, X, X, X, X, None) == tv.TV_EINVAL
     assert L.tree_accept_sample(0, 16, 7, 100, X, X, X, X, X, X, X, X, X, None) == tv.TV_EINVAL

@@ -55,6 +55,71 @@ __device__ __forceinline__ Walk accept_walk(int b, int c, int T_max, int dcap, c
   return {len, mine, __builtin_amdgcn_readlane(pred_l, node)};
 }
 
+// The same walk for trees of up to 256 nodes, by a 256-thread workgroup (thread
+// c = node c; every thread must call it).  Each step broadcasts the prediction
+// at the current node through LDS and takes the lowest matching child with an
+// LDS atomic minimum.  Path entries 0..len go to s_path (at least dcap + 1).
+struct WalkWide {
+  int len, bonus;
+};
+
+__device__ __forceinline__ WalkWide accept_walk_wide(int b, int c, int T_max, int dcap,
+                                                     const int* __restrict__ draft_tokens,
+                                                     const int* __restrict__ parents,
+                                                     const int* __restrict__ tree_size,
+                                                     const int* __restrict__ target_predict,
+                                                     const int* __restrict__ status, int* s_path) {
+  __shared__ int s_bc, s_next;
+  const long long ob = (long long)b * T_max;
+  int T = tree_size[b];
+  const int st = status[b];
+  const int tok_l = c < T_max ? draft_tokens[ob + c] : -1;
+  const int par_l = c < T_max ? parents[ob + c] : -2;
+  const int pred_l = c < T_max ? target_predict[ob + c] : -1;
+  if (st != TV_ST_OK || T < 1 || T > T_max) T = 1;
+  const int tok = c < T ? tok_l : -1;
+  const int par = (c > 0 && c < T) ? par_l : -2;
+  if (c == 0) s_path[0] = 0;
+  int node = 0, len = 0;
+  for (int step = 0; step < dcap; ++step) {
+    if (c == node) s_bc = pred_l;
+    if (c == 0) s_next = 0x7FFFFFFF;
+    __syncthreads();
+    const int pred = s_bc;
+    if (par == node && tok == pred) atomicMin(&s_next, c);
+    __syncthreads();
+    const int nx = s_next;
+    __syncthreads();  // every read before the next step's writes
+    if (nx == 0x7FFFFFFF) break;
+    node = nx;
+    ++len;
+    if (c == 0) s_path[len] = node;
+  }
+  if (c == node) s_bc = pred_l;
+  __syncthreads();
+  const int bonus = s_bc;
+  __syncthreads();
+  return {len, bonus};
+}
+
+__global__ __launch_bounds__(256) void k_tree_accept_wide(int T_max, int dcap, const int* __restrict__ draft_tokens,
+                                                          const int* __restrict__ parents,
+                                                          const int* __restrict__ tree_size,
+                                                          const int* __restrict__ target_predict,
+                                                          const int* __restrict__ status,
+                                                          int* __restrict__ accept_len, int* __restrict__ accept_path,
+                                                          int* __restrict__ bonus_token) {
+  __shared__ int s_path[256];
+  const int b = blockIdx.x, c = threadIdx.x;
+  const WalkWide w = accept_walk_wide(b, c, T_max, dcap, draft_tokens, parents, tree_size, target_predict, status,
+                                      s_path);
+  if (c <= dcap) accept_path[(long long)b * (dcap + 1) + c] = c <= w.len ? s_path[c] : -1;
+  if (c == 0) {
+    accept_len[b] = w.len;
+    bonus_token[b] = w.bonus;
+  }
+}
+
 __global__ __launch_bounds__(64) void k_tree_accept(int T_max, int dcap, const int* __restrict__ draft_tokens,
                                                     const int* __restrict__ parents,
                                                     const int* __restrict__ tree_size,
@@ -117,17 +182,24 @@ __global__ __launch_bounds__(kSampleThreads) void k_tree_accept_sample(
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   constexpr int NWV = kSampleThreads / 64;
   __shared__ double s_red[NWV];
-  __shared__ int s_rem[64];  // tokens rejected at the current node
-  __shared__ int s_path[64];
+  __shared__ int s_rem[kTMaxLimit];  // tokens rejected at the current node
+  __shared__ int s_path[kTMaxLimit];
   __shared__ int s_next, s_nrem, s_pick;
   const long long ob = (long long)b * T_max;
   int T = tree_size[b];
   const bool ok = status[b] == TV_ST_OK && T >= 1 && T <= T_max;
   if (!ok) T = 1;
-  // per-node data in the first wavefront's lanes (lane c = node c)
-  const int tok_l = lane < T ? draft_tokens[ob + lane] : -1;
-  const int par_l = (lane > 0 && lane < T) ? parents[ob + lane] : -2;
-  const float u_l = lane < T_max ? uniforms[ob + lane] : 0.0f;
+  // per-node data in the first wavefront's lanes: node c = lane + 64 q, q < 4
+  constexpr int NQ = kTMaxLimit / 64;
+  int tok_q[NQ], par_q[NQ];
+  float u_q[NQ];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int c = lane + 64 * q;
+    tok_q[q] = c < T ? draft_tokens[ob + c] : -1;
+    par_q[q] = (c > 0 && c < T) ? parents[ob + c] : -2;
+    u_q[q] = c < T_max ? uniforms[ob + c] : 0.0f;
+  }
   auto block_sum = [&](double v) -> double {
     v = wave_sum_f64(v);
     if (lane == 0) s_red[wave] = v;
@@ -176,34 +248,50 @@ __global__ __launch_bounds__(kSampleThreads) void k_tree_accept_sample(
     const float* row = target_probs + (ob + node) * (long long)V;
     // p(x) of every child of this node, fetched together (first wavefront); a
     // token outside the vocabulary has no mass
-    float pc = 0.0f;
-    const bool kid = par_l == node;
-    if (wave == 0 && kid && tok_l >= 0 && tok_l < V) pc = row[tok_l];
+    float pc_q[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      pc_q[q] = 0.0f;
+      if (wave == 0 && par_q[q] == node && tok_q[q] >= 0 && tok_q[q] < V) pc_q[q] = row[tok_q[q]];
+    }
     const double Z = row_sum(row);
     if (wave == 0) {
       // children in ascending id (the current node and every decision are
-      // wave-uniform); lane q keeps the q-th token rejected here
-      unsigned long long kids = __ballot(kid);
+      // wave-uniform); rejected token r sits in lane r % 64, slot r / 64
       double R = 0.0;
-      int next = -1, nr = 0, rem_l = -1;
-      while (kids) {
-        const int c = __ffsll((long long)kids) - 1;
-        kids &= kids - 1;
-        const int x = __builtin_amdgcn_readlane(tok_l, c);
-        const bool seen = __ballot(rem_l == x) != 0ull;
-        const double px = seen ? 0.0 : (double)__int_as_float(__builtin_amdgcn_readlane(__float_as_int(pc), c));
-        const double uc = (double)__int_as_float(__builtin_amdgcn_readlane(__float_as_int(u_l), c));
-        if (uc * (Z - R) < px) {
-          next = c;
-          break;
-        }
-        if (!seen) {
-          R += px;
-          if (lane == nr) rem_l = x;
-          ++nr;
+      int next = -1, nr = 0, rem_q[NQ];
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) rem_q[q] = -1;
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        unsigned long long kids = next < 0 ? __ballot(par_q[q] == node) : 0ull;
+        while (kids) {
+          const int c = __ffsll((long long)kids) - 1;
+          kids &= kids - 1;
+          const int x = __builtin_amdgcn_readlane(tok_q[q], c);
+          bool any = false;
+#pragma unroll
+          for (int r = 0; r < NQ; ++r) any |= rem_q[r] == x;
+          const bool seen = __ballot(any) != 0ull;
+          const double px =
+              seen ? 0.0 : (double)__int_as_float(__builtin_amdgcn_readlane(__float_as_int(pc_q[q]), c));
+          const double uc = (double)__int_as_float(__builtin_amdgcn_readlane(__float_as_int(u_q[q]), c));
+          if (uc * (Z - R) < px) {
+            next = 64 * q + c;
+            break;
+          }
+          if (!seen) {
+            R += px;
+#pragma unroll
+            for (int r = 0; r < NQ; ++r)
+              if (lane == (nr & 63) && (nr >> 6) == r) rem_q[r] = x;
+            ++nr;
+          }
         }
       }
-      if (lane < nr) s_rem[lane] = rem_l;
+#pragma unroll
+      for (int r = 0; r < NQ; ++r)
+        if (lane + 64 * r < nr) s_rem[lane + 64 * r] = rem_q[r];
       if (lane == 0) {
         s_next = next;
         s_nrem = nr;
@@ -250,7 +338,7 @@ __global__ __launch_bounds__(kSampleThreads) void k_tree_accept_sample(
   const double total = block_sum(acc);
   if (tid == 0) s_pick = -1;
   __syncthreads();
-  const double target = (double)__int_as_float(__builtin_amdgcn_readlane(__float_as_int(u_l), 0)) * total;
+  const double target = (double)__int_as_float(__builtin_amdgcn_readlane(__float_as_int(u_q[0]), 0)) * total;
   __shared__ double s_last[NWV];
   __shared__ double s_carry;
   if (total > 0.0) {
@@ -422,12 +510,25 @@ __global__ __launch_bounds__(kCompactThreads) void k_accept_compact(
   __shared__ int s_path[64];
   __shared__ int s_len;
   const int P = prefix_len[b];
-  if (tid < 64) {
-    const Walk w = accept_walk(b, tid, T_max, dcap, draft_tokens, parents, tree_size, target_predict, status);
-    if (tid <= dcap) s_path[tid] = w.mine;
+  if (T_max <= 64) {
+    if (tid < 64) {
+      const Walk w = accept_walk(b, tid, T_max, dcap, draft_tokens, parents, tree_size, target_predict, status);
+      if (tid <= dcap) s_path[tid] = w.mine;
+      if (tid == 0) s_len = w.len;
+      if (g == 0 && blockIdx.y == 0) {
+        if (tid <= dcap) accept_path[(long long)b * (dcap + 1) + tid] = w.mine;
+        if (tid == 0) {
+          accept_len[b] = w.len;
+          bonus_token[b] = w.bonus;
+        }
+      }
+    }
+  } else {  // up to 256 nodes (dcap < 64 here: the compaction stages at most 63 rows)
+    const WalkWide w = accept_walk_wide(b, tid, T_max, dcap, draft_tokens, parents, tree_size, target_predict,
+                                        status, s_path);
     if (tid == 0) s_len = w.len;
     if (g == 0 && blockIdx.y == 0) {
-      if (tid <= dcap) accept_path[(long long)b * (dcap + 1) + tid] = w.mine;
+      if (tid <= dcap) accept_path[(long long)b * (dcap + 1) + tid] = tid <= w.len ? s_path[tid] : -1;
       if (tid == 0) {
         accept_len[b] = w.len;
         bonus_token[b] = w.bonus;
@@ -450,8 +551,14 @@ extern "C" int tree_accept(int B, int T_max, int dcap, const int* draft_tokens, 
   if (!draft_tokens || !parents || !tree_size || !target_predict || !status || !accept_len || !accept_path ||
       !bonus_token)
     return TV_EINVAL;
-  hipLaunchKernelGGL(tv::k_tree_accept, dim3(B), dim3(64), 0, reinterpret_cast<hipStream_t>(stream), T_max, dcap,
-                     draft_tokens, parents, tree_size, target_predict, status, accept_len, accept_path, bonus_token);
+  if (T_max <= 64)
+    hipLaunchKernelGGL(tv::k_tree_accept, dim3(B), dim3(64), 0, reinterpret_cast<hipStream_t>(stream), T_max, dcap,
+                       draft_tokens, parents, tree_size, target_predict, status, accept_len, accept_path,
+                       bonus_token);
+  else
+    hipLaunchKernelGGL(tv::k_tree_accept_wide, dim3(B), dim3(256), 0, reinterpret_cast<hipStream_t>(stream), T_max,
+                       dcap, draft_tokens, parents, tree_size, target_predict, status, accept_len, accept_path,
+                       bonus_token);
   TV_CHECK_LAUNCH();
   return TV_OK;
 }

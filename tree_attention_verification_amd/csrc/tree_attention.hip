@@ -307,8 +307,13 @@ __global__ __launch_bounds__(NW * 64, (NSTAGE == 2 && NW == 4) ? 2 : 1) void k_a
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) qf[kk] = as_bf16x8(qp[kk]);
   }
+  // the packed mask row: nodes 0..63 in mrow, all W words (W <= 8, up to 256
+  // nodes) in mw; words past W read as zero
   const uint32_t* mp = tree_mask + ((long long)b * T_max + i_row) * W;
-  unsigned long long mrow = (unsigned long long)mp[0] | (W > 1 ? ((unsigned long long)mp[1] << 32) : 0ull);
+  uint32_t mw[8];
+#pragma unroll
+  for (int w = 0; w < 8; ++w) mw[w] = w < W ? mp[w] : 0u;
+  unsigned long long mrow = (unsigned long long)mw[0] | ((unsigned long long)mw[1] << 32);
 
   int T = rel ? rel_T : tree_size[b];
   const int P = rel ? rel_P : prefix_len[b];
@@ -372,6 +377,8 @@ __global__ __launch_bounds__(NW * 64, (NSTAGE == 2 && NW == 4) ? 2 : 1) void k_a
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) qf[kk] = as_bf16x8(u32x4{0, 0, 0, 0});
     mrow = 0ull;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) mw[w] = 0u;
   }
   // Q and the mask row are needed now (the empty statement below reads them), so
   // the compiler waits for its loads here; that wait counts every older vector
@@ -385,7 +392,10 @@ __global__ __launch_bounds__(NW * 64, (NSTAGE == 2 && NW == 4) ? 2 : 1) void k_a
     // the queries arrive before their rotary embedding: rotate this lane's half
     // of its row at the node's position P + depth (depth = ancestors in the mask
     // row); the other half of the row is in lane ^ 32
-    const float posf = (float)(P + __popcll(mrow) - 1);
+    int anc = 0;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) anc += __popc(mw[w]);
+    const float posf = (float)(P + anc - 1);
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) {
       const u32x4 mine = __builtin_bit_cast(u32x4, qf[kk]);
@@ -469,13 +479,26 @@ __global__ __launch_bounds__(NW * 64, (NSTAGE == 2 && NW == 4) ? 2 : 1) void k_a
     }
   };
   // tree mask of the tile starting at key kt0 (only tiles that reach past the
-  // prefix), branch-free: the lane's mask row is shifted once so that bit e
-  // stands for key kt0 + e
+  // prefix): the 64-bit window of the lane's mask row in which bit e stands for
+  // key kt0 + e (prefix keys set, nodes past the row clear)
+  auto word_at = [&](int k) -> uint32_t {  // mask word k (wave-uniform k; 0 past the row)
+    uint32_t v = 0u;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) v = k == w ? mw[w] : v;
+    return v;
+  };
   auto mask = [&](int kt0, f32x16 (&s)[2]) __attribute__((always_inline)) {
     if (kt0 + KT > P) {
       const int sh = kt0 - P;  // key kt0+e is tree node sh+e
-      const unsigned long long mt =
-          sh >= 64 ? 0ull : (sh >= 0 ? (mrow >> sh) : (sh <= -64 ? ~0ull : ((mrow << -sh) | ((1ull << -sh) - 1ull))));
+      unsigned long long mt;
+      if (sh < 0) {
+        mt = sh <= -64 ? ~0ull : ((mrow << -sh) | ((1ull << -sh) - 1ull));
+      } else {
+        const int q = sh >> 5, r = sh & 31;
+        const unsigned long long lo = (unsigned long long)word_at(q) | ((unsigned long long)word_at(q + 1) << 32);
+        const unsigned long long hi = word_at(q + 2);
+        mt = r ? ((lo >> r) | (hi << (64 - r))) : lo;
+      }
       const int lim = nkeys - kt0;  // keys of this tile that exist (1..64)
       const unsigned long long mv = lim >= 64 ? mt : (mt & ((1ull << lim) - 1ull));
       const unsigned long long mh = mv >> (4 * h);
@@ -750,11 +773,12 @@ __global__ __launch_bounds__(64) void k_attn_fp32(const float* __restrict__ Q, c
     }
   };
   const uint32_t* mp = tree_mask + ((long long)b * T_max + i) * W;
-  const unsigned long long mrow = (unsigned long long)mp[0] | (W > 1 ? ((unsigned long long)mp[1] << 32) : 0ull);
   __shared__ float s_q[D];
   if constexpr (ROPE) {
     // the query before its rotary embedding: pair (j, j + D/2) turns at P + depth
-    const float posf = (float)(P + __popcll(mrow) - 1);
+    int anc = 0;
+    for (int w = 0; w < W; ++w) anc += __popc(mp[w]);
+    const float posf = (float)(P + anc - 1);
     for (int j = lane; j < D / 2; j += 64) {
       const float p = posf * rope.f_hi[j];
       const float rev = (p - rintf(p)) + (fmaf(posf, rope.f_hi[j], -p) + posf * rope.f_lo[j]);
@@ -771,7 +795,7 @@ __global__ __launch_bounds__(64) void k_attn_fp32(const float* __restrict__ Q, c
 #pragma unroll
   for (int d = 0; d < D; ++d) acc[d] = 0.0f;
   for (int key = lane; key < nkeys; key += 64) {
-    if (!(key < P || ((mrow >> (key - P)) & 1ull))) continue;
+    if (!(key < P || ((mp[(key - P) >> 5] >> ((key - P) & 31)) & 1u))) continue;
     const long long ro = row(key);
     const float* kr = Kc + ro;
     float sc = 0.0f;

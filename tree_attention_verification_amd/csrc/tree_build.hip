@@ -731,12 +731,21 @@ __global__ __launch_bounds__(kSelectThreads) void k_tree_select_dynamic(
     if (tid == 0) status[b] = ok ? TV_ST_OK : TV_ST_LOGPROB;
   } else {
     __syncthreads();
-    if (tid < 64) {
+    if (T_max <= 64) {
+      if (tid < 64) {
+        int st = ok ? TV_ST_OK : TV_ST_LOGPROB, Tm = T;
+        const int P = mo.prefix_len[b];
+        const int p = check_tree(tid, T_max, st, Tm, (tid > 0 && tid < T) ? s_pn[tid] : -1);
+        meta_body(b, tid, T_max, mo.dcap, mo.W, Tm, st, p, P, mo.tree_mask, mo.tree_position_ids, mo.positions,
+                  mo.retrieve_indices, mo.leaf_count, mo.first_child, mo.next_sibling, status);
+      }
+    } else {  // up to 256 nodes: every thread of the workgroup is one node
+      __shared__ WideShared sh_wide;
       int st = ok ? TV_ST_OK : TV_ST_LOGPROB, Tm = T;
       const int P = mo.prefix_len[b];
-      const int p = check_tree(tid, T_max, st, Tm, (tid > 0 && tid < T) ? s_pn[tid] : -1);
-      meta_body(b, tid, T_max, mo.dcap, mo.W, Tm, st, p, P, mo.tree_mask, mo.tree_position_ids, mo.positions,
-                mo.retrieve_indices, mo.leaf_count, mo.first_child, mo.next_sibling, status);
+      const int p = check_tree_wide(tid, T_max, st, Tm, (tid > 0 && tid < T) ? s_pn[tid] : -1, sh_wide);
+      meta_body_wide(b, tid, T_max, mo.dcap, mo.W, Tm, st, p, P, mo.tree_mask, mo.tree_position_ids, mo.positions,
+                     mo.retrieve_indices, mo.leaf_count, mo.first_child, mo.next_sibling, status, sh_wide);
     }
   }
 }
@@ -792,12 +801,21 @@ __global__ __launch_bounds__(kSelectThreads) void k_tree_select_static(
   if constexpr (!META) {
     if (tid == 0) status[b] = ok ? TV_ST_OK : TV_ST_LOGPROB;
   } else {
-    if (tid < 64) {  // t_par was published by the barrier after the levels
+    if (T_max <= 64) {
+      if (tid < 64) {  // t_par was published by the barrier after the levels
+        int st = ok ? TV_ST_OK : TV_ST_LOGPROB, Tm = T;
+        const int P = mo.prefix_len[b];
+        const int p = check_tree(tid, T_max, st, Tm, (tid > 0 && tid < T) ? t_par[tid] : -1);
+        meta_body(b, tid, T_max, mo.dcap, mo.W, Tm, st, p, P, mo.tree_mask, mo.tree_position_ids, mo.positions,
+                  mo.retrieve_indices, mo.leaf_count, mo.first_child, mo.next_sibling, status);
+      }
+    } else {  // up to 256 nodes: every thread of the workgroup is one node
+      __shared__ WideShared sh_wide;
       int st = ok ? TV_ST_OK : TV_ST_LOGPROB, Tm = T;
       const int P = mo.prefix_len[b];
-      const int p = check_tree(tid, T_max, st, Tm, (tid > 0 && tid < T) ? t_par[tid] : -1);
-      meta_body(b, tid, T_max, mo.dcap, mo.W, Tm, st, p, P, mo.tree_mask, mo.tree_position_ids, mo.positions,
-                mo.retrieve_indices, mo.leaf_count, mo.first_child, mo.next_sibling, status);
+      const int p = check_tree_wide(tid, T_max, st, Tm, (tid > 0 && tid < T) ? t_par[tid] : -1, sh_wide);
+      meta_body_wide(b, tid, T_max, mo.dcap, mo.W, Tm, st, p, P, mo.tree_mask, mo.tree_position_ids, mo.positions,
+                     mo.retrieve_indices, mo.leaf_count, mo.first_child, mo.next_sibling, status, sh_wide);
     }
   }
 }

@@ -8,7 +8,8 @@
 // depths (tree_spec.py), and the EAGLE v2 walkthrough's retrieve_indices /
 // tree_position_ids (section 3, third step).
 //
-// One wavefront per request, lane i = node i (T_max <= 64).  The ancestor set of
+// One wavefront per request, lane i = node i (T_max <= 64; larger trees, up to
+// 256 nodes, take the 256-thread workgroup version in tree_meta_body.h).  The ancestor set of
 // every node is built at once by pointer jumping in registers: after round r a
 // lane's mask holds its ancestors up to distance 2^r - 1 and its jump pointer
 // points 2^r levels up, so six rounds cover any tree of <= 64 nodes.  The mask
@@ -42,6 +43,24 @@ __global__ __launch_bounds__(64) void k_tree_mask_positions(int T_max, int dcap,
             leaf_count, first_child, next_sibling, status_out);
 }
 
+// Trees of more than 64 nodes: one 256-thread workgroup per request.
+__global__ __launch_bounds__(kWideNodes) void k_tree_mask_positions_wide(
+    int T_max, int dcap, int W, const int* __restrict__ parents, const int* __restrict__ tree_size,
+    const int* __restrict__ prefix_len, uint32_t* __restrict__ tree_mask, int* __restrict__ tree_position_ids,
+    int* __restrict__ positions, int* __restrict__ retrieve_indices, int* __restrict__ leaf_count,
+    int* __restrict__ first_child, int* __restrict__ next_sibling, const int* status_in, int* status_out) {
+  __shared__ WideShared sh;
+  const int b = blockIdx.x, i = threadIdx.x;
+  const long long ob = (long long)b * T_max;
+  int st = status_in ? status_in[b] : TV_ST_OK;
+  int T = tree_size[b];
+  const int P = prefix_len[b];
+  const int p_l = i < T_max ? parents[ob + i] : -1;
+  const int p = check_tree_wide(i, T_max, st, T, p_l, sh);
+  meta_body_wide(b, i, T_max, dcap, W, T, st, p, P, tree_mask, tree_position_ids, positions, retrieve_indices,
+                 leaf_count, first_child, next_sibling, status_out, sh);
+}
+
 }  // namespace
 }  // namespace tv
 
@@ -56,9 +75,15 @@ extern "C" int tree_mask_positions(int B, int T_max, int dcap, const int* parent
     return TV_EINVAL;
   if (B > 2147483647 / 64) return TV_EINVAL;
   const int W = (T_max + 31) / 32;
-  hipLaunchKernelGGL(tv::k_tree_mask_positions, dim3(B), dim3(64), 0, reinterpret_cast<hipStream_t>(stream), T_max,
-                     dcap, W, parents, tree_size, prefix_len, tree_mask, tree_position_ids, positions,
-                     retrieve_indices, leaf_count, first_child, next_sibling, status_in, status_out);
+  if (T_max <= 64)
+    hipLaunchKernelGGL(tv::k_tree_mask_positions, dim3(B), dim3(64), 0, reinterpret_cast<hipStream_t>(stream),
+                       T_max, dcap, W, parents, tree_size, prefix_len, tree_mask, tree_position_ids, positions,
+                       retrieve_indices, leaf_count, first_child, next_sibling, status_in, status_out);
+  else
+    hipLaunchKernelGGL(tv::k_tree_mask_positions_wide, dim3(B), dim3(tv::kWideNodes), 0,
+                       reinterpret_cast<hipStream_t>(stream), T_max, dcap, W, parents, tree_size, prefix_len,
+                       tree_mask, tree_position_ids, positions, retrieve_indices, leaf_count, first_child,
+                       next_sibling, status_in, status_out);
   TV_CHECK_LAUNCH();
   return TV_OK;
 }

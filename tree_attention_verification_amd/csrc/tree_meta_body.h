@@ -149,3 +149,170 @@ __device__ __forceinline__ void meta_body(int b, int i, int T_max, int dcap, int
 
 }  // namespace
 }  // namespace tv
+
+// ---------------------------------------------------------------------------
+// Trees of up to 256 nodes (T_max in (64, 256]): the same metadata computed by a
+// 256-thread workgroup, thread i = node i, each ancestor set a 256-bit mask of
+// four 64-bit words.  Pointer jumping runs through LDS (a round reads the jump
+// target's mask and pointer, then all threads write theirs), eight rounds at most.
+// ---------------------------------------------------------------------------
+namespace tv {
+namespace {
+
+constexpr int kWideNodes = 256;
+constexpr int kWideWords = kWideNodes / 64;
+
+struct WideShared {
+  unsigned long long m[kWideNodes][kWideWords];   // ancestor masks (final)
+  unsigned long long cm[kWideNodes][kWideWords];  // child masks
+  int a[kWideNodes];                              // jump pointers
+  int leaf[kWideNodes];
+  int cnt[kWideNodes / 64];
+  int flag;
+};
+
+// block-wide OR of a predicate (every thread of the 256 gets it)
+__device__ __forceinline__ bool block_any_wide(bool v, int* s_flag) {
+  __syncthreads();
+  if (threadIdx.x == 0) *s_flag = 0;
+  __syncthreads();
+  if (v) *s_flag = 1;
+  __syncthreads();
+  return *s_flag != 0;
+}
+
+// The checks of check_tree for a 256-thread workgroup (thread i = node i).
+__device__ __forceinline__ int check_tree_wide(int i, int T_max, int& st, int& T, int p_l, WideShared& sh) {
+  if (st == TV_ST_OK && (T < 1 || T > T_max)) st = TV_ST_SIZE;
+  int p = -1;
+  bool bad = false;
+  if (st == TV_ST_OK) {
+    p = i < T ? p_l : -1;
+    bad = (i == 0) ? (p != -1) : (i < T && !(p >= 0 && p < i));
+  }
+  if (block_any_wide(bad, &sh.flag)) st = TV_ST_PARENTS;
+  if (st != TV_ST_OK) {
+    T = 1;
+    p = -1;
+  }
+  return p;
+}
+
+// Ancestor masks of every node (thread i = node i, parent p) into sh.m; returns depth.
+__device__ __forceinline__ int ancestors_wide(int i, int T, int p, WideShared& sh, unsigned long long (&m)[kWideWords]) {
+#pragma unroll
+  for (int w = 0; w < kWideWords; ++w) m[w] = (i < T && (i >> 6) == w) ? (1ull << (i & 63)) : 0ull;
+  int a = (i < T && i > 0) ? p : -1;
+  for (int r = 0; r < 8; ++r) {
+#pragma unroll
+    for (int w = 0; w < kWideWords; ++w) sh.m[i][w] = m[w];
+    sh.a[i] = a;
+    if (!block_any_wide(a >= 0, &sh.flag)) break;  // block_any_wide starts with a barrier: the writes are visible
+    unsigned long long ma[kWideWords];
+    int aa = -1;
+    if (a >= 0) {
+      aa = sh.a[a];
+#pragma unroll
+      for (int w = 0; w < kWideWords; ++w) ma[w] = sh.m[a][w];
+    }
+    __syncthreads();  // every read of this round before the next round's writes
+    if (a >= 0) {
+#pragma unroll
+      for (int w = 0; w < kWideWords; ++w) m[w] |= ma[w];
+      a = aa;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kWideWords; ++w) sh.m[i][w] = m[w];
+  __syncthreads();
+  int pc = 0;
+#pragma unroll
+  for (int w = 0; w < kWideWords; ++w) pc += __popcll(m[w]);
+  return pc - 1;
+}
+
+// meta_body for trees of up to 256 nodes: every thread of the 256-thread
+// workgroup calls it with its node i.
+__device__ __forceinline__ void meta_body_wide(int b, int i, int T_max, int dcap, int W, int T, int st, int p, int P,
+                                               uint32_t* __restrict__ tree_mask,
+                                               int* __restrict__ tree_position_ids, int* __restrict__ positions,
+                                               int* __restrict__ retrieve_indices, int* __restrict__ leaf_count,
+                                               int* __restrict__ first_child, int* __restrict__ next_sibling,
+                                               int* __restrict__ status_out, WideShared& sh) {
+  const long long ob = (long long)b * T_max;
+  unsigned long long m[kWideWords];
+  int depth = ancestors_wide(i, T, p, sh, m);
+  if (st == TV_ST_OK && block_any_wide(i < T && depth > dcap, &sh.flag)) {
+    st = TV_ST_DEPTH;
+    T = 1;
+    p = -1;
+    depth = ancestors_wide(i, T, p, sh, m);
+  }
+  const bool in = i < T;
+  if (i < T_max) {
+    for (int w = 0; w < W; ++w) tree_mask[(ob + i) * W + w] = in ? (uint32_t)(m[w >> 1] >> (32 * (w & 1))) : 0u;
+    tree_position_ids[ob + i] = in ? depth : 0;
+    positions[ob + i] = in ? P + depth : 0;
+  }
+  // child masks: one LDS atomic per node into its parent's mask
+#pragma unroll
+  for (int w = 0; w < kWideWords; ++w) sh.cm[i][w] = 0ull;
+  __syncthreads();
+  if (in && i > 0) atomicOr(&sh.cm[p][i >> 6], 1ull << (i & 63));
+  __syncthreads();
+  int fc = -1, ns = -1;
+  if (in) {
+#pragma unroll
+    for (int w = kWideWords - 1; w >= 0; --w)
+      if (sh.cm[i][w]) fc = 64 * w + __ffsll((long long)sh.cm[i][w]) - 1;
+    if (i > 0) {
+      for (int w = kWideWords - 1; w >= (i >> 6); --w) {
+        unsigned long long later = sh.cm[p][w];
+        if (w == (i >> 6)) later &= (i & 63) == 63 ? 0ull : ~((2ull << (i & 63)) - 1ull);
+        if (later) ns = 64 * w + __ffsll((long long)later) - 1;
+      }
+    }
+  }
+  if (i < T_max) {
+    if (first_child) first_child[ob + i] = fc;
+    if (next_sibling) next_sibling[ob + i] = ns;
+  }
+  // leaves ranked by id: per-wavefront ballots, then the wavefronts' counts
+  const bool leaf = in && fc == -1;
+  const unsigned long long lb = __ballot(leaf);
+  const int lane = i & 63, wv = i >> 6;
+  if (lane == 0) sh.cnt[wv] = __popcll(lb);
+  __syncthreads();
+  int before = 0, nleaf = 0;
+  for (int w = 0; w < kWideNodes / 64; ++w) {
+    if (w < wv) before += sh.cnt[w];
+    nleaf += sh.cnt[w];
+  }
+  if (leaf) sh.leaf[before + __popcll(lb & ((1ull << lane) - 1ull))] = i;
+  __syncthreads();
+  if (i < T_max) {
+    int* row = retrieve_indices + (ob + i) * (dcap + 1);
+    unsigned long long lm[kWideWords];
+    const int lf = i < nleaf ? sh.leaf[i] : -1;
+#pragma unroll
+    for (int w = 0; w < kWideWords; ++w) lm[w] = lf >= 0 ? sh.m[lf][w] : 0ull;
+    int w = 0;
+    for (int k = 0; k <= dcap; ++k) {
+      while (w < kWideWords && lm[w] == 0ull) ++w;
+      int v = -1;
+      if (w < kWideWords) {
+        v = 64 * w + __ffsll((long long)lm[w]) - 1;  // ancestors in ascending id = ascending depth
+        lm[w] &= lm[w] - 1ull;
+      }
+      row[k] = v;
+    }
+  }
+  if (i == 0) {
+    leaf_count[b] = nleaf;
+    status_out[b] = st;
+  }
+}
+
+}  // namespace
+}  // namespace tv

@@ -33,8 +33,9 @@ inline int log2_block(int tokens_per_block) {
   return -1;
 }
 
-// Largest supported padded node count (one wavefront lane per node).
-constexpr int kTMaxLimit = 64;
+// Largest supported padded node count: one wavefront lane per node up to 64,
+// one workgroup thread per node up to 256.
+constexpr int kTMaxLimit = 256;
 // Largest supported top_k (per-thread register lists).
 constexpr int kKMax = 16;
 
