@@ -207,6 +207,9 @@ def main():
     ap.add_argument("--sampling", action="store_true",
                     help="accept by target-only tree rejection sampling (tree_accept_sample, then the compaction) "
                          "from synthetic target distributions instead of the greedy walk")
+    ap.add_argument("--tree-nodes", type=int, default=None, metavar="N",
+                    help="grow the trees to N nodes (65..256; T_max = N): dynamic workloads keep N - 1 draft "
+                         "nodes, the random-tree workload draws sizes in [8, N]")
     ap.add_argument("--copy-mb", type=float, default=0.0,
                     help="before warmup, one device-to-device copy of this many MiB (a plain copy kernel of known "
                          "size that calibrates the HBM byte counters of a profiler run)")
@@ -223,7 +226,9 @@ def main():
 
     _lib.lib()
     torch.cuda.set_device(0)
-    w = gen.make_workload(args.config)
+    w = gen.make_workload(args.config, tree_nodes=args.tree_nodes)
+    if args.tree_nodes:
+        w.name = f"{w.name}+trees{args.tree_nodes}"
     paged = gen.paged_layout(w, args.paged) if args.paged else None
     kv_bytes = (w.Kc.nbytes + w.Vc.nbytes) if paged is None else (paged.K_pool.nbytes + paged.V_pool.nbytes)
     per_copy = w.Q.nbytes + kv_bytes + (w.logprobs.nbytes if w.logprobs is not None else 0)

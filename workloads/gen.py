@@ -194,12 +194,17 @@ def _random_topology(cfg_id: int, b: int, T: int, V: int, max_depth: int, T_max:
 def make_workload(cfg_id: int, *, peaked: bool = False, batch: Optional[int] = None,
                   prefix: Optional[int] = None, T_max: int = T_MAX_DEFAULT,
                   dcap: int = DCAP_DEFAULT, seed_offset: int = 0,
-                  with_attention: bool = True) -> Workload:
+                  with_attention: bool = True, tree_nodes: Optional[int] = None) -> Workload:
     """Build one of the five measured configurations (1..5).
 
     ``batch`` / ``prefix`` shrink a configuration for CPU-sized tests while
     keeping its tree and head shapes; ``seed_offset`` moves every stream;
-    ``with_attention=False`` skips the Q/K/V draws (tree-only tests)."""
+    ``with_attention=False`` skips the Q/K/V draws (tree-only tests);
+    ``tree_nodes`` (65..256) grows the trees: dynamic configurations keep
+    tree_nodes - 1 draft nodes, the random-tree configuration draws sizes in
+    [8, tree_nodes]; T_max becomes tree_nodes."""
+    if tree_nodes is not None:
+        T_max = int(tree_nodes)
     sid = cfg_id + 1000 * seed_offset
     attn = _attn_tensors if with_attention else (lambda *a: (None, None, None))
     if cfg_id == 1:
@@ -226,6 +231,8 @@ def make_workload(cfg_id: int, *, peaked: bool = False, batch: Optional[int] = N
         else:
             B, K, D, TT, Hq = 4, 10, 6, 60, 64
             P = np.full(B, 32768, np.int32)
+        if tree_nodes is not None:
+            TT = int(tree_nodes) - 1
         if batch is not None:
             B = batch
             P = P[:B] if len(P) >= B else np.resize(P, B)
@@ -247,7 +254,8 @@ def make_workload(cfg_id: int, *, peaked: bool = False, batch: Optional[int] = N
         B = 64 if batch is None else batch
         V = 32000
         P = np.full(B, 4096 if prefix is None else prefix, np.int32)
-        sizes = np.array([rng(sid, STREAM_SHAPE, 10_000 + b).integers(8, 65) for b in range(B)], np.int32)
+        top = 64 if tree_nodes is None else int(tree_nodes)
+        sizes = np.array([rng(sid, STREAM_SHAPE, 10_000 + b).integers(8, top + 1) for b in range(B)], np.int32)
         sizes = np.minimum(sizes, T_max).astype(np.int32)
         par = np.full((B, T_max), -1, np.int32)
         tok = np.full((B, T_max), -1, np.int32)
