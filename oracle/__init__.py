@@ -11,6 +11,9 @@ Modules
                 (walk and the cumprod-over-paths formulation).
   attention  -- tree-masked GQA attention, dense softmax in float64.
   kv         -- compaction of the accepted path's K/V rows.
+  sampling   -- target logits filtered into probabilities (temperature, top-k,
+                top-p, min-p) and tree rejection sampling with the drafter's
+                distribution q (min(1, p/q), residual norm(max(0, p - q))).
 
 Sources (cited per function by page title and section):
   [HB]  AI-infra handbook, "Advanced speculative decoding: tree drafts and EAGLE"
