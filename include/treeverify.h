@@ -10,7 +10,9 @@
  *   tree_attention      Q, K/V cache, mask -> O (every node over prefix + ancestors)
  *   (tree_attention_rope the same with the queries' rotary embedding fused in)
  *   tree_accept         target argmax per node -> accepted path, bonus token
- *   (tree_accept_sample the same from target distributions, by rejection sampling)
+ *   (tree_accept_sample the same from target distributions, by rejection sampling;
+ *    tree_sampling_probs filters the target logits into those distributions;
+ *    tree_accept_sample_draft samples with the drafter's distribution as well)
  *   kv_compact          accepted path    -> K/V rows moved to contiguous slots
  *   tree_accept_compact the last two in one launch
  * and the same attention and compaction over a paged K/V cache (a block table
@@ -316,6 +318,78 @@ int tree_accept_sample(int B, int T_max, int dcap, int V, const int* draft_token
                        const int* tree_size, const float* target_probs, const float* uniforms,
                        const int* status, int* accept_len, int* accept_path, int* bonus_token,
                        void* stream);
+
+/* ------------------------------------------------------------------------- *
+ * tree_sampling_probs -- [TRT] "non-greedy: rejection from the target
+ * distribution alone": before the rejection step the target's logits at every
+ * tree node are turned into probabilities with the request's sampling
+ * parameters (temperature, top-k, top-p, min-p), the per-request parameters
+ * repeated over the request's nodes and each node filtered on its own.
+ *
+ * For request b and node i < T_b (T_b = tree_size[b], or 1 when status[b] != 0
+ * or the size is out of range), row probs[b][i] is computed from logits[b][i]:
+ *   - tokens rank by (logit descending, token ascending); NaN ranks as -inf,
+ *     -0.0 equals +0.0;
+ *   - temperature[b] <= 0 (or NaN), top_k[b] == 1 or top_p[b] <= 0: 1.0 on the
+ *     first-ranked token, 0 elsewhere;
+ *   - otherwise the weight of token v is w = float32(exp((l_v - l_max) /
+ *     temperature)) computed in float64, exactly 1 where l_v equals the largest
+ *     logit; then, in this order: top-k (1 < top_k < V) keeps the first top_k
+ *     ranks; top-p (top_p < 1) keeps the shortest rank prefix of those whose
+ *     cumulative weight reaches top_p x their total weight (sums in float64);
+ *     min-p (min_p > 0) drops tokens with w < min_p, the first-ranked token
+ *     always kept; the output is w / (sum of kept w) in float64, rounded to
+ *     float32, and 0 for dropped tokens.
+ * Rows i >= T_b are not written.  The result feeds tree_accept_sample (target
+ * only) or tree_accept_sample_draft.
+ * In:  logits float32 [B][T_max][V]; tree_size [B]; status [B] (nullable = all
+ *      TV_ST_OK); temperature, top_p, min_p float32 [B]; top_k int32 [B]
+ *      (<= 0 or >= V: no top-k).
+ * Out: probs float32 [B][T_max][V] (must not overlap logits).
+ * Requires 1 <= T_max <= 256, 1 <= V <= 262144, B <= 65535.
+ * ------------------------------------------------------------------------- */
+int tree_sampling_probs(int B, int T_max, int V, const float* logits, const int* tree_size,
+                        const int* status, const float* temperature, const int* top_k,
+                        const float* top_p, const float* min_p, float* probs, void* stream);
+
+/* ------------------------------------------------------------------------- *
+ * tree_accept_sample_draft -- tree rejection sampling with the drafter's
+ * distribution: [HB] exercise "trees when sampling" (at a node try its
+ * children in order, accept each with min(1, p(x)/q(x)); after a rejection the
+ * target becomes norm(max(0, p - q)) and q is adjusted to how the candidates
+ * were drawn; when every child is rejected the correction token comes from the
+ * last residual).
+ *
+ * draft_probs[b][n] is q at node n: the drafter's distribution that node n's
+ * children were proposed from.  On entering node n, R = target_probs[b][n] and
+ * Q = draft_probs[b][n] (float64), ZR, ZQ their sums.  Children in ascending
+ * id: child c with token x, r = R(x), s = Q(x) (0 outside [0, V)), is accepted
+ * iff r > 0 and (s == 0 or uniforms[b][c] * s * ZR < r * ZQ), each product
+ * rounded on its own; on acceptance move to c.  On rejection, if ZQ > 0:
+ * R <- max(0, R * ZQ - Q * ZR) elementwise (the residual up to a positive
+ * factor), ZR <- sum(R); with without_replacement != 0 (candidates drawn
+ * without replacement) Q(x) <- 0 and ZQ <- sum(Q), otherwise Q is kept
+ * (independent draws).  The walk stops when every child is rejected, at depth
+ * dcap, or at once when status != 0.  bonus_token: the smallest v whose
+ * cumulative R (float64, token order; R = the node's row p when nothing was
+ * rejected there) exceeds uniforms[b][0] * sum(R); if rounding leaves none, the
+ * last v with R(v) > 0; if sum(R) = 0, the node's best token (p descending,
+ * token ascending).  With draft rows that are the point mass on a chain node's
+ * only child this is tree_accept_sample; with one-hot target rows it is
+ * tree_accept.
+ * In:  as tree_accept_sample, plus draft_probs float32 [B][T_max][V] (rows of
+ *      nodes the walk does not reach are not read).
+ * Out: accept_len, accept_path, bonus_token as tree_accept.
+ * Workspace: tree_accept_sample_draft_workspace_bytes(B, V) bytes (B x V
+ *   float64 residual rows, any contents, 8-byte aligned).
+ * Requires 1 <= T_max <= 256, 0 <= dcap < T_max, 1 <= V <= 262144.
+ * ------------------------------------------------------------------------- */
+size_t tree_accept_sample_draft_workspace_bytes(int B, int V);
+int tree_accept_sample_draft(int B, int T_max, int dcap, int V, const int* draft_tokens,
+                             const int* parents, const int* tree_size, const float* target_probs,
+                             const float* draft_probs, const float* uniforms, const int* status,
+                             int without_replacement, int* accept_len, int* accept_path,
+                             int* bonus_token, void* workspace, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------- *
  * kv_compact -- [TRT] "after acceptance: KV from tree layout back to linear",

@@ -1,0 +1,137 @@
+"""GPU parity of tree_sampling_probs (target logits -> filtered probabilities) against
+the oracle's sampling_probs_row, and of the chain tree_sampling_probs ->
+tree_accept_sample against the oracle's filter + accept_sample.
+
+Bars: the set of kept tokens is bit-exact (both sides take every decision in
+float64 from the same float32 weights; only the order of sums differs); kept
+probabilities within 2e-6 relative (one float32 rounding of w / W, W summed in a
+different order); rows past a request's tree are untouched.  Cases: several
+vocabulary sizes (50 to 128256, i.e. one to ~125 values per thread), mixed
+per-request parameters, ties (logits rounded to a coarse grid), NaN / +-inf / -0.0
+logits, greedy and off settings of every filter, bad statuses, and T_max = 256.
+"""
+import numpy as np
+import pytest
+
+from tests.conftest import gpu_available
+from workloads import gen
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not gpu_available():
+        pytest.skip("no GPU")
+    from tree_attention_verification_amd import _lib
+    _lib.lib()   # raises if the library is missing: no fallback
+
+
+def _dev(x, dtype=None):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x if dtype is None else np.asarray(x, dtype))).cuda()
+
+
+def run_filter(logits, tree_size, status, params):
+    import torch
+    from oracle import sampling as osm
+    from tree_attention_verification_amd import _lib as tv
+    B, T_max, V = logits.shape
+    temp, top_k, top_p, min_p = params
+    out = torch.full((B, T_max, V), -7.0, dtype=torch.float32, device="cuda")
+    tv.tree_sampling_probs(B, T_max, V, _dev(logits), _dev(tree_size, np.int32),
+                           None if status is None else _dev(status, np.int32), _dev(temp, np.float32),
+                           _dev(top_k, np.int32), _dev(top_p, np.float32), _dev(min_p, np.float32), out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    st = np.zeros(B, np.int32) if status is None else status
+    ref = osm.tree_sampling_probs(logits, tree_size, st, temp, top_k, top_p, min_p,
+                                  np.full((B, T_max, V), -7.0, np.float32))
+    np.testing.assert_array_equal(got > 0, ref > 0, err_msg="kept tokens")
+    np.testing.assert_array_equal(got == -7.0, ref == -7.0, err_msg="untouched rows")
+    np.testing.assert_allclose(got, ref, rtol=2e-6, atol=0)
+    return got
+
+
+@pytest.mark.parametrize("V", [50, 1000, 32000, 128256])
+def test_filters_mixed_parameters(V):
+    B = 8 if V <= 32000 else 3
+    w = gen.make_custom(cfg_id=1600 + V % 89, B=B, mode="given", given_sizes=[6, 1, 3, 8, 2, 5, 4, 7][:B], V=V, P=4,
+                        T_max=8, dcap=6)
+    lg = gen.synthetic_target_logits(w, w.given_size)
+    params = gen.sampling_params(w, B)
+    params[1][0] = min(V - 1, 37)            # make sure top-k, top-p and min-p all run somewhere
+    params[2][0], params[3][0], params[0][0] = 0.9, 0.01, 0.8
+    run_filter(lg, w.given_size, None, params)
+
+
+@pytest.mark.parametrize("tie_step", [0.5, 2.0])
+def test_filters_with_ties(tie_step):
+    w = gen.make_custom(cfg_id=1610, B=6, mode="given", given_sizes=[4] * 6, V=3000, P=4, T_max=4, dcap=3)
+    lg = gen.synthetic_target_logits(w, w.given_size, tie_step=tie_step)
+    temp = np.array([1.0, 0.7, 1.3, 1.0, 0.5, 2.0], np.float32)
+    top_k = np.array([5, 0, 100, 2999, 0, 40], np.int32)
+    top_p = np.array([1.0, 0.8, 0.95, 0.3, 0.99, 1.0], np.float32)
+    min_p = np.array([0.0, 0.0, 0.05, 0.0, 0.3, 0.02], np.float32)
+    run_filter(lg, w.given_size, None, (temp, top_k, top_p, min_p))
+
+
+def test_filters_special_values_and_settings():
+    V = 700
+    w = gen.make_custom(cfg_id=1620, B=10, mode="given", given_sizes=[3] * 10, V=V, P=4, T_max=4, dcap=3)
+    lg = gen.synthetic_target_logits(w, w.given_size)
+    lg[0, 0, [3, 9, 11]] = np.nan
+    lg[0, 1, [5, 6]] = np.inf                   # two +inf: they share the mass
+    lg[0, 2, :] = -np.inf                       # an all -inf row: uniform
+    lg[1, 0, :] = -0.0
+    lg[1, 0, 10:20] = 0.0                       # -0.0 and +0.0 rank equal
+    lg[1, 1, ::2] = np.nan
+    temp = np.array([1.0, 1.0, 0.0, -1.0, np.nan, 1.0, 1.0, 1.0, 1.0, 0.9], np.float32)
+    top_k = np.array([3, 0, 0, 0, 0, 1, V, V + 5, -4, V - 1], np.int32)
+    top_p = np.array([1.0, 0.5, 1.0, 1.0, 1.0, 1.0, 0.0, np.nan, 1e-9, 0.999999], np.float32)
+    min_p = np.array([0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 1.0, np.nan, 1e-7], np.float32)
+    status = np.array([0, 0, 0, 0, 0, 0, 0, 0, 2, 0], np.int32)     # request 8: its root row only
+    run_filter(lg, w.given_size, status, (temp, top_k, top_p, min_p))
+
+
+def test_filters_wide_trees():
+    w = gen.make_custom(cfg_id=1630, B=2, mode="given", given_sizes=[256, 130], given_depth=9, V=500, P=4,
+                        T_max=256, dcap=20)
+    lg = gen.synthetic_target_logits(w, w.given_size)
+    params = (np.array([0.8, 1.2], np.float32), np.array([20, 0], np.int32), np.array([0.9, 0.7], np.float32),
+              np.array([0.0, 0.05], np.float32))
+    run_filter(lg, w.given_size, None, params)
+
+
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_filter_then_target_only_sampling(cfg):
+    """The whole non-greedy chain: logits -> tree_sampling_probs -> tree_accept_sample,
+    against the oracle's filter + accept_sample (bit-exact results)."""
+    import torch
+    from oracle import sampling as osm
+    from oracle import tree as ot
+    from tree_attention_verification_amd import _lib as tv
+    from tree_attention_verification_amd.step import TreeVerifyStep
+    w = gen.make_workload(cfg, with_attention=False)
+    st = TreeVerifyStep(w)
+    st.build_meta()
+    torch.cuda.synchronize()
+    tree = st.tree_host()
+    B, T_max, V = w.B, w.T_max, w.V
+    lg = gen.synthetic_target_logits(w, tree["tree_size"])
+    params = gen.sampling_params(w, B)
+    probs = torch.zeros((B, T_max, V), dtype=torch.float32, device="cuda")
+    status = st.status
+    tv.tree_sampling_probs(B, T_max, V, _dev(lg), st.tree_size, status, _dev(params[0]), _dev(params[1]),
+                           _dev(params[2]), _dev(params[3]), probs)
+    _, uni = gen.synthetic_target_probs(w, tree["draft_tokens"], tree["parents"], tree["tree_size"])
+    st.set_target_probs(probs.cpu().numpy(), uni)
+    st.accept_sample()
+    torch.cuda.synchronize()
+    got = st.accept_host()
+    stat = status.cpu().numpy()
+    ref_probs = osm.tree_sampling_probs(lg, tree["tree_size"], stat, *params, np.zeros((B, T_max, V), np.float32))
+    ref = ot.tree_accept_sample(tree["draft_tokens"], tree["parents"], tree["tree_size"], ref_probs, uni, stat,
+                                st.dcap)
+    for k in ("accept_len", "accept_path", "bonus_token"):
+        np.testing.assert_array_equal(got[k], ref[k], err_msg=k)

@@ -153,3 +153,31 @@ def test_rope_call_host_validation():
                                  None) == tv.TV_EUNSUPPORTED    # positions past 2^24
     assert L.tree_attention_rope(0, 1, 64, 8, 4, 96, X, X, X, 4096, X, X, X, X, 1e4, 0.0, X, None, 0,
                                  None) == tv.TV_EUNSUPPORTED
+
+
+def test_sampling_calls_host_validation():
+    L = tv.lib()
+    # tree_sampling_probs(B, T_max, V, logits, size, status, temperature, top_k, top_p, min_p, probs, stream)
+    assert L.tree_sampling_probs(0, 4, 100, X, X, None, X, X, X, X, ctypes.c_void_p(0x100000), None) == tv.TV_EINVAL
+    assert L.tree_sampling_probs(1, 257, 100, X, X, None, X, X, X, X, ctypes.c_void_p(0x100000),
+                                 None) == tv.TV_EUNSUPPORTED
+    assert L.tree_sampling_probs(1, 4, 262145, X, X, None, X, X, X, X, ctypes.c_void_p(0x10000000),
+                                 None) == tv.TV_EUNSUPPORTED
+    assert L.tree_sampling_probs(1, 4, 100, X, X, None, None, X, X, X, ctypes.c_void_p(0x100000),
+                                 None) == tv.TV_EINVAL
+    # the output overlapping the logits
+    assert L.tree_sampling_probs(1, 4, 100, X, X, None, X, X, X, X, ctypes.c_void_p(0x1000 + 400),
+                                 None) == tv.TV_EINVAL
+    # tree_accept_sample_draft(B, T_max, dcap, V, tokens, parents, size, p, q, u, status, wr, len, path, bonus,
+    #                          ws, ws_bytes, stream)
+    assert tv.tree_accept_sample_draft_workspace_bytes(3, 1000) == 3 * 1000 * 8
+    ws = ctypes.c_void_p(0x200000)
+    ok = (1, 16, 7, 100, X, X, X, X, X, X, X, 1, X, X, X, ws, 800, None)
+    bad = lambda i, v: tuple(v if j == i else a for j, a in enumerate(ok))
+    assert L.tree_accept_sample_draft(*bad(2, 16)) == tv.TV_EINVAL                 # dcap >= T_max
+    assert L.tree_accept_sample_draft(*bad(1, 257)) == tv.TV_EUNSUPPORTED
+    assert L.tree_accept_sample_draft(*bad(3, 262145)) == tv.TV_EUNSUPPORTED
+    assert L.tree_accept_sample_draft(*bad(8, None)) == tv.TV_EINVAL                # no draft rows
+    assert L.tree_accept_sample_draft(*bad(16, 799)) == tv.TV_EWORKSPACE            # workspace too small
+    assert L.tree_accept_sample_draft(*bad(15, ctypes.c_void_p(0x200004))) == tv.TV_EWORKSPACE   # misaligned
+    assert L.tree_accept_sample_draft(*bad(15, None)) == tv.TV_EWORKSPACE

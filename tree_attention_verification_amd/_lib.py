@@ -58,6 +58,9 @@ _SIGS = {
     "tree_build_finish": (I, [I, I, I, I, I, P, I, P, SZ, P, P, P, P, P, I, P, P, P, P, P, P, P, P, P]),
     "tree_accept_sample": (I, [I, I, I, I, P, P, P, P, P, P, P, P, P, P]),
     "tree_attention_rope": (I, [I, I, I, I, I, I, P, P, P, LL, P, P, P, P, F, F, P, P, SZ, P]),
+    "tree_sampling_probs": (I, [I, I, I, P, P, P, P, P, P, P, P, P]),
+    "tree_accept_sample_draft_workspace_bytes": (SZ, [I, I]),
+    "tree_accept_sample_draft": (I, [I, I, I, I, P, P, P, P, P, P, P, I, P, P, P, P, SZ, P]),
     "tv_error_string": (ctypes.c_char_p, [I]),
     "tv_status_string": (ctypes.c_char_p, [I]),
 }
@@ -297,6 +300,33 @@ def tree_accept_sample(B, T_max, dcap, V, draft_tokens, parents, tree_size, targ
                                   _dev(accept_path, "accept_path"), _dev(bonus_token, "bonus_token"),
                                   _stream(stream))
     _check("tree_accept_sample", rc)
+
+
+def tree_sampling_probs(B, T_max, V, logits, tree_size, status, temperature, top_k, top_p, min_p, probs,
+                        stream=None):
+    rc = lib().tree_sampling_probs(B, T_max, V, _dev(logits, "logits"), _dev(tree_size, "tree_size"),
+                                   _dev(status, "status"), _dev(temperature, "temperature"), _dev(top_k, "top_k"),
+                                   _dev(top_p, "top_p"), _dev(min_p, "min_p"), _dev(probs, "probs"),
+                                   _stream(stream))
+    _check("tree_sampling_probs", rc)
+
+
+def tree_accept_sample_draft_workspace_bytes(B, V) -> int:
+    return int(lib().tree_accept_sample_draft_workspace_bytes(B, V))
+
+
+def tree_accept_sample_draft(B, T_max, dcap, V, draft_tokens, parents, tree_size, target_probs, draft_probs,
+                             uniforms, status, without_replacement, accept_len, accept_path, bonus_token, workspace,
+                             stream=None):
+    wp, wn = _ws(workspace)
+    rc = lib().tree_accept_sample_draft(B, T_max, dcap, V, _dev(draft_tokens, "draft_tokens"),
+                                        _dev(parents, "parents"), _dev(tree_size, "tree_size"),
+                                        _dev(target_probs, "target_probs"), _dev(draft_probs, "draft_probs"),
+                                        _dev(uniforms, "uniforms"), _dev(status, "status"),
+                                        1 if without_replacement else 0, _dev(accept_len, "accept_len"),
+                                        _dev(accept_path, "accept_path"), _dev(bonus_token, "bonus_token"), wp, wn,
+                                        _stream(stream))
+    _check("tree_accept_sample_draft", rc)
 
 
 def tree_attention_rope(dtype, B, T_max, Hq, Hkv, d, Q, Kc, Vc, S_cap, prefix_len, tree_size, tree_mask, status,

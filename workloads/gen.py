@@ -23,7 +23,8 @@ from typing import List, Optional
 
 import numpy as np
 
-STREAM_LOGITS, STREAM_Q, STREAM_K, STREAM_V, STREAM_TARGET, STREAM_SHAPE, STREAM_ROOT, STREAM_PAGES, STREAM_PROBS = range(9)
+(STREAM_LOGITS, STREAM_Q, STREAM_K, STREAM_V, STREAM_TARGET, STREAM_SHAPE, STREAM_ROOT, STREAM_PAGES, STREAM_PROBS,
+ STREAM_TLOGITS, STREAM_DRAFTQ) = range(11)
 
 T_MAX_DEFAULT = 64
 DCAP_DEFAULT = 7
@@ -410,3 +411,62 @@ def synthetic_target_probs(w: Workload, draft_tokens: np.ndarray, parents: np.nd
             probs[b, i] = row.astype(np.float32)
         uni[b] = g.random(T_max).astype(np.float32)
     return probs, uni
+
+
+def synthetic_target_logits(w: Workload, tree_size: np.ndarray, std_range=(0.5, 4.0), tie_step: float = 0.0):
+    """Stand-in for the target model's raw logits at every tree node: N(0, s^2) with s
+    drawn per request from std_range; with tie_step > 0 the values are rounded to
+    multiples of it (many equal logits).  Rows of padding nodes are N(0, 1) too (they
+    must not be read or written by the consumer).  float32 [B][T_max][V]."""
+    B, T_max, V = len(tree_size), w.T_max, w.V
+    out = np.zeros((B, T_max, V), np.float32)
+    for b in range(B):
+        g = rng(w.cfg_id, STREAM_TLOGITS, b)
+        s = g.uniform(*std_range)
+        x = g.standard_normal((T_max, V)) * s
+        if tie_step > 0:
+            x = np.round(x / tie_step) * tie_step
+        out[b] = x.astype(np.float32)
+    return out
+
+
+def sampling_params(w: Workload, B: int):
+    """Per-request sampling parameters, a mix of the usual settings: temperature in
+    [0.3, 1.5] (0 = greedy for about one request in eight), top_k 0 (off) or in
+    [1, min(V, 100)], top_p 1 (off) or in [0.5, 0.99], min_p 0 (off) or in
+    [0.001, 0.2].  Returns float32 temperature, int32 top_k, float32 top_p, min_p."""
+    g = rng(w.cfg_id, STREAM_TLOGITS, 10_000)
+    temp = np.where(g.random(B) < 0.125, 0.0, g.uniform(0.3, 1.5, B)).astype(np.float32)
+    top_k = np.where(g.random(B) < 0.5, 0, g.integers(1, min(w.V, 100) + 1, B)).astype(np.int32)
+    top_p = np.where(g.random(B) < 0.4, 1.0, g.uniform(0.5, 0.99, B)).astype(np.float32)
+    min_p = np.where(g.random(B) < 0.6, 0.0, g.uniform(0.001, 0.2, B)).astype(np.float32)
+    return temp, top_k, top_p, min_p
+
+
+def synthetic_draft_probs(w: Workload, draft_tokens: np.ndarray, parents: np.ndarray, tree_size: np.ndarray,
+                          concentration: float = 0.3):
+    """Stand-in for the drafter's distribution q at every node (the one its children
+    were proposed from): Gamma(concentration) noise normalised to 1 - m plus mass
+    m ~ U[0.3, 0.9] spread over the node's children's tokens with Dirichlet(1)
+    weights (the drafter proposes tokens it likes); rows of nodes without children
+    are noise only, rows of padding nodes zero.  float32 [B][T_max][V]."""
+    B, T_max = draft_tokens.shape
+    V = w.V
+    q = np.zeros((B, T_max, V), np.float32)
+    for b in range(B):
+        g = rng(w.cfg_id, STREAM_DRAFTQ, b)
+        T = int(tree_size[b])
+        T = 1 if T < 1 or T > T_max else T
+        for i in range(T):
+            noise = g.gamma(concentration, size=V)
+            row = noise / noise.sum()
+            kids = [int(draft_tokens[b, c]) for c in range(1, T) if parents[b, c] == i]
+            kids = [x for x in kids if 0 <= x < V]
+            if kids:
+                m = g.uniform(0.3, 0.9)
+                row = row * (1.0 - m)
+                wts = g.dirichlet(np.ones(len(kids)))
+                for x, wt in zip(kids, wts):
+                    row[x] += m * wt
+            q[b, i] = row.astype(np.float32)
+    return q
