@@ -26,8 +26,10 @@ Readings where the pages are silent (each listed with its reason in the design n
     row), rounded to float32; sums and comparisons of weights are float64;
   * top-k (1 <= k < V) keeps the first k ranks;
   * top-p (< 1; NaN = off) keeps the shortest rank prefix of the top-k survivors whose
-    cumulative weight, added in rank order, reaches top_p x their total weight (so at
-    least one token; all survivors if rounding never reaches it);
+    cumulative weight reaches top_p x their total weight (so at least one token); the
+    weights are added exactly, as integers in units of 2^-32 (round(w 2^32), half to
+    even), and the comparison is (double)cumulative >= (double)top_p x (double)total,
+    so the cut does not depend on the order of the additions;
   * min-p (> 0) drops tokens whose weight is below min_p x the largest weight (which is
     1); the first-ranked token is always kept;
   * the output is w / (sum of the kept w), float64 rounded to float32; dropped tokens
@@ -94,11 +96,14 @@ def sampling_probs_row(logits, temperature, top_k, top_p, min_p):
     surv = order[:n]
     tp = float(np.float32(top_p))
     if tp < 1.0:
-        target = tp * w[surv].sum()
-        cum = np.cumsum(w[surv])
-        hit = np.nonzero(cum >= target)[0]
-        if len(hit):
-            surv = surv[:hit[0] + 1]
+        fx = [int(x) for x in np.rint(w[surv] * 2.0 ** 32)]   # exact integers (w * 2^32 < 2^33)
+        target = tp * float(sum(fx))
+        cum = 0
+        for n, x in enumerate(fx):
+            cum += x
+            if float(cum) >= target:
+                surv = surv[:n + 1]
+                break
     keep = np.zeros(V, bool)
     keep[surv] = True
     mp = float(np.float32(min_p))
