@@ -207,6 +207,11 @@ def main():
     ap.add_argument("--sampling", action="store_true",
                     help="accept by target-only tree rejection sampling (tree_accept_sample, then the compaction) "
                          "from synthetic target distributions instead of the greedy walk")
+    ap.add_argument("--sampling-from", choices=["probs", "logits", "draft"], default="probs",
+                    help="with --sampling: probs = synthetic target distributions (tree_accept_sample); logits = "
+                         "synthetic target logits filtered per request (tree_sampling_probs, then "
+                         "tree_accept_sample); draft = the same filtered rows sampled against synthetic drafter "
+                         "distributions (tree_sampling_probs, then tree_accept_sample_draft)")
     ap.add_argument("--tree-nodes", type=int, default=None, metavar="N",
                     help="grow the trees to N nodes (65..256; T_max = N): dynamic workloads keep N - 1 draft "
                          "nodes, the random-tree workload draws sizes in [8, N]")
@@ -265,6 +270,11 @@ def main():
         probs, uni = gen.synthetic_target_probs(w, th["draft_tokens"], th["parents"], th["tree_size"])
         step.set_target_probs(probs, uni)
         del probs
+        if args.sampling_from != "probs":
+            q = (gen.synthetic_draft_probs(w, th["draft_tokens"], th["parents"], th["tree_size"])
+                 if args.sampling_from == "draft" else None)
+            step.set_sampling_inputs(gen.synthetic_target_logits(w, th["tree_size"]), gen.sampling_params(w, w.B), q)
+            del q
     torch.cuda.synchronize()
     status = mh["status"]
     nodes = int(np.where(status != 0, 1, th["tree_size"]).sum())
@@ -284,7 +294,18 @@ def main():
         if ev is not None:
             ev[1].record(stream)
         if args.sampling:
-            step.accept_sample()
+            if ev is not None:
+                ev[2].record(stream)
+            if args.sampling_from != "probs":
+                step.sampling_probs()
+            if ev is not None:
+                ev[3].record(stream)
+            if args.sampling_from == "draft":
+                step.accept_sample_draft()
+            else:
+                step.accept_sample()
+            if ev is not None:
+                ev[4].record(stream)
             step.compact()
         elif args.unfused:
             step.accept()
@@ -296,14 +317,20 @@ def main():
     for k in range(args.warmup):
         one(k)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(5)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
         one(args.warmup + k, evs[k])
     torch.cuda.synchronize()
     eager_elapsed = time.perf_counter() - t0
-    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    attn_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    sampling_us = None
+    if args.sampling:
+        sampling_us = {"tree_sampling_probs": round(float(np.mean([e[2].elapsed_time(e[3]) for e in evs])) * 1e3, 2)
+                       if args.sampling_from != "probs" else None,
+                       ("tree_accept_sample_draft" if args.sampling_from == "draft" else "tree_accept_sample"):
+                       round(float(np.mean([e[3].elapsed_time(e[4]) for e in evs])) * 1e3, 2)}
     ms_per_step_eager = eager_elapsed * 1e3 / args.steps
 
     # the same steps replayed from captured HIP graphs (one per input copy), the way
@@ -397,10 +424,13 @@ def main():
                        f"tree_build_layer x {w.D + 1} ({args.layerwise} rows), tree_build_finish" if args.layerwise
                        else ("tree_build, tree_mask_positions" if args.unfused else "tree_build_meta"),
                        "tree_attention" + ("_paged" if paged is not None else ""),
-                       ("tree_accept_sample, kv_compact" if args.sampling else
+                       (("tree_sampling_probs, " if args.sampling and args.sampling_from != "probs" else "") +
+                        ("tree_accept_sample_draft, kv_compact" if args.sampling and args.sampling_from == "draft"
+                         else "tree_accept_sample, kv_compact") if args.sampling else
                         "tree_accept, kv_compact" if args.unfused else "tree_accept_compact") +
                        ("_paged" if paged is not None else "")])},
         "stages_us": stages,
+        **({"sampling_us": sampling_us} if sampling_us else {}),
         "roofline": roof,
     }
     if peaks:

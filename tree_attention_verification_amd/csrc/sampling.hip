@@ -46,6 +46,16 @@ __device__ __forceinline__ double block_sum_d(double v, double* s) {
   __syncthreads();
   return t;
 }
+__device__ __forceinline__ unsigned long long block_sum_u64(unsigned long long v, unsigned long long* s) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  if (lane == 0) s[wave] = v;
+  __syncthreads();
+  unsigned long long t = 0ull;
+  for (int w = 0; w < kWaves; ++w) t += s[w];
+  __syncthreads();
+  return t;
+}
 __device__ __forceinline__ int block_sum_i(int v, int* s) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   v = wave_sum_i(v);
@@ -93,6 +103,38 @@ __device__ __forceinline__ unsigned long long block_max_u64(unsigned long long v
   return t;
 }
 
+// Visits v = threadIdx.x + j kThreads (j = 0, 1, ...) in increasing v, with the
+// loads of NB visits issued together (one memory round trip per NB entries);
+// indices past the row are clamped for the load and skipped for the body.
+constexpr int kNB = 8;
+template <class Load, class Body>
+__device__ __forceinline__ void row_pass(int V, Load load, Body body) {
+  using T = decltype(load(0));
+  for (int base = threadIdx.x; base < V; base += kNB * kThreads) {
+    T x[kNB];
+#pragma unroll
+    for (int j = 0; j < kNB; ++j) x[j] = load(min(base + j * kThreads, V - 1));
+#pragma unroll
+    for (int j = 0; j < kNB; ++j)
+      if (base + j * kThreads < V) body(base + j * kThreads, x[j]);
+  }
+}
+// The same over a contiguous range [c0, c1), in order; body returns true to stop.
+template <class Load, class Body>
+__device__ __forceinline__ void range_pass(int c0, int c1, Load load, Body body) {
+  using T = decltype(load(0));
+  for (int base = c0; base < c1; base += kNB) {
+    T x[kNB];
+#pragma unroll
+    for (int j = 0; j < kNB; ++j) x[j] = load(min(base + j, c1 - 1));
+    bool stop = false;
+#pragma unroll
+    for (int j = 0; j < kNB; ++j)
+      if (!stop && base + j < c1) stop = body(base + j, x[j]);
+    if (stop) return;
+  }
+}
+
 // logits: NaN ranks as -inf; order_key canonicalises -0.0
 __device__ __forceinline__ float clean_logit(float x) { return x != x ? -INFINITY : x; }
 __device__ __forceinline__ uint32_t logit_key(float x) { return order_key(clean_logit(x)); }
@@ -108,13 +150,15 @@ __device__ __forceinline__ float key_float(uint32_t k) {
 // written into the output row first and re-read from there.  Each filter keeps
 // a prefix of the ranking, described by a cut (key t, token c): token v with key
 // k is inside iff k > t or (k == t and v <= c).  The top-k and top-p cuts are
-// found by radix selection over the 32-bit order keys, four bits per pass from
-// the top: per pass every thread accumulates sixteen digit counters (counts for
-// top-k, float64 weight for top-p) over the tokens that match the digits chosen
-// so far, the workgroup sums them, and the digit holding the cut is taken.  Equal
-// keys have equal weights; the cut inside a group of equal keys is the n-th of
-// them in token order, found by a scan over contiguous token ranges.
+// found by radix selection over the 32-bit order keys, eight bits per pass from
+// the top, with exact integer totals (counts for top-k, weights in units of
+// 2^-32 for top-p).  Equal keys have equal weights; the cut inside a group of
+// equal keys is the n-th of them in token order, found by a scan over contiguous
+// token ranges.
 // --------------------------------------------------------------------------
+// NPT > 0: V <= NPT kThreads and every thread keeps its NPT (key, weight) pairs in
+// registers after the first read; NPT = 0: the row is re-read on every pass.
+template <int NPT>
 __global__ __launch_bounds__(kThreads) void k_sampling_probs(int T_max, int V, const float* __restrict__ logits,
                                                              const int* __restrict__ tree_size,
                                                              const int* __restrict__ status,
@@ -134,11 +178,30 @@ __global__ __launch_bounds__(kThreads) void k_sampling_probs(int T_max, int V, c
   __shared__ double s_d[kWaves * 16];
   __shared__ int s_i[kWaves * 16];
   __shared__ unsigned long long s_u[kWaves];
-  __shared__ int s_pick;
+  __shared__ unsigned long long s_hist[kWaves * 256];
+  __shared__ unsigned long long s_abv;
+  __shared__ int s_pick, s_sel;
 
   // the first-ranked token
+  struct KW {
+    uint32_t k;
+    float w;
+  };
+  KW reg[NPT > 0 ? NPT : 1];
+  auto ld_l = [&](int v) { return lr[v]; };
   unsigned long long best = 0ull;
-  for (int v = tid; v < V; v += kThreads) best = umax64(best, rank_key(clean_logit(lr[v]), (uint32_t)v));
+  if constexpr (NPT > 0) {
+    float x[NPT];
+#pragma unroll
+    for (int j = 0; j < NPT; ++j) x[j] = lr[min(tid + j * kThreads, V - 1)];
+#pragma unroll
+    for (int j = 0; j < NPT; ++j) {
+      reg[j].k = logit_key(x[j]);
+      if (tid + j * kThreads < V) best = umax64(best, rank_key(clean_logit(x[j]), (uint32_t)(tid + j * kThreads)));
+    }
+  } else {
+    row_pass(V, ld_l, [&](int v, float x) { best = umax64(best, rank_key(clean_logit(x), (uint32_t)v)); });
+  }
   best = block_max_u64(best, s_u);
   const uint32_t kmax = (uint32_t)(best >> 32);
   const int tok0 = (int)key_index(best);
@@ -154,7 +217,26 @@ __global__ __launch_bounds__(kThreads) void k_sampling_probs(int T_max, int V, c
   auto weight = [&](uint32_t key) -> float {
     return key == kmax ? 1.0f : (float)exp(((double)key_float(key) - dmax) / dtau);
   };
-  for (int v = tid; v < V; v += kThreads) orow[v] = weight(logit_key(lr[v]));
+  // (NPT = 0: the weights go to the output row, and each thread re-reads only the
+  // weights it wrote: the same v in every row pass)
+  auto ld_kw = [&](int v) { return KW{logit_key(lr[v]), orow[v]}; };
+  auto ld_k = [&](int v) { return logit_key(lr[v]); };
+  // one pass over the row: body(v, KW) for this thread's tokens in increasing v
+  auto pass = [&](auto body) __attribute__((always_inline)) {
+    if constexpr (NPT > 0) {
+#pragma unroll
+      for (int j = 0; j < NPT; ++j)
+        if (tid + j * kThreads < V) body(tid + j * kThreads, reg[j]);
+    } else {
+      row_pass(V, ld_kw, body);
+    }
+  };
+  if constexpr (NPT > 0) {
+#pragma unroll
+    for (int j = 0; j < NPT; ++j) reg[j].w = weight(reg[j].k);
+  } else {
+    row_pass(V, ld_l, [&](int v, float x) { orow[v] = weight(logit_key(x)); });
+  }
 
   // the n-th token (token order) with key t that satisfies pred, n >= 1: each
   // thread counts its contiguous range, a scan finds the range holding it
@@ -162,22 +244,22 @@ __global__ __launch_bounds__(kThreads) void k_sampling_probs(int T_max, int V, c
   const int c0 = min(V, tid * L), c1 = min(V, c0 + L);
   auto nth_with_key = [&](uint32_t t, int n, uint32_t tk, int ck) -> int {
     int c = 0;
-    for (int v = c0; v < c1; ++v) {
-      const uint32_t k = logit_key(lr[v]);
+    range_pass(c0, c1, ld_k, [&](int v, uint32_t k) {
       c += (k == t && (k > tk || v <= ck)) ? 1 : 0;
-    }
+      return false;
+    });
     if (tid == 0) s_pick = V;
     int lo, hi, tot;
     block_scan<int>(c, s_i, lo, hi, tot);
     if (lo < n && n <= hi) {
       int r = n - lo;
-      for (int v = c0; v < c1; ++v) {
-        const uint32_t k = logit_key(lr[v]);
+      range_pass(c0, c1, ld_k, [&](int v, uint32_t k) {
         if (k == t && (k > tk || v <= ck) && --r == 0) {
           s_pick = v;
-          break;
+          return true;
         }
-      }
+        return false;
+      });
     }
     __syncthreads();
     const int res = s_pick;
@@ -185,119 +267,114 @@ __global__ __launch_bounds__(kThreads) void k_sampling_probs(int T_max, int V, c
     return res;
   };
 
+  // ---- radix selection.  Over the tokens with pred, in rank order, each token
+  // carrying an integer value (1 to count ranks, its weight in units of 2^-32 for
+  // mass), find the key t of the first token at which the running total reaches
+  // `target`, and `above` = the total of the tokens with larger keys.  Eight bits
+  // of the key per pass from the top: each wavefront adds its tokens' values into
+  // its own 256-bin LDS histogram (integer atomics: the totals are exact, so the
+  // order of the additions does not matter), then the first wavefront places the
+  // target among the bins (four bins per lane, a suffix sum over the lanes).
+  // Returns false if the target is never reached.
+  const int lane = tid & 63, wave = tid >> 6;
+  auto radix = [&](auto val, auto pred, double target, uint32_t& t_out, unsigned long long& above_out) -> bool {
+    uint32_t prefix = 0u, pmask = 0u;
+    unsigned long long above = 0ull;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      for (int e = tid; e < kWaves * 256; e += kThreads) s_hist[e] = 0ull;
+      __syncthreads();
+      pass([&](int v, KW e) {
+        if ((e.k & pmask) == prefix && pred(e.k, v)) {
+          const unsigned long long x = val(e);
+          if (x) atomicAdd(&s_hist[wave * 256 + ((e.k >> shift) & 255u)], x);
+        }
+      });
+      __syncthreads();
+      if (wave == 0) {
+        unsigned long long m[4], g = 0ull;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          m[j] = 0ull;
+          for (int w = 0; w < kWaves; ++w) m[j] += s_hist[w * 256 + 4 * lane + j];
+          g += m[j];
+        }
+        unsigned long long suf = g;  // total of this lane's bins and every higher lane's
+        for (int o = 1; o < 64; o <<= 1) {
+          const unsigned long long y = __shfl_down(suf, o, 64);
+          if (lane + o < 64) suf += y;
+        }
+        unsigned long long run = above + (suf - g);
+        int cand = -1;
+        unsigned long long cabove = 0ull;
+        for (int j = 3; j >= 0; --j) {
+          if ((double)(run + m[j]) >= target) {
+            cand = 4 * lane + j;
+            cabove = run;
+            break;
+          }
+          run += m[j];
+        }
+        const unsigned long long hit = __ballot(cand >= 0);
+        if (lane == 0) s_sel = -1;
+        if (hit) {
+          const int L = 63 - __builtin_clzll(hit);  // the highest digit that reaches the target
+          if (lane == L) {
+            s_sel = cand;
+            s_abv = cabove;
+          }
+        }
+      }
+      __syncthreads();
+      const int sel = s_sel;
+      const unsigned long long nab = s_abv;
+      __syncthreads();
+      if (sel < 0) return false;
+      prefix |= (uint32_t)sel << shift;
+      pmask |= 255u << shift;
+      above = nab;
+    }
+    t_out = prefix;
+    above_out = above;
+    return true;
+  };
+  auto all = [](uint32_t, int) { return true; };
+  auto one = [](KW) { return 1ull; };
+  // weight in units of 2^-32 (w <= 1, so at most 2^32; a row's total stays below 2^51)
+  auto fixed = [](float w) { return (unsigned long long)rint((double)w * 4294967296.0); };
+
   // ---- top-k cut (tk, ck); the default keeps everything (every key is > 0)
   uint32_t tk = 0u;
   int ck = V;
   if (kk > 1 && kk < V) {
-    uint32_t prefix = 0u, pmask = 0u;
-    int need = kk;  // ranks still to place at or below the digits chosen so far
-    for (int shift = 28; shift >= 0; shift -= 4) {
-      int cnt[16];
-#pragma unroll
-      for (int d = 0; d < 16; ++d) cnt[d] = 0;
-      for (int v = tid; v < V; v += kThreads) {
-        const uint32_t k = logit_key(lr[v]);
-        if ((k & pmask) == prefix) {
-          const uint32_t dg = (k >> shift) & 15u;
-#pragma unroll
-          for (int d = 0; d < 16; ++d) cnt[d] += dg == (uint32_t)d ? 1 : 0;
-        }
-      }
-      const int lane = tid & 63, wave = tid >> 6;
-#pragma unroll
-      for (int d = 0; d < 16; ++d) {
-        const int x = wave_sum_i(cnt[d]);
-        if (lane == 0) s_i[wave * 16 + d] = x;
-      }
-      __syncthreads();
-      int sel = 0;
-      for (int d = 15; d >= 0; --d) {
-        int c = 0;
-        for (int w = 0; w < kWaves; ++w) c += s_i[w * 16 + d];
-        if (c >= need) {
-          sel = d;
-          break;
-        }
-        need -= c;
-      }
-      __syncthreads();
-      prefix |= (uint32_t)sel << shift;
-      pmask |= 15u << shift;
-    }
-    tk = prefix;
-    ck = nth_with_key(tk, need, 0u, V);
+    unsigned long long above = 0ull;
+    radix(one, all, (double)kk, tk, above);  // always reached: kk < V tokens
+    ck = nth_with_key(tk, kk - (int)above, 0u, V);
   }
   auto in_k = [&](uint32_t k, int v) { return k > tk || (k == tk && v <= ck); };
 
-  // ---- top-p cut (tp_key, cp) over the top-k survivors
+  // ---- top-p cut (tpk, cp) over the top-k survivors
   uint32_t tpk = 0u;
   int cp = V;
   if (tp < 1.0f) {
-    double wk = 0.0;
-    for (int v = tid; v < V; v += kThreads) {
-      const uint32_t k = logit_key(lr[v]);
-      if (in_k(k, v)) wk += (double)orow[v];
-    }
-    const double target = (double)tp * block_sum_d(wk, s_d);
-    uint32_t prefix = 0u, pmask = 0u;
-    double above = 0.0;  // weight of the survivors ranked above the digits chosen so far
-    bool found = true;
-    for (int shift = 28; shift >= 0 && found; shift -= 4) {
-      double m[16];
-#pragma unroll
-      for (int d = 0; d < 16; ++d) m[d] = 0.0;
-      for (int v = tid; v < V; v += kThreads) {
-        const uint32_t k = logit_key(lr[v]);
-        if ((k & pmask) == prefix && in_k(k, v)) {
-          const uint32_t dg = (k >> shift) & 15u;
-          const double w = (double)orow[v];
-#pragma unroll
-          for (int d = 0; d < 16; ++d) m[d] += dg == (uint32_t)d ? w : 0.0;
-        }
-      }
-      const int lane = tid & 63, wave = tid >> 6;
-#pragma unroll
-      for (int d = 0; d < 16; ++d) {
-        const double x = wave_sum_d(m[d]);
-        if (lane == 0) s_d[wave * 16 + d] = x;
-      }
-      __syncthreads();
-      int sel = -1;
-      for (int d = 15; d >= 0; --d) {
-        double md = 0.0;
-        for (int w = 0; w < kWaves; ++w) md += s_d[w * 16 + d];
-        if (above + md >= target) {
-          sel = d;
-          break;
-        }
-        above += md;
-      }
-      __syncthreads();
-      if (sel < 0) {
-        found = false;  // rounding never reaches the target: every survivor stays
-      } else {
-        prefix |= (uint32_t)sel << shift;
-        pmask |= 15u << shift;
-      }
-    }
-    if (found) {
-      tpk = prefix;
-      // tokens with key tpk among the survivors, each of weight wt, join in token
-      // order until the cumulative weight reaches the target
+    unsigned long long wk = 0ull;
+    pass([&](int v, KW e) {
+      if (in_k(e.k, v)) wk += fixed(e.w);
+    });
+    wk = block_sum_u64(wk, s_u);
+    const double target = (double)tp * (double)wk;
+    unsigned long long above = 0ull;
+    if (radix([&](KW e) { return fixed(e.w); }, in_k, target, tpk, above)) {
+      // tokens with key tpk among the survivors, each of the same weight, join in
+      // token order until the running total reaches the target
       int na = 0;
-      for (int v = tid; v < V; v += kThreads) {
-        const uint32_t k = logit_key(lr[v]);
-        na += (k == tpk && in_k(k, v)) ? 1 : 0;
-      }
+      pass([&](int v, KW e) { na += (e.k == tpk && in_k(e.k, v)) ? 1 : 0; });
       na = block_sum_i(na, s_i);
-      const double wt = (double)weight(tpk);
-      double acc = above;
-      int n = 0;
-      do {
-        acc += wt;
-        ++n;
-      } while (acc < target && n < na);
+      const unsigned long long ct = fixed(weight(tpk));
+      int n = 1;
+      while ((double)(above + (unsigned long long)n * ct) < target && n < na) ++n;
       cp = nth_with_key(tpk, n, tk, ck);
+    } else {
+      tpk = 0u;  // never reached: every survivor stays
     }
   }
 
@@ -306,15 +383,11 @@ __global__ __launch_bounds__(kThreads) void k_sampling_probs(int T_max, int V, c
     return in_k(k, v) && (k > tpk || (k == tpk && v <= cp)) && (!(mp > 0.0f) || w >= mp || v == tok0);
   };
   double wsum = 0.0;
-  for (int v = tid; v < V; v += kThreads) {
-    const float w = orow[v];
-    if (keep(logit_key(lr[v]), v, w)) wsum += (double)w;
-  }
+  pass([&](int v, KW e) {
+    if (keep(e.k, v, e.w)) wsum += (double)e.w;
+  });
   const double W = block_sum_d(wsum, s_d);
-  for (int v = tid; v < V; v += kThreads) {
-    const float w = orow[v];
-    orow[v] = keep(logit_key(lr[v]), v, w) ? (float)((double)w / W) : 0.0f;
-  }
+  pass([&](int v, KW e) { orow[v] = keep(e.k, v, e.w) ? (float)((double)e.w / W) : 0.0f; });
 }
 
 // --------------------------------------------------------------------------
@@ -366,10 +439,10 @@ __global__ __launch_bounds__(kThreads) void k_tree_accept_sample_draft(
     }
     r_ws = false;
     double zp = 0.0, zq = 0.0;
-    for (int v = tid; v < V; v += kThreads) {
-      zp += (double)p[v];
-      zq += (double)q[v];
-    }
+    row_pass(V, [&](int v) { return float2{p[v], q[v]}; }, [&](int v, float2 e) {
+      zp += (double)e.x;
+      zq += (double)e.y;
+    });
     double ZR = block_sum_d(zp, s_d);
     double ZQ = block_sum_d(zq, s_d);
     int next = -1;
@@ -395,16 +468,19 @@ __global__ __launch_bounds__(kThreads) void k_tree_accept_sample_draft(
         // R <- max(0, R ZQ - Q ZR); without replacement Q loses x's mass
         const bool rm = without_replacement && inside;
         double zr = 0.0, zq2 = 0.0;
-        for (int v = tid; v < V; v += kThreads) {
-          const double qv = removed(v) ? 0.0 : (double)q[v];
-          const double rv = r_ws ? R[v] : (double)p[v];
-          const double a = rv * ZQ;
+        struct RQ {
+          double r;
+          float q;
+        };
+        row_pass(V, [&](int v) { return RQ{r_ws ? R[v] : (double)p[v], q[v]}; }, [&](int v, RQ e) {
+          const double qv = removed(v) ? 0.0 : (double)e.q;
+          const double a = e.r * ZQ;
           const double bq = qv * ZR;
           const double nr = fmax(0.0, a - bq);
           R[v] = nr;
           zr += nr;
           zq2 += (rm && v == x) ? 0.0 : qv;
-        }
+        });
         ZR = block_sum_d(zr, s_d);
         r_ws = true;
         if (rm) {
@@ -430,7 +506,10 @@ __global__ __launch_bounds__(kThreads) void k_tree_accept_sample_draft(
   const int L = (V + kThreads - 1) / kThreads;
   const int c0 = min(V, tid * L), c1 = min(V, c0 + L);
   double cs = 0.0;
-  for (int v = c0; v < c1; ++v) cs += X(v);
+  range_pass(c0, c1, X, [&](int, double x) {
+    cs += x;
+    return false;
+  });
   double lo, hi, total;
   block_scan<double>(cs, s_d, lo, hi, total);
   if (tid == 0) s_pick = -1;
@@ -440,29 +519,32 @@ __global__ __launch_bounds__(kThreads) void k_tree_accept_sample_draft(
     if (lo <= target && target < hi) {
       double cum = lo;
       int pick = -1, last = -1;
-      for (int v = c0; v < c1; ++v) {
-        const double x = X(v);
+      range_pass(c0, c1, X, [&](int v, double x) {
         if (x > 0.0) last = v;
         cum += x;
         if (cum > target) {
           pick = v;
-          break;
+          return true;
         }
-      }
+        return false;
+      });
       s_pick = pick >= 0 ? pick : last;
     }
     __syncthreads();
     if (s_pick < 0) {  // rounding left the target past the total: the last token with mass
       int last = -1;
-      for (int v = c0; v < c1; ++v)
-        if (X(v) > 0.0) last = v;
+      range_pass(c0, c1, X, [&](int v, double x) {
+        if (x > 0.0) last = v;
+        return false;
+      });
       if (last >= 0) atomicMax(&s_pick, last);
       __syncthreads();
     }
   } else {
     // no residual mass: the node's best token (probability desc, token asc)
     unsigned long long best = 0ull;
-    for (int v = tid; v < V; v += kThreads) best = umax64(best, rank_key(prow[v], (uint32_t)v));
+    row_pass(V, [&](int v) { return prow[v]; },
+             [&](int v, float x) { best = umax64(best, rank_key(x, (uint32_t)v)); });
     best = block_max_u64(best, s_u);
     if (tid == 0) s_pick = (int)key_index(best);
     __syncthreads();
@@ -489,9 +571,11 @@ extern "C" int tree_sampling_probs(int B, int T_max, int V, const float* logits,
   const char* a = reinterpret_cast<const char*>(logits);
   const char* c = reinterpret_cast<const char*>(probs);
   if (a < c + n && c < a + n) return TV_EINVAL;  // the output must not overlap the logits
-  hipLaunchKernelGGL(tv::k_sampling_probs, dim3(T_max, B), dim3(tv::kThreads), 0,
-                     reinterpret_cast<hipStream_t>(stream), T_max, V, logits, tree_size, status, temperature, top_k,
-                     top_p, min_p, probs);
+  // rows of up to 8192 tokens stay in registers (more would spill at 1024 threads)
+  const int npt = (V + tv::kThreads - 1) / tv::kThreads;
+  auto k = npt <= 8 ? tv::k_sampling_probs<8> : tv::k_sampling_probs<0>;
+  hipLaunchKernelGGL(k, dim3(T_max, B), dim3(tv::kThreads), 0, reinterpret_cast<hipStream_t>(stream), T_max, V,
+                     logits, tree_size, status, temperature, top_k, top_p, min_p, probs);
   TV_CHECK_LAUNCH();
   return TV_OK;
 }

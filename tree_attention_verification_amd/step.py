@@ -275,6 +275,36 @@ class TreeVerifyStep:
                               self.parents, self.tree_size, self.target_probs, self.uniforms, self.status,
                               self.accept_len, self.accept_path, self.bonus_token, stream)
 
+    def set_sampling_inputs(self, logits: np.ndarray, params, draft_probs=None):
+        """Target logits [B][T_max][V] with the per-request (temperature, top_k, top_p,
+        min_p), and optionally the drafter's distributions [B][T_max][V]; the probability
+        rows that tree_sampling_probs fills are allocated here."""
+        self.target_logits = _t(np.ascontiguousarray(logits, dtype=np.float32), self.device)
+        temp, top_k, top_p, min_p = params
+        self.temperature = _t(np.asarray(temp, np.float32), self.device)
+        self.top_k = _t(np.asarray(top_k, np.int32), self.device)
+        self.top_p = _t(np.asarray(top_p, np.float32), self.device)
+        self.min_p = _t(np.asarray(min_p, np.float32), self.device)
+        self.target_probs = torch.zeros_like(self.target_logits)
+        if draft_probs is not None:
+            self.draft_probs = _t(np.ascontiguousarray(draft_probs, dtype=np.float32), self.device)
+            V = self.target_logits.shape[-1]
+            self.ws_draft = torch.empty(tv.tree_accept_sample_draft_workspace_bytes(self.B, V), dtype=torch.uint8,
+                                        device=self.device)
+
+    def sampling_probs(self, stream=None):
+        """tree_sampling_probs: the target logits filtered into self.target_probs."""
+        tv.tree_sampling_probs(self.B, self.T_max, self.target_logits.shape[-1], self.target_logits, self.tree_size,
+                               self.status, self.temperature, self.top_k, self.top_p, self.min_p, self.target_probs,
+                               stream)
+
+    def accept_sample_draft(self, without_replacement: bool = True, stream=None):
+        """tree_accept_sample_draft: tree rejection sampling with the drafter's q."""
+        tv.tree_accept_sample_draft(self.B, self.T_max, self.dcap, self.target_probs.shape[-1], self.draft_tokens,
+                                    self.parents, self.tree_size, self.target_probs, self.draft_probs, self.uniforms,
+                                    self.status, without_replacement, self.accept_len, self.accept_path,
+                                    self.bonus_token, self.ws_draft, stream)
+
     def set_target_predict(self, tp: np.ndarray):
         self.target_predict.copy_(torch.from_numpy(np.ascontiguousarray(tp.astype(np.int32))))
 
