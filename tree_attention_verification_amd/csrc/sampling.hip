@@ -179,7 +179,7 @@ __global__ __launch_bounds__(kThreads) void k_sampling_probs(int T_max, int V, c
   __shared__ int s_i[kWaves * 16];
   __shared__ unsigned long long s_u[kWaves];
   __shared__ unsigned long long s_hist[kWaves * 256];
-  __shared__ unsigned long long s_abv;
+  __shared__ unsigned long long s_abv, s_bin;
   __shared__ int s_pick, s_sel;
 
   // the first-ranked token
@@ -231,39 +231,86 @@ __global__ __launch_bounds__(kThreads) void k_sampling_probs(int T_max, int V, c
       row_pass(V, ld_kw, body);
     }
   };
+  // weight in units of 2^-32 (w <= 1, so at most 2^32; a row's total stays below 2^51)
+  auto fixed = [](float w) { return (unsigned long long)rint((double)w * 4294967296.0); };
+  unsigned long long w_all = 0ull;  // this thread's total weight, units of 2^-32
   if constexpr (NPT > 0) {
 #pragma unroll
-    for (int j = 0; j < NPT; ++j) reg[j].w = weight(reg[j].k);
+    for (int j = 0; j < NPT; ++j) {
+      reg[j].w = weight(reg[j].k);
+      if (tid + j * kThreads < V) w_all += fixed(reg[j].w);
+    }
   } else {
-    row_pass(V, ld_l, [&](int v, float x) { orow[v] = weight(logit_key(x)); });
+    row_pass(V, ld_l, [&](int v, float x) {
+      const float w = weight(logit_key(x));
+      orow[v] = w;
+      w_all += fixed(w);
+    });
   }
 
-  // the n-th token (token order) with key t that satisfies pred, n >= 1: each
-  // thread counts its contiguous range, a scan finds the range holding it
-  const int L = (V + kThreads - 1) / kThreads;
-  const int c0 = min(V, tid * L), c1 = min(V, c0 + L);
-  auto nth_with_key = [&](uint32_t t, int n, uint32_t tk, int ck) -> int {
-    int c = 0;
-    range_pass(c0, c1, ld_k, [&](int v, uint32_t k) {
-      c += (k == t && (k > tk || v <= ck)) ? 1 : 0;
-      return false;
-    });
+  const int lane = tid & 63, wave = tid >> 6;
+  // The n-th token (token order, n >= 1) with key t inside the top-k cut (tk, ck),
+  // in one coalesced pass: for each slice of kThreads consecutive tokens, every
+  // wavefront's ballot of its matching tokens goes to LDS, slice-major, so the
+  // entries are in token order; the first wavefront then finds the entry holding
+  // the n-th match (64 entries per lane at most, a scan over the lanes) and the
+  // bit inside it.  With `mass`, also returns the total weight (units of 2^-32) of
+  // the tokens with key > t (all inside the cut, since t >= tk).
+  const int nsl = (V + kThreads - 1) / kThreads;  // <= 256 slices, <= 4096 entries
+  auto nth_with_key = [&](uint32_t t, int n, uint32_t tk, int ck, bool mass, unsigned long long& mass_above) -> int {
+    unsigned long long ma = 0ull;
+    auto body = [&](int j, uint32_t k, float w) __attribute__((always_inline)) {
+      const int v = j * kThreads + tid;
+      const bool f = v < V && k == t && (k > tk || v <= ck);
+      const unsigned long long m = __ballot(f);
+      if (lane == 0) s_hist[j * kWaves + wave] = m;
+      if (mass && v < V && k > t) ma += fixed(w);
+    };
     if (tid == 0) s_pick = V;
-    int lo, hi, tot;
-    block_scan<int>(c, s_i, lo, hi, tot);
-    if (lo < n && n <= hi) {
-      int r = n - lo;
-      range_pass(c0, c1, ld_k, [&](int v, uint32_t k) {
-        if (k == t && (k > tk || v <= ck) && --r == 0) {
-          s_pick = v;
-          return true;
+    if constexpr (NPT > 0) {
+#pragma unroll
+      for (int j = 0; j < NPT; ++j)
+        if (j < nsl) body(j, reg[j].k, reg[j].w);
+    } else {
+      for (int j0 = 0; j0 < nsl; j0 += kNB) {
+        KW x[kNB];
+#pragma unroll
+        for (int jj = 0; jj < kNB; ++jj) x[jj] = ld_kw(min((j0 + jj) * kThreads + tid, V - 1));
+#pragma unroll
+        for (int jj = 0; jj < kNB; ++jj)
+          if (j0 + jj < nsl) body(j0 + jj, x[jj].k, x[jj].w);
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const int ne = nsl * kWaves;
+      const int per = (ne + 63) / 64;
+      const int e0 = min(ne, lane * per), e1 = min(ne, e0 + per);
+      int c = 0;
+      for (int e = e0; e < e1; ++e) c += __popcll(s_hist[e]);
+      int incl = c;
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
+      }
+      if (incl - c < n && n <= incl) {
+        int r = n - (incl - c);
+        for (int e = e0; e < e1; ++e) {
+          unsigned long long mm = s_hist[e];
+          const int pc = __popcll(mm);
+          if (r <= pc) {
+            for (int q = 1; q < r; ++q) mm &= mm - 1;
+            s_pick = (e / kWaves) * kThreads + (e % kWaves) * 64 + (__ffsll((long long)mm) - 1);
+            break;
+          }
+          r -= pc;
         }
-        return false;
-      });
+      }
     }
     __syncthreads();
     const int res = s_pick;
     __syncthreads();
+    mass_above = mass ? block_sum_u64(ma, s_u) : 0ull;
     return res;
   };
 
@@ -276,8 +323,9 @@ __global__ __launch_bounds__(kThreads) void k_sampling_probs(int T_max, int V, c
   // order of the additions does not matter), then the first wavefront places the
   // target among the bins (four bins per lane, a suffix sum over the lanes).
   // Returns false if the target is never reached.
-  const int lane = tid & 63, wave = tid >> 6;
-  auto radix = [&](auto val, auto pred, double target, uint32_t& t_out, unsigned long long& above_out) -> bool {
+  auto radix = [&](auto val, auto pred, double target, uint32_t& t_out, unsigned long long& above_out,
+                   unsigned long long& bin_out) -> bool {
+    unsigned long long bin = 0ull;
     uint32_t prefix = 0u, pmask = 0u;
     unsigned long long above = 0ull;
     for (int shift = 24; shift >= 0; shift -= 8) {
@@ -305,11 +353,12 @@ __global__ __launch_bounds__(kThreads) void k_sampling_probs(int T_max, int V, c
         }
         unsigned long long run = above + (suf - g);
         int cand = -1;
-        unsigned long long cabove = 0ull;
+        unsigned long long cabove = 0ull, cbin = 0ull;
         for (int j = 3; j >= 0; --j) {
           if ((double)(run + m[j]) >= target) {
             cand = 4 * lane + j;
             cabove = run;
+            cbin = m[j];
             break;
           }
           run += m[j];
@@ -321,12 +370,14 @@ __global__ __launch_bounds__(kThreads) void k_sampling_probs(int T_max, int V, c
           if (lane == L) {
             s_sel = cand;
             s_abv = cabove;
+            s_bin = cbin;
           }
         }
       }
       __syncthreads();
       const int sel = s_sel;
       const unsigned long long nab = s_abv;
+      bin = s_bin;
       __syncthreads();
       if (sel < 0) return false;
       prefix |= (uint32_t)sel << shift;
@@ -335,44 +386,41 @@ __global__ __launch_bounds__(kThreads) void k_sampling_probs(int T_max, int V, c
     }
     t_out = prefix;
     above_out = above;
+    bin_out = bin;
     return true;
   };
   auto all = [](uint32_t, int) { return true; };
   auto one = [](KW) { return 1ull; };
-  // weight in units of 2^-32 (w <= 1, so at most 2^32; a row's total stays below 2^51)
-  auto fixed = [](float w) { return (unsigned long long)rint((double)w * 4294967296.0); };
 
   // ---- top-k cut (tk, ck); the default keeps everything (every key is > 0)
   uint32_t tk = 0u;
   int ck = V;
+  const bool with_p = tp < 1.0f;
+  unsigned long long wk = block_sum_u64(w_all, s_u);  // the survivors' total weight (units of 2^-32)
   if (kk > 1 && kk < V) {
-    unsigned long long above = 0ull;
-    radix(one, all, (double)kk, tk, above);  // always reached: kk < V tokens
-    ck = nth_with_key(tk, kk - (int)above, 0u, V);
+    unsigned long long above = 0ull, bin = 0ull, ma = 0ull;
+    radix(one, all, (double)kk, tk, above, bin);  // always reached: kk < V tokens
+    const int need = kk - (int)above;
+    ck = nth_with_key(tk, need, 0u, V, with_p, ma);
+    wk = ma + (unsigned long long)need * fixed(weight(tk));
   }
   auto in_k = [&](uint32_t k, int v) { return k > tk || (k == tk && v <= ck); };
 
   // ---- top-p cut (tpk, cp) over the top-k survivors
   uint32_t tpk = 0u;
   int cp = V;
-  if (tp < 1.0f) {
-    unsigned long long wk = 0ull;
-    pass([&](int v, KW e) {
-      if (in_k(e.k, v)) wk += fixed(e.w);
-    });
-    wk = block_sum_u64(wk, s_u);
+  if (with_p) {
     const double target = (double)tp * (double)wk;
-    unsigned long long above = 0ull;
-    if (radix([&](KW e) { return fixed(e.w); }, in_k, target, tpk, above)) {
-      // tokens with key tpk among the survivors, each of the same weight, join in
-      // token order until the running total reaches the target
-      int na = 0;
-      pass([&](int v, KW e) { na += (e.k == tpk && in_k(e.k, v)) ? 1 : 0; });
-      na = block_sum_i(na, s_i);
+    unsigned long long above = 0ull, bin = 0ull, unused = 0ull;
+    if (radix([&](KW e) { return fixed(e.w); }, in_k, target, tpk, above, bin)) {
+      // tokens with key tpk among the survivors, each of the same weight ct (so the
+      // last bin holds na ct), join in token order until the running total reaches
+      // the target
       const unsigned long long ct = fixed(weight(tpk));
+      const int na = (int)(bin / ct);
       int n = 1;
       while ((double)(above + (unsigned long long)n * ct) < target && n < na) ++n;
-      cp = nth_with_key(tpk, n, tk, ck);
+      cp = nth_with_key(tpk, n, tk, ck, false, unused);
     } else {
       tpk = 0u;  // never reached: every survivor stays
     }
