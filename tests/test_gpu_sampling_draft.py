@@ -172,3 +172,23 @@ def test_draft_sampling_edge_cases_and_workspace_reuse():
         compare(tokens, parents, sizes, probs, q, uni, status, w.dcap, wr, ws)
     for dcap in (0, 1, 3):                           # depth caps (tree validated with the workload's cap)
         compare(tokens, parents, sizes, probs, q, uni, status, dcap, True, ws)
+
+
+def test_draft_sampling_largest_vocabulary_and_tiny_trees():
+    V = 262144                                      # the call's limit (a 32 KB bitmap of removed tokens)
+    w = gen.make_custom(cfg_id=1750, B=2, mode="given", given_sizes=[12, 1], given_depth=3, V=V, P=4, T_max=16,
+                        dcap=5, accept_prob=0.6)
+    for wr in (True, False):
+        compare(*given_case(w), w.dcap, wr)
+    # V = 1: every token is token 0, so every child can be accepted
+    rng = np.random.default_rng(17)
+    parents = np.array([[-1, 0, 0, 1], [-1, 0, -1, -1], [-1, -1, -1, -1]], np.int32)
+    tokens = np.where(parents >= 0, 0, -1).astype(np.int32)
+    tokens[:, 0] = 0
+    sizes = np.array([4, 2, 1], np.int32)
+    probs = rng.random((3, 4, 1)).astype(np.float32)
+    probs[1, 0, 0] = 0.0                             # no mass: the child is rejected, the correction is token 0
+    q = rng.random((3, 4, 1)).astype(np.float32)
+    uni = rng.random((3, 4)).astype(np.float32)
+    for wr in (True, False):
+        compare(tokens, parents, sizes, probs, q, uni, np.zeros(3, np.int32), 3, wr)

@@ -135,3 +135,24 @@ def test_filter_then_target_only_sampling(cfg):
                                 st.dcap)
     for k in ("accept_len", "accept_path", "bonus_token"):
         np.testing.assert_array_equal(got[k], ref[k], err_msg=k)
+
+
+@pytest.mark.parametrize("V", [1, 2, 3])
+def test_filters_tiny_vocabularies(V):
+    B = 6
+    lg = np.random.default_rng(V).normal(0, 1, (B, 1, V)).astype(np.float32)
+    lg[5, 0, :] = 0.5                               # all equal
+    temp = np.array([1.0, 0.5, 1.0, 1.0, 2.0, 1.0], np.float32)
+    top_k = np.array([0, max(V - 1, 0), 1, V, 2, 0], np.int32)
+    top_p = np.array([1.0, 0.5, 1.0, 1e-6, 0.9, 0.6], np.float32)
+    min_p = np.array([0.0, 0.0, 0.5, 0.0, 0.9, 0.0], np.float32)
+    run_filter(lg, np.ones(B, np.int32), None, (temp, top_k, top_p, min_p))
+
+
+def test_filters_largest_vocabulary():
+    V = 262144                                      # the call's limit: 256 slices of 1024 tokens
+    w = gen.make_custom(cfg_id=1640, B=2, mode="given", given_sizes=[2, 1], V=V, P=4, T_max=2, dcap=1)
+    lg = gen.synthetic_target_logits(w, w.given_size, tie_step=0.25)
+    params = (np.array([1.0, 0.7], np.float32), np.array([1000, 0], np.int32), np.array([0.9, 0.95], np.float32),
+              np.array([0.0, 0.001], np.float32))
+    run_filter(lg, w.given_size, None, params)
