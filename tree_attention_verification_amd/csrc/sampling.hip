@@ -30,10 +30,6 @@ __device__ __forceinline__ double wave_sum_d(double v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
 }
-__device__ __forceinline__ int wave_sum_i(int v) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
 
 // sum over the workgroup; every thread gets the same value (s: kWaves slots)
 __device__ __forceinline__ double block_sum_d(double v, double* s) {
@@ -52,16 +48,6 @@ __device__ __forceinline__ unsigned long long block_sum_u64(unsigned long long v
   if (lane == 0) s[wave] = v;
   __syncthreads();
   unsigned long long t = 0ull;
-  for (int w = 0; w < kWaves; ++w) t += s[w];
-  __syncthreads();
-  return t;
-}
-__device__ __forceinline__ int block_sum_i(int v, int* s) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  v = wave_sum_i(v);
-  if (lane == 0) s[wave] = v;
-  __syncthreads();
-  int t = 0;
   for (int w = 0; w < kWaves; ++w) t += s[w];
   __syncthreads();
   return t;
@@ -176,7 +162,6 @@ __global__ __launch_bounds__(kThreads) void k_sampling_probs(int T_max, int V, c
   const float* lr = logits + ((long long)b * T_max + i) * V;
   float* orow = probs + ((long long)b * T_max + i) * V;
   __shared__ double s_d[kWaves * 16];
-  __shared__ int s_i[kWaves * 16];
   __shared__ unsigned long long s_u[kWaves];
   __shared__ unsigned long long s_hist[kWaves * 256];
   __shared__ unsigned long long s_abv, s_bin;
@@ -220,7 +205,6 @@ __global__ __launch_bounds__(kThreads) void k_sampling_probs(int T_max, int V, c
   // (NPT = 0: the weights go to the output row, and each thread re-reads only the
   // weights it wrote: the same v in every row pass)
   auto ld_kw = [&](int v) { return KW{logit_key(lr[v]), orow[v]}; };
-  auto ld_k = [&](int v) { return logit_key(lr[v]); };
   // one pass over the row: body(v, KW) for this thread's tokens in increasing v
   auto pass = [&](auto body) __attribute__((always_inline)) {
     if constexpr (NPT > 0) {
@@ -487,7 +471,7 @@ __global__ __launch_bounds__(kThreads) void k_tree_accept_sample_draft(
     }
     r_ws = false;
     double zp = 0.0, zq = 0.0;
-    row_pass(V, [&](int v) { return float2{p[v], q[v]}; }, [&](int v, float2 e) {
+    row_pass(V, [&](int v) { return float2{p[v], q[v]}; }, [&](int, float2 e) {
       zp += (double)e.x;
       zq += (double)e.y;
     });
