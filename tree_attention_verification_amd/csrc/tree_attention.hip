@@ -667,8 +667,9 @@ __global__ __launch_bounds__(NW * 64, (NSTAGE == 2 && NW == 4) ? 2 : 1) void k_a
 // Merge split partials.  Split s left its normalised output o_s (fp16), its
 // running max m_s (log2 domain) and its row sum l_s; the result is
 // sum_s w_s o_s / sum_s w_s with w_s = exp2(m_s - max m) l_s.  Splits are read
-// sixteen at a time (all loads in flight together) and merged online.
-template <int D>
+// BATCH at a time (all loads in flight together; BATCH >= the split count up to
+// 16, so a call with few splits issues no redundant loads) and merged online.
+template <int D, int BATCH>
 __global__ __launch_bounds__(256) void k_attn_combine(const _Float16* __restrict__ ws_o,
                                                       const float* __restrict__ ws_ml,
                                                       const int* __restrict__ prefix_len,
@@ -679,7 +680,6 @@ __global__ __launch_bounds__(256) void k_attn_combine(const _Float16* __restrict
   typedef _Float16 h8 __attribute__((ext_vector_type(8)));
   constexpr int TPR = D / 8;          // threads per row, 8 outputs each
   constexpr int RPB = 256 / TPR;      // rows per block
-  constexpr int BATCH = 16;
   const int bg = blockIdx.x;
   const int b = bg / Hkv, g = bg % Hkv;
   const int rep = Hq / Hkv;
@@ -916,12 +916,19 @@ int attention_impl(int dtype, int B, int T_max, int Hq, int Hkv, int d, const vo
   if (p.n_split > 1) {
     const int rpb = 256 / (d / 8);
     dim3 grid(B * Hkv, (unsigned)((p.m_pad + rpb - 1) / rpb));
-    if (d == 128)
-      hipLaunchKernelGGL(k_attn_combine<128>, grid, dim3(256), 0, s, ws_o, ws_ml, prefix_len, tree_size, status, S_cap,
-                         T_max, Hq, Hkv, p.n_split, p.chunk_keys, p.m_pad, p.rel, (uint16_t*)O);
-    else
-      hipLaunchKernelGGL(k_attn_combine<64>, grid, dim3(256), 0, s, ws_o, ws_ml, prefix_len, tree_size, status, S_cap,
-                         T_max, Hq, Hkv, p.n_split, p.chunk_keys, p.m_pad, p.rel, (uint16_t*)O);
+#define TV_COMBINE(DD, BB)                                                                                         \
+  hipLaunchKernelGGL((k_attn_combine<DD, BB>), grid, dim3(256), 0, s, ws_o, ws_ml, prefix_len, tree_size, status,   \
+                     S_cap, T_max, Hq, Hkv, p.n_split, p.chunk_keys, p.m_pad, p.rel, (uint16_t*)O)
+    if (d == 128) {
+      if (p.n_split <= 4) TV_COMBINE(128, 4);
+      else if (p.n_split <= 8) TV_COMBINE(128, 8);
+      else TV_COMBINE(128, 16);
+    } else {
+      if (p.n_split <= 4) TV_COMBINE(64, 4);
+      else if (p.n_split <= 8) TV_COMBINE(64, 8);
+      else TV_COMBINE(64, 16);
+    }
+#undef TV_COMBINE
     TV_CHECK_LAUNCH();
   }
   return TV_OK;
