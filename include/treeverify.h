@@ -28,11 +28,14 @@
  *         evaluate_posterior.
  *   [HB]  AI-infra handbook, "Advanced speculative decoding: tree drafts and
  *         EAGLE" -- tree_spec.py (forward_with_mask, tree_mask, depths,
- *         build_draft_tree, tree_speculative_generate) and the KV note after it.
+ *         build_draft_tree, tree_speculative_generate), the KV note after it,
+ *         and the exercise "trees when sampling".
  *   [TRT] "TensorRT-LLM source dissection (22): EAGLE-3 one-model drafter" --
  *         section "dynamic draft tree": the three ledgers (parent buffer, packed
  *         mask [bs, N, ceil(N/32)], position offsets), the tree-build kernel,
- *         greedy verification on the child/sibling lists, KV relocation.
+ *         greedy verification on the child/sibling lists, the non-greedy path
+ *         (target logits filtered per request, target-only rejection sampling),
+ *         KV relocation.
  *
  * Conventions (all calls):
  *   - Every pointer is a DEVICE pointer unless marked "host".  The caller owns
