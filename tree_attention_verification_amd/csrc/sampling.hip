@@ -165,7 +165,7 @@ __global__ __launch_bounds__(kThreads) void k_sampling_probs(int T_max, int V, c
   __shared__ unsigned long long s_u[kWaves];
   __shared__ unsigned long long s_hist[kWaves * 256];
   __shared__ unsigned long long s_abv, s_bin;
-  __shared__ int s_pick, s_sel;
+  __shared__ int s_pick, s_sel, s_cnt;
 
   // the first-ranked token
   struct KW {
@@ -393,7 +393,51 @@ __global__ __launch_bounds__(kThreads) void k_sampling_probs(int T_max, int V, c
   // ---- top-p cut (tpk, cp) over the top-k survivors
   uint32_t tpk = 0u;
   int cp = V;
-  if (with_p) {
+  if (with_p && kk > 1 && kk <= kThreads) {
+    // at most kThreads survivors: gathered into LDS as 64-bit rank keys (key,
+    // then token ascending; the order of the appends does not matter), sorted
+    // descending by a bitonic network, then one exact prefix sum of their weights
+    // in rank order finds the cut
+    unsigned long long* s_list = s_hist;  // kThreads entries
+    if (tid == 0) s_cnt = 0;
+    __syncthreads();
+    pass([&](int v, KW e) {
+      if (in_k(e.k, v)) s_list[atomicAdd(&s_cnt, 1)] = rank_key(key_float(e.k), (uint32_t)v);
+    });
+    __syncthreads();
+    const int n = s_cnt;  // == kk
+    if (tid >= n) s_list[tid] = 0ull;
+    __syncthreads();
+    for (int k2 = 2; k2 <= kThreads; k2 <<= 1) {
+      for (int j = k2 >> 1; j > 0; j >>= 1) {
+        const int ixj = tid ^ j;
+        if (ixj > tid) {
+          const unsigned long long a = s_list[tid], c = s_list[ixj];
+          if (((tid & k2) == 0) == (a < c)) {
+            s_list[tid] = c;
+            s_list[ixj] = a;
+          }
+        }
+        __syncthreads();
+      }
+    }
+    const unsigned long long mine = s_list[tid];
+    const unsigned long long x = tid < n ? fixed(weight((uint32_t)(mine >> 32))) : 0ull;
+    unsigned long long lo, hi, tot;
+    block_scan<unsigned long long>(x, s_u, lo, hi, tot);
+    const double target = (double)tp * (double)tot;
+    if (tid == 0) s_pick = n;
+    __syncthreads();
+    if (tid < n && (double)hi >= target) atomicMin(&s_pick, tid);
+    __syncthreads();
+    const int cut = s_pick;  // the last kept rank
+    if (cut < n) {
+      const unsigned long long kc = s_list[cut];
+      tpk = (uint32_t)(kc >> 32);
+      cp = (int)key_index(kc);
+    }
+    __syncthreads();
+  } else if (with_p) {
     const double target = (double)tp * (double)wk;
     unsigned long long above = 0ull, bin = 0ull, unused = 0ull;
     if (radix([&](KW e) { return fixed(e.w); }, in_k, target, tpk, above, bin)) {
