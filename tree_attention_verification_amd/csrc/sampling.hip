@@ -402,10 +402,13 @@ __global__ __launch_bounds__(kThreads) void k_sampling_probs(int T_max, int V, c
     if (tid == 0) s_cnt = 0;
     __syncthreads();
     pass([&](int v, KW e) {
-      if (in_k(e.k, v)) s_list[atomicAdd(&s_cnt, 1)] = rank_key(key_float(e.k), (uint32_t)v);
+      if (in_k(e.k, v)) {
+        const int pos = atomicAdd(&s_cnt, 1);  // < kk by construction of the cut
+        if (pos < kThreads) s_list[pos] = rank_key(key_float(e.k), (uint32_t)v);
+      }
     });
     __syncthreads();
-    const int n = s_cnt;  // == kk
+    const int n = min(s_cnt, kThreads);  // == kk
     if (tid >= n) s_list[tid] = 0ull;
     __syncthreads();
     for (int k2 = 2; k2 <= kThreads; k2 <<= 1) {
