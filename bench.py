@@ -413,7 +413,10 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
-        "data": "synthetic (seeded draft log-probs, Q/K/V and target argmax; no weights)",
+        "data": "synthetic (seeded draft log-probs, Q/K/V and target " +
+                ({"probs": "distributions", "logits": "logits and per-request sampling parameters",
+                  "draft": "logits, per-request sampling parameters and drafter distributions"}[args.sampling_from]
+                 if args.sampling else "argmax") + "; no weights)",
         "config": {"workload": workload, "batch": w.B, "prefix_len": [int(x) for x in w.prefix_len[:4]] +
                    (["..."] if w.B > 4 else []), "tree_nodes_per_step": nodes, "top_k": w.K, "depth": w.D,
                    "total_tokens": w.total_tokens, "Hq": w.Hq, "Hkv": w.Hkv, "head_dim": w.d, "vocab": w.V,
