@@ -31,24 +31,26 @@ __device__ __forceinline__ double wave_sum_d(double v) {
   return v;
 }
 
-// sum over the workgroup; every thread gets the same value (s: kWaves slots)
+// sum over the workgroup; every thread gets the same value (s: (NT / 64) slots)
+template <int NT = kThreads>
 __device__ __forceinline__ double block_sum_d(double v, double* s) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   v = wave_sum_d(v);
   if (lane == 0) s[wave] = v;
   __syncthreads();
   double t = 0.0;
-  for (int w = 0; w < kWaves; ++w) t += s[w];
+  for (int w = 0; w < (NT / 64); ++w) t += s[w];
   __syncthreads();
   return t;
 }
+template <int NT = kThreads>
 __device__ __forceinline__ unsigned long long block_sum_u64(unsigned long long v, unsigned long long* s) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   if (lane == 0) s[wave] = v;
   __syncthreads();
   unsigned long long t = 0ull;
-  for (int w = 0; w < kWaves; ++w) t += s[w];
+  for (int w = 0; w < (NT / 64); ++w) t += s[w];
   __syncthreads();
   return t;
 }
@@ -56,7 +58,7 @@ __device__ __forceinline__ unsigned long long block_sum_u64(unsigned long long v
 // Exclusive / inclusive prefix of per-thread values in thread order: lo = sum of
 // the earlier threads' values, hi = lo + own.  hi of thread t and lo of thread
 // t + 1 are the same stored number.  total = sum of all.
-template <typename T>
+template <typename T, int NT = kThreads>
 __device__ __forceinline__ void block_scan(T v, T* s, T& lo, T& hi, T& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   T incl = v;
@@ -67,7 +69,7 @@ __device__ __forceinline__ void block_scan(T v, T* s, T& lo, T& hi, T& total) {
   if (lane == 63) s[wave] = incl;
   __syncthreads();
   T off = T(0), tot = T(0);
-  for (int w = 0; w < kWaves; ++w) {
+  for (int w = 0; w < (NT / 64); ++w) {
     if (w < wave) off = off + s[w];
     tot = tot + s[w];
   }
@@ -78,31 +80,32 @@ __device__ __forceinline__ void block_scan(T v, T* s, T& lo, T& hi, T& total) {
   total = tot;
 }
 
+template <int NT = kThreads>
 __device__ __forceinline__ unsigned long long block_max_u64(unsigned long long v, unsigned long long* s) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   v = wave_max_u64(v);
   if (lane == 0) s[wave] = v;
   __syncthreads();
   unsigned long long t = 0ull;
-  for (int w = 0; w < kWaves; ++w) t = umax64(t, s[w]);
+  for (int w = 0; w < (NT / 64); ++w) t = umax64(t, s[w]);
   __syncthreads();
   return t;
 }
 
-// Visits v = threadIdx.x + j kThreads (j = 0, 1, ...) in increasing v, with the
+// Visits v = threadIdx.x + j NT (j = 0, 1, ...) in increasing v, with the
 // loads of NB visits issued together (one memory round trip per NB entries);
 // indices past the row are clamped for the load and skipped for the body.
 constexpr int kNB = 8;
-template <class Load, class Body>
+template <int NT = kThreads, class Load, class Body>
 __device__ __forceinline__ void row_pass(int V, Load load, Body body) {
   using T = decltype(load(0));
-  for (int base = threadIdx.x; base < V; base += kNB * kThreads) {
+  for (int base = threadIdx.x; base < V; base += kNB * NT) {
     T x[kNB];
 #pragma unroll
-    for (int j = 0; j < kNB; ++j) x[j] = load(min(base + j * kThreads, V - 1));
+    for (int j = 0; j < kNB; ++j) x[j] = load(min(base + j * NT, V - 1));
 #pragma unroll
     for (int j = 0; j < kNB; ++j)
-      if (base + j * kThreads < V) body(base + j * kThreads, x[j]);
+      if (base + j * NT < V) body(base + j * NT, x[j]);
   }
 }
 // The same over a contiguous range [c0, c1), in order; body returns true to stop.
@@ -142,10 +145,10 @@ __device__ __forceinline__ float key_float(uint32_t k) {
 // equal keys is the n-th of them in token order, found by a scan over contiguous
 // token ranges.
 // --------------------------------------------------------------------------
-// NPT > 0: V <= NPT kThreads and every thread keeps its NPT (key, weight) pairs in
+// NPT > 0: V <= NPT NT and every thread keeps its NPT (key, weight) pairs in
 // registers after the first read; NPT = 0: the row is re-read on every pass.
-template <int NPT>
-__global__ __launch_bounds__(kThreads) void k_sampling_probs(int T_max, int V, const float* __restrict__ logits,
+template <int NT, int NPT>
+__global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const float* __restrict__ logits,
                                                              const int* __restrict__ tree_size,
                                                              const int* __restrict__ status,
                                                              const float* __restrict__ temperature,
@@ -154,6 +157,7 @@ __global__ __launch_bounds__(kThreads) void k_sampling_probs(int T_max, int V, c
                                                              const float* __restrict__ min_p,
                                                              float* __restrict__ probs) {
 #pragma clang fp contract(off)
+  constexpr int NW = NT / 64;  // wavefronts
   const int i = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x;
   int T = tree_size[b];
@@ -161,9 +165,9 @@ __global__ __launch_bounds__(kThreads) void k_sampling_probs(int T_max, int V, c
   if (i >= T) return;
   const float* lr = logits + ((long long)b * T_max + i) * V;
   float* orow = probs + ((long long)b * T_max + i) * V;
-  __shared__ double s_d[kWaves * 16];
-  __shared__ unsigned long long s_u[kWaves];
-  __shared__ unsigned long long s_hist[kWaves * 256];
+  __shared__ double s_d[NW * 16];
+  __shared__ unsigned long long s_u[NW];
+  __shared__ unsigned long long s_hist[4096];  // radix bins, ballot entries (V / 64), or the survivor list
   __shared__ unsigned long long s_abv, s_bin;
   __shared__ int s_pick, s_sel, s_cnt;
 
@@ -178,16 +182,16 @@ __global__ __launch_bounds__(kThreads) void k_sampling_probs(int T_max, int V, c
   if constexpr (NPT > 0) {
     float x[NPT];
 #pragma unroll
-    for (int j = 0; j < NPT; ++j) x[j] = lr[min(tid + j * kThreads, V - 1)];
+    for (int j = 0; j < NPT; ++j) x[j] = lr[min(tid + j * NT, V - 1)];
 #pragma unroll
     for (int j = 0; j < NPT; ++j) {
       reg[j].k = logit_key(x[j]);
-      if (tid + j * kThreads < V) best = umax64(best, rank_key(clean_logit(x[j]), (uint32_t)(tid + j * kThreads)));
+      if (tid + j * NT < V) best = umax64(best, rank_key(clean_logit(x[j]), (uint32_t)(tid + j * NT)));
     }
   } else {
-    row_pass(V, ld_l, [&](int v, float x) { best = umax64(best, rank_key(clean_logit(x), (uint32_t)v)); });
+    row_pass<NT>(V, ld_l, [&](int v, float x) { best = umax64(best, rank_key(clean_logit(x), (uint32_t)v)); });
   }
-  best = block_max_u64(best, s_u);
+  best = block_max_u64<NT>(best, s_u);
   const uint32_t kmax = (uint32_t)(best >> 32);
   const int tok0 = (int)key_index(best);
   const float tau = temperature[b];
@@ -195,7 +199,7 @@ __global__ __launch_bounds__(kThreads) void k_sampling_probs(int T_max, int V, c
   const float tp = top_p[b], mp = min_p[b];
   // greedy (NaN temperature included); top_k = 1 and top_p <= 0 keep the first token alone
   if (!(tau > 0.0f) || kk == 1 || tp <= 0.0f) {
-    for (int v = tid; v < V; v += kThreads) orow[v] = v == tok0 ? 1.0f : 0.0f;
+    for (int v = tid; v < V; v += NT) orow[v] = v == tok0 ? 1.0f : 0.0f;
     return;
   }
   const double dmax = (double)key_float(kmax), dtau = (double)tau;
@@ -210,9 +214,9 @@ __global__ __launch_bounds__(kThreads) void k_sampling_probs(int T_max, int V, c
     if constexpr (NPT > 0) {
 #pragma unroll
       for (int j = 0; j < NPT; ++j)
-        if (tid + j * kThreads < V) body(tid + j * kThreads, reg[j]);
+        if (tid + j * NT < V) body(tid + j * NT, reg[j]);
     } else {
-      row_pass(V, ld_kw, body);
+      row_pass<NT>(V, ld_kw, body);
     }
   };
   // weight in units of 2^-32 (w <= 1, so at most 2^32; a row's total stays below 2^51)
@@ -222,10 +226,10 @@ __global__ __launch_bounds__(kThreads) void k_sampling_probs(int T_max, int V, c
 #pragma unroll
     for (int j = 0; j < NPT; ++j) {
       reg[j].w = weight(reg[j].k);
-      if (tid + j * kThreads < V) w_all += fixed(reg[j].w);
+      if (tid + j * NT < V) w_all += fixed(reg[j].w);
     }
   } else {
-    row_pass(V, ld_l, [&](int v, float x) {
+    row_pass<NT>(V, ld_l, [&](int v, float x) {
       const float w = weight(logit_key(x));
       orow[v] = w;
       w_all += fixed(w);
@@ -234,20 +238,20 @@ __global__ __launch_bounds__(kThreads) void k_sampling_probs(int T_max, int V, c
 
   const int lane = tid & 63, wave = tid >> 6;
   // The n-th token (token order, n >= 1) with key t inside the top-k cut (tk, ck),
-  // in one coalesced pass: for each slice of kThreads consecutive tokens, every
+  // in one coalesced pass: for each slice of NT consecutive tokens, every
   // wavefront's ballot of its matching tokens goes to LDS, slice-major, so the
   // entries are in token order; the first wavefront then finds the entry holding
   // the n-th match (64 entries per lane at most, a scan over the lanes) and the
   // bit inside it.  With `mass`, also returns the total weight (units of 2^-32) of
   // the tokens with key > t (all inside the cut, since t >= tk).
-  const int nsl = (V + kThreads - 1) / kThreads;  // <= 256 slices, <= 4096 entries
+  const int nsl = (V + NT - 1) / NT;  // <= 256 slices, <= 4096 entries
   auto nth_with_key = [&](uint32_t t, int n, uint32_t tk, int ck, bool mass, unsigned long long& mass_above) -> int {
     unsigned long long ma = 0ull;
     auto body = [&](int j, uint32_t k, float w) __attribute__((always_inline)) {
-      const int v = j * kThreads + tid;
+      const int v = j * NT + tid;
       const bool f = v < V && k == t && (k > tk || v <= ck);
       const unsigned long long m = __ballot(f);
-      if (lane == 0) s_hist[j * kWaves + wave] = m;
+      if (lane == 0) s_hist[j * NW + wave] = m;
       if (mass && v < V && k > t) ma += fixed(w);
     };
     if (tid == 0) s_pick = V;
@@ -259,7 +263,7 @@ __global__ __launch_bounds__(kThreads) void k_sampling_probs(int T_max, int V, c
       for (int j0 = 0; j0 < nsl; j0 += kNB) {
         KW x[kNB];
 #pragma unroll
-        for (int jj = 0; jj < kNB; ++jj) x[jj] = ld_kw(min((j0 + jj) * kThreads + tid, V - 1));
+        for (int jj = 0; jj < kNB; ++jj) x[jj] = ld_kw(min((j0 + jj) * NT + tid, V - 1));
 #pragma unroll
         for (int jj = 0; jj < kNB; ++jj)
           if (j0 + jj < nsl) body(j0 + jj, x[jj].k, x[jj].w);
@@ -267,7 +271,7 @@ __global__ __launch_bounds__(kThreads) void k_sampling_probs(int T_max, int V, c
     }
     __syncthreads();
     if (wave == 0) {
-      const int ne = nsl * kWaves;
+      const int ne = nsl * NW;
       const int per = (ne + 63) / 64;
       const int e0 = min(ne, lane * per), e1 = min(ne, e0 + per);
       int c = 0;
@@ -284,7 +288,7 @@ __global__ __launch_bounds__(kThreads) void k_sampling_probs(int T_max, int V, c
           const int pc = __popcll(mm);
           if (r <= pc) {
             for (int q = 1; q < r; ++q) mm &= mm - 1;
-            s_pick = (e / kWaves) * kThreads + (e % kWaves) * 64 + (__ffsll((long long)mm) - 1);
+            s_pick = (e / NW) * NT + (e % NW) * 64 + (__ffsll((long long)mm) - 1);
             break;
           }
           r -= pc;
@@ -294,7 +298,7 @@ __global__ __launch_bounds__(kThreads) void k_sampling_probs(int T_max, int V, c
     __syncthreads();
     const int res = s_pick;
     __syncthreads();
-    mass_above = mass ? block_sum_u64(ma, s_u) : 0ull;
+    mass_above = mass ? block_sum_u64<NT>(ma, s_u) : 0ull;
     return res;
   };
 
@@ -313,7 +317,7 @@ __global__ __launch_bounds__(kThreads) void k_sampling_probs(int T_max, int V, c
     uint32_t prefix = 0u, pmask = 0u;
     unsigned long long above = 0ull;
     for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int e = tid; e < kWaves * 256; e += kThreads) s_hist[e] = 0ull;
+      for (int e = tid; e < NW * 256; e += NT) s_hist[e] = 0ull;
       __syncthreads();
       pass([&](int v, KW e) {
         if ((e.k & pmask) == prefix && pred(e.k, v)) {
@@ -327,7 +331,7 @@ __global__ __launch_bounds__(kThreads) void k_sampling_probs(int T_max, int V, c
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           m[j] = 0ull;
-          for (int w = 0; w < kWaves; ++w) m[j] += s_hist[w * 256 + 4 * lane + j];
+          for (int w = 0; w < NW; ++w) m[j] += s_hist[w * 256 + 4 * lane + j];
           g += m[j];
         }
         unsigned long long suf = g;  // total of this lane's bins and every higher lane's
@@ -380,7 +384,7 @@ __global__ __launch_bounds__(kThreads) void k_sampling_probs(int T_max, int V, c
   uint32_t tk = 0u;
   int ck = V;
   const bool with_p = tp < 1.0f;
-  unsigned long long wk = block_sum_u64(w_all, s_u);  // the survivors' total weight (units of 2^-32)
+  unsigned long long wk = block_sum_u64<NT>(w_all, s_u);  // the survivors' total weight (units of 2^-32)
   if (kk > 1 && kk < V) {
     unsigned long long above = 0ull, bin = 0ull, ma = 0ull;
     radix(one, all, (double)kk, tk, above, bin);  // always reached: kk < V tokens
@@ -393,25 +397,25 @@ __global__ __launch_bounds__(kThreads) void k_sampling_probs(int T_max, int V, c
   // ---- top-p cut (tpk, cp) over the top-k survivors
   uint32_t tpk = 0u;
   int cp = V;
-  if (with_p && kk > 1 && kk <= kThreads) {
-    // at most kThreads survivors: gathered into LDS as 64-bit rank keys (key,
+  if (with_p && kk > 1 && kk <= NT) {
+    // at most NT survivors: gathered into LDS as 64-bit rank keys (key,
     // then token ascending; the order of the appends does not matter), sorted
     // descending by a bitonic network, then one exact prefix sum of their weights
     // in rank order finds the cut
-    unsigned long long* s_list = s_hist;  // kThreads entries
+    unsigned long long* s_list = s_hist;  // NT entries
     if (tid == 0) s_cnt = 0;
     __syncthreads();
     pass([&](int v, KW e) {
       if (in_k(e.k, v)) {
         const int pos = atomicAdd(&s_cnt, 1);  // < kk by construction of the cut
-        if (pos < kThreads) s_list[pos] = rank_key(key_float(e.k), (uint32_t)v);
+        if (pos < NT) s_list[pos] = rank_key(key_float(e.k), (uint32_t)v);
       }
     });
     __syncthreads();
-    const int n = min(s_cnt, kThreads);  // == kk
+    const int n = min(s_cnt, NT);  // == kk
     if (tid >= n) s_list[tid] = 0ull;
     __syncthreads();
-    for (int k2 = 2; k2 <= kThreads; k2 <<= 1) {
+    for (int k2 = 2; k2 <= NT; k2 <<= 1) {
       for (int j = k2 >> 1; j > 0; j >>= 1) {
         const int ixj = tid ^ j;
         if (ixj > tid) {
@@ -427,7 +431,7 @@ __global__ __launch_bounds__(kThreads) void k_sampling_probs(int T_max, int V, c
     const unsigned long long mine = s_list[tid];
     const unsigned long long x = tid < n ? fixed(weight((uint32_t)(mine >> 32))) : 0ull;
     unsigned long long lo, hi, tot;
-    block_scan<unsigned long long>(x, s_u, lo, hi, tot);
+    block_scan<unsigned long long, NT>(x, s_u, lo, hi, tot);
     const double target = (double)tp * (double)tot;
     if (tid == 0) s_pick = n;
     __syncthreads();
@@ -465,7 +469,7 @@ __global__ __launch_bounds__(kThreads) void k_sampling_probs(int T_max, int V, c
   pass([&](int v, KW e) {
     if (keep(e.k, v, e.w)) wsum += (double)e.w;
   });
-  const double W = block_sum_d(wsum, s_d);
+  const double W = block_sum_d<NT>(wsum, s_d);
   pass([&](int v, KW e) { orow[v] = keep(e.k, v, e.w) ? (float)((double)e.w / W) : 0.0f; });
 }
 
@@ -650,11 +654,17 @@ extern "C" int tree_sampling_probs(int B, int T_max, int V, const float* logits,
   const char* a = reinterpret_cast<const char*>(logits);
   const char* c = reinterpret_cast<const char*>(probs);
   if (a < c + n && c < a + n) return TV_EINVAL;  // the output must not overlap the logits
-  // rows of up to 8192 tokens stay in registers (more would spill at 1024 threads)
-  const int npt = (V + tv::kThreads - 1) / tv::kThreads;
-  auto k = npt <= 8 ? tv::k_sampling_probs<8> : tv::k_sampling_probs<0>;
-  hipLaunchKernelGGL(k, dim3(T_max, B), dim3(tv::kThreads), 0, reinterpret_cast<hipStream_t>(stream), T_max, V,
-                     logits, tree_size, status, temperature, top_k, top_p, min_p, probs);
+  // Few rows: 1024 threads per row (each row's chain of passes is latency-bound,
+  // so more threads per row finish it sooner).  Many rows: 256 threads per row,
+  // several rows per CU hiding each other's latency.  Rows of up to 8 tokens per
+  // thread stay in registers (more would spill).
+  const bool many = (long long)B * T_max >= 512;
+  const int nt = many ? 256 : 1024;
+  const bool regs = V <= 8 * nt;
+  auto k = many ? (regs ? tv::k_sampling_probs<256, 8> : tv::k_sampling_probs<256, 0>)
+                : (regs ? tv::k_sampling_probs<1024, 8> : tv::k_sampling_probs<1024, 0>);
+  hipLaunchKernelGGL(k, dim3(T_max, B), dim3(nt), 0, reinterpret_cast<hipStream_t>(stream), T_max, V, logits,
+                     tree_size, status, temperature, top_k, top_p, min_p, probs);
   TV_CHECK_LAUNCH();
   return TV_OK;
 }
