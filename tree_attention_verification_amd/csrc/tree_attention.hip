@@ -182,7 +182,9 @@ __global__ __launch_bounds__(NW * 64, (NSTAGE == 2 && NW == 4) ? 2 : 1) void k_a
   // NSTAGE LDS tile buffers: NSTAGE - 1 tiles in flight while one is computed.
   // Two are used (64 KB at d = 128; with 4-wavefront workgroups two fit on a CU):
   // measured on MI355X, one tile in flight beat three at every configuration
-  // (cfg2 18.3 -> 16.4 us, cfg3 93.6 -> 89.6, cfg4 284 -> 279, cfg5 264 -> 256).
+  // (one request over a 2048-token prefix 18.3 -> 16.4 us, 16 ragged requests
+  // 93.6 -> 89.6, 4 requests over 32768 tokens 284 -> 279, 64 requests over
+  // 4096 tokens 264 -> 256).
   static_assert(NSTAGE == 2 || NSTAGE == 4, "two or four stage buffers");
   static_assert(!PAGED || NSTAGE == 2, "the paged cache's block numbers are fetched one tile ahead");
   constexpr int kAhead = 5;         // LDS fragment reads issued ahead of the MFMAs that use them
