@@ -192,3 +192,34 @@ def test_draft_sampling_largest_vocabulary_and_tiny_trees():
     uni = rng.random((3, 4)).astype(np.float32)
     for wr in (True, False):
         compare(tokens, parents, sizes, probs, q, uni, np.zeros(3, np.int32), 3, wr)
+
+
+@pytest.mark.parametrize("wr", [True, False])
+def test_filter_then_draft_sampling(wr):
+    """The whole chain with the drafter's q: target logits -> tree_sampling_probs ->
+    tree_accept_sample_draft, against the oracle's filter + accept_sample_draft."""
+    import torch
+    from oracle import sampling as osm
+    from tree_attention_verification_amd.step import TreeVerifyStep
+    w = gen.make_workload(3, with_attention=False)
+    st = TreeVerifyStep(w)
+    st.build_meta()
+    torch.cuda.synchronize()
+    tree = st.tree_host()
+    B, T_max, V = w.B, w.T_max, w.V
+    lg = gen.synthetic_target_logits(w, tree["tree_size"])
+    params = gen.sampling_params(w, B)
+    q = gen.synthetic_draft_probs(w, tree["draft_tokens"], tree["parents"], tree["tree_size"])
+    _, uni = gen.synthetic_target_probs(w, tree["draft_tokens"], tree["parents"], tree["tree_size"])
+    st.set_target_probs(np.zeros((B, T_max, V), np.float32), uni)
+    st.set_sampling_inputs(lg, params, q)
+    st.sampling_probs()
+    st.accept_sample_draft(wr)
+    torch.cuda.synchronize()
+    got = st.accept_host()
+    stat = st.status.cpu().numpy()
+    ref_probs = osm.tree_sampling_probs(lg, tree["tree_size"], stat, *params, np.zeros((B, T_max, V), np.float32))
+    ref = osm.tree_accept_sample_draft(tree["draft_tokens"], tree["parents"], tree["tree_size"], ref_probs, q, uni,
+                                       stat, st.dcap, wr)
+    for k in ("accept_len", "accept_path", "bonus_token"):
+        np.testing.assert_array_equal(got[k], ref[k], err_msg=k)
