@@ -23,13 +23,14 @@ Readings where the pages are silent (each listed with its reason in the design n
   * a temperature <= 0 (or NaN) is greedy: all mass on the first-ranked token;
   * a token's weight is exp((l - l_max) / temperature) in float64, exactly 1 for every
     token whose logit equals the largest (this defines +inf logits and an all -inf
-    row), rounded to float32; sums and comparisons of weights are float64;
+    row), rounded to float32;
   * top-k (1 <= k < V) keeps the first k ranks;
   * top-p (< 1; NaN = off) keeps the shortest rank prefix of the top-k survivors whose
-    cumulative weight reaches top_p x their total weight (so at least one token); the
-    weights are added exactly, as integers in units of 2^-32 (round(w 2^32), half to
-    even), and the comparison is (double)cumulative >= (double)top_p x (double)total,
-    so the cut does not depend on the order of the additions;
+    cumulative weight reaches top_p x their total weight (so at least one token), in
+    exact arithmetic: the cumulative and the total are the exact sums of the float32
+    weights, and cumulative >= top_p x total is decided exactly with top_p's own
+    float32 value (every float32 is an integer multiple of 2^-149, so Python integers
+    in that unit hold the sums, and the comparison is one of integers);
   * min-p (> 0) drops tokens whose weight is below min_p x the largest weight (which is
     1); the first-ranked token is always kept;
   * the output is w / (sum of the kept w), float64 rounded to float32; dropped tokens
@@ -96,12 +97,15 @@ def sampling_probs_row(logits, temperature, top_k, top_p, min_p):
     surv = order[:n]
     tp = float(np.float32(top_p))
     if tp < 1.0:
-        fx = [int(x) for x in np.rint(w[surv] * 2.0 ** 32)]   # exact integers (w * 2^32 < 2^33)
-        target = tp * float(sum(fx))
+        # exact sums: w * 2^149 is an integer for every float32 w (the scaling by a
+        # power of two is exact in float64), and top_p = num / den exactly
+        units = [int(x * 2.0 ** 149) for x in w[surv]]
+        num, den = tp.as_integer_ratio()
+        target = num * sum(units)             # cumulative >= top_p x total  <=>  den x cumulative >= target
         cum = 0
-        for n, x in enumerate(fx):
+        for n, x in enumerate(units):
             cum += x
-            if float(cum) >= target:
+            if den * cum >= target:
                 surv = surv[:n + 1]
                 break
     keep = np.zeros(V, bool)

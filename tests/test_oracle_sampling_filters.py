@@ -78,6 +78,34 @@ def test_worked_example():
     assert (got > 0).tolist() == [True, True, False, False]
 
 
+def test_top_p_cut_counts_every_tail_weight():
+    # Two tokens of weight 1 and 1000 tail tokens of weight ~1e-11 (logit ln 1e-11 at
+    # temperature 1).  The exact total is 2 + 1000 w_t, so top_p 0.5 needs more than
+    # the first token (1 < 0.5 (2 + 1000 w_t)) and keeps exactly two.  A top-p sum
+    # that drops weights below some unit (e.g. 2^-33) would keep one.
+    lt = np.float32(math.log(1e-11))
+    lg = np.full(1002, lt, np.float32)
+    lg[0] = lg[1] = 0.0
+    w_t = float(np.float32(math.exp(float(lt))))
+    assert 0 < w_t < 2.0 ** -33 and 1.0 < 0.5 * (2.0 + 1000 * w_t)
+    for k in (0, 500):                       # the radix path (no top-k) and a top-k survivor list
+        got = osm.sampling_probs_row(lg, 1.0, k, 0.5, 0.0)
+        assert (got > 0).tolist() == [True, True] + [False] * 1000, k
+        assert got[:2].tolist() == [0.5, 0.5]
+    # with top_p exactly at a cumulative boundary the cut is inclusive (>=): four equal
+    # weights, top_p 0.5 keeps two; the next float32 above 0.5 keeps three
+    lg4 = np.zeros(4, np.float32)
+    assert (osm.sampling_probs_row(lg4, 1.0, 0, 0.5, 0.0) > 0).tolist() == [True, True, False, False]
+    above = float(np.nextafter(np.float32(0.5), np.float32(1.0)))
+    assert (osm.sampling_probs_row(lg4, 1.0, 0, above, 0.0) > 0).tolist() == [True, True, True, False]
+    # a subnormal weight still counts: 2 + w_s at top_p 0.5 keeps two, 2 alone keeps one
+    lgs = np.array([0.0, 0.0, -100.0], np.float32)          # exp(-100) ~ 3.7e-44: a float32 subnormal
+    ws = float(np.float32(math.exp(-100.0)))
+    assert 0 < ws < 2.0 ** -126
+    assert (osm.sampling_probs_row(lgs, 1.0, 0, 0.5, 0.0) > 0).tolist() == [True, True, False]
+    assert (osm.sampling_probs_row(lgs[:2], 1.0, 0, 0.5, 0.0) > 0).tolist() == [True, False]
+
+
 def test_ties_cut_in_token_order():
     lg = np.array([1.0, 2.0, 1.0, 2.0, 1.0, 0.0], np.float32)   # rank: 1, 3, 0, 2, 4, 5
     got = osm.sampling_probs_row(lg, 1.0, 3, 1.0, 0.0)
