@@ -2,8 +2,8 @@
 the oracle's sampling_probs_row, and of the chain tree_sampling_probs ->
 tree_accept_sample against the oracle's filter + accept_sample.
 
-Bars: the set of kept tokens is bit-exact (both sides take every decision in
-float64 from the same float32 weights; only the order of sums differs); kept
+Bars: the set of kept tokens is bit-exact (the top-k and top-p cuts are exact on
+both sides: counts, and exact sums of the same float32 weights); kept
 probabilities within 2e-6 relative (one float32 rounding of w / W, W summed in a
 different order); rows past a request's tree are untouched.  Cases: several
 vocabulary sizes (50 to 128256, i.e. one to ~125 values per thread), mixed
@@ -101,6 +101,72 @@ def test_filters_wide_trees():
     params = (np.array([0.8, 1.2], np.float32), np.array([20, 0], np.int32), np.array([0.9, 0.7], np.float32),
               np.array([0.0, 0.05], np.float32))
     run_filter(lg, w.given_size, None, params)
+
+
+def _tail_rows(V):
+    """Rows whose top-p cut depends on weights far below 2^-33 (the exact sums decide):
+      0: two tokens of weight 1 + a tail of ~1e-11: top_p 0.5 keeps 2 (1 < 0.5 (2 + tail));
+      1: weight 1, four tied tokens of weight 0.5, the same tail: top_p 0.5 needs two of
+         the tie group (without the tail, 1 + 0.5 would reach exactly half of 3);
+      2: four equal weights, top_p 0.5: the cut lands exactly on a cumulative (2 kept);
+      3: as 2 with the next float32 above 0.5 (3 kept);
+      4: two tokens of weight 1 and one float32-subnormal weight: top_p 0.5 keeps 2."""
+    lt = np.float32(np.log(1e-11))
+    rows = np.full((5, V), -np.inf, np.float32)
+    rows[0, :] = lt
+    rows[0, [7, V - 3]] = 0.0
+    rows[1, :] = lt
+    rows[1, 11] = 0.0
+    rows[1, [2, 30, 40, V - 1]] = np.float32(np.log(0.5))
+    rows[2, [0, 5, 9, 13]] = 1.5
+    rows[3, [0, 5, 9, 13]] = 1.5
+    rows[4, [1, 4]] = 0.0
+    rows[4, 8] = -100.0
+    top_p = np.array([0.5, 0.5, 0.5, np.nextafter(np.float32(0.5), np.float32(1)), 0.5], np.float32)
+    kept = [2, 3, 2, 3, 2]
+    return rows, top_p, kept
+
+
+@pytest.mark.parametrize("many", [False, True])
+@pytest.mark.parametrize("top_k", [0, 200, 700])
+def test_filters_exact_top_p_cut(many, top_k):
+    """The top-p cut follows the exact sums of the float32 weights: tail weights of
+    ~1e-11 (and a subnormal) move it.  top_k 0 and 700 take the radix path at 256
+    threads per row, 200 the sorted survivor list; 0 the radix path at 1024 threads,
+    200 and 700 the survivor list there.  `many` launches >= 512 rows, which selects
+    the 256-thread kernel."""
+    from oracle import sampling as osm
+    V = 3000
+    rows, top_p, kept = _tail_rows(V)
+    B, T_max = (8, 64) if many else (5, 1)
+    lg = np.random.default_rng(7).normal(0, 1, (B, T_max, V)).astype(np.float32)
+    tree_size = np.ones(B, np.int32)
+    tp = np.full(B, 0.9, np.float32)
+    for r in range(5):
+        lg[r, 0] = rows[r]
+        tp[r] = top_p[r]
+        if top_k == 0 or top_k > 3:
+            ref = osm.sampling_probs_row(rows[r], 1.0, top_k, top_p[r], 0.0)
+            assert int((ref > 0).sum()) == kept[r], r
+    params = (np.ones(B, np.float32), np.full(B, top_k, np.int32), tp, np.zeros(B, np.float32))
+    run_filter(lg, tree_size, None, params)
+
+
+@pytest.mark.parametrize("tie_step", [0.0, 0.25])
+def test_filters_many_rows_large_vocabulary(tie_step):
+    """>= 512 rows (the 256-thread kernel) at V = 32000, which keeps every row in
+    memory (no register copy): top_k <= 256 takes the sorted survivor list, top_k in
+    257..1024 and no top-k take the radix top-p passes; ties from rounded logits."""
+    B, T_max, V = 8, 64, 32000
+    sizes = np.array([64, 40, 64, 10, 64, 33, 17, 64], np.int32)
+    w = gen.make_custom(cfg_id=1650, B=B, mode="given", given_sizes=list(sizes), V=V, P=4, T_max=T_max, dcap=20,
+                        given_depth=8)
+    lg = gen.synthetic_target_logits(w, w.given_size, tie_step=tie_step)
+    temp = np.array([1.0, 0.7, 1.3, 1.0, 0.5, 2.0, 0.9, 1.1], np.float32)
+    top_k = np.array([300, 1000, 0, 256, 100, 257, 1024, 0], np.int32)
+    top_p = np.array([0.9, 0.95, 0.8, 0.7, 0.99, 0.6, 0.85, 1.0], np.float32)
+    min_p = np.array([0.0, 0.0, 0.01, 0.0, 0.0, 0.05, 0.0, 0.02], np.float32)
+    run_filter(lg, w.given_size, None, (temp, top_k, top_p, min_p))
 
 
 @pytest.mark.parametrize("cfg", [2, 3])

@@ -92,6 +92,196 @@ __device__ __forceinline__ unsigned long long block_max_u64(unsigned long long v
   return t;
 }
 
+// ---- exact sums of float32 weights.  Every float32 w in [0, 1] is an integer
+// number of units of 2^-149: w = m 2^s units with an integer m < 2^24 and
+// 0 <= s <= 126.  A sum of weights is held as NL limbs of 32-bit digits (limb j
+// weighs 2^(32 j) units), each limb in a 64-bit word that may exceed 32 bits until
+// it is normalised (carry-save).  A weight adds less than 2^32 to at most two
+// adjacent limbs and a row has at most 2^18 tokens, so no word overflows.
+constexpr int NL = 5;
+struct Wide {
+  unsigned long long l[NL];
+};
+
+__device__ __forceinline__ Wide wzero() {
+  Wide r;
+#pragma unroll
+  for (int i = 0; i < NL; ++i) r.l[i] = 0ull;
+  return r;
+}
+__device__ __forceinline__ void wadd(Wide& a, const Wide& b) {
+#pragma unroll
+  for (int i = 0; i < NL; ++i) a.l[i] += b.l[i];
+}
+// limb-wise difference, for b <= a limb by limb (b a partial sum of a)
+__device__ __forceinline__ Wide wsub(Wide a, const Wide& b) {
+#pragma unroll
+  for (int i = 0; i < NL; ++i) a.l[i] -= b.l[i];
+  return a;
+}
+__device__ __forceinline__ Wide wmul(Wide a, unsigned long long k) {  // k < 2^18, limbs < 2^32
+#pragma unroll
+  for (int i = 0; i < NL; ++i) a.l[i] *= k;
+  return a;
+}
+// w = m 2^s units: the limb j = s / 32 and the mantissa shifted into it (< 2^56;
+// its bits 32 and up belong to limb j + 1)
+__device__ __forceinline__ void weight_parts(float w, int& j, unsigned long long& x) {
+  const uint32_t u = __float_as_uint(w);
+  const uint32_t e = u >> 23;  // w >= 0: no sign bit
+  const uint32_t m = e ? ((u & 0x7FFFFFu) | 0x800000u) : u;
+  const int s = e ? (int)e - 1 : 0;
+  j = s >> 5;
+  x = (unsigned long long)m << (s & 31);
+}
+__device__ __forceinline__ Wide wide_of(float w) {
+  int j;
+  unsigned long long x;
+  weight_parts(w, j, x);
+  Wide r;
+#pragma unroll
+  for (int i = 0; i < NL; ++i)
+    r.l[i] = (i == j ? (x & 0xFFFFFFFFull) : 0ull) + (i == j + 1 ? (x >> 32) : 0ull);
+  return r;
+}
+// A normalised sum: NN limbs of 32 bits (192 bits; a row's total is below 2^167)
+constexpr int NN = 6;
+struct Norm {
+  uint32_t l[NN];
+};
+__device__ __forceinline__ Norm norm_of(const Wide& a) {
+  Norm n;
+  unsigned long long c = 0ull;
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const unsigned long long v = a.l[i] + c;
+    n.l[i] = (uint32_t)v;
+    c = v >> 32;
+  }
+  n.l[NL] = (uint32_t)c;
+  return n;
+}
+__device__ __forceinline__ Norm nzero() {
+  Norm r;
+#pragma unroll
+  for (int i = 0; i < NN; ++i) r.l[i] = 0u;
+  return r;
+}
+__device__ __forceinline__ Norm nadd(const Norm& a, const Norm& b) {
+  Norm r;
+  unsigned long long c = 0ull;
+#pragma unroll
+  for (int i = 0; i < NN; ++i) {
+    const unsigned long long v = (unsigned long long)a.l[i] + b.l[i] + c;
+    r.l[i] = (uint32_t)v;
+    c = v >> 32;
+  }
+  return r;
+}
+__device__ __forceinline__ bool nge(const Norm& a, const Norm& b) {
+  bool gt = false, eq = true;  // decided from the top limb down
+#pragma unroll
+  for (int i = NN - 1; i >= 0; --i) {
+    gt = gt || (eq && a.l[i] > b.l[i]);
+    eq = eq && a.l[i] == b.l[i];
+  }
+  return gt || eq;
+}
+// a value every lane holds the same copy of: kept in scalar registers
+__device__ __forceinline__ Norm nuniform(const Norm& a) {
+  Norm r;
+#pragma unroll
+  for (int i = 0; i < NN; ++i) r.l[i] = (uint32_t)__builtin_amdgcn_readfirstlane((int)a.l[i]);
+  return r;
+}
+__device__ __forceinline__ Norm nshfl_down(const Norm& a, int o) {
+  Norm r;
+#pragma unroll
+  for (int i = 0; i < NN; ++i) r.l[i] = (uint32_t)__shfl_down((int)a.l[i], o, 64);
+  return r;
+}
+__device__ __forceinline__ Wide wshfl_xor(const Wide& a, int m) {
+  Wide r;
+#pragma unroll
+  for (int i = 0; i < NL; ++i) r.l[i] = __shfl_xor(a.l[i], m, 64);
+  return r;
+}
+// t[k] for a run-time k (0 past the end), without indexing registers dynamically
+__device__ __forceinline__ unsigned long long limb_at(const unsigned long long (&t)[NN + 1], int k) {
+  unsigned long long v = 0ull;
+#pragma unroll
+  for (int i = 0; i <= NN; ++i) v = i == k ? t[i] : v;
+  return v;
+}
+// ceil(x / 2^q) of NN + 1 limbs of 32 bits (0 <= q < 32 NN; the result fits NN limbs)
+__device__ __forceinline__ Norm nshr_ceil(const unsigned long long (&t)[NN + 1], int q) {
+  const int ws = q >> 5, bs = q & 31;
+  bool sticky = (limb_at(t, ws) & ((1ull << bs) - 1ull)) != 0ull;
+#pragma unroll
+  for (int i = 0; i < NN; ++i) sticky |= i < ws && t[i] != 0ull;
+  Norm r;
+#pragma unroll
+  for (int i = 0; i < NN; ++i)
+    r.l[i] = (uint32_t)((limb_at(t, i + ws) >> bs) | (limb_at(t, i + ws + 1) << (32 - bs)));
+  Norm one = nzero();
+  one.l[0] = sticky ? 1u : 0u;
+  return nadd(r, one);
+}
+// a float32 x > 0 is m 2^(s - 149) exactly: an integer m < 2^24 and s >= 0
+__device__ __forceinline__ void float_parts(float x, unsigned long long& m, int& s) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t e = u >> 23;
+  m = e ? ((u & 0x7FFFFFu) | 0x800000u) : u;
+  s = e ? (int)e - 1 : 0;
+}
+// ceil(p z) for a float32 p in (0, 1): an integer cumulative c has c >= p z
+// exactly when c >= ceil(p z).  p = m 2^-q with q = 149 - s >= 24.
+__device__ __forceinline__ Norm nthreshold(float p, const Norm& z) {
+  unsigned long long m;
+  int s;
+  float_parts(p, m, s);
+  unsigned long long t[NN + 1];
+  unsigned long long c = 0ull;
+#pragma unroll
+  for (int i = 0; i < NN; ++i) {  // m z, limb by limb (z's limbs < 2^32, m < 2^24)
+    const unsigned long long v = (unsigned long long)z.l[i] * m + c;
+    t[i] = v & 0xFFFFFFFFull;
+    c = v >> 32;
+  }
+  t[NN] = c;
+  return nshr_ceil(t, 149 - s);
+}
+// the smallest n >= 1 with above + n c >= thr, for a float32 weight c > 0 and
+// above < thr (2^31 - 1 stands for anything larger)
+__device__ __forceinline__ int ntie_count(const Norm& thr, const Norm& above, float c) {
+  unsigned long long t[NN + 1];
+  long long br = 0;
+#pragma unroll
+  for (int i = 0; i < NN; ++i) {  // t = thr - above, borrows propagated
+    const long long v = (long long)thr.l[i] - (long long)above.l[i] - br;
+    br = v < 0 ? 1 : 0;
+    t[i] = (unsigned long long)(v + (br << 32));
+  }
+  t[NN] = 0ull;
+  // c = m 2^s units: n = ceil(ceil(t / 2^s) / m), the division digit by digit
+  unsigned long long m;
+  int s;
+  float_parts(c, m, s);
+  const Norm d = nshr_ceil(t, s);
+  unsigned long long rem = 0ull, hiq = 0ull, q0 = 0ull;
+#pragma unroll
+  for (int i = NN - 1; i >= 0; --i) {
+    const unsigned long long cur = (rem << 32) | d.l[i];  // rem < m < 2^24
+    const unsigned long long qd = cur / m;
+    rem = cur % m;
+    if (i > 0) hiq |= qd;
+    else q0 = qd;
+  }
+  if (hiq || q0 >= 0x7FFFFFFFull) return 0x7FFFFFFF;
+  const long long n = (long long)q0 + (rem ? 1 : 0);
+  return n < 1 ? 1 : (int)n;
+}
+
 // Visits v = threadIdx.x + j NT (j = 0, 1, ...) in increasing v, with the
 // loads of NB visits issued together (one memory round trip per NB entries);
 // indices past the row are clamped for the load and skipped for the body.
@@ -140,8 +330,9 @@ __device__ __forceinline__ float key_float(uint32_t k) {
 // a prefix of the ranking, described by a cut (key t, token c): token v with key
 // k is inside iff k > t or (k == t and v <= c).  The top-k and top-p cuts are
 // found by radix selection over the 32-bit order keys, eight bits per pass from
-// the top, with exact integer totals (counts for top-k, weights in units of
-// 2^-32 for top-p).  Equal keys have equal weights; the cut inside a group of
+// the top, with exact totals (counts for top-k; for top-p the exact sums of the
+// float32 weights, as Wide integers in units of 2^-149, and the exact threshold
+// ceil(top_p x total)).  Equal keys have equal weights; the cut inside a group of
 // equal keys is the n-th of them in token order, found by a scan over contiguous
 // token ranges.
 // --------------------------------------------------------------------------
@@ -167,8 +358,13 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
   float* orow = probs + ((long long)b * T_max + i) * V;
   __shared__ double s_d[NW * 16];
   __shared__ unsigned long long s_u[NW];
-  __shared__ unsigned long long s_hist[4096];  // radix bins, ballot entries (V / 64), or the survivor list
-  __shared__ unsigned long long s_abv, s_bin;
+  __shared__ Wide s_w[NW];
+  // radix bins (per-wavefront counts, or NL x 256 limbs of weight sums), ballot
+  // entries (V / 64), or the survivor list
+  __shared__ unsigned long long s_hist[4096];
+  static_assert(NW * 256 <= 4096 && NL * 256 <= 4096, "radix bins fit");
+  __shared__ Norm s_abv;
+  __shared__ unsigned long long s_abvc;
   __shared__ int s_pick, s_sel, s_cnt;
 
   // the first-ranked token
@@ -219,20 +415,30 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
       row_pass<NT>(V, ld_kw, body);
     }
   };
-  // weight in units of 2^-32 (w <= 1, so at most 2^32; a row's total stays below 2^51)
-  auto fixed = [](float w) { return (unsigned long long)rint((double)w * 4294967296.0); };
-  unsigned long long w_all = 0ull;  // this thread's total weight, units of 2^-32
+  // the workgroup's sum of one Wide per thread (every thread gets it, carry-save)
+  auto block_wsum = [&](Wide v) -> Wide {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) wadd(v, wshfl_xor(v, o));
+    if ((tid & 63) == 0) s_w[tid >> 6] = v;
+    __syncthreads();
+    Wide t = wzero();
+    for (int w = 0; w < NW; ++w) wadd(t, s_w[w]);
+    __syncthreads();
+    return t;
+  };
+  const bool with_p = tp < 1.0f;
+  Wide w_all = wzero();  // this thread's total weight (only needed for top-p)
   if constexpr (NPT > 0) {
 #pragma unroll
     for (int j = 0; j < NPT; ++j) {
       reg[j].w = weight(reg[j].k);
-      if (tid + j * NT < V) w_all += fixed(reg[j].w);
+      if (with_p && tid + j * NT < V) wadd(w_all, wide_of(reg[j].w));
     }
   } else {
     row_pass<NT>(V, ld_l, [&](int v, float x) {
       const float w = weight(logit_key(x));
       orow[v] = w;
-      w_all += fixed(w);
+      if (with_p) wadd(w_all, wide_of(w));
     });
   }
 
@@ -242,17 +448,17 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
   // wavefront's ballot of its matching tokens goes to LDS, slice-major, so the
   // entries are in token order; the first wavefront then finds the entry holding
   // the n-th match (64 entries per lane at most, a scan over the lanes) and the
-  // bit inside it.  With `mass`, also returns the total weight (units of 2^-32) of
-  // the tokens with key > t (all inside the cut, since t >= tk).
+  // bit inside it.  With `mass`, also returns the exact total weight of the
+  // tokens with key > t (all inside the cut, since t >= tk).
   const int nsl = (V + NT - 1) / NT;  // <= 256 slices, <= 4096 entries
-  auto nth_with_key = [&](uint32_t t, int n, uint32_t tk, int ck, bool mass, unsigned long long& mass_above) -> int {
-    unsigned long long ma = 0ull;
+  auto nth_with_key = [&](uint32_t t, int n, uint32_t tk, int ck, bool mass, Wide& mass_above) -> int {
+    Wide ma = wzero();
     auto body = [&](int j, uint32_t k, float w) __attribute__((always_inline)) {
       const int v = j * NT + tid;
       const bool f = v < V && k == t && (k > tk || v <= ck);
       const unsigned long long m = __ballot(f);
       if (lane == 0) s_hist[j * NW + wave] = m;
-      if (mass && v < V && k > t) ma += fixed(w);
+      if (mass && v < V && k > t) wadd(ma, wide_of(w));
     };
     if (tid == 0) s_pick = V;
     if constexpr (NPT > 0) {
@@ -298,32 +504,26 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
     __syncthreads();
     const int res = s_pick;
     __syncthreads();
-    mass_above = mass ? block_sum_u64<NT>(ma, s_u) : 0ull;
+    mass_above = mass ? block_wsum(ma) : wzero();
     return res;
   };
 
-  // ---- radix selection.  Over the tokens with pred, in rank order, each token
-  // carrying an integer value (1 to count ranks, its weight in units of 2^-32 for
-  // mass), find the key t of the first token at which the running total reaches
-  // `target`, and `above` = the total of the tokens with larger keys.  Eight bits
-  // of the key per pass from the top: each wavefront adds its tokens' values into
-  // its own 256-bin LDS histogram (integer atomics: the totals are exact, so the
+  // ---- radix selection over the keys, eight bits per pass from the top.  Each
+  // pass histograms the tokens whose key matches the digits chosen so far into 256
+  // bins of the next digit (LDS integer atomics: the totals are exact, so the
   // order of the additions does not matter), then the first wavefront places the
-  // target among the bins (four bins per lane, a suffix sum over the lanes).
-  // Returns false if the target is never reached.
-  auto radix = [&](auto val, auto pred, double target, uint32_t& t_out, unsigned long long& above_out,
-                   unsigned long long& bin_out) -> bool {
-    unsigned long long bin = 0ull;
+  // target among the bins (four bins per lane, a suffix sum over the lanes) and
+  // the highest bin at which the running total reaches the target is chosen.
+  // Counts (top-k): the key of the kk-th ranked token and the number of tokens
+  // with larger keys.
+  auto radix_count = [&](int kk_, uint32_t& t_out, int& above_out) {
     uint32_t prefix = 0u, pmask = 0u;
     unsigned long long above = 0ull;
     for (int shift = 24; shift >= 0; shift -= 8) {
       for (int e = tid; e < NW * 256; e += NT) s_hist[e] = 0ull;
       __syncthreads();
       pass([&](int v, KW e) {
-        if ((e.k & pmask) == prefix && pred(e.k, v)) {
-          const unsigned long long x = val(e);
-          if (x) atomicAdd(&s_hist[wave * 256 + ((e.k >> shift) & 255u)], x);
-        }
+        if ((e.k & pmask) == prefix) atomicAdd(&s_hist[wave * 256 + ((e.k >> shift) & 255u)], 1ull);
       });
       __syncthreads();
       if (wave == 0) {
@@ -341,62 +541,123 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
         }
         unsigned long long run = above + (suf - g);
         int cand = -1;
-        unsigned long long cabove = 0ull, cbin = 0ull;
+        unsigned long long cabove = 0ull;
+#pragma unroll
         for (int j = 3; j >= 0; --j) {
-          if ((double)(run + m[j]) >= target) {
+          if (cand < 0 && run + m[j] >= (unsigned long long)kk_) {
             cand = 4 * lane + j;
             cabove = run;
-            cbin = m[j];
-            break;
           }
           run += m[j];
         }
         const unsigned long long hit = __ballot(cand >= 0);
-        if (lane == 0) s_sel = -1;
-        if (hit) {
-          const int L = 63 - __builtin_clzll(hit);  // the highest digit that reaches the target
-          if (lane == L) {
-            s_sel = cand;
-            s_abv = cabove;
-            s_bin = cbin;
+        if (hit && lane == 63 - __builtin_clzll(hit)) {  // the highest digit that reaches the target
+          s_sel = cand;
+          s_abvc = cabove;
+        }
+      }
+      __syncthreads();
+      const int sel = s_sel;  // always found: kk_ < V tokens
+      above = s_abvc;
+      __syncthreads();
+      prefix |= (uint32_t)sel << shift;
+      pmask |= 255u << shift;
+    }
+    t_out = prefix;
+    above_out = (int)above;
+  };
+  // Weights (top-p): over the tokens with pred, the key of the first token at
+  // which the exact cumulative weight reaches thr, the exact weight of the tokens
+  // with larger keys, and false if thr is never reached.  The bins hold NL
+  // carry-save limbs each (limb-major: s_hist[limb 256 + bin]); a token adds to
+  // the one or two limbs its weight covers.
+  auto radix_mass = [&](auto pred, const Norm& thr, uint32_t& t_out, Norm& above_out) -> bool {
+    uint32_t prefix = 0u, pmask = 0u;
+    Norm above = nzero();
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      for (int e = tid; e < NL * 256; e += NT) s_hist[e] = 0ull;
+      __syncthreads();
+      pass([&](int v, KW e) {
+        if ((e.k & pmask) == prefix && pred(e.k, v) && e.w > 0.0f) {
+          int j;
+          unsigned long long x;
+          weight_parts(e.w, j, x);
+          const int bin = (int)((e.k >> shift) & 255u);
+          atomicAdd(&s_hist[j * 256 + bin], x & 0xFFFFFFFFull);
+          if (x >> 32) atomicAdd(&s_hist[(j + 1) * 256 + bin], x >> 32);
+        }
+      });
+      __syncthreads();
+      if (wave == 0) {
+        auto bin_at = [&](int bin) {
+          Wide x;
+#pragma unroll
+          for (int i = 0; i < NL; ++i) x.l[i] = s_hist[i * 256 + bin];
+          return x;
+        };
+        Wide g = wzero();
+#pragma unroll
+        for (int j = 0; j < 4; ++j) wadd(g, bin_at(4 * lane + j));
+        Norm suf = norm_of(g);  // this lane's bins and every higher lane's
+        for (int o = 1; o < 64; o <<= 1) {
+          const Norm y = nshfl_down(suf, o);
+          if (lane + o < 64) suf = nadd(suf, y);
+        }
+        Norm run = nshfl_down(suf, 1);  // every higher lane's bins
+        if (lane == 63) run = nzero();
+        run = nadd(run, above);
+        int cand = -1;
+        Norm cabove = nzero();
+#pragma unroll
+        for (int j = 3; j >= 0; --j) {  // (unrolled, no early exit: nothing is indexed dynamically)
+          const Norm r2 = nadd(run, norm_of(bin_at(4 * lane + j)));
+          if (cand < 0 && nge(r2, thr)) {
+            cand = 4 * lane + j;
+            cabove = run;
           }
+          run = r2;
+        }
+        const unsigned long long hit = __ballot(cand >= 0);
+        if (lane == 0) s_sel = -1;
+        if (hit && lane == 63 - __builtin_clzll(hit)) {  // the highest digit that reaches thr
+          s_sel = cand;
+          s_abv = cabove;
         }
       }
       __syncthreads();
       const int sel = s_sel;
-      const unsigned long long nab = s_abv;
-      bin = s_bin;
+      above = nuniform(s_abv);
       __syncthreads();
       if (sel < 0) return false;
       prefix |= (uint32_t)sel << shift;
       pmask |= 255u << shift;
-      above = nab;
     }
     t_out = prefix;
     above_out = above;
-    bin_out = bin;
     return true;
   };
-  auto all = [](uint32_t, int) { return true; };
-  auto one = [](KW) { return 1ull; };
 
   // ---- top-k cut (tk, ck); the default keeps everything (every key is > 0)
   uint32_t tk = 0u;
   int ck = V;
-  const bool with_p = tp < 1.0f;
-  unsigned long long wk = block_sum_u64<NT>(w_all, s_u);  // the survivors' total weight (units of 2^-32)
+  Norm wk = with_p ? nuniform(norm_of(block_wsum(w_all))) : nzero();  // the survivors' exact total weight
   if (kk > 1 && kk < V) {
-    unsigned long long above = 0ull, bin = 0ull, ma = 0ull;
-    radix(one, all, (double)kk, tk, above, bin);  // always reached: kk < V tokens
-    const int need = kk - (int)above;
+    int above = 0;
+    Wide ma = wzero();
+    radix_count(kk, tk, above);
+    const int need = kk - above;
     ck = nth_with_key(tk, need, 0u, V, with_p, ma);
-    wk = ma + (unsigned long long)need * fixed(weight(tk));
+    wadd(ma, wmul(wide_of(weight(tk)), (unsigned long long)need));
+    wk = nuniform(norm_of(ma));
   }
   auto in_k = [&](uint32_t k, int v) { return k > tk || (k == tk && v <= ck); };
 
-  // ---- top-p cut (tpk, cp) over the top-k survivors
+  // ---- top-p cut (tpk, cp) over the top-k survivors: the shortest rank prefix
+  // whose exact cumulative weight c satisfies c >= top_p x total, i.e.
+  // c >= thr = ceil(top_p x total) (c is an integer number of units)
   uint32_t tpk = 0u;
   int cp = V;
+  const Norm thr = with_p ? nuniform(nthreshold(tp, wk)) : nzero();
   if (with_p && kk > 1 && kk <= NT) {
     // at most NT survivors: gathered into LDS as 64-bit rank keys (key,
     // then token ascending; the order of the appends does not matter), sorted
@@ -429,13 +690,21 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
       }
     }
     const unsigned long long mine = s_list[tid];
-    const unsigned long long x = tid < n ? fixed(weight((uint32_t)(mine >> 32))) : 0ull;
-    unsigned long long lo, hi, tot;
-    block_scan<unsigned long long, NT>(x, s_u, lo, hi, tot);
-    const double target = (double)tp * (double)tot;
+    // inclusive prefix (rank order) of the exact weights: a lane scan, then the
+    // totals of the earlier wavefronts
+    Wide incl = tid < n ? wide_of(weight((uint32_t)(mine >> 32))) : wzero();
+    for (int o = 1; o < 64; o <<= 1) {
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        const unsigned long long y = __shfl_up(incl.l[i], o, 64);
+        if (lane >= o) incl.l[i] += y;
+      }
+    }
+    if (lane == 63) s_w[wave] = incl;
     if (tid == 0) s_pick = n;
     __syncthreads();
-    if (tid < n && (double)hi >= target) atomicMin(&s_pick, tid);
+    for (int w = 0; w < wave; ++w) wadd(incl, s_w[w]);
+    if (tid < n && nge(norm_of(incl), thr)) atomicMin(&s_pick, tid);
     __syncthreads();
     const int cut = s_pick;  // the last kept rank
     if (cut < n) {
@@ -445,16 +714,12 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
     }
     __syncthreads();
   } else if (with_p) {
-    const double target = (double)tp * (double)wk;
-    unsigned long long above = 0ull, bin = 0ull, unused = 0ull;
-    if (radix([&](KW e) { return fixed(e.w); }, in_k, target, tpk, above, bin)) {
-      // tokens with key tpk among the survivors, each of the same weight ct (so the
-      // last bin holds na ct), join in token order until the running total reaches
-      // the target
-      const unsigned long long ct = fixed(weight(tpk));
-      const int na = (int)(bin / ct);
-      int n = 1;
-      while ((double)(above + (unsigned long long)n * ct) < target && n < na) ++n;
+    Norm above = nzero();
+    Wide unused = wzero();
+    if (radix_mass(in_k, thr, tpk, above)) {
+      // the survivors with key tpk all weigh ct: in token order, the first n of
+      // them bring the cumulative to thr (n = ceil((thr - above) / ct))
+      const int n = ntie_count(thr, above, weight(tpk));
       cp = nth_with_key(tpk, n, tk, ck, false, unused);
     } else {
       tpk = 0u;  // never reached: every survivor stays
