@@ -9,6 +9,9 @@ Bars (from the specification of the step):
     bound alone would accept an all-zero output because these outputs are ~1e-2);
   * fp32 attention: max-abs <= 1e-4 (the handbook's chain-vs-tree bar is 1e-3; the
     fp32 kernel's observed error is ~1e-6).
+The bars are stated for V ~ N(0, 1) * 0.5.  Attention is linear in V, so a test that
+scales V by s compares outputs in units of s (g / s against ref / s; the Frobenius
+ratio is unchanged by the scaling).
 """
 from __future__ import annotations
 
@@ -44,14 +47,15 @@ def check_meta(gpu, ref):
         np.testing.assert_array_equal(gpu[k], ref[k], err_msg=k)
 
 
-def check_attention(o_gpu, o_ref, w, tree_size, status, label=""):
-    """Compare the rows each request writes (i < T_b; T_b = 1 when status != 0)."""
+def check_attention(o_gpu, o_ref, w, tree_size, status, label="", v_scale=1.0):
+    """Compare the rows each request writes (i < T_b; T_b = 1 when status != 0), in
+    units of v_scale (V's scale relative to the configured N(0, 1) * 0.5)."""
     T_eff = np.where(status != 0, 1, tree_size)
     rows = np.zeros(o_ref.shape[:2], dtype=bool)
     for b in range(w.B):
         rows[b, :T_eff[b]] = True
-    g = oa.to_f64(o_gpu)[rows]
-    r = o_ref[rows]
+    g = oa.to_f64(o_gpu)[rows] / v_scale
+    r = o_ref[rows] / v_scale
     assert np.isfinite(g).all(), f"{label}: non-finite output"
     if w.dtype == "bf16":
         err = np.abs(g - r)
@@ -65,7 +69,8 @@ def check_attention(o_gpu, o_ref, w, tree_size, status, label=""):
     return float(err), 0.0
 
 
-def run_pipeline_and_compare(w, *, attention="full", samples=64, seed=0, fused=False, paged=None, rope_theta=None):
+def run_pipeline_and_compare(w, *, attention="full", samples=64, seed=0, fused=False, paged=None, rope_theta=None,
+                             v_scale=1.0):
     """Full pass on the GPU, each stage checked against the oracle.
 
     attention: 'full' compares every written row with the dense oracle; 'sampled'
@@ -111,7 +116,10 @@ def run_pipeline_and_compare(w, *, attention="full", samples=64, seed=0, fused=F
             o_ref = oa.tree_attention_paged(w.Q, paged.K_pool, paged.V_pool, paged.block_table,
                                             paged.tokens_per_block, w.prefix_len, ref_tree["tree_size"],
                                             ref_meta["tree_mask"], status=status)
-        errs = check_attention(o_gpu, o_ref, w, ref_tree["tree_size"], status, w.name)
+        errs = check_attention(o_gpu, o_ref, w, ref_tree["tree_size"], status, w.name, v_scale)
+        # rows past each request's tree stay as the caller left them (zero)
+        T_eff = np.where(status != 0, 1, ref_tree["tree_size"])
+        assert all(not o_gpu[b, T_eff[b]:].any() for b in range(w.B))
     else:
         rng = np.random.default_rng(seed)
         T_eff = np.where(status != 0, 1, ref_tree["tree_size"])

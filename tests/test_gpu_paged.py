@@ -62,9 +62,9 @@ def test_paged_ragged_batch16_full():
     run(gen.make_workload(3), 32)
 
 
-def test_paged_large_batch_full_size_sampled():
-    # the large-batch workload at full size, 16 tokens per block
-    run(gen.make_workload(5), 16, attention="sampled", samples=96)
+def test_paged_large_batch_full_size():
+    # the large-batch workload at full size, 16 tokens per block, every written row
+    run(gen.make_workload(5), 16)
 
 
 def test_paged_many_requests_d64():

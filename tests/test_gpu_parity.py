@@ -3,9 +3,9 @@
 Every test runs the five calls on the GPU and compares each stage with the oracle
 on the same seeded inputs (tests/parity_util.py states the bars).  Sizes: the five
 configurations at sizes the oracle finishes in seconds (spanning several key
-tiles and a ragged tail), the long-context and large-batch configurations at full
-size in the launch configuration the benchmark times (attention checked on
-sampled rows), plus fuzzed shapes and the degenerate cases of the method.
+tiles and a ragged tail), all five at full size in the launch configuration the
+benchmark times (every written attention row compared), plus fuzzed shapes and
+the degenerate cases of the method.
 """
 import numpy as np
 import pytest
@@ -53,16 +53,33 @@ def test_cfg5_random_trees_reduced():
     run(gen.make_workload(5, batch=12, prefix=777))
 
 
-def test_cfg4_full_size_sampled():
-    run(gen.make_workload(4), attention="sampled", samples=96)
+def test_cfg4_full_size():
+    # every written row (4 requests x 61 nodes x 64 heads over 32829 keys, 8 splits)
+    run(gen.make_workload(4))
 
 
-def test_cfg5_full_size_sampled():
-    run(gen.make_workload(5), attention="sampled", samples=96)
+def test_cfg5_full_size():
+    # every written row of 64 requests with trees of 8..64 nodes over 4096-token prefixes
+    run(gen.make_workload(5))
 
 
-def test_cfg3_full_size_sampled_more_rows():
-    run(gen.make_workload(3), attention="sampled", samples=256, seed=3)
+def _scaled_v(w, factor):
+    v = (w.Vc.astype(np.uint32) << np.uint32(16)).view(np.float32) * np.float32(factor)
+    w.Vc = gen.f32_to_bf16_bits(v)
+    return w
+
+
+@pytest.mark.parametrize("factor", [1e5, 1e-6])
+def test_split_partials_keep_the_range_of_v(factor):
+    """V scaled far above fp16's largest value (|v| up to ~2e5) and far below its
+    normal range (~1e-7): outputs through the split-KV partials (one request over a
+    2048-token prefix: 11 splits; two over 9000 tokens: 8 splits) must keep bf16's
+    range, like the unsplit path and the oracle.  The bars apply in units of the
+    scale (attention is linear in V)."""
+    run(_scaled_v(gen.make_workload(2), factor), v_scale=factor)
+    run(_scaled_v(gen.make_workload(4, batch=2, prefix=9000), factor), v_scale=factor)
+    # the unsplit path (a short prefix: one split) against the same bar
+    run(_scaled_v(gen.make_workload(2, prefix=100), factor), v_scale=factor)
 
 
 # ----------------------------------------------------------------------------- tree shapes

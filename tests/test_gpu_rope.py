@@ -38,8 +38,9 @@ def test_rope_fp32_static_tree():
     run(gen.make_workload(1), 10000.0)
 
 
-def test_rope_long_context_sampled():
-    run(gen.make_workload(4), 500000.0, attention="sampled", samples=96)
+def test_rope_long_context_full_size():
+    # positions ~32800, every written row
+    run(gen.make_workload(4), 500000.0)
 
 
 @pytest.mark.parametrize("theta", [10000.0, 1.0e6])

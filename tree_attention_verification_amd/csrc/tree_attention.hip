@@ -29,8 +29,9 @@
 //   * The tree mask is read once per row (one 64-bit word) and only the tile(s)
 //     reaching past the prefix apply it; no T x T boolean is formed.
 //   * Long key ranges are split across workgroups (split-KV); each split writes
-//     its running max and row sum (fp32) and its normalised output (fp16, half
-//     the bytes of fp32; the values are bounded by max |v|), and k_attn_combine
+//     its running max and row sum (fp32) and its normalised output (bf16: half
+//     the bytes of fp32 with fp32's exponent range, so any finite bf16 V stays
+//     finite and small outputs keep their relative precision), and k_attn_combine
 //     merges them with a log-sum-exp weighting.  With several requests the splits
 //     follow each request's own length and the longest requests start first.
 //   * K/V tile 0, the Q fragments and the mask row are requested before the
@@ -173,7 +174,7 @@ __global__ __launch_bounds__(NW * 64, (NSTAGE == 2 && NW == 4) ? 2 : 1) void k_a
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Kc, const uint16_t* __restrict__ Vc,
     long long S_cap, const int* __restrict__ prefix_len, const int* __restrict__ tree_size,
     const uint32_t* __restrict__ tree_mask, const int* __restrict__ status, int T_max, int Hq, int Hkv, int W,
-    float sl2, uint16_t* __restrict__ O, _Float16* __restrict__ ws_o, float* __restrict__ ws_ml, int n_split,
+    float sl2, uint16_t* __restrict__ O, uint16_t* __restrict__ ws_o, float* __restrict__ ws_ml, int n_split,
     int chunk_keys, int n_rowblk, int n_units, long long m_pad, int B, int rel, Paging pg, Rope rope) {
   constexpr int NT = NW * 64;
   constexpr int KSTEPS = D / 16;     // 16-wide k-steps of QK^T (KSTEPS/2 per half of d)
@@ -646,7 +647,7 @@ __global__ __launch_bounds__(NW * 64, (NSTAGE == 2 && NW == 4) ? 2 : 1) void k_a
       }
   } else {
     const long long prow = ((long long)bg * n_split + split) * m_pad + r;
-    _Float16* wp = ws_o + prow * D;
+    uint16_t* wp = ws_o + prow * D;
     // a split can see no key of a row (tree keys only, none an ancestor): l = 0
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
 #pragma unroll
@@ -654,10 +655,10 @@ __global__ __launch_bounds__(NW * 64, (NSTAGE == 2 && NW == 4) ? 2 : 1) void k_a
 #pragma unroll
       for (int v4 = 0; v4 < 4; ++v4) {
         const int d0 = 32 * db + 8 * v4 + 4 * h;
-        typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-        *reinterpret_cast<h4*>(wp + d0) =
-            h4{(_Float16)(acc[db][4 * v4 + 0] * inv), (_Float16)(acc[db][4 * v4 + 1] * inv),
-               (_Float16)(acc[db][4 * v4 + 2] * inv), (_Float16)(acc[db][4 * v4 + 3] * inv)};
+        u32x2 w2;
+        w2[0] = pack_bf16(acc[db][4 * v4 + 0] * inv, acc[db][4 * v4 + 1] * inv);
+        w2[1] = pack_bf16(acc[db][4 * v4 + 2] * inv, acc[db][4 * v4 + 3] * inv);
+        *reinterpret_cast<u32x2*>(wp + d0) = w2;
       }
     if (h == 0) {
       ws_ml[2 * prow] = m_run;
@@ -666,20 +667,20 @@ __global__ __launch_bounds__(NW * 64, (NSTAGE == 2 && NW == 4) ? 2 : 1) void k_a
   }
 }
 
-// Merge split partials.  Split s left its normalised output o_s (fp16), its
+// Merge split partials.  Split s left its normalised output o_s (bf16), its
 // running max m_s (log2 domain) and its row sum l_s; the result is
 // sum_s w_s o_s / sum_s w_s with w_s = exp2(m_s - max m) l_s.  Splits are read
 // BATCH at a time (all loads in flight together; BATCH >= the split count up to
 // 16, so a call with few splits issues no redundant loads) and merged online.
 template <int D, int BATCH>
-__global__ __launch_bounds__(256) void k_attn_combine(const _Float16* __restrict__ ws_o,
+__global__ __launch_bounds__(256) void k_attn_combine(const uint16_t* __restrict__ ws_o,
                                                       const float* __restrict__ ws_ml,
                                                       const int* __restrict__ prefix_len,
                                                       const int* __restrict__ tree_size,
                                                       const int* __restrict__ status, long long S_cap, int T_max,
                                                       int Hq, int Hkv, int n_split, int chunk_keys, long long m_pad,
                                                       int rel, uint16_t* __restrict__ O) {
-  typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+  typedef __bf16 h8 __attribute__((ext_vector_type(8)));
   constexpr int TPR = D / 8;          // threads per row, 8 outputs each
   constexpr int RPB = 256 / TPR;      // rows per block
   const int bg = blockIdx.x;
@@ -836,7 +837,7 @@ __global__ __launch_bounds__(64) void k_attn_fp32(const float* __restrict__ Q, c
 template <int D, int NW, int NS, bool PAGED, bool ROPE>
 void launch_bf16(const Plan& p, int B, hipStream_t s, const void* Q, const void* Kc, const void* Vc, long long S_cap,
                  const int* prefix_len, const int* tree_size, const uint32_t* tree_mask, const int* status,
-                 int T_max, int Hq, int Hkv, int W, float sl2, void* O, _Float16* ws_o, float* ws_ml,
+                 int T_max, int Hq, int Hkv, int W, float sl2, void* O, uint16_t* ws_o, float* ws_ml,
                  const Paging& pg, const Rope& rope) {
   hipLaunchKernelGGL((k_attn_bf16<D, NW, NS, PAGED, ROPE>), dim3(p.grid), dim3(NW * 64), 0, s, (const uint16_t*)Q,
                      (const uint16_t*)Kc, (const uint16_t*)Vc, S_cap, prefix_len, tree_size, tree_mask, status, T_max,
@@ -846,7 +847,7 @@ void launch_bf16(const Plan& p, int B, hipStream_t s, const void* Q, const void*
 
 size_t ws_bytes_for(const Plan& p, int B, int Hkv, int d) {
   if (p.n_split <= 1) return 0;
-  return (size_t)B * Hkv * p.n_split * p.m_pad * ((size_t)d * sizeof(_Float16) + 2 * sizeof(float)) + 256;
+  return (size_t)B * Hkv * p.n_split * p.m_pad * ((size_t)d * sizeof(uint16_t) + 2 * sizeof(float)) + 256;
 }
 
 // Both entry points: S_cap is the rows each request can hold (the linear slab, or
@@ -894,7 +895,7 @@ int attention_impl(int dtype, int B, int T_max, int Hq, int Hkv, int d, const vo
   const Plan p = make_plan(B, T_max, Hq, Hkv, S_cap);
   const size_t need = ws_bytes_for(p, B, Hkv, d);
   if (need && (!workspace || ws_bytes < need)) return TV_EWORKSPACE;
-  _Float16* ws_o = reinterpret_cast<_Float16*>(workspace);
+  uint16_t* ws_o = reinterpret_cast<uint16_t*>(workspace);
   float* ws_ml = need ? reinterpret_cast<float*>(ws_o + (size_t)B * Hkv * p.n_split * p.m_pad * d) : nullptr;
   const float sl2 = scale * kLog2e;
 #define TV_ATTN_LAUNCH(DD, NWW, NSS, PG, RP)                                                                     \
