@@ -404,7 +404,10 @@ int tree_accept_sample_draft(int B, int T_max, int dcap, int V, const int* draft
  * head and k = 1..L (L = accept_len[b]) row P_b + k receives the old row
  * P_b + accept_path[b][k]; all sources of a (request, head, layer) are read
  * before any destination is written, so overlapping paths are safe.  Other rows
- * are untouched.  new_prefix_len[b] = P_b + L + 1 (nullable).  Requires
+ * are untouched.  new_prefix_len[b] = P_b + L + 1 (nullable); it must not
+ * overlap prefix_len, accept_len or accept_path (TV_EINVAL: the workgroups of a
+ * request read those while one of them writes new_prefix_len, so a prefix grown
+ * in place would move the wrong rows -- write it to a buffer of its own).  Requires
  * d*elem_bytes to be a multiple of 16 and <= 1024, dcap < 64, and
  * 2 * dcap * d * elem_bytes <= 65536 (the K and V rows of one path are staged
  * in on-chip memory; TV_EUNSUPPORTED otherwise).
@@ -421,7 +424,8 @@ int kv_compact(int B, int n_layers, int Hkv, int d, int elem_bytes, void* Kc, vo
  * is taken from draft_tokens/parents/target_predict directly).  Results equal
  * tree_accept then kv_compact on the same inputs.  For a step that runs both
  * calls back to back: each (request, kv head, layer) workgroup repeats the
- * request's walk, which saves one kernel boundary.
+ * request's walk, which saves one kernel boundary.  new_prefix_len must not
+ * overlap prefix_len (TV_EINVAL), as in kv_compact.
  * ------------------------------------------------------------------------- */
 int tree_accept_compact(int B, int T_max, int dcap, const int* draft_tokens, const int* parents,
                         const int* tree_size, const int* target_predict, const int* status,

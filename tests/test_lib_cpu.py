@@ -48,7 +48,7 @@ def test_tree_build_host_validation():
 
 def test_other_calls_host_validation():
     L = tv.lib()
-    # tree_mask_positions: dcap must be < T_max, T_max <= 64
+    # tree_mask_positions: dcap must be < T_max, T_max <= 256
     assert L.tree_mask_positions(1, 64, 64, X, X, X, X, X, X, X, X, None, None, None, X, None) == tv.TV_EINVAL
     assert L.tree_mask_positions(1, 257, 7, X, X, X, X, X, X, X, X, None, None, None, X, None) == tv.TV_EUNSUPPORTED
     # tree_attention: Hq % Hkv, head dim, dtype, misaligned pointers, workspace
@@ -67,6 +67,28 @@ def test_other_calls_host_validation():
     # kv_compact: row bytes must be a multiple of 16
     assert L.kv_compact(1, 1, 8, 100, 2, X, X, 4096, 0, X, X, X, 7, None, None) == tv.TV_EUNSUPPORTED
     assert L.kv_compact(1, 1, 8, 128, 3, X, X, 4096, 0, X, X, X, 7, None, None) == tv.TV_EINVAL
+
+
+def test_compaction_refuses_new_prefix_len_aliasing_its_inputs():
+    # new_prefix_len written over prefix_len (a prefix grown in place), accept_len or
+    # accept_path would race with the workgroups still reading them
+    L = tv.lib()
+    pre, path, alen, new = (ctypes.c_void_p(a) for a in (0x10000, 0x20000, 0x30000, 0x40000))
+    inside = ctypes.c_void_p(0x20000 + 4 * 8 * 3)          # inside accept_path [4][8]
+    # kv_compact(B, n_layers, Hkv, d, elem, K, V, S_cap, stride, prefix, path, len, dcap, newlen, stream)
+    assert L.kv_compact(4, 1, 8, 128, 2, X, X, 4096, 0, pre, path, alen, 7, pre, None) == tv.TV_EINVAL
+    assert L.kv_compact(4, 1, 8, 128, 2, X, X, 4096, 0, pre, path, alen, 7, alen, None) == tv.TV_EINVAL
+    assert L.kv_compact(4, 1, 8, 128, 2, X, X, 4096, 0, pre, path, alen, 7, inside, None) == tv.TV_EINVAL
+    shifted = ctypes.c_void_p(0x10000 + 12)                # overlapping the last entry
+    assert L.kv_compact(4, 1, 8, 128, 2, X, X, 4096, 0, pre, path, alen, 7, shifted, None) == tv.TV_EINVAL
+    assert L.kv_compact_paged(4, 1, 8, 128, 2, X, X, 100, 16, X, 10, 0, pre, path, alen, 7, pre,
+                              None) == tv.TV_EINVAL
+    # tree_accept_compact(B, T_max, dcap, tokens, parents, size, predict, status, len, path, bonus, n_layers, Hkv,
+    #                     d, elem, K, V, S_cap, stride, prefix, newlen, stream)
+    assert L.tree_accept_compact(4, 16, 7, X, X, X, X, X, alen, path, X, 1, 8, 128, 2, X, X, 4096, 0, pre, pre,
+                                 None) == tv.TV_EINVAL
+    assert L.tree_accept_compact_paged(4, 16, 7, X, X, X, X, X, alen, path, X, 1, 8, 128, 2, X, X, 100, 16, X, 10,
+                                       0, pre, pre, None) == tv.TV_EINVAL
 
 
 def test_python_binding_refuses_host_tensors():

@@ -600,6 +600,12 @@ int paged_args(int B, int Hkv, int d, long long num_blocks, int tokens_per_block
   return TV_OK;
 }
 
+// [a, a + na) and [b, b + nb) share a byte (host: pointers are only compared)
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return a && b && x < y + nb && y < x + na;
+}
+
 int kv_compact_impl(int B, int n_layers, int Hkv, int d, int elem_bytes, void* Kc, void* Vc, long long S_cap,
                     long long per_layer, long long layer_stride_elems, const int* prefix_len, const int* accept_path,
                     const int* accept_len, int dcap, int* new_prefix_len, void* stream, const Paging& pg) {
@@ -609,6 +615,11 @@ int kv_compact_impl(int B, int n_layers, int Hkv, int d, int elem_bytes, void* K
                                 &chunks16, &stage);
   if (rc != TV_OK) return rc;
   if (!prefix_len || !accept_path || !accept_len) return TV_EINVAL;
+  // every workgroup of a request reads these while one of them writes new_prefix_len
+  const size_t nb = (size_t)B * sizeof(int);
+  if (overlaps(new_prefix_len, nb, prefix_len, nb) || overlaps(new_prefix_len, nb, accept_len, nb) ||
+      overlaps(new_prefix_len, nb, accept_path, nb * (dcap + 1)))
+    return TV_EINVAL;
   hipLaunchKernelGGL(k_kv_compact, dim3(B * Hkv, n_layers), dim3(kCompactThreads), stage,
                      reinterpret_cast<hipStream_t>(stream), Hkv, chunks16, reinterpret_cast<uint4*>(Kc),
                      reinterpret_cast<uint4*>(Vc), S_cap, layer_stride_elems * elem_bytes / 16, prefix_len,
@@ -634,6 +645,9 @@ int accept_compact_impl(int B, int T_max, int dcap, const int* draft_tokens, con
                                 &chunks16, &stage);
   if (rc != TV_OK) return rc;
   if (!prefix_len) return TV_EINVAL;
+  // every workgroup of a request reads prefix_len while one of them writes new_prefix_len
+  const size_t nb = (size_t)B * sizeof(int);
+  if (overlaps(new_prefix_len, nb, prefix_len, nb)) return TV_EINVAL;
   hipLaunchKernelGGL(k_accept_compact, dim3(B * Hkv, n_layers), dim3(kCompactThreads), stage,
                      reinterpret_cast<hipStream_t>(stream), T_max, dcap, draft_tokens, parents, tree_size,
                      target_predict, status, accept_len, accept_path, bonus_token, Hkv, chunks16,
