@@ -3,9 +3,13 @@
 A step = tree_build -> tree_mask_positions -> tree_attention -> tree_accept ->
 kv_compact over one batch of synthetic inputs, all through the C ABI on one HIP
 stream (by default through tree_build_meta, tree_attention, tree_accept_compact:
-the same five stages in two kernel launches fewer; --unfused runs five calls).  The default workload is the EAGLE-2 dynamic tree at batch 1 (top_k 10,
-depth 6, 60 draft nodes + root, prefix 2048, Llama-3-8B attention heads 32/8/128,
-bf16); --config 1..5 selects another of the five measured workloads, and
+the same five stages in two kernel launches fewer; --unfused runs five calls).
+The default workload is the largest one that fits one GPU: 64 requests over
+4096-token prefixes with random trees of 8..64 nodes (depth <= 7), Llama-3-8B
+attention heads 32/8/128, bf16, ~1.1 GB of K/V (the tree-build stage is the
+metadata call, the trees being given); --config 1..4 selects another of the five
+workloads (2: the EAGLE-2 dynamic tree at batch 1, top_k 10, depth 6, 60 draft
+nodes + root over a 2048-token prefix), and
 --paged N keeps the K/V cache in a paged pool of N-token blocks placed at seeded
 random physical blocks (tree_attention_paged, tree_accept_compact_paged /
 kv_compact_paged through the block table).
@@ -19,7 +23,7 @@ same kernels and arguments, without per-call host launch overhead; --no-graph
 reports the eager rate instead).  Prints ONE JSON line on stdout; diagnostics go
 to stderr.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 5]
 """
 from __future__ import annotations
 
@@ -180,6 +184,7 @@ def cpu_baseline(w, seconds: float, paged=None):
         total_t += time.perf_counter() - t0
         reps += 1
     return {"value": total_nodes / total_t, "unit": "tree-nodes/s", "cores": int(threads), "kind": "oracle",
+            "host_cpu_count": os.cpu_count(),
             "sample": f"{reps} full step(s) of the first {nb} of {w.B} request(s) ({total_t:.1f} s; tree ops "
                       f"single-threaded, float64 attention on {threads} BLAS thread(s))"}
 
@@ -189,7 +194,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--config", type=int, default=5)
     ap.add_argument("--rotate-mb", type=float, default=512.0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
