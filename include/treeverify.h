@@ -250,6 +250,28 @@ int tree_attention(int dtype, int B, int T_max, int Hq, int Hkv, int d,
                    void* workspace, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------- *
+ * tree_attention_noalloc -- tree_attention for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, checks and results as
+ * tree_attention, without the workspace: the split-KV partials go to a scratch
+ * array the library holds in device memory, one per GPU, of
+ * tree_attention_noalloc_max_bytes() bytes (64 MiB), kept until the process
+ * ends.  A shape whose tree_attention_workspace_bytes(...) exceeds that is
+ * refused with TV_EWORKSPACE before any device call.  The call allocates
+ * nothing; its first call on a device looks up that device's scratch address
+ * (TV_ELAUNCH if the runtime cannot).  Every call on one GPU shares the array:
+ * calls that overlap on one GPU (concurrent streams, or threads) race on it and
+ * must be serialised by the caller.  Nothing in the scratch needs clearing
+ * between calls.
+ * ------------------------------------------------------------------------- */
+size_t tree_attention_noalloc_max_bytes(void);
+int tree_attention_noalloc(int dtype, int B, int T_max, int Hq, int Hkv, int d,
+                           const void* Q, const void* Kc, const void* Vc, long long S_cap,
+                           const int* prefix_len, const int* tree_size,
+                           const uint32_t* tree_mask, const int* status, float scale, void* O,
+                           void* stream);
+
+/* ------------------------------------------------------------------------- *
  * tree_attention_rope -- tree_attention with the rotary position embedding of
  * the queries fused in ([HB] forward_with_mask rotates the tree's queries and
  * keys at position prefix + depth, siblings sharing a position).

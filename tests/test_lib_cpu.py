@@ -203,3 +203,16 @@ def test_sampling_calls_host_validation():
     assert L.tree_accept_sample_draft(*bad(16, 799)) == tv.TV_EWORKSPACE            # workspace too small
     assert L.tree_accept_sample_draft(*bad(15, ctypes.c_void_p(0x200004))) == tv.TV_EWORKSPACE   # misaligned
     assert L.tree_accept_sample_draft(*bad(15, None)) == tv.TV_EWORKSPACE
+
+
+def test_noalloc_attention_refuses_partials_beyond_its_scratch():
+    # 511 requests with 256 query rows each and two key splits need ~66 MiB of split
+    # partials: more than the 64 MiB scratch, refused before any device call
+    L = tv.lib()
+    cap = tv.tree_attention_noalloc_max_bytes()
+    assert cap == 64 << 20
+    assert tv.tree_attention_workspace_bytes(0, 511, 64, 4, 1, 128, 4096) > cap
+    assert L.tree_attention_noalloc(0, 511, 64, 4, 1, 128, X, X, X, 4096, X, X, X, X, 0.0, X,
+                                    None) == tv.TV_EWORKSPACE
+    # the argument checks of tree_attention still apply
+    assert L.tree_attention_noalloc(0, 1, 64, 6, 4, 128, X, X, X, 4096, X, X, X, X, 0.0, X, None) == tv.TV_EINVAL

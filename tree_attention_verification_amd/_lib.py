@@ -47,6 +47,8 @@ _SIGS = {
     "tree_build_meta": (I, [I, I, I, I, I, I, P, I, P, I, P, I, P, P, P, P, P, P, SZ, I, P, P, P, P, P, P, P, P, P]),
     "tree_attention_workspace_bytes": (SZ, [I, I, I, I, I, I, LL]),
     "tree_attention": (I, [I, I, I, I, I, I, P, P, P, LL, P, P, P, P, F, P, P, SZ, P]),
+    "tree_attention_noalloc": (I, [I, I, I, I, I, I, P, P, P, LL, P, P, P, P, F, P, P]),
+    "tree_attention_noalloc_max_bytes": (SZ, []),
     "tree_accept": (I, [I, I, I, P, P, P, P, P, P, P, P, P]),
     "kv_compact": (I, [I, I, I, I, I, P, P, LL, LL, P, P, P, I, P, P]),
     "tree_accept_compact": (I, [I, I, I, P, P, P, P, P, P, P, P, I, I, I, I, P, P, LL, LL, P, P, P]),
@@ -190,6 +192,19 @@ def tree_attention(dtype, B, T_max, Hq, Hkv, d, Q, Kc, Vc, S_cap, prefix_len, tr
                               _dev(tree_mask, "tree_mask"), _dev(status, "status"), float(scale), _dev(O, "O"),
                               wp, wn, _stream(stream))
     _check("tree_attention", rc)
+
+
+def tree_attention_noalloc_max_bytes() -> int:
+    return int(lib().tree_attention_noalloc_max_bytes())
+
+
+def tree_attention_noalloc(dtype, B, T_max, Hq, Hkv, d, Q, Kc, Vc, S_cap, prefix_len, tree_size, tree_mask, status,
+                           scale, O, stream=None):
+    rc = lib().tree_attention_noalloc(dtype, B, T_max, Hq, Hkv, d, _dev(Q, "Q"), _dev(Kc, "Kc"), _dev(Vc, "Vc"),
+                                      S_cap, _dev(prefix_len, "prefix_len"), _dev(tree_size, "tree_size"),
+                                      _dev(tree_mask, "tree_mask"), _dev(status, "status"), float(scale),
+                                      _dev(O, "O"), _stream(stream))
+    _check("tree_attention_noalloc", rc)
 
 
 def tree_accept(B, T_max, dcap, draft_tokens, parents, tree_size, target_predict, status, accept_len, accept_path,

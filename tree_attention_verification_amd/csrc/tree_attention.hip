@@ -45,6 +45,8 @@
 // over lanes with a per-lane online softmax, merged through LDS.
 #include "tv_common.h"
 
+#include <mutex>
+
 namespace tv {
 namespace {
 
@@ -940,6 +942,41 @@ int attention_impl(int dtype, int B, int T_max, int Hq, int Hkv, int d, const vo
 }  // namespace
 }  // namespace tv
 
+namespace tv {
+constexpr size_t kScratchBytes = 64ull << 20;
+}
+
+// Scratch of tree_attention_noalloc: the split-KV partials live in this
+// file-scope device array instead of a caller workspace.  Each GPU the library
+// runs on holds its own copy (64 MiB) until the process ends.  Host code never
+// passes the array's name to a kernel: on the host it is a stand-in, not a device
+// address.  Its address on each device comes from hipGetSymbolAddress, taken
+// once per device with that device current, and is used instead.
+static __device__ __align__(256) unsigned char scratch[tv::kScratchBytes];
+
+namespace tv {
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// the current device's address of `scratch` (nullptr on failure)
+void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+}  // namespace tv
+
 extern "C" size_t tree_attention_workspace_bytes(int dtype, int B, int T_max, int Hq, int Hkv, int d,
                                                  long long S_cap) {
   if (dtype != TV_DTYPE_BF16 || B <= 0 || T_max <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || S_cap <= 0) return 0;
@@ -953,6 +990,26 @@ extern "C" int tree_attention(int dtype, int B, int T_max, int Hq, int Hkv, int 
                               size_t ws_bytes, void* stream) {
   return tv::attention_impl(dtype, B, T_max, Hq, Hkv, d, Q, Kc, Vc, S_cap, prefix_len, tree_size, tree_mask, status,
                             scale, O, workspace, ws_bytes, stream, tv::Paging{});
+}
+
+extern "C" size_t tree_attention_noalloc_max_bytes(void) { return tv::kScratchBytes; }
+
+extern "C" int tree_attention_noalloc(int dtype, int B, int T_max, int Hq, int Hkv, int d, const void* Q,
+                                      const void* Kc, const void* Vc, long long S_cap, const int* prefix_len,
+                                      const int* tree_size, const uint32_t* tree_mask, const int* status,
+                                      float scale, void* O, void* stream) {
+  // the sizes are checked on the host first: a call whose split partials would not
+  // fit the scratch array is refused before any device call
+  if (dtype == TV_DTYPE_BF16 && B > 0 && T_max > 0 && Hq > 0 && Hkv > 0 && Hq % Hkv == 0 && S_cap > 0 &&
+      tree_attention_workspace_bytes(dtype, B, T_max, Hq, Hkv, d, S_cap) > tv::kScratchBytes)
+    return TV_EWORKSPACE;
+  void* ws = nullptr;
+  if (dtype == TV_DTYPE_BF16 && tree_attention_workspace_bytes(dtype, B, T_max, Hq, Hkv, d, S_cap) > 0) {
+    ws = tv::scratch_on_current_device();
+    if (!ws) return TV_ELAUNCH;
+  }
+  return tv::attention_impl(dtype, B, T_max, Hq, Hkv, d, Q, Kc, Vc, S_cap, prefix_len, tree_size, tree_mask, status,
+                            scale, O, ws, ws ? tv::kScratchBytes : 0, stream, tv::Paging{});
 }
 
 extern "C" int tree_attention_rope(int dtype, int B, int T_max, int Hq, int Hkv, int d, const void* Q,
