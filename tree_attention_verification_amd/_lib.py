@@ -17,7 +17,9 @@ import re
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libtreeverify.so")
+# the in-tree build; TREEVERIFY_LIB names another build of the same library (e.g. one
+# whose host code is compiled with sanitizers, for the host-validation tests)
+LIB_PATH = os.environ.get("TREEVERIFY_LIB") or os.path.join(_HERE, "libtreeverify.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "treeverify.h")
 
 TV_OK, TV_EINVAL, TV_EUNSUPPORTED, TV_EWORKSPACE, TV_ELAUNCH = 0, -1, -2, -3, -4
