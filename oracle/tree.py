@@ -255,26 +255,21 @@ def validate(parents, tree_size: int, T_max: int, dcap: int) -> int:
 
 
 def ancestor_sets(parents, T: int):
-    """Row i of the tree mask: node i itself and every ancestor, found by walking the
-    parent pointers up to the root ([HB] tree_mask: the walk stops at parent -1)."""
+    """Row i of the tree mask as an integer bitset: node i and all of its ancestors
+    ([HB] tree_mask; [TRT] packed ancestor mask).  The ancestor relation is the
+    transitive closure of the parent relation; since a validated tree numbers every
+    parent before its children, the closure follows in one pass in node order:
+    A(i) = {i} united with A(parent of i)."""
     rows = []
     for i in range(T):
-        seen = set()
-        j = i
-        while j != -1:
-            seen.add(j)
-            j = parents[j]
-        rows.append(seen)
+        rows.append((1 << i) | (rows[parents[i]] if parents[i] >= 0 else 0))
     return rows
 
 
 def depths(parents, T: int):
-    """[HB] depths: 0 at the root, otherwise one more than the parent's depth
-    (parents precede children)."""
-    d = []
-    for i in range(T):
-        d.append(0 if parents[i] == -1 else d[parents[i]] + 1)
-    return d
+    """Depth of every node ([HB] depths; [E2] tree_position_ids): the number of its
+    ancestors other than itself, read off the ancestor bitsets."""
+    return [bin(a).count("1") - 1 for a in ancestor_sets(parents, T)]
 
 
 def mask_positions(parents, tree_size: int, prefix_len: int, T_max: int, dcap: int, status_in: int = 0):
@@ -296,8 +291,8 @@ def mask_positions(parents, tree_size: int, prefix_len: int, T_max: int, dcap: i
     dep = depths(par, T)
     mask = np.zeros((T_max, W), dtype=np.uint32)
     for i in range(T):
-        for j in rows[i]:
-            mask[i, j >> 5] |= np.uint32(1 << (j & 31))
+        for w in range(W):
+            mask[i, w] = np.uint32((rows[i] >> (32 * w)) & 0xFFFFFFFF)
     tpos = np.zeros(T_max, np.int32)
     pos = np.zeros(T_max, np.int32)
     for i in range(T):
@@ -338,14 +333,15 @@ def accept_walk(draft_tokens, parents, tree_size: int, target_predict, status: i
     path = [0]
     if status == ST_OK:
         T = int(tree_size)
-        node = 0
+        # (parent, token) -> the lowest-index child of that parent carrying that token
+        step = {}
+        for c in range(1, T):
+            step.setdefault((int(parents[c]), int(draft_tokens[c])), c)
         while len(path) <= dcap:
-            pred = target_predict[node]
-            child = next((c for c in range(1, T) if parents[c] == node and draft_tokens[c] == pred), None)
-            if child is None:
+            nxt = step.get((path[-1], int(target_predict[path[-1]])))
+            if nxt is None:
                 break
-            path.append(child)
-            node = child
+            path.append(nxt)
     padded = path + [-1] * (dcap + 1 - len(path))
     return len(path) - 1, padded, int(target_predict[path[-1]])
 
