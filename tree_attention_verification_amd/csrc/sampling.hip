@@ -25,6 +25,9 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxV = 262144;  // vocabulary limit (the removed-token bitmap is 32 KB of LDS)
+constexpr int kKlMaxV = 32768;   // largest row whose keys stay in LDS (128 KB)
+constexpr int kOnDemandK = 4096; // top-k survivors up to which weights are formed on demand
+constexpr int kFastK = 256;      // top-k up to which the candidates of a threshold are ranked directly
 
 __device__ __forceinline__ double wave_sum_d(double v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
@@ -337,8 +340,12 @@ __device__ __forceinline__ float key_float(uint32_t k) {
 // token ranges.
 // --------------------------------------------------------------------------
 // NPT > 0: V <= NPT NT and every thread keeps its NPT (key, weight) pairs in
-// registers after the first read; NPT = 0: the row is re-read on every pass.
-template <int NT, int NPT>
+// registers after the first read; NPT = 0: KL: the keys are kept in LDS (V <=
+// kKlMaxV), else the logits are re-read on every pass.
+// With top-k on and at most kOnDemandK survivors, the weights are formed only
+// for the tokens that need one (the survivors), when they need it; otherwise
+// every weight is formed once and kept (registers, or the output row).
+template <int NT, int NPT, bool KL = false>
 __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const float* __restrict__ logits,
                                                              const int* __restrict__ tree_size,
                                                              const int* __restrict__ status,
@@ -359,13 +366,20 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
   __shared__ double s_d[NW * 16];
   __shared__ unsigned long long s_u[NW];
   __shared__ Wide s_w[NW];
-  // radix bins (per-wavefront counts, or NL x 256 limbs of weight sums), ballot
-  // entries (V / 64), or the survivor list
-  __shared__ unsigned long long s_hist[4096];
-  static_assert(NW * 256 <= 4096 && NL * 256 <= 4096, "radix bins fit");
+  // radix bins (counts: CSETS sets of 256, shared by the wavefronts w % CSETS; or
+  // NL x 256 limbs of weight sums), ballot entries (V / 64), or the survivor list
+  constexpr int CSETS = KL ? 4 : NW;
+  constexpr int HIST = KL ? NL * 256 : 4096;
+  __shared__ unsigned long long s_hist[HIST];
+  static_assert(CSETS * 256 <= HIST && NL * 256 <= HIST && NT <= HIST && (!KL || kKlMaxV / 64 <= HIST),
+                "radix bins, survivor list and ballot entries fit");
   __shared__ Norm s_abv;
+  __shared__ Wide s_wt_total;
+  __shared__ unsigned long long s_top[NT];  // the top-k survivors in rank order (top-k fast path)
   __shared__ unsigned long long s_abvc;
   __shared__ int s_pick, s_sel, s_cnt;
+  extern __shared__ uint32_t s_key[];  // KL: the order key of token v
+  static_assert(!KL || (NPT == 0 && NT == 1024), "keys in LDS: 1024 threads, no register copy");
 
   // the first-ranked token
   struct KW {
@@ -383,6 +397,20 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
     for (int j = 0; j < NPT; ++j) {
       reg[j].k = logit_key(x[j]);
       if (tid + j * NT < V) best = umax64(best, rank_key(clean_logit(x[j]), (uint32_t)(tid + j * NT)));
+    }
+  } else if constexpr (KL) {
+    // the whole row in flight at once (up to kKlMaxV / NT = 32 tokens per thread)
+    constexpr int J = kKlMaxV / NT;
+    float x[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) x[j] = tid + j * NT < V ? lr[tid + j * NT] : -INFINITY;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int v = tid + j * NT;
+      if (v < V) {
+        s_key[v] = logit_key(x[j]);  // read back by this thread only (the same v in every pass)
+        best = umax64(best, rank_key(clean_logit(x[j]), (uint32_t)v));
+      }
     }
   } else {
     row_pass<NT>(V, ld_l, [&](int v, float x) { best = umax64(best, rank_key(clean_logit(x), (uint32_t)v)); });
@@ -402,9 +430,15 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
   auto weight = [&](uint32_t key) -> float {
     return key == kmax ? 1.0f : (float)exp(((double)key_float(key) - dmax) / dtau);
   };
-  // (NPT = 0: the weights go to the output row, and each thread re-reads only the
-  // weights it wrote: the same v in every row pass)
-  auto ld_kw = [&](int v) { return KW{logit_key(lr[v]), orow[v]}; };
+  // Weights formed on demand (top-k on with few survivors) or kept: NPT > 0 in
+  // registers, NPT = 0 in the output row, where each thread re-reads only the
+  // weights it wrote (the same v in every row pass).
+  const bool stored = NPT > 0 || !(kk > 1 && kk < V && kk <= kOnDemandK);
+  auto wt = [&](uint32_t k, float w) -> float { return stored ? w : weight(k); };
+  auto ld_kw = [&](int v) {
+    const uint32_t k = KL ? s_key[v] : logit_key(lr[v]);
+    return KW{k, stored ? orow[v] : 0.0f};
+  };
   // one pass over the row: body(v, KW) for this thread's tokens in increasing v
   auto pass = [&](auto body) __attribute__((always_inline)) {
     if constexpr (NPT > 0) {
@@ -415,14 +449,21 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
       row_pass<NT>(V, ld_kw, body);
     }
   };
-  // the workgroup's sum of one Wide per thread (every thread gets it, carry-save)
+  // the workgroup's sum of one Wide per thread (every thread gets it, carry-save):
+  // wavefront totals by butterfly, then the first wavefront adds them
   auto block_wsum = [&](Wide v) -> Wide {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) wadd(v, wshfl_xor(v, o));
     if ((tid & 63) == 0) s_w[tid >> 6] = v;
     __syncthreads();
-    Wide t = wzero();
-    for (int w = 0; w < NW; ++w) wadd(t, s_w[w]);
+    if (tid < 64) {
+      Wide t = (tid < NW) ? s_w[tid] : wzero();
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) wadd(t, wshfl_xor(t, o));
+      if (tid == 0) s_wt_total = t;
+    }
+    __syncthreads();
+    const Wide t = s_wt_total;
     __syncthreads();
     return t;
   };
@@ -434,12 +475,20 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
       reg[j].w = weight(reg[j].k);
       if (with_p && tid + j * NT < V) wadd(w_all, wide_of(reg[j].w));
     }
-  } else {
-    row_pass<NT>(V, ld_l, [&](int v, float x) {
-      const float w = weight(logit_key(x));
-      orow[v] = w;
-      if (with_p) wadd(w_all, wide_of(w));
-    });
+  } else if (stored) {
+    if constexpr (KL) {
+      for (int v = tid; v < V; v += NT) {
+        const float w = weight(s_key[v]);
+        orow[v] = w;
+        if (with_p) wadd(w_all, wide_of(w));
+      }
+    } else {
+      row_pass<NT>(V, ld_l, [&](int v, float x) {
+        const float w = weight(logit_key(x));
+        orow[v] = w;
+        if (with_p) wadd(w_all, wide_of(w));
+      });
+    }
   }
 
   const int lane = tid & 63, wave = tid >> 6;
@@ -458,7 +507,7 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
       const bool f = v < V && k == t && (k > tk || v <= ck);
       const unsigned long long m = __ballot(f);
       if (lane == 0) s_hist[j * NW + wave] = m;
-      if (mass && v < V && k > t) wadd(ma, wide_of(w));
+      if (mass && v < V && k > t) wadd(ma, wide_of(wt(k, w)));
     };
     if (tid == 0) s_pick = V;
     if constexpr (NPT > 0) {
@@ -516,14 +565,15 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
   // the highest bin at which the running total reaches the target is chosen.
   // Counts (top-k): the key of the kk-th ranked token and the number of tokens
   // with larger keys.
-  auto radix_count = [&](int kk_, uint32_t& t_out, int& above_out) {
+  // `visit(f)` calls f(key) for every element counted (each token, or one value per thread).
+  auto radix_count = [&](int kk_, uint32_t& t_out, int& above_out, auto visit) {
     uint32_t prefix = 0u, pmask = 0u;
     unsigned long long above = 0ull;
     for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int e = tid; e < NW * 256; e += NT) s_hist[e] = 0ull;
+      for (int e = tid; e < CSETS * 256; e += NT) s_hist[e] = 0ull;
       __syncthreads();
-      pass([&](int v, KW e) {
-        if ((e.k & pmask) == prefix) atomicAdd(&s_hist[wave * 256 + ((e.k >> shift) & 255u)], 1ull);
+      visit([&](uint32_t k) {
+        if ((k & pmask) == prefix) atomicAdd(&s_hist[(wave % CSETS) * 256 + ((k >> shift) & 255u)], 1ull);
       });
       __syncthreads();
       if (wave == 0) {
@@ -531,7 +581,7 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           m[j] = 0ull;
-          for (int w = 0; w < NW; ++w) m[j] += s_hist[w * 256 + 4 * lane + j];
+          for (int w = 0; w < CSETS; ++w) m[j] += s_hist[w * 256 + 4 * lane + j];
           g += m[j];
         }
         unsigned long long suf = g;  // total of this lane's bins and every higher lane's
@@ -578,10 +628,11 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
       for (int e = tid; e < NL * 256; e += NT) s_hist[e] = 0ull;
       __syncthreads();
       pass([&](int v, KW e) {
-        if ((e.k & pmask) == prefix && pred(e.k, v) && e.w > 0.0f) {
+        const float w = (e.k & pmask) == prefix && pred(e.k, v) ? wt(e.k, e.w) : 0.0f;
+        if (w > 0.0f) {
           int j;
           unsigned long long x;
-          weight_parts(e.w, j, x);
+          weight_parts(w, j, x);
           const int bin = (int)((e.k >> shift) & 255u);
           atomicAdd(&s_hist[j * 256 + bin], x & 0xFFFFFFFFull);
           if (x >> 32) atomicAdd(&s_hist[(j + 1) * 256 + bin], x >> 32);
@@ -640,15 +691,60 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
   // ---- top-k cut (tk, ck); the default keeps everything (every key is > 0)
   uint32_t tk = 0u;
   int ck = V;
-  Norm wk = with_p ? nuniform(norm_of(block_wsum(w_all))) : nzero();  // the survivors' exact total weight
-  if (kk > 1 && kk < V) {
-    int above = 0;
-    Wide ma = wzero();
-    radix_count(kk, tk, above);
-    const int need = kk - above;
-    ck = nth_with_key(tk, need, 0u, V, with_p, ma);
-    wadd(ma, wmul(wide_of(weight(tk)), (unsigned long long)need));
-    wk = nuniform(norm_of(ma));
+  Norm wk = nzero();  // the survivors' exact total weight (top-p)
+  // Fast path, 1 < top_k <= kFastK: at least top_k tokens reach tau, the key of
+  // the top_k-th best of the per-thread best tokens (each thread's best is a
+  // distinct token), so the top_k survivors are among the tokens whose key
+  // reaches tau: usually a few more than top_k.  They are gathered into LDS and
+  // ranked exactly by counting, which leaves them in rank order in s_top.  With
+  // more candidates than the list holds, the general path below runs instead.
+  bool sorted = false;
+  if (kk > 1 && kk <= kFastK && kk < V) {
+    unsigned long long tm = 0ull;  // this thread's best token as a rank key
+    pass([&](int v, KW e) { tm = umax64(tm, ((unsigned long long)e.k << 32) | (0xFFFFFFFFu - (uint32_t)v)); });
+    uint32_t tau_k = 0u;
+    int above_t = 0;
+    const uint32_t mk = (uint32_t)(tm >> 32);  // 0 (below every key) for a thread without tokens
+    radix_count(kk, tau_k, above_t, [&](auto f) { f(mk); });
+    unsigned long long* s_cand = s_hist;
+    if (tid == 0) s_cnt = 0;
+    __syncthreads();
+    pass([&](int v, KW e) {
+      if (e.k >= tau_k) {
+        const int pos = atomicAdd(&s_cnt, 1);
+        if (pos < HIST) s_cand[pos] = ((unsigned long long)e.k << 32) | (0xFFFFFFFFu - (uint32_t)v);
+      }
+    });
+    __syncthreads();
+    const int m = s_cnt;
+    if (m <= HIST) {
+      for (int t = tid; t < m; t += NT) {
+        const unsigned long long my = s_cand[t];
+        int rk = 0;
+        for (int o = 0; o < m; ++o) rk += s_cand[o] > my;  // (all lanes read the same entry)
+        if (rk < kk) s_top[rk] = my;
+      }
+      __syncthreads();
+      const unsigned long long last = s_top[kk - 1];
+      tk = (uint32_t)(last >> 32);
+      ck = (int)key_index(last);
+      sorted = true;
+      if (with_p) wk = nuniform(norm_of(block_wsum(tid < kk ? wide_of(weight((uint32_t)(s_top[tid] >> 32)))
+                                                               : wzero())));
+    }
+    __syncthreads();
+  }
+  if (!sorted) {
+    if (with_p) wk = nuniform(norm_of(block_wsum(w_all)));
+    if (kk > 1 && kk < V) {
+      int above = 0;
+      Wide ma = wzero();
+      radix_count(kk, tk, above, [&](auto f) { pass([&](int, KW e) { f(e.k); }); });
+      const int need = kk - above;
+      ck = nth_with_key(tk, need, 0u, V, with_p, ma);
+      wadd(ma, wmul(wide_of(weight(tk)), (unsigned long long)need));
+      wk = nuniform(norm_of(ma));
+    }
   }
   auto in_k = [&](uint32_t k, int v) { return k > tk || (k == tk && v <= ck); };
 
@@ -661,22 +757,24 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
   if (with_p && kk > 1 && kk <= NT) {
     // at most NT survivors: gathered into LDS as 64-bit rank keys (key,
     // then token ascending; the order of the appends does not matter), sorted
-    // descending by a bitonic network, then one exact prefix sum of their weights
-    // in rank order finds the cut
-    unsigned long long* s_list = s_hist;  // NT entries
-    if (tid == 0) s_cnt = 0;
-    __syncthreads();
-    pass([&](int v, KW e) {
-      if (in_k(e.k, v)) {
-        const int pos = atomicAdd(&s_cnt, 1);  // < kk by construction of the cut
-        if (pos < NT) s_list[pos] = rank_key(key_float(e.k), (uint32_t)v);
-      }
-    });
-    __syncthreads();
-    const int n = min(s_cnt, NT);  // == kk
+    // descending by a bitonic network (the fast path has them in order already),
+    // then one exact prefix sum of their weights in rank order finds the cut
+    unsigned long long* s_list = sorted ? s_top : s_hist;  // NT entries
+    const int n = sorted ? kk : min(kk, NT);
+    if (!sorted) {
+      if (tid == 0) s_cnt = 0;
+      __syncthreads();
+      pass([&](int v, KW e) {
+        if (in_k(e.k, v)) {
+          const int pos = atomicAdd(&s_cnt, 1);  // < kk by construction of the cut
+          if (pos < NT) s_list[pos] = rank_key(key_float(e.k), (uint32_t)v);
+        }
+      });
+      __syncthreads();
+    }
     if (tid >= n) s_list[tid] = 0ull;
     __syncthreads();
-    for (int k2 = 2; k2 <= NT; k2 <<= 1) {
+    for (int k2 = 2; !sorted && k2 <= NT; k2 <<= 1) {
       for (int j = k2 >> 1; j > 0; j >>= 1) {
         const int ixj = tid ^ j;
         if (ixj > tid) {
@@ -727,15 +825,20 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
   }
 
   // ---- min-p, the kept total and the output
-  auto keep = [&](uint32_t k, int v, float w) {
-    return in_k(k, v) && (k > tpk || (k == tpk && v <= cp)) && (!(mp > 0.0f) || w >= mp || v == tok0);
+  // the weight of a kept token, 0 for the others (a weight is formed only for the
+  // top-k and top-p survivors)
+  auto kept_w = [&](uint32_t k, int v, float w) -> float {
+    if (!(in_k(k, v) && (k > tpk || (k == tpk && v <= cp)))) return 0.0f;
+    const float x = wt(k, w);
+    return (!(mp > 0.0f) || x >= mp || v == tok0) ? x : 0.0f;
   };
   double wsum = 0.0;
-  pass([&](int v, KW e) {
-    if (keep(e.k, v, e.w)) wsum += (double)e.w;
-  });
+  pass([&](int v, KW e) { wsum += (double)kept_w(e.k, v, e.w); });
   const double W = block_sum_d<NT>(wsum, s_d);
-  pass([&](int v, KW e) { orow[v] = keep(e.k, v, e.w) ? (float)((double)e.w / W) : 0.0f; });
+  pass([&](int v, KW e) {
+    const float x = kept_w(e.k, v, e.w);
+    orow[v] = x > 0.0f ? (float)((double)x / W) : 0.0f;
+  });
 }
 
 // --------------------------------------------------------------------------
@@ -923,12 +1026,27 @@ extern "C" int tree_sampling_probs(int B, int T_max, int V, const float* logits,
   // so more threads per row finish it sooner).  Many rows: 256 threads per row,
   // several rows per CU hiding each other's latency.  Rows of up to 8 tokens per
   // thread stay in registers (more would spill).
+  // Rows that do not fit the registers but whose keys fit LDS: 1024 threads with
+  // the keys in LDS (one row per CU; every pass after the first read stays on chip).
   const bool many = (long long)B * T_max >= 512;
-  const int nt = many ? 256 : 1024;
+  int nt = many ? 256 : 1024;
   const bool regs = V <= 8 * nt;
-  auto k = many ? (regs ? tv::k_sampling_probs<256, 8> : tv::k_sampling_probs<256, 0>)
-                : (regs ? tv::k_sampling_probs<1024, 8> : tv::k_sampling_probs<1024, 0>);
-  hipLaunchKernelGGL(k, dim3(T_max, B), dim3(nt), 0, reinterpret_cast<hipStream_t>(stream), T_max, V, logits,
+  const bool kl = !regs && V <= tv::kKlMaxV;
+  if (kl) nt = 1024;
+  auto k = kl ? tv::k_sampling_probs<1024, 0, true>
+              : many ? (regs ? tv::k_sampling_probs<256, 8> : tv::k_sampling_probs<256, 0>)
+                     : (regs ? tv::k_sampling_probs<1024, 8> : tv::k_sampling_probs<1024, 0>);
+  const size_t dyn = kl ? (size_t)V * sizeof(uint32_t) : 0;
+  if (kl) {
+    static bool attr_set = false;  // the LDS a launch may ask for, raised once
+    if (!attr_set) {
+      if (hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)(tv::kKlMaxV * sizeof(uint32_t))) != hipSuccess)
+        return TV_ELAUNCH;
+      attr_set = true;
+    }
+  }
+  hipLaunchKernelGGL(k, dim3(T_max, B), dim3(nt), dyn, reinterpret_cast<hipStream_t>(stream), T_max, V, logits,
                      tree_size, status, temperature, top_k, top_p, min_p, probs);
   TV_CHECK_LAUNCH();
   return TV_OK;
