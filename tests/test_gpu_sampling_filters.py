@@ -169,6 +169,27 @@ def test_filters_many_rows_large_vocabulary(tie_step):
     run_filter(lg, w.given_size, None, (temp, top_k, top_p, min_p))
 
 
+@pytest.mark.parametrize("many", [False, True])
+@pytest.mark.parametrize("V", [50, 700, 32000])
+def test_filters_top_p_value_bins(many, V):
+    """Top-p without a small top-k: the first radix level bins the weights by value.
+    Temperatures from 0.05 (the weights spread over many bins) to 1e4 (every token in
+    the top bin, so the key levels run inside it), coarse ties, and top_k >= V (off)
+    and between 1025 and V (the radix top-k, then the bins over its survivors)."""
+    B, T_max = (8, 64) if many else (8, 2)
+    rng = np.random.default_rng(V + 11 * many)
+    lg = rng.normal(0, 2, (B, T_max, V)).astype(np.float32)
+    lg[2] = np.round(lg[2] * 2) / 2                      # ties on a grid of 0.5
+    lg[5] = np.round(lg[5] * 8) / 8
+    tree_size = np.full(B, T_max, np.int32)
+    tree_size[[1, 6]] = [3, 1]
+    temp = np.array([0.05, 1e4, 1.0, 0.7, 1.0, 2.0, 0.3, 1e4], np.float32)
+    top_k = np.array([0, 0, V + 3, V, min(V - 1, 1500), 0, 0, min(V - 1, 2000)], np.int32)
+    top_p = np.array([0.9, 0.5, 0.8, 0.95, 0.7, 0.999, 0.1, 0.6], np.float32)
+    min_p = np.array([0.0, 0.0, 0.0, 0.01, 0.0, 0.0, 0.0, 0.0], np.float32)
+    run_filter(lg, tree_size, None, (temp, top_k, top_p, min_p))
+
+
 @pytest.mark.parametrize("cfg", [2, 3])
 def test_filter_then_target_only_sampling(cfg):
     """The whole non-greedy chain: logits -> tree_sampling_probs -> tree_accept_sample,

@@ -26,7 +26,6 @@ constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxV = 262144;  // vocabulary limit (the removed-token bitmap is 32 KB of LDS)
 constexpr int kKlMaxV = 32768;   // largest row whose keys stay in LDS (128 KB)
-constexpr int kOnDemandK = 4096; // top-k survivors up to which weights are formed on demand
 constexpr int kFastK = 256;      // top-k up to which the candidates of a threshold are ranked directly
 
 __device__ __forceinline__ double wave_sum_d(double v) {
@@ -147,6 +146,18 @@ __device__ __forceinline__ Wide wide_of(float w) {
     r.l[i] = (i == j ? (x & 0xFFFFFFFFull) : 0ull) + (i == j + 1 ? (x >> 32) : 0ull);
   return r;
 }
+// ms 2^s units as a Wide, for ms < 2^44 and 0 <= s <= 126 (limbs chosen by
+// selects: nothing is indexed at run time)
+__device__ __forceinline__ Wide wide_shifted(unsigned long long ms, int s) {
+  const int q = s >> 5, r = s & 31;
+  const unsigned long long lo = ms << r, hi = r ? ms >> (64 - r) : 0ull;  // ms 2^r; hi < 2^13
+  Wide x;
+#pragma unroll
+  for (int i = 0; i < NL; ++i)
+    x.l[i] = (i == q ? (lo & 0xFFFFFFFFull) : 0ull) + (i == q + 1 ? (lo >> 32) : 0ull) + (i == q + 2 ? hi : 0ull) +
+             (i == NL - 1 && q + 2 == NL ? (hi << 32) : 0ull);
+  return x;
+}
 // A normalised sum: NN limbs of 32 bits (192 bits; a row's total is below 2^167)
 constexpr int NN = 6;
 struct Norm {
@@ -190,6 +201,12 @@ __device__ __forceinline__ bool nge(const Norm& a, const Norm& b) {
   }
   return gt || eq;
 }
+// an int / u32 / u64 every lane holds alike, moved to scalar registers
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ uint32_t uni(uint32_t x) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)x); }
+__device__ __forceinline__ unsigned long long uni(unsigned long long x) {
+  return ((unsigned long long)uni((uint32_t)(x >> 32)) << 32) | uni((uint32_t)x);
+}
 // a value every lane holds the same copy of: kept in scalar registers
 __device__ __forceinline__ Norm nuniform(const Norm& a) {
   Norm r;
@@ -201,6 +218,18 @@ __device__ __forceinline__ Norm nshfl_down(const Norm& a, int o) {
   Norm r;
 #pragma unroll
   for (int i = 0; i < NN; ++i) r.l[i] = (uint32_t)__shfl_down((int)a.l[i], o, 64);
+  return r;
+}
+__device__ __forceinline__ Norm nshfl(const Norm& a, int src) {
+  Norm r;
+#pragma unroll
+  for (int i = 0; i < NN; ++i) r.l[i] = (uint32_t)__shfl((int)a.l[i], src, 64);
+  return r;
+}
+__device__ __forceinline__ Wide wshfl_down(const Wide& a, int o) {
+  Wide r;
+#pragma unroll
+  for (int i = 0; i < NL; ++i) r.l[i] = __shfl_down(a.l[i], o, 64);
   return r;
 }
 __device__ __forceinline__ Wide wshfl_xor(const Wide& a, int m) {
@@ -254,6 +283,13 @@ __device__ __forceinline__ Norm nthreshold(float p, const Norm& z) {
   t[NN] = c;
   return nshr_ceil(t, 149 - s);
 }
+// the value of a sum in units of 2^-149, rounded to double
+__device__ __forceinline__ double norm_to_double(const Norm& a) {
+  double r = 0.0;
+#pragma unroll
+  for (int i = NN - 1; i >= 0; --i) r = r * 4294967296.0 + (double)a.l[i];
+  return r * 0x1p-149;
+}
 // the smallest n >= 1 with above + n c >= thr, for a float32 weight c > 0 and
 // above < thr (2^31 - 1 stands for anything larger)
 __device__ __forceinline__ int ntie_count(const Norm& thr, const Norm& above, float c) {
@@ -288,17 +324,35 @@ __device__ __forceinline__ int ntie_count(const Norm& thr, const Norm& above, fl
 // Visits v = threadIdx.x + j NT (j = 0, 1, ...) in increasing v, with the
 // loads of NB visits issued together (one memory round trip per NB entries);
 // indices past the row are clamped for the load and skipped for the body.
+// PF: the next NB loads are issued before the current ones are processed, so
+// that neither their latency nor stores in the body hold them up.
 constexpr int kNB = 8;
-template <int NT = kThreads, class Load, class Body>
+template <int NT = kThreads, bool PF = false, class Load, class Body>
 __device__ __forceinline__ void row_pass(int V, Load load, Body body) {
   using T = decltype(load(0));
-  for (int base = threadIdx.x; base < V; base += kNB * NT) {
+  if constexpr (PF) {
     T x[kNB];
 #pragma unroll
-    for (int j = 0; j < kNB; ++j) x[j] = load(min(base + j * NT, V - 1));
+    for (int j = 0; j < kNB; ++j) x[j] = load(min((int)threadIdx.x + j * NT, V - 1));
+    for (int base = threadIdx.x; base < V; base += kNB * NT) {
+      T y[kNB];
 #pragma unroll
-    for (int j = 0; j < kNB; ++j)
-      if (base + j * NT < V) body(base + j * NT, x[j]);
+      for (int j = 0; j < kNB; ++j) y[j] = load(min(base + (kNB + j) * NT, V - 1));
+#pragma unroll
+      for (int j = 0; j < kNB; ++j)
+        if (base + j * NT < V) body(base + j * NT, x[j]);
+#pragma unroll
+      for (int j = 0; j < kNB; ++j) x[j] = y[j];
+    }
+  } else {
+    for (int base = threadIdx.x; base < V; base += kNB * NT) {
+      T x[kNB];
+#pragma unroll
+      for (int j = 0; j < kNB; ++j) x[j] = load(min(base + j * NT, V - 1));
+#pragma unroll
+      for (int j = 0; j < kNB; ++j)
+        if (base + j * NT < V) body(base + j * NT, x[j]);
+    }
   }
 }
 // The same over a contiguous range [c0, c1), in order; body returns true to stop.
@@ -327,24 +381,26 @@ __device__ __forceinline__ float key_float(uint32_t k) {
 // --------------------------------------------------------------------------
 // tree_sampling_probs: one workgroup per (node row, request).
 //
-// Tokens rank by (logit descending, token ascending).  Weights
-// w = fp32(exp((l - l_max) / temperature)) (exactly 1 at the largest logit) are
-// written into the output row first and re-read from there.  Each filter keeps
-// a prefix of the ranking, described by a cut (key t, token c): token v with key
-// k is inside iff k > t or (k == t and v <= c).  The top-k and top-p cuts are
-// found by radix selection over the 32-bit order keys, eight bits per pass from
-// the top, with exact totals (counts for top-k; for top-p the exact sums of the
-// float32 weights, as Wide integers in units of 2^-149, and the exact threshold
-// ceil(top_p x total)).  Equal keys have equal weights; the cut inside a group of
-// equal keys is the n-th of them in token order, found by a scan over contiguous
-// token ranges.
+// Tokens rank by (logit descending, token ascending), with weights
+// w = fp32(exp((l - l_max) / temperature)) (exactly 1 at the largest logit).
+// Each filter keeps a prefix of the ranking, described by a cut (key t, token c):
+// token v with key k is inside iff k > t or (k == t and v <= c).  Both cuts are
+// found by radix selection over a 16-bit value code (a monotone map of the logit
+// that spreads the tokens over its bins), one byte per level, until the chosen
+// bin holds few enough tokens to rank them directly in LDS; key levels over the
+// 32-bit order keys take over only for bins of many equal or nearly equal
+// logits.  The top-k levels count tokens; the top-p levels sum the float32
+// weights exactly, as integers in units of 2^-149, against the exact threshold
+// ceil(top_p x total).  For a small top-k, the survivors come instead from the
+// few candidates that can make it, ranked directly, and top-p then cuts that
+// ranked list.  Equal keys have equal weights; a cut inside a group of equal
+// keys is the n-th of them in token order.
 // --------------------------------------------------------------------------
 // NPT > 0: V <= NPT NT and every thread keeps its NPT (key, weight) pairs in
 // registers after the first read; NPT = 0: KL: the keys are kept in LDS (V <=
-// kKlMaxV), else the logits are re-read on every pass.
-// With top-k on and at most kOnDemandK survivors, the weights are formed only
-// for the tokens that need one (the survivors), when they need it; otherwise
-// every weight is formed once and kept (registers, or the output row).
+// kKlMaxV), else the logits are re-read on every pass.  With NPT = 0 a weight is
+// formed where a pass needs it: every one for the first top-p level, only the
+// chosen bin's or the kept tokens' afterwards.
 template <int NT, int NPT, bool KL = false>
 __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const float* __restrict__ logits,
                                                              const int* __restrict__ tree_size,
@@ -357,7 +413,7 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
 #pragma clang fp contract(off)
   constexpr int NW = NT / 64;  // wavefronts
   const int i = blockIdx.x, b = blockIdx.y;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int T = tree_size[b];
   if ((status && status[b] != TV_ST_OK) || T < 1 || T > T_max) T = 1;
   if (i >= T) return;
@@ -367,21 +423,22 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
   __shared__ unsigned long long s_u[NW];
   __shared__ Wide s_w[NW];
   // radix bins (counts: CSETS sets of 256, shared by the wavefronts w % CSETS; or
-  // NL x 256 limbs of weight sums), ballot entries (V / 64), or the survivor list
+  // up to 1024 words of weight sums), ballot entries (V / 64), or gathered tokens
   constexpr int CSETS = KL ? 4 : NW;
-  constexpr int HIST = KL ? NL * 256 : 4096;
+  constexpr int HIST = KL ? 1536 : 4096;
   __shared__ unsigned long long s_hist[HIST];
-  static_assert(CSETS * 256 <= HIST && NL * 256 <= HIST && NT <= HIST && (!KL || kKlMaxV / 64 <= HIST),
-                "radix bins, survivor list and ballot entries fit");
-  __shared__ Norm s_abv;
-  __shared__ Wide s_wt_total;
-  __shared__ unsigned long long s_top[NT];  // the top-k survivors in rank order (top-k fast path)
+  static_assert(CSETS * 256 <= HIST && 1024 <= HIST && NT <= HIST && (!KL || kKlMaxV / 64 <= HIST),
+                "radix bins, gathered tokens and ballot entries fit");
+  __shared__ Norm s_abv, s_thr, s_kept, s_nw[NW];
+  __shared__ unsigned long long s_top[NT];  // ranked tokens, best first
   __shared__ unsigned long long s_abvc;
   __shared__ int s_pick, s_sel, s_cnt;
   extern __shared__ uint32_t s_key[];  // KL: the order key of token v
   static_assert(!KL || (NPT == 0 && NT == 1024), "keys in LDS: 1024 threads, no register copy");
 
-  // the first-ranked token
+  // a token's 64-bit rank key (key, then token ascending; the larger ranks first)
+  auto tok_key = [](uint32_t k, int v) { return ((unsigned long long)k << 32) | (0xFFFFFFFFu - (uint32_t)v); };
+  // the first-ranked token, and the smallest key of a finite logit
   struct KW {
     uint32_t k;
     float w;
@@ -389,6 +446,12 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
   KW reg[NPT > 0 ? NPT : 1];
   auto ld_l = [&](int v) { return lr[v]; };
   unsigned long long best = 0ull;
+  uint32_t kmin = 0xFFFFFFFFu;
+  constexpr uint32_t kNegInfKey = 0x007FFFFFu;  // the order key of -inf
+  auto see = [&](uint32_t k, int v) {
+    best = umax64(best, tok_key(k, v));
+    if (k > kNegInfKey) kmin = min(kmin, k);
+  };
   if constexpr (NPT > 0) {
     float x[NPT];
 #pragma unroll
@@ -396,7 +459,7 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
 #pragma unroll
     for (int j = 0; j < NPT; ++j) {
       reg[j].k = logit_key(x[j]);
-      if (tid + j * NT < V) best = umax64(best, rank_key(clean_logit(x[j]), (uint32_t)(tid + j * NT)));
+      if (tid + j * NT < V) see(reg[j].k, tid + j * NT);
     }
   } else if constexpr (KL) {
     // the whole row in flight at once (up to kKlMaxV / NT = 32 tokens per thread)
@@ -408,14 +471,16 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
     for (int j = 0; j < J; ++j) {
       const int v = tid + j * NT;
       if (v < V) {
-        s_key[v] = logit_key(x[j]);  // read back by this thread only (the same v in every pass)
-        best = umax64(best, rank_key(clean_logit(x[j]), (uint32_t)v));
+        const uint32_t k = logit_key(x[j]);
+        s_key[v] = k;  // read back by this thread only (the same v in every pass)
+        see(k, v);
       }
     }
   } else {
-    row_pass<NT>(V, ld_l, [&](int v, float x) { best = umax64(best, rank_key(clean_logit(x), (uint32_t)v)); });
+    row_pass<NT>(V, ld_l, [&](int v, float x) { see(logit_key(x), v); });
   }
   best = block_max_u64<NT>(best, s_u);
+  kmin = ~(uint32_t)block_max_u64<NT>((unsigned long long)(~kmin), s_u);
   const uint32_t kmax = (uint32_t)(best >> 32);
   const int tok0 = (int)key_index(best);
   const float tau = temperature[b];
@@ -430,23 +495,36 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
   auto weight = [&](uint32_t key) -> float {
     return key == kmax ? 1.0f : (float)exp(((double)key_float(key) - dmax) / dtau);
   };
-  // Weights formed on demand (top-k on with few survivors) or kept: NPT > 0 in
-  // registers, NPT = 0 in the output row, where each thread re-reads only the
-  // weights it wrote (the same v in every row pass).
-  const bool stored = NPT > 0 || !(kk > 1 && kk < V && kk <= kOnDemandK);
-  auto wt = [&](uint32_t k, float w) -> float { return stored ? w : weight(k); };
-  auto ld_kw = [&](int v) {
-    const uint32_t k = KL ? s_key[v] : logit_key(lr[v]);
-    return KW{k, stored ? orow[v] : 0.0f};
-  };
-  // one pass over the row: body(v, KW) for this thread's tokens in increasing v
+  // Weights: with NPT > 0 formed once and kept in registers.  Otherwise a row
+  // whose survivors are a short ranked list forms their weights per list entry;
+  // any other row forms every survivor's weight once and stores it in the output
+  // row, where the same thread reads it back (`stored`).
+  if constexpr (NPT > 0) {
+#pragma unroll
+    for (int j = 0; j < NPT; ++j) reg[j].w = weight(reg[j].k);
+  }
+  bool stored = false;
+  auto wt = [&](uint32_t k, float w) -> float { return (NPT > 0 || stored) ? w : weight(k); };
+  auto ld_k = [&](int v) { return KW{KL ? s_key[v] : logit_key(lr[v]), 0.0f}; };
+  auto ld_kw = [&](int v) { return KW{KL ? s_key[v] : logit_key(lr[v]), stored ? orow[v] : 0.0f}; };
+  // one pass over the row: body(v, KW) for this thread's tokens in increasing v;
+  // pass_k leaves the weight out (0) where it is not in registers
   auto pass = [&](auto body) __attribute__((always_inline)) {
     if constexpr (NPT > 0) {
 #pragma unroll
       for (int j = 0; j < NPT; ++j)
         if (tid + j * NT < V) body(tid + j * NT, reg[j]);
     } else {
-      row_pass<NT>(V, ld_kw, body);
+      row_pass<NT, true>(V, ld_kw, body);
+    }
+  };
+  auto pass_k = [&](auto body) __attribute__((always_inline)) {
+    if constexpr (NPT > 0) {
+#pragma unroll
+      for (int j = 0; j < NPT; ++j)
+        if (tid + j * NT < V) body(tid + j * NT, reg[j]);
+    } else {
+      row_pass<NT, !KL>(V, ld_k, body);
     }
   };
   // the workgroup's sum of one Wide per thread (every thread gets it, carry-save):
@@ -454,74 +532,63 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
   auto block_wsum = [&](Wide v) -> Wide {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) wadd(v, wshfl_xor(v, o));
-    if ((tid & 63) == 0) s_w[tid >> 6] = v;
+    if (lane == 0) s_w[wave] = v;
     __syncthreads();
     if (tid < 64) {
       Wide t = (tid < NW) ? s_w[tid] : wzero();
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) wadd(t, wshfl_xor(t, o));
-      if (tid == 0) s_wt_total = t;
+      if (tid == 0) s_w[0] = t;
     }
     __syncthreads();
-    const Wide t = s_wt_total;
+    const Wide t = s_w[0];
     __syncthreads();
     return t;
   };
   const bool with_p = tp < 1.0f;
-  Wide w_all = wzero();  // this thread's total weight (only needed for top-p)
-  if constexpr (NPT > 0) {
-#pragma unroll
-    for (int j = 0; j < NPT; ++j) {
-      reg[j].w = weight(reg[j].k);
-      if (with_p && tid + j * NT < V) wadd(w_all, wide_of(reg[j].w));
-    }
-  } else if (stored) {
-    if constexpr (KL) {
-      for (int v = tid; v < V; v += NT) {
-        const float w = weight(s_key[v]);
-        orow[v] = w;
-        if (with_p) wadd(w_all, wide_of(w));
-      }
-    } else {
-      row_pass<NT>(V, ld_l, [&](int v, float x) {
-        const float w = weight(logit_key(x));
-        orow[v] = w;
-        if (with_p) wadd(w_all, wide_of(w));
-      });
-    }
-  }
 
-  const int lane = tid & 63, wave = tid >> 6;
+  // ---- value code: 16 bits, 65535 - floor((l_max - l) 65536 / range) clamped to
+  // [0, 65535] and 65535 for the largest logit, in float32, where range spans the
+  // finite logits (at most 104 temperatures: weights below that are 0).  Float
+  // rounding is monotone, so a larger key never gets a smaller code: each code
+  // holds a contiguous range of keys, and the codes spread the tokens by value
+  // (the top byte of a key puts nearly all of them into two or three bins).
+  const float fmax = key_float(kmax);
+  const float range = fminf(fmax - key_float(kmin), 104.0f * tau);
+  const float vinv = (range > 0.0f && range <= __FLT_MAX__) ? 65536.0f / range : 0.0f;
+  auto vcode = [&](uint32_t k) -> uint32_t {
+    if (k == kmax) return 65535u;
+    const float d = (fmax - key_float(k)) * vinv;  // >= 0, or NaN (-> 0) from inf * 0
+    return d < 65535.0f ? 65535u - (uint32_t)d : 0u;
+  };
+
   // The n-th token (token order, n >= 1) with key t inside the top-k cut (tk, ck),
   // in one coalesced pass: for each slice of NT consecutive tokens, every
   // wavefront's ballot of its matching tokens goes to LDS, slice-major, so the
   // entries are in token order; the first wavefront then finds the entry holding
   // the n-th match (64 entries per lane at most, a scan over the lanes) and the
-  // bit inside it.  With `mass`, also returns the exact total weight of the
-  // tokens with key > t (all inside the cut, since t >= tk).
+  // bit inside it.
   const int nsl = (V + NT - 1) / NT;  // <= 256 slices, <= 4096 entries
-  auto nth_with_key = [&](uint32_t t, int n, uint32_t tk, int ck, bool mass, Wide& mass_above) -> int {
-    Wide ma = wzero();
-    auto body = [&](int j, uint32_t k, float w) __attribute__((always_inline)) {
+  auto nth_with_key = [&](uint32_t t, int n, uint32_t tk, int ck) -> int {
+    auto body = [&](int j, uint32_t k) __attribute__((always_inline)) {
       const int v = j * NT + tid;
       const bool f = v < V && k == t && (k > tk || v <= ck);
       const unsigned long long m = __ballot(f);
       if (lane == 0) s_hist[j * NW + wave] = m;
-      if (mass && v < V && k > t) wadd(ma, wide_of(wt(k, w)));
     };
     if (tid == 0) s_pick = V;
     if constexpr (NPT > 0) {
 #pragma unroll
       for (int j = 0; j < NPT; ++j)
-        if (j < nsl) body(j, reg[j].k, reg[j].w);
+        if (j < nsl) body(j, reg[j].k);
     } else {
       for (int j0 = 0; j0 < nsl; j0 += kNB) {
         KW x[kNB];
 #pragma unroll
-        for (int jj = 0; jj < kNB; ++jj) x[jj] = ld_kw(min((j0 + jj) * NT + tid, V - 1));
+        for (int jj = 0; jj < kNB; ++jj) x[jj] = ld_k(min((j0 + jj) * NT + tid, V - 1));
 #pragma unroll
         for (int jj = 0; jj < kNB; ++jj)
-          if (j0 + jj < nsl) body(j0 + jj, x[jj].k, x[jj].w);
+          if (j0 + jj < nsl) body(j0 + jj, x[jj].k);
       }
     }
     __syncthreads();
@@ -551,293 +618,451 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
       }
     }
     __syncthreads();
-    const int res = s_pick;
+    const int res = uni(s_pick);
     __syncthreads();
-    mass_above = mass ? block_wsum(ma) : wzero();
     return res;
   };
 
-  // ---- radix selection over the keys, eight bits per pass from the top.  Each
-  // pass histograms the tokens whose key matches the digits chosen so far into 256
-  // bins of the next digit (LDS integer atomics: the totals are exact, so the
-  // order of the additions does not matter), then the first wavefront places the
-  // target among the bins (four bins per lane, a suffix sum over the lanes) and
-  // the highest bin at which the running total reaches the target is chosen.
-  // Counts (top-k): the key of the kk-th ranked token and the number of tokens
-  // with larger keys.
-  // `visit(f)` calls f(key) for every element counted (each token, or one value per thread).
-  auto radix_count = [&](int kk_, uint32_t& t_out, int& above_out, auto visit) {
-    uint32_t prefix = 0u, pmask = 0u;
-    unsigned long long above = 0ull;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int e = tid; e < CSETS * 256; e += NT) s_hist[e] = 0ull;
-      __syncthreads();
-      visit([&](uint32_t k) {
-        if ((k & pmask) == prefix) atomicAdd(&s_hist[(wave % CSETS) * 256 + ((k >> shift) & 255u)], 1ull);
-      });
-      __syncthreads();
-      if (wave == 0) {
-        unsigned long long m[4], g = 0ull;
+  // ---- radix selection by counts (top-k), eight bits per level.  A level counts
+  // the tokens with in_level(k, v) into 256 bins of digit(k) (LDS integer atomics),
+  // then the first wavefront places the target among the bins (four bins per
+  // lane, a suffix sum over the lanes) and the highest digit at which above + the
+  // count of that digit and every higher one reaches the target is chosen (-1:
+  // never); above gains the count of the higher digits.
+  auto count_level = [&](int target, int& above, auto visit, auto digit) -> int {
+    for (int e = tid; e < CSETS * 256; e += NT) s_hist[e] = 0ull;
+    __syncthreads();
+    visit([&](uint32_t k) { atomicAdd(&s_hist[(wave % CSETS) * 256 + digit(k)], 1ull); });
+    __syncthreads();
+    if (wave == 0) {
+      unsigned long long m[4], g = 0ull;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          m[j] = 0ull;
-          for (int w = 0; w < CSETS; ++w) m[j] += s_hist[w * 256 + 4 * lane + j];
-          g += m[j];
-        }
-        unsigned long long suf = g;  // total of this lane's bins and every higher lane's
-        for (int o = 1; o < 64; o <<= 1) {
-          const unsigned long long y = __shfl_down(suf, o, 64);
-          if (lane + o < 64) suf += y;
-        }
-        unsigned long long run = above + (suf - g);
-        int cand = -1;
-        unsigned long long cabove = 0ull;
-#pragma unroll
-        for (int j = 3; j >= 0; --j) {
-          if (cand < 0 && run + m[j] >= (unsigned long long)kk_) {
-            cand = 4 * lane + j;
-            cabove = run;
-          }
-          run += m[j];
-        }
-        const unsigned long long hit = __ballot(cand >= 0);
-        if (hit && lane == 63 - __builtin_clzll(hit)) {  // the highest digit that reaches the target
-          s_sel = cand;
-          s_abvc = cabove;
-        }
+      for (int j = 0; j < 4; ++j) {
+        m[j] = 0ull;
+        for (int w = 0; w < CSETS; ++w) m[j] += s_hist[w * 256 + 4 * lane + j];
+        g += m[j];
       }
-      __syncthreads();
-      const int sel = s_sel;  // always found: kk_ < V tokens
-      above = s_abvc;
-      __syncthreads();
-      prefix |= (uint32_t)sel << shift;
-      pmask |= 255u << shift;
-    }
-    t_out = prefix;
-    above_out = (int)above;
-  };
-  // Weights (top-p): over the tokens with pred, the key of the first token at
-  // which the exact cumulative weight reaches thr, the exact weight of the tokens
-  // with larger keys, and false if thr is never reached.  The bins hold NL
-  // carry-save limbs each (limb-major: s_hist[limb 256 + bin]); a token adds to
-  // the one or two limbs its weight covers.
-  auto radix_mass = [&](auto pred, const Norm& thr, uint32_t& t_out, Norm& above_out) -> bool {
-    uint32_t prefix = 0u, pmask = 0u;
-    Norm above = nzero();
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int e = tid; e < NL * 256; e += NT) s_hist[e] = 0ull;
-      __syncthreads();
-      pass([&](int v, KW e) {
-        const float w = (e.k & pmask) == prefix && pred(e.k, v) ? wt(e.k, e.w) : 0.0f;
-        if (w > 0.0f) {
-          int j;
-          unsigned long long x;
-          weight_parts(w, j, x);
-          const int bin = (int)((e.k >> shift) & 255u);
-          atomicAdd(&s_hist[j * 256 + bin], x & 0xFFFFFFFFull);
-          if (x >> 32) atomicAdd(&s_hist[(j + 1) * 256 + bin], x >> 32);
-        }
-      });
-      __syncthreads();
-      if (wave == 0) {
-        auto bin_at = [&](int bin) {
-          Wide x;
-#pragma unroll
-          for (int i = 0; i < NL; ++i) x.l[i] = s_hist[i * 256 + bin];
-          return x;
-        };
-        Wide g = wzero();
-#pragma unroll
-        for (int j = 0; j < 4; ++j) wadd(g, bin_at(4 * lane + j));
-        Norm suf = norm_of(g);  // this lane's bins and every higher lane's
-        for (int o = 1; o < 64; o <<= 1) {
-          const Norm y = nshfl_down(suf, o);
-          if (lane + o < 64) suf = nadd(suf, y);
-        }
-        Norm run = nshfl_down(suf, 1);  // every higher lane's bins
-        if (lane == 63) run = nzero();
-        run = nadd(run, above);
-        int cand = -1;
-        Norm cabove = nzero();
-#pragma unroll
-        for (int j = 3; j >= 0; --j) {  // (unrolled, no early exit: nothing is indexed dynamically)
-          const Norm r2 = nadd(run, norm_of(bin_at(4 * lane + j)));
-          if (cand < 0 && nge(r2, thr)) {
-            cand = 4 * lane + j;
-            cabove = run;
-          }
-          run = r2;
-        }
-        const unsigned long long hit = __ballot(cand >= 0);
-        if (lane == 0) s_sel = -1;
-        if (hit && lane == 63 - __builtin_clzll(hit)) {  // the highest digit that reaches thr
-          s_sel = cand;
-          s_abv = cabove;
-        }
+      unsigned long long suf = g;  // total of this lane's bins and every higher lane's
+      for (int o = 1; o < 64; o <<= 1) {
+        const unsigned long long y = __shfl_down(suf, o, 64);
+        if (lane + o < 64) suf += y;
       }
-      __syncthreads();
-      const int sel = s_sel;
-      above = nuniform(s_abv);
-      __syncthreads();
-      if (sel < 0) return false;
-      prefix |= (uint32_t)sel << shift;
-      pmask |= 255u << shift;
+      unsigned long long run = (unsigned long long)above + (suf - g);
+      int cand = -1;
+      unsigned long long cabove = 0ull;
+#pragma unroll
+      for (int j = 3; j >= 0; --j) {
+        if (cand < 0 && run + m[j] >= (unsigned long long)target) {
+          cand = 4 * lane + j;
+          cabove = run;
+        }
+        run += m[j];
+      }
+      const unsigned long long hit = __ballot(cand >= 0);
+      if (lane == 0) s_sel = -1;
+      if (hit && lane == 63 - __builtin_clzll(hit)) {  // the highest digit that reaches the target
+        s_sel = cand;
+        s_abvc = cabove;
+      }
     }
-    t_out = prefix;
-    above_out = above;
-    return true;
+    __syncthreads();
+    const int sel = uni(s_sel);
+    if (sel >= 0) above = uni((int)s_abvc);
+    __syncthreads();
+    return sel;
   };
-
-  // ---- top-k cut (tk, ck); the default keeps everything (every key is > 0)
-  uint32_t tk = 0u;
-  int ck = V;
-  Norm wk = nzero();  // the survivors' exact total weight (top-p)
-  // Fast path, 1 < top_k <= kFastK: at least top_k tokens reach tau, the key of
-  // the top_k-th best of the per-thread best tokens (each thread's best is a
-  // distinct token), so the top_k survivors are among the tokens whose key
-  // reaches tau: usually a few more than top_k.  They are gathered into LDS and
-  // ranked exactly by counting, which leaves them in rank order in s_top.  With
-  // more candidates than the list holds, the general path below runs instead.
-  bool sorted = false;
-  if (kk > 1 && kk <= kFastK && kk < V) {
-    unsigned long long tm = 0ull;  // this thread's best token as a rank key
-    pass([&](int v, KW e) { tm = umax64(tm, ((unsigned long long)e.k << 32) | (0xFFFFFFFFu - (uint32_t)v)); });
-    uint32_t tau_k = 0u;
-    int above_t = 0;
-    const uint32_t mk = (uint32_t)(tm >> 32);  // 0 (below every key) for a thread without tokens
-    radix_count(kk, tau_k, above_t, [&](auto f) { f(mk); });
-    unsigned long long* s_cand = s_hist;
+  // Gathers the tokens with f(k, v, w) into s_hist as rank keys (in any order)
+  // and returns their number; entries past cap (<= HIST) are dropped.  w is the
+  // stored weight once the weights are stored (else 0, or the register copy).
+  auto gather = [&](int cap, auto f) -> int {
     if (tid == 0) s_cnt = 0;
     __syncthreads();
-    pass([&](int v, KW e) {
-      if (e.k >= tau_k) {
+    auto body = [&](int v, KW e) {
+      if (f(e.k, v, e.w)) {
         const int pos = atomicAdd(&s_cnt, 1);
-        if (pos < HIST) s_cand[pos] = ((unsigned long long)e.k << 32) | (0xFFFFFFFFu - (uint32_t)v);
+        if (pos < cap) s_hist[pos] = tok_key(e.k, v);
       }
-    });
-    __syncthreads();
-    const int m = s_cnt;
-    if (m <= HIST) {
-      for (int t = tid; t < m; t += NT) {
-        const unsigned long long my = s_cand[t];
-        int rk = 0;
-        for (int o = 0; o < m; ++o) rk += s_cand[o] > my;  // (all lanes read the same entry)
-        if (rk < kk) s_top[rk] = my;
-      }
-      __syncthreads();
-      const unsigned long long last = s_top[kk - 1];
-      tk = (uint32_t)(last >> 32);
-      ck = (int)key_index(last);
-      sorted = true;
-      if (with_p) wk = nuniform(norm_of(block_wsum(tid < kk ? wide_of(weight((uint32_t)(s_top[tid] >> 32)))
-                                                               : wzero())));
+    };
+    if (stored) {
+      pass(body);
+    } else {
+      pass_k(body);
     }
     __syncthreads();
-  }
-  if (!sorted) {
-    if (with_p) wk = nuniform(norm_of(block_wsum(w_all)));
-    if (kk > 1 && kk < V) {
-      int above = 0;
-      Wide ma = wzero();
-      radix_count(kk, tk, above, [&](auto f) { pass([&](int, KW e) { f(e.k); }); });
-      const int need = kk - above;
-      ck = nth_with_key(tk, need, 0u, V, with_p, ma);
-      wadd(ma, wmul(wide_of(weight(tk)), (unsigned long long)need));
-      wk = nuniform(norm_of(ma));
-    }
-  }
-  auto in_k = [&](uint32_t k, int v) { return k > tk || (k == tk && v <= ck); };
-
-  // ---- top-p cut (tpk, cp) over the top-k survivors: the shortest rank prefix
-  // whose exact cumulative weight c satisfies c >= top_p x total, i.e.
-  // c >= thr = ceil(top_p x total) (c is an integer number of units)
-  uint32_t tpk = 0u;
-  int cp = V;
-  const Norm thr = with_p ? nuniform(nthreshold(tp, wk)) : nzero();
-  if (with_p && kk > 1 && kk <= NT) {
-    // at most NT survivors: gathered into LDS as 64-bit rank keys (key,
-    // then token ascending; the order of the appends does not matter), sorted
-    // descending by a bitonic network (the fast path has them in order already),
-    // then one exact prefix sum of their weights in rank order finds the cut
-    unsigned long long* s_list = sorted ? s_top : s_hist;  // NT entries
-    const int n = sorted ? kk : min(kk, NT);
-    if (!sorted) {
-      if (tid == 0) s_cnt = 0;
-      __syncthreads();
-      pass([&](int v, KW e) {
-        if (in_k(e.k, v)) {
-          const int pos = atomicAdd(&s_cnt, 1);  // < kk by construction of the cut
-          if (pos < NT) s_list[pos] = rank_key(key_float(e.k), (uint32_t)v);
-        }
-      });
-      __syncthreads();
-    }
-    if (tid >= n) s_list[tid] = 0ull;
+    const int m = uni(s_cnt);
     __syncthreads();
-    for (int k2 = 2; !sorted && k2 <= NT; k2 <<= 1) {
-      for (int j = k2 >> 1; j > 0; j >>= 1) {
-        const int ixj = tid ^ j;
-        if (ixj > tid) {
-          const unsigned long long a = s_list[tid], c = s_list[ixj];
-          if (((tid & k2) == 0) == (a < c)) {
-            s_list[tid] = c;
-            s_list[ixj] = a;
-          }
-        }
-        __syncthreads();
-      }
+    return m;
+  };
+  // Ranks the m (<= HIST) distinct rank keys of s_hist by counting the larger
+  // ones: the first nkeep (<= NT) go in rank order into s_top.
+  auto rank_into_top = [&](int m, int nkeep) {
+    for (int t = tid; t < m; t += NT) {
+      const unsigned long long my = s_hist[t];
+      int rk = 0;
+      for (int o = 0; o < m; ++o) rk += s_hist[o] > my;  // (all lanes read the same entry)
+      if (rk < nkeep) s_top[rk] = my;
     }
-    const unsigned long long mine = s_list[tid];
-    // inclusive prefix (rank order) of the exact weights: a lane scan, then the
-    // totals of the earlier wavefronts
-    Wide incl = tid < n ? wide_of(weight((uint32_t)(mine >> 32))) : wzero();
+    __syncthreads();
+  };
+  // s_top[0..n) in rank order (n <= NT): the first index at which above + the
+  // exact inclusive cumulative weight reaches thr (n if none), with that
+  // cumulative in `kept`; a lane scan, then the totals of the earlier wavefronts.
+  // own_total: thr = ceil(top_p x the list's total) instead (above = 0).
+  auto list_cut = [&](int n, const Norm& above, const Norm& thr, bool own_total, Norm& kept) -> int {
+    Wide incl = tid < n ? wide_of(weight((uint32_t)(s_top[tid] >> 32))) : wzero();
     for (int o = 1; o < 64; o <<= 1) {
 #pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        const unsigned long long y = __shfl_up(incl.l[i], o, 64);
-        if (lane >= o) incl.l[i] += y;
+      for (int i2 = 0; i2 < NL; ++i2) {
+        const unsigned long long y = __shfl_up(incl.l[i2], o, 64);
+        if (lane >= o) incl.l[i2] += y;
       }
     }
     if (lane == 63) s_w[wave] = incl;
     if (tid == 0) s_pick = n;
     __syncthreads();
     for (int w = 0; w < wave; ++w) wadd(incl, s_w[w]);
-    if (tid < n && nge(norm_of(incl), thr)) atomicMin(&s_pick, tid);
+    const Norm c = nadd(norm_of(incl), above);
+    Norm th = thr;
+    if (own_total) {
+      if (tid == n - 1) s_thr = nthreshold(tp, c);
+      __syncthreads();
+      th = nuniform(s_thr);
+    }
+    if (tid < n && nge(c, th)) atomicMin(&s_pick, tid);
     __syncthreads();
-    const int cut = s_pick;  // the last kept rank
-    if (cut < n) {
-      const unsigned long long kc = s_list[cut];
-      tpk = (uint32_t)(kc >> 32);
-      cp = (int)key_index(kc);
+    const int cut = uni(s_pick);
+    if (tid == cut) s_kept = c;
+    __syncthreads();
+    kept = nuniform(s_kept);
+    __syncthreads();
+    return cut;
+  };
+
+  // ---- top-k cut (tk, ck): token v with key k survives iff k > tk or (k == tk
+  // and v <= ck); the default keeps everything (every key is > 0)
+  uint32_t tk = 0u;
+  int ck = V;
+  // top-p over at most NT top-k survivors ranks them all in s_top
+  const bool listed = with_p && kk > 1 && kk < V && kk <= NT;
+  // Fast path, 1 < top_k <= kFastK: take c, the top_k-th largest value code
+  // among the per-thread best tokens (distinct tokens, so at least top_k tokens
+  // reach c and the top_k survivors all do: codes are monotone).  The tokens whose
+  // code reaches c, usually a few more than top_k, are gathered into LDS and
+  // ranked exactly by counting, which leaves the survivors in rank order in s_top.
+  // With more candidates than the list holds, the general path below runs instead.
+  bool sorted = false;
+  if (kk > 1 && kk <= kFastK && kk < V) {
+    unsigned long long tm = 0ull;  // this thread's best token as a rank key
+    pass_k([&](int v, KW e) { tm = umax64(tm, tok_key(e.k, v)); });
+    // a thread without tokens has tm = 0: key 0, below every token's key, code 0
+    const uint32_t mc = tm ? vcode((uint32_t)(tm >> 32)) : 0u;
+    int above_t = 0;
+    const uint32_t ch = (uint32_t)max(0, count_level(kk, above_t, [&](auto f) { f(mc); },
+                                                     [](uint32_t c) { return c >> 8; }));
+    const uint32_t c_k =
+        (ch << 8) | (uint32_t)max(0, count_level(kk, above_t, [&](auto f) { if ((mc >> 8) == ch) f(mc); },
+                                                 [](uint32_t c) { return c & 255u; }));
+    const int m = gather(HIST, [&](uint32_t k, int, float) { return vcode(k) >= c_k; });
+    if (m <= HIST) {
+      rank_into_top(m, kk);
+      const unsigned long long last = uni(s_top[kk - 1]);
+      tk = (uint32_t)(last >> 32);
+      ck = (int)key_index(last);
+      sorted = true;
+    }
+  }
+  if (!sorted && kk > 1 && kk < V) {
+    // Value levels: the high byte of the code over every token, then the low byte
+    // inside the chosen high byte; the tokens of the chosen bin are ranked
+    // directly when at most NT, else key levels run inside the chosen code.
+    int above = 0;
+    auto all = [&](auto f) { pass_k([&](int, KW e) { f(e.k); }); };
+    const uint32_t hs = (uint32_t)count_level(kk, above, all, [&](uint32_t k) { return vcode(k) >> 8; });
+    uint32_t code = 0u;
+    int m = gather(NT, [&](uint32_t k, int, float) { return (vcode(k) >> 8) == hs; });
+    if (m > NT) {
+      auto in_hs = [&](auto f) { pass_k([&](int, KW e) { if ((vcode(e.k) >> 8) == hs) f(e.k); }); };
+      code = (hs << 8) | (uint32_t)count_level(kk, above, in_hs, [&](uint32_t k) { return vcode(k) & 255u; });
+      m = gather(NT, [&](uint32_t k, int, float) { return vcode(k) == code; });
+    }
+    if (m <= NT) {
+      // the (kk - above)-th ranked of the bin's m tokens is the last survivor
+      const int n = kk - above;
+      for (int t = tid; t < m; t += NT) {
+        const unsigned long long my = s_hist[t];
+        int rk = 0;
+        for (int o = 0; o < m; ++o) rk += s_hist[o] > my;
+        if (rk == n - 1) s_abvc = my;
+      }
+      __syncthreads();
+      const unsigned long long lastk = uni(s_abvc);
+      tk = (uint32_t)(lastk >> 32);
+      ck = (int)key_index(lastk);
+      __syncthreads();
+    } else {
+      // key levels over the tokens of the code, then the cut inside the equal keys
+      uint32_t prefix = 0u;
+      for (int shift = 24; shift >= 0; shift -= 8) {
+        const uint32_t pmask = shift == 24 ? 0u : (0xFFFFFFFFu << (shift + 8));
+        auto in_code = [&](auto f) {
+          pass_k([&](int, KW e) { if (vcode(e.k) == code && (e.k & pmask) == prefix) f(e.k); });
+        };
+        prefix |= (uint32_t)max(count_level(kk, above, in_code, [&](uint32_t k) { return (k >> shift) & 255u; }), 0)
+                  << shift;
+      }
+      tk = prefix;
+      ck = nth_with_key(tk, kk - above, 0u, V);
+    }
+    if (listed) {
+      // all kk survivors, ranked
+      const int n = min(NT, gather(NT, [&](uint32_t k, int v, float) { return k > tk || (k == tk && v <= ck); }));
+      rank_into_top(n, n);  // (n = kk)
+    }
+  }
+  auto in_k = [&](uint32_t k, int v) { return k > tk || (k == tk && v <= ck); };
+  // the survivors are s_top[0..kk) (a small top-k) or are described by the cut
+  const bool as_list = sorted || listed;
+
+  // ---- top-p radix, by the float32 bits u of the survivors' weights (w grows
+  // with the key, so the bits order the tokens as the keys do, up to equal
+  // weights).  Level 0 bins by u >> 20 (the exponent and 3 mantissa bits, 1024
+  // bins), level 1 by the next 8 bits, level 2 by the next 8, level 3 by the
+  // last 4.  Every token of a bin has the same exponent, so a bin's exact weight
+  // is (the sum of the 24-bit mantissas m) 2^s units: one 64-bit word per bin
+  // holds the sum of (m + 2^44), i.e. the mantissa sum (< 2^42: a row has fewer
+  // than 2^18 tokens) and, above bit 44, the count, with one atomic per token.
+  constexpr unsigned long long kCnt1 = 1ull << 44;
+  auto lev_shift = [](int lev) { return lev == 0 ? 20 : lev == 1 ? 12 : lev == 2 ? 4 : 0; };
+  auto lev_bins = [](int lev) { return lev == 0 ? 1024 : lev == 3 ? 16 : 256; };
+  auto w_word = [](float w) {  // m + 2^44 for a weight w > 0
+    const uint32_t u = __float_as_uint(w);
+    return ((u >> 23) ? (unsigned long long)((u & 0x7FFFFFu) | 0x800000u) : (unsigned long long)u) + kCnt1;
+  };
+  Norm above = nzero(), thr = nzero();
+  // After a level's sums (the bins of one exponent e, or, at level 0, bin b of
+  // exponent b >> 3), every thread takes nb / NT (at least one) consecutive bins:
+  // an exact suffix sum over the threads (a lane scan, then the wavefront totals)
+  // gives each the weight of all higher bins, and the one bin at which above +
+  // that weight first reaches thr is chosen (-1: never), with its count in
+  // s_cnt.  `above` gains the weight of the higher bins; level 0 sets thr from
+  // the total.
+  auto w_select = [&](int lev, uint32_t prefix) __attribute__((always_inline)) -> int {
+    const int nb = lev_bins(lev);
+    const int bpt = (nb + NT - 1) / NT;  // 1, or 4 with 256 threads and 1024 bins
+    const int e_fix = lev == 1 ? (int)(prefix >> 3) : lev == 2 ? (int)(prefix >> 11) : (int)(prefix >> 19);
+    auto bin_at = [&](int bin) {  // the bin's weight as a Wide (0 past the bins)
+      const unsigned long long word = bin < nb ? s_hist[bin] : 0ull;
+      const int e = lev == 0 ? (bin >> 3) : e_fix;
+      return wide_shifted(word & (kCnt1 - 1), e ? e - 1 : 0);
+    };
+    if (tid == 0) s_sel = -1;
+    __syncthreads();
+    // carry-save sums: a bin's limbs are below 2^46, so 1024 of them fit a limb
+    Wide suf = wzero();  // this thread's bins and those of the higher lanes of its wavefront
+#pragma unroll 1
+    for (int j = 0; j < bpt; ++j) wadd(suf, bin_at(tid * bpt + j));
+    for (int o = 1; o < 64; o <<= 1) {
+      const Wide y = wshfl_down(suf, o);
+      if (lane + o < 64) wadd(suf, y);
+    }
+    if (lane == 0) s_w[wave] = suf;
+    Wide run = wshfl_down(suf, 1);  // the higher lanes' bins
+    if (lane == 63) run = wzero();
+    __syncthreads();
+    for (int w = wave + 1; w < NW; ++w) wadd(run, s_w[w]);  // the higher wavefronts' bins
+    if (lev == 0 && tid == 0) {  // thr from the total
+      Wide z = wzero();
+      for (int w = 0; w < NW; ++w) wadd(z, s_w[w]);
+      s_thr = nthreshold(tp, norm_of(z));
+    }
+    if (lev == 0) __syncthreads();
+    const Norm th = lev == 0 ? nuniform(s_thr) : thr;
+#pragma unroll 1
+    for (int j = bpt - 1; j >= 0; --j) {
+      const int bin = tid * bpt + j;
+      const Norm r0 = nadd(norm_of(run), above);
+      wadd(run, bin_at(bin));
+      const Norm r2 = nadd(norm_of(run), above);
+      if (bin < nb && !nge(r0, th) && nge(r2, th)) {  // the one bin where the cumulative crosses thr
+        s_sel = bin;
+        s_abv = r0;
+        s_cnt = (int)(s_hist[bin] >> 44);
+      }
     }
     __syncthreads();
+    const int sel = uni(s_sel);
+    if (sel >= 0) above = nuniform(s_abv);
+    thr = th;
+    __syncthreads();
+    return sel;
+  };
+
+  // ---- one pass forming every survivor's weight (unless they are a ranked
+  // list): NPT = 0 stores it into the output row (0 for the others), and the pass
+  // also does the first top-p level's sums or, without top-p, sums the kept weights
+  double wsum = 0.0;
+  if (!as_list) {
+    if (with_p) {
+      for (int e = tid; e < 1024; e += NT) s_hist[e] = 0ull;
+      __syncthreads();
+    }
+    pass_k([&](int v, KW e) {
+      const float w = in_k(e.k, v) ? wt(e.k, e.w) : 0.0f;
+      if constexpr (NPT == 0) orow[v] = w;
+      if (with_p) {
+        if (w > 0.0f) atomicAdd(&s_hist[__float_as_uint(w) >> 20], w_word(w));
+      } else if (!(mp > 0.0f) || w >= mp || v == tok0) {
+        wsum += (double)w;
+      }
+    });
+    stored = NPT == 0;  // later passes read the weights back (ld_kw)
+  }
+
+  // ---- top-p cut (tpk, cp) over the top-k survivors: the shortest rank prefix
+  // whose exact cumulative weight c satisfies c >= top_p x total, i.e.
+  // c >= thr = ceil(top_p x total) (c is an integer number of units).  kept: the
+  // exact weight of the prefix, when the cut is found.
+  uint32_t tpk = 0u;
+  int cp = V;
+  int n_list = kk;  // the ranked survivors that stay (as_list)
+  bool have_kept = false;
+  Norm kept = nzero();
+  if (listed) {
+    const int cut = list_cut(kk, nzero(), nzero(), true, kept);
+    if (cut < kk) n_list = cut + 1;
   } else if (with_p) {
-    Norm above = nzero();
-    Wide unused = wzero();
-    if (radix_mass(in_k, thr, tpk, above)) {
-      // the survivors with key tpk all weigh ct: in token order, the first n of
-      // them bring the cumulative to thr (n = ceil((thr - above) / ct))
-      const int n = ntie_count(thr, above, weight(tpk));
-      cp = nth_with_key(tpk, n, tk, ck, false, unused);
-    } else {
-      tpk = 0u;  // never reached: every survivor stays
+    // levels until the chosen bin holds at most NT tokens, which are then ranked
+    // in a list; a bin of more than NT equal weights at the last level is cut by
+    // counting: n of its tokens, the first n in rank order
+    uint32_t prefix = 0u;  // u >> (the last level's shift)
+    int m = 0, sh = 20;
+    bool reached = true;
+#pragma unroll 1
+    for (int lev = 0; lev < 4; ++lev) {
+      if (lev > 0) {
+        const int sh0 = sh, nb = lev_bins(lev);
+        sh = lev_shift(lev);
+        for (int e = tid; e < nb; e += NT) s_hist[e] = 0ull;
+        __syncthreads();
+        pass([&](int v, KW e) {
+          const float w = in_k(e.k, v) ? wt(e.k, e.w) : 0.0f;
+          const uint32_t u = __float_as_uint(w);
+          if (w > 0.0f && (u >> sh0) == prefix) atomicAdd(&s_hist[(u >> sh) & (nb - 1)], w_word(w));
+        });
+      }
+      const int sel = w_select(lev, prefix);
+      if (sel < 0) {  // never reached: every survivor stays
+        reached = false;
+        break;
+      }
+      m = uni(s_cnt);
+      prefix = lev == 0 ? (uint32_t)sel : (prefix << (lev == 3 ? 4 : 8)) | (uint32_t)sel;
+      if (m <= NT) break;
+    }
+    if (reached && m <= NT) {
+      __syncthreads();
+      gather(NT, [&](uint32_t k, int v, float w) {
+        const float x = in_k(k, v) ? wt(k, w) : 0.0f;
+        return x > 0.0f && (__float_as_uint(x) >> sh) == prefix;
+      });
+      rank_into_top(m, m);
+      // every weight of the bin is m_t 2^s units (one exponent): the cut is the
+      // first rank whose inclusive mantissa sum reaches need = ceil((thr - above)
+      // / 2^s) (< 2^43: the bin's total reaches thr)
+      const uint32_t e = prefix >> (23 - sh);
+      const int sx = e ? (int)e - 1 : 0;
+      unsigned long long dt[NN + 1];
+      long long br = 0;
+#pragma unroll
+      for (int i = 0; i < NN; ++i) {  // thr - above, borrows propagated
+        const long long d = (long long)thr.l[i] - (long long)above.l[i] - br;
+        br = d < 0 ? 1 : 0;
+        dt[i] = (unsigned long long)(d + (br << 32));
+      }
+      dt[NN] = 0ull;
+      const Norm nq = nshr_ceil(dt, sx);
+      const unsigned long long need = ((unsigned long long)nq.l[1] << 32) | nq.l[0];
+      unsigned long long mt = 0ull;
+      if (tid < m) {
+        const uint32_t u = __float_as_uint(weight((uint32_t)(s_top[tid] >> 32)));
+        mt = (u >> 23) ? ((u & 0x7FFFFFu) | 0x800000u) : u;
+      }
+      unsigned long long lo_c, hi_c, tot_c;
+      block_scan<unsigned long long, NT>(mt, s_u, lo_c, hi_c, tot_c);
+      if (tid == 0) s_pick = m;
+      __syncthreads();
+      if (tid < m && hi_c >= need && lo_c < need) s_pick = tid;  // (exactly one)
+      __syncthreads();
+      const int cut = uni(s_pick);
+      if (cut < m) {
+        if (tid == cut) s_kept = nadd(above, norm_of(wide_shifted(hi_c, sx)));
+        __syncthreads();
+        kept = nuniform(s_kept);
+        const unsigned long long ck2 = uni(s_top[cut]);
+        tpk = (uint32_t)(ck2 >> 32);
+        cp = (int)key_index(ck2);
+        have_kept = true;
+      }
+    } else if (reached) {
+      // more than NT survivors of the one weight c = prefix: the first n of them in
+      // rank order (n = ceil((thr - above) / c)) keep; key levels find the n-th
+      // one's key
+      const float c = __uint_as_float(prefix);
+      const int n = ntie_count(thr, above, c);
+      int ab = 0;
+      uint32_t kp = 0u;
+      for (int shift = 24; shift >= 0; shift -= 8) {
+        const uint32_t pmask = shift == 24 ? 0u : (0xFFFFFFFFu << (shift + 8));
+        auto in_c = [&](auto f) {
+          pass([&](int v, KW e) {
+            if (in_k(e.k, v) && wt(e.k, e.w) == c && (e.k & pmask) == kp) f(e.k);
+          });
+        };
+        kp |= (uint32_t)max(count_level(n, ab, in_c, [&](uint32_t k) { return (k >> shift) & 255u; }), 0)
+              << shift;
+      }
+      tpk = kp;
+      cp = nth_with_key(tpk, n - ab, tk, ck);
     }
   }
 
-  // ---- min-p, the kept total and the output
-  // the weight of a kept token, 0 for the others (a weight is formed only for the
-  // top-k and top-p survivors)
+  // ---- min-p, the kept total and the output.  The kept tokens are a rank prefix.
+  if (as_list) {
+    // s_top[0..n_list) ranked; min-p keeps the entries with w >= min_p (a prefix,
+    // the first entry always): their exact total is W, the last kept rank key
+    // bounds the zero-filled tokens, and each kept entry is written by its thread
+    const float w_t = tid < n_list ? weight((uint32_t)(s_top[tid] >> 32)) : 0.0f;
+    const bool keep = tid < n_list && (!(mp > 0.0f) || w_t >= mp || tid == 0);
+    const int n_keep = __syncthreads_count(keep);
+    const double W = norm_to_double(norm_of(block_wsum(keep ? wide_of(w_t) : wzero())));
+    const unsigned long long last = s_top[n_keep - 1];
+    pass_k([&](int v, KW e) {
+      if (tok_key(e.k, v) < last) orow[v] = 0.0f;
+    });
+    if (keep) orow[key_index(s_top[tid])] = (float)((double)w_t * (1.0 / W));
+    return;
+  }
   auto kept_w = [&](uint32_t k, int v, float w) -> float {
     if (!(in_k(k, v) && (k > tpk || (k == tpk && v <= cp)))) return 0.0f;
     const float x = wt(k, w);
     return (!(mp > 0.0f) || x >= mp || v == tok0) ? x : 0.0f;
   };
-  double wsum = 0.0;
-  pass([&](int v, KW e) { wsum += (double)kept_w(e.k, v, e.w); });
-  const double W = block_sum_d<NT>(wsum, s_d);
+  double W;
+  if (!with_p) {
+    W = block_sum_d<NT>(wsum, s_d);
+  } else if (have_kept && !(mp > 0.0f)) {
+    W = norm_to_double(kept);
+  } else {
+    double ws = 0.0;
+    pass([&](int v, KW e) { ws += (double)kept_w(e.k, v, e.w); });
+    W = block_sum_d<NT>(ws, s_d);
+  }
+  // w / W as w (1 / W) in double: within one double rounding of the quotient
+  const double rW = 1.0 / W;
   pass([&](int v, KW e) {
     const float x = kept_w(e.k, v, e.w);
-    orow[v] = x > 0.0f ? (float)((double)x / W) : 0.0f;
+    // (NPT = 0: a token outside the top-k cut already holds 0)
+    if (NPT > 0 || x > 0.0f || in_k(e.k, v)) orow[v] = x > 0.0f ? (float)((double)x * rW) : 0.0f;
   });
 }
 
