@@ -190,6 +190,28 @@ def test_filters_top_p_value_bins(many, V):
     run_filter(lg, tree_size, None, (temp, top_k, top_p, min_p))
 
 
+@pytest.mark.parametrize("V,B", [(2000, 512), (32000, 64), (40000, 24)])
+def test_filters_weights_bit_exact(V, B):
+    """Every weight is fp32(exp((l - l_max) / temperature)) to the bit: one row per
+    request, min_p set to the oracle's weight of a chosen token (which must stay)
+    or to the next float32 above it (which must go), over weights from ~1 down to
+    the subnormal range.  A weight one ulp off on the GPU flips that token."""
+    from oracle import sampling as osm
+    rng = np.random.default_rng(V + B)
+    lg = (rng.normal(0, 1, (B, 1, V)) * rng.uniform(1, 40, (B, 1, 1))).astype(np.float32)
+    temp = rng.uniform(0.2, 3.0, B).astype(np.float32)
+    min_p = np.zeros(B, np.float32)
+    for b in range(B):
+        row = osm.rank_order(lg[b, 0])[0]
+        w = osm.filter_weights(row, float(temp[b]))
+        cand = np.nonzero((w > 0) & (w < 1))[0]
+        j = int(cand[rng.integers(0, len(cand))])
+        wj = np.float32(w[j])
+        min_p[b] = wj if b % 2 == 0 else np.nextafter(wj, np.float32(2))
+    params = (temp, np.zeros(B, np.int32), np.ones(B, np.float32), min_p)
+    run_filter(lg, np.ones(B, np.int32), None, params)
+
+
 @pytest.mark.parametrize("cfg", [2, 3])
 def test_filter_then_target_only_sampling(cfg):
     """The whole non-greedy chain: logits -> tree_sampling_probs -> tree_accept_sample,

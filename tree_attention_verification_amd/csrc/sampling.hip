@@ -401,6 +401,50 @@ __device__ __forceinline__ float key_float(uint32_t k) {
 // kKlMaxV), else the logits are re-read on every pass.  With NPT = 0 a weight is
 // formed where a pass needs it: every one for the first top-p level, only the
 // chosen bin's or the kept tokens' afterwards.
+// The requests in order of their rows' cost, so that the rows still starting as
+// the grid drains are short ones.  The filter settings decide a row's cost: a
+// radix top-p cut (most), then a full pass without top-p (or with a long top-k),
+// a short ranked top-k list with top-p, without it, and greedy (least).  Returns
+// the y-th request of that order (requests of one class keep their order).
+template <int NT>
+__device__ __forceinline__ int request_by_cost(int y, int B, int V, const float* __restrict__ temperature,
+                                               const int* __restrict__ top_k, const float* __restrict__ top_p) {
+  constexpr int NW = NT / 64;
+  __shared__ int s_cc[5], s_wc[NW], s_req;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  auto cls = [&](int r) -> int {
+    const float t = temperature[r], p = top_p[r];
+    const int k = top_k[r];
+    if (!(t > 0.0f) || k == 1 || p <= 0.0f) return 4;
+    if (p < 1.0f) return (k > 1 && k < V && k <= NT) ? 2 : 0;
+    return (k > 1 && k < V && k <= kFastK) ? 3 : 1;
+  };
+  if (tid < 5) s_cc[tid] = 0;
+  __syncthreads();
+  for (int r = tid; r < B; r += NT) atomicAdd(&s_cc[cls(r)], 1);
+  __syncthreads();
+  int c = 0, base = 0;
+  while (c < 4 && y >= base + s_cc[c]) base += s_cc[c++];
+  const int pos = y - base;  // the request's place among those of class c
+  int seen = 0;
+  for (int r0 = 0; r0 < B; r0 += NT) {
+    const int r = r0 + tid;
+    const bool f = r < B && cls(r) == c;
+    const unsigned long long bal = __ballot(f);
+    if (lane == 0) s_wc[wave] = __popcll(bal);
+    __syncthreads();
+    int before = 0, tot = 0;
+    for (int w = 0; w < NW; ++w) {
+      before += w < wave ? s_wc[w] : 0;
+      tot += s_wc[w];
+    }
+    if (f && seen + before + __popcll(bal & ((1ull << lane) - 1ull)) == pos) s_req = r;
+    seen += tot;
+    __syncthreads();
+  }
+  return s_req;
+}
+
 template <int NT, int NPT, bool KL = false>
 __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const float* __restrict__ logits,
                                                              const int* __restrict__ tree_size,
@@ -412,8 +456,10 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
                                                              float* __restrict__ probs) {
 #pragma clang fp contract(off)
   constexpr int NW = NT / 64;  // wavefronts
-  const int i = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int i = blockIdx.x;
+  const int b = gridDim.y > 1 ? uni(request_by_cost<NT>(blockIdx.y, (int)gridDim.y, V, temperature, top_k, top_p))
+                              : (int)blockIdx.y;
   int T = tree_size[b];
   if ((status && status[b] != TV_ST_OK) || T < 1 || T > T_max) T = 1;
   if (i >= T) return;
@@ -435,6 +481,8 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
   __shared__ int s_pick, s_sel, s_cnt;
   extern __shared__ uint32_t s_key[];  // KL: the order key of token v
   static_assert(!KL || (NPT == 0 && NT == 1024), "keys in LDS: 1024 threads, no register copy");
+  __shared__ double s_exp2[64];  // 2^(j / 64) (visible after the first barrier below)
+  if (tid < 64) s_exp2[tid] = exp2((double)tid * 0.015625);
 
   // a token's 64-bit rank key (key, then token ascending; the larger ranks first)
   auto tok_key = [](uint32_t k, int v) { return ((unsigned long long)k << 32) | (0xFFFFFFFFu - (uint32_t)v); };
@@ -492,8 +540,30 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
     return;
   }
   const double dmax = (double)key_float(kmax), dtau = (double)tau;
+  // w = fp32(exp(d / tau)), d = l - l_max <= 0.  Fast path (a table-driven
+  // exponential in the manner of Tang's method): t = d log2(e) / tau to within a
+  // few ulps, 2^t = 2^(k / 64) 2^f with |f| <= 1/128, 2^(j / 64) from a table
+  // and 2^f from its degree-4 Taylor polynomial: relative error below 2^-43.  The
+  // float32 rounding of that double is the rounding of the exact value unless
+  // the double lies within 2^16 ulps of a float32 rounding midpoint (about one
+  // value in 4096), or the result would be subnormal; those take the exact path:
+  // the quotient d / tau, then exp in double.
+  const double c2 = (1.0 / dtau) * 1.4426950408889634;  // log2(e) / tau
   auto weight = [&](uint32_t key) -> float {
-    return key == kmax ? 1.0f : (float)exp(((double)key_float(key) - dmax) / dtau);
+    if (key == kmax) return 1.0f;
+    const double d = (double)key_float(key) - dmax;
+    const double t = d * c2;
+    if (t >= -125.0) {
+      const double kf = rint(t * 64.0);
+      const int ki = (int)kf;
+      const double f = t - kf * 0.015625;
+      const double p = 1.0 + f * (0.6931471805599453 +
+                                  f * (0.24022650695910072 + f * (0.05550410866482158 + f * 0.009618129107628477)));
+      const double y = ldexp(s_exp2[ki & 63] * p, ki >> 6);
+      const uint32_t lo = (uint32_t)__double_as_longlong(y) & 0x1FFFFFFFu;  // the bits float32 rounds away
+      if (lo - 0x0FFF0000u > 0x20000u) return (float)y;
+    }
+    return (float)exp(d / dtau);
   };
   // Weights: with NPT > 0 formed once and kept in registers.  Otherwise a row
   // whose survivors are a short ranked list forms their weights per list entry;
