@@ -406,7 +406,13 @@ int tree_sampling_probs(int B, int T_max, int V, const float* logits, const int*
  *      nodes the walk does not reach are not read).
  * Out: accept_len, accept_path, bonus_token as tree_accept.
  * Workspace: tree_accept_sample_draft_workspace_bytes(B, V) bytes (B x V
- *   float64 residual rows, any contents, 8-byte aligned).
+ *   float64 words per request, any contents, 8-byte aligned): the residual
+ *   rows, or, when few requests share a large vocabulary and several
+ *   workgroups split each row between them, the slots through which they
+ *   exchange their partial sums.  Those workgroups wait for each other with
+ *   bounded waits; a request whose wait runs out (all of a call's workgroups
+ *   are sized to be resident at once, so this does not happen unless other
+ *   work holds the device's CUs for seconds) gets accept_len = bonus_token = -1.
  * Requires 1 <= T_max <= 256, 0 <= dcap < T_max, 1 <= V <= 262144.
  * ------------------------------------------------------------------------- */
 size_t tree_accept_sample_draft_workspace_bytes(int B, int V);

@@ -45,6 +45,88 @@ __device__ __forceinline__ double block_sum_d(double v, double* s) {
   __syncthreads();
   return t;
 }
+// Wavefront reductions by DPP moves (no LDS round trips): an inclusive scan in
+// rows of 16 lanes (row_shr 1, 2, 4, 8; lanes without a source read 0), then
+// lane 15 of rows 0 and 2 into rows 1 and 3 (row_bcast 15) and lane 31 into
+// rows 2 and 3 (row_bcast 31): lane 63 ends with the whole wavefront's value.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ unsigned long long dpp_u64(unsigned long long x) {
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)x, CTRL, ROWS, 0xF, true);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(x >> 32), CTRL, ROWS, 0xF, true);
+  return ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+template <class Op>
+__device__ __forceinline__ unsigned long long wave_reduce_dpp(unsigned long long v, Op op) {
+  v = op(v, dpp_u64<0x111, 0xF>(v));
+  v = op(v, dpp_u64<0x112, 0xF>(v));
+  v = op(v, dpp_u64<0x114, 0xF>(v));
+  v = op(v, dpp_u64<0x118, 0xF>(v));
+  v = op(v, dpp_u64<0x142, 0xA>(v));
+  v = op(v, dpp_u64<0x143, 0xC>(v));
+  return ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63) << 32) |
+         (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+}
+__device__ __forceinline__ double wave_sum_dpp(double v) {
+  return __longlong_as_double((long long)wave_reduce_dpp(
+      (unsigned long long)__double_as_longlong(v), [](unsigned long long x, unsigned long long y) {
+        return (unsigned long long)__double_as_longlong(__longlong_as_double((long long)x) +
+                                                        __longlong_as_double((long long)y));
+      }));
+}
+__device__ __forceinline__ unsigned long long wave_max_dpp(unsigned long long v) {
+  return wave_reduce_dpp(v, [](unsigned long long x, unsigned long long y) { return x > y ? x : y; });
+}
+
+// two sums and two maxima at once (one round of barriers); every thread gets all
+template <int NT = kThreads>
+__device__ __forceinline__ void block_sum2_max2(double& a, double& c, unsigned long long& m0, unsigned long long& m1,
+                                                unsigned long long* s) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  a = wave_sum_dpp(a);
+  c = wave_sum_dpp(c);
+  m0 = wave_max_dpp(m0);
+  m1 = wave_max_dpp(m1);
+  if (lane == 0) {
+    s[4 * wave] = (unsigned long long)__double_as_longlong(a);
+    s[4 * wave + 1] = (unsigned long long)__double_as_longlong(c);
+    s[4 * wave + 2] = m0;
+    s[4 * wave + 3] = m1;
+  }
+  __syncthreads();
+  double ta = 0.0, tc = 0.0;
+  unsigned long long t0 = 0ull, t1 = 0ull;
+  for (int w = 0; w < (NT / 64); ++w) {
+    ta += __longlong_as_double((long long)s[4 * w]);
+    tc += __longlong_as_double((long long)s[4 * w + 1]);
+    t0 = umax64(t0, s[4 * w + 2]);
+    t1 = umax64(t1, s[4 * w + 3]);
+  }
+  __syncthreads();
+  a = ta;
+  c = tc;
+  m0 = t0;
+  m1 = t1;
+}
+// two sums at once (one round of barriers); every thread gets both
+template <int NT = kThreads>
+__device__ __forceinline__ void block_sum_d2(double& a, double& c, double* s) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  a = wave_sum_d(a);
+  c = wave_sum_d(c);
+  if (lane == 0) {
+    s[2 * wave] = a;
+    s[2 * wave + 1] = c;
+  }
+  __syncthreads();
+  double ta = 0.0, tc = 0.0;
+  for (int w = 0; w < (NT / 64); ++w) {
+    ta += s[2 * w];
+    tc += s[2 * w + 1];
+  }
+  __syncthreads();
+  a = ta;
+  c = tc;
+}
 template <int NT = kThreads>
 __device__ __forceinline__ unsigned long long block_sum_u64(unsigned long long v, unsigned long long* s) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -1304,6 +1386,275 @@ __global__ __launch_bounds__(kThreads) void k_tree_accept_sample_draft(
   }
 }
 
+// --------------------------------------------------------------------------
+// tree_accept_sample_draft, sliced: S workgroups per request, workgroup s owning
+// tokens [s L, min(V, (s + 1) L)) with its slice of R (float64) and Q (float32)
+// in LDS, so that a pass over the residual streams through S CUs instead of
+// one.  The workgroups of a request take the same walk: each computes every
+// decision from the same values -- the slice sums, exchanged through the
+// workspace and added in slice order, and R(x), Q(x) of the child's token,
+// which each re-derives from p(x), q(x) by replaying the node's updates with
+// the operations of the slice pass.  Exchange g uses its own slots in the
+// workspace (4 words per workgroup, set to an empty mark by k_slice_reset):
+// each workgroup stores its words and polls the others' until none is empty.
+// Slots and marks are only touched by device-scope atomics, which are performed
+// past the per-XCD caches, so no cache is written back or invalidated.  Every
+// wait is bounded, and a request whose wait runs out gets accept_len =
+// bonus_token = -1.  The host launches at most as many workgroups as the
+// device holds at once, so all of a request's workgroups are resident together.
+// --------------------------------------------------------------------------
+constexpr int kSliceMax = 8;          // workgroups per request
+constexpr int kSliceSpin = 1 << 22;   // polls of a slot before a wait gives up
+constexpr unsigned long long kSlotEmpty = ~0ull;  // (no exchanged word is all ones)
+// exchanges a walk makes at most: one per node entered (<= dcap + 1 <= T_max)
+// and one per rejection (< T_max)
+__host__ __device__ constexpr int slice_exchanges(int T_max) { return 2 * T_max; }
+
+// slot words of request b: its workspace row, exchange-major, 4 words per slice
+__global__ void k_slice_reset(double* __restrict__ ws, int V, int words) {
+  unsigned long long* row = reinterpret_cast<unsigned long long*>(ws + (long long)blockIdx.x * V);
+  for (int e = threadIdx.x; e < words; e += blockDim.x) row[e] = kSlotEmpty;
+}
+
+template <int NT>
+__global__ __launch_bounds__(NT) void k_tree_accept_sample_draft_sliced(
+    int S, int L, int T_max, int dcap, int V, int without_replacement, const int* __restrict__ draft_tokens,
+    const int* __restrict__ parents, const int* __restrict__ tree_size, const float* __restrict__ target_probs,
+    const float* __restrict__ draft_probs, const float* __restrict__ uniforms, const int* __restrict__ status,
+    int* __restrict__ accept_len, int* __restrict__ accept_path, int* __restrict__ bonus_token,
+    double* __restrict__ ws) {
+#pragma clang fp contract(off)
+  constexpr int NW = NT / 64;
+  const int sl = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int v0 = sl * L, n = max(0, min(V, v0 + L) - v0);  // this slice: tokens v0 .. v0 + n - 1
+  extern __shared__ double s_R[];                            // L residual values
+  float* s_Q = reinterpret_cast<float*>(s_R + L);           // L draft values
+  uint32_t* s_rm = reinterpret_cast<uint32_t*>(s_Q + L);    // (L + 31) / 32 words: removed tokens
+  __shared__ int s_tok[kTMaxLimit], s_par[kTMaxLimit], s_path[kTMaxLimit], s_hx[kTMaxLimit];
+  __shared__ float s_uni[kTMaxLimit], s_px[kTMaxLimit], s_qx[kTMaxLimit];
+  __shared__ double s_hq[kTMaxLimit], s_hr[kTMaxLimit];      // ZQ, ZR of each update at this node
+  __shared__ double s_d[NW * 16];
+  __shared__ unsigned long long s_u[NW], s_all[kSliceMax][4], s_r4[4 * NW];
+  __shared__ int s_dec, s_fail, s_pick;
+  const long long ob = (long long)b * T_max;
+  int T = tree_size[b];
+  const bool ok = status[b] == TV_ST_OK && T >= 1 && T <= T_max;
+  if (!ok) T = 1;
+  for (int c = tid; c < T_max; c += NT) {
+    s_tok[c] = c < T ? draft_tokens[ob + c] : -1;
+    s_par[c] = (c > 0 && c < T) ? parents[ob + c] : -2;
+    s_uni[c] = uniforms[ob + c];
+  }
+  if (tid == 0) {
+    s_path[0] = 0;
+    s_fail = 0;
+  }
+  const int nwd = (n + 31) / 32;
+  auto removed = [&](int t) { return (s_rm[t >> 5] >> (t & 31)) & 1u; };
+  unsigned long long* slots = reinterpret_cast<unsigned long long*>(ws + (long long)b * V);
+  int gen = 0;
+  // every workgroup publishes 4 words in exchange gen's slots, then waits for
+  // the request's others: all S x 4 end in s_all
+  auto exchange = [&](unsigned long long a0, unsigned long long a1, unsigned long long a2,
+                      unsigned long long a3) __attribute__((always_inline)) {
+    __syncthreads();
+    unsigned long long* g = slots + (long long)gen * S * 4;
+    if (tid < 4)
+      __hip_atomic_store(g + sl * 4 + tid, tid == 0 ? a0 : tid == 1 ? a1 : tid == 2 ? a2 : a3, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    if (tid < 4 * S) {
+      unsigned long long v;
+      int spins = 0;
+      while ((v = __hip_atomic_load(g + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == kSlotEmpty) {
+        if (++spins > kSliceSpin || s_fail) {
+          s_fail = 1;
+          break;
+        }
+      }
+      s_all[tid >> 2][tid & 3] = v;
+    }
+    __syncthreads();
+    ++gen;
+  };
+  auto dsum = [&](int f) {  // field f of every slice as float64, added in slice order
+    double t = 0.0;
+    for (int s2 = 0; s2 < S; ++s2) t += __longlong_as_double((long long)s_all[s2][f]);
+    return t;
+  };
+  auto as_u = [](double x) { return (unsigned long long)__double_as_longlong(x); };
+  // Node entry: R = p and Q = q on the slice, the removed set cleared, p(x) and
+  // q(x) of the node's children gathered; the slice sums of p and q, the last
+  // token with p > 0 (+ 1; 0: none) and the best p as a rank key, exchanged.
+  auto enter = [&](int nd) {
+    const float* p = target_probs + (ob + nd) * (long long)V;
+    const float* q = draft_probs + (ob + nd) * (long long)V;
+    double a = 0.0, c = 0.0;
+    int lastp = 0;
+    unsigned long long bst = 0ull;
+    row_pass<NT>(n, [&](int t) { return float2{p[v0 + t], q[v0 + t]}; }, [&](int t, float2 e) {
+      s_R[t] = (double)e.x;
+      s_Q[t] = e.y;
+      a += (double)e.x;
+      c += (double)e.y;
+      if (e.x > 0.0f) lastp = v0 + t + 1;
+      bst = umax64(bst, rank_key(e.x, (uint32_t)(v0 + t)));
+    });
+    for (int w = tid; w < nwd; w += NT) s_rm[w] = 0u;
+    for (int c2 = tid; c2 < T; c2 += NT) {
+      const int x = s_tok[c2];
+      const bool in = c2 > 0 && s_par[c2] == nd && x >= 0 && x < V;
+      s_px[c2] = in ? p[x] : 0.0f;
+      s_qx[c2] = in ? q[x] : 0.0f;
+    }
+    unsigned long long lp = (unsigned long long)lastp;
+    block_sum2_max2<NT>(a, c, lp, bst, s_r4);
+    exchange(as_u(a), as_u(c), lp, bst);
+    unsigned long long bb = 0ull;
+    for (int s2 = 0; s2 < S; ++s2) bb = umax64(bb, s_all[s2][3]);
+    return bb;  // the node's best token over every slice
+  };
+
+  int node = 0, len = 0, entered = -1;
+  unsigned long long besta = 0ull;  // the entered node's best token (rank key)
+  while (ok && len < dcap) {
+    besta = enter(node);
+    entered = node;
+    if (s_fail) break;
+    double ZR = dsum(0), ZQ = dsum(1);
+    int next = -1, nrej = 0;
+    for (int c = 1; c < T; ++c) {
+      if (s_par[c] != node) continue;
+      const int x = s_tok[c];
+      const bool inside = x >= 0 && x < V;
+      bool acc;
+      {
+        // R(x) and Q(x) now: p(x), q(x) through this node's updates so far (every
+        // thread alike: the same values, so no barrier)
+        double r = 0.0, s = 0.0;
+        if (inside) {
+          const double qx = (double)s_qx[c];
+          bool gone = false;
+          r = (double)s_px[c];
+          for (int j = 0; j < nrej; ++j) {
+            if (s_hq[j] > 0.0) {
+              const double qv = gone ? 0.0 : qx;
+              const double a = r * s_hq[j];
+              const double bq = qv * s_hr[j];
+              r = fmax(0.0, a - bq);
+            }
+            if (s_hx[j] == x) gone = true;
+          }
+          s = gone ? 0.0 : qx;
+        }
+        const double lhs = ((double)s_uni[c] * s) * ZR;
+        const double rhs = r * ZQ;
+        acc = r > 0.0 && (s == 0.0 || lhs < rhs);
+      }
+      if (acc) {
+        next = c;
+        break;
+      }
+      const bool rm = without_replacement && inside;
+      // this rejection's update, for the later replays: every thread writes the
+      // same values (and reads back its own write, with or without a barrier)
+      s_hx[nrej] = rm ? x : -1;
+      s_hq[nrej] = ZQ;
+      s_hr[nrej] = ZR;
+      ++nrej;
+      if (ZQ > 0.0) {
+        // R <- max(0, R ZQ - Q ZR) on the slice; without replacement Q loses x
+        double a = 0.0, c2 = 0.0;
+        int lastp = 0;
+        for (int t = tid; t < n; t += NT) {
+          const double qv = removed(t) ? 0.0 : (double)s_Q[t];
+          const double ra = s_R[t] * ZQ;
+          const double rb = qv * ZR;
+          const double nr = fmax(0.0, ra - rb);
+          s_R[t] = nr;
+          a += nr;
+          c2 += (rm && v0 + t == x) ? 0.0 : qv;
+          if (nr > 0.0) lastp = v0 + t + 1;
+        }
+        unsigned long long lp = (unsigned long long)lastp, unused = 0ull;
+        block_sum2_max2<NT>(a, c2, lp, unused, s_r4);
+        if (rm && x >= v0 && x < v0 + n && tid == 0) s_rm[(x - v0) >> 5] |= 1u << ((x - v0) & 31);
+        exchange(as_u(a), as_u(c2), lp, 0ull);
+        if (s_fail) break;
+        ZR = dsum(0);
+        if (rm) ZQ = dsum(1);
+      }
+    }
+    if (s_fail || next < 0) break;
+    ++len;
+    node = next;
+    if (tid == 0) s_path[len] = node;
+  }
+
+  // ---- the correction token at `node`, from R on the slices (p when nothing was
+  // rejected there, or when the walk stopped before entering it).  The last
+  // exchange holds every slice's sum of R and its last token with R > 0.
+  if (!s_fail && entered != node) besta = enter(node);
+  // this slice: each thread a contiguous range of it, in token order
+  const int Lt = (n + NT - 1) / NT;
+  const int c0 = min(n, tid * Lt), c1 = min(n, c0 + Lt);
+  double cs = 0.0;
+  for (int t = c0; t < c1; ++t) cs += s_R[t];
+  double lo, hi, tot;
+  block_scan<double, NT>(cs, s_d, lo, hi, tot);
+  if (tid == 0) s_pick = -1;
+  __syncthreads();
+  if (!s_fail) {
+    double total = 0.0;
+    unsigned long long lpa = 0ull;
+    for (int s2 = 0; s2 < S; ++s2) {
+      total += __longlong_as_double((long long)s_all[s2][0]);
+      lpa = s_all[s2][2] > lpa ? s_all[s2][2] : lpa;
+    }
+    int writer = 0, fallback;  // the workgroup that writes the bonus token, and its value if no pick
+    double pre = 0.0;
+    if (total > 0.0) {
+      const double target = (double)s_uni[0] * total;
+      fallback = (int)lpa - 1;  // the last token with mass (rounding past every cumulative)
+      bool found = false;
+      for (int s2 = 0; s2 < S && !found; ++s2) {
+        const double z = __longlong_as_double((long long)s_all[s2][0]);
+        if (pre <= target && target < pre + z) {
+          writer = s2;
+          found = true;
+        } else {
+          pre += z;
+        }
+      }
+      if (found && writer == sl) {
+        // inside this slice: cumulative = (the earlier slices) + the in-slice prefix
+        const double tl = target - pre;
+        if (lo <= tl && tl < hi) {
+          double cum = pre + lo;
+          int pick = -1;
+          for (int t = c0; t < c1; ++t) {
+            cum += s_R[t];
+            if (cum > target) {
+              pick = v0 + t;
+              break;
+            }
+          }
+          if (pick >= 0) s_pick = pick;
+        }
+      }
+    } else {
+      fallback = (int)key_index(besta);  // no residual mass: the node's best token
+    }
+    __syncthreads();
+    if (sl == writer && tid == 0) bonus_token[b] = s_pick >= 0 ? s_pick : fallback;
+  }
+  if (sl == 0) {
+    for (int t = tid; t <= dcap; t += NT)
+      accept_path[(long long)b * (dcap + 1) + t] = (!s_fail && t <= len) ? s_path[t] : -1;
+    if (tid == 0) accept_len[b] = s_fail ? -1 : len;
+  }
+  if (s_fail && tid == 0) bonus_token[b] = -1;
+}
+
 }  // namespace
 }  // namespace tv
 
@@ -1364,10 +1715,43 @@ extern "C" int tree_accept_sample_draft(int B, int T_max, int dcap, int V, const
     return TV_EINVAL;
   if (!workspace || ws_bytes < (size_t)B * V * sizeof(double) || (reinterpret_cast<uintptr_t>(workspace) & 7))
     return TV_EWORKSPACE;
-  hipLaunchKernelGGL(tv::k_tree_accept_sample_draft, dim3(B), dim3(tv::kThreads), 0,
-                     reinterpret_cast<hipStream_t>(stream), T_max, dcap, V, without_replacement ? 1 : 0,
-                     draft_tokens, parents, tree_size, target_probs, draft_probs, uniforms, status, accept_len,
-                     accept_path, bonus_token, reinterpret_cast<double*>(workspace));
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  double* ws = reinterpret_cast<double*>(workspace);
+  // Few requests over a large vocabulary: S workgroups per request (the sliced
+  // kernel), S as large as the device holds all B x S of them at once (at most
+  // kSliceMax, slices of at least 1024 tokens and at most 5120).
+  constexpr int kSliceNT = 512;
+  constexpr int kSliceLdsCap = 5120 * 12 + 5120 / 8;  // the LDS the residency count assumes
+  static int cap[8];  // per device: sliced workgroups resident at once, 0 = not yet known
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return TV_ELAUNCH;
+  int& cp = cap[dev & 7];
+  if (cp == 0) {
+    int cus = 0, per = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per, reinterpret_cast<const void*>(tv::k_tree_accept_sample_draft_sliced<kSliceNT>), kSliceNT,
+            kSliceLdsCap) != hipSuccess)
+      return TV_ELAUNCH;
+    cp = max(1, cus * per);
+  }
+  // (the exchange slots live in each request's workspace row: 4 words per slice
+  // and exchange)
+  const int S = std::min(std::min(std::min(tv::kSliceMax, cp / B), V / 1024), V / (4 * tv::slice_exchanges(T_max)));
+  const int L = S >= 2 ? ((V + S - 1) / S + 63) / 64 * 64 : 0;
+  if (S >= 2 && L <= 5120) {
+    const size_t dyn = (size_t)L * 12 + (size_t)(L + 31) / 32 * 4;
+    hipLaunchKernelGGL(tv::k_slice_reset, dim3(B), dim3(256), 0, st, ws, V, 4 * S * tv::slice_exchanges(T_max));
+    TV_CHECK_LAUNCH();
+    hipLaunchKernelGGL(tv::k_tree_accept_sample_draft_sliced<kSliceNT>, dim3(S, B), dim3(kSliceNT), dyn, st, S, L,
+                       T_max, dcap, V, without_replacement ? 1 : 0, draft_tokens, parents, tree_size, target_probs,
+                       draft_probs, uniforms, status, accept_len, accept_path, bonus_token, ws);
+    TV_CHECK_LAUNCH();
+    return TV_OK;
+  }
+  hipLaunchKernelGGL(tv::k_tree_accept_sample_draft, dim3(B), dim3(tv::kThreads), 0, st, T_max, dcap, V,
+                     without_replacement ? 1 : 0, draft_tokens, parents, tree_size, target_probs, draft_probs,
+                     uniforms, status, accept_len, accept_path, bonus_token, ws);
   TV_CHECK_LAUNCH();
   return TV_OK;
 }
