@@ -483,24 +483,64 @@ __device__ __forceinline__ float key_float(uint32_t k) {
 // kKlMaxV), else the logits are re-read on every pass.  With NPT = 0 a weight is
 // formed where a pass needs it: every one for the first top-p level, only the
 // chosen bin's or the kept tokens' afterwards.
-// The requests in order of their rows' cost, so that the rows still starting as
+// Rows are launched in order of their cost, so that the rows still starting as
 // the grid drains are short ones.  The filter settings decide a row's cost: a
 // radix top-p cut (most), then a full pass without top-p (or with a long top-k),
-// a short ranked top-k list with top-p, without it, and greedy (least).  Returns
-// the y-th request of that order (requests of one class keep their order).
+// a short ranked top-k list with top-p, without it, and greedy (least).
+template <int NT>
+__device__ __forceinline__ int cost_class(int r, int V, const float* __restrict__ temperature,
+                                          const int* __restrict__ top_k, const float* __restrict__ top_p) {
+  const float t = temperature[r], p = top_p[r];
+  const int k = top_k[r];
+  if (!(t > 0.0f) || k == 1 || p <= 0.0f) return 4;
+  if (p < 1.0f) return (k > 1 && k < V && k <= NT) ? 2 : 0;
+  return (k > 1 && k < V && k <= kFastK) ? 3 : 1;
+}
+
+// Up to NT requests: the k-th row of all requests' rows in cost order (the
+// requests of one class, and each request's rows, keep their order).  A request
+// whose status or tree size is invalid has one row.  Sets (b, i) and returns
+// true, or returns false for k past the last row.
+template <int NT>
+__device__ __forceinline__ bool row_by_cost(int k, int B, int V, int T_max, const int* __restrict__ tree_size,
+                                            const int* __restrict__ status, const float* __restrict__ temperature,
+                                            const int* __restrict__ top_k, const float* __restrict__ top_p,
+                                            int& b, int& i) {
+  constexpr int NW = NT / 64;
+  __shared__ int s_sc[NW], s_b, s_i;
+  const int tid = threadIdx.x;
+  int c_r = 5, n_r = 0;
+  if (tid < B) {
+    c_r = cost_class<NT>(tid, V, temperature, top_k, top_p);
+    const int T = tree_size[tid];
+    n_r = ((status && status[tid] != TV_ST_OK) || T < 1 || T > T_max) ? 1 : T;
+  }
+  int first = 0, rows = 0;  // this request's first row in the order; all rows
+  for (int c = 0; c < 5; ++c) {
+    int lo, hi, tot;
+    block_scan<int, NT>(c_r == c ? n_r : 0, s_sc, lo, hi, tot);
+    first += c < c_r ? tot : (c == c_r ? lo : 0);
+    rows += tot;
+  }
+  if (k >= rows) return false;
+  if (tid < B && first <= k && k < first + n_r) {
+    s_b = tid;
+    s_i = k - first;
+  }
+  __syncthreads();
+  b = __builtin_amdgcn_readfirstlane(s_b);
+  i = __builtin_amdgcn_readfirstlane(s_i);
+  return true;
+}
+
+// More than NT requests: the y-th request in cost order.
 template <int NT>
 __device__ __forceinline__ int request_by_cost(int y, int B, int V, const float* __restrict__ temperature,
                                                const int* __restrict__ top_k, const float* __restrict__ top_p) {
   constexpr int NW = NT / 64;
   __shared__ int s_cc[5], s_wc[NW], s_req;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  auto cls = [&](int r) -> int {
-    const float t = temperature[r], p = top_p[r];
-    const int k = top_k[r];
-    if (!(t > 0.0f) || k == 1 || p <= 0.0f) return 4;
-    if (p < 1.0f) return (k > 1 && k < V && k <= NT) ? 2 : 0;
-    return (k > 1 && k < V && k <= kFastK) ? 3 : 1;
-  };
+  auto cls = [&](int r) { return cost_class<NT>(r, V, temperature, top_k, top_p); };
   if (tid < 5) s_cc[tid] = 0;
   __syncthreads();
   for (int r = tid; r < B; r += NT) atomicAdd(&s_cc[cls(r)], 1);
@@ -539,9 +579,16 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
 #pragma clang fp contract(off)
   constexpr int NW = NT / 64;  // wavefronts
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int i = blockIdx.x;
-  const int b = gridDim.y > 1 ? uni(request_by_cost<NT>(blockIdx.y, (int)gridDim.y, V, temperature, top_k, top_p))
-                              : (int)blockIdx.y;
+  // grid (T_max * B): one block per row, rows in cost order; grid (T_max, B):
+  // block (i, y) takes row i of the y-th request in cost order
+  int i = blockIdx.x, b = 0;
+  if ((int)gridDim.x > T_max) {
+    if (!row_by_cost<NT>(blockIdx.x, (int)gridDim.x / T_max, V, T_max, tree_size, status, temperature, top_k,
+                         top_p, b, i))
+      return;
+  } else if (gridDim.y > 1) {
+    b = uni(request_by_cost<NT>(blockIdx.y, (int)gridDim.y, V, temperature, top_k, top_p));
+  }
   int T = tree_size[b];
   if ((status && status[b] != TV_ST_OK) || T < 1 || T > T_max) T = 1;
   if (i >= T) return;
@@ -1692,7 +1739,10 @@ extern "C" int tree_sampling_probs(int B, int T_max, int V, const float* logits,
       attr_set = true;
     }
   }
-  hipLaunchKernelGGL(k, dim3(T_max, B), dim3(nt), dyn, reinterpret_cast<hipStream_t>(stream), T_max, V, logits,
+  // up to nt requests: blocks walk the rows in cost order, those past the last
+  // row end at once; more: one block per (row, request)
+  const dim3 grid = B > 1 && B <= nt ? dim3(T_max * B) : dim3(T_max, B);
+  hipLaunchKernelGGL(k, grid, dim3(nt), dyn, reinterpret_cast<hipStream_t>(stream), T_max, V, logits,
                      tree_size, status, temperature, top_k, top_p, min_p, probs);
   TV_CHECK_LAUNCH();
   return TV_OK;
