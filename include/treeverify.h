@@ -332,17 +332,25 @@ int tree_accept(int B, int T_max, int dcap, const int* draft_tokens, const int* 
  * best token (probability desc, token asc).
  * In:  draft_tokens, parents [B][T_max], tree_size [B], status [B];
  *      target_probs float32 [B][T_max][V] (the target's distribution at every
- *      node after the caller's temperature / top-k / top-p filtering; rows of
- *      nodes the walk does not reach are not read); uniforms float32 [B][T_max]
- *      in [0, 1): entry c >= 1 is the draw for child c's test, entry 0 the draw
- *      for the correction token.
+ *      node after the caller's temperature / top-k / top-p filtering; rows
+ *      i >= T_b are never read); uniforms float32 [B][T_max] in [0, 1): entry
+ *      c >= 1 is the draw for child c's test, entry 0 the draw for the
+ *      correction token.
  * Out: accept_len, accept_path, bonus_token as tree_accept.
- * Requires 1 <= T_max <= 256, 0 <= dcap < T_max, 1 <= V <= 262144.
+ * Workspace (optional): NULL, or at least tree_accept_sample_workspace_bytes(B,
+ *      T_max) bytes (8-byte aligned, contents arbitrary, overwritten).  With it,
+ *      a call whose rows total at most 32 MB first sums every row i < T_b on
+ *      its own workgroup (as many CUs as rows), so the walk's decisions read Z
+ *      instead of passing over each visited row; the results are the same
+ *      either way (each row is summed in the same order).  A workspace that is
+ *      too small or misaligned gives TV_EWORKSPACE.
+ * Requires 1 <= T_max <= 256, 0 <= dcap < T_max, 1 <= V <= 262144, B <= 65535.
  * ------------------------------------------------------------------------- */
+size_t tree_accept_sample_workspace_bytes(int B, int T_max);
 int tree_accept_sample(int B, int T_max, int dcap, int V, const int* draft_tokens, const int* parents,
                        const int* tree_size, const float* target_probs, const float* uniforms,
                        const int* status, int* accept_len, int* accept_path, int* bonus_token,
-                       void* stream);
+                       void* workspace, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------- *
  * tree_sampling_probs -- [TRT] "non-greedy: rejection from the target

@@ -51,12 +51,14 @@ def run_sampling(w, probs=None, uniforms=None, status=None, tokens=None, dcap=No
     stat = st.status.cpu().numpy() if status is None else status
     if status is not None:
         st.status.copy_(torch.from_numpy(np.ascontiguousarray(status, dtype=np.int32)))
-    st.accept_sample()
-    torch.cuda.synchronize()
-    got = st.accept_host()
     ref = ot.tree_accept_sample(tok, ref_tree["parents"], ref_tree["tree_size"], probs, uniforms, stat, st.dcap)
-    for k in ("accept_len", "accept_path", "bonus_token"):
-        np.testing.assert_array_equal(got[k], ref[k], err_msg=k)
+    # with the workspace (every row's sum first, when the rows are few) and without
+    for ws in (True, False):
+        st.accept_sample(workspace=ws)
+        torch.cuda.synchronize()
+        got = st.accept_host()
+        for k in ("accept_len", "accept_path", "bonus_token"):
+            np.testing.assert_array_equal(got[k], ref[k], err_msg=f"{k} (workspace {ws})")
     return got, ref
 
 
@@ -66,6 +68,17 @@ def test_sampling_dynamic_batch1():
 
 def test_sampling_ragged_batch16():
     run_sampling(gen.make_workload(3, with_attention=False))
+
+
+@pytest.mark.parametrize("V", [1000, 32000, 128256])
+def test_sampling_few_rows_large_vocab(V):
+    # few enough rows that the workspace path sums every row first, vocabularies
+    # up to 128256 (a partial last piece at 128256 and 1000)
+    w = gen.make_custom(cfg_id=1260 + V % 89, B=3, mode="given", given_sizes=[16, 9, 1], given_depth=6, V=V, P=10,
+                        accept_prob=0.85, T_max=16)
+    assert w.B * w.T_max * V * 4 <= 32 << 20
+    got, _ = run_sampling(w)
+    assert got["accept_len"].max() >= 1
 
 
 @pytest.mark.parametrize("V", [50, 1000, 32000, 128256])

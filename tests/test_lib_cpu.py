@@ -157,12 +157,21 @@ def test_layer_calls_host_validation():
 
 def test_accept_sample_host_validation():
     L = tv.lib()
-    # tree_accept_sample(B, T_max, dcap, V, tokens, parents, size, probs, uniforms, status, len, path, bonus, stream)
-    assert L.tree_accept_sample(1, 16, 16, 100, X, X, X, X, X, X, X, X, X, None) == tv.TV_EINVAL   # dcap >= T_max
-    assert L.tree_accept_sample(1, 257, 7, 100, X, X, X, X, X, X, X, X, X, None) == tv.TV_EUNSUPPORTED
-    assert L.tree_accept_sample(1, 16, 7, 0, X, X, X, X, X, X, X, X, X, None) == tv.TV_EINVAL      # V = 0
-    assert L.tree_accept_sample(1, 16, 7, 100, X, X, X, None, X, X, X, X, X, None) == tv.TV_EINVAL
-    assert L.tree_accept_sample(0, 16, 7, 100, X, X, X, X, X, X, X, X, X, None) == tv.TV_EINVAL
+    # tree_accept_sample(B, T_max, dcap, V, tokens, parents, size, probs, uniforms, status, len, path, bonus,
+    #                    ws, ws_bytes, stream)
+    assert L.tree_accept_sample(1, 16, 16, 100, X, X, X, X, X, X, X, X, X, None, 0, None) == tv.TV_EINVAL  # dcap
+    assert L.tree_accept_sample(1, 257, 7, 100, X, X, X, X, X, X, X, X, X, None, 0, None) == tv.TV_EUNSUPPORTED
+    assert L.tree_accept_sample(1, 16, 7, 0, X, X, X, X, X, X, X, X, X, None, 0, None) == tv.TV_EINVAL      # V = 0
+    assert L.tree_accept_sample(1, 16, 7, 100, X, X, X, None, X, X, X, X, X, None, 0, None) == tv.TV_EINVAL
+    assert L.tree_accept_sample(0, 16, 7, 100, X, X, X, X, X, X, X, X, X, None, 0, None) == tv.TV_EINVAL
+    # the optional workspace: B x T_max float64 sums, 8-byte aligned
+    assert tv.tree_accept_sample_workspace_bytes(3, 16) == 3 * 16 * 8
+    assert tv.tree_accept_sample_workspace_bytes(0, 16) == 0
+    ws = ctypes.c_void_p(0x200000)
+    assert L.tree_accept_sample(3, 16, 7, 100, X, X, X, X, X, X, X, X, X, ws, 3 * 16 * 8 - 1,
+                                None) == tv.TV_EWORKSPACE
+    assert L.tree_accept_sample(3, 16, 7, 100, X, X, X, X, X, X, X, X, X, ctypes.c_void_p(0x200004), 4096,
+                                None) == tv.TV_EWORKSPACE
 
 
 def test_rope_call_host_validation():

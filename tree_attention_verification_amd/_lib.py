@@ -60,7 +60,8 @@ _SIGS = {
     "tree_build_layer_workspace_bytes": (SZ, [I, I, I, I]),
     "tree_build_layer": (I, [I, I, I, I, I, P, I, P, SZ, P, P, P]),
     "tree_build_finish": (I, [I, I, I, I, I, P, I, P, SZ, P, P, P, P, P, I, P, P, P, P, P, P, P, P, P]),
-    "tree_accept_sample": (I, [I, I, I, I, P, P, P, P, P, P, P, P, P, P]),
+    "tree_accept_sample_workspace_bytes": (SZ, [I, I]),
+    "tree_accept_sample": (I, [I, I, I, I, P, P, P, P, P, P, P, P, P, P, SZ, P]),
     "tree_attention_rope": (I, [I, I, I, I, I, I, P, P, P, LL, P, P, P, P, F, F, P, P, SZ, P]),
     "tree_sampling_probs": (I, [I, I, I, P, P, P, P, P, P, P, P, P]),
     "tree_accept_sample_draft_workspace_bytes": (SZ, [I, I]),
@@ -309,12 +310,17 @@ def tree_build_finish(B, V, K, D, total_tokens, root_token, T_max, state, draft_
     _check("tree_build_finish", rc)
 
 
+def tree_accept_sample_workspace_bytes(B, T_max) -> int:
+    return int(lib().tree_accept_sample_workspace_bytes(B, T_max))
+
+
 def tree_accept_sample(B, T_max, dcap, V, draft_tokens, parents, tree_size, target_probs, uniforms, status,
-                       accept_len, accept_path, bonus_token, stream=None):
+                       accept_len, accept_path, bonus_token, workspace=None, stream=None):
+    wp, wn = _ws(workspace)
     rc = lib().tree_accept_sample(B, T_max, dcap, V, _dev(draft_tokens, "draft_tokens"), _dev(parents, "parents"),
                                   _dev(tree_size, "tree_size"), _dev(target_probs, "target_probs"),
                                   _dev(uniforms, "uniforms"), _dev(status, "status"), _dev(accept_len, "accept_len"),
-                                  _dev(accept_path, "accept_path"), _dev(bonus_token, "bonus_token"),
+                                  _dev(accept_path, "accept_path"), _dev(bonus_token, "bonus_token"), wp, wn,
                                   _stream(stream))
     _check("tree_accept_sample", rc)
 

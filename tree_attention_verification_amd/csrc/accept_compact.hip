@@ -151,7 +151,11 @@ __global__ __launch_bounds__(64) void k_tree_accept(int T_max, int dcap, const i
 // 16-byte loads in flight per thread cover it in one round trip).  Per visited
 // node one coalesced pass over the row gives Z while the
 // first wavefront fetches p(x) of every child at once (lane c = node c), so the
-// sequential decisions only move data between lanes.  The correction cuts the
+// sequential decisions only move data between lanes.  With Z of every row
+// already known (k_row_mass, one workgroup per row, for calls whose rows are few
+// enough that reading them all costs less than the walk's chain of passes), the
+// first wavefront fetches every child's p(x) from its parent's row up front and
+// the walk reads no row at all.  The correction cuts the
 // row into 1024 contiguous chunks: each wavefront sums its chunks with coalesced
 // loads, a block scan of the chunk sums finds the chunk holding the target, and
 // the first wavefront scans that chunk.
@@ -174,13 +178,80 @@ __device__ __forceinline__ double wave_incl_f64(double v, int lane) {
   return v;
 }
 
+constexpr int kSampleWaves = kSampleThreads / 64;
+
+// A row is read in pieces of kPiece entries; in piece k thread t owns the 8
+// contiguous entries [k kPiece + 8 t, + 8) (a wavefront reads 2 KB contiguous).
+__device__ __forceinline__ void load8(const float* __restrict__ row, int V, int vec4, int k, float (&x)[8]) {
+  const int v0 = k * kPiece + 8 * (int)threadIdx.x;
+  if (vec4 && v0 + 8 <= V) {
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    const f4 a = *reinterpret_cast<const f4*>(row + v0), c = *reinterpret_cast<const f4*>(row + v0 + 4);
+    x[0] = a[0]; x[1] = a[1]; x[2] = a[2]; x[3] = a[3];
+    x[4] = c[0]; x[5] = c[1]; x[6] = c[2]; x[7] = c[3];
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = v0 + e < V ? row[v0 + e] : 0.0f;
+  }
+}
+
+// the workgroup's float64 sum of one value per thread: wavefront butterflies,
+// then the wavefronts in order (every thread gets it)
+__device__ __forceinline__ double sample_block_sum(double v, double* s_red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  v = wave_sum_f64(v);
+  if (lane == 0) s_red[wave] = v;
+  __syncthreads();
+  double t = 0.0;
+#pragma unroll
+  for (int w = 0; w < kSampleWaves; ++w) t += s_red[w];
+  __syncthreads();
+  return t;
+}
+
+// float64 sum of a whole row (four pieces' loads in flight at a time), in the
+// one order both kernels use: each thread adds its entries piece by piece, then
+// the workgroup sum above
+__device__ __forceinline__ double row_sum_f64(const float* __restrict__ row, int V, int vec4, double* s_red) {
+  const int n_pieces = (V + kPiece - 1) / kPiece;
+  double acc = 0.0;
+  for (int k0 = 0; k0 < n_pieces; k0 += 4) {
+    float x[4][8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (k0 + u < n_pieces) load8(row, V, vec4, k0 + u, x[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (k0 + u < n_pieces)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc += (double)x[u][e];
+  }
+  return sample_block_sum(acc, s_red);
+}
+
+// Z of row (b, i) for every node i < T_b: one workgroup per row, grid (T_max, B)
+__global__ __launch_bounds__(kSampleThreads) void k_row_mass(int T_max, int V, int vec4,
+                                                             const int* __restrict__ tree_size,
+                                                             const int* __restrict__ status,
+                                                             const float* __restrict__ target_probs,
+                                                             double* __restrict__ Z) {
+  const int i = blockIdx.x, b = blockIdx.y;
+  int T = tree_size[b];
+  if (!(status[b] == TV_ST_OK && T >= 1 && T <= T_max)) T = 1;
+  if (i >= T) return;
+  __shared__ double s_red[kSampleWaves];
+  const long long r = (long long)b * T_max + i;
+  const double z = row_sum_f64(target_probs + r * V, V, vec4, s_red);
+  if (threadIdx.x == 0) Z[r] = z;
+}
+
 __global__ __launch_bounds__(kSampleThreads) void k_tree_accept_sample(
     int T_max, int dcap, int V, int vec4, const int* __restrict__ draft_tokens, const int* __restrict__ parents,
     const int* __restrict__ tree_size, const float* __restrict__ target_probs, const float* __restrict__ uniforms,
-    const int* __restrict__ status, int* __restrict__ accept_len, int* __restrict__ accept_path,
-    int* __restrict__ bonus_token) {
+    const int* __restrict__ status, const double* __restrict__ Zpre, int* __restrict__ accept_len,
+    int* __restrict__ accept_path, int* __restrict__ bonus_token) {
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  constexpr int NWV = kSampleThreads / 64;
+  constexpr int NWV = kSampleWaves;
   __shared__ double s_red[NWV];
   __shared__ int s_rem[kTMaxLimit];  // tokens rejected at the current node
   __shared__ int s_path[kTMaxLimit];
@@ -200,61 +271,50 @@ __global__ __launch_bounds__(kSampleThreads) void k_tree_accept_sample(
     par_q[q] = (c > 0 && c < T) ? parents[ob + c] : -2;
     u_q[q] = c < T_max ? uniforms[ob + c] : 0.0f;
   }
-  auto block_sum = [&](double v) -> double {
-    v = wave_sum_f64(v);
-    if (lane == 0) s_red[wave] = v;
-    __syncthreads();
-    double t = 0.0;
-#pragma unroll
-    for (int w = 0; w < NWV; ++w) t += s_red[w];
-    __syncthreads();
-    return t;
-  };
-  // A row is read in pieces of kPiece entries; in piece k thread t owns the 8
-  // contiguous entries [k kPiece + 8 t, + 8) (a wavefront reads 2 KB contiguous).
+  auto block_sum = [&](double v) -> double { return sample_block_sum(v, s_red); };
   const int n_pieces = (V + kPiece - 1) / kPiece;
   auto load8 = [&](const float* row, int k, float (&x)[8]) __attribute__((always_inline)) {
-    const int v0 = k * kPiece + 8 * tid;
-    if (vec4 && v0 + 8 <= V) {
-      typedef float f4 __attribute__((ext_vector_type(4)));
-      const f4 a = *reinterpret_cast<const f4*>(row + v0), c = *reinterpret_cast<const f4*>(row + v0 + 4);
-      x[0] = a[0]; x[1] = a[1]; x[2] = a[2]; x[3] = a[3];
-      x[4] = c[0]; x[5] = c[1]; x[6] = c[2]; x[7] = c[3];
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = v0 + e < V ? row[v0 + e] : 0.0f;
-    }
+    tv::load8(row, V, vec4, k, x);
   };
-  // float64 sum of a whole row (four pieces' loads in flight at a time)
-  auto row_sum = [&](const float* row) -> double {
-    double acc = 0.0;
-    for (int k0 = 0; k0 < n_pieces; k0 += 4) {
-      float x[4][8];
+  // With every row's Z given: p(x) of every node, from its parent's row, fetched
+  // once (first wavefront; a token outside the vocabulary has no mass)
+  // and Z of every node (lane c = node c)
+  float pall_q[NQ];
+  double z_q[NQ];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (k0 + u < n_pieces) load8(row, k0 + u, x[u]);
+  for (int q = 0; q < NQ; ++q) {
+    pall_q[q] = 0.0f;
+    z_q[q] = 0.0;
+    if (Zpre && wave == 0 && par_q[q] >= 0 && par_q[q] < T && tok_q[q] >= 0 && tok_q[q] < V)
+      pall_q[q] = target_probs[(ob + par_q[q]) * (long long)V + tok_q[q]];
+    if (Zpre && wave == 0 && lane + 64 * q < T) z_q[q] = Zpre[ob + lane + 64 * q];
+  }
+  // Z of node n (wave-uniform n) from the lane that holds it
+  auto z_of = [&](int n) -> double {
+    double z = z_q[0];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (k0 + u < n_pieces)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc += (double)x[u][e];
-    }
-    return block_sum(acc);
+    for (int q = 1; q < NQ; ++q) z = (n >> 6) == q ? z_q[q] : z;
+    const long long bits = __double_as_longlong(z);
+    const int lo = __builtin_amdgcn_readlane((int)(bits & 0xFFFFFFFF), n & 63);
+    const int hi = __builtin_amdgcn_readlane((int)(bits >> 32), n & 63);
+    return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
   };
 
   int node = 0, len = 0, nrem = 0;
   if (tid == 0) s_path[0] = 0;
   while (ok && len < dcap) {
     const float* row = target_probs + (ob + node) * (long long)V;
-    // p(x) of every child of this node, fetched together (first wavefront); a
-    // token outside the vocabulary has no mass
+    // p(x) of every child of this node, fetched together (first wavefront)
     float pc_q[NQ];
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       pc_q[q] = 0.0f;
-      if (wave == 0 && par_q[q] == node && tok_q[q] >= 0 && tok_q[q] < V) pc_q[q] = row[tok_q[q]];
+      if (wave == 0 && par_q[q] == node) {
+        if (Zpre) pc_q[q] = pall_q[q];
+        else if (tok_q[q] >= 0 && tok_q[q] < V) pc_q[q] = row[tok_q[q]];
+      }
     }
-    const double Z = row_sum(row);
+    const double Z = Zpre ? z_of(node) : row_sum_f64(row, V, vec4, s_red);
     if (wave == 0) {
       // children in ascending id (the current node and every decision are
       // wave-uniform); rejected token r sits in lane r % 64, slot r / 64
@@ -315,18 +375,35 @@ __global__ __launch_bounds__(kSampleThreads) void k_tree_accept_sample(
     for (int q = 0; q < nrem; ++q) r |= s_rem[q] == v;
     return r;
   };
+  // which of this thread's entries are removed: bit e of byte k stands for entry
+  // k kPiece + 8 tid + e (each thread writes and reads only its own bytes)
+  __shared__ uint8_t s_rbits[kMaxPieces * kSampleThreads];
+  for (int k = 0; k < n_pieces; ++k) s_rbits[k * kSampleThreads + tid] = 0;
+  for (int q = 0; q < nrem; ++q) {
+    const int v = s_rem[q];
+    if (v >= 0 && v < V && ((v % kPiece) >> 3) == tid) s_rbits[(v / kPiece) * kSampleThreads + tid] |= 1u << (v & 7);
+  }
   // residual mass of this thread's run of a piece
   auto run_mass = [&](int k, float (&x)[8]) -> double {
     const int v0 = k * kPiece + 8 * tid;
+    const uint32_t rb = s_rbits[k * kSampleThreads + tid];
     double run = 0.0;
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-      if (v0 + e < V && !removed(v0 + e)) run += (double)x[e];
+      if (v0 + e < V && !((rb >> e) & 1u)) run += (double)x[e];
     return run;
   };
-  // pass 1: the residual total, hence the target
+  // pass 1: the residual total, hence the target (pieces 0..3 stay in registers
+  // for pass 2)
+  float xa[4][8];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    if (u < n_pieces) load8(row, u, xa[u]);
   double acc = 0.0;
-  for (int k0 = 0; k0 < n_pieces; k0 += 4) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    if (u < n_pieces) acc += run_mass(u, xa[u]);
+  for (int k0 = 4; k0 < n_pieces; k0 += 4) {
     float x[4][8];
 #pragma unroll
     for (int u = 0; u < 4; ++u)
@@ -339,45 +416,63 @@ __global__ __launch_bounds__(kSampleThreads) void k_tree_accept_sample(
   if (tid == 0) s_pick = -1;
   __syncthreads();
   const double target = (double)__int_as_float(__builtin_amdgcn_readlane(__float_as_int(u_q[0]), 0)) * total;
-  __shared__ double s_last[NWV];
-  __shared__ double s_carry;
+  __shared__ double s_last[4][NWV];
   if (total > 0.0) {
-    // pass 2, piece by piece: a block inclusive scan of the runs' masses; run
-    // (k, t) spans [I(k, t-1), I(k, t)) of the cumulative mass, each boundary one
-    // stored number shared by both neighbours, so at most one run holds the target
+    // pass 2, four pieces at a time: a block inclusive scan of the runs' masses;
+    // run (k, t) spans [I(k, t-1), I(k, t)) of the cumulative mass, each boundary
+    // one stored number shared by both neighbours, so at most one run holds the
+    // target.  The four pieces' wavefront scans share one barrier; the carry into
+    // piece k + 1 is the last thread's upper bound of piece k, which every thread
+    // forms itself with the same additions.
     double carry = 0.0;
-    for (int k = 0; k < n_pieces; ++k) {
-      float x[8];
-      load8(row, k, x);
-      const double incl = wave_incl_f64(run_mass(k, x), lane);
-      if (lane == 63) s_last[wave] = incl;
-      __syncthreads();
-      double off = carry;
-      for (int w = 0; w < wave; ++w) off += s_last[w];
-      const double hi = off + incl;
-      const double up = __shfl_up(hi, 1, 64);
-      const double lo = lane > 0 ? up : off;
-      if (lo <= target && target < hi) {
-        // this run holds the target: walk it; if rounding keeps the sum below the
-        // target, its last entry with mass
-        const int v0 = k * kPiece + 8 * tid;
-        double cum = lo;
-        int pick = -1, last = -1;
-        for (int e = 0; e < 8 && v0 + e < V; ++e) {
-          if (removed(v0 + e)) continue;
-          if (x[e] > 0.0f) last = v0 + e;
-          cum += (double)x[e];
-          if (cum > target) {
-            pick = v0 + e;
-            break;
-          }
-        }
-        s_pick = pick >= 0 ? pick : last;
+    auto scan_group = [&](int k0, float (&x)[4][8]) __attribute__((always_inline)) {
+      double incl[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) incl[u] = k0 + u < n_pieces ? wave_incl_f64(run_mass(k0 + u, x[u]), lane) : 0.0;
+      if (lane == 63) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) s_last[u][wave] = incl[u];
       }
-      if (tid == kSampleThreads - 1) s_carry = hi;
       __syncthreads();
-      carry = s_carry;
-      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (k0 + u >= n_pieces) break;
+        double off = carry;
+        for (int w = 0; w < wave; ++w) off += s_last[u][w];
+        const double hi = off + incl[u];
+        const double up = __shfl_up(hi, 1, 64);
+        const double lo = lane > 0 ? up : off;
+        if (lo <= target && target < hi) {
+          // this run holds the target: walk it; if rounding keeps the sum below
+          // the target, its last entry with mass
+          const int v0 = (k0 + u) * kPiece + 8 * tid;
+          const uint32_t rb = s_rbits[(k0 + u) * kSampleThreads + tid];
+          double cum = lo;
+          int pick = -1, last = -1;
+          for (int e = 0; e < 8 && v0 + e < V; ++e) {
+            if ((rb >> e) & 1u) continue;
+            if (x[u][e] > 0.0f) last = v0 + e;
+            cum += (double)x[u][e];
+            if (cum > target) {
+              pick = v0 + e;
+              break;
+            }
+          }
+          s_pick = pick >= 0 ? pick : last;
+        }
+        double c = carry;
+        for (int w = 0; w < NWV - 1; ++w) c += s_last[u][w];
+        carry = c + s_last[u][NWV - 1];
+      }
+      __syncthreads();  // (s_last is rewritten by the next group)
+    };
+    scan_group(0, xa);
+    for (int k0 = 4; k0 < n_pieces; k0 += 4) {
+      float x[4][8];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (k0 + u < n_pieces) load8(row, k0 + u, x[u]);
+      scan_group(k0, x);
     }
     __syncthreads();
     if (s_pick < 0) {  // rounding left the target past the total: the last token with residual mass
@@ -660,19 +755,37 @@ int accept_compact_impl(int B, int T_max, int dcap, const int* draft_tokens, con
 }  // namespace
 }  // namespace tv
 
+extern "C" size_t tree_accept_sample_workspace_bytes(int B, int T_max) {
+  if (B <= 0 || T_max <= 0) return 0;
+  return (size_t)B * T_max * sizeof(double);
+}
+
 extern "C" int tree_accept_sample(int B, int T_max, int dcap, int V, const int* draft_tokens, const int* parents,
                                   const int* tree_size, const float* target_probs, const float* uniforms,
                                   const int* status, int* accept_len, int* accept_path, int* bonus_token,
-                                  void* stream) {
+                                  void* workspace, size_t ws_bytes, void* stream) {
   if (B <= 0 || T_max <= 0 || dcap < 0 || dcap >= T_max || V <= 0) return TV_EINVAL;
-  if (T_max > tv::kTMaxLimit || V > tv::kMaxPieces * tv::kPiece) return TV_EUNSUPPORTED;
+  if (T_max > tv::kTMaxLimit || V > tv::kMaxPieces * tv::kPiece || B > 65535) return TV_EUNSUPPORTED;
   if (!draft_tokens || !parents || !tree_size || !target_probs || !uniforms || !status || !accept_len ||
       !accept_path || !bonus_token)
     return TV_EINVAL;
+  const size_t zbytes = (size_t)B * T_max * sizeof(double);
+  if (workspace && (ws_bytes < zbytes || (reinterpret_cast<uintptr_t>(workspace) & 7))) return TV_EWORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int vec4 = (V % 4 == 0) && ((reinterpret_cast<uintptr_t>(target_probs) & 15) == 0);
-  hipLaunchKernelGGL(tv::k_tree_accept_sample, dim3(B), dim3(tv::kSampleThreads), 0,
-                     reinterpret_cast<hipStream_t>(stream), T_max, dcap, V, vec4, draft_tokens, parents, tree_size,
-                     target_probs, uniforms, status, accept_len, accept_path, bonus_token);
+  // Every row's Z first, on as many CUs as there are rows, when reading all the
+  // rows costs less than the walk's passes over the visited ones (up to 32 MB of
+  // rows: a few microseconds; the walk spends a few per visited node).
+  double* Z = nullptr;
+  if (workspace && (double)B * T_max * V * sizeof(float) <= 32.0 * (1 << 20)) {
+    Z = reinterpret_cast<double*>(workspace);
+    hipLaunchKernelGGL(tv::k_row_mass, dim3(T_max, B), dim3(tv::kSampleThreads), 0, st, T_max, V, vec4, tree_size,
+                       status, target_probs, Z);
+    TV_CHECK_LAUNCH();
+  }
+  hipLaunchKernelGGL(tv::k_tree_accept_sample, dim3(B), dim3(tv::kSampleThreads), 0, st, T_max, dcap, V, vec4,
+                     draft_tokens, parents, tree_size, target_probs, uniforms, status, Z, accept_len, accept_path,
+                     bonus_token);
   TV_CHECK_LAUNCH();
   return TV_OK;
 }

@@ -268,12 +268,23 @@ class TreeVerifyStep:
         """The target's distribution at every node [B][T_max][V] and the draws [B][T_max]."""
         self.target_probs = _t(np.ascontiguousarray(probs, dtype=np.float32), self.device)
         self.uniforms = _t(np.ascontiguousarray(uniforms, dtype=np.float32), self.device)
+        self._alloc_ws_sample()
 
-    def accept_sample(self, stream=None):
-        """tree_accept_sample: target-only tree rejection sampling."""
+    def _alloc_ws_sample(self):
+        """tree_accept_sample's optional workspace (one float64 per row), allocated once."""
+        if getattr(self, "ws_sample", None) is None:
+            self.ws_sample = torch.empty(tv.tree_accept_sample_workspace_bytes(self.B, self.T_max),
+                                         dtype=torch.uint8, device=self.device)
+
+    def accept_sample(self, stream=None, workspace=True):
+        """tree_accept_sample: target-only tree rejection sampling (workspace=False: the
+        call without its optional workspace, which sums each visited row on the way)."""
+        if workspace:
+            self._alloc_ws_sample()
         tv.tree_accept_sample(self.B, self.T_max, self.dcap, self.target_probs.shape[-1], self.draft_tokens,
                               self.parents, self.tree_size, self.target_probs, self.uniforms, self.status,
-                              self.accept_len, self.accept_path, self.bonus_token, stream)
+                              self.accept_len, self.accept_path, self.bonus_token,
+                              self.ws_sample if workspace else None, stream)
 
     def set_sampling_inputs(self, logits: np.ndarray, params, draft_probs=None):
         """Target logits [B][T_max][V] with the per-request (temperature, top_k, top_p,
@@ -286,6 +297,7 @@ class TreeVerifyStep:
         self.top_p = _t(np.asarray(top_p, np.float32), self.device)
         self.min_p = _t(np.asarray(min_p, np.float32), self.device)
         self.target_probs = torch.zeros_like(self.target_logits)
+        self._alloc_ws_sample()
         if draft_probs is not None:
             self.draft_probs = _t(np.ascontiguousarray(draft_probs, dtype=np.float32), self.device)
             V = self.target_logits.shape[-1]
