@@ -125,6 +125,36 @@ def test_sampling_edge_cases():
     run_sampling(w, probs, uni, status=status, tokens=tokens)
 
 
+def test_sampling_wide_nodes():
+    # one level under the root: 64 children (the widest node tested a child per
+    # lane), 65 and 129 (one child at a time), some with repeated tokens (a
+    # repeat brings no mass) and tokens outside the vocabulary
+    w = gen.make_custom(cfg_id=1250, B=4, mode="given", given_sizes=[65, 66, 130, 40], given_depth=1, V=300, P=4,
+                        T_max=160, dcap=3, accept_prob=0.3)
+    assert all(int((w.given_parents[b, 1:w.given_size[b]] == 0).sum()) == w.given_size[b] - 1 for b in range(4))
+    tokens = w.given_tokens.copy()
+    tokens[1, 1:66] = np.arange(65) % 23            # 65 children, 23 distinct tokens
+    tokens[2, 1:130] = np.arange(129) % 50          # 129 children, 50 distinct tokens
+    tokens[3, 1:40] = np.arange(39) % 7             # 39 children, 7 distinct tokens
+    tokens[3, 5] = -1
+    tokens[3, 9] = w.V + 2
+    tokens[1, 60] = 250                             # first occurrences past the repeats
+    tokens[2, 100] = 299
+    probs, uni = gen.synthetic_target_probs(w, tokens, w.given_parents, w.given_size)
+    uni[0, 40] = 0.0     # u = 0: taken if no earlier child is and its token has mass
+    uni[1, 31] = 0.0     # a repeated token (child 8's): no mass, so not taken
+    uni[1, 60] = 0.0
+    uni[2, 100] = 0.0    # past the 64th child
+    got, _ = run_sampling(w, probs, uni, tokens=tokens)
+    assert got["accept_len"].tolist()[:3] == [1, 1, 1]
+    # every child rejected (the correction leaves out each distinct rejected token once)
+    uni2 = uni.copy()
+    uni2[:, 1:] = np.float32(np.nextafter(np.float32(1.0), np.float32(0.0)))
+    probs2 = probs.copy()
+    probs2[:, 0] *= 0.5                              # less than the full mass on any child
+    run_sampling(w, probs2, uni2, tokens=tokens)
+
+
 @pytest.mark.parametrize("dcap", [0, 1, 3])
 def test_sampling_depth_cap(dcap):
     w = gen.make_custom(cfg_id=1230 + dcap, B=4, mode="given", given_sizes=[64, 50, 20, 8], given_depth=7, V=500,

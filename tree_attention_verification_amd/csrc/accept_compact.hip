@@ -254,6 +254,8 @@ __global__ __launch_bounds__(kSampleThreads) void k_tree_accept_sample(
   constexpr int NWV = kSampleWaves;
   __shared__ double s_red[NWV];
   __shared__ int s_rem[kTMaxLimit];  // tokens rejected at the current node
+  __shared__ int s_cx[64], s_cid[64];  // up to 64 children of the current node: token, node id
+  __shared__ float s_cp[64], s_cu[64];  // and p(x), draw
   __shared__ int s_path[kTMaxLimit];
   __shared__ int s_next, s_nrem, s_pick;
   const long long ob = (long long)b * T_max;
@@ -316,45 +318,105 @@ __global__ __launch_bounds__(kSampleThreads) void k_tree_accept_sample(
     }
     const double Z = Zpre ? z_of(node) : row_sum_f64(row, V, vec4, s_red);
     if (wave == 0) {
-      // children in ascending id (the current node and every decision are
-      // wave-uniform); rejected token r sits in lane r % 64, slot r / 64
-      double R = 0.0;
-      int next = -1, nr = 0, rem_q[NQ];
-#pragma unroll
-      for (int q = 0; q < NQ; ++q) rem_q[q] = -1;
+      // the node's children (ascending id) and their number
+      unsigned long long km[NQ];
+      int m = 0;
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
-        unsigned long long kids = next < 0 ? __ballot(par_q[q] == node) : 0ull;
-        while (kids) {
-          const int c = __ffsll((long long)kids) - 1;
-          kids &= kids - 1;
-          const int x = __builtin_amdgcn_readlane(tok_q[q], c);
-          bool any = false;
+        km[q] = __ballot(par_q[q] == node);
+        m += __popcll(km[q]);
+      }
+      if (m <= 64) {
+        // Up to 64 children, child j (in ascending id) in lane j: whether an
+        // earlier child has its token (then it brings no mass), R_j = the mass of
+        // the earlier rejected tokens added in child order, and every child's
+        // test at once; the first child that passes is taken.  The same additions
+        // and comparisons as one child at a time.
+        int before = 0;
 #pragma unroll
-          for (int r = 0; r < NQ; ++r) any |= rem_q[r] == x;
-          const bool seen = __ballot(any) != 0ull;
-          const double px =
-              seen ? 0.0 : (double)__int_as_float(__builtin_amdgcn_readlane(__float_as_int(pc_q[q]), c));
-          const double uc = (double)__int_as_float(__builtin_amdgcn_readlane(__float_as_int(u_q[q]), c));
-          if (uc * (Z - R) < px) {
-            next = 64 * q + c;
-            break;
+        for (int q = 0; q < NQ; ++q) {
+          if ((km[q] >> lane) & 1ull) {
+            const int j = before + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(km[q] >> 32),
+                                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)km[q], 0u));
+            s_cx[j] = tok_q[q];
+            s_cp[j] = pc_q[q];
+            s_cu[j] = u_q[q];
+            s_cid[j] = 64 * q + lane;
           }
-          if (!seen) {
-            R += px;
+          before += __popcll(km[q]);
+        }
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        const bool live = lane < m;
+        const int xj = live ? s_cx[lane] : 0;
+        const float pj = live ? s_cp[lane] : 0.0f, uj = live ? s_cu[lane] : 0.0f;
+        const int idj = live ? s_cid[lane] : -1;
+        bool dup = false;
+        for (int i = 0; i < m; ++i) dup |= i < lane && __builtin_amdgcn_readlane(xj, i) == xj;
+        const double pe = (live && !dup) ? (double)pj : 0.0;
+        double R = 0.0, Rj = 0.0;
+        for (int i = 0; i < m; ++i) {
+          Rj = lane == i ? R : Rj;
+          const long long pb = __double_as_longlong(pe);
+          const int lo = __builtin_amdgcn_readlane((int)(pb & 0xFFFFFFFF), i);
+          const int hi = __builtin_amdgcn_readlane((int)(pb >> 32), i);
+          R += __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+        }
+        const unsigned long long am = __ballot(live && (double)uj * (Z - Rj) < pe);
+        int next = -1, nr = 0;
+        if (am) {
+          next = __builtin_amdgcn_readlane(idj, __ffsll((long long)am) - 1);
+        } else {  // every child rejected: their distinct tokens
+          const unsigned long long kk = __ballot(live && !dup);
+          if (live && !dup)
+            s_rem[(int)__builtin_amdgcn_mbcnt_hi((uint32_t)(kk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)kk, 0u))] = xj;
+          nr = __popcll(kk);
+        }
+        if (lane == 0) {
+          s_next = next;
+          s_nrem = nr;
+        }
+      } else {
+        // children in ascending id (the current node and every decision are
+        // wave-uniform); rejected token r sits in lane r % 64, slot r / 64
+        double R = 0.0;
+        int next = -1, nr = 0, rem_q[NQ];
 #pragma unroll
-            for (int r = 0; r < NQ; ++r)
-              if (lane == (nr & 63) && (nr >> 6) == r) rem_q[r] = x;
-            ++nr;
+        for (int q = 0; q < NQ; ++q) rem_q[q] = -1;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+          unsigned long long kids = next < 0 ? __ballot(par_q[q] == node) : 0ull;
+          while (kids) {
+            const int c = __ffsll((long long)kids) - 1;
+            kids &= kids - 1;
+            const int x = __builtin_amdgcn_readlane(tok_q[q], c);
+            bool any = false;
+#pragma unroll
+            for (int r = 0; r < NQ; ++r) any |= rem_q[r] == x;
+            const bool seen = __ballot(any) != 0ull;
+            const double px =
+                seen ? 0.0 : (double)__int_as_float(__builtin_amdgcn_readlane(__float_as_int(pc_q[q]), c));
+            const double uc = (double)__int_as_float(__builtin_amdgcn_readlane(__float_as_int(u_q[q]), c));
+            if (uc * (Z - R) < px) {
+              next = 64 * q + c;
+              break;
+            }
+            if (!seen) {
+              R += px;
+#pragma unroll
+              for (int r = 0; r < NQ; ++r)
+                if (lane == (nr & 63) && (nr >> 6) == r) rem_q[r] = x;
+              ++nr;
+            }
           }
         }
-      }
 #pragma unroll
-      for (int r = 0; r < NQ; ++r)
-        if (lane + 64 * r < nr) s_rem[lane + 64 * r] = rem_q[r];
-      if (lane == 0) {
-        s_next = next;
-        s_nrem = nr;
+        for (int r = 0; r < NQ; ++r)
+          if (lane + 64 * r < nr) s_rem[lane + 64 * r] = rem_q[r];
+        if (lane == 0) {
+          s_next = next;
+          s_nrem = nr;
+        }
       }
     }
     __syncthreads();
