@@ -242,12 +242,18 @@ __global__ __launch_bounds__(kTopkThreads) void k_row_topk(const float* __restri
 #pragma unroll
       for (int i = 0; i < kTopkVec; ++i)  // clamped addresses: every load is in bounds and issued at once
         x[i] = __builtin_nontemporal_load(r4 + min(t0 / 4 + i * kTopkThreads + tid, last4));
+      // (end is a multiple of 4 here, so a vector is inside the range or past it as a whole)
 #pragma unroll
-      for (int j = 0; j < kTopkVec * 4; ++j) {
-        const bool in = idx_of(j) < end;
-        const float v = x[j >> 2][j & 3];
-        bad |= in && (LOGITS ? !isfinite(v) : !(v <= 0.0f));  // log-probs: NaN or positive
-        k[j] = in ? order_key(v) : 0u;
+      for (int i = 0; i < kTopkVec; ++i) {
+        const bool in = t0 / 4 + i * kTopkThreads + tid <= last4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float v = x[i][e];
+          bad |= in && (LOGITS ? !isfinite(v) : !(v <= 0.0f));  // log-probs: NaN or positive
+          // order_key(v): -0.0 + 0.0 = +0.0, then the sign-dependent flip
+          const uint32_t u = __float_as_uint(v + 0.0f);
+          k[4 * i + e] = in ? u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u) : 0u;
+        }
       }
       if constexpr (LOGITS) {
         float xs[kTopkVec * 4];
