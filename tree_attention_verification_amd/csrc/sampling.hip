@@ -656,6 +656,7 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
   } else {
     row_pass<NT>(V, ld_l, [&](int v, float x) { see(logit_key(x), v); });
   }
+  const unsigned long long best_own = best;  // this thread's first-ranked token (0: none)
   best = block_max_u64<NT>(best, s_u);
   kmin = ~(uint32_t)block_max_u64<NT>((unsigned long long)(~kmin), s_u);
   const uint32_t kmax = (uint32_t)(best >> 32);
@@ -907,20 +908,28 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
   // exact inclusive cumulative weight reaches thr (n if none), with that
   // cumulative in `kept`; a lane scan, then the totals of the earlier wavefronts.
   // own_total: thr = ceil(top_p x the list's total) instead (above = 0).
+  // Only the wavefronts up to the one holding entry n take part in the sums.
   auto list_cut = [&](int n, const Norm& above, const Norm& thr, bool own_total, Norm& kept) -> int {
-    Wide incl = tid < n ? wide_of(weight((uint32_t)(s_top[tid] >> 32))) : wzero();
-    for (int o = 1; o < 64; o <<= 1) {
+    const bool act = wave * 64 <= n;  // (wave-uniform)
+    Wide incl = wzero();
+    if (act) {
+      if (tid < n) incl = wide_of(weight((uint32_t)(s_top[tid] >> 32)));
+      for (int o = 1; o < 64; o <<= 1) {
 #pragma unroll
-      for (int i2 = 0; i2 < NL; ++i2) {
-        const unsigned long long y = __shfl_up(incl.l[i2], o, 64);
-        if (lane >= o) incl.l[i2] += y;
+        for (int i2 = 0; i2 < NL; ++i2) {
+          const unsigned long long y = __shfl_up(incl.l[i2], o, 64);
+          if (lane >= o) incl.l[i2] += y;
+        }
       }
+      if (lane == 63) s_w[wave] = incl;
     }
-    if (lane == 63) s_w[wave] = incl;
     if (tid == 0) s_pick = n;
     __syncthreads();
-    for (int w = 0; w < wave; ++w) wadd(incl, s_w[w]);
-    const Norm c = nadd(norm_of(incl), above);
+    Norm c = nzero();
+    if (act) {
+      for (int w = 0; w < wave; ++w) wadd(incl, s_w[w]);
+      c = nadd(norm_of(incl), above);
+    }
     Norm th = thr;
     if (own_total) {
       if (tid == n - 1) s_thr = nthreshold(tp, c);
@@ -951,8 +960,7 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
   // With more candidates than the list holds, the general path below runs instead.
   bool sorted = false;
   if (kk > 1 && kk <= kFastK && kk < V) {
-    unsigned long long tm = 0ull;  // this thread's best token as a rank key
-    pass_k([&](int v, KW e) { tm = umax64(tm, tok_key(e.k, v)); });
+    const unsigned long long tm = best_own;  // this thread's best token as a rank key (the first pass's)
     // a thread without tokens has tm = 0: key 0, below every token's key, code 0
     const uint32_t mc = tm ? vcode((uint32_t)(tm >> 32)) : 0u;
     int above_t = 0;
@@ -1234,10 +1242,16 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
     const bool keep = tid < n_list && (!(mp > 0.0f) || w_t >= mp || tid == 0);
     const int n_keep = __syncthreads_count(keep);
     const double W = norm_to_double(norm_of(block_wsum(keep ? wide_of(w_t) : wzero())));
-    const unsigned long long last = s_top[n_keep - 1];
-    pass_k([&](int v, KW e) {
-      if (tok_key(e.k, v) < last) orow[v] = 0.0f;
-    });
+    // every token 0 (16-byte stores where the row allows), then the kept ones:
+    // the barrier orders the two stores of a kept token (one workgroup)
+    if (!(reinterpret_cast<uintptr_t>(orow) & 15)) {
+      const float4 z = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      for (int v4 = tid; v4 < (V >> 2); v4 += NT) reinterpret_cast<float4*>(orow)[v4] = z;
+      for (int v = (V & ~3) + tid; v < V; v += NT) orow[v] = 0.0f;
+    } else {
+      for (int v = tid; v < V; v += NT) orow[v] = 0.0f;
+    }
+    __syncthreads();
     if (keep) orow[key_index(s_top[tid])] = (float)((double)w_t * (1.0 / W));
     return;
   }
