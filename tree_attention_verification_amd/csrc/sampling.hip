@@ -1053,9 +1053,13 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
   // that weight first reaches thr is chosen (-1: never), with its count in
   // s_cnt.  `above` gains the weight of the higher bins; level 0 sets thr from
   // the total.
+  // The sums run on the first WT threads (the same exact integers whichever
+  // threads add them; fewer wavefronts issue fewer of the wide additions).
+  constexpr int WT = NT < 256 ? NT : 256, WW = WT / 64;
   auto w_select = [&](int lev, uint32_t prefix) __attribute__((always_inline)) -> int {
     const int nb = lev_bins(lev);
-    const int bpt = (nb + NT - 1) / NT;  // 1, or 4 with 256 threads and 1024 bins
+    const int bpt = (nb + WT - 1) / WT;  // 4 at level 0 (1024 bins), else 1
+    const bool part = tid < WT;          // (wave-uniform)
     const int e_fix = lev == 1 ? (int)(prefix >> 3) : lev == 2 ? (int)(prefix >> 11) : (int)(prefix >> 19);
     auto bin_at = [&](int bin) {  // the bin's weight as a Wide (0 past the bins)
       const unsigned long long word = bin < nb ? s_hist[bin] : 0ull;
@@ -1066,34 +1070,41 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
     __syncthreads();
     // carry-save sums: a bin's limbs are below 2^46, so 1024 of them fit a limb
     Wide suf = wzero();  // this thread's bins and those of the higher lanes of its wavefront
+    Wide run = wzero();
+    if (part) {
 #pragma unroll 1
-    for (int j = 0; j < bpt; ++j) wadd(suf, bin_at(tid * bpt + j));
-    for (int o = 1; o < 64; o <<= 1) {
-      const Wide y = wshfl_down(suf, o);
-      if (lane + o < 64) wadd(suf, y);
+      for (int j = 0; j < bpt; ++j) wadd(suf, bin_at(tid * bpt + j));
+      for (int o = 1; o < 64; o <<= 1) {
+        const Wide y = wshfl_down(suf, o);
+        if (lane + o < 64) wadd(suf, y);
+      }
+      if (lane == 0) s_w[wave] = suf;
+      run = wshfl_down(suf, 1);  // the higher lanes' bins
+      if (lane == 63) run = wzero();
     }
-    if (lane == 0) s_w[wave] = suf;
-    Wide run = wshfl_down(suf, 1);  // the higher lanes' bins
-    if (lane == 63) run = wzero();
     __syncthreads();
-    for (int w = wave + 1; w < NW; ++w) wadd(run, s_w[w]);  // the higher wavefronts' bins
+    if (part) {
+      for (int w = wave + 1; w < WW; ++w) wadd(run, s_w[w]);  // the higher wavefronts' bins
+    }
     if (lev == 0 && tid == 0) {  // thr from the total
       Wide z = wzero();
-      for (int w = 0; w < NW; ++w) wadd(z, s_w[w]);
+      for (int w = 0; w < WW; ++w) wadd(z, s_w[w]);
       s_thr = nthreshold(tp, norm_of(z));
     }
     if (lev == 0) __syncthreads();
     const Norm th = lev == 0 ? nuniform(s_thr) : thr;
+    if (part) {
 #pragma unroll 1
-    for (int j = bpt - 1; j >= 0; --j) {
-      const int bin = tid * bpt + j;
-      const Norm r0 = nadd(norm_of(run), above);
-      wadd(run, bin_at(bin));
-      const Norm r2 = nadd(norm_of(run), above);
-      if (bin < nb && !nge(r0, th) && nge(r2, th)) {  // the one bin where the cumulative crosses thr
-        s_sel = bin;
-        s_abv = r0;
-        s_cnt = (int)(s_hist[bin] >> 44);
+      for (int j = bpt - 1; j >= 0; --j) {
+        const int bin = tid * bpt + j;
+        const Norm r0 = nadd(norm_of(run), above);
+        wadd(run, bin_at(bin));
+        const Norm r2 = nadd(norm_of(run), above);
+        if (bin < nb && !nge(r0, th) && nge(r2, th)) {  // the one bin where the cumulative crosses thr
+          s_sel = bin;
+          s_abv = r0;
+          s_cnt = (int)(s_hist[bin] >> 44);
+        }
       }
     }
     __syncthreads();
