@@ -1502,9 +1502,9 @@ __global__ __launch_bounds__(NT) void k_tree_accept_sample_draft_sliced(
   extern __shared__ double s_R[];                            // L residual values
   float* s_Q = reinterpret_cast<float*>(s_R + L);           // L draft values
   uint32_t* s_rm = reinterpret_cast<uint32_t*>(s_Q + L);    // (L + 31) / 32 words: removed tokens
-  __shared__ int s_tok[kTMaxLimit], s_par[kTMaxLimit], s_path[kTMaxLimit], s_hx[kTMaxLimit];
+  __shared__ int s_tok[kTMaxLimit], s_par[kTMaxLimit], s_path[kTMaxLimit], s_gc[kTMaxLimit];
   __shared__ float s_uni[kTMaxLimit], s_px[kTMaxLimit], s_qx[kTMaxLimit];
-  __shared__ double s_hq[kTMaxLimit], s_hr[kTMaxLimit];      // ZQ, ZR of each update at this node
+  __shared__ double s_rc[kTMaxLimit];  // R(x) of each pending child of the current node (s_gc: x removed)
   __shared__ double s_d[NW * 16];
   __shared__ unsigned long long s_u[NW], s_all[kSliceMax][4], s_r4[4 * NW];
   __shared__ int s_dec, s_fail, s_pick;
@@ -1593,31 +1593,25 @@ __global__ __launch_bounds__(NT) void k_tree_accept_sample_draft_sliced(
     entered = node;
     if (s_fail) break;
     double ZR = dsum(0), ZQ = dsum(1);
-    int next = -1, nrej = 0;
+    int next = -1;
+    // R(x) of every child: p(x) until an update (thread c holds child c)
+    if (tid < T) {
+      const int xc = s_tok[tid];
+      s_rc[tid] = (s_par[tid] == node && xc >= 0 && xc < V) ? (double)s_px[tid] : 0.0;
+      s_gc[tid] = 0;
+    }
+    __syncthreads();
     for (int c = 1; c < T; ++c) {
       if (s_par[c] != node) continue;
       const int x = s_tok[c];
       const bool inside = x >= 0 && x < V;
       bool acc;
       {
-        // R(x) and Q(x) now: p(x), q(x) through this node's updates so far (every
-        // thread alike: the same values, so no barrier)
-        double r = 0.0, s = 0.0;
-        if (inside) {
-          const double qx = (double)s_qx[c];
-          bool gone = false;
-          r = (double)s_px[c];
-          for (int j = 0; j < nrej; ++j) {
-            if (s_hq[j] > 0.0) {
-              const double qv = gone ? 0.0 : qx;
-              const double a = r * s_hq[j];
-              const double bq = qv * s_hr[j];
-              r = fmax(0.0, a - bq);
-            }
-            if (s_hx[j] == x) gone = true;
-          }
-          s = gone ? 0.0 : qx;
-        }
+        // R(x) and Q(x) now: p(x), q(x) through this node's updates so far, kept
+        // up to date by thread c (the same operations as the slice pass that
+        // holds x)
+        const double r = s_rc[c];
+        const double s = (inside && !s_gc[c]) ? (double)s_qx[c] : 0.0;
         const double lhs = ((double)s_uni[c] * s) * ZR;
         const double rhs = r * ZQ;
         acc = r > 0.0 && (s == 0.0 || lhs < rhs);
@@ -1627,25 +1621,51 @@ __global__ __launch_bounds__(NT) void k_tree_accept_sample_draft_sliced(
         break;
       }
       const bool rm = without_replacement && inside;
-      // this rejection's update, for the later replays: every thread writes the
-      // same values (and reads back its own write, with or without a barrier)
-      s_hx[nrej] = rm ? x : -1;
-      s_hq[nrej] = ZQ;
-      s_hr[nrej] = ZR;
-      ++nrej;
+      // the later children's R(x): this rejection's update, then x removed from Q
+      // (the barriers of the exchange below order it before their tests)
+      if (tid > c && tid < T && s_par[tid] == node) {
+        const int xc = s_tok[tid];
+        if (xc >= 0 && xc < V) {
+          if (ZQ > 0.0) {
+            const double qv = s_gc[tid] ? 0.0 : (double)s_qx[tid];
+            const double a = s_rc[tid] * ZQ;
+            const double bq = qv * ZR;
+            s_rc[tid] = fmax(0.0, a - bq);
+          }
+          if (rm && xc == x) s_gc[tid] = 1;
+        }
+      }
+      if (!(ZQ > 0.0)) __syncthreads();  // (no exchange below to order the update)
       if (ZQ > 0.0) {
         // R <- max(0, R ZQ - Q ZR) on the slice; without replacement Q loses x
         double a = 0.0, c2 = 0.0;
         int lastp = 0;
-        for (int t = tid; t < n; t += NT) {
-          const double qv = removed(t) ? 0.0 : (double)s_Q[t];
-          const double ra = s_R[t] * ZQ;
-          const double rb = qv * ZR;
-          const double nr = fmax(0.0, ra - rb);
-          s_R[t] = nr;
-          a += nr;
-          c2 += (rm && v0 + t == x) ? 0.0 : qv;
-          if (nr > 0.0) lastp = v0 + t + 1;
+        // (eight entries' reads in flight together; entries in increasing t)
+        for (int t0 = tid; t0 < n; t0 += 8 * NT) {
+          double rv[8];
+          float qq[8];
+          uint32_t rw[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int t = min(t0 + u * NT, n - 1);
+            rv[u] = s_R[t];
+            qq[u] = s_Q[t];
+            rw[u] = s_rm[t >> 5];
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int t = t0 + u * NT;
+            if (t < n) {
+              const double qv = ((rw[u] >> (t & 31)) & 1u) ? 0.0 : (double)qq[u];
+              const double ra = rv[u] * ZQ;
+              const double rb = qv * ZR;
+              const double nr = fmax(0.0, ra - rb);
+              s_R[t] = nr;
+              a += nr;
+              c2 += (rm && v0 + t == x) ? 0.0 : qv;
+              if (nr > 0.0) lastp = v0 + t + 1;
+            }
+          }
         }
         unsigned long long lp = (unsigned long long)lastp, unused = 0ull;
         block_sum2_max2<NT>(a, c2, lp, unused, s_r4);
