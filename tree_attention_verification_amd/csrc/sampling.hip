@@ -1497,7 +1497,7 @@ __global__ __launch_bounds__(NT) void k_tree_accept_sample_draft_sliced(
     double* __restrict__ ws) {
 #pragma clang fp contract(off)
   constexpr int NW = NT / 64;
-  const int sl = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int sl = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int v0 = sl * L, n = max(0, min(V, v0 + L) - v0);  // this slice: tokens v0 .. v0 + n - 1
   extern __shared__ double s_R[];                            // L residual values
   float* s_Q = reinterpret_cast<float*>(s_R + L);           // L draft values
@@ -1505,6 +1505,7 @@ __global__ __launch_bounds__(NT) void k_tree_accept_sample_draft_sliced(
   __shared__ int s_tok[kTMaxLimit], s_par[kTMaxLimit], s_path[kTMaxLimit], s_gc[kTMaxLimit];
   __shared__ float s_uni[kTMaxLimit], s_px[kTMaxLimit], s_qx[kTMaxLimit];
   __shared__ double s_rc[kTMaxLimit];  // R(x) of each pending child of the current node (s_gc: x removed)
+  __shared__ unsigned long long s_km[kTMaxLimit / 64];  // the entered node's children
   __shared__ double s_d[NW * 16];
   __shared__ unsigned long long s_u[NW], s_all[kSliceMax][4], s_r4[4 * NW];
   __shared__ int s_dec, s_fail, s_pick;
@@ -1578,6 +1579,10 @@ __global__ __launch_bounds__(NT) void k_tree_accept_sample_draft_sliced(
       s_px[c2] = in ? p[x] : 0.0f;
       s_qx[c2] = in ? q[x] : 0.0f;
     }
+    {  // the node's children as a bit mask (node c: bit c % 64 of word c / 64)
+      const unsigned long long km = __ballot(tid > 0 && tid < T && s_par[tid] == nd);
+      if (lane == 0 && wave < kTMaxLimit / 64) s_km[wave] = km;
+    }
     unsigned long long lp = (unsigned long long)lastp;
     block_sum2_max2<NT>(a, c, lp, bst, s_r4);
     exchange(as_u(a), as_u(c), lp, bst);
@@ -1601,8 +1606,14 @@ __global__ __launch_bounds__(NT) void k_tree_accept_sample_draft_sliced(
       s_gc[tid] = 0;
     }
     __syncthreads();
-    for (int c = 1; c < T; ++c) {
-      if (s_par[c] != node) continue;
+    // the children in ascending id, from the mask
+    int kq = 0;
+    unsigned long long kmask = s_km[0];
+    for (;;) {
+      while (kmask == 0ull && kq + 1 < kTMaxLimit / 64 && (kq + 1) * 64 < T) kmask = s_km[++kq];
+      if (kmask == 0ull) break;
+      const int c = 64 * kq + __ffsll((long long)kmask) - 1;
+      kmask &= kmask - 1ull;
       const int x = s_tok[c];
       const bool inside = x >= 0 && x < V;
       bool acc;
