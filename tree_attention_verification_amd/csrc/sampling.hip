@@ -176,6 +176,11 @@ __device__ __forceinline__ unsigned long long block_max_u64(unsigned long long v
   return t;
 }
 
+// s_waitcnt immediate (gfx9 encoding) that waits for every vector memory
+// operation of the wavefront, stores included, and for nothing else: vmcnt 0
+// (bits 3:0 and 15:14), expcnt 7 (bits 6:4), lgkmcnt 15 (bits 11:8)
+constexpr int kVmemStoresDone = (7 << 4) | (15 << 8);
+
 // ---- exact sums of float32 weights.  Every float32 w in [0, 1] is an integer
 // number of units of 2^-149: w = m 2^s units with an integer m < 2^24 and
 // 0 <= s <= 126.  A sum of weights is held as NL limbs of 32-bit digits (limb j
@@ -1253,8 +1258,10 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
     const bool keep = tid < n_list && (!(mp > 0.0f) || w_t >= mp || tid == 0);
     const int n_keep = __syncthreads_count(keep);
     const double W = norm_to_double(norm_of(block_wsum(keep ? wide_of(w_t) : wzero())));
-    // every token 0 (16-byte stores where the row allows), then the kept ones:
-    // the barrier orders the two stores of a kept token (one workgroup)
+    // every token 0 (16-byte stores where the row allows), then the kept ones.
+    // The two stores of a kept token come from different wavefronts: each thread
+    // waits until its zero stores are done (in this CU's L2) before the barrier,
+    // which a workgroup barrier alone does not do for global memory.
     if (!(reinterpret_cast<uintptr_t>(orow) & 15)) {
       const float4 z = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
       for (int v4 = tid; v4 < (V >> 2); v4 += NT) reinterpret_cast<float4*>(orow)[v4] = z;
@@ -1262,6 +1269,7 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
     } else {
       for (int v = tid; v < V; v += NT) orow[v] = 0.0f;
     }
+    __builtin_amdgcn_s_waitcnt(kVmemStoresDone);
     __syncthreads();
     if (keep) orow[key_index(s_top[tid])] = (float)((double)w_t * (1.0 / W));
     return;
