@@ -1389,6 +1389,9 @@ __global__ __launch_bounds__(kThreads) void k_tree_accept_sample_draft(
           zr += nr;
           zq2 += (rm && v == x) ? 0.0 : qv;
         });
+        // other threads read R next (the tests, the correction's ranges): every
+        // store is done before the barrier below
+        __builtin_amdgcn_s_waitcnt(kVmemStoresDone);
         ZR = block_sum_d(zr, s_d);
         r_ws = true;
         if (rm) {
