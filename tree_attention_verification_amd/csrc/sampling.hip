@@ -1034,6 +1034,18 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
   auto in_k = [&](uint32_t k, int v) { return k > tk || (k == tk && v <= ck); };
   // the survivors are s_top[0..kk) (a small top-k) or are described by the cut
   const bool as_list = sorted || listed;
+  if (as_list) {
+    // The output row of a list is 0 but for the kept entries: every token 0 now
+    // (16-byte stores where the row allows), so that the stores drain while the
+    // cut and the kept total are worked out; the kept entries follow at the end.
+    if (!(reinterpret_cast<uintptr_t>(orow) & 15)) {
+      const float4 z = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      for (int v4 = tid; v4 < (V >> 2); v4 += NT) reinterpret_cast<float4*>(orow)[v4] = z;
+      for (int v = (V & ~3) + tid; v < V; v += NT) orow[v] = 0.0f;
+    } else {
+      for (int v = tid; v < V; v += NT) orow[v] = 0.0f;
+    }
+  }
 
   // ---- top-p radix, by the float32 bits u of the survivors' weights (w grows
   // with the key, so the bits order the tokens as the keys do, up to equal
@@ -1252,23 +1264,14 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
   // ---- min-p, the kept total and the output.  The kept tokens are a rank prefix.
   if (as_list) {
     // s_top[0..n_list) ranked; min-p keeps the entries with w >= min_p (a prefix,
-    // the first entry always): their exact total is W, the last kept rank key
-    // bounds the zero-filled tokens, and each kept entry is written by its thread
+    // the first entry always): their exact total is W, and each kept entry is
+    // written by its thread over the zero the row already holds.  The two stores
+    // of a kept token come from different wavefronts: each thread waits until its
+    // zero stores are done (in this CU's L2) before the barrier, which a
+    // workgroup barrier alone does not do for global memory.
     const float w_t = tid < n_list ? weight((uint32_t)(s_top[tid] >> 32)) : 0.0f;
     const bool keep = tid < n_list && (!(mp > 0.0f) || w_t >= mp || tid == 0);
-    const int n_keep = __syncthreads_count(keep);
     const double W = norm_to_double(norm_of(block_wsum(keep ? wide_of(w_t) : wzero())));
-    // every token 0 (16-byte stores where the row allows), then the kept ones.
-    // The two stores of a kept token come from different wavefronts: each thread
-    // waits until its zero stores are done (in this CU's L2) before the barrier,
-    // which a workgroup barrier alone does not do for global memory.
-    if (!(reinterpret_cast<uintptr_t>(orow) & 15)) {
-      const float4 z = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-      for (int v4 = tid; v4 < (V >> 2); v4 += NT) reinterpret_cast<float4*>(orow)[v4] = z;
-      for (int v = (V & ~3) + tid; v < V; v += NT) orow[v] = 0.0f;
-    } else {
-      for (int v = tid; v < V; v += NT) orow[v] = 0.0f;
-    }
     __builtin_amdgcn_s_waitcnt(kVmemStoresDone);
     __syncthreads();
     if (keep) orow[key_index(s_top[tid])] = (float)((double)w_t * (1.0 / W));
