@@ -164,18 +164,48 @@ constexpr int kSampleThreads = 1024;
 constexpr int kPiece = 8 * kSampleThreads;  // row entries read per pass step (8 per thread)
 constexpr int kMaxPieces = 32;              // V <= 262144
 
-__device__ __forceinline__ double wave_sum_f64(double v) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+// A float64 moved between lanes by one DPP control (both halves alike); lanes
+// with no source (bound_ctrl) or outside row_mask read 0.
+template <int CTRL, int ROWS, bool BOUND>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(b & 0xFFFFFFFF), CTRL, ROWS, 0xF, BOUND);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), CTRL, ROWS, 0xF, BOUND);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
+// inclusive prefix sum over the 16 lanes of each row (row_shr 1, 2, 4, 8)
+__device__ __forceinline__ double row_incl_f64(double v) {
+  v += dpp_f64<0x111, 0xF, true>(v);
+  v += dpp_f64<0x112, 0xF, true>(v);
+  v += dpp_f64<0x114, 0xF, true>(v);
+  v += dpp_f64<0x118, 0xF, true>(v);
   return v;
 }
 
-// inclusive prefix sum over the wavefront
-__device__ __forceinline__ double wave_incl_f64(double v, int lane) {
-  for (int o = 1; o < 64; o <<= 1) {
-    const double y = __shfl_up(v, o, 64);
-    if (lane >= o) v += y;
-  }
+// inclusive prefix sum over the wavefront: within the rows, then row 0's total
+// into row 1 and row 2's into row 3 (row_bcast:15), rows 0-1's into rows 2-3
+// (row_bcast:31); no LDS round trip
+__device__ __forceinline__ double wave_incl_f64(double v) {
+  v = row_incl_f64(v);
+  v += dpp_f64<0x142, 0xA, false>(v);
+  v += dpp_f64<0x143, 0xC, false>(v);
   return v;
+}
+
+// the wavefront's sum (every lane gets it)
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  const long long b = __double_as_longlong(wave_incl_f64(v));
+  const int lo = __builtin_amdgcn_readlane((int)(b & 0xFFFFFFFF), 63);
+  const int hi = __builtin_amdgcn_readlane((int)(b >> 32), 63);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane((int)(b & 0xFFFFFFFF), l);
+  const int hi = __builtin_amdgcn_readlane((int)(b >> 32), l);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
 }
 
 constexpr int kSampleWaves = kSampleThreads / 64;
@@ -480,17 +510,19 @@ __global__ __launch_bounds__(kSampleThreads) void k_tree_accept_sample(
   const double target = (double)__int_as_float(__builtin_amdgcn_readlane(__float_as_int(u_q[0]), 0)) * total;
   __shared__ double s_last[4][NWV];
   if (total > 0.0) {
-    // pass 2, four pieces at a time: a block inclusive scan of the runs' masses;
-    // run (k, t) spans [I(k, t-1), I(k, t)) of the cumulative mass, each boundary
-    // one stored number shared by both neighbours, so at most one run holds the
-    // target.  The four pieces' wavefront scans share one barrier; the carry into
-    // piece k + 1 is the last thread's upper bound of piece k, which every thread
-    // forms itself with the same additions.
+    // pass 2, four pieces at a time: a block inclusive scan of the runs' masses
+    // (within a wavefront by DPP); run (k, t) spans [lo, hi) of the cumulative
+    // mass, each boundary one computed number that both neighbours take, so the
+    // runs tile the total.  Wavefront w starts at carry + t_0 + ... + t_(w-1)
+    // added in this order (t: the wavefronts' totals), which every wavefront
+    // forms alike, and its last lane ends where wavefront w + 1 starts.  A run of
+    // no width takes no target; should rounding still leave two runs holding it,
+    // the larger token is taken.
     double carry = 0.0;
     auto scan_group = [&](int k0, float (&x)[4][8]) __attribute__((always_inline)) {
       double incl[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) incl[u] = k0 + u < n_pieces ? wave_incl_f64(run_mass(k0 + u, x[u]), lane) : 0.0;
+      for (int u = 0; u < 4; ++u) incl[u] = k0 + u < n_pieces ? wave_incl_f64(run_mass(k0 + u, x[u])) : 0.0;
       if (lane == 63) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) s_last[u][wave] = incl[u];
@@ -499,12 +531,20 @@ __global__ __launch_bounds__(kSampleThreads) void k_tree_accept_sample(
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         if (k0 + u >= n_pieces) break;
-        double off = carry;
-        for (int w = 0; w < wave; ++w) off += s_last[u][w];
-        const double hi = off + incl[u];
+        const double tv = lane < NWV ? s_last[u][lane] : 0.0;
+        double o = carry, off = carry, nxt = carry;
+        for (int w = 0; w < NWV; ++w) {
+          const double tw = readlane_f64(tv, w);
+          if (w == wave) {
+            off = o;
+            nxt = o + tw;
+          }
+          o = o + tw;
+        }
+        const double hi = lane == 63 ? nxt : off + incl[u];
         const double up = __shfl_up(hi, 1, 64);
         const double lo = lane > 0 ? up : off;
-        if (lo <= target && target < hi) {
+        if (lo < hi && lo <= target && target < hi) {
           // this run holds the target: walk it; if rounding keeps the sum below
           // the target, its last entry with mass
           const int v0 = (k0 + u) * kPiece + 8 * tid;
@@ -520,11 +560,9 @@ __global__ __launch_bounds__(kSampleThreads) void k_tree_accept_sample(
               break;
             }
           }
-          s_pick = pick >= 0 ? pick : last;
+          atomicMax(&s_pick, pick >= 0 ? pick : last);
         }
-        double c = carry;
-        for (int w = 0; w < NWV - 1; ++w) c += s_last[u][w];
-        carry = c + s_last[u][NWV - 1];
+        carry = o;
       }
       __syncthreads();  // (s_last is rewritten by the next group)
     };
