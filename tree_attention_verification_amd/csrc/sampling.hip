@@ -1430,7 +1430,9 @@ __global__ __launch_bounds__(kThreads) void k_tree_accept_sample_draft(
   __syncthreads();
   if (total > 0.0) {
     const double target = (double)s_uni[0] * total;
-    if (lo <= target && target < hi) {
+    // (a range of no width takes no target; should rounding leave two ranges
+    // holding it, the larger token is taken)
+    if (lo < hi && lo <= target && target < hi) {
       double cum = lo;
       int pick = -1, last = -1;
       range_pass(c0, c1, X, [&](int v, double x) {
@@ -1442,7 +1444,7 @@ __global__ __launch_bounds__(kThreads) void k_tree_accept_sample_draft(
         }
         return false;
       });
-      s_pick = pick >= 0 ? pick : last;
+      atomicMax(&s_pick, pick >= 0 ? pick : last);
     }
     __syncthreads();
     if (s_pick < 0) {  // rounding left the target past the total: the last token with mass
@@ -1745,7 +1747,9 @@ __global__ __launch_bounds__(NT) void k_tree_accept_sample_draft_sliced(
       if (found && writer == sl) {
         // inside this slice: cumulative = (the earlier slices) + the in-slice prefix
         const double tl = target - pre;
-        if (lo <= tl && tl < hi) {
+        // (a range of no width takes no target; should rounding leave two
+        // ranges holding it, the larger token is taken)
+        if (lo < hi && lo <= tl && tl < hi) {
           double cum = pre + lo;
           int pick = -1;
           for (int t = c0; t < c1; ++t) {
@@ -1755,7 +1759,7 @@ __global__ __launch_bounds__(NT) void k_tree_accept_sample_draft_sliced(
               break;
             }
           }
-          if (pick >= 0) s_pick = pick;
+          if (pick >= 0) atomicMax(&s_pick, pick);
         }
       }
     } else {
