@@ -691,9 +691,10 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
     if (t >= -125.0) {
       const double kf = rint(t * 64.0);
       const int ki = (int)kf;
-      const double f = t - kf * 0.015625;
-      const double p = 1.0 + f * (0.6931471805599453 +
-                                  f * (0.24022650695910072 + f * (0.05550410866482158 + f * 0.009618129107628477)));
+      const double f = fma(kf, -0.015625, t);  // (exact)
+      // (fused: a result within the error bound is all the check below needs)
+      const double p = fma(f, fma(f, fma(f, fma(f, 0.009618129107628477, 0.05550410866482158), 0.24022650695910072),
+                                  0.6931471805599453), 1.0);
       const double y = ldexp(s_exp2[ki & 63] * p, ki >> 6);
       const uint32_t lo = (uint32_t)__double_as_longlong(y) & 0x1FFFFFFFu;  // the bits float32 rounds away
       if (lo - 0x0FFF0000u > 0x20000u) return (float)y;
