@@ -30,35 +30,35 @@ def run(w, **kw):
 
 
 # ----------------------------------------------------------------------------- configurations
-def test_cfg1_tiny_static_fp32():
+def test_tiny_static_fp32_p128():
     r = run(gen.make_workload(1))
     assert list(r["tree_size"]) == [11]
 
 
-def test_cfg2_eagle2_dynamic_full():
+def test_eagle2_dynamic_b1_p2048_full():
     r = run(gen.make_workload(2))
     assert list(r["tree_size"]) == [61]
 
 
-def test_cfg3_ragged_batch16_full():
+def test_ragged_b16_p512_8192_full():
     r = run(gen.make_workload(3))
     assert (r["tree_size"] == 49).all()
 
 
-def test_cfg4_long_context_reduced_prefix():
+def test_long_context_b4_reduced_prefix():
     run(gen.make_workload(4, batch=2, prefix=3000))
 
 
-def test_cfg5_random_trees_reduced():
+def test_random_trees_b64_reduced():
     run(gen.make_workload(5, batch=12, prefix=777))
 
 
-def test_cfg4_full_size():
+def test_long_context_b4_p32768_full_size():
     # every written row (4 requests x 61 nodes x 64 heads over 32829 keys, 8 splits)
     run(gen.make_workload(4))
 
 
-def test_cfg5_full_size():
+def test_random_trees_b64_p4096_full_size():
     # every written row of 64 requests with trees of 8..64 nodes over 4096-token prefixes
     run(gen.make_workload(5))
 
@@ -273,10 +273,10 @@ def test_kv_compact_several_layers_with_padded_layer_stride():
 # ----------------------------------------------------------------------------- fused entry points
 def _fused_cases():
     return {
-        "cfg1-static-fp32": lambda: gen.make_workload(1),
-        "cfg2": lambda: gen.make_workload(2),
-        "cfg3-ragged": lambda: gen.make_workload(3),
-        "cfg5-reduced": lambda: gen.make_workload(5, batch=12, prefix=777),
+        "tiny-static-fp32": lambda: gen.make_workload(1),
+        "eagle2-b1-p2048": lambda: gen.make_workload(2),
+        "ragged-b16": lambda: gen.make_workload(3),
+        "random-trees-reduced": lambda: gen.make_workload(5, batch=12, prefix=777),
         "dynamic-K16": lambda: gen.make_custom(cfg_id=516, mode="dynamic", K=16, D=2, total_tokens=63, V=777,
                                                P=70, Hq=4, Hkv=2, d=64, dtype="bf16"),
         "dynamic-deeper-than-dcap": lambda: gen.make_custom(cfg_id=517, mode="dynamic", K=1, D=6, total_tokens=6,
