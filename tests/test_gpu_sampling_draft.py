@@ -174,6 +174,32 @@ def test_draft_sampling_edge_cases_and_workspace_reuse():
         compare(tokens, parents, sizes, probs, q, uni, status, dcap, True, ws)
 
 
+@pytest.mark.parametrize("V", [700, 32000])
+def test_draft_sampling_wide_nodes_and_repeated_tokens(V):
+    # one level under the root with 64, 65 and 129 children (the child mask's later
+    # words), tokens repeated among siblings (a repeat's mass is already removed
+    # without replacement) and outside the vocabulary; V = 700 takes the one
+    # workgroup per request kernel, V = 32000 the sliced one
+    w = gen.make_custom(cfg_id=1760 + V % 7, B=4, mode="given", given_sizes=[65, 66, 130, 40], given_depth=1,
+                        V=V, P=4, T_max=160, dcap=3, accept_prob=0.3)
+    tokens, parents, sizes, probs, q, uni, status = given_case(w)
+    tokens = tokens.copy()
+    tokens[1, 1:66] = np.arange(65) % 23
+    tokens[2, 1:130] = np.arange(129) % 50
+    tokens[3, 1:40] = np.arange(39) % 7
+    tokens[3, 5] = -1
+    tokens[3, 9] = V + 2
+    q = gen.synthetic_draft_probs(w, tokens, parents, sizes)
+    for wr in (True, False):
+        compare(tokens, parents, sizes, probs, q, uni, status, w.dcap, wr)
+    # every child rejected: the residual after all of a node's updates
+    uni2 = uni.copy()
+    uni2[:, 1:] = np.float32(np.nextafter(np.float32(1.0), np.float32(0.0)))
+    for wr in (True, False):
+        got = compare(tokens, parents, sizes, probs, q, uni2, status, w.dcap, wr)
+        assert (got["accept_len"] == 0).any()
+
+
 def test_draft_sampling_largest_vocabulary_and_tiny_trees():
     V = 262144                                      # the call's limit (a 32 KB bitmap of removed tokens)
     w = gen.make_custom(cfg_id=1750, B=2, mode="given", given_sizes=[12, 1], given_depth=3, V=V, P=4, T_max=16,
