@@ -73,7 +73,7 @@ def _scaled_v(w, factor):
 def test_split_partials_keep_the_range_of_v(factor):
     """V scaled far above fp16's largest value (|v| up to ~2e5) and far below its
     normal range (~1e-7): outputs through the split-KV partials (one request over a
-    2048-token prefix: 11 splits; two over 9000 tokens: 8 splits) must keep bf16's
+    2048-token prefix: 7 splits; two over 9000 tokens: 8 splits) must keep bf16's
     range, like the unsplit path and the oracle.  The bars apply in units of the
     scale (attention is linear in V)."""
     run(_scaled_v(gen.make_workload(2), factor), v_scale=factor)

@@ -52,5 +52,5 @@ def _noalloc_against_workspace_call(w):
 def test_noalloc_two_calls_second_smaller():
     # 1: two requests over 9000-token prefixes, 61-node trees, 64 query heads (8 splits, ~33 MiB of partials)
     _noalloc_against_workspace_call(gen.make_workload(4, batch=2, prefix=9000))
-    # 2: one request over 2048 tokens (11 splits, ~6 MiB): reads only what it wrote
+    # 2: one request over 2048 tokens (7 splits, ~4 MiB): reads only what it wrote
     _noalloc_against_workspace_call(gen.make_workload(2))

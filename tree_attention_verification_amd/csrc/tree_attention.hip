@@ -113,14 +113,18 @@ Plan plan_with(int B, int T_max, int Hq, int Hkv, long long S_cap, int nw, long 
 // Launch shape: 8-wavefront workgroups (two per SIMD, so one wavefront's softmax
 // overlaps the other's MFMAs) with splits of >= 256 keys, aiming at 512
 // workgroups.  When that leaves most of the chip idle (a single request: 8 kv
-// heads x ~9 splits = 72 workgroups), 4-wavefront workgroups with >= 192-key
-// splits spread the same work over more than twice as many CUs (measured on
-// MI355X: 17.9 vs 21.7 us for 61 nodes x 32 heads over a 2048-token prefix).
+// heads x ~9 splits = 72 workgroups), 4-wavefront workgroups (half the rows
+// each, one wavefront per SIMD) with splits of >= 320 keys spread the work over
+// more CUs.  Measured on MI355X for 61 nodes x 32 heads over a 2048-token prefix
+// (one call, combine included, the step's tree build between calls): splits of
+// 3, 4 or 5 tiles all take 19.4 us, so the longest (7 splits, 112 workgroups)
+// is kept for its fewer partials (11 -> 7 per row); 6 tiles 20.1 us, 8 tiles
+// 20.8 us; 8-wavefront workgroups over all 256 rows 22.6-23.8 us.
 Plan make_plan(int B, int T_max, int Hq, int Hkv, long long S_cap) {
   const long long m_max = (long long)(Hq / Hkv) * T_max;
   if (m_max <= 128) return plan_with(B, T_max, Hq, Hkv, S_cap, 4, 4 * KT);
   const Plan p = plan_with(B, T_max, Hq, Hkv, S_cap, 8, 4 * KT);
-  if (p.grid < 128) return plan_with(B, T_max, Hq, Hkv, S_cap, 4, 3 * KT);
+  if (p.grid < 128) return plan_with(B, T_max, Hq, Hkv, S_cap, 4, 5 * KT);
   return p;
 }
 
