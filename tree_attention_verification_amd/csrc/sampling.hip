@@ -485,9 +485,11 @@ __device__ __forceinline__ float key_float(uint32_t k) {
 // --------------------------------------------------------------------------
 // NPT > 0: V <= NPT NT and every thread keeps its NPT (key, weight) pairs in
 // registers after the first read; NPT = 0: KL: the keys are kept in LDS (V <=
-// kKlMaxV), else the logits are re-read on every pass.  With NPT = 0 a weight is
-// formed where a pass needs it: every one for the first top-p level, only the
-// chosen bin's or the kept tokens' afterwards.
+// kKlMaxV), else the logits are re-read on every pass.  With NPT = 0 the weights
+// are formed once, in the pass that does the first top-p level (or sums the kept
+// weights), and kept for the later passes: in LDS in place of the keys (KL; the
+// few keys still needed afterwards are formed again from the logits), else in the
+// output row.
 // Rows are launched in order of their cost, so that the rows still starting as
 // the grid drains are short ones.  The filter settings decide a row's cost: a
 // radix top-p cut (most), then a full pass without top-p (or with a long top-k),
@@ -710,9 +712,18 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
     for (int j = 0; j < NPT; ++j) reg[j].w = weight(reg[j].k);
   }
   bool stored = false;
+  // KL: once the weights are formed, each token's LDS slot holds its weight
+  // (float bits; 0 outside the top-k cut) in place of its key, so no pass after
+  // that touches global memory but the output and the few keys still needed,
+  // which come back from the logits (key_at)
+  bool lw = false;
+  auto key_at = [&](int v) { return logit_key(lr[v]); };
   auto wt = [&](uint32_t k, float w) -> float { return (NPT > 0 || stored) ? w : weight(k); };
-  auto ld_k = [&](int v) { return KW{KL ? s_key[v] : logit_key(lr[v]), 0.0f}; };
-  auto ld_kw = [&](int v) { return KW{KL ? s_key[v] : logit_key(lr[v]), stored ? orow[v] : 0.0f}; };
+  auto ld_k = [&](int v) { return KW{KL ? (lw ? key_at(v) : s_key[v]) : logit_key(lr[v]), 0.0f}; };
+  auto ld_kw = [&](int v) {
+    if (KL && lw) return KW{0u, __uint_as_float(s_key[v])};
+    return KW{KL ? s_key[v] : logit_key(lr[v]), stored ? orow[v] : 0.0f};
+  };
   // one pass over the row: body(v, KW) for this thread's tokens in increasing v;
   // pass_k leaves the weight out (0) where it is not in registers
   auto pass = [&](auto body) __attribute__((always_inline)) {
@@ -886,7 +897,7 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
     auto body = [&](int v, KW e) {
       if (f(e.k, v, e.w)) {
         const int pos = atomicAdd(&s_cnt, 1);
-        if (pos < cap) s_hist[pos] = tok_key(e.k, v);
+        if (pos < cap) s_hist[pos] = tok_key(lw ? key_at(v) : e.k, v);
       }
     };
     if (stored) {
@@ -1144,14 +1155,16 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
     }
     pass_k([&](int v, KW e) {
       const float w = in_k(e.k, v) ? wt(e.k, e.w) : 0.0f;
-      if constexpr (NPT == 0) orow[v] = w;
+      if constexpr (KL) s_key[v] = __float_as_uint(w);  // (this thread's own slot, read just above)
+      else if constexpr (NPT == 0) orow[v] = w;
       if (with_p) {
         if (w > 0.0f) atomicAdd(&s_hist[__float_as_uint(w) >> 20], w_word(w));
       } else if (!(mp > 0.0f) || w >= mp || v == tok0) {
         wsum += (double)w;
       }
     });
-    stored = NPT == 0;  // later passes read the weights back (ld_kw)
+    stored = NPT == 0;  // later passes read the weights back (ld_kw): from LDS (KL) or the output row
+    lw = KL;
   }
 
   // ---- top-p cut (tpk, cp) over the top-k survivors: the shortest rank prefix
@@ -1181,7 +1194,7 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
         for (int e = tid; e < nb; e += NT) s_hist[e] = 0ull;
         __syncthreads();
         pass([&](int v, KW e) {
-          const float w = in_k(e.k, v) ? wt(e.k, e.w) : 0.0f;
+          const float w = lw ? e.w : (in_k(e.k, v) ? wt(e.k, e.w) : 0.0f);
           const uint32_t u = __float_as_uint(w);
           if (w > 0.0f && (u >> sh0) == prefix) atomicAdd(&s_hist[(u >> sh) & (nb - 1)], w_word(w));
         });
@@ -1198,7 +1211,7 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
     if (reached && m <= NT) {
       __syncthreads();
       gather(NT, [&](uint32_t k, int v, float w) {
-        const float x = in_k(k, v) ? wt(k, w) : 0.0f;
+        const float x = lw ? w : (in_k(k, v) ? wt(k, w) : 0.0f);
         return x > 0.0f && (__float_as_uint(x) >> sh) == prefix;
       });
       rank_into_top(m, m);
@@ -1251,7 +1264,14 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
         const uint32_t pmask = shift == 24 ? 0u : (0xFFFFFFFFu << (shift + 8));
         auto in_c = [&](auto f) {
           pass([&](int v, KW e) {
-            if (in_k(e.k, v) && wt(e.k, e.w) == c && (e.k & pmask) == kp) f(e.k);
+            if (lw) {
+              if (e.w == c) {  // (c > 0: inside the top-k cut)
+                const uint32_t k = key_at(v);
+                if ((k & pmask) == kp) f(k);
+              }
+            } else if (in_k(e.k, v) && wt(e.k, e.w) == c && (e.k & pmask) == kp) {
+              f(e.k);
+            }
           });
         };
         kp |= (uint32_t)max(count_level(n, ab, in_c, [&](uint32_t k) { return (k >> shift) & 255u; }), 0)
@@ -1278,7 +1298,20 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
     if (keep) orow[key_index(s_top[tid])] = (float)((double)w_t * (1.0 / W));
     return;
   }
+  // the top-p cut by weight: w grows with the key, so a weight above the cut
+  // token's ranks above it and one below ranks below; only equal weights need
+  // the key (tpk = 0: no cut)
+  const float w_cut = tpk ? weight(tpk) : 0.0f;
   auto kept_w = [&](uint32_t k, int v, float w) -> float {
+    if (lw) {
+      if (!(w > 0.0f)) return 0.0f;  // (outside the top-k cut, or no weight)
+      if (tpk && !(w > w_cut)) {
+        if (w < w_cut) return 0.0f;
+        const uint32_t kv = key_at(v);
+        if (!(kv > tpk || (kv == tpk && v <= cp))) return 0.0f;
+      }
+      return (!(mp > 0.0f) || w >= mp || v == tok0) ? w : 0.0f;
+    }
     if (!(in_k(k, v) && (k > tpk || (k == tpk && v <= cp)))) return 0.0f;
     const float x = wt(k, w);
     return (!(mp > 0.0f) || x >= mp || v == tok0) ? x : 0.0f;
@@ -1297,8 +1330,8 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
   const double rW = 1.0 / W;
   pass([&](int v, KW e) {
     const float x = kept_w(e.k, v, e.w);
-    // (NPT = 0: a token outside the top-k cut already holds 0)
-    if (NPT > 0 || x > 0.0f || in_k(e.k, v)) orow[v] = x > 0.0f ? (float)((double)x * rW) : 0.0f;
+    // (NPT = 0 without LDS weights: a token outside the top-k cut already holds 0)
+    if (NPT > 0 || lw || x > 0.0f || in_k(e.k, v)) orow[v] = x > 0.0f ? (float)((double)x * rW) : 0.0f;
   });
 }
 
