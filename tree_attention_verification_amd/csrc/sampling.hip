@@ -176,6 +176,28 @@ __device__ __forceinline__ unsigned long long block_max_u64(unsigned long long v
   return t;
 }
 
+// The workgroup maximum of two values at once (one barrier pair); s holds
+// 2 NT / 64 entries.
+template <int NT = kThreads>
+__device__ __forceinline__ void block_max2_u64(unsigned long long& a, unsigned long long& c, unsigned long long* s) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  a = wave_max_u64(a);
+  c = wave_max_u64(c);
+  if (lane == 0) {
+    s[wave] = a;
+    s[NT / 64 + wave] = c;
+  }
+  __syncthreads();
+  unsigned long long ta = 0ull, tc = 0ull;
+  for (int w = 0; w < (NT / 64); ++w) {
+    ta = umax64(ta, s[w]);
+    tc = umax64(tc, s[NT / 64 + w]);
+  }
+  __syncthreads();
+  a = ta;
+  c = tc;
+}
+
 // s_waitcnt immediate (gfx9 encoding) that waits for every vector memory
 // operation of the wavefront, stores included, and for nothing else: vmcnt 0
 // (bits 3:0 and 15:14), expcnt 7 (bits 6:4), lgkmcnt 15 (bits 11:8)
@@ -651,21 +673,36 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
     float x[J];
 #pragma unroll
     for (int j = 0; j < J; ++j) x[j] = tid + j * NT < V ? lr[tid + j * NT] : -INFINITY;
+    // this thread's tokens come in increasing v, so its first-ranked token is the
+    // first one of the largest key (only a strictly larger key replaces it); the
+    // smallest finite key is tracked as k - (key(-inf) + 1), which wraps the key
+    // of -inf to the top
+    uint32_t bk = 0u, kf = 0xFFFFFFFFu;
+    int bv = 0;
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       const int v = tid + j * NT;
       if (v < V) {
         const uint32_t k = logit_key(x[j]);
         s_key[v] = k;  // read back by this thread only (the same v in every pass)
-        see(k, v);
+        if (k > bk) {
+          bk = k;
+          bv = v;
+        }
+        kf = min(kf, k - (kNegInfKey + 1u));
       }
     }
+    if (bk) best = tok_key(bk, bv);
+    if (kf != 0xFFFFFFFFu) kmin = kf + (kNegInfKey + 1u);
   } else {
     row_pass<NT>(V, ld_l, [&](int v, float x) { see(logit_key(x), v); });
   }
   const unsigned long long best_own = best;  // this thread's first-ranked token (0: none)
-  best = block_max_u64<NT>(best, s_u);
-  kmin = ~(uint32_t)block_max_u64<NT>((unsigned long long)(~kmin), s_u);
+  {
+    unsigned long long nk = (unsigned long long)(~kmin);
+    block_max2_u64<NT>(best, nk, s_hist);
+    kmin = ~(uint32_t)nk;
+  }
   const uint32_t kmax = (uint32_t)(best >> 32);
   const int tok0 = (int)key_index(best);
   const float tau = temperature[b];
@@ -986,7 +1023,26 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
     const uint32_t c_k =
         (ch << 8) | (uint32_t)max(0, count_level(kk, above_t, [&](auto f) { if ((mc >> 8) == ch) f(mc); },
                                                  [](uint32_t c) { return c & 255u; }));
-    const int m = gather(HIST, [&](uint32_t k, int, float) { return vcode(k) >= c_k; });
+    // the tokens whose code reaches c_k are those whose key reaches k_c, the
+    // smallest key with that code (codes grow with the key over [key(-inf), kmax],
+    // which holds every token's key): a 64-way search on each wavefront's lanes,
+    // the same in every wavefront, then one comparison per token
+    uint32_t k_c = kNegInfKey;
+    if (vcode(k_c) < c_k) {
+      uint32_t lo = k_c, hi = kmax;  // vcode(lo) < c_k <= vcode(hi)
+      while (hi - lo > 1u) {
+        const unsigned long long step = ((unsigned long long)(hi - lo) + 63ull) / 64ull;
+        const uint32_t p = (uint32_t)min((unsigned long long)lo + step * (unsigned long long)(lane + 1),
+                                         (unsigned long long)hi);
+        const unsigned long long ok = __ballot(vcode(p) >= c_k);  // (lane 63 probes hi)
+        const int f = __ffsll((long long)ok) - 1;
+        const uint32_t nh = (uint32_t)__builtin_amdgcn_readlane((int)p, f);
+        lo = f ? (uint32_t)__builtin_amdgcn_readlane((int)p, f - 1) : lo;
+        hi = nh;
+      }
+      k_c = hi;
+    }
+    const int m = gather(HIST, [&](uint32_t k, int, float) { return k >= k_c; });
     if (m <= HIST) {
       rank_into_top(m, kk);
       const unsigned long long last = uni(s_top[kk - 1]);
