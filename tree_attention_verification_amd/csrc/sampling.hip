@@ -757,9 +757,10 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
   auto key_at = [&](int v) { return logit_key(lr[v]); };
   auto wt = [&](uint32_t k, float w) -> float { return (NPT > 0 || stored) ? w : weight(k); };
   auto ld_k = [&](int v) { return KW{KL ? (lw ? key_at(v) : s_key[v]) : logit_key(lr[v]), 0.0f}; };
+  // (only passes after the weight pass read weights: with KL they are in LDS)
   auto ld_kw = [&](int v) {
-    if (KL && lw) return KW{0u, __uint_as_float(s_key[v])};
-    return KW{KL ? s_key[v] : logit_key(lr[v]), stored ? orow[v] : 0.0f};
+    if constexpr (KL) return KW{0u, __uint_as_float(s_key[v])};
+    else return KW{logit_key(lr[v]), stored ? orow[v] : 0.0f};
   };
   // one pass over the row: body(v, KW) for this thread's tokens in increasing v;
   // pass_k leaves the weight out (0) where it is not in registers
@@ -928,13 +929,16 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
   // Gathers the tokens with f(k, v, w) into s_hist as rank keys (in any order)
   // and returns their number; entries past cap (<= HIST) are dropped.  w is the
   // stored weight once the weights are stored (else 0, or the register copy).
+  // by_w (KL, once the weights are in LDS): the gathered entries rank by weight,
+  // then token, instead of by key, then token
+  bool by_w = false;
   auto gather = [&](int cap, auto f) -> int {
     if (tid == 0) s_cnt = 0;
     __syncthreads();
     auto body = [&](int v, KW e) {
       if (f(e.k, v, e.w)) {
         const int pos = atomicAdd(&s_cnt, 1);
-        if (pos < cap) s_hist[pos] = tok_key(lw ? key_at(v) : e.k, v);
+        if (pos < cap) s_hist[pos] = tok_key(lw ? (by_w ? __float_as_uint(e.w) : key_at(v)) : e.k, v);
       }
     };
     if (stored) {
@@ -1229,6 +1233,11 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
   // exact weight of the prefix, when the cut is found.
   uint32_t tpk = 0u;
   int cp = V;
+  // KL: the cut by weight: a weight above w_cut stays, one below goes, and one
+  // equal to it stays if tie_all (every token of that weight is inside the cut)
+  // or its key is inside (tpk, cp)
+  bool tie_all = false;
+  float w_cut = 0.0f;
   int n_list = kk;  // the ranked survivors that stay (as_list)
   bool have_kept = false;
   Norm kept = nzero();
@@ -1250,7 +1259,7 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
         for (int e = tid; e < nb; e += NT) s_hist[e] = 0ull;
         __syncthreads();
         pass([&](int v, KW e) {
-          const float w = lw ? e.w : (in_k(e.k, v) ? wt(e.k, e.w) : 0.0f);
+          const float w = KL ? e.w : (in_k(e.k, v) ? wt(e.k, e.w) : 0.0f);
           const uint32_t u = __float_as_uint(w);
           if (w > 0.0f && (u >> sh0) == prefix) atomicAdd(&s_hist[(u >> sh) & (nb - 1)], w_word(w));
         });
@@ -1266,10 +1275,15 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
     }
     if (reached && m <= NT) {
       __syncthreads();
+      // KL: the bin's tokens are ranked by weight (w grows with the key, so only
+      // equal weights may be out of key order: they are sorted out below when the
+      // cut falls among them), and each entry carries its weight
+      by_w = KL;
       gather(NT, [&](uint32_t k, int v, float w) {
-        const float x = lw ? w : (in_k(k, v) ? wt(k, w) : 0.0f);
+        const float x = KL ? w : (in_k(k, v) ? wt(k, w) : 0.0f);
         return x > 0.0f && (__float_as_uint(x) >> sh) == prefix;
       });
+      by_w = false;
       rank_into_top(m, m);
       // every weight of the bin is m_t 2^s units (one exponent): the cut is the
       // first rank whose inclusive mantissa sum reaches need = ceil((thr - above)
@@ -1289,7 +1303,7 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
       const unsigned long long need = ((unsigned long long)nq.l[1] << 32) | nq.l[0];
       unsigned long long mt = 0ull;
       if (tid < m) {
-        const uint32_t u = __float_as_uint(weight((uint32_t)(s_top[tid] >> 32)));
+        const uint32_t u = KL ? (uint32_t)(s_top[tid] >> 32) : __float_as_uint(weight((uint32_t)(s_top[tid] >> 32)));
         mt = (u >> 23) ? ((u & 0x7FFFFFu) | 0x800000u) : u;
       }
       unsigned long long lo_c, hi_c, tot_c;
@@ -1304,8 +1318,50 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
         __syncthreads();
         kept = nuniform(s_kept);
         const unsigned long long ck2 = uni(s_top[cut]);
-        tpk = (uint32_t)(ck2 >> 32);
-        cp = (int)key_index(ck2);
+        if constexpr (KL) {
+          // the tokens of the cut's weight are entries first..last; the first
+          // cut - first + 1 of them in key order stay
+          const uint32_t uc = (uint32_t)(ck2 >> 32);
+          w_cut = __uint_as_float(uc);
+          if (tid == 0) {
+            s_pick = m;
+            s_sel = -1;
+          }
+          __syncthreads();
+          if (tid < m && (uint32_t)(s_top[tid] >> 32) == uc) {
+            atomicMin(&s_pick, tid);
+            atomicMax(&s_sel, tid);
+          }
+          __syncthreads();
+          const int first = uni(s_pick), last = uni(s_sel);
+          const int n_t = cut - first + 1, g = last - first + 1;
+          __syncthreads();
+          tie_all = n_t == g;
+          if (!tie_all) {
+            // their keys, and the n_t-th of them in (key desc, token asc) order
+            if (tid >= first && tid <= last) {
+              const int v = (int)key_index(s_top[tid]);
+              s_hist[tid - first] = tok_key(key_at(v), v);
+            }
+            __syncthreads();
+            for (int t = tid; t < g; t += NT) {
+              const unsigned long long my = s_hist[t];
+              int rk = 0;
+              for (int o = 0; o < g; ++o) rk += s_hist[o] > my;
+              if (rk == n_t - 1) s_abvc = my;
+            }
+            __syncthreads();
+            const unsigned long long lastk = uni(s_abvc);
+            tpk = (uint32_t)(lastk >> 32);
+            cp = (int)key_index(lastk);
+            __syncthreads();
+          } else {
+            tpk = 1u;  // (a cut exists; equal weights need no key)
+          }
+        } else {
+          tpk = (uint32_t)(ck2 >> 32);
+          cp = (int)key_index(ck2);
+        }
         have_kept = true;
       }
     } else if (reached) {
@@ -1320,7 +1376,7 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
         const uint32_t pmask = shift == 24 ? 0u : (0xFFFFFFFFu << (shift + 8));
         auto in_c = [&](auto f) {
           pass([&](int v, KW e) {
-            if (lw) {
+            if constexpr (KL) {
               if (e.w == c) {  // (c > 0: inside the top-k cut)
                 const uint32_t k = key_at(v);
                 if ((k & pmask) == kp) f(k);
@@ -1354,17 +1410,19 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
     if (keep) orow[key_index(s_top[tid])] = (float)((double)w_t * (1.0 / W));
     return;
   }
-  // the top-p cut by weight: w grows with the key, so a weight above the cut
-  // token's ranks above it and one below ranks below; only equal weights need
-  // the key (tpk = 0: no cut)
-  const float w_cut = tpk ? weight(tpk) : 0.0f;
+  // KL: the top-p cut by weight: w grows with the key, so a weight above the
+  // cut's ranks above it and one below ranks below; only equal weights may need
+  // the key (tpk = 0: no cut).  A cut set by key alone takes the weight of its key.
+  if (KL && tpk && w_cut == 0.0f) w_cut = weight(tpk);
   auto kept_w = [&](uint32_t k, int v, float w) -> float {
-    if (lw) {
+    if constexpr (KL) {
       if (!(w > 0.0f)) return 0.0f;  // (outside the top-k cut, or no weight)
       if (tpk && !(w > w_cut)) {
         if (w < w_cut) return 0.0f;
-        const uint32_t kv = key_at(v);
-        if (!(kv > tpk || (kv == tpk && v <= cp))) return 0.0f;
+        if (!tie_all) {
+          const uint32_t kv = key_at(v);
+          if (!(kv > tpk || (kv == tpk && v <= cp))) return 0.0f;
+        }
       }
       return (!(mp > 0.0f) || w >= mp || v == tok0) ? w : 0.0f;
     }
@@ -1387,7 +1445,7 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
   pass([&](int v, KW e) {
     const float x = kept_w(e.k, v, e.w);
     // (NPT = 0 without LDS weights: a token outside the top-k cut already holds 0)
-    if (NPT > 0 || lw || x > 0.0f || in_k(e.k, v)) orow[v] = x > 0.0f ? (float)((double)x * rW) : 0.0f;
+    if (NPT > 0 || KL || x > 0.0f || in_k(e.k, v)) orow[v] = x > 0.0f ? (float)((double)x * rW) : 0.0f;
   });
 }
 
