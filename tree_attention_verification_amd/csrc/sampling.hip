@@ -636,7 +636,7 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
   __shared__ Norm s_abv, s_thr, s_kept, s_nw[NW];
   __shared__ unsigned long long s_top[NT];  // ranked tokens, best first
   __shared__ unsigned long long s_abvc;
-  __shared__ int s_pick, s_sel, s_cnt;
+  __shared__ int s_pick, s_sel, s_cnt, s_fsel;
   extern __shared__ uint32_t s_key[];  // KL: the order key of token v
   static_assert(!KL || (NPT == 0 && NT == 1024), "keys in LDS: 1024 threads, no register copy");
   __shared__ double s_exp2[64];  // 2^(j / 64) (visible after the first barrier below)
@@ -1204,6 +1204,108 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
     return sel;
   };
 
+  // Level 0 decided by float64 sums first.  A bin's weight (its mantissa sum,
+  // < 2^42, times 2^(e - 1) units) is exact in float64; the suffix sums over the
+  // bins (4 per thread on the first WT threads, a lane scan, then the wavefront
+  // totals) and the threshold top_p x total take at most ~25 roundings of
+  // non-negative terms, so each is within total x 2^-48 of its exact value.  A
+  // bin whose cumulative before it is below the threshold and after it above it
+  // by more than total x 2^-40 on both sides is therefore the exact crossing.
+  // Only that bin's exact "above" and the exact threshold are then formed (two
+  // workgroup sums of Wide).  Returns -2 when no bin clears the margin (a
+  // crossing within it, or none at all): the exact w_select decides then.
+  auto w_select0_fast = [&]() -> int {
+    const bool part = tid < WT;  // (wave-uniform)
+    __syncthreads();  // the bins' sums are complete
+    if (tid == 0) s_fsel = -1;
+    unsigned long long ms[4];
+    double dv[4];
+    double S = 0.0;
+    // the first WT threads: bins 4 tid .. 4 tid + 3, one exponent e = tid / 2
+    const int e = tid >> 1, sx = e ? e - 1 : 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ms[j] = part ? (s_hist[4 * tid + j] & (kCnt1 - 1)) : 0ull;
+      dv[j] = ldexp((double)ms[j], sx);
+      S += dv[j];
+    }
+    // inclusive prefix over the lanes by DPP moves (as wave_reduce_dpp), then the
+    // wavefront totals: the bins above this thread's = total - prefix
+    unsigned long long x = (unsigned long long)__double_as_longlong(S);
+    auto addd = [](unsigned long long a, unsigned long long b) {
+      return (unsigned long long)__double_as_longlong(__longlong_as_double((long long)a) +
+                                                      __longlong_as_double((long long)b));
+    };
+    x = addd(x, dpp_u64<0x111, 0xF>(x));
+    x = addd(x, dpp_u64<0x112, 0xF>(x));
+    x = addd(x, dpp_u64<0x114, 0xF>(x));
+    x = addd(x, dpp_u64<0x118, 0xF>(x));
+    x = addd(x, dpp_u64<0x142, 0xA>(x));
+    x = addd(x, dpp_u64<0x143, 0xC>(x));
+    const double incl = __longlong_as_double((long long)x);
+    if (lane == 63 && part) s_d[wave] = incl;  // the wavefront's total
+    __syncthreads();
+    double tot = 0.0, above_w = 0.0;
+    for (int w = 0; w < WW; ++w) {
+      const double v = s_d[w];
+      tot += v;
+      if (w > wave) above_w += v;
+    }
+    const double thr_d = (double)tp * tot;
+    const double marg = tot * 0x1p-40;
+    if (part) {
+      double r = (s_d[wave] - incl) + above_w;  // every bin above this thread's
+#pragma unroll
+      for (int j = 3; j >= 0; --j) {
+        const double r0 = r;
+        r += dv[j];
+        if (r0 + marg < thr_d && r - marg >= thr_d) s_fsel = 4 * tid + j;  // (at most one)
+      }
+    }
+    __syncthreads();
+    const int sel = uni(s_fsel);
+    if (sel < 0) return -2;
+    // exact: the bins above sel and all bins, as carry-save limbs summed by DPP
+    // within each wavefront, then the wavefronts' limbs added in LDS
+    if (part) {
+      unsigned long long ma = 0ull, mz = 0ull;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        mz += ms[j];
+        if (4 * tid + j > sel) ma += ms[j];
+      }
+      const Wide wa = wide_shifted(ma, sx), wz = wide_shifted(mz, sx);  // (mantissa sums < 2^44)
+      auto addu = [](unsigned long long a, unsigned long long b) { return a + b; };
+#pragma unroll
+      for (int l = 0; l < NL; ++l) {
+        const unsigned long long ta = wave_reduce_dpp(wa.l[l], addu);
+        const unsigned long long tz = wave_reduce_dpp(wz.l[l], addu);
+        if (lane == 0) {
+          s_hist[1024 + wave * 2 * NL + l] = ta;
+          s_hist[1024 + wave * 2 * NL + NL + l] = tz;
+        }
+      }
+    }
+    __syncthreads();
+    if (tid == 0) {
+      Wide wa = wzero(), wz = wzero();
+      for (int w = 0; w < WW; ++w)
+#pragma unroll
+        for (int l = 0; l < NL; ++l) {
+          wa.l[l] += s_hist[1024 + w * 2 * NL + l];
+          wz.l[l] += s_hist[1024 + w * 2 * NL + NL + l];
+        }
+      s_abv = norm_of(wa);
+      s_thr = nthreshold(tp, norm_of(wz));
+      s_cnt = (int)(s_hist[sel] >> 44);
+    }
+    __syncthreads();
+    above = nuniform(s_abv);
+    thr = nuniform(s_thr);
+    __syncthreads();
+    return sel;
+  };
+
   // ---- one pass forming every survivor's weight (unless they are a ranked
   // list): NPT = 0 stores it into the output row (0 for the others), and the pass
   // also does the first top-p level's sums or, without top-p, sums the kept weights
@@ -1264,7 +1366,13 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
           if (w > 0.0f && (u >> sh0) == prefix) atomicAdd(&s_hist[(u >> sh) & (nb - 1)], w_word(w));
         });
       }
-      const int sel = w_select(lev, prefix);
+      // (the float64 level 0 on the keys-in-LDS variant only: the others keep
+      // their registers for their own passes)
+      int sel = -2;
+      if constexpr (KL) {
+        if (lev == 0) sel = w_select0_fast();
+      }
+      if (sel == -2) sel = w_select(lev, prefix);
       if (sel < 0) {  // never reached: every survivor stays
         reached = false;
         break;
