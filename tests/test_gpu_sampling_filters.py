@@ -152,6 +152,37 @@ def test_filters_exact_top_p_cut(many, top_k):
     run_filter(lg, tree_size, None, params)
 
 
+@pytest.mark.parametrize("V,many", [(3000, True), (32000, False)])
+def test_filters_top_p_cut_on_a_weight_bin_boundary(V, many):
+    """top_p x total equal to the exact weight above a level-0 radix bin (weights 1, 1
+    in one bin and 0.5 x 4 in the next; top_p 0.5 of the total 4 is exactly the first
+    bin's 2): no float64 estimate of the cumulatives can tell on which side the cut
+    falls, so the exact bin choice decides (2 kept).  The next float32 above 0.5
+    keeps 3, and so does top_p 0.5 once a tail of ~1e-11 weights is added (its
+    mass puts the threshold past the boundary).
+    Both shapes keep the row's keys in LDS (V = 3000 at 256 threads per row, V = 32000
+    at 1024)."""
+    from oracle import sampling as osm
+    B, T_max = (8, 64) if many else (4, 1)
+    lg = np.random.default_rng(11).normal(0, 1, (B, T_max, V)).astype(np.float32)
+    half = np.float32(np.log(0.5))
+    tp = np.full(B, 0.9, np.float32)
+    cases = [(-np.inf, np.float32(0.5), 2), (-np.inf, np.nextafter(np.float32(0.5), np.float32(1)), 3),
+             (np.float32(np.log(1e-11)), np.float32(0.5), 3),
+             (np.float32(np.log(1e-11)), np.nextafter(np.float32(0.5), np.float32(1)), 3)]
+    for r, (fill, p_, kept) in enumerate(cases):
+        row = np.full(V, fill, np.float32)
+        row[[3, V - 2]] = 0.0
+        row[[5, 17, V // 2, V - 1]] = half
+        lg[r, 0] = row
+        tp[r] = p_
+        ref = osm.sampling_probs_row(row, 1.0, 0, p_, 0.0)
+        assert int((ref > 0).sum()) == kept, (r, int((ref > 0).sum()))
+    tree_size = np.ones(B, np.int32)
+    params = (np.ones(B, np.float32), np.zeros(B, np.int32), tp, np.zeros(B, np.float32))
+    run_filter(lg, tree_size, None, params)
+
+
 @pytest.mark.parametrize("tie_step", [0.0, 0.25])
 def test_filters_many_rows_large_vocabulary(tie_step):
     """>= 512 rows (the 256-thread kernel) at V = 32000, which keeps every row in
