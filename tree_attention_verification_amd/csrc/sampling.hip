@@ -637,6 +637,7 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
   __shared__ unsigned long long s_top[NT];  // ranked tokens, best first
   __shared__ unsigned long long s_abvc;
   __shared__ int s_pick, s_sel, s_cnt, s_fsel;
+  __shared__ uint32_t s_kc;
   extern __shared__ uint32_t s_key[];  // KL: the order key of token v
   static_assert(!KL || (NPT == 0 && NT == 1024), "keys in LDS: 1024 threads, no register copy");
   __shared__ double s_exp2[64];  // 2^(j / 64) (visible after the first barrier below)
@@ -952,13 +953,34 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
     return m;
   };
   // Ranks the m (<= HIST) distinct rank keys of s_hist by counting the larger
-  // ones: the first nkeep (<= NT) go in rank order into s_top.
+  // ones: the first nkeep (<= NT) go in rank order into s_top.  With the keys in
+  // LDS and m <= NT / 2, each entry has G = 2..16 adjacent lanes, each counting
+  // every G-th entry, and the G counts are added by lane exchanges.
   auto rank_into_top = [&](int m, int nkeep) {
-    for (int t = tid; t < m; t += NT) {
-      const unsigned long long my = s_hist[t];
-      int rk = 0;
-      for (int o = 0; o < m; ++o) rk += s_hist[o] > my;  // (all lanes read the same entry)
-      if (rk < nkeep) s_top[rk] = my;
+    auto by_one = [&]() {
+      for (int t = tid; t < m; t += NT) {
+        const unsigned long long my = s_hist[t];
+        int rk = 0;
+        for (int o = 0; o < m; ++o) rk += s_hist[o] > my;  // (all lanes read the same entry)
+        if (rk < nkeep) s_top[rk] = my;
+      }
+    };
+    if constexpr (KL) {
+      int G = 1;
+      while (G < 16 && m * G * 2 <= NT) G *= 2;
+      if (G == 1) {
+        by_one();
+      } else {
+        const int t = tid / G, q = tid % G;  // (m G <= NT: every entry has its lanes)
+        const unsigned long long my = t < m ? s_hist[t] : 0ull;
+        int rk = 0;
+        if (t < m)
+          for (int o = q; o < m; o += G) rk += s_hist[o] > my;
+        for (int off = 1; off < G; off <<= 1) rk += __shfl_xor(rk, off, 64);  // (G divides 64)
+        if (t < m && q == 0 && rk < nkeep) s_top[rk] = my;
+      }
+    } else {
+      by_one();  // (the other variants keep their registers for their own passes)
     }
     __syncthreads();
   };
@@ -1032,19 +1054,28 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
     // which holds every token's key): a 64-way search on each wavefront's lanes,
     // the same in every wavefront, then one comparison per token
     uint32_t k_c = kNegInfKey;
-    if (vcode(k_c) < c_k) {
-      uint32_t lo = k_c, hi = kmax;  // vcode(lo) < c_k <= vcode(hi)
-      while (hi - lo > 1u) {
-        const unsigned long long step = ((unsigned long long)(hi - lo) + 63ull) / 64ull;
-        const uint32_t p = (uint32_t)min((unsigned long long)lo + step * (unsigned long long)(lane + 1),
-                                         (unsigned long long)hi);
-        const unsigned long long ok = __ballot(vcode(p) >= c_k);  // (lane 63 probes hi)
-        const int f = __ffsll((long long)ok) - 1;
-        const uint32_t nh = (uint32_t)__builtin_amdgcn_readlane((int)p, f);
-        lo = f ? (uint32_t)__builtin_amdgcn_readlane((int)p, f - 1) : lo;
-        hi = nh;
+    // (keys in LDS: the first wavefront searches and the others take k_c from
+    // LDS; the other variants search on every wavefront, the same value)
+    if (!KL || wave == 0) {
+      if (vcode(k_c) < c_k) {
+        uint32_t lo = k_c, hi = kmax;  // vcode(lo) < c_k <= vcode(hi)
+        while (hi - lo > 1u) {
+          const unsigned long long step = ((unsigned long long)(hi - lo) + 63ull) / 64ull;
+          const uint32_t p = (uint32_t)min((unsigned long long)lo + step * (unsigned long long)(lane + 1),
+                                           (unsigned long long)hi);
+          const unsigned long long ok = __ballot(vcode(p) >= c_k);  // (lane 63 probes hi)
+          const int f = __ffsll((long long)ok) - 1;
+          const uint32_t nh = (uint32_t)__builtin_amdgcn_readlane((int)p, f);
+          lo = f ? (uint32_t)__builtin_amdgcn_readlane((int)p, f - 1) : lo;
+          hi = nh;
+        }
+        k_c = hi;
       }
-      k_c = hi;
+    }
+    if constexpr (KL) {
+      if (tid == 0) s_kc = k_c;
+      __syncthreads();
+      k_c = s_kc;
     }
     const int m = gather(HIST, [&](uint32_t k, int, float) { return k >= k_c; });
     if (m <= HIST) {
