@@ -235,11 +235,23 @@ __global__ __launch_bounds__(NW * 64, (NSTAGE == 2 && NW == 4) ? 2 : 1) void k_a
       const int Te = (sl != TV_ST_OK || Tl < 1 || Tl > T_max) ? 1 : Tl;
       nk = (Pl < 0 || (long long)Pl + Te > S_cap) ? 0 : Pl + Te;
     }
-    int rank = 0;
-    for (int o = 0; o < B; ++o) {
+    // the rank, counted by every wavefront over its share of the requests and
+    // added up through LDS (one barrier; the whole count repeated on every
+    // wavefront took ~4 us of each workgroup's prologue with 64 requests)
+    __shared__ int s_rank[NW][64];
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const int per = (B + NW - 1) / NW;
+    const int o0 = min(B, wv * per), o1 = min(B, o0 + per);
+    int part = 0;
+    for (int o = o0; o < o1; ++o) {
       const int x = __builtin_amdgcn_readlane(nk, o);
-      rank += (x > nk) || (x == nk && o < lane);
+      part += (x > nk) || (x == nk && o < lane);
     }
+    s_rank[wv][lane] = part;
+    __syncthreads();
+    int rank = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) rank += s_rank[w][lane];
     const unsigned long long m = __ballot(lane < B && rank == bg / Hkv);
     const int bsel = __ffsll((long long)m) - 1;
     bg = bsel * Hkv + bg % Hkv;
