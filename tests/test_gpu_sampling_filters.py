@@ -53,8 +53,10 @@ def run_filter(logits, tree_size, status, params):
     return got
 
 
-@pytest.mark.parametrize("V", [50, 1000, 32000, 128256])
+@pytest.mark.parametrize("V", [50, 1000, 20001, 32000, 128256])
 def test_filters_mixed_parameters(V):
+    """V = 20001 keeps its keys in LDS but, not a multiple of 4, reads its logits
+    one float at a time; V = 32000 reads them four at a time."""
     B = 8 if V <= 32000 else 3
     w = gen.make_custom(cfg_id=1600 + V % 89, B=B, mode="given", given_sizes=[6, 1, 3, 8, 2, 5, 4, 7][:B], V=V, P=4,
                         T_max=8, dcap=6)

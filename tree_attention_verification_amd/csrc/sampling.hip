@@ -715,26 +715,45 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
   } else if constexpr (KL) {
     // the whole row in flight at once (up to kKlMaxV / NT = 32 tokens per thread)
     constexpr int J = kKlMaxV / NT;
-    float x[J];
-#pragma unroll
-    for (int j = 0; j < J; ++j) x[j] = tid + j * NT < V ? lr[tid + j * NT] : -INFINITY;
     // this thread's tokens come in increasing v, so its first-ranked token is the
     // first one of the largest key (only a strictly larger key replaces it); the
     // smallest finite key is tracked as k - (key(-inf) + 1), which wraps the key
     // of -inf to the top
     uint32_t bk = 0u, kf = 0xFFFFFFFFu;
     int bv = 0;
+    auto take = [&](int v, float xv) __attribute__((always_inline)) {
+      const uint32_t k = logit_key(xv);
+      s_key[v] = k;  // (the later passes read it after the workgroup maxima's barrier)
+      if (k > bk) {
+        bk = k;
+        bv = v;
+      }
+      kf = min(kf, k - (kNegInfKey + 1u));
+    };
+    if ((V & 3) == 0 && !(reinterpret_cast<uintptr_t>(lr) & 15)) {
+      // 16-byte loads: thread t takes tokens 4 (t + j NT) .. + 3
+      typedef float f4 __attribute__((ext_vector_type(4)));
+      const f4* l4 = reinterpret_cast<const f4*>(lr);
+      f4 x4[J / 4];
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const int v = tid + j * NT;
-      if (v < V) {
-        const uint32_t k = logit_key(x[j]);
-        s_key[v] = k;  // read back by this thread only (the same v in every pass)
-        if (k > bk) {
-          bk = k;
-          bv = v;
+      for (int j = 0; j < J / 4; ++j)
+        x4[j] = tid + j * NT < (V >> 2) ? l4[tid + j * NT] : f4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+      for (int j = 0; j < J / 4; ++j) {
+        const int v = 4 * (tid + j * NT);
+        if (v < V) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) take(v + e, x4[j][e]);
         }
-        kf = min(kf, k - (kNegInfKey + 1u));
+      }
+    } else {
+      float x[J];
+#pragma unroll
+      for (int j = 0; j < J; ++j) x[j] = tid + j * NT < V ? lr[tid + j * NT] : -INFINITY;
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int v = tid + j * NT;
+        if (v < V) take(v, x[j]);
       }
     }
     if (bk) best = tok_key(bk, bv);
