@@ -480,6 +480,26 @@ __device__ __forceinline__ void range_pass(int c0, int c1, Load load, Body body)
   }
 }
 
+// Over a row of 4 n tokens, four consecutive ones per visit: thread t visits
+// quads q = t + j NT (tokens 4 q .. 4 q + 3) in increasing q, with the loads of
+// kQB quads issued together; indices past the row are clamped for the load and
+// skipped for the body.
+constexpr int kQB = 4;
+template <int NT, class Load, class Body>
+__device__ __forceinline__ void quad_pass(int n4, Load load, Body body) {
+  using T = decltype(load(0));
+  for (int base = threadIdx.x; base < n4; base += kQB * NT) {
+    T x[kQB];
+#pragma unroll
+    for (int j = 0; j < kQB; ++j) x[j] = load(min(base + j * NT, n4 - 1));
+#pragma unroll
+    for (int j = 0; j < kQB; ++j)
+      if (base + j * NT < n4) body(base + j * NT, x[j]);
+  }
+}
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 // logits: NaN ranks as -inf; order_key canonicalises -0.0
 __device__ __forceinline__ float clean_logit(float x) { return x != x ? -INFINITY : x; }
 __device__ __forceinline__ uint32_t logit_key(float x) { return order_key(clean_logit(x)); }
@@ -667,6 +687,9 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
   if (i >= T) return;
   const float* lr = logits + ((long long)b * T_max + i) * V;
   float* orow = probs + ((long long)b * T_max + i) * V;
+  // keys in LDS, rows of a multiple of 4 tokens on 16-byte boundaries: every pass
+  // over the row takes four consecutive tokens per visit (16-byte loads and stores)
+  const bool q4 = KL && (V & 3) == 0 && !((reinterpret_cast<uintptr_t>(lr) | reinterpret_cast<uintptr_t>(orow)) & 15);
   __shared__ double s_d[NW * 16];
   __shared__ unsigned long long s_u[NW];
   __shared__ Wide s_w[NW];
@@ -682,7 +705,7 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
   __shared__ unsigned long long s_abvc;
   __shared__ int s_pick, s_sel, s_cnt, s_fsel;
   __shared__ uint32_t s_kc;
-  extern __shared__ uint32_t s_key[];  // KL: the order key of token v
+  extern __shared__ __align__(16) uint32_t s_key[];  // KL: the order key of token v
   static_assert(!KL || (NPT == 0 && NT == 1024), "keys in LDS: 1024 threads, no register copy");
   __shared__ double s_exp2[64];  // 2^(j / 64) (visible after the first barrier below)
   if (tid < 64) s_exp2[tid] = exp2((double)tid * 0.015625);
@@ -730,14 +753,13 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
       }
       kf = min(kf, k - (kNegInfKey + 1u));
     };
-    if ((V & 3) == 0 && !(reinterpret_cast<uintptr_t>(lr) & 15)) {
+    if (q4) {
       // 16-byte loads: thread t takes tokens 4 (t + j NT) .. + 3
-      typedef float f4 __attribute__((ext_vector_type(4)));
-      const f4* l4 = reinterpret_cast<const f4*>(lr);
-      f4 x4[J / 4];
+      const f32x4* l4 = reinterpret_cast<const f32x4*>(lr);
+      f32x4 x4[J / 4];
 #pragma unroll
       for (int j = 0; j < J / 4; ++j)
-        x4[j] = tid + j * NT < (V >> 2) ? l4[tid + j * NT] : f4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        x4[j] = tid + j * NT < (V >> 2) ? l4[tid + j * NT] : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
       for (int j = 0; j < J / 4; ++j) {
         const int v = 4 * (tid + j * NT);
@@ -828,13 +850,21 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
   };
   // one pass over the row: body(v, KW) for this thread's tokens in increasing v;
   // pass_k leaves the weight out (0) where it is not in registers
+  const u32x4* s_key4 = reinterpret_cast<const u32x4*>(s_key);
   auto pass = [&](auto body) __attribute__((always_inline)) {
     if constexpr (NPT > 0) {
 #pragma unroll
       for (int j = 0; j < NPT; ++j)
         if (tid + j * NT < V) body(tid + j * NT, reg[j]);
     } else {
-      row_pass<NT, true>(V, ld_kw, body);
+      if (KL && q4) {
+        quad_pass<NT>(V >> 2, [&](int q) { return s_key4[q]; }, [&](int q, u32x4 u) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) body(4 * q + e, KW{0u, __uint_as_float(u[e])});
+        });
+      } else {
+        row_pass<NT, true>(V, ld_kw, body);
+      }
     }
   };
   auto pass_k = [&](auto body) __attribute__((always_inline)) {
@@ -843,7 +873,19 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
       for (int j = 0; j < NPT; ++j)
         if (tid + j * NT < V) body(tid + j * NT, reg[j]);
     } else {
-      row_pass<NT, !KL>(V, ld_k, body);
+      if (KL && q4 && lw) {
+        quad_pass<NT>(V >> 2, [&](int q) { return reinterpret_cast<const f32x4*>(lr)[q]; }, [&](int q, f32x4 x) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) body(4 * q + e, KW{logit_key(x[e]), 0.0f});
+        });
+      } else if (KL && q4) {
+        quad_pass<NT>(V >> 2, [&](int q) { return s_key4[q]; }, [&](int q, u32x4 u) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) body(4 * q + e, KW{u[e], 0.0f});
+        });
+      } else {
+        row_pass<NT, !KL>(V, ld_k, body);
+      }
     }
   };
   // the workgroup's sum of one Wide per thread (every thread gets it, carry-save):
@@ -1644,6 +1686,18 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
   }
   // w / W as w (1 / W) in double: within one double rounding of the quotient
   const double rW = 1.0 / W;
+  if (KL && q4) {
+    quad_pass<NT>(V >> 2, [&](int q) { return s_key4[q]; }, [&](int q, u32x4 u) {
+      f32x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x = kept_w(0u, 4 * q + e, __uint_as_float(u[e]));
+        o[e] = x > 0.0f ? (float)((double)x * rW) : 0.0f;
+      }
+      reinterpret_cast<f32x4*>(orow)[q] = o;
+    });
+    return;
+  }
   pass([&](int v, KW e) {
     const float x = kept_w(e.k, v, e.w);
     // (NPT = 0 without LDS weights: a token outside the top-k cut already holds 0)
