@@ -55,14 +55,20 @@ __device__ __forceinline__ unsigned long long dpp_u64(unsigned long long x) {
   const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(x >> 32), CTRL, ROWS, 0xF, true);
   return ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
 }
+// (every lane ends with the inclusive scan of the lanes up to its own)
 template <class Op>
-__device__ __forceinline__ unsigned long long wave_reduce_dpp(unsigned long long v, Op op) {
+__device__ __forceinline__ unsigned long long wave_scan_dpp(unsigned long long v, Op op) {
   v = op(v, dpp_u64<0x111, 0xF>(v));
   v = op(v, dpp_u64<0x112, 0xF>(v));
   v = op(v, dpp_u64<0x114, 0xF>(v));
   v = op(v, dpp_u64<0x118, 0xF>(v));
   v = op(v, dpp_u64<0x142, 0xA>(v));
   v = op(v, dpp_u64<0x143, 0xC>(v));
+  return v;
+}
+template <class Op>
+__device__ __forceinline__ unsigned long long wave_reduce_dpp(unsigned long long v, Op op) {
+  v = wave_scan_dpp(v, op);
   return ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63) << 32) |
          (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
 }
@@ -339,12 +345,6 @@ __device__ __forceinline__ Wide wshfl_down(const Wide& a, int o) {
   Wide r;
 #pragma unroll
   for (int i = 0; i < NL; ++i) r.l[i] = __shfl_down(a.l[i], o, 64);
-  return r;
-}
-__device__ __forceinline__ Wide wshfl_xor(const Wide& a, int m) {
-  Wide r;
-#pragma unroll
-  for (int i = 0; i < NL; ++i) r.l[i] = __shfl_xor(a.l[i], m, 64);
   return r;
 }
 // t[k] for a run-time k (0 past the end), without indexing registers dynamically
@@ -888,24 +888,6 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
       }
     }
   };
-  // the workgroup's sum of one Wide per thread (every thread gets it, carry-save):
-  // wavefront totals by butterfly, then the first wavefront adds them
-  auto block_wsum = [&](Wide v) -> Wide {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) wadd(v, wshfl_xor(v, o));
-    if (lane == 0) s_w[wave] = v;
-    __syncthreads();
-    if (tid < 64) {
-      Wide t = (tid < NW) ? s_w[tid] : wzero();
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) wadd(t, wshfl_xor(t, o));
-      if (tid == 0) s_w[0] = t;
-    }
-    __syncthreads();
-    const Wide t = s_w[0];
-    __syncthreads();
-    return t;
-  };
   const bool with_p = tp < 1.0f;
 
   // ---- value code: 16 bits, 65535 - floor((l_max - l) 65536 / range) clamped to
@@ -1099,13 +1081,10 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
     Wide incl = wzero();
     if (act) {
       if (tid < n) incl = wide_of(weight((uint32_t)(s_top[tid] >> 32)));
-      for (int o = 1; o < 64; o <<= 1) {
+      // (inclusive prefix of every limb over the lanes, by DPP moves)
 #pragma unroll
-        for (int i2 = 0; i2 < NL; ++i2) {
-          const unsigned long long y = __shfl_up(incl.l[i2], o, 64);
-          if (lane >= o) incl.l[i2] += y;
-        }
-      }
+      for (int i2 = 0; i2 < NL; ++i2)
+        incl.l[i2] = wave_scan_dpp(incl.l[i2], [](unsigned long long a, unsigned long long b) { return a + b; });
       if (lane == 63) s_w[wave] = incl;
     }
     if (tid == 0) s_pick = n;
@@ -1646,11 +1625,23 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
     // of a kept token come from different wavefronts: each thread waits until its
     // zero stores are done (in this CU's L2) before the barrier, which a
     // workgroup barrier alone does not do for global memory.
+    // The total: limbs summed by DPP on the wavefronts holding entries, then
+    // their sums in LDS (the barrier in between also orders the stores).
     const float w_t = tid < n_list ? weight((uint32_t)(s_top[tid] >> 32)) : 0.0f;
     const bool keep = tid < n_list && (!(mp > 0.0f) || w_t >= mp || tid == 0);
-    const double W = norm_to_double(norm_of(block_wsum(keep ? wide_of(w_t) : wzero())));
+    const int nwl = (n_list + 63) >> 6;  // (n_list >= 1)
+    if (wave < nwl) {
+      Wide t = keep ? wide_of(w_t) : wzero();
+#pragma unroll
+      for (int l = 0; l < NL; ++l)
+        t.l[l] = wave_reduce_dpp(t.l[l], [](unsigned long long a, unsigned long long b) { return a + b; });
+      if (lane == 0) s_w[wave] = t;
+    }
     __builtin_amdgcn_s_waitcnt(kVmemStoresDone);
     __syncthreads();
+    Wide tw = wzero();
+    for (int w = 0; w < nwl; ++w) wadd(tw, s_w[w]);
+    const double W = norm_to_double(norm_of(tw));
     if (keep) orow[key_index(s_top[tid])] = (float)((double)w_t * (1.0 / W));
     return;
   }
