@@ -14,9 +14,11 @@
 //
 // Both run one 1024-thread workgroup per row (filter) or per request (walk).
 // Every float64 sum is formed in a fixed order (each thread in index order, the
-// wavefront by a butterfly, the wavefronts in index order), so results do not
+// wavefront by a fixed tree of lane moves, the wavefronts in index order), so results do not
 // depend on scheduling.  Products and differences that decide an outcome are
 // rounded one at a time (no fused multiply-add), as written.
+#include <type_traits>
+
 #include "tv_common.h"
 
 namespace tv {
@@ -33,18 +35,6 @@ __device__ __forceinline__ double wave_sum_d(double v) {
   return v;
 }
 
-// sum over the workgroup; every thread gets the same value (s: (NT / 64) slots)
-template <int NT = kThreads>
-__device__ __forceinline__ double block_sum_d(double v, double* s) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  v = wave_sum_d(v);
-  if (lane == 0) s[wave] = v;
-  __syncthreads();
-  double t = 0.0;
-  for (int w = 0; w < (NT / 64); ++w) t += s[w];
-  __syncthreads();
-  return t;
-}
 // Wavefront reductions by DPP moves (no LDS round trips): an inclusive scan in
 // rows of 16 lanes (row_shr 1, 2, 4, 8; lanes without a source read 0), then
 // lane 15 of rows 0 and 2 into rows 1 and 3 (row_bcast 15) and lane 31 into
@@ -72,6 +62,10 @@ __device__ __forceinline__ unsigned long long wave_reduce_dpp(unsigned long long
   return ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63) << 32) |
          (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
 }
+__device__ __forceinline__ unsigned long long readlane_u64(unsigned long long v, int l) {
+  return ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l) << 32) |
+         (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+}
 __device__ __forceinline__ double wave_sum_dpp(double v) {
   return __longlong_as_double((long long)wave_reduce_dpp(
       (unsigned long long)__double_as_longlong(v), [](unsigned long long x, unsigned long long y) {
@@ -81,6 +75,28 @@ __device__ __forceinline__ double wave_sum_dpp(double v) {
 }
 __device__ __forceinline__ unsigned long long wave_max_dpp(unsigned long long v) {
   return wave_reduce_dpp(v, [](unsigned long long x, unsigned long long y) { return x > y ? x : y; });
+}
+__device__ __forceinline__ int wave_incl_scan_dpp(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr 1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);  // row_shr 2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr 4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);  // row_shr 8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, true);  // row_bcast 15 into rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, true);  // row_bcast 31 into rows 2, 3
+  return v;
+}
+
+// sum over the workgroup; every thread gets the same value (s: (NT / 64) slots)
+template <int NT = kThreads>
+__device__ __forceinline__ double block_sum_d(double v, double* s) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  v = wave_sum_dpp(v);
+  if (lane == 0) s[wave] = v;
+  __syncthreads();
+  double t = 0.0;
+  for (int w = 0; w < (NT / 64); ++w) t += s[w];
+  __syncthreads();
+  return t;
 }
 
 // two sums and two maxima at once (one round of barriers); every thread gets all
@@ -152,9 +168,15 @@ template <typename T, int NT = kThreads>
 __device__ __forceinline__ void block_scan(T v, T* s, T& lo, T& hi, T& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   T incl = v;
-  for (int o = 1; o < 64; o <<= 1) {
-    const T y = __shfl_up(incl, o, 64);
-    if (lane >= o) incl = incl + y;
+  if constexpr (std::is_same_v<T, int>) {
+    incl = wave_incl_scan_dpp(v);
+  } else if constexpr (std::is_same_v<T, unsigned long long>) {
+    incl = wave_scan_dpp(v, [](unsigned long long a, unsigned long long b) { return a + b; });
+  } else {
+    for (int o = 1; o < 64; o <<= 1) {
+      const T y = __shfl_up(incl, o, 64);
+      if (lane >= o) incl = incl + y;
+    }
   }
   if (lane == 63) s[wave] = incl;
   __syncthreads();
@@ -164,8 +186,12 @@ __device__ __forceinline__ void block_scan(T v, T* s, T& lo, T& hi, T& total) {
     tot = tot + s[w];
   }
   __syncthreads();
-  const T up = __shfl_up(incl, 1, 64);
-  lo = lane > 0 ? off + up : off;
+  if constexpr (std::is_same_v<T, int> || std::is_same_v<T, unsigned long long>) {
+    lo = off + (incl - v);  // (exact)
+  } else {
+    const T up = __shfl_up(incl, 1, 64);
+    lo = lane > 0 ? off + up : off;
+  }
   hi = off + incl;
   total = tot;
 }
@@ -173,7 +199,7 @@ __device__ __forceinline__ void block_scan(T v, T* s, T& lo, T& hi, T& total) {
 template <int NT = kThreads>
 __device__ __forceinline__ unsigned long long block_max_u64(unsigned long long v, unsigned long long* s) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  v = wave_max_u64(v);
+  v = wave_max_dpp(v);
   if (lane == 0) s[wave] = v;
   __syncthreads();
   unsigned long long t = 0ull;
@@ -187,8 +213,8 @@ __device__ __forceinline__ unsigned long long block_max_u64(unsigned long long v
 template <int NT = kThreads>
 __device__ __forceinline__ void block_max2_u64(unsigned long long& a, unsigned long long& c, unsigned long long* s) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  a = wave_max_u64(a);
-  c = wave_max_u64(c);
+  a = wave_max_dpp(a);
+  c = wave_max_dpp(c);
   if (lane == 0) {
     s[wave] = a;
     s[NT / 64 + wave] = c;
@@ -586,15 +612,6 @@ __device__ __forceinline__ bool row_by_cost(int k, int B, int V, int T_max, cons
 // r; the five class totals and prefixes are DPP scans over the lanes), so a
 // workgroup finds its row without a barrier: the workgroup-wide scans of
 // row_by_cost took ~4.7 us of every row's workgroup (measured, 2410 rows).
-__device__ __forceinline__ int wave_incl_scan_dpp(int v) {
-  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr 1
-  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);  // row_shr 2
-  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr 4
-  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);  // row_shr 8
-  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, true);  // row_bcast 15 into rows 1, 3
-  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, true);  // row_bcast 31 into rows 2, 3
-  return v;
-}
 template <int NT>
 __device__ __forceinline__ bool row_by_cost_wave(int k, int B, int V, int T_max, const int* __restrict__ tree_size,
                                                  const int* __restrict__ status,
@@ -941,11 +958,7 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
       const int e0 = min(ne, lane * per), e1 = min(ne, e0 + per);
       int c = 0;
       for (int e = e0; e < e1; ++e) c += __popcll(s_hist[e]);
-      int incl = c;
-      for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += y;
-      }
+      const int incl = wave_incl_scan_dpp(c);
       if (incl - c < n && n <= incl) {
         int r = n - (incl - c);
         for (int e = e0; e < e1; ++e) {
@@ -985,12 +998,9 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
         for (int w = 0; w < CSETS; ++w) m[j] += s_hist[w * 256 + 4 * lane + j];
         g += m[j];
       }
-      unsigned long long suf = g;  // total of this lane's bins and every higher lane's
-      for (int o = 1; o < 64; o <<= 1) {
-        const unsigned long long y = __shfl_down(suf, o, 64);
-        if (lane + o < 64) suf += y;
-      }
-      unsigned long long run = (unsigned long long)above + (suf - g);
+      // the higher lanes' bins: the wavefront's total less the inclusive prefix
+      const unsigned long long inc = wave_scan_dpp(g, [](unsigned long long a, unsigned long long b) { return a + b; });
+      unsigned long long run = (unsigned long long)above + (readlane_u64(inc, 63) - inc);
       int cand = -1;
       unsigned long long cabove = 0ull;
 #pragma unroll
@@ -1273,18 +1283,22 @@ __global__ __launch_bounds__(NT) void k_sampling_probs(int T_max, int V, const f
     if (tid == 0) s_sel = -1;
     __syncthreads();
     // carry-save sums: a bin's limbs are below 2^46, so 1024 of them fit a limb
-    Wide suf = wzero();  // this thread's bins and those of the higher lanes of its wavefront
     Wide run = wzero();
     if (part) {
+      Wide own = wzero();
 #pragma unroll 1
-      for (int j = 0; j < bpt; ++j) wadd(suf, bin_at(tid * bpt + j));
-      for (int o = 1; o < 64; o <<= 1) {
-        const Wide y = wshfl_down(suf, o);
-        if (lane + o < 64) wadd(suf, y);
+      for (int j = 0; j < bpt; ++j) wadd(own, bin_at(tid * bpt + j));
+      // limb by limb: the inclusive prefix over the lanes (DPP moves) and the
+      // wavefront's total; the higher lanes' bins are their difference (exact:
+      // each limb of a prefix is at most that limb of the total)
+      Wide inc, tot;
+#pragma unroll
+      for (int l = 0; l < NL; ++l) {
+        inc.l[l] = wave_scan_dpp(own.l[l], [](unsigned long long a, unsigned long long b) { return a + b; });
+        tot.l[l] = readlane_u64(inc.l[l], 63);
       }
-      if (lane == 0) s_w[wave] = suf;
-      run = wshfl_down(suf, 1);  // the higher lanes' bins
-      if (lane == 63) run = wzero();
+      run = wsub(tot, inc);  // the higher lanes' bins
+      if (lane == 0) s_w[wave] = tot;
     }
     __syncthreads();
     if (part) {
