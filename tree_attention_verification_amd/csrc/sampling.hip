@@ -58,13 +58,7 @@ __device__ __forceinline__ unsigned long long wave_scan_dpp(unsigned long long v
 }
 template <class Op>
 __device__ __forceinline__ unsigned long long wave_reduce_dpp(unsigned long long v, Op op) {
-  v = wave_scan_dpp(v, op);
-  return ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63) << 32) |
-         (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
-}
-__device__ __forceinline__ unsigned long long readlane_u64(unsigned long long v, int l) {
-  return ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l) << 32) |
-         (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  return readlane_u64(wave_scan_dpp(v, op), 63);
 }
 __device__ __forceinline__ double wave_sum_dpp(double v) {
   return __longlong_as_double((long long)wave_reduce_dpp(
