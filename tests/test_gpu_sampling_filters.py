@@ -8,7 +8,8 @@ probabilities within 2e-6 relative (one float32 rounding of w / W, W summed in a
 different order); rows past a request's tree are untouched.  Cases: several
 vocabulary sizes (50 to 128256, i.e. one to ~125 values per thread), mixed
 per-request parameters, ties (logits rounded to a coarse grid), NaN / +-inf / -0.0
-logits, greedy and off settings of every filter, bad statuses, and T_max = 256.
+logits, greedy and off settings of every filter, bad statuses, T_max = 256, and rows
+off 16-byte boundaries.
 """
 import numpy as np
 import pytest
@@ -32,14 +33,19 @@ def _dev(x, dtype=None):
     return torch.from_numpy(np.ascontiguousarray(x if dtype is None else np.asarray(x, dtype))).cuda()
 
 
-def run_filter(logits, tree_size, status, params):
+def run_filter(logits, tree_size, status, params, offset=0):
+    """offset > 0: the logits and the output start `offset` floats into larger
+    buffers (rows no longer on 16-byte boundaries)."""
     import torch
     from oracle import sampling as osm
     from tree_attention_verification_amd import _lib as tv
     B, T_max, V = logits.shape
     temp, top_k, top_p, min_p = params
-    out = torch.full((B, T_max, V), -7.0, dtype=torch.float32, device="cuda")
-    tv.tree_sampling_probs(B, T_max, V, _dev(logits), _dev(tree_size, np.int32),
+    n = B * T_max * V
+    out = torch.full((n + offset,), -7.0, dtype=torch.float32, device="cuda")[offset:].view(B, T_max, V)
+    lg = torch.zeros(n + offset, dtype=torch.float32, device="cuda")
+    lg[offset:] = _dev(logits).reshape(-1)
+    tv.tree_sampling_probs(B, T_max, V, lg[offset:].view(B, T_max, V), _dev(tree_size, np.int32),
                            None if status is None else _dev(status, np.int32), _dev(temp, np.float32),
                            _dev(top_k, np.int32), _dev(top_p, np.float32), _dev(min_p, np.float32), out)
     torch.cuda.synchronize()
@@ -65,6 +71,21 @@ def test_filters_mixed_parameters(V):
     params[1][0] = min(V - 1, 37)            # make sure top-k, top-p and min-p all run somewhere
     params[2][0], params[3][0], params[0][0] = 0.9, 0.01, 0.8
     run_filter(lg, w.given_size, None, params)
+
+
+@pytest.mark.parametrize("offset", [1, 2])
+def test_filters_rows_off_16_byte_boundaries(offset):
+    """V = 32000 with the logits and the output shifted by 4 or 8 bytes: the rows
+    keep their keys in LDS but take the one-token passes."""
+    V = 32000
+    w = gen.make_custom(cfg_id=1660 + offset, B=6, mode="given", given_sizes=[5, 2, 8, 1, 6, 3], V=V, P=4,
+                        T_max=8, dcap=6)
+    lg = gen.synthetic_target_logits(w, w.given_size)
+    params = gen.sampling_params(w, 6)
+    params[1][0] = 37
+    params[2][0], params[3][0], params[0][0] = 0.9, 0.01, 0.8
+    params[1][1], params[2][1], params[3][1], params[0][1] = 0, 0.7, 0.0, 1.1   # radix top-p
+    run_filter(lg, w.given_size, None, params, offset=offset)
 
 
 @pytest.mark.parametrize("tie_step", [0.5, 2.0])
